@@ -1,0 +1,379 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each ``check_*`` takes an ``oracle.Oracle`` and raises AssertionError on a
+mismatch.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutants.py`` runs them on builds of the oracle with a mistake
+planted in the C source and requires that some check fails for every mistake.
+
+What each pin compares against:
+  * bf16 codec      -- torch's own fp32<->bf16 conversions (a library routine).
+  * residual        -- torch fp32 add then bf16 rounding: both routes must give
+                       the same bits for every finite bf16 pair.
+  * RMSNorm         -- torch.nn.functional.rms_norm in float64 (library routine);
+                       closed forms (constant, one-hot and zero rows); exact
+                       scale invariance at eps = 0.
+  * LayerNorm fwd   -- torch.nn.functional.layer_norm / var_mean in float64;
+                       invariants (zero mean, closed-form second moment,
+                       constant row -> bias, affine consistency).
+  * LayerNorm bwd   -- torch autograd in float64; central finite differences of
+                       sum(dy * LayerNorm(x)) with the statistics recomputed
+                       from x; column sums against math.fsum.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+F = torch.nn.functional
+
+
+# ---------------------------------------------------------------- helpers
+def torch_bf16_bits(values_f32: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def rand_bf16(rng, shape, mean=0.0, std=1.0) -> np.ndarray:
+    return torch_bf16_bits((rng.standard_normal(shape) * std + mean).astype(np.float32))
+
+
+def close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.abs(a - b)
+    lim = atol + rtol * np.abs(b)
+    bad = ~(err <= lim)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                           f"max err {float(err.max()):.3e}")
+
+
+def ln_np(x, w, b, eps):
+    """LayerNorm in float64 numpy, statistics recomputed from x (test-side)."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * w + b
+
+
+def stats_np(x, eps):
+    mu = x.mean(axis=-1)
+    var = ((x - mu[:, None]) ** 2).mean(axis=-1)
+    return mu, 1.0 / np.sqrt(var + eps)
+
+
+# ---------------------------------------------------------------- bf16 codec
+def check_bf16_decode(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = o.bf16_decode(bits)
+    ref = torch_bf16_to_f64(bits)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan_ref), "NaN patterns differ"
+    assert np.array_equal(mine[~nan_ref], ref[~nan_ref]), "decoded values differ"
+    assert np.array_equal(np.signbit(mine[~nan_ref]), np.signbit(ref[~nan_ref])), "zero signs"
+
+
+def _encode_cases(rng) -> np.ndarray:
+    cases = []
+    hi = np.arange(65536, dtype=np.uint32) << 16
+    # exact bf16 values, exact ties, just below / above ties
+    for low in (0x0000, 0x8000, 0x7FFF, 0x8001, 0x4000, 0xC000, 0xFFFF, 0x0001):
+        cases.append(hi | np.uint32(low))
+    # fp32 subnormals and the smallest normals
+    cases.append(np.arange(0, 1 << 20, 37, dtype=np.uint32))
+    cases.append(np.arange(0x007F0000, 0x00810000, 3, dtype=np.uint32))
+    # the overflow boundary: largest finite bf16 .. fp32 max
+    cases.append(np.arange(0x7F7F0000, 0x7F800000, 1, dtype=np.uint32))
+    cases.append(rng.integers(0, 1 << 32, size=1_000_000, dtype=np.uint64).astype(np.uint32))
+    u = np.concatenate(cases)
+    u = np.concatenate([u, u ^ np.uint32(0x80000000)])
+    f = u.view(np.float32)
+    return f[np.isfinite(f)]
+
+
+def check_bf16_encode(o):
+    rng = np.random.default_rng(1234)
+    f = _encode_cases(rng)
+    mine = o.bf16_encode(f.astype(np.float64))
+    ref = torch_bf16_bits(f)
+    bad = mine != ref
+    assert not bad.any(), (f"{int(bad.sum())} encodings differ, e.g. fp32 bits "
+                           f"{hex(f[bad][0].view(np.uint32))}: {hex(mine[bad][0])} vs "
+                           f"{hex(ref[bad][0])}")
+
+
+# ---------------------------------------------------------------- fused residual
+def _wide_pairs(rng, n):
+    """bf16 pairs (x, r) covering equal, near and far exponents and cancellation."""
+    x = rand_bf16(rng, (n,))
+    scale = np.exp2(rng.integers(-30, 31, size=n)).astype(np.float32)
+    r = torch_bf16_bits(torch_bf16_to_f64(rand_bf16(rng, (n,))).astype(np.float32) * scale)
+    r[: n // 8] = x[: n // 8] ^ np.uint16(0x8000)  # exact cancellation -> +0
+    # sums past the largest finite bf16 / fp32 (must overflow to +-inf)
+    big = np.array([0x7F7F, 0x7F7E, 0x7F00, 0xFF7F, 0x7F7F], np.uint16)
+    x[n // 8: n // 8 + 5] = big
+    r[n // 8: n // 8 + 5] = np.array([0x7F7F, 0x7F7F, 0x7F7F, 0xFF7F, 0x7F70], np.uint16)
+    return x, r
+
+
+def check_fused_residual(o):
+    rng = np.random.default_rng(7)
+    x, r = _wide_pairs(rng, 64 * 512)
+    x = x.reshape(64, 512)
+    r = r.reshape(64, 512)
+    w = rand_bf16(rng, (512,), 1.0, 0.1)
+    _, res, _ = o.fused_add_rmsnorm(x, r, w, 1e-6)
+    with np.errstate(over="ignore"):
+        s32 = torch_bf16_to_f64(x).astype(np.float32) + torch_bf16_to_f64(r).astype(np.float32)
+    ref = torch_bf16_bits(s32)
+    bad = res != ref
+    assert not bad.any(), f"{int(bad.sum())} residual bits differ"
+    assert (res.reshape(-1)[: (64 * 512) // 8] == 0).all(), "x + (-x) must give +0"
+
+
+# ---------------------------------------------------------------- RMSNorm
+def check_rms_library(o):
+    rng = np.random.default_rng(11)
+    for rows, hidden in ((5, 64), (3, 1000), (2, 4096)):
+        x = rand_bf16(rng, (rows, hidden))
+        r = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        eps = float(np.float32(1e-6))
+        xd, rd, wd = (torch.from_numpy(torch_bf16_to_f64(a)) for a in (x, r, w))
+        out, rstd = o.rmsnorm_fwd(x, w, eps)
+        ref = F.rms_norm(xd, (hidden,), wd, eps).numpy()
+        close(out, ref, 1e-13, 1e-300, "rmsnorm vs torch rms_norm")
+        ref_rstd = torch.rsqrt((xd * xd).mean(-1) + eps).numpy()
+        close(rstd, ref_rstd, 1e-13, 0, "rmsnorm rstd")
+        fout, _, _ = o.fused_add_rmsnorm(x, r, w, eps)
+        fref = F.rms_norm(xd + rd, (hidden,), wd, eps).numpy()
+        close(fout, fref, 1e-13, 1e-300, "fused vs torch rms_norm(x + r)")
+
+
+def check_rms_closed_forms(o):
+    hidden = 256
+    eps = float(np.float32(1e-6))
+    rng = np.random.default_rng(3)
+    w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+    wd = torch_bf16_to_f64(w)
+    consts = np.array([1.0, -3.5, 0.0078125, 96.0], np.float32)
+    x = torch_bf16_bits(np.repeat(consts[:, None], hidden, axis=1))
+    out, _ = o.rmsnorm_fwd(x, w, eps)
+    c = consts.astype(np.float64)[:, None]
+    close(out, c / np.sqrt(c * c + eps) * wd, 1e-15, 0, "constant row")
+    out0, _ = o.rmsnorm_fwd(x, w, 0.0)
+    assert np.array_equal(out0, np.sign(c) * wd), "constant row at eps=0 must equal sign*w"
+    a = np.float64(2.5)
+    xh = np.zeros((3, hidden), np.float32)
+    ks = [0, 17, hidden - 1]
+    for i, k in enumerate(ks):
+        xh[i, k] = a
+    out, _ = o.rmsnorm_fwd(torch_bf16_bits(xh), w, eps)
+    for i, k in enumerate(ks):
+        exp = a / math.sqrt(a * a / hidden + eps) * wd[k]
+        close(out[i, k], exp, 1e-15, 0, "one-hot value")
+        others = np.delete(out[i], k)
+        assert (others == 0).all(), "one-hot: other outputs must be exactly 0"
+    out, _ = o.rmsnorm_fwd(np.zeros((2, hidden), np.uint16), w, eps)
+    assert (out == 0).all(), "zero row"
+    # fused: r = -x + c gives the constant row c
+    xr = rand_bf16(rng, (4, hidden))
+    xrd = torch_bf16_to_f64(xr).astype(np.float32)
+    r = torch_bf16_bits(np.repeat(consts[:, None], hidden, axis=1) - xrd)
+    fout, res, _ = o.fused_add_rmsnorm(xr, r, w, eps)
+    sd = torch_bf16_to_f64(xr) + torch_bf16_to_f64(r)
+    close(fout, sd / np.sqrt((sd * sd).mean(1, keepdims=True) + eps) * wd, 1e-14, 1e-300,
+          "fused near-constant rows")
+
+
+def _scale_bits(bits, k):
+    return torch_bf16_bits((torch_bf16_to_f64(bits) * 2.0 ** k).astype(np.float32))
+
+
+def check_rms_scale_invariance(o):
+    rng = np.random.default_rng(5)
+    x = rand_bf16(rng, (6, 512))
+    r = rand_bf16(rng, (6, 512))
+    w = rand_bf16(rng, (512,), 1.0, 0.1)
+    base, _ = o.rmsnorm_fwd(x, w, 0.0)
+    fbase, _, _ = o.fused_add_rmsnorm(x, r, w, 0.0)
+    for k in (-7, -1, 3, 12):
+        out, _ = o.rmsnorm_fwd(_scale_bits(x, k), w, 0.0)
+        assert np.array_equal(out, base), f"RMSNorm(2^{k} x) != RMSNorm(x) at eps=0"
+        fout, _, _ = o.fused_add_rmsnorm(_scale_bits(x, k), _scale_bits(r, k), w, 0.0)
+        assert np.array_equal(fout, fbase), f"fused not scale invariant at 2^{k}"
+    # eps > 0: scaling by alpha is the same as dividing eps by alpha^2
+    eps = 1e-2
+    out_a, _ = o.rmsnorm_fwd(_scale_bits(x, 3), w, eps)
+    out_b, _ = o.rmsnorm_fwd(x, w, eps / 64.0)
+    close(out_a, out_b, 1e-14, 1e-300, "scaling vs eps/alpha^2")
+
+
+# ---------------------------------------------------------------- LayerNorm forward
+def check_ln_library(o):
+    rng = np.random.default_rng(13)
+    for rows, hidden in ((4, 64), (3, 768), (2, 12288)):
+        x = rand_bf16(rng, (rows, hidden), 0.5, 2.0)
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        b = rand_bf16(rng, (hidden,), 0.0, 0.1)
+        eps = float(np.float32(1e-5))
+        xd, wd, bd = (torch.from_numpy(torch_bf16_to_f64(a)) for a in (x, w, b))
+        y, mean, rstd = o.layernorm_fwd(x, w, b, eps)
+        ref = F.layer_norm(xd, (hidden,), wd, bd, eps).numpy()
+        close(y, ref, 1e-12, 1e-13, "layernorm vs torch layer_norm")
+        var, mu = torch.var_mean(xd, dim=-1, unbiased=False)
+        close(mean, mu.numpy(), 1e-13, 1e-15, "mean vs torch var_mean")
+        close(rstd, (1.0 / torch.sqrt(var + eps)).numpy(), 1e-13, 0, "rstd vs torch var_mean")
+
+
+def check_ln_invariants(o):
+    rng = np.random.default_rng(17)
+    eps = float(np.float32(1e-5))
+    for hidden in (64, 1024, 12288):
+        x = rand_bf16(rng, (3, hidden), 0.5, 2.0)
+        ones = torch_bf16_bits(np.ones(hidden, np.float32))
+        zeros = np.zeros(hidden, np.uint16)
+        y, mean, rstd = o.layernorm_fwd(x, ones, zeros, eps)
+        assert (np.abs(y.sum(1)) <= 1e-12 * hidden).all(), "sum of y must be 0"
+        xd = torch_bf16_to_f64(x)
+        var = ((xd - xd.mean(1, keepdims=True)) ** 2).mean(1)
+        close((y * y).mean(1), var / (var + eps), 1e-12, 0, "second moment var/(var+eps)")
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        b = rand_bf16(rng, (hidden,), 0.0, 0.1)
+        yab, _, _ = o.layernorm_fwd(x, w, b, eps)
+        close(yab, y * torch_bf16_to_f64(w) + torch_bf16_to_f64(b), 1e-13, 1e-14,
+              "affine consistency")
+        const = torch_bf16_bits(np.full((2, hidden), -1.75, np.float32))
+        yc, mc, rc = o.layernorm_fwd(const, w, b, eps)
+        assert np.array_equal(yc, np.broadcast_to(torch_bf16_to_f64(b), yc.shape)), \
+            "constant row must give y = b"
+        assert (mc == -1.75).all() and np.allclose(rc, 1 / math.sqrt(eps), rtol=1e-15)
+
+
+# ---------------------------------------------------------------- LayerNorm backward
+def check_lnb_autograd(o):
+    rng = np.random.default_rng(19)
+    eps = float(np.float32(1e-5))
+    for rows, hidden in ((5, 64), (7, 1024), (3, 4096)):
+        x = rand_bf16(rng, (rows, hidden))
+        dy = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        b = rand_bf16(rng, (hidden,), 0.0, 0.1)
+        xd = torch_bf16_to_f64(x)
+        mu, rstd = stats_np(xd, eps)
+        dx, dw, db = o.layernorm_bwd(dy, x, mu, rstd, w)
+        xt = torch.from_numpy(xd.copy()).requires_grad_(True)
+        wt = torch.from_numpy(torch_bf16_to_f64(w)).requires_grad_(True)
+        bt = torch.from_numpy(torch_bf16_to_f64(b)).requires_grad_(True)
+        F.layer_norm(xt, (hidden,), wt, bt, eps).backward(torch.from_numpy(torch_bf16_to_f64(dy)))
+        scale = np.abs(xt.grad.numpy()).max()
+        close(dx, xt.grad.numpy(), 1e-10, 1e-12 * scale, "dx vs autograd")
+        close(dw, wt.grad.numpy(), 1e-10, 1e-11, "dweight vs autograd")
+        close(db, bt.grad.numpy(), 1e-12, 1e-12, "dbias vs autograd")
+
+
+def check_lnb_finite_differences(o):
+    rng = np.random.default_rng(23)
+    eps = float(np.float32(1e-5))
+    for rows, hidden in ((1, 8), (3, 16), (3, 64)):
+        x = rand_bf16(rng, (rows, hidden), 0.5, 2.0)
+        dy = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        b = rand_bf16(rng, (hidden,), 0.0, 0.1)
+        xd, dyd, wd, bd = (torch_bf16_to_f64(a) for a in (x, dy, w, b))
+        mu, rstd = stats_np(xd, eps)
+        dx, dw, db = o.layernorm_bwd(dy, x, mu, rstd, w)
+
+        def loss_row(i, xrow, wv=wd, bv=bd):
+            return float(np.sum(dyd[i] * ln_np(xrow[None, :], wv, bv, eps)[0]))
+
+        fd = np.empty_like(xd)
+        for i in range(rows):
+            for j in range(hidden):
+                h = 1e-5 * max(1.0, abs(xd[i, j]))
+                xp = xd[i].copy()
+                xm = xd[i].copy()
+                xp[j] += h
+                xm[j] -= h
+                fd[i, j] = (loss_row(i, xp) - loss_row(i, xm)) / (2 * h)
+        close(dx, fd, 1e-6, 1e-6 * np.abs(fd).max(), "dx vs central finite differences")
+        fdw = np.empty(hidden)
+        fdb = np.empty(hidden)
+        for j in range(hidden):
+            wp, wm, bp, bm = wd.copy(), wd.copy(), bd.copy(), bd.copy()
+            wp[j] += 1e-3
+            wm[j] -= 1e-3
+            bp[j] += 1e-3
+            bm[j] -= 1e-3
+            fdw[j] = sum(loss_row(i, xd[i], wp, bd) - loss_row(i, xd[i], wm, bd)
+                         for i in range(rows)) / 2e-3
+            fdb[j] = sum(loss_row(i, xd[i], wd, bp) - loss_row(i, xd[i], wd, bm)
+                         for i in range(rows)) / 2e-3
+        close(dw, fdw, 1e-8, 1e-9, "dweight vs finite differences")
+        close(db, fdb, 1e-8, 1e-9, "dbias vs finite differences")
+
+
+def check_lnb_column_sums(o):
+    rng = np.random.default_rng(29)
+    eps = float(np.float32(1e-5))
+    rows, hidden = 3000, 96
+    x = rand_bf16(rng, (rows, hidden))
+    dy = rand_bf16(rng, (rows, hidden))
+    w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+    xd, dyd = torch_bf16_to_f64(x), torch_bf16_to_f64(dy)
+    mu, rstd = stats_np(xd, eps)
+    dx, dw, db = o.layernorm_bwd(dy, x, mu, rstd, w)
+    xhat = (xd - mu[:, None]) * rstd[:, None]
+    for j in range(hidden):
+        assert db[j] == math.fsum(dyd[:, j]), f"dbias[{j}] != fsum"
+        ref = math.fsum(dyd[:, j] * xhat[:, j])
+        assert abs(dw[j] - ref) <= 1e-12 * math.fsum(np.abs(dyd[:, j] * xhat[:, j])), \
+            f"dweight[{j}] vs fsum"
+    # inner-reduction invariants: sum_j dx = 0 and sum_j dx * xhat = rstd*H*c2*eps/(var+eps)
+    g = dyd * torch_bf16_to_f64(w)
+    c2 = (g * xhat).mean(1)
+    var = 1.0 / rstd ** 2 - eps
+    close(dx.sum(1), np.zeros(rows), 0, 1e-11 * np.abs(dx).sum(1).max(), "sum_j dx = 0")
+    close((dx * xhat).sum(1), rstd * hidden * c2 * eps / (var + eps), 1e-6,
+          1e-11 * np.abs(dx * xhat).sum(1).max(), "sum_j dx*xhat closed form")
+
+
+def check_thread_count_independence(o):
+    rng = np.random.default_rng(31)
+    x = rand_bf16(rng, (37, 256))
+    r = rand_bf16(rng, (37, 256))
+    w = rand_bf16(rng, (256,), 1.0, 0.1)
+    b = rand_bf16(rng, (256,), 0.0, 0.1)
+    a1 = o.fused_add_rmsnorm(x, r, w, 1e-6, nthreads=1)
+    a7 = o.fused_add_rmsnorm(x, r, w, 1e-6, nthreads=7)
+    for u, v in zip(a1, a7):
+        assert np.array_equal(u, v)
+    y1 = o.layernorm_fwd(x, w, b, 1e-5, nthreads=1)
+    y5 = o.layernorm_fwd(x, w, b, 1e-5, nthreads=5)
+    for u, v in zip(y1, y5):
+        assert np.array_equal(u, v)
+    d1 = o.layernorm_bwd(r, x, y1[1], y1[2], w, nthreads=1)
+    d6 = o.layernorm_bwd(r, x, y1[1], y1[2], w, nthreads=6)
+    for u, v in zip(d1, d6):
+        assert np.array_equal(u, v)
+
+
+ALL_CHECKS = [
+    check_bf16_decode,
+    check_bf16_encode,
+    check_fused_residual,
+    check_rms_library,
+    check_rms_closed_forms,
+    check_rms_scale_invariance,
+    check_ln_library,
+    check_ln_invariants,
+    check_lnb_autograd,
+    check_lnb_finite_differences,
+    check_lnb_column_sums,
+    check_thread_count_independence,
+]

@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in a copy of the oracle's C source (CPU only) and
+require that at least one pin in oracle_checks.py catches each of them.
+
+This shows the pins are strong enough that a dropped term, a wrong sign, a
+wrong divisor or index, or a rounding slip anywhere in the oracle would not go
+unnoticed.  The mutated copies are built in a temporary directory; the real
+oracle is untouched."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_checks
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, exact text in oracle.c, replacement)
+MUTANTS = [
+    ("decode_bias", "e - 127 - 7", "e - 126 - 7"),
+    ("decode_subnormal_quantum", "ldexp((double)f, -133)", "ldexp((double)f, -134)"),
+    ("encode_ties_up", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    ("encode_truncate", "if (frac > 0.5) return fl + 1.0;", "if (frac > 2.0) return fl + 1.0;"),
+    ("encode_subnormal_floor", "if (q < -133) q = -133;", "if (q < -140) q = -140;"),
+    ("encode_no_overflow", "if (e >= 255) return", "if (e >= 256) return"),
+    ("residual_subtract", "if (c->r) v += orc_bf16_decode(c->r[base + j]);",
+     "if (c->r) v -= orc_bf16_decode(c->r[base + j]);"),
+    ("rms_divisor", "sqrt(ss / (double)H + c->eps)", "sqrt(ss / (double)(H - 1) + c->eps)"),
+    ("rms_eps_outside", "1.0 / sqrt(ss / (double)H + c->eps)",
+     "1.0 / (sqrt(ss / (double)H) + c->eps)"),
+    ("rms_no_weight", "s[j] * rstd * orc_bf16_decode(c->w[j])", "s[j] * rstd"),
+    ("rms_weight_index", "s[j] * rstd * orc_bf16_decode(c->w[j])",
+     "s[j] * rstd * orc_bf16_decode(c->w[H - 1 - j])"),
+    ("rms_abs_sum", "ss += s[j] * s[j];", "ss += fabs(s[j]);"),
+    ("ln_unbiased", "sq / (double)H", "sq / (double)(H - 1)"),
+    ("ln_one_pass_var", "const double d = orc_bf16_decode(xr[j]) - mu;",
+     "const double d = orc_bf16_decode(xr[j]);"),
+    ("ln_no_bias", "+\n                              orc_bf16_decode(c->b[j]);",
+     "+\n                              0.0;"),
+    ("ln_mean_sign", "(orc_bf16_decode(xr[j]) - mu) * rstd", "(orc_bf16_decode(xr[j]) + mu) * rstd"),
+    ("ln_mean_divisor", "const double mu = sum / (double)H;",
+     "const double mu = sum / (double)(H + 1);"),
+    ("lnb_drop_c1", "(g - c1 - lnb_xhat(c, i, j) * c2)", "(g - lnb_xhat(c, i, j) * c2)"),
+    ("lnb_drop_c2", "(g - c1 - lnb_xhat(c, i, j) * c2)", "(g - c1)"),
+    ("lnb_sign_c1", "(g - c1 - lnb_xhat(c, i, j) * c2)", "(g + c1 - lnb_xhat(c, i, j) * c2)"),
+    ("lnb_no_rstd", "c->dx[i * H + j] = c->rstd[i] * (", "c->dx[i * H + j] = 1.0 * ("),
+    ("lnb_g_without_w", "const double g = orc_bf16_decode(c->dy[i * H + j]) * orc_bf16_decode(c->w[j]);\n            sum_g",
+     "const double g = orc_bf16_decode(c->dy[i * H + j]);\n            sum_g"),
+    ("lnb_xhat_sign", "(orc_bf16_decode(c->x[i * c->hidden + j]) - c->mean[i]) * c->rstd[i]",
+     "(orc_bf16_decode(c->x[i * c->hidden + j]) + c->mean[i]) * c->rstd[i]"),
+    ("lnb_dweight_no_xhat", "dw += d * lnb_xhat(c, i, j);", "dw += d;"),
+    ("lnb_dbias_scaled", "db += d;", "db += d * lnb_xhat(c, i, j);"),
+    ("lnb_c2_divisor", "const double c2 = sum_gx / (double)H;",
+     "const double c2 = sum_gx / (double)(H - 1);"),
+    ("lnb_cols_skip_first_row", "for (int64_t i = 0; i < c->rows; ++i) {",
+     "for (int64_t i = 1; i < c->rows; ++i) {"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_mutant_list_applies_cleanly():
+    src = open(SRC).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) >= 1, f"mutant {name}: text not found in oracle.c"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(workdir, name, old, new):
+    src = open(SRC).read()
+    assert old in src
+    d = workdir / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), d / "oracle.h")
+    (d / "oracle.c").write_text(src.replace(old, new))
+    lib = oracle.build(sources=[str(d / "oracle.c")], out_path=str(d / "liboracle.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for check in oracle_checks.ALL_CHECKS:
+        try:
+            check(o)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no pin catches the planted mistake '{name}'"

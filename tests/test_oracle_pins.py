@@ -1,0 +1,16 @@
+"""The oracle against its pins (CPU only): see oracle_checks.py for what each
+check compares against."""
+import pytest
+
+import oracle
+import oracle_checks
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("check", oracle_checks.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(orc, check):
+    check(orc)
