@@ -1,0 +1,280 @@
+"""Inner-persistent row normalization for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``librownorm.so`` (C ABI declared in
+``include/norm.h``).  It only checks tensor metadata and marshals pointers,
+sizes and the current HIP stream; every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library is missing the
+import of an op raises.
+
+Operations (names as in the C ABI):
+  * ``fused_add_rmsnorm``  -- residual <- bf16(x + residual);
+                              out <- bf16(RMSNorm(x + residual) * w)
+  * ``rmsnorm_fwd``        -- out <- bf16(RMSNorm(x) * w)
+  * ``layernorm_fwd``      -- y <- bf16(LayerNorm(x) * w + b), fp32 mean/rstd
+  * ``layernorm_bwd``      -- dx (bf16), dweight/dbias (fp32) from dy, x, mean, rstd, w
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librownorm.so")
+
+HIDDEN_SIZES = (1024, 2048, 4096, 8192, 12288, 16384)
+
+OP_FUSED_ADD_RMSNORM = 0
+OP_RMSNORM_FWD = 1
+OP_LAYERNORM_FWD = 2
+OP_LAYERNORM_BWD = 3
+OPS = {"fused_add_rmsnorm": 0, "rmsnorm_fwd": 1, "layernorm_fwd": 2, "layernorm_bwd": 3}
+
+STATUS = {
+    0: "NORM_SUCCESS",
+    1: "NORM_ERROR_INVALID_VALUE",
+    2: "NORM_ERROR_UNSUPPORTED_HIDDEN",
+    3: "NORM_ERROR_MISALIGNED",
+    4: "NORM_ERROR_WORKSPACE",
+    5: "NORM_ERROR_LAUNCH",
+    6: "NORM_ERROR_DEVICE",
+}
+
+
+class NormError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class LaunchCfg(ctypes.Structure):
+    _fields_ = [("threads_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("grid", ctypes.c_int32)]
+
+    def astuple(self):
+        return (self.threads_per_row, self.rows_per_block, self.grid)
+
+    def __repr__(self):
+        return (f"LaunchCfg(threads_per_row={self.threads_per_row}, "
+                f"rows_per_block={self.rows_per_block}, grid={self.grid})")
+
+
+@dataclass(frozen=True)
+class Cfg:
+    threads_per_row: int
+    rows_per_block: int = 1
+    grid: int = 0
+
+    def c(self) -> LaunchCfg:
+        return LaunchCfg(self.threads_per_row, self.rows_per_block, self.grid)
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_cfgp = ctypes.POINTER(LaunchCfg)
+
+
+def lib() -> ctypes.CDLL:
+    """Load librownorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m row_normalization_persistent_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.norm_status_string.argtypes = [ctypes.c_int]
+    L.norm_status_string.restype = ctypes.c_char_p
+    L.norm_fused_add_rmsnorm_cfg.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp]
+    L.norm_rmsnorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp]
+    L.norm_layernorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp,
+                                         _vp]
+    L.norm_layernorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _i64, _i64, _f32, _cfgp, _vp]
+    L.norm_fused_add_rmsnorm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]
+    L.norm_rmsnorm_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _vp]
+    L.norm_layernorm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]
+    L.norm_layernorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _i64, _i64, _f32, _vp]
+    for n in ("norm_fused_add_rmsnorm_cfg", "norm_rmsnorm_fwd_cfg", "norm_layernorm_fwd_cfg",
+              "norm_layernorm_bwd_cfg", "norm_fused_add_rmsnorm", "norm_rmsnorm_fwd",
+              "norm_layernorm_fwd", "norm_layernorm_bwd"):
+        getattr(L, n).restype = ctypes.c_int
+    L.norm_layernorm_bwd_workspace_bytes.argtypes = [_i64, _i64]
+    L.norm_layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.norm_layernorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
+    L.norm_layernorm_bwd_workspace_bytes_cfg.restype = ctypes.c_size_t
+    L.norm_select_config.argtypes = [ctypes.c_int, _i64, _i64, ctypes.c_int32, _cfgp]
+    L.norm_select_config.restype = ctypes.c_int
+    L.norm_list_configs.argtypes = [ctypes.c_int, _i64, _cfgp, ctypes.c_int32]
+    L.norm_list_configs.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().norm_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise NormError(status, f"{what}: {status_string(status)}")
+
+
+def _cfg_ptr(cfg):
+    if cfg is None:
+        return None
+    c = cfg.c() if isinstance(cfg, Cfg) else cfg
+    return ctypes.byref(c)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _mat(t: torch.Tensor, name: str, dtype=torch.bfloat16) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _rows_hidden(x: torch.Tensor):
+    if x.dim() < 1:
+        raise ValueError("x must have a hidden dimension")
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    return rows, hidden
+
+
+def _vec(t, hidden, name, dtype=torch.bfloat16):
+    _mat(t, name, dtype)
+    if t.numel() != hidden:
+        raise ValueError(f"{name} must hold hidden={hidden} elements")
+    return t
+
+
+def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, stream=None):
+    """residual <- bf16(x + residual) in place; returns (out, residual)."""
+    _mat(x, "x")
+    _mat(residual, "residual")
+    rows, hidden = _rows_hidden(x)
+    if residual.shape != x.shape:
+        raise ValueError("residual must have x's shape")
+    _vec(weight, hidden, "weight")
+    out = torch.empty_like(x) if out is None else _mat(out, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    _check(lib().norm_fused_add_rmsnorm_cfg(out.data_ptr(), residual.data_ptr(), x.data_ptr(),
+                                            weight.data_ptr(), rows, hidden, float(eps),
+                                            _cfg_ptr(cfg), _stream(stream)),
+           "norm_fused_add_rmsnorm")
+    return out, residual
+
+
+def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None):
+    _mat(x, "x")
+    rows, hidden = _rows_hidden(x)
+    _vec(weight, hidden, "weight")
+    out = torch.empty_like(x) if out is None else _mat(out, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    _check(lib().norm_rmsnorm_fwd_cfg(out.data_ptr(), x.data_ptr(), weight.data_ptr(), rows,
+                                      hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
+           "norm_rmsnorm_fwd")
+    return out
+
+
+def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
+                  with_stats: bool = True, cfg=None, stream=None):
+    """Returns (y, mean, rstd); mean/rstd are None when with_stats is False."""
+    _mat(x, "x")
+    rows, hidden = _rows_hidden(x)
+    _vec(weight, hidden, "weight")
+    _vec(bias, hidden, "bias")
+    y = torch.empty_like(x) if y is None else _mat(y, "y")
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    if with_stats:
+        mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+        _mat(mean, "mean", torch.float32)
+        _mat(rstd, "rstd", torch.float32)
+        if mean.numel() != rows or rstd.numel() != rows:
+            raise ValueError("mean/rstd must hold one value per row")
+        mp, rp = mean.data_ptr(), rstd.data_ptr()
+    else:
+        mean = rstd = None
+        mp = rp = None
+    _check(lib().norm_layernorm_fwd_cfg(y.data_ptr(), mp, rp, x.data_ptr(), weight.data_ptr(),
+                                        bias.data_ptr(), rows, hidden, float(eps),
+                                        _cfg_ptr(cfg), _stream(stream)),
+           "norm_layernorm_fwd")
+    return y, mean, rstd
+
+
+def workspace_bytes(rows: int, hidden: int, cfg=None) -> int:
+    if cfg is None:
+        return int(lib().norm_layernorm_bwd_workspace_bytes(rows, hidden))
+    return int(lib().norm_layernorm_bwd_workspace_bytes_cfg(rows, hidden, _cfg_ptr(cfg)))
+
+
+def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
+                  dbias=None, workspace=None, cfg=None, stream=None):
+    """Returns (dx, dweight, dbias).  ``workspace`` (uint8 device tensor) is
+    allocated when not given."""
+    _mat(dy, "dy")
+    _mat(x, "x")
+    rows, hidden = _rows_hidden(x)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    _mat(mean, "mean", torch.float32)
+    _mat(rstd, "rstd", torch.float32)
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must hold one value per row")
+    _vec(weight, hidden, "weight")
+    dx = torch.empty_like(x) if dx is None else _mat(dx, "dx")
+    dev = x.device
+    dweight = torch.empty(hidden, dtype=torch.float32, device=dev) if dweight is None else dweight
+    dbias = torch.empty(hidden, dtype=torch.float32, device=dev) if dbias is None else dbias
+    _vec(dweight, hidden, "dweight", torch.float32)
+    _vec(dbias, hidden, "dbias", torch.float32)
+    need = workspace_bytes(rows, hidden, cfg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _mat(workspace, "workspace", workspace.dtype)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().norm_layernorm_bwd_cfg(dx.data_ptr(), dweight.data_ptr(), dbias.data_ptr(),
+                                        dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
+                                        rstd.data_ptr(), weight.data_ptr(),
+                                        workspace.data_ptr(), ws_bytes, rows, hidden,
+                                        float(eps), _cfg_ptr(cfg), _stream(stream)),
+           "norm_layernorm_bwd")
+    return dx, dweight, dbias
+
+
+def select_config(op, rows: int, hidden: int, cu_count: int = 0) -> Cfg:
+    op = OPS.get(op, op)
+    c = LaunchCfg()
+    _check(lib().norm_select_config(int(op), rows, hidden, cu_count, ctypes.byref(c)),
+           "norm_select_config")
+    return Cfg(*c.astuple())
+
+
+def list_configs(op, hidden: int):
+    op = OPS.get(op, op)
+    n = lib().norm_list_configs(int(op), hidden, None, 0)
+    arr = (LaunchCfg * max(n, 1))()
+    lib().norm_list_configs(int(op), hidden, arr, n)
+    return [Cfg(*arr[i].astuple()) for i in range(n)]

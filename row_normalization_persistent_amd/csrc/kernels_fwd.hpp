@@ -1,0 +1,291 @@
+// Forward row-normalization kernels: fused residual-add + RMSNorm, RMSNorm,
+// LayerNorm.  One row per T lanes, R rows per workgroup; the whole row stays
+// in registers between the reduction and the normalize step, so every input
+// byte is read from HBM once and every output byte written once ("inner
+// persistent" normalization in "optimize inner persistent scheduler for
+// static fusion", author description).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace rownorm {
+
+// Sum of 8 per-element accumulators in a fixed tree.
+__device__ __forceinline__ float tree8(const float (&a)[8]) {
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// ---------------------------------------------------------------------------
+// Fused residual-add + RMSNorm ("optimize inner persistent scheduler for
+// static fusion", changes walkthrough: the benchmarked op updates its residual
+// input in place).  s = x + r in fp32; residual <- bf16(s);
+// out <- bf16(s * rsqrt(mean(s^2) + eps) * w), with s re-derived from the
+// x and r registers (the same fp32 sum) instead of re-read.
+// ---------------------------------------------------------------------------
+template <int H, int T, int R>
+__global__ __launch_bounds__(T * R) void fused_add_rmsnorm_kernel(
+    u32x4* out, u32x4* residual, const u32x4* x, const u32x4* __restrict__ weight,
+    int64_t rows, float eps) {
+    using S = Shape<H, T, R>;
+    constexpr int V = S::kVecs;
+    __shared__ float red[S::kWaves > 1 ? R * S::kWaves : 1];
+
+    const int lane = threadIdx.x % T;
+    const int rib = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + rib;
+    const bool valid = row < rows;
+    if constexpr (S::kWaves == 1) {
+        if (!valid) return;  // whole wave, no barrier follows
+    }
+    const int64_t base = row * S::kRowVecs + lane;
+
+    // Issue the whole row (x and r interleaved, in the order they are
+    // consumed), then the weight, before any arithmetic.
+    u32x4 xv[V], rv[V], wv[V];
+    if (valid) {
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            xv[b] = load_stream(x + base + b * T);
+            rv[b] = load_stream(residual + base + b * T);
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < V; ++b) xv[b] = rv[b] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = weight[lane + b * T];
+    issue_fence();
+
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8], rf[8], s[8];
+        unpack8(xv[b], xf);
+        unpack8(rv[b], rf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            s[k] = xf[k] + rf[k];
+            acc[k] += s[k] * s[k];
+        }
+        if (valid) store_stream(residual + base + b * T, pack8(s));
+    }
+    const float ss = row_sum<T>(tree8(acc), red + rib * S::kWaves, lane);
+    const float rstd = fast_rsqrt(ss * (1.0f / H) + eps);
+    if (!valid) return;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8], rf[8], wf[8], o[8];
+        unpack8(xv[b], xf);
+        unpack8(rv[b], rf);
+        unpack8(wv[b], wf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = (xf[k] + rf[k]) * rstd * wf[k];
+        store_stream(out + base + b * T, pack8(o));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm forward ("TMA inner persistent scheduler", description summary).
+// ---------------------------------------------------------------------------
+template <int H, int T, int R>
+__global__ __launch_bounds__(T * R) void rmsnorm_fwd_kernel(
+    u32x4* out, const u32x4* x, const u32x4* __restrict__ weight, int64_t rows, float eps) {
+    using S = Shape<H, T, R>;
+    constexpr int V = S::kVecs;
+    __shared__ float red[S::kWaves > 1 ? R * S::kWaves : 1];
+
+    const int lane = threadIdx.x % T;
+    const int rib = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + rib;
+    const bool valid = row < rows;
+    if constexpr (S::kWaves == 1) {
+        if (!valid) return;
+    }
+    const int64_t base = row * S::kRowVecs + lane;
+
+    u32x4 xv[V], wv[V];
+    if (valid) {
+#pragma unroll
+        for (int b = 0; b < V; ++b) xv[b] = load_stream(x + base + b * T);
+    } else {
+#pragma unroll
+        for (int b = 0; b < V; ++b) xv[b] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = weight[lane + b * T];
+    issue_fence();
+
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8];
+        unpack8(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += xf[k] * xf[k];
+    }
+    const float ss = row_sum<T>(tree8(acc), red + rib * S::kWaves, lane);
+    const float rstd = fast_rsqrt(ss * (1.0f / H) + eps);
+    if (!valid) return;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8], wf[8], o[8];
+        unpack8(xv[b], xf);
+        unpack8(wv[b], wf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = xf[k] * rstd * wf[k];
+        store_stream(out + base + b * T, pack8(o));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm forward with affine weight/bias ("TMA inner persistent
+// scheduler", description summary).  Two-pass statistics: the mean first,
+// then the sum of squared deviations from it, both over the row held in
+// registers (the second pass costs no memory traffic).
+// ---------------------------------------------------------------------------
+template <int H, int T, int R>
+__global__ __launch_bounds__(T * R) void layernorm_fwd_kernel(
+    u32x4* y, float* mean_out, float* rstd_out, const u32x4* x,
+    const u32x4* __restrict__ weight, const u32x4* __restrict__ bias, int64_t rows, float eps) {
+    using S = Shape<H, T, R>;
+    constexpr int V = S::kVecs;
+    constexpr int kSlot = S::kWaves > 1 ? R * S::kWaves : 1;
+    __shared__ float red[2 * kSlot];
+
+    const int lane = threadIdx.x % T;
+    const int rib = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + rib;
+    const bool valid = row < rows;
+    if constexpr (S::kWaves == 1) {
+        if (!valid) return;
+    }
+    const int64_t base = row * S::kRowVecs + lane;
+
+    u32x4 xv[V], wv[V], bv[V];
+    if (valid) {
+#pragma unroll
+        for (int b = 0; b < V; ++b) xv[b] = load_stream(x + base + b * T);
+    } else {
+#pragma unroll
+        for (int b = 0; b < V; ++b) xv[b] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = weight[lane + b * T];
+#pragma unroll
+    for (int b = 0; b < V; ++b) bv[b] = bias[lane + b * T];
+    issue_fence();
+
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8];
+        unpack8(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += xf[k];
+    }
+    const float mu = row_sum<T>(tree8(acc), red + rib * S::kWaves, lane) * (1.0f / H);
+
+    float acc2[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8];
+        unpack8(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float d = xf[k] - mu;
+            acc2[k] += d * d;
+        }
+    }
+    const float var = row_sum<T>(tree8(acc2), red + kSlot + rib * S::kWaves, lane) * (1.0f / H);
+    const float rstd = fast_rsqrt(var + eps);
+    if (!valid) return;
+    if (mean_out != nullptr && lane == 0) {
+        mean_out[row] = mu;
+        rstd_out[row] = rstd;
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[8], wf[8], bf[8], o[8];
+        unpack8(xv[b], xf);
+        unpack8(wv[b], wf);
+        unpack8(bv[b], bf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = (xf[k] - mu) * rstd * wf[k] + bf[k];
+        store_stream(y + base + b * T, pack8(o));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers and the compile-time shape lists.
+// ---------------------------------------------------------------------------
+struct OpFused {
+    static constexpr int kMaxVecs = 16;  // x and r held: 8 VGPRs per vector
+};
+struct OpRms {
+    static constexpr int kMaxVecs = 32;  // x held: 4 VGPRs per vector
+};
+struct OpLnFwd {
+    static constexpr int kMaxVecs = 32;
+};
+
+template <class Op, int H, int T, int R>
+constexpr bool shape_ok() {
+    return T % kWave == 0 && H % (8 * T) == 0 && H / (8 * T) <= Op::kMaxVecs &&
+           T * R <= 1024;
+}
+
+template <class Op, int H, int T, int R>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.rows + R - 1) / R));
+    const dim3 block(T * R);
+    if constexpr (std::is_same_v<Op, OpFused>) {
+        hipLaunchKernelGGL((fused_add_rmsnorm_kernel<H, T, R>), grid, block, 0, stream,
+                           (u32x4*)a.out, (u32x4*)a.residual, (const u32x4*)a.x,
+                           (const u32x4*)a.weight, a.rows, a.eps);
+    } else if constexpr (std::is_same_v<Op, OpRms>) {
+        hipLaunchKernelGGL((rmsnorm_fwd_kernel<H, T, R>), grid, block, 0, stream,
+                           (u32x4*)a.out, (const u32x4*)a.x, (const u32x4*)a.weight, a.rows,
+                           a.eps);
+    } else {
+        hipLaunchKernelGGL((layernorm_fwd_kernel<H, T, R>), grid, block, 0, stream,
+                           (u32x4*)a.out, a.mean, a.rstd, (const u32x4*)a.x,
+                           (const u32x4*)a.weight, (const u32x4*)a.bias, a.rows, a.eps);
+    }
+    return hipGetLastError();
+}
+
+// (lanes per row, rows per workgroup) pairs tried for every hidden size;
+// pairs that do not divide the row or exceed the register budget are skipped
+// at compile time.
+template <int T, int R>
+struct LR {};
+using FwdShapeList = std::tuple<LR<64, 1>, LR<64, 2>, LR<64, 4>, LR<64, 8>, LR<128, 1>,
+                                LR<128, 2>, LR<128, 4>, LR<256, 1>, LR<256, 2>, LR<512, 1>,
+                                LR<512, 2>, LR<1024, 1>>;
+
+template <class Op, int H, int T, int R>
+void add_fwd_entry(std::vector<FwdEntry>& v, LR<T, R>) {
+    if constexpr (shape_ok<Op, H, T, R>()) v.push_back({H, T, R, &launch_fwd<Op, H, T, R>});
+}
+
+template <class Op, int H, class... Ls>
+void add_fwd_entries_h(std::vector<FwdEntry>& v, std::tuple<Ls...>) {
+    (add_fwd_entry<Op, H>(v, Ls{}), ...);
+}
+
+template <class Op>
+std::vector<FwdEntry> build_fwd_table() {
+    std::vector<FwdEntry> v;
+    add_fwd_entries_h<Op, 1024>(v, FwdShapeList{});
+    add_fwd_entries_h<Op, 2048>(v, FwdShapeList{});
+    add_fwd_entries_h<Op, 4096>(v, FwdShapeList{});
+    add_fwd_entries_h<Op, 8192>(v, FwdShapeList{});
+    add_fwd_entries_h<Op, 12288>(v, FwdShapeList{});
+    add_fwd_entries_h<Op, 16384>(v, FwdShapeList{});
+    return v;
+}
+
+}  // namespace rownorm

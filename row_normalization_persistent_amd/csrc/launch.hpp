@@ -1,0 +1,71 @@
+// Host-side launch tables shared by the kernel translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+namespace rownorm {
+
+// Hidden sizes every operation is compiled for (the hidden size of a given
+// model is fixed, so it is a template constant: "optimize inner persistent
+// scheduler for static fusion", author description).
+constexpr int kHiddenSizes[] = {1024, 2048, 4096, 8192, 12288, 16384};
+
+struct FwdArgs {
+    void* out;             // fused/rms: out; layernorm: y
+    void* residual;        // fused only (in/out)
+    const void* x;
+    const void* weight;
+    const void* bias;      // layernorm only
+    float* mean;           // layernorm only (may be null together with rstd)
+    float* rstd;
+    int64_t rows;
+    float eps;
+};
+
+struct BwdArgs {
+    void* dx;
+    const void* dy;
+    const void* x;
+    const float* mean;
+    const float* rstd;
+    const void* weight;
+    float* workspace;      // [grid][2][hidden] fp32 partial column sums
+    float* dweight;
+    float* dbias;
+    int64_t rows;
+    int32_t grid;
+};
+
+using FwdLauncher = hipError_t (*)(const FwdArgs&, hipStream_t);
+using BwdLauncher = hipError_t (*)(const BwdArgs&, hipStream_t);
+
+struct FwdEntry {
+    int hidden, lanes, rows_per_block;
+    FwdLauncher launch;
+};
+
+struct BwdEntry {
+    int hidden, lanes;
+    BwdLauncher launch;
+};
+
+// Compiled shapes, one table per operation (defined in the kernel units).
+const std::vector<FwdEntry>& fused_add_rmsnorm_table();
+const std::vector<FwdEntry>& rmsnorm_fwd_table();
+const std::vector<FwdEntry>& layernorm_fwd_table();
+const std::vector<BwdEntry>& layernorm_bwd_table();
+
+// Column-reduce geometry of LayerNorm backward.
+constexpr int kColReduceThreads = 256;
+constexpr int kColReduceCols = 64;  // flat [2][hidden] columns per workgroup
+// Largest persistent grid for a hidden size: the workspace ([grid][2][hidden]
+// fp32) must stay addressable by one 32-bit buffer descriptor, with room for
+// the column reduce's range-checked reads one pass past the last slab.
+constexpr int64_t max_bwd_grid(int64_t hidden) {
+    return ((int64_t(1) << 31) - 1) / (8 * hidden) - 128;
+}
+
+}  // namespace rownorm

@@ -1,0 +1,108 @@
+"""Comparison rules between the HIP path and the oracle.
+
+* bf16 residual of the fused op: bit-exact (exactly one correct rounding of
+  x + r exists, and the oracle's exact sum rounded once equals the kernel's
+  fp32 sum rounded once for every finite input).
+* bf16 normalized outputs: |gpu - ref| <= 2 ulp_bf16(ref), ref the unrounded
+  fp64 oracle value; ulp_bf16(v) = 2^max(floor(log2|v|) - 7, -133).
+  For the outputs formed by cancellation (LayerNorm y, LayerNorm dx) a floor
+  of 2^-16 * M is added, M the magnitude of the terms that cancel (fp32 sums
+  over the row leave errors of order 2^-24 * sum|terms|; 2^-16 is 256x that
+  and is at most 1/256 bf16 ulp at scale M, so it only matters for outputs
+  cancelled far below the row's scale).
+* fp32 statistics (LayerNorm mean, rstd): |gpu - ref| <= 1e-6 + 1e-5 |ref|.
+* fp32 column sums (dweight, dbias): |gpu - ref| <= 1e-3 |ref| + 1e-3 sqrt(sum_i t_i^2),
+  t the summed terms (dy * xhat or dy): relative 1e-3, with the column's RMS
+  scale as the absolute floor for columns that cancel to near zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+FLOOR = 2.0 ** -16
+
+
+def bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def ulp_bf16(ref: np.ndarray) -> np.ndarray:
+    a = np.abs(ref)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, e, -126.0)
+    return np.exp2(np.maximum(e - 7.0, -133.0))
+
+
+def assert_bits_equal(got: np.ndarray, exp: np.ndarray, what: str):
+    got = np.asarray(got).view(np.uint16)
+    exp = np.asarray(exp).view(np.uint16)
+    assert got.shape == exp.shape, what
+    bad = got != exp
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} bits differ; first at "
+                             f"{tuple(idx)}: {hex(got[tuple(idx)])} vs {hex(exp[tuple(idx)])}")
+
+
+def assert_bf16_close(got_bits: np.ndarray, ref: np.ndarray, what: str, ulps: float = 2.0,
+                      floor_scale: np.ndarray | None = None) -> dict:
+    got = bits_to_f64(got_bits)
+    assert got.shape == ref.shape, what
+    err = np.abs(got - ref)
+    lim = ulps * ulp_bf16(ref)
+    if floor_scale is not None:
+        lim = lim + FLOOR * floor_scale
+    bad = ~(err <= lim)  # NaN in got fails
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside {ulps} bf16 ulp; "
+                             f"first at {idx}: got {got[idx]!r} ref {ref[idx]!r}")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        e = err / ulp_bf16(ref)
+    only_floor = 0
+    if floor_scale is not None:
+        only_floor = int((err > ulps * ulp_bf16(ref)).sum())
+    return {"max_err_ulp": float(np.nanmax(e)), "passed_only_by_floor": only_floor}
+
+
+def assert_f32_close(got: np.ndarray, ref: np.ndarray, what: str, rtol=1e-5, atol=1e-6):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    bad = ~(err <= atol + rtol * np.abs(ref))
+    if bad.any():
+        i = int(np.argwhere(bad.reshape(-1))[0][0])
+        raise AssertionError(f"{what}: {int(bad.sum())} outside rtol {rtol} atol {atol}; "
+                             f"first {i}: {got.reshape(-1)[i]!r} vs {ref.reshape(-1)[i]!r}")
+
+
+def assert_colsum_close(got: np.ndarray, ref: np.ndarray, terms_sq_sum: np.ndarray, what: str,
+                        rtol=1e-3):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    lim = rtol * np.abs(ref) + rtol * np.sqrt(terms_sq_sum)
+    bad = ~(err <= lim)
+    if bad.any():
+        j = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{what}: {int(bad.sum())} columns outside tolerance; first {j}: "
+                             f"{got[j]!r} vs {ref[j]!r} (limit {lim[j]!r})")
+
+
+def layernorm_y_scale(xd, mean, rstd, wd, bd):
+    """M for LayerNorm y: rstd * (|x - mu| + mean_j |x|) * |w| + |b|."""
+    mabs = np.abs(xd).mean(axis=1, keepdims=True)
+    return rstd[:, None] * (np.abs(xd - mean[:, None]) + mabs) * np.abs(wd) + np.abs(bd)
+
+
+def layernorm_dx_scale(xd, dyd, wd, mean, rstd):
+    """M for LayerNorm dx: q (|g| + |c1| + |xhat||c2| + mean|g| + |xhat| mean|g xhat|)."""
+    xhat = (xd - mean[:, None]) * rstd[:, None]
+    g = dyd * wd
+    c1 = g.mean(axis=1, keepdims=True)
+    gx = g * xhat
+    c2 = gx.mean(axis=1, keepdims=True)
+    return rstd[:, None] * (np.abs(g) + np.abs(c1) + np.abs(xhat) * np.abs(c2)
+                            + np.abs(g).mean(axis=1, keepdims=True)
+                            + np.abs(xhat) * np.abs(gx).mean(axis=1, keepdims=True))

@@ -1,0 +1,207 @@
+"""The C-ABI library on the host (no GPU): it loads, exports exactly what
+include/norm.h declares, and its host logic (launch-shape tables, workspace
+sizing, argument validation) behaves as documented.  Every call here returns
+before the library makes any HIP call; no kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import row_normalization_persistent_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "norm.h")
+
+SUCCESS, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"NORM_API\s+[\w\s\*]+?\b(norm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
+               "norm_layernorm_bwd"):
+        assert op in names
+    assert len(names) == 13
+
+
+def test_library_exports_every_declared_symbol():
+    L = rn.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared_functions(), "library exports more or less than the header"
+
+
+def test_library_targets_gfx950_only():
+    blob = open(rn.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[a-z+-]*gfx[0-9a-z]+", blob))
+    assert targets == {b"amdgcn-amd-amdhsa--gfx950"}, targets
+
+
+def test_status_strings():
+    for code, name in rn.STATUS.items():
+        assert rn.status_string(code).startswith(name)
+    assert rn.status_string(99) == "unknown norm_status"
+
+
+def test_compiled_shapes_cover_every_hidden_size():
+    for op in rn.OPS:
+        for h in rn.HIDDEN_SIZES:
+            cfgs = rn.list_configs(op, h)
+            assert cfgs, (op, h)
+            for c in cfgs:
+                assert c.threads_per_row % 64 == 0
+                assert h % (8 * c.threads_per_row) == 0
+                assert c.threads_per_row * c.rows_per_block <= 1024
+        assert rn.list_configs(op, 3000) == []
+
+
+def test_select_config_small_batches_spread_rows_over_more_lanes():
+    big = rn.select_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
+    small = rn.select_config("fused_add_rmsnorm", 1, 4096, cu_count=256)
+    assert big.threads_per_row == 64
+    assert small.threads_per_row > big.threads_per_row
+    prev = 1 << 30
+    for rows in (1, 4, 16, 64, 256, 1024, 4096):  # non-increasing lanes per row
+        c = rn.select_config("fused_add_rmsnorm", rows, 4096, cu_count=256)
+        assert c in rn.list_configs("fused_add_rmsnorm", 4096)
+        assert c.threads_per_row <= prev
+        prev = c.threads_per_row
+    for op in ("rmsnorm_fwd", "layernorm_fwd"):
+        for h in rn.HIDDEN_SIZES:
+            for rows in (1, 64, 2048, 8192):
+                assert rn.select_config(op, rows, h, cu_count=256) in rn.list_configs(op, h)
+    for h in rn.HIDDEN_SIZES:
+        c = rn.select_config("layernorm_bwd", 8192, h)
+        assert rn.Cfg(c.threads_per_row, 1, 0) in rn.list_configs("layernorm_bwd", h)
+        assert c.grid > 0
+
+
+def test_workspace_bytes():
+    for h in rn.HIDDEN_SIZES:
+        c = rn.select_config("layernorm_bwd", 8192, h)
+        assert rn.workspace_bytes(8192, h) == c.grid * 2 * h * 4
+        assert rn.workspace_bytes(3, h) == 3 * 2 * h * 4  # never more slabs than rows
+        assert rn.workspace_bytes(0, h) == 0
+        assert rn.workspace_bytes(100, h, rn.Cfg(256, 1, 7)) == 7 * 2 * h * 4
+    assert rn.workspace_bytes(10, 1000) == 0
+    assert rn.workspace_bytes(-1, 4096) == 0
+
+
+# ---- argument validation (fake device addresses; nothing is dereferenced)
+A = 1 << 32  # a 16-byte aligned fake address
+MB = 1 << 24
+
+
+def fused(out=A, res=A + MB, x=A + 2 * MB, w=A + 3 * MB, rows=4, hidden=4096, eps=1e-6, cfg=None):
+    return rn.lib().norm_fused_add_rmsnorm_cfg(out, res, x, w, rows, hidden, eps, cfg, None)
+
+
+def test_fused_validation():
+    assert fused(rows=0) == SUCCESS  # nothing to do, no launch
+    assert fused(rows=-1) == INVALID
+    assert fused(eps=float("nan")) == INVALID
+    assert fused(eps=float("inf")) == INVALID
+    assert fused(eps=-1e-6) == INVALID
+    assert fused(hidden=4000) == UNSUPPORTED
+    assert fused(hidden=0) == UNSUPPORTED
+    assert fused(out=0) == INVALID
+    assert fused(res=0) == INVALID
+    assert fused(x=0) == INVALID
+    assert fused(w=0) == INVALID
+    assert fused(x=A + 2 * MB + 8) == MISALIGNED
+    assert fused(res=A + MB + 2) == MISALIGNED
+    assert fused(w=A + 3 * MB + 4) == MISALIGNED
+    assert fused(res=A + 2 * MB) == INVALID   # residual may alias nothing
+    assert fused(out=A + MB) == INVALID       # out == residual
+    assert fused(out=A + 2 * MB + 64) == INVALID  # partial overlap with x
+    assert fused(w=A + 16) == INVALID         # weight inside out
+    bad = rn.LaunchCfg(96, 1, 0)
+    assert fused(cfg=ctypes.byref(bad)) == INVALID  # not a compiled shape
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 4, 3))) == INVALID  # grid is bwd-only
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(0, 1, 0))) == INVALID
+
+
+def rms(out=A, x=A + MB, w=A + 2 * MB, rows=4, hidden=2048, eps=1e-6):
+    return rn.lib().norm_rmsnorm_fwd_cfg(out, x, w, rows, hidden, eps, None, None)
+
+
+def test_rmsnorm_validation():
+    assert rms(rows=0) == SUCCESS
+    assert rms(hidden=2049) == UNSUPPORTED
+    assert rms(out=0) == INVALID
+    assert rms(out=A + 8) == MISALIGNED
+    assert rms(out=A + MB + 16) == INVALID  # partial overlap with x
+    assert rms(w=A + 32) == INVALID
+
+
+def lnf(y=A, mean=A + MB, rstd=A + MB + 65536, x=A + 2 * MB, w=A + 3 * MB, b=A + 3 * MB + 65536,
+        rows=4, hidden=1024, eps=1e-5):
+    return rn.lib().norm_layernorm_fwd_cfg(y, mean, rstd, x, w, b, rows, hidden, eps, None, None)
+
+
+def test_layernorm_fwd_validation():
+    assert lnf(rows=0) == SUCCESS
+    assert lnf(eps=-1.0) == INVALID
+    assert lnf(hidden=1000) == UNSUPPORTED
+    assert lnf(b=0) == INVALID
+    assert lnf(mean=0) == INVALID   # mean and rstd are both given or both null
+    assert lnf(rstd=0) == INVALID
+    assert lnf(mean=A + MB + 2) == MISALIGNED
+    assert lnf(b=A + 3 * MB + 65536 + 8) == MISALIGNED
+    assert lnf(mean=A + MB, rstd=A + MB + 8) == INVALID  # mean/rstd overlap
+
+
+GB = 1 << 30
+
+
+def lnb(dx=A, dw=A + GB, db=A + GB + 65536, dy=A + 2 * GB, x=A + 3 * GB, mean=A + 4 * GB,
+        rstd=A + 4 * GB + 65536, w=A + 5 * GB, ws=A + 6 * GB, ws_bytes=None, rows=8192,
+        hidden=4096, eps=1e-5, cfg=None):
+    if ws_bytes is None:
+        ws_bytes = rn.workspace_bytes(rows, hidden) - 4
+    return rn.lib().norm_layernorm_bwd_cfg(dx, dw, db, dy, x, mean, rstd, w, ws, ws_bytes, rows,
+                                           hidden, eps, cfg, None)
+
+
+def test_layernorm_bwd_validation():
+    # all checks pass except the workspace size: proves the order of checks
+    assert lnb() == WORKSPACE
+    assert lnb(rows=-2) == INVALID
+    assert lnb(eps=float("nan")) == INVALID
+    assert lnb(hidden=5000) == UNSUPPORTED
+    assert lnb(dw=0) == INVALID
+    assert lnb(ws=0) == INVALID
+    assert lnb(dy=0) == INVALID
+    assert lnb(mean=0) == INVALID
+    assert lnb(dx=A + 4) == MISALIGNED
+    assert lnb(mean=A + 4 * GB + 2) == MISALIGNED
+    assert lnb(ws=A + 6 * GB + 4) == MISALIGNED
+    assert lnb(db=A + GB + 4 * 4096 - 8) == INVALID  # dweight overlaps dbias
+    assert lnb(dx=A + 2 * GB) == WORKSPACE           # dx == dy is allowed
+    assert lnb(dx=A + 2 * GB + 16) == INVALID        # partial overlap
+    assert lnb(ws=A + 3 * GB) == INVALID             # workspace over x
+    assert lnb(cfg=ctypes.byref(rn.LaunchCfg(96, 1, 0))) == INVALID
+    assert lnb(cfg=ctypes.byref(rn.LaunchCfg(256, 2, 0))) == INVALID
+    assert lnb(cfg=ctypes.byref(rn.LaunchCfg(256, 1, -1))) == INVALID
+    small = rn.LaunchCfg(256, 1, 4)
+    assert lnb(cfg=ctypes.byref(small), ws_bytes=4 * 2 * 4096 * 4 - 1) == WORKSPACE
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(4, 4096, dtype=torch.bfloat16)
+    w = torch.zeros(4096, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # host tensors are refused before any call
+        rn.fused_add_rmsnorm(x, x.clone(), w, 1e-6)
+    with pytest.raises(TypeError):
+        rn.rmsnorm_fwd(x.float(), w, 1e-6)
