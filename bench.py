@@ -15,9 +15,13 @@ cost does not pace the GPU.
 
 Also reported, on the same line:
   roofline      the dominant kernel (the kernel instantiation with the most
-                GPU time in a step), timed with HIP events on its own stream
-                over a second timed pass of the same launches
-  sweep         per-rows achieved GB/s, % of the 8 TB/s peak, rows/s
+                GPU time in a step): its launches of a step over every buffer
+                set, captured in one graph and replayed for about K steps
+                between two HIP events on the launch stream; achieved =
+                algorithmic bytes per launch / average launch time
+  kernels       the same for every instantiation the sweep uses
+  sweep         per-rows GB/s, % of the 8 TB/s peak, rows/s (eager launches,
+                an event pair around each, so dispatch overhead is included)
   other_ops     RMSNorm / LayerNorm forward / LayerNorm backward at their
                 largest workload, GB/s by the same rule
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
@@ -53,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-ops", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="turn rocprofv3 CSV output under DIR/{stats,fetch,write} into the "
+                         "summaries under profiles/ and exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -62,6 +69,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels are "
               "single-GPU and rows shard across GPUs with no communication.", file=sys.stderr)
@@ -144,7 +154,64 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s over the sweep")
 
-    # ---- second timed pass: every launch bracketed by events on its stream
+    # ---- per kernel instantiation: graphs holding only that instantiation's
+    # launches of a step (one graph per buffer set, same row mix as the step),
+    # timed with one event pair per replay on the launch stream; the dominant
+    # kernel is the instantiation with the most GPU time per step
+    groups = {}
+    for i, c in enumerate(cfgs):
+        key = (c.threads_per_row, c.rows_per_block)
+        g = groups.setdefault(key, {"idx": [], "bytes": 0})
+        g["idx"].append(i)
+        g["bytes"] += fused_bytes(SWEEP_ROWS[i])
+    for key, g in groups.items():
+        # one graph walks the instantiation's launches over all buffer sets in
+        # turn, so each replay is N_SETS steps' worth and the per-replay launch
+        # cost is spread over N_SETS * len(idx) kernels
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            cg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cg, stream=stream):
+                for k in range(N_SETS):
+                    for i in g["idx"]:
+                        launch(sets[k], i)
+            cg.replay()
+        reps = max(1, args.steps // N_SETS)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                cg.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        g["us_per_step"] = e0.elapsed_time(e1) * 1e3 / (reps * N_SETS)
+        g["avg_launch_us"] = g["us_per_step"] / len(g["idx"])
+        g["avg_bytes"] = g["bytes"] / len(g["idx"])
+        g["GBps"] = g["avg_bytes"] / (g["avg_launch_us"] * 1e-6) / 1e9
+        del cg
+    dom_key = max(groups, key=lambda k: groups[k]["us_per_step"])
+    dom = groups[dom_key]
+    achieved = dom["GBps"]
+    kname = f"fused_add_rmsnorm_kernel<{HIDDEN}, {dom_key[0]}, {dom_key[1]}>"
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(kname),
+                "kernel": kname, "launches_per_step": len(dom["idx"]),
+                "rows_per_launch": [SWEEP_ROWS[i] for i in dom["idx"]],
+                "algorithmic_bytes_per_launch": round(dom["avg_bytes"]),
+                "avg_launch_us": round(dom["avg_launch_us"], 3)}
+    log(f"dominant kernel {kname}: {dom['avg_launch_us']:.2f} us/launch avg, {achieved:.0f} GB/s")
+    kernels = [{"kernel": f"fused_add_rmsnorm_kernel<{HIDDEN}, {k[0]}, {k[1]}>",
+                "rows": [SWEEP_ROWS[i] for i in g["idx"]],
+                "us_per_step": round(g["us_per_step"], 3),
+                "avg_launch_us": round(g["avg_launch_us"], 3), "GBps": round(g["GBps"], 1)}
+               for k, g in groups.items()]
+
+    # ---- per-rows table: eager launches, each bracketed by events on the
+    # launch stream (the event pair adds ~1-2 us of dispatch overhead, which
+    # dominates the smallest batches)
     n_launch = len(SWEEP_ROWS)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_launch)] for _ in range(args.steps)]
@@ -158,7 +225,6 @@ def main():
                 evs[k][i][1].record(stream)
     torch.cuda.synchronize()
     dur_us = np.array([[a.elapsed_time(b) * 1e3 for a, b in row] for row in evs])  # [K, 14]
-
     sweep = []
     for i, rows in enumerate(SWEEP_ROWS):
         med = float(np.median(dur_us[:, i]))
@@ -170,29 +236,6 @@ def main():
                       "rows_per_s": round(rows / (med * 1e-6)),
                       "cfg": [cfgs[i].threads_per_row, cfgs[i].rows_per_block]})
         log(f"  rows {rows:5d}: {med:8.2f} us  {gbps:7.0f} GB/s  cfg {cfgs[i]}")
-
-    # dominant kernel: the instantiation with the most GPU time per step
-    groups = {}
-    for i, c in enumerate(cfgs):
-        key = (c.threads_per_row, c.rows_per_block)
-        g = groups.setdefault(key, {"idx": [], "bytes": 0})
-        g["idx"].append(i)
-        g["bytes"] += fused_bytes(SWEEP_ROWS[i])
-    dom_key = max(groups, key=lambda k: dur_us[:, groups[k]["idx"]].sum())
-    dom = groups[dom_key]
-    n_dom = len(dom["idx"])
-    avg_dur = float(dur_us[:, dom["idx"]].sum() / (args.steps * n_dom))
-    avg_bytes = dom["bytes"] / n_dom
-    achieved = avg_bytes / (avg_dur * 1e-6) / 1e9
-    kname = f"fused_add_rmsnorm_kernel<{HIDDEN}, {dom_key[0]}, {dom_key[1]}>"
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic(kname, avg_bytes),
-                "kernel": kname, "launches_per_step": n_dom,
-                "rows_per_launch": [SWEEP_ROWS[i] for i in dom["idx"]],
-                "algorithmic_bytes_per_launch": round(avg_bytes),
-                "avg_launch_us": round(avg_dur, 3)}
-    log(f"dominant kernel {kname}: {avg_dur:.2f} us/launch avg, {achieved:.0f} GB/s")
 
     result = {
         "metric": "achieved HBM GB/s (% of peak) for fused add+RMSNorm, hidden 4096, rows 1-8192",
@@ -215,7 +258,10 @@ def main():
                    "launch": "hip graph replay" if graphs is not None else "eager",
                    "buffer_sets": N_SETS},
         "roofline": roofline,
+        "kernels": kernels,
         "sweep": sweep,
+        "sweep_note": "eager launches with an event pair around each; includes dispatch "
+                      "overhead, so small batches read low",
     }
 
     if not args.no_other_ops:
@@ -226,9 +272,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def load_traffic(kernel: str, alg_bytes: float):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
-    scaled by the copy-kernel calibration; None when absent or stale."""
+def load_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (profiles/traffic.json, written by
+    `bench.py --summarize-pmc`), or None when absent or taken from a different
+    kernel source."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -237,9 +285,9 @@ def load_traffic(kernel: str, alg_bytes: float):
         entry = t["kernels"][kernel]
     except (KeyError, ValueError):
         return None
-    if entry.get("source_sha256") != kernel_source_digest():
+    if t.get("kernel_source_sha256") != kernel_source_digest():
         return None
-    return round(entry["bytes_per_launch"])
+    return round(entry["hbm_bytes_per_launch"])
 
 
 def kernel_source_digest() -> str:
@@ -247,7 +295,7 @@ def kernel_source_digest() -> str:
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "row_normalization_persistent_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("device_common.hpp", "kernels_fwd.hpp"):
+    for name in ("device_common.hpp", "kernels_fwd.hpp", "api.hip"):
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
@@ -376,6 +424,148 @@ def cpu_baseline(inp, seconds):
             "kind": "oracle",
             "sample": f"{reps} pass(es) of the full rows 1..8192 sweep at hidden 4096 "
                       f"({reps * sum(SWEEP_ROWS)} rows) in {t:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/)
+# ---------------------------------------------------------------------------
+PROFILE_COMMANDS = [
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $DIR/stats -o bench -- "
+    "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $DIR/fetch -o bench -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $DIR/write -o bench -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --summarize-profiles $DIR",
+]
+CALIBRATION_BYTES = 1 << 30  # the 1 GiB device copy of the copy_ceiling pass
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").replace("rownorm::", "")
+
+
+def _tpl(name: str):
+    return [int(v) for v in name.split("<")[1].split(">")[0].split(",")]
+
+
+def _rows_of(name: str, grid: int):
+    """Rows processed by a dispatch of one of our kernels (grid in work-items)."""
+    short = _short(name)
+    if short.startswith(("fused_add_rmsnorm_kernel", "rmsnorm_fwd_kernel", "layernorm_fwd_kernel")):
+        return grid // _tpl(short)[1]
+    return None
+
+
+def _alg_bytes(name: str, rows):
+    short = _short(name)
+    if rows is None:
+        return None
+    h = _tpl(short)[0]
+    if short.startswith("fused_add_rmsnorm_kernel"):
+        return fused_bytes(rows, h)
+    if short.startswith("rmsnorm_fwd_kernel"):
+        return 4 * h * rows + 2 * h
+    if short.startswith("layernorm_fwd_kernel"):
+        return (4 * h + 8) * rows + 4 * h
+    return None
+
+
+def summarize_profiles(d: str):
+    import csv
+    import collections
+
+    os.makedirs(PROFILES, exist_ok=True)
+    cmds = "\n".join("    " + c for c in PROFILE_COMMANDS)
+
+    # -- kernel trace statistics
+    stats = list(csv.DictReader(open(os.path.join(d, "stats", "bench_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, "stats", "bench_kernel_trace.csv"))))
+    per = collections.defaultdict(list)
+    for r in trace:
+        rows = _rows_of(r["Kernel_Name"], int(r["Grid_Size_X"]))
+        per[(_short(r["Kernel_Name"]), rows)].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel durations: fused residual-add + RMSNorm, hidden 4096, rows 1-8192 sweep",
+             "", "Produced on one MI355X (gfx950, 256 CUs) by:", "", cmds, "",
+             "`bench.py` runs the sweep from HIP graphs, then the per-instantiation graph pass "
+             "behind `roofline`, the eager per-rows pass, the other operations and the "
+             "1 GiB copy.  `--stats` summary (all dispatches of the command):", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", "Median duration per launch size (kernel trace):", "",
+              "| kernel | rows | launches | median us | GB/s (algorithmic) |",
+              "|---|---:|---:|---:|---:|"]
+    for (k, rows), v in sorted(per.items(), key=lambda kv: (kv[0][0], kv[0][1] or 0)):
+        if rows is None:
+            continue
+        med = float(np.median(v))
+        gbps = _alg_bytes(k, rows) / (med * 1e-6) / 1e9
+        lines.append(f"| `{k}` | {rows} | {len(v)} | {med:.2f} | {gbps:.0f} |")
+    lines += ["", "Launches chained in one HIP graph start as soon as their predecessor ends, "
+              "so under the tracer a small launch's interval also covers the dependency wait; "
+              "the large launches' intervals are their execution time."]
+    open(os.path.join(PROFILES, "fused_add_rmsnorm_h4096_sweep_kernel_stats.md"), "w").write(
+        "\n".join(lines) + "\n")
+
+    # -- HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
+    def counters(sub):
+        out = collections.defaultdict(list)
+        calib = []
+        for r in csv.DictReader(open(os.path.join(d, sub, "bench_counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            val = float(r["Counter_Value"]) * 1024.0
+            if "copyBuffer" in name:
+                calib.append(val)
+            rows = _rows_of(name, int(r["Grid_Size"]))
+            out[(_short(name), rows)].append(val)
+        return out, max(calib)
+    fetch, f_cal = counters("fetch")
+    write, w_cal = counters("write")
+    f_scale = CALIBRATION_BYTES / f_cal
+    w_scale = CALIBRATION_BYTES / w_cal
+    lines = ["# HBM traffic per launch: FETCH_SIZE and WRITE_SIZE, calibrated", "",
+             "Produced on one MI355X (gfx950) by:", "", cmds, "",
+             f"Calibration: the 1 GiB device-to-device copy in `bench.py` (1 GiB read, 1 GiB "
+             f"written) reads FETCH_SIZE = {f_cal / 2**20:.1f} MiB and WRITE_SIZE = "
+             f"{w_cal / 2**20:.1f} MiB, so FETCH_SIZE is scaled by {f_scale:.4f} and "
+             f"WRITE_SIZE by {w_scale:.4f}.", "",
+             "| kernel | rows | dispatches | read MiB (scaled) | written MiB (scaled) | "
+             "algorithmic MiB | HBM / algorithmic |", "|---|---:|---:|---:|---:|---:|---:|"]
+    kernels = {}
+    groups = collections.defaultdict(lambda: {"hbm": [], "alg": [], "rows": []})
+    for key in sorted(set(fetch) & set(write), key=lambda k: (k[0], k[1] or 0)):
+        k, rows = key
+        if not k.startswith(("fused_add", "rmsnorm", "layernorm")):
+            continue
+        rd = float(np.mean(fetch[key])) * f_scale
+        wr = float(np.mean(write[key])) * w_scale
+        alg = _alg_bytes(k, rows)
+        ratio = f"{(rd + wr) / alg:.4f}" if alg else "-"
+        algs = f"{alg / 2**20:.2f}" if alg else "-"
+        lines.append(f"| `{k}` | {rows if rows is not None else '-'} | {len(fetch[key])} | "
+                     f"{rd / 2**20:.2f} | {wr / 2**20:.2f} | {algs} | {ratio} |")
+        if alg:
+            n = min(len(fetch[key]), len(write[key]))
+            groups[k]["hbm"] += [rd + wr] * n
+            groups[k]["alg"] += [alg] * n
+            groups[k]["rows"].append(rows)
+    for k, g in groups.items():
+        kernels[k] = {"hbm_bytes_per_launch": float(np.mean(g["hbm"])),
+                      "algorithmic_bytes_per_launch": float(np.mean(g["alg"])),
+                      "rows": sorted(g["rows"])}
+    lines += ["", "Per-launch averages over each kernel's dispatches (the mix of row counts "
+              "the sweep gives it) are in `profiles/traffic.json`, which `bench.py` reports as "
+              "`roofline.traffic` while the kernel sources are unchanged."]
+    open(os.path.join(PROFILES, "fused_add_rmsnorm_h4096_sweep_hbm_traffic.md"), "w").write(
+        "\n".join(lines) + "\n")
+    json.dump({"kernel_source_sha256": kernel_source_digest(),
+               "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels},
+              open(os.path.join(PROFILES, "traffic.json"), "w"), indent=1)
+    print(f"wrote summaries to {PROFILES}")
 
 
 if __name__ == "__main__":

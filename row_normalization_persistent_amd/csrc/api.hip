@@ -93,13 +93,17 @@ const BwdEntry* find_bwd(int64_t hidden, int lanes) {
 }
 
 // ---- launch-shape choice ----------------------------------------------------
-// Forward ops: with enough rows for every SIMD of every CU to own a row per
-// wave, one row per wave (4 waves per workgroup) keeps each row's reduction
-// inside one wave (no LDS, no barrier).  With fewer rows, each row is spread
-// over more lanes (the small-batch rule of "optimize inner persistent
-// scheduler for static fusion", author description), so the machine still
-// issues enough parallel 16-byte loads; beyond 64 lanes the row's waves meet
-// in LDS.
+// Forward ops, chosen from steady-state measurements on MI355X (graph-replayed
+// launches over cold buffers):
+//  * Small batches: when rows alone cannot give every SIMD of every CU a wave,
+//    each row is spread over more lanes (the small-batch rule of "optimize
+//    inner persistent scheduler for static fusion", author description), so
+//    the machine still issues enough parallel 16-byte loads; beyond 64 lanes
+//    the row's waves meet in LDS.
+//  * Large batches: a lane holds at most 8 16-byte vectors of the row (wider
+//    per-lane buffers plus the weight/bias vectors cost occupancy), and from
+//    4096 rows up the RMS kernels run best at 4 vectors per lane.
+//  * Rows per workgroup: 4 for one-wave rows, 2 for two-wave rows, else 1.
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     const int64_t target_waves = 4 * (int64_t)cu;
     auto valid = [&](int l) {
@@ -107,10 +111,9 @@ norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
             if (e.hidden == hidden && e.lanes == l) return true;
         return false;
     };
-    // at most 8 16-byte vectors of the row per lane: wider per-lane buffers
-    // (plus the weight/bias vectors) cost occupancy and ran slower
+    const int max_vecs = (op != NORM_OP_LAYERNORM_FWD && rows >= 16 * (int64_t)cu) ? 4 : 8;
     int lanes = 64;
-    while (lanes < 1024 && (hidden / (8 * lanes) > 8 || !valid(lanes))) lanes *= 2;
+    while (lanes < 1024 && (hidden / (8 * lanes) > max_vecs || !valid(lanes))) lanes *= 2;
     while (lanes < 1024 && rows * (lanes / 64) < target_waves && valid(lanes * 2)) lanes *= 2;
     int rpb = lanes == 64 ? 4 : (lanes == 128 ? 2 : 1);
     while (rpb > 1 && !find_fwd(op, hidden, lanes, rpb)) rpb /= 2;

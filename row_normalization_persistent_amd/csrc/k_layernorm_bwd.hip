@@ -153,16 +153,17 @@ __global__ __launch_bounds__(T) void layernorm_bwd_rows_kernel(
 // Column reduce.  A workgroup owns kColReduceCols = 64 consecutive columns of
 // the flat [2][H] slab (dweight columns, then dbias columns); its 256 lanes
 // form 16 column groups of 4 columns x 16 slab streams.  Stream s adds the
-// slabs s, s + 16, s + 32, ... (eight independent loads in flight per pass;
-// slabs past the last are range-checked to zero by the workspace
-// descriptor), then the 16 stream sums of each column are added in stream
-// order.  The summation order is fixed, so the result is bit-reproducible.
+// slabs s, s + 16, s + 32, ... (16 independent loads in flight per pass, so
+// the default 256 slabs take one memory round trip; slabs past the last are
+// range-checked to zero by the workspace descriptor), then the 16 stream sums
+// of each column are added in stream order.  The summation order is fixed,
+// so the result is bit-reproducible.
 __global__ __launch_bounds__(kColReduceThreads) void layernorm_bwd_colreduce_kernel(
     const float* __restrict__ workspace, int32_t grid_slabs, int32_t hidden,
     float* __restrict__ dweight, float* __restrict__ dbias) {
     constexpr int kGroups = kColReduceCols / 4;                // 16 groups of 4 columns
     constexpr int kStreams = kColReduceThreads / kGroups;      // 16 slab streams
-    constexpr int kUnroll = 8;
+    constexpr int kUnroll = 16;
     const int cg = threadIdx.x % kGroups;
     const int stream = threadIdx.x / kGroups;
     const int flat = blockIdx.x * kColReduceCols + cg * 4;     // < 2 * hidden

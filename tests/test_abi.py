@@ -66,24 +66,29 @@ def test_compiled_shapes_cover_every_hidden_size():
 
 
 def test_select_config_small_batches_spread_rows_over_more_lanes():
-    big = rn.select_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
+    # the small-batch rule: fewer rows -> more lanes per row, never fewer
     small = rn.select_config("fused_add_rmsnorm", 1, 4096, cu_count=256)
-    assert big.threads_per_row == 64
-    assert small.threads_per_row > big.threads_per_row
+    mid = rn.select_config("fused_add_rmsnorm", 1024, 4096, cu_count=256)
+    assert small.threads_per_row > mid.threads_per_row == 64
     prev = 1 << 30
-    for rows in (1, 4, 16, 64, 256, 1024, 4096):  # non-increasing lanes per row
+    for rows in (1, 4, 16, 64, 256, 512, 1024, 2048):
         c = rn.select_config("fused_add_rmsnorm", rows, 4096, cu_count=256)
-        assert c in rn.list_configs("fused_add_rmsnorm", 4096)
         assert c.threads_per_row <= prev
         prev = c.threads_per_row
-    for op in ("rmsnorm_fwd", "layernorm_fwd"):
+    # fewer CUs fill up with fewer rows
+    assert (rn.select_config("fused_add_rmsnorm", 256, 4096, cu_count=64).threads_per_row
+            <= rn.select_config("fused_add_rmsnorm", 256, 4096, cu_count=256).threads_per_row)
+    for op in ("fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"):
         for h in rn.HIDDEN_SIZES:
-            for rows in (1, 64, 2048, 8192):
-                assert rn.select_config(op, rows, h, cu_count=256) in rn.list_configs(op, h)
+            for rows in (1, 64, 1024, 2048, 4096, 8192, 1 << 20):
+                c = rn.select_config(op, rows, h, cu_count=256)
+                assert c in rn.list_configs(op, h), (op, h, rows, c)
+                assert h // (8 * c.threads_per_row) <= 8  # at most 8 vectors per lane
     for h in rn.HIDDEN_SIZES:
         c = rn.select_config("layernorm_bwd", 8192, h)
         assert rn.Cfg(c.threads_per_row, 1, 0) in rn.list_configs("layernorm_bwd", h)
-        assert c.grid > 0
+        assert c.grid == 256
+        assert rn.select_config("layernorm_bwd", 5, h).grid == 5
 
 
 def test_workspace_bytes():
