@@ -9,9 +9,9 @@ once per launch) divided by the step's wall time.
 
 Steps rotate over several independent buffer sets whose total footprint is far
 beyond the 256 MB Infinity Cache plus the 8 x 4 MB L2, so every step reads its
-inputs from HBM (nothing is re-read warm).  Launches are replayed from one HIP
-graph per buffer set (captured once, before timing), so the host's per-launch
-cost does not pace the GPU.
+inputs from HBM (nothing is re-read warm).  Launches are replayed from HIP
+graphs captured before timing (one per cycle of the buffer sets, i.e. three
+steps), so the host's per-launch cost does not pace the GPU.
 
 Also reported, on the same line:
   roofline      the dominant kernel (the kernel instantiation with the most
@@ -23,7 +23,8 @@ Also reported, on the same line:
   sweep         per-rows GB/s, % of the 8 TB/s peak, rows/s (eager launches,
                 an event pair around each, so dispatch overhead is included)
   other_ops     RMSNorm / LayerNorm forward / LayerNorm backward at their
-                largest workload, GB/s by the same rule
+                largest workload: one graph of back-to-back launches over
+                >= 1.2 GB of buffer sets (cold reads), time per launch
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="turn rocprofv3 CSV output under DIR/{stats,fetch,write} into the "
                          "summaries under profiles/ and exit (no GPU needed)")
+    ap.add_argument("--profiles-out", metavar="DIR", default=PROFILES,
+                    help="where --summarize-profiles writes (default: profiles/)")
     return ap.parse_args()
 
 
@@ -70,7 +73,7 @@ def log(msg):
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.profiles_out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels are "
@@ -122,7 +125,12 @@ def main():
         for i in range(len(SWEEP_ROWS)):
             launch(s, i)
 
-    graphs = None
+    # One graph per buffer set (one step each) and one graph for a whole
+    # cycle of N_SETS steps (sets 0, 1, 2 in turn): K steps run as K // N_SETS
+    # cycle replays plus K % N_SETS single-step replays, so the per-replay
+    # submission cost is spread over N_SETS steps, as when a whole model pass
+    # is captured in one graph.
+    graphs = cycle = None
     if not args.no_graph:
         graphs = []
         torch.cuda.synchronize()
@@ -132,22 +140,29 @@ def main():
                 with torch.cuda.graph(g, stream=stream):
                     step_eager(k)
                 graphs.append(g)
+            cycle = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cycle, stream=stream):
+                for k in range(N_SETS):
+                    step_eager(k)
         torch.cuda.synchronize()
 
-    def step(k):
-        if graphs is not None:
-            with torch.cuda.stream(stream):
-                graphs[k % N_SETS].replay()
-        else:
-            step_eager(k)
+    def run_steps(n):
+        """Exactly n steps, starting at buffer set 0."""
+        if graphs is None:
+            for k in range(n):
+                step_eager(k)
+            return
+        with torch.cuda.stream(stream):
+            for _ in range(n // N_SETS):
+                cycle.replay()
+            for k in range(n % N_SETS):
+                graphs[k].replay()
 
     # ---- warmup, then the timed region: exactly K steps
-    for k in range(args.warmup):
-        step(k)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
+    run_steps(args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -255,7 +270,8 @@ def main():
                                "~N(0,1), weight ~N(1,0.1), eps 1e-6, seed 0",
                    "hidden": HIDDEN, "rows": list(SWEEP_ROWS), "bytes_per_step": step_bytes,
                    "pct_peak": round(100 * value / HBM_PEAK_GBPS, 1),
-                   "launch": "hip graph replay" if graphs is not None else "eager",
+                   "launch": ("hip graph replay, one graph per 3-step cycle of the buffer "
+                              "sets" if graphs is not None else "eager"),
                    "buffer_sets": N_SETS},
         "roofline": roofline,
         "kernels": kernels,
@@ -265,7 +281,7 @@ def main():
     }
 
     if not args.no_other_ops:
-        result["other_ops"] = other_ops(torch, rn, wl, dev, stream, min(args.steps, 50))
+        result["other_ops"] = other_ops(torch, rn, wl, dev, stream, max(3, min(args.steps, 50) // 5))
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -313,79 +329,99 @@ def timed_events(torch, stream, fn, reps):
     return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
 
 
+def graph_time_per_launch(torch, stream, launches, reps):
+    """Average time per launch of `launches` (callables, one per buffer set),
+    captured in one graph and replayed `reps` times between two events."""
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for fn in launches:
+                fn()
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+
+
+def _n_sets(per_set_bytes: int) -> int:
+    """Buffer sets so that consecutive launches cycle through >= 1.2 GB (cold)."""
+    return max(3, -(-int(1.2e9) // per_set_bytes))
+
+
 def other_ops(torch, rn, wl, dev, stream, reps):
-    """The other three operations at their largest workload, cold buffers."""
+    """The other three operations at their largest workload: back-to-back
+    launches over enough buffer sets that every launch reads cold data,
+    replayed from one graph; time per launch."""
     out = []
-    nset = 3
     # RMSNorm, hidden 16384, rows 4096
     h, rows = 16384, 4096
     i = wl.rmsnorm_inputs(rows, h, seed=0)
-    xs = [wl.to_device_bf16(i["x"], dev) for _ in range(nset)]
-    os_ = [torch.empty_like(xs[0]) for _ in range(nset)]
+    n = _n_sets(2 * rows * h * 2)
+    x0 = wl.to_device_bf16(i["x"], dev)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    ys = [torch.empty_like(x0) for _ in range(n)]
     w = wl.to_device_bf16(i["w"], dev)
-    for k in range(3):
-        rn.rmsnorm_fwd(xs[k % nset], w, i["eps"], out=os_[k % nset], stream=stream)
-    d = timed_events(torch, stream,
-                     lambda k: rn.rmsnorm_fwd(xs[k % nset], w, i["eps"], out=os_[k % nset],
-                                              stream=stream), reps)
-    b = 4 * h * rows + 2 * h
-    out.append(_op_rec("rmsnorm_fwd", rows, h, b, d))
-    del xs, os_
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_fwd", rows, h, 4 * h * rows + 2 * h, t))
+    del xs, ys, x0
     # LayerNorm forward, hidden 16384, rows 2048
     h, rows = 16384, 2048
     i = wl.layernorm_fwd_inputs(rows, h, seed=0)
-    xs = [wl.to_device_bf16(i["x"], dev) for _ in range(nset)]
-    ys = [torch.empty_like(xs[0]) for _ in range(nset)]
-    ms = [torch.empty(rows, device=dev) for _ in range(nset)]
-    rs = [torch.empty(rows, device=dev) for _ in range(nset)]
+    n = _n_sets(2 * rows * h * 2)
+    x0 = wl.to_device_bf16(i["x"], dev)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    ys = [torch.empty_like(x0) for _ in range(n)]
+    st = torch.empty(n, 2, rows, device=dev)
     w, bb = wl.to_device_bf16(i["w"], dev), wl.to_device_bf16(i["b"], dev)
-
-    def lnf(k):
-        j = k % nset
-        rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=ms[j], rstd=rs[j], stream=stream)
-    for k in range(3):
-        lnf(k)
-    d = timed_events(torch, stream, lnf, reps)
-    out.append(_op_rec("layernorm_fwd", rows, h, (4 * h + 8) * rows + 4 * h, d))
-    del xs, ys
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
+                                      rstd=st[j, 1], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_fwd", rows, h, (4 * h + 8) * rows + 4 * h, t))
+    del xs, ys, x0
     # LayerNorm backward, hidden 4096 and 8192, rows 8192
     for h in (4096, 8192):
         rows = 8192
         i = wl.layernorm_bwd_inputs(rows, h, seed=0)
-        x = wl.to_device_bf16(i["x"], dev)
+        n = _n_sets(3 * rows * h * 2)
+        x0 = wl.to_device_bf16(i["x"], dev)
         w = wl.to_device_bf16(i["w"], dev)
         zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
-        _, mean, rstd = rn.layernorm_fwd(x, w, zb, i["eps"], stream=stream)
-        xs = [x] + [x.clone() for _ in range(nset - 1)]
-        dys = [wl.to_device_bf16(i["dy"], dev) for _ in range(nset)]
-        dxs = [torch.empty_like(x) for _ in range(nset)]
+        _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
+        dy0 = wl.to_device_bf16(i["dy"], dev)
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
+        dxs = [torch.empty_like(x0) for _ in range(n)]
         dw = torch.empty(h, device=dev)
         db = torch.empty(h, device=dev)
         ws = torch.empty(rn.workspace_bytes(rows, h), dtype=torch.uint8, device=dev)
-
-        def lnb(k):
-            j = k % nset
-            rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j], dweight=dw,
-                             dbias=db, workspace=ws, stream=stream)
-        for k in range(3):
-            lnb(k)
-        d = timed_events(torch, stream, lnb, reps)
-        out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, d,
+        t = graph_time_per_launch(torch, stream, [
+            (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
+                                          dweight=dw, dbias=db, workspace=ws, stream=stream))
+            for j in range(n)], reps)
+        out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
                            note="rows kernel + column-reduce kernel; workspace not counted"))
-        del xs, dys, dxs
+        del xs, dys, dxs, x0, dy0
     torch.cuda.synchronize()
     return out
 
 
-def _op_rec(op, rows, hidden, nbytes, d, note=None):
-    med = float(np.median(d))
-    gbps = nbytes / (med * 1e-6) / 1e9
+def _op_rec(op, rows, hidden, nbytes, us, note=None):
+    gbps = nbytes / (us * 1e-6) / 1e9
     rec = {"op": op, "rows": rows, "hidden": hidden, "algorithmic_bytes": nbytes,
-           "us_median": round(med, 3), "GBps": round(gbps, 1),
+           "us_per_launch": round(us, 3), "GBps": round(gbps, 1),
            "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
     if note:
         rec["note"] = note
-    log(f"  {op} {rows}x{hidden}: {med:.2f} us, {gbps:.0f} GB/s")
+    log(f"  {op} {rows}x{hidden}: {us:.2f} us, {gbps:.0f} GB/s")
     return rec
 
 
@@ -471,11 +507,11 @@ def _alg_bytes(name: str, rows):
     return None
 
 
-def summarize_profiles(d: str):
+def summarize_profiles(d: str, out_dir: str = PROFILES):
     import csv
     import collections
 
-    os.makedirs(PROFILES, exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     cmds = "\n".join("    " + c for c in PROFILE_COMMANDS)
 
     # -- kernel trace statistics
@@ -508,7 +544,7 @@ def summarize_profiles(d: str):
     lines += ["", "Launches chained in one HIP graph start as soon as their predecessor ends, "
               "so under the tracer a small launch's interval also covers the dependency wait; "
               "the large launches' intervals are their execution time."]
-    open(os.path.join(PROFILES, "fused_add_rmsnorm_h4096_sweep_kernel_stats.md"), "w").write(
+    open(os.path.join(out_dir, "fused_add_rmsnorm_h4096_sweep_kernel_stats.md"), "w").write(
         "\n".join(lines) + "\n")
 
     # -- HBM traffic from FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
@@ -560,12 +596,12 @@ def summarize_profiles(d: str):
     lines += ["", "Per-launch averages over each kernel's dispatches (the mix of row counts "
               "the sweep gives it) are in `profiles/traffic.json`, which `bench.py` reports as "
               "`roofline.traffic` while the kernel sources are unchanged."]
-    open(os.path.join(PROFILES, "fused_add_rmsnorm_h4096_sweep_hbm_traffic.md"), "w").write(
+    open(os.path.join(out_dir, "fused_add_rmsnorm_h4096_sweep_hbm_traffic.md"), "w").write(
         "\n".join(lines) + "\n")
     json.dump({"kernel_source_sha256": kernel_source_digest(),
                "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels},
-              open(os.path.join(PROFILES, "traffic.json"), "w"), indent=1)
-    print(f"wrote summaries to {PROFILES}")
+              open(os.path.join(out_dir, "traffic.json"), "w"), indent=1)
+    print(f"wrote summaries to {out_dir}")
 
 
 if __name__ == "__main__":
