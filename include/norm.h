@@ -190,6 +190,17 @@ NORM_API norm_status norm_layernorm_bwd_cfg(void* dx, float* dweight, float* dbi
 NORM_API norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden,
                                int32_t cu_count, norm_launch_cfg* cfg);
 
+/* Human-readable description of the launch the library would make for
+ * (op, rows, hidden) on a device with `cu_count` compute units (<= 0: the
+ * current device): kernel instantiation, lanes per row, rows per workgroup,
+ * 16-byte vectors per lane, workgroup size, grid, ring depth and workspace.
+ * Writes a NUL-terminated string of at most `len` bytes to `buf` (which may be
+ * NULL when len is 0) and returns the full length without the NUL, or -1 for
+ * invalid arguments or an unsupported hidden.  Host logic only when
+ * cu_count > 0. */
+NORM_API int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden,
+                                      int32_t cu_count, char* buf, size_t len);
+
 /* Enumerate the compiled launch shapes of (op, hidden): writes up to
  * `capacity` entries to `out` (which may be NULL when capacity is 0) and
  * returns the total count; 0 for an unsupported hidden. */

@@ -112,6 +112,9 @@ def lib() -> ctypes.CDLL:
     L.norm_select_config.restype = ctypes.c_int
     L.norm_list_configs.argtypes = [ctypes.c_int, _i64, _cfgp, ctypes.c_int32]
     L.norm_list_configs.restype = ctypes.c_int32
+    L.norm_describe_config.argtypes = [ctypes.c_int, _i64, _i64, ctypes.c_int32, ctypes.c_char_p,
+                                       ctypes.c_size_t]
+    L.norm_describe_config.restype = ctypes.c_int32
     _lib = L
     return L
 
@@ -270,6 +273,17 @@ def select_config(op, rows: int, hidden: int, cu_count: int = 0) -> Cfg:
     _check(lib().norm_select_config(int(op), rows, hidden, cu_count, ctypes.byref(c)),
            "norm_select_config")
     return Cfg(*c.astuple())
+
+
+def describe_config(op, rows: int, hidden: int, cu_count: int = 0) -> str:
+    """The launch the library would make, as text (kernel, lanes, grid, ...)."""
+    op = OPS.get(op, op)
+    n = lib().norm_describe_config(int(op), rows, hidden, cu_count, None, 0)
+    if n < 0:
+        raise NormError(1, f"norm_describe_config: invalid arguments ({op}, {rows}, {hidden})")
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().norm_describe_config(int(op), rows, hidden, cu_count, buf, n + 1)
+    return buf.value.decode()
 
 
 def list_configs(op, hidden: int):

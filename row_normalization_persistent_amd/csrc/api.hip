@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "launch.hpp"
@@ -138,6 +139,11 @@ norm_launch_cfg choose_bwd(int64_t rows, int64_t hidden) {
         if (best == 0 || e.lanes > best) best = e.lanes;
     }
     return norm_launch_cfg{best, 1, default_bwd_grid(rows)};
+}
+
+int bwd_depth_of(int64_t hidden, int lanes) {
+    const BwdEntry* e = find_bwd(hidden, lanes);
+    return e ? e->depth : 0;
 }
 
 size_t bwd_workspace_bytes(int64_t hidden, int32_t grid) {
@@ -348,6 +354,48 @@ norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden, int32_t
     }
     *cfg = choose_fwd(op, rows, hidden, cu);
     return NORM_SUCCESS;
+}
+
+int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
+                             char* buf, size_t len) {
+    static const char* const kNames[] = {"fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd",
+                                         "layernorm_bwd"};
+    norm_launch_cfg c;
+    if (norm_select_config(op, rows, hidden, cu_count, &c) != NORM_SUCCESS) return -1;
+    const int vecs = (int)(hidden / (8 * c.threads_per_row));
+    char tmp[512];
+    int n;
+    if (op == NORM_OP_LAYERNORM_BWD) {
+        n = std::snprintf(tmp, sizeof tmp,
+                          "%s rows=%lld hidden=%lld: layernorm_bwd_rows_kernel<%lld,%d,%d> "
+                          "(%d lanes per row, %d vectors per lane, ring of %d rows) on a "
+                          "persistent grid of %d workgroups, then layernorm_bwd_colreduce_kernel "
+                          "(%lld workgroups of %d); workspace %zu bytes",
+                          kNames[op], (long long)rows, (long long)hidden, (long long)hidden,
+                          c.threads_per_row, bwd_depth_of(hidden, c.threads_per_row),
+                          c.threads_per_row, vecs, bwd_depth_of(hidden, c.threads_per_row),
+                          c.grid, (long long)(2 * hidden / kColReduceCols), kColReduceThreads,
+                          bwd_workspace_bytes(hidden, rows > 0 ? c.grid : 0));
+    } else {
+        const char* kern = op == NORM_OP_FUSED_ADD_RMSNORM ? "fused_add_rmsnorm_kernel"
+                           : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd_kernel"
+                                                           : "layernorm_fwd_kernel";
+        n = std::snprintf(tmp, sizeof tmp,
+                          "%s rows=%lld hidden=%lld: %s<%lld,%d,%d> (%d lanes per row, %d rows "
+                          "per workgroup of %d, %d vectors per lane), grid %lld",
+                          kNames[op], (long long)rows, (long long)hidden, kern,
+                          (long long)hidden, c.threads_per_row, c.rows_per_block,
+                          c.threads_per_row, c.rows_per_block,
+                          c.threads_per_row * c.rows_per_block, vecs,
+                          (long long)((rows + c.rows_per_block - 1) / c.rows_per_block));
+    }
+    if (n < 0) return -1;
+    if (buf && len > 0) {
+        const size_t k = (size_t)n < len - 1 ? (size_t)n : len - 1;
+        std::memcpy(buf, tmp, k);
+        buf[k] = '\0';
+    }
+    return n;
 }
 
 int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int32_t capacity) {

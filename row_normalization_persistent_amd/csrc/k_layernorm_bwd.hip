@@ -236,7 +236,8 @@ using BwdShapeList = std::tuple<Lanes<64>, Lanes<128>, Lanes<256>, Lanes<512>, L
 
 template <int H, int T>
 void add_bwd_entry(std::vector<BwdEntry>& v, Lanes<T>) {
-    if constexpr (H % (8 * T) == 0 && H / (8 * T) <= 4) v.push_back({H, T, &launch_bwd<H, T>});
+    if constexpr (H % (8 * T) == 0 && H / (8 * T) <= 4)
+        v.push_back({H, T, bwd_depth<H, T>(), &launch_bwd<H, T>});
 }
 
 template <int H, class... Ls>

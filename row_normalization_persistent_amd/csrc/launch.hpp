@@ -48,7 +48,7 @@ struct FwdEntry {
 };
 
 struct BwdEntry {
-    int hidden, lanes;
+    int hidden, lanes, depth;  // depth: rows kept in flight per workgroup
     BwdLauncher launch;
 };
 

@@ -28,7 +28,7 @@ def test_header_declares_the_four_operations():
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
                "norm_layernorm_bwd"):
         assert op in names
-    assert len(names) == 13
+    assert len(names) == 14
 
 
 def test_library_exports_every_declared_symbol():
@@ -89,6 +89,21 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
         assert rn.Cfg(c.threads_per_row, 1, 0) in rn.list_configs("layernorm_bwd", h)
         assert c.grid == 256
         assert rn.select_config("layernorm_bwd", 5, h).grid == 5
+
+
+def test_describe_config():
+    d = rn.describe_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
+    c = rn.select_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
+    assert f"fused_add_rmsnorm_kernel<4096,{c.threads_per_row},{c.rows_per_block}>" in d
+    d = rn.describe_config("layernorm_bwd", 8192, 4096, cu_count=256)
+    assert "persistent grid of 256" in d and f"workspace {rn.workspace_bytes(8192, 4096)}" in d
+    with pytest.raises(rn.NormError):
+        rn.describe_config("rmsnorm_fwd", 4, 1000, cu_count=256)
+    L = rn.lib()
+    buf = ctypes.create_string_buffer(8)  # truncated, still NUL-terminated
+    n = L.norm_describe_config(0, 16, 4096, 256, buf, 8)
+    full = rn.describe_config(0, 16, 4096, cu_count=256)
+    assert n == len(full) and buf.value.decode() == full[:7]
 
 
 def test_workspace_bytes():
