@@ -15,7 +15,10 @@ no fast-math); this module only marshals numpy arrays into it.  Definitions:
   PR 5587), description summary; LayerNorm per Ba, Kiros & Hinton (2016)
   eq. 4 with biased variance and eps inside the square root;
 * LayerNorm backward as a combined inner + outer reduction -- "Llu/ln bwd"
-  (nvFuser PR 207), author note and review thread.
+  (nvFuser PR 207), author note and review thread;
+* RMSNorm backward (and the fused residual-add + RMSNorm backward) -- the same
+  combined inner + outer reduction applied to RMSNorm; the gradient of
+  Zhang & Sennrich (2019) eq. 4 with the statistic recomputed from x.
 """
 from __future__ import annotations
 
@@ -67,8 +70,10 @@ def _bind(lib):
                                       _f64p, _f64p, _f64p, ctypes.c_int]
     lib.orc_layernorm_bwd.argtypes = [_u16p, _u16p, _f64p, _f64p, _u16p, _i64, _i64,
                                       _f64p, _f64p, _f64p, ctypes.c_int]
+    lib.orc_rmsnorm_bwd.argtypes = [_u16p, _u16p, _u16p, _u16p, _i64, _i64, ctypes.c_double,
+                                    _f64p, _f64p, _f64p, ctypes.c_int]
     for name in ("orc_fused_add_rmsnorm", "orc_rmsnorm_fwd", "orc_layernorm_fwd",
-                 "orc_layernorm_bwd"):
+                 "orc_layernorm_bwd", "orc_rmsnorm_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -180,6 +185,27 @@ class Oracle:
         return dx, dw, db
 
 
+    def rmsnorm_bwd(self, dy, x, w, eps: float, dres=None, nthreads: int = 1):
+        """RMSNorm backward with rstd recomputed from x; dres (optional bf16
+        bits) is added to dx (the fused residual-add + RMSNorm backward).
+        Returns (dx_f64, dweight_f64, rstd_f64)."""
+        dy, x, w = _u16(dy), _u16(x), _u16(w)
+        rows, hidden = _shape(x)
+        assert dy.shape == x.shape and w.shape == (hidden,)
+        dres_p = None
+        if dres is not None:
+            dres = _u16(dres)
+            assert dres.shape == x.shape
+            dres_p = _p16(dres)
+        dx = np.empty((rows, hidden), np.float64)
+        dw = np.empty((hidden,), np.float64)
+        rstd = np.empty((rows,), np.float64)
+        _check(self.lib.orc_rmsnorm_bwd(_p16(dy), _p16(x), _p16(w), dres_p, rows, hidden,
+                                        float(eps), _p64(dx), _p64(dw), _p64(rstd), nthreads),
+               "rmsnorm_bwd")
+        return dx, dw, rstd
+
+
 _default: Oracle | None = None
 
 
@@ -212,3 +238,7 @@ def layernorm_fwd(x, w, b, eps, nthreads=1):
 
 def layernorm_bwd(dy, x, mean, rstd, w, nthreads=1):
     return default().layernorm_bwd(dy, x, mean, rstd, w, nthreads)
+
+
+def rmsnorm_bwd(dy, x, w, eps, dres=None, nthreads=1):
+    return default().rmsnorm_bwd(dy, x, w, eps, dres, nthreads)

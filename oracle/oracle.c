@@ -298,3 +298,74 @@ int orc_layernorm_bwd(const uint16_t* dy, const uint16_t* x,
     parallel_ranges(lnb_cols, &c, hidden, nthreads);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm backward: inner (per-row dx) and outer (per-column dweight) sums. */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *dy, *x, *w, *dres;
+    int64_t rows, hidden;
+    double eps;
+    double *dx, *dweight, *rstd;
+} rmsb_ctx;
+
+static double rmsb_rstd(const rmsb_ctx* c, int64_t i) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < c->hidden; ++j) {
+        const double v = orc_bf16_decode(c->x[i * c->hidden + j]);
+        ss += v * v;
+    }
+    return 1.0 / sqrt(ss / (double)c->hidden + c->eps);
+}
+
+static void rmsb_rows(const void* p, int64_t begin, int64_t end) {
+    const rmsb_ctx* c = (const rmsb_ctx*)p;
+    const int64_t H = c->hidden;
+    for (int64_t i = begin; i < end; ++i) {
+        const double rstd = rmsb_rstd(c, i);
+        c->rstd[i] = rstd;
+        double sum_gx = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            const double g = orc_bf16_decode(c->dy[i * H + j]) * orc_bf16_decode(c->w[j]);
+            sum_gx += g * orc_bf16_decode(c->x[i * H + j]) * rstd;
+        }
+        const double cc = sum_gx / (double)H;
+        for (int64_t j = 0; j < H; ++j) {
+            const double g = orc_bf16_decode(c->dy[i * H + j]) * orc_bf16_decode(c->w[j]);
+            const double xhat = orc_bf16_decode(c->x[i * H + j]) * rstd;
+            double v = rstd * (g - xhat * cc);
+            if (c->dres) v += orc_bf16_decode(c->dres[i * H + j]);
+            c->dx[i * H + j] = v;
+        }
+    }
+}
+
+static void rmsb_cols(const void* p, int64_t begin, int64_t end) {
+    const rmsb_ctx* c = (const rmsb_ctx*)p;
+    for (int64_t j = begin; j < end; ++j) {
+        double dw = 0.0;
+        for (int64_t i = 0; i < c->rows; ++i)
+            dw += orc_bf16_decode(c->dy[i * c->hidden + j]) *
+                  (orc_bf16_decode(c->x[i * c->hidden + j]) * c->rstd[i]);
+        c->dweight[j] = dw;
+    }
+}
+
+int orc_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w,
+                    const uint16_t* dres, int64_t rows, int64_t hidden, double eps,
+                    double* dx, double* dweight, double* rstd_out, int nthreads) {
+    if (bad_common(rows, hidden, eps) || !dweight) return -1;
+    if (rows == 0) {
+        for (int64_t j = 0; j < hidden; ++j) dweight[j] = 0.0;
+        return 0;
+    }
+    if (!dy || !x || !w || !dx) return -1;
+    double* rstd = rstd_out ? rstd_out : (double*)malloc((size_t)rows * sizeof(double));
+    if (!rstd) return -1;
+    rmsb_ctx c = {dy, x, w, dres, rows, hidden, eps, dx, dweight, rstd};
+    parallel_ranges(rmsb_rows, &c, rows, nthreads);
+    parallel_ranges(rmsb_cols, &c, hidden, nthreads);
+    if (!rstd_out) free(rstd);
+    return 0;
+}

@@ -77,6 +77,17 @@ int orc_layernorm_bwd(const uint16_t* dy, const uint16_t* x,
                       int64_t rows, int64_t hidden,
                       double* dx, double* dweight, double* dbias, int nthreads);
 
+/* RMSNorm backward (and the fused residual-add + RMSNorm backward), with the
+ * per-row statistic recomputed from x:
+ *   rstd = 1/sqrt(mean_j(x^2) + eps),  xhat = x * rstd,  g = dy * w,
+ *   c = mean_j (g * xhat),  dx = rstd * (g - xhat * c)  [+ dres]   (per row)
+ *   dweight_j = sum_i dy_ij * xhat_ij                               (per column)
+ * dres (may be NULL) is the gradient arriving at the fused op's residual
+ * output; the fused op's x and residual inputs both receive dx. */
+int orc_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w,
+                    const uint16_t* dres, int64_t rows, int64_t hidden, double eps,
+                    double* dx, double* dweight, double* rstd_out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,10 @@ What each pin compares against:
   * LayerNorm bwd   -- torch autograd in float64; central finite differences of
                        sum(dy * LayerNorm(x)) with the statistics recomputed
                        from x; column sums against math.fsum.
+  * RMSNorm bwd     -- torch autograd of rms_norm in float64 (with and without
+                       the fused op's residual gradient); central finite
+                       differences; fsum column sums; closed forms (constant
+                       row, orthogonality to x at eps = 0).
 """
 from __future__ import annotations
 
@@ -363,6 +367,102 @@ def check_thread_count_independence(o):
         assert np.array_equal(u, v)
 
 
+# ---------------------------------------------------------------- RMSNorm backward
+def rms_np(x, w, eps):
+    """RMSNorm in float64 numpy, statistic recomputed from x (test-side)."""
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * w
+
+
+def check_rmsb_autograd(o):
+    rng = np.random.default_rng(37)
+    eps = float(np.float32(1e-6))
+    for rows, hidden in ((5, 64), (7, 1024), (3, 4096)):
+        x = rand_bf16(rng, (rows, hidden))
+        dy = rand_bf16(rng, (rows, hidden))
+        dres = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        xt = torch.from_numpy(torch_bf16_to_f64(x)).requires_grad_(True)
+        wt = torch.from_numpy(torch_bf16_to_f64(w)).requires_grad_(True)
+        F.rms_norm(xt, (hidden,), wt, eps).backward(torch.from_numpy(torch_bf16_to_f64(dy)))
+        dx, dw, rstd = o.rmsnorm_bwd(dy, x, w, eps)
+        scale = np.abs(xt.grad.numpy()).max()
+        close(dx, xt.grad.numpy(), 1e-10, 1e-12 * scale, "rmsnorm dx vs autograd")
+        close(dw, wt.grad.numpy(), 1e-10, 1e-11, "rmsnorm dweight vs autograd")
+        xd = torch_bf16_to_f64(x)
+        close(rstd, 1.0 / np.sqrt((xd * xd).mean(1) + eps), 1e-14, 0, "rmsnorm bwd rstd")
+        # the fused op: s = x + r feeds both out and the residual output, so the
+        # residual gradient adds to the normalization's input gradient
+        st = torch.from_numpy(xd.copy()).requires_grad_(True)
+        out = F.rms_norm(st, (hidden,), torch.from_numpy(torch_bf16_to_f64(w)), eps)
+        (out * torch.from_numpy(torch_bf16_to_f64(dy))).sum().add(
+            (st * torch.from_numpy(torch_bf16_to_f64(dres))).sum()).backward()
+        fdx, fdw, _ = o.rmsnorm_bwd(dy, x, w, eps, dres=dres)
+        close(fdx, st.grad.numpy(), 1e-10, 1e-12 * scale, "fused bwd ds vs autograd")
+        assert np.array_equal(fdw, dw), "the residual gradient must not touch dweight"
+
+
+def check_rmsb_finite_differences(o):
+    rng = np.random.default_rng(41)
+    eps = 1e-3
+    for rows, hidden in ((1, 8), (3, 16), (2, 64)):
+        x = rand_bf16(rng, (rows, hidden))
+        dy = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        xd, dyd, wd = (torch_bf16_to_f64(a) for a in (x, dy, w))
+        dx, dw, _ = o.rmsnorm_bwd(dy, x, w, eps)
+
+        def loss_row(i, xrow, wv=wd):
+            return float(np.sum(dyd[i] * rms_np(xrow[None, :], wv, eps)[0]))
+
+        fd = np.empty_like(xd)
+        for i in range(rows):
+            for j in range(hidden):
+                h = 1e-5 * max(1.0, abs(xd[i, j]))
+                xp, xm = xd[i].copy(), xd[i].copy()
+                xp[j] += h
+                xm[j] -= h
+                fd[i, j] = (loss_row(i, xp) - loss_row(i, xm)) / (2 * h)
+        close(dx, fd, 1e-6, 1e-6 * np.abs(fd).max(), "rmsnorm dx vs finite differences")
+        fdw = np.empty(hidden)
+        for j in range(hidden):
+            wp, wm = wd.copy(), wd.copy()
+            wp[j] += 1e-3
+            wm[j] -= 1e-3
+            fdw[j] = sum(loss_row(i, xd[i], wp) - loss_row(i, xd[i], wm) for i in range(rows)) / 2e-3
+        close(dw, fdw, 1e-8, 1e-9, "rmsnorm dweight vs finite differences")
+
+
+def check_rmsb_sums_and_closed_forms(o):
+    rng = np.random.default_rng(43)
+    rows, hidden = 2000, 96
+    eps = float(np.float32(1e-6))
+    x = rand_bf16(rng, (rows, hidden))
+    dy = rand_bf16(rng, (rows, hidden))
+    w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+    xd, dyd, wd = (torch_bf16_to_f64(a) for a in (x, dy, w))
+    dx, dw, rstd = o.rmsnorm_bwd(dy, x, w, eps)
+    xhat = xd * rstd[:, None]
+    for j in range(hidden):
+        ref = math.fsum(dyd[:, j] * xhat[:, j])
+        assert abs(dw[j] - ref) <= 1e-12 * math.fsum(np.abs(dyd[:, j] * xhat[:, j])), \
+            f"rmsnorm dweight[{j}] vs fsum"
+    # sum_j dx * x = rstd * sum_j(g x) * eps / (mean(x^2) + eps)
+    g = dyd * wd
+    ms = (xd * xd).mean(1)
+    close((dx * xd).sum(1), rstd * (g * xd).sum(1) * eps / (ms + eps), 1e-6,
+          1e-12 * np.abs(dx * xd).sum(1).max(), "sum_j dx*x closed form")
+    # constant row c > 0 at eps = 0: xhat = 1, dx = (g - mean(g)) / c
+    c = 2.5
+    xc = torch_bf16_bits(np.full((3, hidden), c, np.float32))
+    dxc, _, _ = o.rmsnorm_bwd(dy[:3], xc, w, 0.0)
+    gc = dyd[:3] * wd
+    close(dxc, (gc - gc.mean(1, keepdims=True)) / c, 1e-13, 1e-15, "constant row dx")
+    # the residual gradient is added once, unchanged
+    dres = rand_bf16(rng, (rows, hidden))
+    fdx, _, _ = o.rmsnorm_bwd(dy, x, w, eps, dres=dres)
+    assert np.array_equal(fdx, dx + torch_bf16_to_f64(dres)), "dres must be added as is"
+
+
 ALL_CHECKS = [
     check_bf16_decode,
     check_bf16_encode,
@@ -375,5 +475,8 @@ ALL_CHECKS = [
     check_lnb_autograd,
     check_lnb_finite_differences,
     check_lnb_column_sums,
+    check_rmsb_autograd,
+    check_rmsb_finite_differences,
+    check_rmsb_sums_and_closed_forms,
     check_thread_count_independence,
 ]

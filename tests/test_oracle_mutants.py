@@ -52,8 +52,22 @@ MUTANTS = [
     ("lnb_dbias_scaled", "db += d;", "db += d * lnb_xhat(c, i, j);"),
     ("lnb_c2_divisor", "const double c2 = sum_gx / (double)H;",
      "const double c2 = sum_gx / (double)(H - 1);"),
-    ("lnb_cols_skip_first_row", "for (int64_t i = 0; i < c->rows; ++i) {",
-     "for (int64_t i = 1; i < c->rows; ++i) {"),
+    ("lnb_cols_skip_first_row", "for (int64_t i = 0; i < c->rows; ++i) {\n            const double d",
+     "for (int64_t i = 1; i < c->rows; ++i) {\n            const double d"),
+    ("rmsb_divisor", "return 1.0 / sqrt(ss / (double)c->hidden + c->eps);",
+     "return 1.0 / sqrt(ss / (double)(c->hidden - 1) + c->eps);"),
+    ("rmsb_drop_c", "double v = rstd * (g - xhat * cc);", "double v = rstd * g;"),
+    ("rmsb_sign_c", "double v = rstd * (g - xhat * cc);", "double v = rstd * (g + xhat * cc);"),
+    ("rmsb_c_divisor", "const double cc = sum_gx / (double)H;",
+     "const double cc = sum_gx / (double)(H - 1);"),
+    ("rmsb_dres_subtracted", "if (c->dres) v += orc_bf16_decode(c->dres[i * H + j]);",
+     "if (c->dres) v -= orc_bf16_decode(c->dres[i * H + j]);"),
+    ("rmsb_dw_no_rstd", "(orc_bf16_decode(c->x[i * c->hidden + j]) * c->rstd[i]);",
+     "orc_bf16_decode(c->x[i * c->hidden + j]);"),
+    ("rmsb_gx_no_w", "orc_bf16_decode(c->w[j]);\n            sum_gx",
+     "1.0;\n            sum_gx"),
+    ("rmsb_gx_no_rstd", "sum_gx += g * orc_bf16_decode(c->x[i * H + j]) * rstd;",
+     "sum_gx += g * orc_bf16_decode(c->x[i * H + j]);"),
 ]
 
 
