@@ -22,8 +22,9 @@ Also reported, on the same line:
   kernels       the same for every instantiation the sweep uses
   sweep         per-rows GB/s, % of the 8 TB/s peak, rows/s (eager launches,
                 an event pair around each, so dispatch overhead is included)
-  other_ops     RMSNorm / LayerNorm forward / LayerNorm backward at their
-                largest workload: one graph of back-to-back launches over
+  other_ops     RMSNorm / LayerNorm forward / LayerNorm backward / RMSNorm
+                backward / fused add + RMSNorm backward at their largest
+                workload: one graph of back-to-back launches over
                 >= 1.2 GB of buffer sets (cold reads), time per launch
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
@@ -410,6 +411,32 @@ def other_ops(torch, rn, wl, dev, stream, reps):
         out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
                            note="rows kernel + column-reduce kernel; workspace not counted"))
         del xs, dys, dxs, x0, dy0
+    # RMSNorm backward and the fused residual-add + RMSNorm backward, hidden 4096, rows 8192
+    h, rows = 4096, 8192
+    i = wl.rmsnorm_bwd_inputs(rows, h, seed=0)
+    n = _n_sets(4 * rows * h * 2)
+    x0, dy0, dr0 = (wl.to_device_bf16(i[k], dev) for k in ("x", "dy", "dres"))
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
+    drs = [dr0] + [dr0.clone() for _ in range(n - 1)]
+    dxs = [torch.empty_like(x0) for _ in range(n)]
+    w = wl.to_device_bf16(i["w"], dev)
+    dw = torch.empty(h, device=dev)
+    ws = torch.empty(rn.workspace_bytes(rows, h, op="rmsnorm_bwd"), dtype=torch.uint8, device=dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, i["eps"], dx=dxs[j], dweight=dw,
+                                    workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
+                       note="rows kernel + column-reduce kernel; workspace not counted"))
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.fused_add_rmsnorm_bwd(dys[j], xs[j], w, i["eps"], dres=drs[j],
+                                              ds=dxs[j], dweight=dw, workspace=ws,
+                                              stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, 8 * h * rows + 6 * h, t,
+                       note="dout, dres, s read; ds written; workspace not counted"))
+    del xs, dys, drs, dxs, x0, dy0, dr0
     torch.cuda.synchronize()
     return out
 

@@ -79,7 +79,9 @@ typedef enum {
     NORM_OP_FUSED_ADD_RMSNORM = 0,
     NORM_OP_RMSNORM_FWD = 1,
     NORM_OP_LAYERNORM_FWD = 2,
-    NORM_OP_LAYERNORM_BWD = 3
+    NORM_OP_LAYERNORM_BWD = 3,
+    NORM_OP_RMSNORM_BWD = 4,
+    NORM_OP_FUSED_ADD_RMSNORM_BWD = 5
 } norm_op;
 
 /* Launch shape of one kernel instantiation.
@@ -88,9 +90,9 @@ typedef enum {
  *                     of the row live in each lane's registers.
  *   rows_per_block  : rows handled side by side by one workgroup
  *                     (workgroup size = threads_per_row * rows_per_block).
- *   grid            : LayerNorm backward only: number of persistent
- *                     workgroups (one partial column-sum slab each); 0 lets
- *                     the library choose.  Ignored (must be 0) elsewhere. */
+ *   grid            : backward ops only: number of persistent workgroups (one
+ *                     partial column-sum slab each); 0 lets the library
+ *                     choose.  Must be 0 for the forward ops. */
 typedef struct {
     int32_t threads_per_row;
     int32_t rows_per_block;
@@ -152,6 +154,42 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
                                int64_t rows, int64_t hidden, float eps,
                                hipStream_t stream);
 
+/* RMSNorm backward with the same combined inner + outer reduction ("Llu/ln
+ * bwd", author note and review thread, applied to RMSNorm), the per-row
+ * statistic recomputed from x with `eps` (no saved statistic is needed):
+ *   rstd = rsqrt(mean_j x^2 + eps),  xhat = x * rstd,  g = dy * weight
+ *   dx   = bf16(rstd * (g - xhat * mean_j(g * xhat)))   (per row)
+ *   dweight_j = sum_i dy_ij * xhat_ij                    (per column)
+ * dx, dy, x: [rows, hidden] bf16 (dx may equal dy exactly); weight: [hidden]
+ * bf16; dweight: [hidden] fp32, overwritten.  workspace: at least
+ * norm_rmsnorm_bwd_workspace_bytes(rows, hidden) bytes, 16-byte aligned,
+ * contents ignored on entry.  Column sums are bitwise reproducible run to run. */
+NORM_API norm_status norm_rmsnorm_bwd(void* dx, float* dweight, const void* dy, const void* x,
+                                      const void* weight, void* workspace,
+                                      size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                      float eps, hipStream_t stream);
+
+/* Backward of norm_fused_add_rmsnorm ("optimize inner persistent scheduler
+ * for static fusion", changes walkthrough: the fused residual-add + RMSNorm).
+ * The forward's s = x + residual feeds both out = RMSNorm(s) * weight and the
+ * residual output, so x and the residual input receive the same gradient:
+ *   ds = bf16(RMSNormBackward(dout; s, weight, eps) + dres)
+ * s: the residual output of the forward (bf16 [rows, hidden]); dout: gradient
+ * of out; dres: gradient of the residual output, or NULL for none.  ds may
+ * equal dout or dres exactly.  dweight and workspace as for norm_rmsnorm_bwd. */
+NORM_API norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const void* dout,
+                                                const void* dres, const void* s,
+                                                const void* weight, void* workspace,
+                                                size_t workspace_bytes, int64_t rows,
+                                                int64_t hidden, float eps, hipStream_t stream);
+
+/* Bytes of workspace the two RMSNorm backward ops need (library's launch
+ * choice, or a given shape).  Pure host arithmetic; 0 for an unsupported
+ * hidden or rows <= 0. */
+NORM_API size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
+NORM_API size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
+                                                     const norm_launch_cfg* cfg);
+
 /* Bytes of workspace norm_layernorm_bwd needs for (rows, hidden) with the
  * library's own launch choice.  Pure host arithmetic (no HIP call); returns 0
  * for an unsupported hidden or rows < 0. */
@@ -175,6 +213,18 @@ NORM_API norm_status norm_layernorm_fwd_cfg(void* y, float* mean, float* rstd, c
                                    const void* weight, const void* bias,
                                    int64_t rows, int64_t hidden, float eps,
                                    const norm_launch_cfg* cfg, hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_bwd_cfg(void* dx, float* dweight, const void* dy,
+                                          const void* x, const void* weight, void* workspace,
+                                          size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                          float eps, const norm_launch_cfg* cfg,
+                                          hipStream_t stream);
+NORM_API norm_status norm_fused_add_rmsnorm_bwd_cfg(void* ds, float* dweight, const void* dout,
+                                                    const void* dres, const void* s,
+                                                    const void* weight, void* workspace,
+                                                    size_t workspace_bytes, int64_t rows,
+                                                    int64_t hidden, float eps,
+                                                    const norm_launch_cfg* cfg,
+                                                    hipStream_t stream);
 NORM_API norm_status norm_layernorm_bwd_cfg(void* dx, float* dweight, float* dbias,
                                    const void* dy, const void* x, const float* mean,
                                    const float* rstd, const void* weight,

@@ -12,6 +12,9 @@ Operations (names as in the C ABI):
   * ``rmsnorm_fwd``        -- out <- bf16(RMSNorm(x) * w)
   * ``layernorm_fwd``      -- y <- bf16(LayerNorm(x) * w + b), fp32 mean/rstd
   * ``layernorm_bwd``      -- dx (bf16), dweight/dbias (fp32) from dy, x, mean, rstd, w
+  * ``rmsnorm_bwd``        -- dx (bf16), dweight (fp32) from dy, x, w (rstd recomputed)
+  * ``fused_add_rmsnorm_bwd`` -- ds = RMSNorm backward of dout at s, plus dres;
+                              the gradient of both the x and residual inputs
 """
 from __future__ import annotations
 
@@ -30,7 +33,10 @@ OP_FUSED_ADD_RMSNORM = 0
 OP_RMSNORM_FWD = 1
 OP_LAYERNORM_FWD = 2
 OP_LAYERNORM_BWD = 3
-OPS = {"fused_add_rmsnorm": 0, "rmsnorm_fwd": 1, "layernorm_fwd": 2, "layernorm_bwd": 3}
+OP_RMSNORM_BWD = 4
+OP_FUSED_ADD_RMSNORM_BWD = 5
+OPS = {"fused_add_rmsnorm": 0, "rmsnorm_fwd": 1, "layernorm_fwd": 2, "layernorm_bwd": 3,
+       "rmsnorm_bwd": 4, "fused_add_rmsnorm_bwd": 5}
 
 STATUS = {
     0: "NORM_SUCCESS",
@@ -100,10 +106,23 @@ def lib() -> ctypes.CDLL:
     L.norm_layernorm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]
     L.norm_layernorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      ctypes.c_size_t, _i64, _i64, _f32, _vp]
+    L.norm_rmsnorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
+                                       _f32, _cfgp, _vp]
+    L.norm_rmsnorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
+                                   _f32, _vp]
+    L.norm_fused_add_rmsnorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 ctypes.c_size_t, _i64, _i64, _f32, _cfgp, _vp]
+    L.norm_fused_add_rmsnorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                             _i64, _i64, _f32, _vp]
     for n in ("norm_fused_add_rmsnorm_cfg", "norm_rmsnorm_fwd_cfg", "norm_layernorm_fwd_cfg",
               "norm_layernorm_bwd_cfg", "norm_fused_add_rmsnorm", "norm_rmsnorm_fwd",
-              "norm_layernorm_fwd", "norm_layernorm_bwd"):
+              "norm_layernorm_fwd", "norm_layernorm_bwd", "norm_rmsnorm_bwd_cfg",
+              "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd_cfg", "norm_fused_add_rmsnorm_bwd"):
         getattr(L, n).restype = ctypes.c_int
+    L.norm_rmsnorm_bwd_workspace_bytes.argtypes = [_i64, _i64]
+    L.norm_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.norm_rmsnorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
+    L.norm_rmsnorm_bwd_workspace_bytes_cfg.restype = ctypes.c_size_t
     L.norm_layernorm_bwd_workspace_bytes.argtypes = [_i64, _i64]
     L.norm_layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.norm_layernorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
@@ -227,10 +246,17 @@ def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
     return y, mean, rstd
 
 
-def workspace_bytes(rows: int, hidden: int, cfg=None) -> int:
+def workspace_bytes(rows: int, hidden: int, cfg=None, op: str = "layernorm_bwd") -> int:
+    """Workspace bytes a backward op needs (LayerNorm: two partial slabs per
+    workgroup; the RMSNorm backward ops: one)."""
+    rms = OPS.get(op, op) in (OP_RMSNORM_BWD, OP_FUSED_ADD_RMSNORM_BWD)
     if cfg is None:
-        return int(lib().norm_layernorm_bwd_workspace_bytes(rows, hidden))
-    return int(lib().norm_layernorm_bwd_workspace_bytes_cfg(rows, hidden, _cfg_ptr(cfg)))
+        fn = lib().norm_rmsnorm_bwd_workspace_bytes if rms else \
+            lib().norm_layernorm_bwd_workspace_bytes
+        return int(fn(rows, hidden))
+    fn = lib().norm_rmsnorm_bwd_workspace_bytes_cfg if rms else \
+        lib().norm_layernorm_bwd_workspace_bytes_cfg
+    return int(fn(rows, hidden, _cfg_ptr(cfg)))
 
 
 def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
@@ -265,6 +291,59 @@ def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=
                                         float(eps), _cfg_ptr(cfg), _stream(stream)),
            "norm_layernorm_bwd")
     return dx, dweight, dbias
+
+
+def _bwd_common(dy, x, weight, dx, dweight, workspace, cfg, op):
+    _mat(dy, "dy")
+    _mat(x, "x")
+    rows, hidden = _rows_hidden(x)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    _vec(weight, hidden, "weight")
+    dx = torch.empty_like(x) if dx is None else _mat(dx, "dx")
+    if dx.shape != x.shape:
+        raise ValueError("dx must have x's shape")
+    dweight = torch.empty(hidden, dtype=torch.float32, device=x.device) if dweight is None \
+        else dweight
+    _vec(dweight, hidden, "dweight", torch.float32)
+    need = workspace_bytes(rows, hidden, cfg, op)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _mat(workspace, "workspace", workspace.dtype)
+    return rows, hidden, dx, dweight, workspace, workspace.numel() * workspace.element_size()
+
+
+def rmsnorm_bwd(dy, x, weight, eps: float, dx=None, dweight=None, workspace=None, cfg=None,
+                stream=None):
+    """Returns (dx, dweight); rstd is recomputed from x with eps."""
+    rows, hidden, dx, dweight, workspace, wsb = _bwd_common(dy, x, weight, dx, dweight,
+                                                            workspace, cfg, "rmsnorm_bwd")
+    _check(lib().norm_rmsnorm_bwd_cfg(dx.data_ptr(), dweight.data_ptr(), dy.data_ptr(),
+                                      x.data_ptr(), weight.data_ptr(), workspace.data_ptr(), wsb,
+                                      rows, hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
+           "norm_rmsnorm_bwd")
+    return dx, dweight
+
+
+def fused_add_rmsnorm_bwd(dout, s, weight, eps: float, dres=None, ds=None, dweight=None,
+                          workspace=None, cfg=None, stream=None):
+    """Backward of fused_add_rmsnorm at its residual output s: returns (ds,
+    dweight), ds the gradient of both the x and residual inputs."""
+    rows, hidden, ds, dweight, workspace, wsb = _bwd_common(dout, s, weight, ds, dweight,
+                                                            workspace, cfg,
+                                                            "fused_add_rmsnorm_bwd")
+    if dres is not None:
+        _mat(dres, "dres")
+        if dres.shape != s.shape:
+            raise ValueError("dres must have s's shape")
+    _check(lib().norm_fused_add_rmsnorm_bwd_cfg(ds.data_ptr(), dweight.data_ptr(),
+                                                dout.data_ptr(),
+                                                dres.data_ptr() if dres is not None else None,
+                                                s.data_ptr(), weight.data_ptr(),
+                                                workspace.data_ptr(), wsb, rows, hidden,
+                                                float(eps), _cfg_ptr(cfg), _stream(stream)),
+           "norm_fused_add_rmsnorm_bwd")
+    return ds, dweight
 
 
 def select_config(op, rows: int, hidden: int, cu_count: int = 0) -> Cfg:

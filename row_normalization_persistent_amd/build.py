@@ -28,7 +28,7 @@ SOURCES = [
     "k_fused_add_rmsnorm.hip",
     "k_rmsnorm_fwd.hip",
     "k_layernorm_fwd.hip",
-    "k_layernorm_bwd.hip",
+    "k_norm_bwd.hip",
 ]
 
 HIPCC_FLAGS = [

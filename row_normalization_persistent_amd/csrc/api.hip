@@ -87,8 +87,20 @@ const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb) {
     return nullptr;
 }
 
-const BwdEntry* find_bwd(int64_t hidden, int lanes) {
-    for (const BwdEntry& e : layernorm_bwd_table())
+bool is_bwd(norm_op op) {
+    return op == NORM_OP_LAYERNORM_BWD || op == NORM_OP_RMSNORM_BWD ||
+           op == NORM_OP_FUSED_ADD_RMSNORM_BWD;
+}
+
+const std::vector<BwdEntry>& bwd_table(norm_op op) {
+    return op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_table() : rmsnorm_bwd_table();
+}
+
+// partial-sum slabs per workgroup: dweight and dbias for LayerNorm, dweight for RMSNorm
+int bwd_outs(norm_op op) { return op == NORM_OP_LAYERNORM_BWD ? 2 : 1; }
+
+const BwdEntry* find_bwd(norm_op op, int64_t hidden, int lanes) {
+    for (const BwdEntry& e : bwd_table(op))
         if (e.hidden == hidden && e.lanes == lanes) return &e;
     return nullptr;
 }
@@ -130,24 +142,24 @@ int32_t default_bwd_grid(int64_t rows) {
     return (int32_t)(rows < kSlabs ? (rows > 0 ? rows : 1) : kSlabs);
 }
 
-norm_launch_cfg choose_bwd(int64_t rows, int64_t hidden) {
+norm_launch_cfg choose_bwd(norm_op op, int64_t rows, int64_t hidden) {
     // one 16-byte vector of x and of dy per lane when compiled (512 lanes at
     // hidden 4096, 1024 at 8192), else the shape with the fewest vectors per lane
     int best = 0;
-    for (const BwdEntry& e : layernorm_bwd_table()) {
+    for (const BwdEntry& e : bwd_table(op)) {
         if (e.hidden != hidden) continue;
         if (best == 0 || e.lanes > best) best = e.lanes;
     }
     return norm_launch_cfg{best, 1, default_bwd_grid(rows)};
 }
 
-int bwd_depth_of(int64_t hidden, int lanes) {
-    const BwdEntry* e = find_bwd(hidden, lanes);
+int bwd_depth_of(norm_op op, int64_t hidden, int lanes) {
+    const BwdEntry* e = find_bwd(op, hidden, lanes);
     return e ? e->depth : 0;
 }
 
-size_t bwd_workspace_bytes(int64_t hidden, int32_t grid) {
-    return (size_t)grid * 2 * (size_t)hidden * sizeof(float);
+size_t bwd_workspace_bytes(norm_op op, int64_t hidden, int32_t grid) {
+    return (size_t)grid * (size_t)bwd_outs(op) * (size_t)hidden * sizeof(float);
 }
 
 norm_status from_hip(hipError_t e) { return e == hipSuccess ? NORM_SUCCESS : NORM_ERROR_LAUNCH; }
@@ -204,40 +216,45 @@ norm_status run_fwd(norm_op op, const FwdArgs& a, int64_t hidden, const norm_lau
     return from_hip(e->launch(a, stream));
 }
 
-norm_status run_bwd(BwdArgs a, int64_t hidden, float eps, size_t workspace_bytes,
+norm_status run_bwd(norm_op op, BwdArgs a, int64_t hidden, float eps, size_t workspace_bytes,
                     const norm_launch_cfg* cfg, hipStream_t stream) {
+    const bool ln = op == NORM_OP_LAYERNORM_BWD;
     if (a.rows < 0 || a.rows > kMaxRows || !eps_ok(eps)) return NORM_ERROR_INVALID_VALUE;
     if (cfg && (cfg->threads_per_row <= 0 || cfg->rows_per_block != 1 || cfg->grid < 0))
         return NORM_ERROR_INVALID_VALUE;
     if (!hidden_supported(hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     if (cfg && cfg->grid > max_bwd_grid(hidden)) return NORM_ERROR_INVALID_VALUE;
     const bool any = a.rows > 0;
-    if (!a.dweight || !a.dbias || !a.workspace) return NORM_ERROR_INVALID_VALUE;
-    if (any && (!a.dx || !a.dy || !a.x || !a.mean || !a.rstd || !a.weight))
+    if (!a.dweight || (ln && !a.dbias) || !a.workspace) return NORM_ERROR_INVALID_VALUE;
+    if (any && (!a.dx || !a.dy || !a.x || !a.weight || (ln && (!a.mean || !a.rstd))))
         return NORM_ERROR_INVALID_VALUE;
-    if (!aligned(a.dweight, 4) || !aligned(a.dbias, 4) || !aligned(a.workspace, 16))
+    if (!aligned(a.dweight, 4) || (ln && !aligned(a.dbias, 4)) || !aligned(a.workspace, 16))
         return NORM_ERROR_MISALIGNED;
     if (any && (!aligned(a.dx, 16) || !aligned(a.dy, 16) || !aligned(a.x, 16) ||
-                !aligned(a.weight, 16) || !aligned(a.mean, 4) || !aligned(a.rstd, 4)))
+                !aligned(a.weight, 16) || (a.dres && !aligned(a.dres, 16)) ||
+                (ln && (!aligned(a.mean, 4) || !aligned(a.rstd, 4)))))
         return NORM_ERROR_MISALIGNED;
 
-    norm_launch_cfg c = cfg ? *cfg : choose_bwd(a.rows, hidden);
+    norm_launch_cfg c = cfg ? *cfg : choose_bwd(op, a.rows, hidden);
     if (c.grid == 0) c.grid = default_bwd_grid(a.rows);
-    const BwdEntry* e = find_bwd(hidden, c.threads_per_row);
+    const BwdEntry* e = find_bwd(op, hidden, c.threads_per_row);
     if (!e) return NORM_ERROR_INVALID_VALUE;
     a.grid = c.grid;
-    const size_t ws_need = bwd_workspace_bytes(hidden, any ? c.grid : 0);
+    a.eps = eps;
+    const size_t ws_need = bwd_workspace_bytes(op, hidden, any ? c.grid : 0);
 
     const uint64_t mat = any ? (uint64_t)a.rows * (uint64_t)hidden * 2 : 0;
     const uint64_t vec = any ? (uint64_t)hidden * 2 : 0;
-    const uint64_t stat = (uint64_t)a.rows * 4;
+    const uint64_t stat = ln ? (uint64_t)a.rows * 4 : 0;
     const uint64_t col = (uint64_t)hidden * 4;
     const Span dx{a.dx, mat}, dy{a.dy, mat}, x{a.x, mat}, mean{a.mean, stat},
-        rstd{a.rstd, stat}, w{a.weight, vec}, dw{a.dweight, col}, db{a.dbias, col},
-        ws{a.workspace, ws_need};
-    const Span ins[] = {dy, x, mean, rstd, w};
+        rstd{a.rstd, stat}, dres{a.dres, a.dres ? mat : 0}, w{a.weight, vec},
+        dw{a.dweight, col}, db{a.dbias, ln ? col : 0}, ws{a.workspace, ws_need};
+    // outputs overlap no input, except dx == dy (or dx == dres) exactly
+    const Span ins[] = {dy, x, mean, rstd, dres, w};
     for (const Span& in : ins) {
-        if (bad_overlap(dx, in, in.p == a.dy)) return NORM_ERROR_INVALID_VALUE;
+        if (bad_overlap(dx, in, in.p == a.dy || (a.dres && in.p == a.dres)))
+            return NORM_ERROR_INVALID_VALUE;
         if (bad_overlap(dw, in, false) || bad_overlap(db, in, false) || bad_overlap(ws, in, false))
             return NORM_ERROR_INVALID_VALUE;
     }
@@ -314,8 +331,9 @@ norm_status norm_layernorm_bwd_cfg(void* dx, float* dweight, float* dbias, const
                                    const void* weight, void* workspace, size_t workspace_bytes,
                                    int64_t rows, int64_t hidden, float eps,
                                    const norm_launch_cfg* cfg, hipStream_t stream) {
-    BwdArgs a{dx, dy, x, mean, rstd, weight, (float*)workspace, dweight, dbias, rows, 0};
-    return run_bwd(a, hidden, eps, workspace_bytes, cfg, stream);
+    BwdArgs a{dx, dy, x, mean, rstd, nullptr, weight, (float*)workspace, dweight, dbias, rows, 0,
+              0.0f};
+    return run_bwd(NORM_OP_LAYERNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
 }
 
 norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias, const void* dy,
@@ -326,25 +344,70 @@ norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias, const voi
                                   workspace_bytes, rows, hidden, eps, nullptr, stream);
 }
 
+norm_status norm_rmsnorm_bwd_cfg(void* dx, float* dweight, const void* dy, const void* x,
+                                 const void* weight, void* workspace, size_t workspace_bytes,
+                                 int64_t rows, int64_t hidden, float eps,
+                                 const norm_launch_cfg* cfg, hipStream_t stream) {
+    BwdArgs a{dx, dy, x, nullptr, nullptr, nullptr, weight, (float*)workspace, dweight, nullptr,
+              rows, 0, 0.0f};
+    return run_bwd(NORM_OP_RMSNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
+}
+
+norm_status norm_rmsnorm_bwd(void* dx, float* dweight, const void* dy, const void* x,
+                             const void* weight, void* workspace, size_t workspace_bytes,
+                             int64_t rows, int64_t hidden, float eps, hipStream_t stream) {
+    return norm_rmsnorm_bwd_cfg(dx, dweight, dy, x, weight, workspace, workspace_bytes, rows,
+                                hidden, eps, nullptr, stream);
+}
+
+norm_status norm_fused_add_rmsnorm_bwd_cfg(void* ds, float* dweight, const void* dout,
+                                           const void* dres, const void* s, const void* weight,
+                                           void* workspace, size_t workspace_bytes, int64_t rows,
+                                           int64_t hidden, float eps, const norm_launch_cfg* cfg,
+                                           hipStream_t stream) {
+    BwdArgs a{ds, dout, s, nullptr, nullptr, dres, weight, (float*)workspace, dweight, nullptr,
+              rows, 0, 0.0f};
+    return run_bwd(NORM_OP_FUSED_ADD_RMSNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
+}
+
+norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const void* dout,
+                                       const void* dres, const void* s, const void* weight,
+                                       void* workspace, size_t workspace_bytes, int64_t rows,
+                                       int64_t hidden, float eps, hipStream_t stream) {
+    return norm_fused_add_rmsnorm_bwd_cfg(ds, dweight, dout, dres, s, weight, workspace,
+                                          workspace_bytes, rows, hidden, eps, nullptr, stream);
+}
+
+static size_t ws_bytes_for(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg* cfg) {
+    if (rows <= 0 || !hidden_supported(hidden)) return 0;
+    const int32_t g = (cfg && cfg->grid > 0) ? cfg->grid : default_bwd_grid(rows);
+    return bwd_workspace_bytes(op, hidden, g);
+}
+
 size_t norm_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
-    if (rows < 0 || !hidden_supported(hidden)) return 0;
-    return bwd_workspace_bytes(hidden, rows > 0 ? default_bwd_grid(rows) : 0);
+    return ws_bytes_for(NORM_OP_LAYERNORM_BWD, rows, hidden, nullptr);
 }
 
 size_t norm_layernorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                               const norm_launch_cfg* cfg) {
-    if (rows < 0 || !hidden_supported(hidden)) return 0;
-    if (rows == 0) return 0;
-    const int32_t g = (cfg && cfg->grid > 0) ? cfg->grid : default_bwd_grid(rows);
-    return bwd_workspace_bytes(hidden, g);
+    return ws_bytes_for(NORM_OP_LAYERNORM_BWD, rows, hidden, cfg);
+}
+
+size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
+    return ws_bytes_for(NORM_OP_RMSNORM_BWD, rows, hidden, nullptr);
+}
+
+size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
+                                            const norm_launch_cfg* cfg) {
+    return ws_bytes_for(NORM_OP_RMSNORM_BWD, rows, hidden, cfg);
 }
 
 norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
                                norm_launch_cfg* cfg) {
-    if (!cfg || rows < 0 || (int)op < 0 || (int)op > 3) return NORM_ERROR_INVALID_VALUE;
+    if (!cfg || rows < 0 || (int)op < 0 || (int)op > 5) return NORM_ERROR_INVALID_VALUE;
     if (!hidden_supported(hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
-    if (op == NORM_OP_LAYERNORM_BWD) {
-        *cfg = choose_bwd(rows, hidden);
+    if (is_bwd(op)) {
+        *cfg = choose_bwd(op, rows, hidden);
         return NORM_SUCCESS;
     }
     int cu = cu_count;
@@ -358,24 +421,27 @@ norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden, int32_t
 
 int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
                              char* buf, size_t len) {
-    static const char* const kNames[] = {"fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd",
-                                         "layernorm_bwd"};
+    static const char* const kNames[] = {"fused_add_rmsnorm", "rmsnorm_fwd",  "layernorm_fwd",
+                                         "layernorm_bwd",     "rmsnorm_bwd", "fused_add_rmsnorm_bwd"};
     norm_launch_cfg c;
     if (norm_select_config(op, rows, hidden, cu_count, &c) != NORM_SUCCESS) return -1;
     const int vecs = (int)(hidden / (8 * c.threads_per_row));
     char tmp[512];
     int n;
-    if (op == NORM_OP_LAYERNORM_BWD) {
+    if (is_bwd(op)) {
+        const int depth = bwd_depth_of(op, hidden, c.threads_per_row);
         n = std::snprintf(tmp, sizeof tmp,
-                          "%s rows=%lld hidden=%lld: layernorm_bwd_rows_kernel<%lld,%d,%d> "
+                          "%s rows=%lld hidden=%lld: %s_bwd_rows_kernel<%lld,%d,%d%s> "
                           "(%d lanes per row, %d vectors per lane, ring of %d rows) on a "
-                          "persistent grid of %d workgroups, then layernorm_bwd_colreduce_kernel "
+                          "persistent grid of %d workgroups, then norm_bwd_colreduce_kernel "
                           "(%lld workgroups of %d); workspace %zu bytes",
-                          kNames[op], (long long)rows, (long long)hidden, (long long)hidden,
-                          c.threads_per_row, bwd_depth_of(hidden, c.threads_per_row),
-                          c.threads_per_row, vecs, bwd_depth_of(hidden, c.threads_per_row),
-                          c.grid, (long long)(2 * hidden / kColReduceCols), kColReduceThreads,
-                          bwd_workspace_bytes(hidden, rows > 0 ? c.grid : 0));
+                          kNames[op], (long long)rows, (long long)hidden,
+                          op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm",
+                          (long long)hidden, c.threads_per_row, depth,
+                          op == NORM_OP_LAYERNORM_BWD ? "" : ",dres?", c.threads_per_row, vecs,
+                          depth, c.grid,
+                          (long long)(bwd_outs(op) * hidden / kColReduceCols), kColReduceThreads,
+                          bwd_workspace_bytes(op, hidden, rows > 0 ? c.grid : 0));
     } else {
         const char* kern = op == NORM_OP_FUSED_ADD_RMSNORM ? "fused_add_rmsnorm_kernel"
                            : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd_kernel"
@@ -400,9 +466,9 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
 
 int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int32_t capacity) {
     int32_t n = 0;
-    if ((int)op < 0 || (int)op > 3) return 0;
-    if (op == NORM_OP_LAYERNORM_BWD) {
-        for (const BwdEntry& e : layernorm_bwd_table()) {
+    if ((int)op < 0 || (int)op > 5) return 0;
+    if (is_bwd(op)) {
+        for (const BwdEntry& e : bwd_table(op)) {
             if (e.hidden != hidden) continue;
             if (out && n < capacity) out[n] = norm_launch_cfg{e.lanes, 1, 0};
             ++n;

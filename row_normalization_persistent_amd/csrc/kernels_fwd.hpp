@@ -221,14 +221,16 @@ __global__ __launch_bounds__(T * R) void layernorm_fwd_kernel(
 // ---------------------------------------------------------------------------
 // Launchers and the compile-time shape lists.
 // ---------------------------------------------------------------------------
+// Widest per-lane row buffer compiled: what stays within a lane's 256 VGPRs
+// without spills on gfx950 (row vectors plus the weight, and bias, vectors).
 struct OpFused {
-    static constexpr int kMaxVecs = 16;  // x and r held: 8 VGPRs per vector
+    static constexpr int kMaxVecs = 16;  // x, r, w: 12 VGPRs per vector
 };
 struct OpRms {
-    static constexpr int kMaxVecs = 32;  // x held: 4 VGPRs per vector
+    static constexpr int kMaxVecs = 16;  // x, w: 8 VGPRs per vector
 };
 struct OpLnFwd {
-    static constexpr int kMaxVecs = 32;
+    static constexpr int kMaxVecs = 12;  // x, w, b: 12 VGPRs per vector
 };
 
 template <class Op, int H, int T, int R>

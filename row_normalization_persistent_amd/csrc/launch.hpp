@@ -26,17 +26,19 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-    void* dx;
-    const void* dy;
-    const void* x;
-    const float* mean;
-    const float* rstd;
+    void* dx;              // RMSNorm-fused: the gradient of x and of the residual input
+    const void* dy;        // RMSNorm-fused: the gradient of out
+    const void* x;         // RMSNorm-fused: s, the residual output of the forward
+    const float* mean;     // LayerNorm only
+    const float* rstd;     // LayerNorm only
+    const void* dres;      // RMSNorm-fused only: gradient of the residual output, or null
     const void* weight;
-    float* workspace;      // [grid][2][hidden] fp32 partial column sums
+    float* workspace;      // [grid][outs][hidden] fp32 partial column sums
     float* dweight;
-    float* dbias;
+    float* dbias;          // LayerNorm only
     int64_t rows;
     int32_t grid;
+    float eps;             // RMSNorm only (the statistic is recomputed)
 };
 
 using FwdLauncher = hipError_t (*)(const FwdArgs&, hipStream_t);
@@ -57,6 +59,7 @@ const std::vector<FwdEntry>& fused_add_rmsnorm_table();
 const std::vector<FwdEntry>& rmsnorm_fwd_table();
 const std::vector<FwdEntry>& layernorm_fwd_table();
 const std::vector<BwdEntry>& layernorm_bwd_table();
+const std::vector<BwdEntry>& rmsnorm_bwd_table();
 
 // Column-reduce geometry of LayerNorm backward.
 constexpr int kColReduceThreads = 256;

@@ -14,6 +14,9 @@ a fixed order, then bf16 rounding):
 * LayerNorm forward: x ~ N(0.5, 2); w ~ N(1, 0.1); b ~ N(0, 0.1); eps = fp32(1e-5)
 * LayerNorm backward: x, dy ~ N(0, 1); w ~ N(1, 0.1); the per-row mean/rstd are
   computed by the caller from x with eps = fp32(1e-5)
+* RMSNorm backward (and the fused residual-add + RMSNorm backward): x, dy ~ N(0, 1);
+  w ~ N(1, 0.1); dres ~ N(0, 1) (gradient of the fused op's residual output);
+  eps = fp32(1e-6)
 
 ``N(m, s)`` means mean m and standard deviation s.
 """
@@ -34,6 +37,8 @@ LAYERNORM_FWD_HIDDEN = (1024, 4096, 12288, 16384)
 LAYERNORM_FWD_ROWS = 2048
 LAYERNORM_BWD_HIDDEN = (4096, 8192)
 LAYERNORM_BWD_ROWS = 8192
+RMSNORM_BWD_HIDDEN = (4096, 8192)
+RMSNORM_BWD_ROWS = 8192
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -84,6 +89,16 @@ def layernorm_bwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
     dy = _normal(rng, (rows, hidden), 0.0, 1.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
     return {"x": bf16_bits(x), "dy": bf16_bits(dy), "w": bf16_bits(w), "eps": EPS_LN}
+
+
+def rmsnorm_bwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (rows, hidden), 0.0, 1.0)
+    dy = _normal(rng, (rows, hidden), 0.0, 1.0)
+    w = _normal(rng, (hidden,), 1.0, 0.1)
+    dres = _normal(rng, (rows, hidden), 0.0, 1.0)
+    return {"x": bf16_bits(x), "dy": bf16_bits(dy), "w": bf16_bits(w), "dres": bf16_bits(dres),
+            "eps": EPS_RMS}
 
 
 def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:

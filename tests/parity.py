@@ -106,3 +106,16 @@ def layernorm_dx_scale(xd, dyd, wd, mean, rstd):
     return rstd[:, None] * (np.abs(g) + np.abs(c1) + np.abs(xhat) * np.abs(c2)
                             + np.abs(g).mean(axis=1, keepdims=True)
                             + np.abs(xhat) * np.abs(gx).mean(axis=1, keepdims=True))
+
+
+def rmsnorm_dx_scale(xd, dyd, wd, rstd, dresd=None):
+    """M for RMSNorm dx: rstd (|g| + |xhat||c| + |xhat| mean|g xhat|) [+ |dres|]."""
+    xhat = xd * rstd[:, None]
+    g = dyd * wd
+    gx = g * xhat
+    c = gx.mean(axis=1, keepdims=True)
+    m = rstd[:, None] * (np.abs(g) + np.abs(xhat) * np.abs(c)
+                         + np.abs(xhat) * np.abs(gx).mean(axis=1, keepdims=True))
+    if dresd is not None:
+        m = m + np.abs(dresd)
+    return m

@@ -26,9 +26,9 @@ def declared_functions():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
-               "norm_layernorm_bwd"):
+               "norm_layernorm_bwd", "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd"):
         assert op in names
-    assert len(names) == 14
+    assert len(names) == 20
 
 
 def test_library_exports_every_declared_symbol():
@@ -108,6 +108,9 @@ def test_describe_config():
 
 def test_workspace_bytes():
     for h in rn.HIDDEN_SIZES:
+        g = rn.select_config("rmsnorm_bwd", 8192, h).grid
+        assert rn.workspace_bytes(8192, h, op="rmsnorm_bwd") == g * h * 4  # one slab
+        assert rn.workspace_bytes(8192, h, op="fused_add_rmsnorm_bwd") == g * h * 4
         c = rn.select_config("layernorm_bwd", 8192, h)
         assert rn.workspace_bytes(8192, h) == c.grid * 2 * h * 4
         assert rn.workspace_bytes(3, h) == 3 * 2 * h * 4  # never more slabs than rows
@@ -225,3 +228,34 @@ def test_python_binding_rejects_bad_tensors():
         rn.fused_add_rmsnorm(x, x.clone(), w, 1e-6)
     with pytest.raises(TypeError):
         rn.rmsnorm_fwd(x.float(), w, 1e-6)
+
+
+def rmsb(dx=A, dw=A + GB, dy=A + 2 * GB, x=A + 3 * GB, w=A + 5 * GB, ws=A + 6 * GB,
+         ws_bytes=None, rows=8192, hidden=4096, eps=1e-6, dres=None, cfg=None):
+    if ws_bytes is None:
+        ws_bytes = rn.workspace_bytes(rows, hidden, op="rmsnorm_bwd") - 4
+    if dres is None:
+        return rn.lib().norm_rmsnorm_bwd_cfg(dx, dw, dy, x, w, ws, ws_bytes, rows, hidden, eps,
+                                             cfg, None)
+    return rn.lib().norm_fused_add_rmsnorm_bwd_cfg(dx, dw, dy, dres, x, w, ws, ws_bytes, rows,
+                                                   hidden, eps, cfg, None)
+
+
+def test_rmsnorm_bwd_validation():
+    assert rmsb() == WORKSPACE  # everything else valid: proves the order of checks
+    assert rmsb(dres=A + 4 * GB) == WORKSPACE
+    assert rmsb(rows=-1) == INVALID
+    assert rmsb(eps=-1.0) == INVALID
+    assert rmsb(eps=float("nan")) == INVALID
+    assert rmsb(hidden=4095) == UNSUPPORTED
+    assert rmsb(dw=0) == INVALID
+    assert rmsb(x=0) == INVALID
+    assert rmsb(dy=A + 2 * GB + 8) == MISALIGNED
+    assert rmsb(dres=A + 4 * GB + 8) == MISALIGNED
+    assert rmsb(dx=A + 2 * GB) == WORKSPACE                 # dx == dy allowed
+    assert rmsb(dx=A + 4 * GB, dres=A + 4 * GB) == WORKSPACE  # ds == dres allowed
+    assert rmsb(dx=A + 3 * GB) == INVALID                   # dx == x is not
+    assert rmsb(dx=A + 2 * GB + 16) == INVALID
+    assert rmsb(ws=A + 1 * GB + 64) == INVALID              # workspace over dweight
+    assert rmsb(cfg=ctypes.byref(rn.LaunchCfg(512, 1, 4)),
+                ws_bytes=4 * 4096 * 4 - 1) == WORKSPACE
