@@ -5,17 +5,33 @@
  * Every operation normalizes the rows of a row-major [rows, hidden] bf16
  * matrix.  Each row is read from HBM once into registers, reduced there, and
  * written once ("inner persistent": the row stays on-chip between the
- * reduction and the normalize step).  The hidden size is a compile-time
- * constant of the kernel that runs; the supported set is
- *     {1024, 2048, 4096, 8192, 12288, 16384}.
+ * reduction and the normalize step).  Two kernel families do the work:
+ *   - compiled-hidden kernels, where hidden is a template constant ("optimize
+ *     inner persistent scheduler for static fusion", author description: the
+ *     hidden size of a model is static), for hidden in
+ *         {1024, 2048, 4096, 8192, 12288, 16384}
+ *     with contiguous rows and 16-byte-aligned bf16 pointers;
+ *   - run-time-hidden kernels for everything else (the non-static path of the
+ *     same page, reviewer guide, split logic): any hidden >= 1, row strides,
+ *     and bf16 pointers aligned to 2 bytes or more.  Rows are read with the
+ *     widest access (16, 8, 4 or 2 bytes) that hidden, every row stride and
+ *     every bf16 pointer allow.  Largest hidden: forward 65536 (LayerNorm
+ *     49152) with 16-byte accesses, 8192 * (access elements) otherwise;
+ *     backward 16384 with 16- or 8-byte accesses, 8192 otherwise.
+ * The library picks the family; the arithmetic and results (within rounding)
+ * are the same.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Tensors are DEVICE pointers into memory of the calling thread's current
- *   HIP device, row-major and contiguous: element (i, j) of a [rows, hidden]
- *   matrix sits at index i * hidden + j.  bf16 tensors are passed as
- *   void* / const void* holding IEEE bf16 bit patterns and must be 16-byte
- *   aligned; fp32 tensors must be 4-byte aligned.
+ *   HIP device.  Matrices are row-major with unit column stride: element
+ *   (i, j) of a [rows, hidden] matrix sits at index i * ld + j, where ld (the
+ *   leading dimension, in elements, ld >= hidden) is `hidden` for the entry
+ *   points without an ld argument and given explicitly to the `_ex` entry
+ *   points.  bf16 tensors are passed as void* / const void* holding IEEE bf16
+ *   bit patterns and must be 2-byte aligned (16-byte aligned for a
+ *   `norm_launch_cfg` that names a compiled-hidden shape); fp32 tensors must
+ *   be 4-byte aligned; the backward workspace 16-byte aligned.
  * - Ownership: the caller allocates and frees every buffer (workspace
  *   included).  The library never allocates, frees, or keeps a pointer past
  *   the call.  Its only state is a per-device cache of the compute-unit count.
@@ -27,13 +43,15 @@
  *   enqueued when the code is not NORM_SUCCESS.  Argument checks run before
  *   any HIP call, in this order: rows < 0 / bad eps / bad config ->
  *   INVALID_VALUE; then, for the forward ops, rows == 0 -> SUCCESS with
- *   nothing enqueued; hidden not supported -> UNSUPPORTED_HIDDEN; null
- *   pointer -> INVALID_VALUE; misaligned pointer -> MISALIGNED; buffers that
- *   overlap other than by an allowed exact alias -> INVALID_VALUE; workspace
- *   too small -> WORKSPACE.  LayerNorm backward with rows == 0 enqueues only
- *   the zero-fill of dweight and dbias.  Choosing a launch shape may query
- *   the current device once (DEVICE on failure).  A launch failure reported
- *   by HIP returns LAUNCH.
+ *   nothing enqueued; hidden < 1 or beyond every kernel -> UNSUPPORTED_HIDDEN;
+ *   null pointer or ld < hidden -> INVALID_VALUE; misaligned pointer ->
+ *   MISALIGNED; buffers that overlap other than by an allowed exact alias ->
+ *   INVALID_VALUE (two matrices with the same ld whose rows interleave
+ *   without sharing an element, such as two column slices of one wider
+ *   matrix, do not overlap); workspace too small -> WORKSPACE.  The backward
+ *   ops with rows == 0 enqueue only the zero-fill of dweight (and dbias).
+ *   Choosing a launch shape may query the current device once (DEVICE on
+ *   failure).  A launch failure reported by HIP returns LAUNCH.
  * - Arithmetic: bf16 inputs are widened exactly to fp32, every sum and product
  *   is fp32, every bf16 store rounds to nearest-even, rstd uses the hardware
  *   reciprocal square root.
@@ -68,8 +86,8 @@ extern "C" {
 typedef enum {
     NORM_SUCCESS = 0,
     NORM_ERROR_INVALID_VALUE = 1,      /* bad rows/eps/pointer/overlap/config */
-    NORM_ERROR_UNSUPPORTED_HIDDEN = 2, /* hidden not in the compiled set       */
-    NORM_ERROR_MISALIGNED = 3,         /* bf16 ptr not 16 B, fp32 ptr not 4 B  */
+    NORM_ERROR_UNSUPPORTED_HIDDEN = 2, /* no kernel holds a row this wide      */
+    NORM_ERROR_MISALIGNED = 3,         /* pointer alignment too small           */
     NORM_ERROR_WORKSPACE = 4,          /* LayerNorm-backward workspace too small */
     NORM_ERROR_LAUNCH = 5,             /* HIP reported an error at launch       */
     NORM_ERROR_DEVICE = 6              /* the current device could not be queried */
@@ -85,18 +103,27 @@ typedef enum {
 } norm_op;
 
 /* Launch shape of one kernel instantiation.
- *   threads_per_row : lanes that share one row (a multiple of 64, the wave
- *                     size); hidden / (8 * threads_per_row) 16-byte vectors
- *                     of the row live in each lane's registers.
- *   rows_per_block  : rows handled side by side by one workgroup
- *                     (workgroup size = threads_per_row * rows_per_block).
- *   grid            : backward ops only: number of persistent workgroups (one
- *                     partial column-sum slab each); 0 lets the library
- *                     choose.  Must be 0 for the forward ops. */
+ *   threads_per_row : lanes that share one row.  Compiled-hidden shapes: a
+ *                     multiple of 64 (the wave size); hidden / (8 * lanes)
+ *                     16-byte vectors of the row live in each lane's
+ *                     registers.  Run-time-hidden shapes: 8, 16, ..., 1024
+ *                     (rows narrower than a wave share it).
+ *   rows_per_block  : rows handled side by side by one workgroup.  Run-time
+ *                     shapes: max(1, 256 / threads_per_row), workgroups of
+ *                     max(256, threads_per_row) lanes.
+ *   grid            : backward ops only: number of persistent workgroups; 0
+ *                     lets the library choose.  Each row group of a workgroup
+ *                     writes one partial column-sum slab.  Must be 0 for the
+ *                     forward ops.
+ *   vector_elems    : 0 for a compiled-hidden shape; 1, 2, 4 or 8 for a
+ *                     run-time-hidden shape whose accesses move that many
+ *                     bf16 elements (hidden, every ld and every bf16 pointer
+ *                     must allow it). */
 typedef struct {
     int32_t threads_per_row;
     int32_t rows_per_block;
     int32_t grid;
+    int32_t vector_elems;
 } norm_launch_cfg;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -183,25 +210,27 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const 
                                                 size_t workspace_bytes, int64_t rows,
                                                 int64_t hidden, float eps, hipStream_t stream);
 
-/* Bytes of workspace the two RMSNorm backward ops need (library's launch
- * choice, or a given shape).  Pure host arithmetic; 0 for an unsupported
- * hidden or rows <= 0. */
+/* Bytes of workspace the two RMSNorm backward ops need: with the library's
+ * choice, enough for any layout (strides, alignment) of this hidden size; or
+ * for a given shape.  Pure host arithmetic; 0 for an unsupported hidden or
+ * rows <= 0. */
 NORM_API size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 NORM_API size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                                      const norm_launch_cfg* cfg);
 
 /* Bytes of workspace norm_layernorm_bwd needs for (rows, hidden) with the
- * library's own launch choice.  Pure host arithmetic (no HIP call); returns 0
- * for an unsupported hidden or rows < 0. */
+ * library's own launch choice, for any layout (strides, alignment) of this
+ * hidden size.  Pure host arithmetic (no HIP call); returns 0 for an
+ * unsupported hidden or rows <= 0. */
 NORM_API size_t norm_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 
 /* Bytes of workspace a given LayerNorm-backward launch shape needs. */
 NORM_API size_t norm_layernorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                               const norm_launch_cfg* cfg);
 
-/* Variants of the four operations that run a given compiled launch shape
- * instead of the library's choice (cfg == NULL means the library's choice).
- * A shape that was not compiled for (op, hidden) returns INVALID_VALUE. */
+/* Variants of the operations that run a given launch shape instead of the
+ * library's choice (cfg == NULL means the library's choice).  A shape that
+ * was not compiled for (op, hidden) returns INVALID_VALUE. */
 NORM_API norm_status norm_fused_add_rmsnorm_cfg(void* out, void* residual, const void* x,
                                        const void* weight, int64_t rows, int64_t hidden,
                                        float eps, const norm_launch_cfg* cfg,
@@ -232,11 +261,58 @@ NORM_API norm_status norm_layernorm_bwd_cfg(void* dx, float* dweight, float* dbi
                                    int64_t rows, int64_t hidden, float eps,
                                    const norm_launch_cfg* cfg, hipStream_t stream);
 
+/* Strided variants ("_ex"): every matrix argument is followed by its leading
+ * dimension (row stride in elements, >= hidden), so rows may be slices of
+ * wider matrices (for instance the query or key part of a fused projection
+ * output); `cfg` as for the "_cfg" variants (NULL: the library's choice).
+ * Semantics, aliasing rules and errors are those of the operation without
+ * the suffix; an exact alias also needs equal leading dimensions. */
+NORM_API norm_status norm_fused_add_rmsnorm_ex(void* out, int64_t ld_out, void* residual,
+                                               int64_t ld_residual, const void* x, int64_t ld_x,
+                                               const void* weight, int64_t rows, int64_t hidden,
+                                               float eps, const norm_launch_cfg* cfg,
+                                               hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_fwd_ex(void* out, int64_t ld_out, const void* x, int64_t ld_x,
+                                         const void* weight, int64_t rows, int64_t hidden,
+                                         float eps, const norm_launch_cfg* cfg,
+                                         hipStream_t stream);
+NORM_API norm_status norm_layernorm_fwd_ex(void* y, int64_t ld_y, float* mean, float* rstd,
+                                           const void* x, int64_t ld_x, const void* weight,
+                                           const void* bias, int64_t rows, int64_t hidden,
+                                           float eps, const norm_launch_cfg* cfg,
+                                           hipStream_t stream);
+NORM_API norm_status norm_layernorm_bwd_ex(void* dx, int64_t ld_dx, float* dweight, float* dbias,
+                                           const void* dy, int64_t ld_dy, const void* x,
+                                           int64_t ld_x, const float* mean, const float* rstd,
+                                           const void* weight, void* workspace,
+                                           size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                           float eps, const norm_launch_cfg* cfg,
+                                           hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_bwd_ex(void* dx, int64_t ld_dx, float* dweight, const void* dy,
+                                         int64_t ld_dy, const void* x, int64_t ld_x,
+                                         const void* weight, void* workspace,
+                                         size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                         float eps, const norm_launch_cfg* cfg,
+                                         hipStream_t stream);
+/* ld_dres is ignored when dres is NULL. */
+NORM_API norm_status norm_fused_add_rmsnorm_bwd_ex(void* ds, int64_t ld_ds, float* dweight,
+                                                   const void* dout, int64_t ld_dout,
+                                                   const void* dres, int64_t ld_dres,
+                                                   const void* s, int64_t ld_s,
+                                                   const void* weight, void* workspace,
+                                                   size_t workspace_bytes, int64_t rows,
+                                                   int64_t hidden, float eps,
+                                                   const norm_launch_cfg* cfg,
+                                                   hipStream_t stream);
+
 /* The library's launch choice for (op, rows, hidden) on a device with
  * `cu_count` compute units (the small-batch rule of "optimize inner
  * persistent scheduler for static fusion", author description: when the
  * batch cannot fill the machine, spread each row over more lanes).
- * cu_count <= 0 queries the current device.  Pure host logic otherwise. */
+ * cu_count <= 0 queries the current device.  Pure host logic otherwise.
+ * The choice assumes contiguous rows and 16-byte-aligned pointers; a call
+ * with strides or smaller alignment may run a run-time-hidden shape with
+ * narrower accesses instead. */
 NORM_API norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden,
                                int32_t cu_count, norm_launch_cfg* cfg);
 
@@ -251,9 +327,11 @@ NORM_API norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden
 NORM_API int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden,
                                       int32_t cu_count, char* buf, size_t len);
 
-/* Enumerate the compiled launch shapes of (op, hidden): writes up to
- * `capacity` entries to `out` (which may be NULL when capacity is 0) and
- * returns the total count; 0 for an unsupported hidden. */
+/* Enumerate the launch shapes that can run (op, hidden): the compiled-hidden
+ * shapes (when hidden is compiled), then the run-time-hidden shapes at the
+ * widest access width hidden allows.  Writes up to `capacity` entries to
+ * `out` (which may be NULL when capacity is 0) and returns the total count;
+ * 0 for an unsupported hidden. */
 NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out,
                           int32_t capacity);
 

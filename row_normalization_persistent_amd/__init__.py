@@ -27,6 +27,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librownorm.so")
 
+# hidden sizes of the compiled-hidden kernels; any other hidden runs on the
+# run-time-hidden kernels
 HIDDEN_SIZES = (1024, 2048, 4096, 8192, 12288, 16384)
 
 OP_FUSED_ADD_RMSNORM = 0
@@ -57,24 +59,32 @@ class NormError(RuntimeError):
 
 class LaunchCfg(ctypes.Structure):
     _fields_ = [("threads_per_row", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
-                ("grid", ctypes.c_int32)]
+                ("grid", ctypes.c_int32), ("vector_elems", ctypes.c_int32)]
 
     def astuple(self):
-        return (self.threads_per_row, self.rows_per_block, self.grid)
+        return (self.threads_per_row, self.rows_per_block, self.grid, self.vector_elems)
 
     def __repr__(self):
         return (f"LaunchCfg(threads_per_row={self.threads_per_row}, "
-                f"rows_per_block={self.rows_per_block}, grid={self.grid})")
+                f"rows_per_block={self.rows_per_block}, grid={self.grid}, "
+                f"vector_elems={self.vector_elems})")
 
 
 @dataclass(frozen=True)
 class Cfg:
+    """A launch shape.  vector_elems == 0: a compiled-hidden shape; 1, 2, 4, 8:
+    a run-time-hidden shape with accesses of that many bf16 elements."""
     threads_per_row: int
     rows_per_block: int = 1
     grid: int = 0
+    vector_elems: int = 0
+
+    @property
+    def runtime_hidden(self) -> bool:
+        return self.vector_elems != 0
 
     def c(self) -> LaunchCfg:
-        return LaunchCfg(self.threads_per_row, self.rows_per_block, self.grid)
+        return LaunchCfg(self.threads_per_row, self.rows_per_block, self.grid, self.vector_elems)
 
 
 _lib = None
@@ -95,30 +105,42 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     L.norm_status_string.argtypes = [ctypes.c_int]
     L.norm_status_string.restype = ctypes.c_char_p
-    L.norm_fused_add_rmsnorm_cfg.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp]
-    L.norm_rmsnorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp]
-    L.norm_layernorm_fwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp,
-                                         _vp]
-    L.norm_layernorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                         ctypes.c_size_t, _i64, _i64, _f32, _cfgp, _vp]
-    L.norm_fused_add_rmsnorm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]
-    L.norm_rmsnorm_fwd.argtypes = [_vp, _vp, _vp, _i64, _i64, _f32, _vp]
-    L.norm_layernorm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]
-    L.norm_layernorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                     ctypes.c_size_t, _i64, _i64, _f32, _vp]
-    L.norm_rmsnorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
-                                       _f32, _cfgp, _vp]
-    L.norm_rmsnorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i64, _i64,
-                                   _f32, _vp]
-    L.norm_fused_add_rmsnorm_bwd_cfg.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                                 ctypes.c_size_t, _i64, _i64, _f32, _cfgp, _vp]
-    L.norm_fused_add_rmsnorm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
-                                             _i64, _i64, _f32, _vp]
-    for n in ("norm_fused_add_rmsnorm_cfg", "norm_rmsnorm_fwd_cfg", "norm_layernorm_fwd_cfg",
-              "norm_layernorm_bwd_cfg", "norm_fused_add_rmsnorm", "norm_rmsnorm_fwd",
-              "norm_layernorm_fwd", "norm_layernorm_bwd", "norm_rmsnorm_bwd_cfg",
-              "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd_cfg", "norm_fused_add_rmsnorm_bwd"):
-        getattr(L, n).restype = ctypes.c_int
+    _sz = ctypes.c_size_t
+    sigs = {
+        "norm_fused_add_rmsnorm_cfg": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp],
+        "norm_rmsnorm_fwd_cfg": [_vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp],
+        "norm_layernorm_fwd_cfg": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _cfgp, _vp],
+        "norm_layernorm_bwd_cfg": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64,
+                                   _f32, _cfgp, _vp],
+        "norm_fused_add_rmsnorm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_rmsnorm_fwd": [_vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_layernorm_fwd": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_layernorm_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64,
+                               _f32, _vp],
+        "norm_rmsnorm_bwd_cfg": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _f32, _cfgp,
+                                 _vp],
+        "norm_rmsnorm_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _f32, _vp],
+        "norm_fused_add_rmsnorm_bwd_cfg": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64,
+                                           _f32, _cfgp, _vp],
+        "norm_fused_add_rmsnorm_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _f32,
+                                       _vp],
+        # strided variants: every matrix pointer is followed by its leading dimension
+        "norm_fused_add_rmsnorm_ex": [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _f32,
+                                      _cfgp, _vp],
+        "norm_rmsnorm_fwd_ex": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _f32, _cfgp, _vp],
+        "norm_layernorm_fwd_ex": [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _f32,
+                                  _cfgp, _vp],
+        "norm_layernorm_bwd_ex": [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp,
+                                  _sz, _i64, _i64, _f32, _cfgp, _vp],
+        "norm_rmsnorm_bwd_ex": [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _sz, _i64, _i64,
+                                _f32, _cfgp, _vp],
+        "norm_fused_add_rmsnorm_bwd_ex": [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                          _vp, _sz, _i64, _i64, _f32, _cfgp, _vp],
+    }
+    for n, args in sigs.items():
+        fn = getattr(L, n)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
     L.norm_rmsnorm_bwd_workspace_bytes.argtypes = [_i64, _i64]
     L.norm_rmsnorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.norm_rmsnorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
@@ -160,16 +182,45 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _mat(t: torch.Tensor, name: str, dtype=torch.bfloat16) -> torch.Tensor:
+def _tensor(t, name: str, dtype=torch.bfloat16) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _mat(t, name: str, dtype=torch.bfloat16) -> torch.Tensor:
+    """A contiguous device tensor."""
+    _tensor(t, name, dtype)
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _rows(t, name: str, hidden: int | None = None, dtype=torch.bfloat16):
+    """A [..., hidden] bf16 device tensor viewed as rows: returns (rows,
+    hidden, ld), ld the row stride in elements.  The last dimension must be
+    unit-stride and the leading dimensions must collapse to one stride (any
+    contiguous tensor, a column slice of a wider matrix, ...)."""
+    _tensor(t, name, dtype)
+    if t.dim() < 1:
+        raise ValueError(f"{name} must have a hidden dimension")
+    h = t.shape[-1]
+    if hidden is not None and h != hidden:
+        raise ValueError(f"{name} must have hidden={hidden} columns, got {h}")
+    rows = t.numel() // h if h else 0
+    if t.is_contiguous() or rows <= 1:
+        return rows, h, h
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a unit stride along its last dimension")
+    try:
+        v = t.view(rows, h)
+    except RuntimeError as e:
+        raise ValueError(f"{name}: leading dimensions do not collapse to one row stride") from e
+    return rows, h, v.stride(0)
 
 
 def _rows_hidden(x: torch.Tensor):
@@ -187,33 +238,39 @@ def _vec(t, hidden, name, dtype=torch.bfloat16):
     return t
 
 
+def _like(t, out, name):
+    """`out` (validated, shape of t, any row stride) or a new contiguous tensor."""
+    if out is None:
+        return torch.empty(t.shape, dtype=t.dtype, device=t.device)
+    if out.shape != t.shape:
+        raise ValueError(f"{name} must have shape {tuple(t.shape)}")
+    return out
+
+
 def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, stream=None):
-    """residual <- bf16(x + residual) in place; returns (out, residual)."""
-    _mat(x, "x")
-    _mat(residual, "residual")
-    rows, hidden = _rows_hidden(x)
+    """residual <- bf16(x + residual) in place; returns (out, residual).
+    x, residual and out may be row-strided views (e.g. column slices)."""
+    rows, hidden, ld_x = _rows(x, "x")
     if residual.shape != x.shape:
         raise ValueError("residual must have x's shape")
+    _, _, ld_r = _rows(residual, "residual")
     _vec(weight, hidden, "weight")
-    out = torch.empty_like(x) if out is None else _mat(out, "out")
-    if out.shape != x.shape:
-        raise ValueError("out must have x's shape")
-    _check(lib().norm_fused_add_rmsnorm_cfg(out.data_ptr(), residual.data_ptr(), x.data_ptr(),
-                                            weight.data_ptr(), rows, hidden, float(eps),
-                                            _cfg_ptr(cfg), _stream(stream)),
+    out = _like(x, out, "out")
+    _, _, ld_o = _rows(out, "out")
+    _check(lib().norm_fused_add_rmsnorm_ex(out.data_ptr(), ld_o, residual.data_ptr(), ld_r,
+                                           x.data_ptr(), ld_x, weight.data_ptr(), rows, hidden,
+                                           float(eps), _cfg_ptr(cfg), _stream(stream)),
            "norm_fused_add_rmsnorm")
     return out, residual
 
 
 def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None):
-    _mat(x, "x")
-    rows, hidden = _rows_hidden(x)
+    rows, hidden, ld_x = _rows(x, "x")
     _vec(weight, hidden, "weight")
-    out = torch.empty_like(x) if out is None else _mat(out, "out")
-    if out.shape != x.shape:
-        raise ValueError("out must have x's shape")
-    _check(lib().norm_rmsnorm_fwd_cfg(out.data_ptr(), x.data_ptr(), weight.data_ptr(), rows,
-                                      hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
+    out = _like(x, out, "out")
+    _, _, ld_o = _rows(out, "out")
+    _check(lib().norm_rmsnorm_fwd_ex(out.data_ptr(), ld_o, x.data_ptr(), ld_x, weight.data_ptr(),
+                                     rows, hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
            "norm_rmsnorm_fwd")
     return out
 
@@ -221,13 +278,11 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None):
 def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
                   with_stats: bool = True, cfg=None, stream=None):
     """Returns (y, mean, rstd); mean/rstd are None when with_stats is False."""
-    _mat(x, "x")
-    rows, hidden = _rows_hidden(x)
+    rows, hidden, ld_x = _rows(x, "x")
     _vec(weight, hidden, "weight")
     _vec(bias, hidden, "bias")
-    y = torch.empty_like(x) if y is None else _mat(y, "y")
-    if y.shape != x.shape:
-        raise ValueError("y must have x's shape")
+    y = _like(x, y, "y")
+    _, _, ld_y = _rows(y, "y")
     if with_stats:
         mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
         rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
@@ -239,16 +294,17 @@ def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
     else:
         mean = rstd = None
         mp = rp = None
-    _check(lib().norm_layernorm_fwd_cfg(y.data_ptr(), mp, rp, x.data_ptr(), weight.data_ptr(),
-                                        bias.data_ptr(), rows, hidden, float(eps),
-                                        _cfg_ptr(cfg), _stream(stream)),
+    _check(lib().norm_layernorm_fwd_ex(y.data_ptr(), ld_y, mp, rp, x.data_ptr(), ld_x,
+                                       weight.data_ptr(), bias.data_ptr(), rows, hidden,
+                                       float(eps), _cfg_ptr(cfg), _stream(stream)),
            "norm_layernorm_fwd")
     return y, mean, rstd
 
 
 def workspace_bytes(rows: int, hidden: int, cfg=None, op: str = "layernorm_bwd") -> int:
     """Workspace bytes a backward op needs (LayerNorm: two partial slabs per
-    workgroup; the RMSNorm backward ops: one)."""
+    row walker; the RMSNorm backward ops: one).  Without cfg: enough for any
+    layout of this hidden size."""
     rms = OPS.get(op, op) in (OP_RMSNORM_BWD, OP_FUSED_ADD_RMSNORM_BWD)
     if cfg is None:
         fn = lib().norm_rmsnorm_bwd_workspace_bytes if rms else \
@@ -259,50 +315,14 @@ def workspace_bytes(rows: int, hidden: int, cfg=None, op: str = "layernorm_bwd")
     return int(fn(rows, hidden, _cfg_ptr(cfg)))
 
 
-def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
-                  dbias=None, workspace=None, cfg=None, stream=None):
-    """Returns (dx, dweight, dbias).  ``workspace`` (uint8 device tensor) is
-    allocated when not given."""
-    _mat(dy, "dy")
-    _mat(x, "x")
-    rows, hidden = _rows_hidden(x)
-    if dy.shape != x.shape:
-        raise ValueError("dy must have x's shape")
-    _mat(mean, "mean", torch.float32)
-    _mat(rstd, "rstd", torch.float32)
-    if mean.numel() != rows or rstd.numel() != rows:
-        raise ValueError("mean/rstd must hold one value per row")
-    _vec(weight, hidden, "weight")
-    dx = torch.empty_like(x) if dx is None else _mat(dx, "dx")
-    dev = x.device
-    dweight = torch.empty(hidden, dtype=torch.float32, device=dev) if dweight is None else dweight
-    dbias = torch.empty(hidden, dtype=torch.float32, device=dev) if dbias is None else dbias
-    _vec(dweight, hidden, "dweight", torch.float32)
-    _vec(dbias, hidden, "dbias", torch.float32)
-    need = workspace_bytes(rows, hidden, cfg)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _mat(workspace, "workspace", workspace.dtype)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().norm_layernorm_bwd_cfg(dx.data_ptr(), dweight.data_ptr(), dbias.data_ptr(),
-                                        dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
-                                        rstd.data_ptr(), weight.data_ptr(),
-                                        workspace.data_ptr(), ws_bytes, rows, hidden,
-                                        float(eps), _cfg_ptr(cfg), _stream(stream)),
-           "norm_layernorm_bwd")
-    return dx, dweight, dbias
-
-
 def _bwd_common(dy, x, weight, dx, dweight, workspace, cfg, op):
-    _mat(dy, "dy")
-    _mat(x, "x")
-    rows, hidden = _rows_hidden(x)
+    rows, hidden, ld_x = _rows(x, "x")
     if dy.shape != x.shape:
         raise ValueError("dy must have x's shape")
+    _, _, ld_dy = _rows(dy, "dy")
     _vec(weight, hidden, "weight")
-    dx = torch.empty_like(x) if dx is None else _mat(dx, "dx")
-    if dx.shape != x.shape:
-        raise ValueError("dx must have x's shape")
+    dx = _like(x, dx, "dx")
+    _, _, ld_dx = _rows(dx, "dx")
     dweight = torch.empty(hidden, dtype=torch.float32, device=x.device) if dweight is None \
         else dweight
     _vec(dweight, hidden, "dweight", torch.float32)
@@ -310,17 +330,40 @@ def _bwd_common(dy, x, weight, dx, dweight, workspace, cfg, op):
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _mat(workspace, "workspace", workspace.dtype)
-    return rows, hidden, dx, dweight, workspace, workspace.numel() * workspace.element_size()
+    wsb = workspace.numel() * workspace.element_size()
+    return rows, hidden, (ld_dx, ld_dy, ld_x), dx, dweight, workspace, wsb
+
+
+def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
+                  dbias=None, workspace=None, cfg=None, stream=None):
+    """Returns (dx, dweight, dbias).  ``workspace`` (uint8 device tensor) is
+    allocated when not given."""
+    rows, hidden, (ld_dx, ld_dy, ld_x), dx, dweight, workspace, wsb = _bwd_common(
+        dy, x, weight, dx, dweight, workspace, cfg, "layernorm_bwd")
+    _mat(mean, "mean", torch.float32)
+    _mat(rstd, "rstd", torch.float32)
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must hold one value per row")
+    dbias = torch.empty(hidden, dtype=torch.float32, device=x.device) if dbias is None else dbias
+    _vec(dbias, hidden, "dbias", torch.float32)
+    _check(lib().norm_layernorm_bwd_ex(dx.data_ptr(), ld_dx, dweight.data_ptr(),
+                                       dbias.data_ptr(), dy.data_ptr(), ld_dy, x.data_ptr(), ld_x,
+                                       mean.data_ptr(), rstd.data_ptr(), weight.data_ptr(),
+                                       workspace.data_ptr(), wsb, rows, hidden, float(eps),
+                                       _cfg_ptr(cfg), _stream(stream)),
+           "norm_layernorm_bwd")
+    return dx, dweight, dbias
 
 
 def rmsnorm_bwd(dy, x, weight, eps: float, dx=None, dweight=None, workspace=None, cfg=None,
                 stream=None):
     """Returns (dx, dweight); rstd is recomputed from x with eps."""
-    rows, hidden, dx, dweight, workspace, wsb = _bwd_common(dy, x, weight, dx, dweight,
-                                                            workspace, cfg, "rmsnorm_bwd")
-    _check(lib().norm_rmsnorm_bwd_cfg(dx.data_ptr(), dweight.data_ptr(), dy.data_ptr(),
-                                      x.data_ptr(), weight.data_ptr(), workspace.data_ptr(), wsb,
-                                      rows, hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
+    rows, hidden, (ld_dx, ld_dy, ld_x), dx, dweight, workspace, wsb = _bwd_common(
+        dy, x, weight, dx, dweight, workspace, cfg, "rmsnorm_bwd")
+    _check(lib().norm_rmsnorm_bwd_ex(dx.data_ptr(), ld_dx, dweight.data_ptr(), dy.data_ptr(),
+                                     ld_dy, x.data_ptr(), ld_x, weight.data_ptr(),
+                                     workspace.data_ptr(), wsb, rows, hidden, float(eps),
+                                     _cfg_ptr(cfg), _stream(stream)),
            "norm_rmsnorm_bwd")
     return dx, dweight
 
@@ -329,19 +372,19 @@ def fused_add_rmsnorm_bwd(dout, s, weight, eps: float, dres=None, ds=None, dweig
                           workspace=None, cfg=None, stream=None):
     """Backward of fused_add_rmsnorm at its residual output s: returns (ds,
     dweight), ds the gradient of both the x and residual inputs."""
-    rows, hidden, ds, dweight, workspace, wsb = _bwd_common(dout, s, weight, ds, dweight,
-                                                            workspace, cfg,
-                                                            "fused_add_rmsnorm_bwd")
+    rows, hidden, (ld_ds, ld_dout, ld_s), ds, dweight, workspace, wsb = _bwd_common(
+        dout, s, weight, ds, dweight, workspace, cfg, "fused_add_rmsnorm_bwd")
+    ld_dres = hidden
     if dres is not None:
-        _mat(dres, "dres")
         if dres.shape != s.shape:
             raise ValueError("dres must have s's shape")
-    _check(lib().norm_fused_add_rmsnorm_bwd_cfg(ds.data_ptr(), dweight.data_ptr(),
-                                                dout.data_ptr(),
-                                                dres.data_ptr() if dres is not None else None,
-                                                s.data_ptr(), weight.data_ptr(),
-                                                workspace.data_ptr(), wsb, rows, hidden,
-                                                float(eps), _cfg_ptr(cfg), _stream(stream)),
+        _, _, ld_dres = _rows(dres, "dres")
+    _check(lib().norm_fused_add_rmsnorm_bwd_ex(ds.data_ptr(), ld_ds, dweight.data_ptr(),
+                                               dout.data_ptr(), ld_dout,
+                                               dres.data_ptr() if dres is not None else None,
+                                               ld_dres, s.data_ptr(), ld_s, weight.data_ptr(),
+                                               workspace.data_ptr(), wsb, rows, hidden,
+                                               float(eps), _cfg_ptr(cfg), _stream(stream)),
            "norm_fused_add_rmsnorm_bwd")
     return ds, dweight
 

@@ -29,6 +29,11 @@ SOURCES = [
     "k_rmsnorm_fwd.hip",
     "k_layernorm_fwd.hip",
     "k_norm_bwd.hip",
+    "k_fused_add_rmsnorm_dyn.hip",
+    "k_rmsnorm_fwd_dyn.hip",
+    "k_layernorm_fwd_dyn.hip",
+    "k_layernorm_bwd_dyn.hip",
+    "k_rmsnorm_bwd_dyn.hip",
 ]
 
 HIPCC_FLAGS = [

@@ -1,7 +1,9 @@
-// C ABI of the row-normalization library: argument validation, launch-shape
-// choice and dispatch to the compiled kernel shapes.  Declared in norm.h.
+// C ABI of the row-normalization library: argument validation, the choice
+// between the compiled-hidden kernels and the run-time-hidden kernels, the
+// launch-shape choice, and dispatch.  Declared in norm.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -15,38 +17,62 @@ using namespace rownorm;
 
 namespace {
 
-bool hidden_supported(int64_t hidden) {
+bool hidden_compiled(int64_t hidden) {
     for (int h : kHiddenSizes)
         if (h == hidden) return true;
     return false;
 }
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-struct Span {
-    const void* p;
-    uint64_t bytes;
-};
-
-// True if the spans share a byte, unless they are the same span and that
-// exact alias is allowed.
-bool bad_overlap(Span a, Span b, bool exact_alias_ok) {
-    if (a.bytes == 0 || b.bytes == 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
-    const uintptr_t a1 = a0 + a.bytes, b1 = b0 + b.bytes;
-    if (a1 <= b0 || b1 <= a0) return false;
-    return !(exact_alias_ok && a0 == b0 && a.bytes == b.bytes);
-}
+uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+bool aligned(const void* p, uintptr_t a) { return addr(p) % a == 0; }
 
 bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.0f; }
 
-// Sanity bound on rows; each launch also checks that its grid and total
-// work-item count fit HIP's 32-bit launch limits.
+// Sanity bounds; each launch also checks that its grid and total work-item
+// count fit HIP's 32-bit launch limits.
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxLd = int64_t(1) << 40;  // elements
+// Largest hidden any kernel family can hold in registers (the run-time path,
+// 16-byte accesses, 1024 lanes x 8 accesses); the exact limit depends on the
+// operation and the access width (see the tables).
+constexpr int64_t kMaxHidden = 65536;
 
-bool launch_fits(int64_t rows, int lanes, int rpb) {
-    const int64_t groups = (rows + rpb - 1) / rpb;
-    return groups <= INT32_MAX && groups * lanes * rpb <= (int64_t)UINT32_MAX;
+bool valid_elems(int32_t w) { return w == 0 || w == 1 || w == 2 || w == 4 || w == 8; }
+
+// ---- memory regions and overlap ---------------------------------------------------
+// A [rows, cols] matrix of `elem`-byte values whose rows start `ld` elements
+// apart (a vector is one row).
+struct Region {
+    const void* p;
+    int64_t rows, ld, cols;
+    int elem;
+    uint64_t bytes() const {
+        if (!p || rows <= 0 || cols <= 0) return 0;
+        return (uint64_t)((rows - 1) * ld + cols) * (uint64_t)elem;
+    }
+};
+
+Region vec_region(const void* p, int64_t n, int elem) { return Region{p, 1, n, n, elem}; }
+
+// True if two regions share a byte.  An exact alias (same base, stride and
+// width) is allowed when `exact_ok`; two matrices with the same row stride
+// whose rows interleave without touching (column windows disjoint modulo the
+// stride, e.g. two slices of one wider matrix) never conflict.
+bool conflict(const Region& a, const Region& b, bool exact_ok) {
+    const uint64_t na = a.bytes(), nb = b.bytes();
+    if (na == 0 || nb == 0) return false;
+    const uintptr_t a0 = addr(a.p), b0 = addr(b.p);
+    if (a0 + na <= b0 || b0 + nb <= a0) return false;
+    if (exact_ok && a0 == b0 && a.ld == b.ld && a.cols == b.cols && a.elem == b.elem)
+        return false;
+    if (a.elem == b.elem && a.ld == b.ld && a.ld > 0) {
+        const int64_t d = (int64_t)(b0 - a0);  // two's complement difference
+        if (d % a.elem == 0) {
+            const int64_t m = ((d / a.elem) % a.ld + a.ld) % a.ld;
+            if (m >= a.cols && m + b.cols <= a.ld) return false;
+        }
+    }
+    return true;
 }
 
 // ---- compute-unit count, cached per device ---------------------------------
@@ -73,6 +99,11 @@ norm_status current_cu_count(int* cu) {
 }
 
 // ---- tables ----------------------------------------------------------------
+bool is_bwd(norm_op op) {
+    return op == NORM_OP_LAYERNORM_BWD || op == NORM_OP_RMSNORM_BWD ||
+           op == NORM_OP_FUSED_ADD_RMSNORM_BWD;
+}
+
 const std::vector<FwdEntry>& fwd_table(norm_op op) {
     switch (op) {
         case NORM_OP_FUSED_ADD_RMSNORM: return fused_add_rmsnorm_table();
@@ -81,28 +112,78 @@ const std::vector<FwdEntry>& fwd_table(norm_op op) {
     }
 }
 
-const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb) {
-    for (const FwdEntry& e : fwd_table(op))
-        if (e.hidden == hidden && e.lanes == lanes && e.rows_per_block == rpb) return &e;
-    return nullptr;
-}
-
-bool is_bwd(norm_op op) {
-    return op == NORM_OP_LAYERNORM_BWD || op == NORM_OP_RMSNORM_BWD ||
-           op == NORM_OP_FUSED_ADD_RMSNORM_BWD;
+const std::vector<DynFwdEntry>& dyn_fwd_table(norm_op op) {
+    switch (op) {
+        case NORM_OP_FUSED_ADD_RMSNORM: return fused_add_rmsnorm_dyn_table();
+        case NORM_OP_RMSNORM_FWD: return rmsnorm_fwd_dyn_table();
+        default: return layernorm_fwd_dyn_table();
+    }
 }
 
 const std::vector<BwdEntry>& bwd_table(norm_op op) {
     return op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_table() : rmsnorm_bwd_table();
 }
 
-// partial-sum slabs per workgroup: dweight and dbias for LayerNorm, dweight for RMSNorm
-int bwd_outs(norm_op op) { return op == NORM_OP_LAYERNORM_BWD ? 2 : 1; }
+const std::vector<DynBwdEntry>& dyn_bwd_table(norm_op op) {
+    return op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_dyn_table() : rmsnorm_bwd_dyn_table();
+}
+
+const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb) {
+    for (const FwdEntry& e : fwd_table(op))
+        if (e.hidden == hidden && e.lanes == lanes && e.rows_per_block == rpb) return &e;
+    return nullptr;
+}
 
 const BwdEntry* find_bwd(norm_op op, int64_t hidden, int lanes) {
     for (const BwdEntry& e : bwd_table(op))
         if (e.hidden == hidden && e.lanes == lanes) return &e;
     return nullptr;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The run-time-hidden instantiation with access width w and `lanes` lanes
+// whose per-lane access count is the smallest compiled one covering the row.
+template <class Entry>
+const Entry* find_dyn(const std::vector<Entry>& table, int64_t hidden, int w, int lanes) {
+    const int64_t need = ceil_div(hidden / w, lanes);
+    const Entry* best = nullptr;
+    for (const Entry& e : table)
+        if (e.elems == w && e.lanes == lanes && e.vecs >= need && (!best || e.vecs < best->vecs))
+            best = &e;
+    return best;
+}
+
+// Widest row the run-time-hidden instantiations of a table hold at access width w.
+template <class Entry>
+int64_t max_dyn_hidden(const std::vector<Entry>& table, int w) {
+    int64_t m = 0;
+    for (const Entry& e : table)
+        if (e.elems == w) m = std::max<int64_t>(m, (int64_t)e.lanes * e.vecs * w);
+    return m;
+}
+
+// partial-sum slabs per walker: dweight and dbias for LayerNorm, dweight for RMSNorm
+int bwd_outs(norm_op op) { return op == NORM_OP_LAYERNORM_BWD ? 2 : 1; }
+
+// ---- access width ---------------------------------------------------------------
+// Widest access (elements: 8, 4, 2, 1) that divides hidden and every leading
+// dimension, and that every bf16 pointer is aligned to.
+int shape_width(int64_t hidden, std::initializer_list<int64_t> lds) {
+    int w = 8;
+    for (;;) {
+        bool ok = hidden % w == 0;
+        for (int64_t ld : lds) ok = ok && ld % w == 0;
+        if (ok || w == 1) return w;
+        w /= 2;
+    }
+}
+
+int pointer_width(std::initializer_list<const void*> ptrs) {
+    int w = 8;
+    for (const void* p : ptrs)
+        while (w > 1 && p && !aligned(p, 2 * (uintptr_t)w)) w /= 2;
+    return w;
 }
 
 // ---- launch-shape choice ----------------------------------------------------
@@ -130,16 +211,34 @@ norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     while (lanes < 1024 && rows * (lanes / 64) < target_waves && valid(lanes * 2)) lanes *= 2;
     int rpb = lanes == 64 ? 4 : (lanes == 128 ? 2 : 1);
     while (rpb > 1 && !find_fwd(op, hidden, lanes, rpb)) rpb /= 2;
-    return norm_launch_cfg{lanes, rpb, 0};
+    return norm_launch_cfg{lanes, rpb, 0, 0};
+}
+
+// Run-time-hidden forward: the same two rules in units of accesses of w
+// elements, starting from 8 lanes a row (rows narrower than a wave share it),
+// and never more lanes than the row has accesses.  Returns lanes 0 when no
+// compiled instantiation holds the row.
+norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, int cu) {
+    const int64_t nacc = hidden / w;
+    const int64_t target_lanes = 4 * (int64_t)cu * 64;
+    const int64_t vcap = (op != NORM_OP_LAYERNORM_FWD && rows >= 16 * (int64_t)cu) ? 4 : 8;
+    int lanes = 8;
+    while (lanes < 1024 && ceil_div(nacc, lanes) > vcap) lanes *= 2;
+    while (lanes < 1024 && lanes < nacc && rows * lanes < target_lanes) lanes *= 2;
+    for (; lanes <= 1024; lanes *= 2)
+        if (find_dyn(dyn_fwd_table(op), hidden, w, lanes))
+            return norm_launch_cfg{lanes, dyn_rows_per_block(lanes), 0, w};
+    return norm_launch_cfg{0, 0, 0, w};
 }
 
 // LayerNorm backward: one persistent workgroup per compute unit of the
 // largest part (256 on MI355X) made the best trade-off between rows in flight
 // and partial-sum slabs to reduce; the grid is a constant, not a device query,
 // so the workspace size is pure host arithmetic.
-int32_t default_bwd_grid(int64_t rows) {
-    constexpr int64_t kSlabs = 256;
-    return (int32_t)(rows < kSlabs ? (rows > 0 ? rows : 1) : kSlabs);
+int32_t default_bwd_grid(int64_t rows, int rows_per_block = 1) {
+    constexpr int64_t kGroups = 256;
+    const int64_t g = ceil_div(std::max<int64_t>(rows, 1), rows_per_block);
+    return (int32_t)std::min(g, kGroups);
 }
 
 norm_launch_cfg choose_bwd(norm_op op, int64_t rows, int64_t hidden) {
@@ -150,119 +249,319 @@ norm_launch_cfg choose_bwd(norm_op op, int64_t rows, int64_t hidden) {
         if (e.hidden != hidden) continue;
         if (best == 0 || e.lanes > best) best = e.lanes;
     }
-    return norm_launch_cfg{best, 1, default_bwd_grid(rows)};
+    return norm_launch_cfg{best, 1, default_bwd_grid(rows), 0};
 }
 
-int bwd_depth_of(norm_op op, int64_t hidden, int lanes) {
-    const BwdEntry* e = find_bwd(op, hidden, lanes);
-    return e ? e->depth : 0;
+// Run-time-hidden backward: the fewest lanes that give each lane one access
+// (at most 1024), falling back to fewer lanes with more accesses each where
+// that shape is not compiled.
+norm_launch_cfg choose_dyn_bwd(norm_op op, int64_t rows, int64_t hidden, int w) {
+    const int64_t nacc = hidden / w;
+    int lanes = 8;
+    while (lanes < 1024 && lanes < nacc) lanes *= 2;
+    for (; lanes >= 8; lanes /= 2)
+        if (find_dyn(dyn_bwd_table(op), hidden, w, lanes)) {
+            const int r = dyn_rows_per_block(lanes);
+            return norm_launch_cfg{lanes, r, default_bwd_grid(rows, r), w};
+        }
+    return norm_launch_cfg{0, 0, 0, w};
 }
 
-size_t bwd_workspace_bytes(norm_op op, int64_t hidden, int32_t grid) {
+size_t static_ws_bytes(norm_op op, int64_t hidden, int64_t grid) {
     return (size_t)grid * (size_t)bwd_outs(op) * (size_t)hidden * sizeof(float);
+}
+
+size_t dyn_ws_bytes(norm_op op, int64_t hidden, int64_t slabs) {
+    return (size_t)slabs * (size_t)bwd_outs(op) * (size_t)dyn_padded_hidden(hidden) *
+           sizeof(float);
+}
+
+// The column reduce addresses the workspace with 32-bit byte offsets and
+// reads up to 255 slabs past the last one (range-checked to zero).
+bool dyn_slabs_fit(norm_op op, int64_t hidden, int64_t slabs) {
+    return (slabs + 256) * bwd_outs(op) * dyn_padded_hidden(hidden) * 4 <= INT32_MAX;
 }
 
 norm_status from_hip(hipError_t e) { return e == hipSuccess ? NORM_SUCCESS : NORM_ERROR_LAUNCH; }
 
 // ---- forward entry -------------------------------------------------------------
-norm_status run_fwd(norm_op op, const FwdArgs& a, int64_t hidden, const norm_launch_cfg* cfg,
-                    hipStream_t stream) {
-    if (a.rows < 0 || a.rows > kMaxRows || !eps_ok(a.eps)) return NORM_ERROR_INVALID_VALUE;
-    if (cfg && (cfg->grid != 0 || cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0))
-        return NORM_ERROR_INVALID_VALUE;
-    if (a.rows == 0) return NORM_SUCCESS;
-    if (!hidden_supported(hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+struct FwdCall {
+    void* out;
+    int64_t ld_out;
+    void* residual;
+    int64_t ld_res;
+    const void* x;
+    int64_t ld_x;
+    const void* weight;
+    const void* bias;
+    float* mean;
+    float* rstd;
+    int64_t rows, hidden;
+    float eps;
+};
 
+norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
+                    hipStream_t stream) {
     const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
     const bool ln = op == NORM_OP_LAYERNORM_FWD;
-    if (!a.out || !a.x || !a.weight || (fused && !a.residual) || (ln && !a.bias))
+    if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
+    if (cfg && (cfg->grid != 0 || cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
+                !valid_elems(cfg->vector_elems)))
         return NORM_ERROR_INVALID_VALUE;
-    if (ln && ((a.mean == nullptr) != (a.rstd == nullptr))) return NORM_ERROR_INVALID_VALUE;
-    if (!aligned(a.out, 16) || !aligned(a.x, 16) || !aligned(a.weight, 16) ||
-        (fused && !aligned(a.residual, 16)) || (ln && !aligned(a.bias, 16)) ||
-        (ln && a.mean && (!aligned(a.mean, 4) || !aligned(a.rstd, 4))))
+    if (c.rows == 0) return NORM_SUCCESS;
+    if (c.hidden < 1 || c.hidden > kMaxHidden) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    if (!c.out || !c.x || !c.weight || (fused && !c.residual) || (ln && !c.bias))
+        return NORM_ERROR_INVALID_VALUE;
+    if (ln && ((c.mean == nullptr) != (c.rstd == nullptr))) return NORM_ERROR_INVALID_VALUE;
+    const int64_t ld_res = fused ? c.ld_res : c.hidden;
+    for (int64_t ld : {c.ld_out, c.ld_x, ld_res})
+        if (ld < c.hidden || ld > kMaxLd) return NORM_ERROR_INVALID_VALUE;
+    if (!aligned(c.out, 2) || !aligned(c.x, 2) || !aligned(c.weight, 2) ||
+        (fused && !aligned(c.residual, 2)) || (ln && !aligned(c.bias, 2)) ||
+        (ln && c.mean && (!aligned(c.mean, 4) || !aligned(c.rstd, 4))))
         return NORM_ERROR_MISALIGNED;
 
-    const uint64_t mat = (uint64_t)a.rows * (uint64_t)hidden * 2;
-    const uint64_t vec = (uint64_t)hidden * 2;
-    const uint64_t stat = (uint64_t)a.rows * 4;
-    const Span out{a.out, mat}, x{a.x, mat}, w{a.weight, vec};
-    const Span res{fused ? a.residual : nullptr, fused ? mat : 0};
-    const Span b{ln ? a.bias : nullptr, ln ? vec : 0};
-    const Span mean{ln ? a.mean : nullptr, (ln && a.mean) ? stat : 0};
-    const Span rstd{ln ? a.rstd : nullptr, (ln && a.rstd) ? stat : 0};
+    const Region out{c.out, c.rows, c.ld_out, c.hidden, 2}, x{c.x, c.rows, c.ld_x, c.hidden, 2};
+    const Region res{fused ? c.residual : nullptr, c.rows, ld_res, c.hidden, 2};
+    const Region w = vec_region(c.weight, c.hidden, 2);
+    const Region b = vec_region(ln ? c.bias : nullptr, c.hidden, 2);
+    const Region mean = vec_region(ln ? c.mean : nullptr, c.rows, 4);
+    const Region rstd = vec_region(ln ? c.rstd : nullptr, c.rows, 4);
     // outputs must not overlap anything, except out == x exactly
-    if (bad_overlap(out, x, true) || bad_overlap(out, w, false) || bad_overlap(out, res, false) ||
-        bad_overlap(out, b, false) || bad_overlap(out, mean, false) ||
-        bad_overlap(out, rstd, false) || bad_overlap(res, x, false) ||
-        bad_overlap(res, w, false) || bad_overlap(res, b, false) || bad_overlap(mean, x, false) ||
-        bad_overlap(mean, w, false) || bad_overlap(mean, b, false) ||
-        bad_overlap(mean, rstd, false) || bad_overlap(rstd, x, false) ||
-        bad_overlap(rstd, w, false) || bad_overlap(rstd, b, false))
+    if (conflict(out, x, true) || conflict(out, w, false) || conflict(out, res, false) ||
+        conflict(out, b, false) || conflict(out, mean, false) || conflict(out, rstd, false) ||
+        conflict(res, x, false) || conflict(res, w, false) || conflict(res, b, false) ||
+        conflict(mean, x, false) || conflict(mean, w, false) || conflict(mean, b, false) ||
+        conflict(mean, rstd, false) || conflict(rstd, x, false) || conflict(rstd, w, false) ||
+        conflict(rstd, b, false))
         return NORM_ERROR_INVALID_VALUE;
 
-    norm_launch_cfg c;
-    if (cfg) {
-        c = *cfg;
+    const int ws = shape_width(c.hidden, {c.ld_out, c.ld_x, ld_res});
+    const int wp = pointer_width({c.out, c.x, c.weight, fused ? c.residual : nullptr,
+                                  ln ? c.bias : nullptr});
+    const int w_max = std::min(ws, wp);
+    const bool contiguous = c.ld_out == c.hidden && c.ld_x == c.hidden && ld_res == c.hidden;
+    const bool compiled_ok = hidden_compiled(c.hidden) && contiguous && w_max == 8;
+
+    if (!compiled_ok && !(cfg && cfg->vector_elems == 0) &&
+        c.hidden > max_dyn_hidden(dyn_fwd_table(op), cfg ? cfg->vector_elems : w_max))
+        return NORM_ERROR_UNSUPPORTED_HIDDEN;
+
+    norm_launch_cfg k;
+    if (cfg && cfg->vector_elems == 0) {  // a compiled-hidden shape was asked for
+        if (!hidden_compiled(c.hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+        if (!contiguous) return NORM_ERROR_INVALID_VALUE;
+        if (wp < 8) return NORM_ERROR_MISALIGNED;
+        k = *cfg;
+    } else if (cfg) {  // a run-time-hidden shape was asked for
+        if (cfg->vector_elems > ws) return NORM_ERROR_INVALID_VALUE;
+        if (cfg->vector_elems > wp) return NORM_ERROR_MISALIGNED;
+        k = *cfg;
     } else {
         int cu = 0;
         const norm_status st = current_cu_count(&cu);
         if (st != NORM_SUCCESS) return st;
-        c = choose_fwd(op, a.rows, hidden, cu);
+        k = compiled_ok ? choose_fwd(op, c.rows, c.hidden, cu)
+                        : choose_dyn_fwd(op, c.rows, c.hidden, w_max, cu);
+        if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     }
-    const FwdEntry* e = find_fwd(op, hidden, c.threads_per_row, c.rows_per_block);
-    if (!e || !launch_fits(a.rows, c.threads_per_row, c.rows_per_block))
+
+    if (k.vector_elems == 0) {
+        const FwdEntry* e = find_fwd(op, c.hidden, k.threads_per_row, k.rows_per_block);
+        if (!e) return NORM_ERROR_INVALID_VALUE;
+        const int64_t groups = ceil_div(c.rows, k.rows_per_block);
+        if (groups > INT32_MAX ||
+            groups * k.threads_per_row * k.rows_per_block > (int64_t)UINT32_MAX)
+            return NORM_ERROR_INVALID_VALUE;
+        const FwdArgs a{c.out, c.residual, c.x, c.weight, c.bias, c.mean, c.rstd, c.rows, c.eps};
+        return from_hip(e->launch(a, stream));
+    }
+    if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row)) {
         return NORM_ERROR_INVALID_VALUE;
+    }
+    const DynFwdEntry* e =
+        find_dyn(dyn_fwd_table(op), c.hidden, k.vector_elems, k.threads_per_row);
+    if (!e) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
+    const int64_t groups = ceil_div(c.rows, k.rows_per_block);
+    if (groups > INT32_MAX || groups * dyn_block_size(k.threads_per_row) > (int64_t)UINT32_MAX)
+        return NORM_ERROR_INVALID_VALUE;
+    const DynFwdArgs a{c.out,     c.residual, c.x,   c.weight, c.bias,   c.mean,
+                       c.rstd,    c.ld_out,   ld_res, c.ld_x,  c.rows,   (int32_t)c.hidden,
+                       c.eps};
     return from_hip(e->launch(a, stream));
 }
 
-norm_status run_bwd(norm_op op, BwdArgs a, int64_t hidden, float eps, size_t workspace_bytes,
-                    const norm_launch_cfg* cfg, hipStream_t stream) {
+// ---- backward entry ------------------------------------------------------------
+struct BwdCall {
+    void* dx;
+    int64_t ld_dx;
+    const void* dy;
+    int64_t ld_dy;
+    const void* x;
+    int64_t ld_x;
+    const float* mean;
+    const float* rstd;
+    const void* dres;
+    int64_t ld_dres;
+    const void* weight;
+    void* workspace;
+    size_t workspace_bytes;
+    float* dweight;
+    float* dbias;
+    int64_t rows, hidden;
+    float eps;
+};
+
+norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
+                    hipStream_t stream) {
     const bool ln = op == NORM_OP_LAYERNORM_BWD;
-    if (a.rows < 0 || a.rows > kMaxRows || !eps_ok(eps)) return NORM_ERROR_INVALID_VALUE;
-    if (cfg && (cfg->threads_per_row <= 0 || cfg->rows_per_block != 1 || cfg->grid < 0))
+    if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
+    if (cfg && (cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 || cfg->grid < 0 ||
+                !valid_elems(cfg->vector_elems)))
         return NORM_ERROR_INVALID_VALUE;
-    if (!hidden_supported(hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
-    if (cfg && cfg->grid > max_bwd_grid(hidden)) return NORM_ERROR_INVALID_VALUE;
-    const bool any = a.rows > 0;
-    if (!a.dweight || (ln && !a.dbias) || !a.workspace) return NORM_ERROR_INVALID_VALUE;
-    if (any && (!a.dx || !a.dy || !a.x || !a.weight || (ln && (!a.mean || !a.rstd))))
+    if (c.hidden < 1 || c.hidden > kMaxHidden) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    const bool any = c.rows > 0;
+    if (!c.dweight || (ln && !c.dbias) || !c.workspace) return NORM_ERROR_INVALID_VALUE;
+    if (any && (!c.dx || !c.dy || !c.x || !c.weight || (ln && (!c.mean || !c.rstd))))
         return NORM_ERROR_INVALID_VALUE;
-    if (!aligned(a.dweight, 4) || (ln && !aligned(a.dbias, 4)) || !aligned(a.workspace, 16))
+    const int64_t ld_dres = c.dres ? c.ld_dres : c.hidden;
+    for (int64_t ld : {c.ld_dx, c.ld_dy, c.ld_x, ld_dres})
+        if (ld < c.hidden || ld > kMaxLd) return NORM_ERROR_INVALID_VALUE;
+    if (!aligned(c.dweight, 4) || (ln && !aligned(c.dbias, 4)) || !aligned(c.workspace, 16))
         return NORM_ERROR_MISALIGNED;
-    if (any && (!aligned(a.dx, 16) || !aligned(a.dy, 16) || !aligned(a.x, 16) ||
-                !aligned(a.weight, 16) || (a.dres && !aligned(a.dres, 16)) ||
-                (ln && (!aligned(a.mean, 4) || !aligned(a.rstd, 4)))))
+    if (any && (!aligned(c.dx, 2) || !aligned(c.dy, 2) || !aligned(c.x, 2) ||
+                !aligned(c.weight, 2) || (c.dres && !aligned(c.dres, 2)) ||
+                (ln && (!aligned(c.mean, 4) || !aligned(c.rstd, 4)))))
         return NORM_ERROR_MISALIGNED;
 
-    norm_launch_cfg c = cfg ? *cfg : choose_bwd(op, a.rows, hidden);
-    if (c.grid == 0) c.grid = default_bwd_grid(a.rows);
-    const BwdEntry* e = find_bwd(op, hidden, c.threads_per_row);
-    if (!e) return NORM_ERROR_INVALID_VALUE;
-    a.grid = c.grid;
-    a.eps = eps;
-    const size_t ws_need = bwd_workspace_bytes(op, hidden, any ? c.grid : 0);
+    const int ws_w = shape_width(c.hidden, {c.ld_dx, c.ld_dy, c.ld_x, ld_dres});
+    const int wp = any ? pointer_width({c.dx, c.dy, c.x, c.weight, c.dres}) : 8;
+    const int w_max = std::min(ws_w, wp);
+    const bool contiguous = c.ld_dx == c.hidden && c.ld_dy == c.hidden && c.ld_x == c.hidden &&
+                            ld_dres == c.hidden;
+    const bool compiled_ok = hidden_compiled(c.hidden) && contiguous && w_max == 8;
 
-    const uint64_t mat = any ? (uint64_t)a.rows * (uint64_t)hidden * 2 : 0;
-    const uint64_t vec = any ? (uint64_t)hidden * 2 : 0;
-    const uint64_t stat = ln ? (uint64_t)a.rows * 4 : 0;
-    const uint64_t col = (uint64_t)hidden * 4;
-    const Span dx{a.dx, mat}, dy{a.dy, mat}, x{a.x, mat}, mean{a.mean, stat},
-        rstd{a.rstd, stat}, dres{a.dres, a.dres ? mat : 0}, w{a.weight, vec},
-        dw{a.dweight, col}, db{a.dbias, ln ? col : 0}, ws{a.workspace, ws_need};
-    // outputs overlap no input, except dx == dy (or dx == dres) exactly
-    const Span ins[] = {dy, x, mean, rstd, dres, w};
-    for (const Span& in : ins) {
-        if (bad_overlap(dx, in, in.p == a.dy || (a.dres && in.p == a.dres)))
+    if (!compiled_ok && !(cfg && cfg->vector_elems == 0) &&
+        c.hidden > max_dyn_hidden(dyn_bwd_table(op), cfg ? cfg->vector_elems : w_max))
+        return NORM_ERROR_UNSUPPORTED_HIDDEN;
+
+    norm_launch_cfg k;
+    if (cfg && cfg->vector_elems == 0) {
+        if (!hidden_compiled(c.hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+        if (!contiguous || cfg->rows_per_block != 1) return NORM_ERROR_INVALID_VALUE;
+        if (wp < 8) return NORM_ERROR_MISALIGNED;
+        k = *cfg;
+        if (k.grid == 0) k.grid = default_bwd_grid(c.rows);
+        if (k.grid > max_bwd_grid(c.hidden)) return NORM_ERROR_INVALID_VALUE;
+    } else if (cfg) {
+        if (cfg->vector_elems > ws_w) return NORM_ERROR_INVALID_VALUE;
+        if (cfg->vector_elems > wp) return NORM_ERROR_MISALIGNED;
+        k = *cfg;
+        if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row))
             return NORM_ERROR_INVALID_VALUE;
-        if (bad_overlap(dw, in, false) || bad_overlap(db, in, false) || bad_overlap(ws, in, false))
+        if (k.grid == 0) k.grid = default_bwd_grid(c.rows, k.rows_per_block);
+    } else {
+        k = compiled_ok ? choose_bwd(op, c.rows, c.hidden)
+                        : choose_dyn_bwd(op, c.rows, c.hidden, w_max);
+        if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    }
+
+    const BwdEntry* se = nullptr;
+    const DynBwdEntry* de = nullptr;
+    size_t ws_need = 0;
+    if (k.vector_elems == 0) {
+        se = find_bwd(op, c.hidden, k.threads_per_row);
+        if (!se) return NORM_ERROR_INVALID_VALUE;
+        ws_need = static_ws_bytes(op, c.hidden, any ? k.grid : 0);
+    } else {
+        de = find_dyn(dyn_bwd_table(op), c.hidden, k.vector_elems, k.threads_per_row);
+        if (!de) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
+        const int64_t slabs = (int64_t)k.grid * k.rows_per_block;
+        if (!dyn_slabs_fit(op, c.hidden, slabs)) return NORM_ERROR_INVALID_VALUE;
+        ws_need = dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
+    }
+
+    const int64_t mrows = any ? c.rows : 0;
+    const Region dx{c.dx, mrows, c.ld_dx, c.hidden, 2}, dy{c.dy, mrows, c.ld_dy, c.hidden, 2},
+        x{c.x, mrows, c.ld_x, c.hidden, 2}, dres{c.dres, mrows, ld_dres, c.hidden, 2};
+    const Region mean = vec_region(ln ? c.mean : nullptr, mrows, 4),
+                 rstd = vec_region(ln ? c.rstd : nullptr, mrows, 4),
+                 w = vec_region(any ? c.weight : nullptr, c.hidden, 2),
+                 dw = vec_region(c.dweight, c.hidden, 4),
+                 db = vec_region(ln ? c.dbias : nullptr, c.hidden, 4),
+                 wsr = vec_region(c.workspace, (int64_t)ws_need, 1);
+    // outputs overlap no input, except dx == dy (or dx == dres) exactly
+    for (const Region* in : {&dy, &x, &mean, &rstd, &dres, &w}) {
+        const bool alias_ok = in == &dy || in == &dres;
+        if (conflict(dx, *in, alias_ok) || conflict(dw, *in, false) ||
+            conflict(db, *in, false) || conflict(wsr, *in, false))
             return NORM_ERROR_INVALID_VALUE;
     }
-    if (bad_overlap(dx, dw, false) || bad_overlap(dx, db, false) || bad_overlap(dx, ws, false) ||
-        bad_overlap(dw, db, false) || bad_overlap(dw, ws, false) || bad_overlap(db, ws, false))
+    if (conflict(dx, dw, false) || conflict(dx, db, false) || conflict(dx, wsr, false) ||
+        conflict(dw, db, false) || conflict(dw, wsr, false) || conflict(db, wsr, false))
         return NORM_ERROR_INVALID_VALUE;
-    if (workspace_bytes < ws_need) return NORM_ERROR_WORKSPACE;
-    return from_hip(e->launch(a, stream));
+    if (c.workspace_bytes < ws_need) return NORM_ERROR_WORKSPACE;
+
+    if (se) {
+        const BwdArgs a{c.dx,     c.dy,      c.x,    c.mean, c.rstd,    c.dres, c.weight,
+                        (float*)c.workspace, c.dweight, c.dbias, c.rows, k.grid, c.eps};
+        return from_hip(se->launch(a, stream));
+    }
+    const DynBwdArgs a{c.dx,    c.dy,     c.x,       c.mean,  c.rstd,
+                       c.dres,  c.weight, (float*)c.workspace, c.dweight, c.dbias,
+                       c.ld_dx, c.ld_dy,  c.ld_x,    ld_dres, c.rows,
+                       (int32_t)c.hidden, k.grid, c.eps};
+    return from_hip(de->launch(a, stream));
+}
+
+// Workspace for (op, rows, hidden): the given shape's, or with cfg == NULL the
+// largest the library's choice can need for any layout of this hidden size
+// (the compiled kernels, or the run-time kernels at any access width).
+size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg* cfg) {
+    if (rows <= 0 || hidden < 1 || hidden > kMaxHidden) return 0;
+    if (cfg) {
+        if (cfg->vector_elems == 0) {
+            if (!hidden_compiled(hidden)) return 0;
+            return static_ws_bytes(op, hidden, cfg->grid > 0 ? cfg->grid : default_bwd_grid(rows));
+        }
+        if (!valid_elems(cfg->vector_elems) || cfg->threads_per_row <= 0) return 0;
+        const int r = dyn_rows_per_block(cfg->threads_per_row);
+        const int64_t g = cfg->grid > 0 ? cfg->grid : default_bwd_grid(rows, r);
+        return dyn_ws_bytes(op, hidden, g * r);
+    }
+    size_t need = 0;
+    if (hidden_compiled(hidden))
+        need = static_ws_bytes(op, hidden, choose_bwd(op, rows, hidden).grid);
+    for (int w : {8, 4, 2, 1}) {
+        if (hidden % w) continue;
+        const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w);
+        if (k.threads_per_row)
+            need = std::max(need, dyn_ws_bytes(op, hidden, (int64_t)k.grid * k.rows_per_block));
+    }
+    return need;
+}
+
+// The library's choice for contiguous, 16-byte-aligned buffers.
+norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
+                   norm_launch_cfg* cfg) {
+    if (hidden < 1 || hidden > kMaxHidden) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    const int w = shape_width(hidden, {});
+    norm_launch_cfg k;
+    if (is_bwd(op)) {
+        k = hidden_compiled(hidden) ? choose_bwd(op, rows, hidden)
+                                    : choose_dyn_bwd(op, rows, hidden, w);
+    } else {
+        int cu = cu_count;
+        if (cu <= 0) {
+            const norm_status st = current_cu_count(&cu);
+            if (st != NORM_SUCCESS) return st;
+        }
+        k = hidden_compiled(hidden) ? choose_fwd(op, rows, hidden, cu)
+                                    : choose_dyn_fwd(op, rows, hidden, w, cu);
+    }
+    if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    *cfg = k;
+    return NORM_SUCCESS;
 }
 
 }  // namespace
@@ -274,11 +573,11 @@ const char* norm_status_string(norm_status status) {
         case NORM_SUCCESS: return "NORM_SUCCESS";
         case NORM_ERROR_INVALID_VALUE: return "NORM_ERROR_INVALID_VALUE: invalid argument";
         case NORM_ERROR_UNSUPPORTED_HIDDEN:
-            return "NORM_ERROR_UNSUPPORTED_HIDDEN: hidden must be one of 1024, 2048, 4096, 8192, "
-                   "12288, 16384";
+            return "NORM_ERROR_UNSUPPORTED_HIDDEN: no kernel holds a row of this hidden size "
+                   "(forward: up to 65536, backward: up to 16384, less for narrow accesses)";
         case NORM_ERROR_MISALIGNED:
-            return "NORM_ERROR_MISALIGNED: bf16 pointers need 16-byte, fp32 pointers 4-byte "
-                   "alignment";
+            return "NORM_ERROR_MISALIGNED: bf16 pointers need 2-byte (compiled shapes: 16-byte) "
+                   "alignment, fp32 pointers 4-byte, the workspace 16-byte";
         case NORM_ERROR_WORKSPACE: return "NORM_ERROR_WORKSPACE: workspace too small";
         case NORM_ERROR_LAUNCH: return "NORM_ERROR_LAUNCH: HIP reported a launch error";
         case NORM_ERROR_DEVICE: return "NORM_ERROR_DEVICE: could not query the current device";
@@ -286,12 +585,23 @@ const char* norm_status_string(norm_status status) {
     return "unknown norm_status";
 }
 
+// ---- forward ------------------------------------------------------------------------
+norm_status norm_fused_add_rmsnorm_ex(void* out, int64_t ld_out, void* residual,
+                                      int64_t ld_residual, const void* x, int64_t ld_x,
+                                      const void* weight, int64_t rows, int64_t hidden,
+                                      float eps, const norm_launch_cfg* cfg,
+                                      hipStream_t stream) {
+    const FwdCall c{out,    ld_out,  residual, ld_residual, x,      ld_x, weight,
+                    nullptr, nullptr, nullptr, rows,        hidden, eps};
+    return run_fwd(NORM_OP_FUSED_ADD_RMSNORM, c, cfg, stream);
+}
+
 norm_status norm_fused_add_rmsnorm_cfg(void* out, void* residual, const void* x,
                                        const void* weight, int64_t rows, int64_t hidden,
                                        float eps, const norm_launch_cfg* cfg,
                                        hipStream_t stream) {
-    FwdArgs a{out, residual, x, weight, nullptr, nullptr, nullptr, rows, eps};
-    return run_fwd(NORM_OP_FUSED_ADD_RMSNORM, a, hidden, cfg, stream);
+    return norm_fused_add_rmsnorm_ex(out, hidden, residual, hidden, x, hidden, weight, rows,
+                                     hidden, eps, cfg, stream);
 }
 
 norm_status norm_fused_add_rmsnorm(void* out, void* residual, const void* x, const void* weight,
@@ -299,11 +609,18 @@ norm_status norm_fused_add_rmsnorm(void* out, void* residual, const void* x, con
     return norm_fused_add_rmsnorm_cfg(out, residual, x, weight, rows, hidden, eps, nullptr, stream);
 }
 
+norm_status norm_rmsnorm_fwd_ex(void* out, int64_t ld_out, const void* x, int64_t ld_x,
+                                const void* weight, int64_t rows, int64_t hidden, float eps,
+                                const norm_launch_cfg* cfg, hipStream_t stream) {
+    const FwdCall c{out,    ld_out,  nullptr, hidden, x,      ld_x, weight,
+                    nullptr, nullptr, nullptr, rows,  hidden, eps};
+    return run_fwd(NORM_OP_RMSNORM_FWD, c, cfg, stream);
+}
+
 norm_status norm_rmsnorm_fwd_cfg(void* out, const void* x, const void* weight, int64_t rows,
                                  int64_t hidden, float eps, const norm_launch_cfg* cfg,
                                  hipStream_t stream) {
-    FwdArgs a{out, nullptr, x, weight, nullptr, nullptr, nullptr, rows, eps};
-    return run_fwd(NORM_OP_RMSNORM_FWD, a, hidden, cfg, stream);
+    return norm_rmsnorm_fwd_ex(out, hidden, x, hidden, weight, rows, hidden, eps, cfg, stream);
 }
 
 norm_status norm_rmsnorm_fwd(void* out, const void* x, const void* weight, int64_t rows,
@@ -311,12 +628,21 @@ norm_status norm_rmsnorm_fwd(void* out, const void* x, const void* weight, int64
     return norm_rmsnorm_fwd_cfg(out, x, weight, rows, hidden, eps, nullptr, stream);
 }
 
+norm_status norm_layernorm_fwd_ex(void* y, int64_t ld_y, float* mean, float* rstd,
+                                  const void* x, int64_t ld_x, const void* weight,
+                                  const void* bias, int64_t rows, int64_t hidden, float eps,
+                                  const norm_launch_cfg* cfg, hipStream_t stream) {
+    const FwdCall c{y, ld_y, nullptr, hidden, x, ld_x, weight, bias, mean, rstd, rows, hidden,
+                    eps};
+    return run_fwd(NORM_OP_LAYERNORM_FWD, c, cfg, stream);
+}
+
 norm_status norm_layernorm_fwd_cfg(void* y, float* mean, float* rstd, const void* x,
                                    const void* weight, const void* bias, int64_t rows,
                                    int64_t hidden, float eps, const norm_launch_cfg* cfg,
                                    hipStream_t stream) {
-    FwdArgs a{y, nullptr, x, weight, bias, mean, rstd, rows, eps};
-    return run_fwd(NORM_OP_LAYERNORM_FWD, a, hidden, cfg, stream);
+    return norm_layernorm_fwd_ex(y, hidden, mean, rstd, x, hidden, weight, bias, rows, hidden,
+                                 eps, cfg, stream);
 }
 
 norm_status norm_layernorm_fwd(void* y, float* mean, float* rstd, const void* x,
@@ -326,14 +652,27 @@ norm_status norm_layernorm_fwd(void* y, float* mean, float* rstd, const void* x,
                                   stream);
 }
 
+// ---- backward -----------------------------------------------------------------------
+norm_status norm_layernorm_bwd_ex(void* dx, int64_t ld_dx, float* dweight, float* dbias,
+                                  const void* dy, int64_t ld_dy, const void* x, int64_t ld_x,
+                                  const float* mean, const float* rstd, const void* weight,
+                                  void* workspace, size_t workspace_bytes, int64_t rows,
+                                  int64_t hidden, float eps, const norm_launch_cfg* cfg,
+                                  hipStream_t stream) {
+    const BwdCall c{dx,     ld_dx,  dy,        ld_dy,           x,       ld_x,  mean,
+                    rstd,   nullptr, hidden,   weight,          workspace, workspace_bytes,
+                    dweight, dbias, rows,      hidden,          eps};
+    return run_bwd(NORM_OP_LAYERNORM_BWD, c, cfg, stream);
+}
+
 norm_status norm_layernorm_bwd_cfg(void* dx, float* dweight, float* dbias, const void* dy,
                                    const void* x, const float* mean, const float* rstd,
                                    const void* weight, void* workspace, size_t workspace_bytes,
                                    int64_t rows, int64_t hidden, float eps,
                                    const norm_launch_cfg* cfg, hipStream_t stream) {
-    BwdArgs a{dx, dy, x, mean, rstd, nullptr, weight, (float*)workspace, dweight, dbias, rows, 0,
-              0.0f};
-    return run_bwd(NORM_OP_LAYERNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
+    return norm_layernorm_bwd_ex(dx, hidden, dweight, dbias, dy, hidden, x, hidden, mean, rstd,
+                                 weight, workspace, workspace_bytes, rows, hidden, eps, cfg,
+                                 stream);
 }
 
 norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias, const void* dy,
@@ -344,13 +683,23 @@ norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias, const voi
                                   workspace_bytes, rows, hidden, eps, nullptr, stream);
 }
 
+norm_status norm_rmsnorm_bwd_ex(void* dx, int64_t ld_dx, float* dweight, const void* dy,
+                                int64_t ld_dy, const void* x, int64_t ld_x, const void* weight,
+                                void* workspace, size_t workspace_bytes, int64_t rows,
+                                int64_t hidden, float eps, const norm_launch_cfg* cfg,
+                                hipStream_t stream) {
+    const BwdCall c{dx,      ld_dx,   dy,      ld_dy,  x,         ld_x,  nullptr,
+                    nullptr, nullptr, hidden,  weight, workspace, workspace_bytes,
+                    dweight, nullptr, rows,    hidden, eps};
+    return run_bwd(NORM_OP_RMSNORM_BWD, c, cfg, stream);
+}
+
 norm_status norm_rmsnorm_bwd_cfg(void* dx, float* dweight, const void* dy, const void* x,
                                  const void* weight, void* workspace, size_t workspace_bytes,
                                  int64_t rows, int64_t hidden, float eps,
                                  const norm_launch_cfg* cfg, hipStream_t stream) {
-    BwdArgs a{dx, dy, x, nullptr, nullptr, nullptr, weight, (float*)workspace, dweight, nullptr,
-              rows, 0, 0.0f};
-    return run_bwd(NORM_OP_RMSNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
+    return norm_rmsnorm_bwd_ex(dx, hidden, dweight, dy, hidden, x, hidden, weight, workspace,
+                               workspace_bytes, rows, hidden, eps, cfg, stream);
 }
 
 norm_status norm_rmsnorm_bwd(void* dx, float* dweight, const void* dy, const void* x,
@@ -360,14 +709,27 @@ norm_status norm_rmsnorm_bwd(void* dx, float* dweight, const void* dy, const voi
                                 hidden, eps, nullptr, stream);
 }
 
+norm_status norm_fused_add_rmsnorm_bwd_ex(void* ds, int64_t ld_ds, float* dweight,
+                                          const void* dout, int64_t ld_dout, const void* dres,
+                                          int64_t ld_dres, const void* s, int64_t ld_s,
+                                          const void* weight, void* workspace,
+                                          size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                          float eps, const norm_launch_cfg* cfg,
+                                          hipStream_t stream) {
+    const BwdCall c{ds,      ld_ds,   dout,   ld_dout, s,         ld_s,  nullptr,
+                    nullptr, dres,    ld_dres, weight, workspace, workspace_bytes,
+                    dweight, nullptr, rows,    hidden, eps};
+    return run_bwd(NORM_OP_FUSED_ADD_RMSNORM_BWD, c, cfg, stream);
+}
+
 norm_status norm_fused_add_rmsnorm_bwd_cfg(void* ds, float* dweight, const void* dout,
                                            const void* dres, const void* s, const void* weight,
                                            void* workspace, size_t workspace_bytes, int64_t rows,
                                            int64_t hidden, float eps, const norm_launch_cfg* cfg,
                                            hipStream_t stream) {
-    BwdArgs a{ds, dout, s, nullptr, nullptr, dres, weight, (float*)workspace, dweight, nullptr,
-              rows, 0, 0.0f};
-    return run_bwd(NORM_OP_FUSED_ADD_RMSNORM_BWD, a, hidden, eps, workspace_bytes, cfg, stream);
+    return norm_fused_add_rmsnorm_bwd_ex(ds, hidden, dweight, dout, hidden, dres, hidden, s,
+                                         hidden, weight, workspace, workspace_bytes, rows, hidden,
+                                         eps, cfg, stream);
 }
 
 norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const void* dout,
@@ -378,45 +740,29 @@ norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const void* dou
                                           workspace_bytes, rows, hidden, eps, nullptr, stream);
 }
 
-static size_t ws_bytes_for(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg* cfg) {
-    if (rows <= 0 || !hidden_supported(hidden)) return 0;
-    const int32_t g = (cfg && cfg->grid > 0) ? cfg->grid : default_bwd_grid(rows);
-    return bwd_workspace_bytes(op, hidden, g);
-}
-
+// ---- queries ---------------------------------------------------------------------------
 size_t norm_layernorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
-    return ws_bytes_for(NORM_OP_LAYERNORM_BWD, rows, hidden, nullptr);
+    return ws_query(NORM_OP_LAYERNORM_BWD, rows, hidden, nullptr);
 }
 
 size_t norm_layernorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                               const norm_launch_cfg* cfg) {
-    return ws_bytes_for(NORM_OP_LAYERNORM_BWD, rows, hidden, cfg);
+    return ws_query(NORM_OP_LAYERNORM_BWD, rows, hidden, cfg);
 }
 
 size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
-    return ws_bytes_for(NORM_OP_RMSNORM_BWD, rows, hidden, nullptr);
+    return ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, nullptr);
 }
 
 size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                             const norm_launch_cfg* cfg) {
-    return ws_bytes_for(NORM_OP_RMSNORM_BWD, rows, hidden, cfg);
+    return ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, cfg);
 }
 
 norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
                                norm_launch_cfg* cfg) {
     if (!cfg || rows < 0 || (int)op < 0 || (int)op > 5) return NORM_ERROR_INVALID_VALUE;
-    if (!hidden_supported(hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
-    if (is_bwd(op)) {
-        *cfg = choose_bwd(op, rows, hidden);
-        return NORM_SUCCESS;
-    }
-    int cu = cu_count;
-    if (cu <= 0) {
-        const norm_status st = current_cu_count(&cu);
-        if (st != NORM_SUCCESS) return st;
-    }
-    *cfg = choose_fwd(op, rows, hidden, cu);
-    return NORM_SUCCESS;
+    return select(op, rows, hidden, cu_count, cfg);
 }
 
 int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
@@ -425,35 +771,64 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                                          "layernorm_bwd",     "rmsnorm_bwd", "fused_add_rmsnorm_bwd"};
     norm_launch_cfg c;
     if (norm_select_config(op, rows, hidden, cu_count, &c) != NORM_SUCCESS) return -1;
-    const int vecs = (int)(hidden / (8 * c.threads_per_row));
-    char tmp[512];
+    const bool dyn = c.vector_elems != 0;
+    const int w = dyn ? c.vector_elems : 8;
+    int vecs = (int)(hidden / (w * c.threads_per_row));
+    int depth = 0;
+    if (dyn && is_bwd(op)) {
+        const DynBwdEntry* e = find_dyn(dyn_bwd_table(op), hidden, w, c.threads_per_row);
+        vecs = e->vecs;
+        depth = e->depth;
+    } else if (dyn) {
+        vecs = find_dyn(dyn_fwd_table(op), hidden, w, c.threads_per_row)->vecs;
+    } else if (is_bwd(op)) {
+        depth = find_bwd(op, hidden, c.threads_per_row)->depth;
+    }
+    char tmp[640];
     int n;
     if (is_bwd(op)) {
-        const int depth = bwd_depth_of(op, hidden, c.threads_per_row);
-        n = std::snprintf(tmp, sizeof tmp,
-                          "%s rows=%lld hidden=%lld: %s_bwd_rows_kernel<%lld,%d,%d%s> "
-                          "(%d lanes per row, %d vectors per lane, ring of %d rows) on a "
-                          "persistent grid of %d workgroups, then norm_bwd_colreduce_kernel "
-                          "(%lld workgroups of %d); workspace %zu bytes",
-                          kNames[op], (long long)rows, (long long)hidden,
+        const int64_t slabs = (int64_t)c.grid * c.rows_per_block;
+        const int64_t padded = dyn ? dyn_padded_hidden(hidden) : hidden;
+        char kern[96];
+        if (dyn)
+            std::snprintf(kern, sizeof kern, "norm_bwd_dyn_rows_kernel<%d,%d,%d,%d,%s>", w,
+                          c.threads_per_row, vecs, depth,
+                          op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?");
+        else
+            std::snprintf(kern, sizeof kern, "%s_bwd_rows_kernel<%lld,%d,%d%s>",
                           op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm",
                           (long long)hidden, c.threads_per_row, depth,
-                          op == NORM_OP_LAYERNORM_BWD ? "" : ",dres?", c.threads_per_row, vecs,
-                          depth, c.grid,
-                          (long long)(bwd_outs(op) * hidden / kColReduceCols), kColReduceThreads,
-                          bwd_workspace_bytes(op, hidden, rows > 0 ? c.grid : 0));
-    } else {
-        const char* kern = op == NORM_OP_FUSED_ADD_RMSNORM ? "fused_add_rmsnorm_kernel"
-                           : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd_kernel"
-                                                           : "layernorm_fwd_kernel";
+                          op == NORM_OP_LAYERNORM_BWD ? "" : ",dres?");
         n = std::snprintf(tmp, sizeof tmp,
-                          "%s rows=%lld hidden=%lld: %s<%lld,%d,%d> (%d lanes per row, %d rows "
-                          "per workgroup of %d, %d vectors per lane), grid %lld",
+                          "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
+                          "workgroup, %d %d-byte accesses per lane, ring of %d rows) on a "
+                          "persistent grid of %d workgroups, then norm_bwd_colreduce_kernel "
+                          "(%lld workgroups of %d) over %lld slabs; workspace %zu bytes",
                           kNames[op], (long long)rows, (long long)hidden, kern,
-                          (long long)hidden, c.threads_per_row, c.rows_per_block,
-                          c.threads_per_row, c.rows_per_block,
-                          c.threads_per_row * c.rows_per_block, vecs,
-                          (long long)((rows + c.rows_per_block - 1) / c.rows_per_block));
+                          c.threads_per_row, c.rows_per_block, vecs, 2 * w, depth, c.grid,
+                          (long long)(bwd_outs(op) * padded / kColReduceCols), kColReduceThreads,
+                          (long long)slabs,
+                          dyn ? dyn_ws_bytes(op, hidden, rows > 0 ? slabs : 0)
+                              : static_ws_bytes(op, hidden, rows > 0 ? c.grid : 0));
+    } else {
+        const char* kern = op == NORM_OP_FUSED_ADD_RMSNORM ? "fused_add_rmsnorm"
+                           : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd"
+                                                           : "layernorm_fwd";
+        char inst[96];
+        if (dyn)
+            std::snprintf(inst, sizeof inst, "%s_dyn_kernel<%d,%d,%d>", kern, w,
+                          c.threads_per_row, vecs);
+        else
+            std::snprintf(inst, sizeof inst, "%s_kernel<%lld,%d,%d>", kern, (long long)hidden,
+                          c.threads_per_row, c.rows_per_block);
+        const int block = dyn ? dyn_block_size(c.threads_per_row)
+                              : c.threads_per_row * c.rows_per_block;
+        n = std::snprintf(tmp, sizeof tmp,
+                          "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
+                          "workgroup of %d, %d %d-byte accesses per lane), grid %lld",
+                          kNames[op], (long long)rows, (long long)hidden, inst,
+                          c.threads_per_row, c.rows_per_block, block, vecs, 2 * w,
+                          (long long)ceil_div(rows, c.rows_per_block));
     }
     if (n < 0) return -1;
     if (buf && len > 0) {
@@ -466,19 +841,25 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
 
 int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int32_t capacity) {
     int32_t n = 0;
-    if ((int)op < 0 || (int)op > 5) return 0;
-    if (is_bwd(op)) {
-        for (const BwdEntry& e : bwd_table(op)) {
-            if (e.hidden != hidden) continue;
-            if (out && n < capacity) out[n] = norm_launch_cfg{e.lanes, 1, 0};
-            ++n;
-        }
-        return n;
-    }
-    for (const FwdEntry& e : fwd_table(op)) {
-        if (e.hidden != hidden) continue;
-        if (out && n < capacity) out[n] = norm_launch_cfg{e.lanes, e.rows_per_block, 0};
+    if ((int)op < 0 || (int)op > 5 || hidden < 1 || hidden > kMaxHidden) return 0;
+    auto put = [&](norm_launch_cfg c) {
+        if (out && n < capacity) out[n] = c;
         ++n;
+    };
+    if (is_bwd(op)) {
+        for (const BwdEntry& e : bwd_table(op))
+            if (e.hidden == hidden) put(norm_launch_cfg{e.lanes, 1, 0, 0});
+    } else {
+        for (const FwdEntry& e : fwd_table(op))
+            if (e.hidden == hidden) put(norm_launch_cfg{e.lanes, e.rows_per_block, 0, 0});
+    }
+    // run-time-hidden shapes at the widest access a contiguous row allows
+    const int w = shape_width(hidden, {});
+    for (int lanes = 8; lanes <= 1024; lanes *= 2) {
+        if (lanes > 8 && lanes / 2 >= hidden / w) break;
+        const bool ok = is_bwd(op) ? find_dyn(dyn_bwd_table(op), hidden, w, lanes) != nullptr
+                                   : find_dyn(dyn_fwd_table(op), hidden, w, lanes) != nullptr;
+        if (ok) put(norm_launch_cfg{lanes, dyn_rows_per_block(lanes), 0, w});
     }
     return n;
 }

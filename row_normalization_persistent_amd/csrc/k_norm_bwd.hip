@@ -130,7 +130,9 @@ __device__ __forceinline__ void rms_bwd_row(const RmsRow<V, DRES>& cur, const fl
     float s1 = ((a1[0] + a1[1]) + (a1[2] + a1[3])) + ((a1[4] + a1[5]) + (a1[6] + a1[7]));
     float s2 = ((a2[0] + a2[1]) + (a2[2] + a2[3])) + ((a2[4] + a2[5]) + (a2[6] + a2[7]));
     row_sum2<T>(s1, s2, red, lane);
-    const float rstd = fast_rsqrt(s1 * (1.0f / H) + eps);
+    // a row past the end (all zeros) must add exactly nothing to the column
+    // sums, also at eps = 0, where rsqrt(0) is inf and 0 * inf is NaN
+    const float rstd = row < rows ? fast_rsqrt(s1 * (1.0f / H) + eps) : 0.0f;
     const float coef = rstd * rstd * rstd * s2 * (1.0f / H);  // rstd * mean_j(g * xhat) * rstd
     const rsrc_t rdx = row_rsrc(dx, row, rows, H * 2);  // drops the stores of rows >= rows
 #pragma unroll
@@ -273,23 +275,25 @@ __global__ __launch_bounds__(T) void rmsnorm_bwd_rows_kernel(
 }
 
 // Column reduce.  A workgroup owns kColReduceCols = 64 consecutive columns of
-// the flat [outs][H] slab (dweight columns, then dbias columns); its 256 lanes
+// the flat [outs][padded] slab (dweight columns, then dbias columns; padded is
+// a multiple of 64, so a workgroup never straddles two outputs); its 256 lanes
 // form 16 column groups of 4 columns x 16 slab streams.  Stream s adds the
 // slabs s, s + 16, s + 32, ... (16 independent loads in flight per pass, so
 // the default 256 slabs take one memory round trip; slabs past the last are
 // range-checked to zero by the workspace descriptor), then the 16 stream sums
 // of each column are added in stream order.  The summation order is fixed,
-// so the result is bit-reproducible.
+// so the result is bit-reproducible.  Columns in the padding (hidden <= j <
+// padded) are summed but not stored.
 __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
-    const float* __restrict__ workspace, int32_t grid_slabs, int32_t hidden, int32_t outs,
-    float* __restrict__ dweight, float* __restrict__ dbias) {
+    const float* __restrict__ workspace, int32_t grid_slabs, int32_t hidden, int32_t padded,
+    int32_t outs, float* __restrict__ dweight, float* __restrict__ dbias) {
     constexpr int kGroups = kColReduceCols / 4;                // 16 groups of 4 columns
     constexpr int kStreams = kColReduceThreads / kGroups;      // 16 slab streams
     constexpr int kUnroll = 16;
     const int cg = threadIdx.x % kGroups;
     const int stream = threadIdx.x / kGroups;
-    const int flat = blockIdx.x * kColReduceCols + cg * 4;     // < outs * hidden
-    const int slab_bytes = outs * hidden * 4;
+    const int flat = blockIdx.x * kColReduceCols + cg * 4;     // < outs * padded
+    const int slab_bytes = outs * padded * 4;
     const rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(workspace), (short)0, grid_slabs * slab_bytes, kRsrcWord3);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -311,12 +315,23 @@ __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
         f32x4 s = part[0][cg];
 #pragma unroll
         for (int i = 1; i < kStreams; ++i) s += part[i][cg];
-        float* dst = flat < hidden ? dweight + flat : dbias + (flat - hidden);
-        dst[0] = s.x;
-        dst[1] = s.y;
-        dst[2] = s.z;
-        dst[3] = s.w;
+        const int o = flat / padded;
+        const int col = flat - o * padded;
+        float* dst = (o == 0 ? dweight : dbias) + col;
+        if (col + 0 < hidden) dst[0] = s.x;
+        if (col + 1 < hidden) dst[1] = s.y;
+        if (col + 2 < hidden) dst[2] = s.z;
+        if (col + 3 < hidden) dst[3] = s.w;
     }
+}
+
+hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t hidden,
+                                 int32_t padded, int32_t outs, float* dweight, float* dbias,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(norm_bwd_colreduce_kernel, dim3(outs * padded / kColReduceCols),
+                       dim3(kColReduceThreads), 0, stream, workspace, slabs, hidden, padded, outs,
+                       dweight, dbias);
+    return hipGetLastError();
 }
 
 // Rows in flight per workgroup (the register ring depth): the deepest ring
@@ -342,11 +357,9 @@ constexpr int bwd_depth() {
 
 template <int H, int T>
 hipError_t launch_colreduce(const BwdArgs& a, int outs, hipStream_t stream) {
-    const int slabs = a.rows > 0 ? a.grid : 0;
-    hipLaunchKernelGGL(norm_bwd_colreduce_kernel, dim3(outs * H / kColReduceCols),
-                       dim3(kColReduceThreads), 0, stream, (const float*)a.workspace, slabs, H,
-                       outs, a.dweight, a.dbias);
-    return hipGetLastError();
+    static_assert(H % kColReduceCols == 0, "compiled hidden sizes need no padding");
+    return launch_norm_colreduce(a.workspace, a.rows > 0 ? a.grid : 0, H, H, outs, a.dweight,
+                                 a.dbias, stream);
 }
 
 template <int H, int T>

@@ -1,0 +1,237 @@
+// Forward kernels of the run-time-hidden path (layout and masking rules in
+// dyn_common.hpp).  Same arithmetic as the compiled-hidden kernels: the fused
+// residual-add + RMSNorm ("optimize inner persistent scheduler for static
+// fusion", author description and changes walkthrough), RMSNorm and LayerNorm
+// ("TMA inner persistent scheduler", description summary); hidden, the row
+// strides and 1/hidden are kernel arguments instead of constants.
+//
+// Template parameters: W elements per access, T lanes per row, V accesses per
+// lane.  A workgroup of dyn_block<T>() lanes holds R = block / T rows; row
+// group g of workgroup k normalizes row k*R + g.
+#pragma once
+
+#include <type_traits>
+#include <utility>
+
+#include "dyn_common.hpp"
+#include "launch.hpp"
+
+namespace rownorm {
+
+template <int W, int T>
+__device__ __forceinline__ int dyn_off(int b, int lane) { return (b * T + lane) * (2 * W); }
+
+template <int W, int T, int V>
+__global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(DynFwdArgs a) {
+    constexpr int R = dyn_block<T>() / T;
+    __shared__ float red[dyn_red_floats<T>()];
+    const int lane = threadIdx.x % T;
+    const int g = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + g;
+    const int rb = a.hidden * 2;
+    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
+    const rsrc_t rr = row_rsrc_ld(a.residual, row, a.rows, a.ld_res * 2, rb);
+    const rsrc_t ro = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
+    raw_t<W> xv[V], rv[V], wv[V];
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
+        rv[b] = aload<W, kCachePolicyNT>(rr, dyn_off<W, T>(b, lane));
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+    issue_fence();
+    float acc = 0.0f;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W], rf[W], sv[W];
+        aunpack<W>(xv[b], xf);
+        aunpack<W>(rv[b], rf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            sv[k] = xf[k] + rf[k];
+            acc += sv[k] * sv[k];  // accesses past the row's end are 0 + 0
+        }
+        astore<W, kCachePolicyNT>(rr, dyn_off<W, T>(b, lane), apack<W>(sv));
+    }
+    const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
+    const float rstd = fast_rsqrt(ss / (float)a.hidden + a.eps);
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W], rf[W], wf[W], o[W];
+        aunpack<W>(xv[b], xf);
+        aunpack<W>(rv[b], rf);
+        aunpack<W>(wv[b], wf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) o[k] = (xf[k] + rf[k]) * rstd * wf[k];
+        astore<W, kCachePolicyNT>(ro, dyn_off<W, T>(b, lane), apack<W>(o));
+    }
+}
+
+template <int W, int T, int V>
+__global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdArgs a) {
+    constexpr int R = dyn_block<T>() / T;
+    __shared__ float red[dyn_red_floats<T>()];
+    const int lane = threadIdx.x % T;
+    const int g = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + g;
+    const int rb = a.hidden * 2;
+    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
+    const rsrc_t ro = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
+    raw_t<W> xv[V], wv[V];
+#pragma unroll
+    for (int b = 0; b < V; ++b) xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+    issue_fence();
+    float acc = 0.0f;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W];
+        aunpack<W>(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc += xf[k] * xf[k];
+    }
+    const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
+    const float rstd = fast_rsqrt(ss / (float)a.hidden + a.eps);
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W], wf[W], o[W];
+        aunpack<W>(xv[b], xf);
+        aunpack<W>(wv[b], wf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) o[k] = xf[k] * rstd * wf[k];
+        astore<W, kCachePolicyNT>(ro, dyn_off<W, T>(b, lane), apack<W>(o));
+    }
+}
+
+template <int W, int T, int V>
+__global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFwdArgs a) {
+    constexpr int R = dyn_block<T>() / T;
+    constexpr int kRed = dyn_red_floats<T>();
+    __shared__ float red[2 * kRed];  // mean and variance use different slots: one barrier each
+    const int lane = threadIdx.x % T;
+    const int g = threadIdx.x / T;
+    const int64_t row = (int64_t)blockIdx.x * R + g;
+    const int rb = a.hidden * 2;
+    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
+    const rsrc_t ry = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
+    const rsrc_t rbias = row_rsrc_ld(a.bias, 0, 1, 0, rb);
+    raw_t<W> xv[V], wv[V], bv[V];
+#pragma unroll
+    for (int b = 0; b < V; ++b) xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+        bv[b] = aload<W, 0>(rbias, dyn_off<W, T>(b, lane));
+    }
+    issue_fence();
+    const float inv_h = 1.0f / (float)a.hidden;
+    float acc = 0.0f;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W];
+        aunpack<W>(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) acc += xf[k];
+    }
+    const float mu = dyn_row_sum<T>(acc, red + g * (T / kWave), lane) * inv_h;
+    float acc2 = 0.0f;
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        // an access past the row's end holds zeros, but (0 - mu)^2 must not count
+        const bool in_row = (b * T + lane) * W < a.hidden;
+        float xf[W];
+        aunpack<W>(xv[b], xf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const float d = in_row ? xf[k] - mu : 0.0f;
+            acc2 += d * d;
+        }
+    }
+    const float var = dyn_row_sum<T>(acc2, red + kRed + g * (T / kWave), lane) * inv_h;
+    const float rstd = fast_rsqrt(var + a.eps);
+    if (a.mean != nullptr && lane == 0 && row < a.rows) {
+        a.mean[row] = mu;
+        a.rstd[row] = rstd;
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        float xf[W], wf[W], bf[W], o[W];
+        aunpack<W>(xv[b], xf);
+        aunpack<W>(wv[b], wf);
+        aunpack<W>(bv[b], bf);
+#pragma unroll
+        for (int k = 0; k < W; ++k) o[k] = (xf[k] - mu) * rstd * wf[k] + bf[k];
+        astore<W, kCachePolicyNT>(ry, dyn_off<W, T>(b, lane), apack<W>(o));
+    }
+}
+
+struct OpFusedDyn {};
+struct OpRmsDyn {};
+struct OpLnFwdDyn {};
+
+template <class Op, int W, int T, int V>
+hipError_t launch_fwd_dyn(const DynFwdArgs& a, hipStream_t stream) {
+    constexpr int R = dyn_block<T>() / T;
+    const dim3 grid((unsigned)((a.rows + R - 1) / R));
+    const dim3 block(dyn_block<T>());
+    if constexpr (std::is_same_v<Op, OpFusedDyn>)
+        hipLaunchKernelGGL((fused_add_rmsnorm_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+    else if constexpr (std::is_same_v<Op, OpRmsDyn>)
+        hipLaunchKernelGGL((rmsnorm_fwd_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((layernorm_fwd_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+// Accesses per lane compiled for each width: every count up to 8 for 16-byte
+// accesses, powers of two for the narrower ones (rarer layouts, where the
+// host rounds the count up and the extra accesses fall past the row's end).
+template <int W>
+using DynVecs = std::conditional_t<W == 8, std::integer_sequence<int, 1, 2, 3, 4, 5, 6, 7, 8>,
+                                   std::integer_sequence<int, 1, 2, 4, 8>>;
+
+// LayerNorm keeps x, weight and bias in registers; at 1024 lanes (128 VGPRs a
+// lane) more than 6 16-byte accesses per lane would spill.
+template <class Op, int W, int T, int V>
+constexpr bool dyn_fwd_fits() {
+    return !(std::is_same_v<Op, OpLnFwdDyn> && T == 1024 && V * W > 48);
+}
+
+template <class Op, int W, int T, int V>
+void add_dyn_fwd_one(std::vector<DynFwdEntry>& v) {
+    if constexpr (dyn_fwd_fits<Op, W, T, V>()) v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V>});
+}
+
+template <class Op, int W, int T, int... Vs>
+void add_dyn_fwd(std::vector<DynFwdEntry>& v, std::integer_sequence<int, Vs...>) {
+    (add_dyn_fwd_one<Op, W, T, Vs>(v), ...);
+}
+
+template <class Op, int W>
+void add_dyn_fwd_w(std::vector<DynFwdEntry>& v) {
+    add_dyn_fwd<Op, W, 8>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 16>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 32>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 64>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 128>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 256>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 512>(v, DynVecs<W>{});
+    add_dyn_fwd<Op, W, 1024>(v, DynVecs<W>{});
+}
+
+template <class Op>
+std::vector<DynFwdEntry> build_dyn_fwd_table() {
+    std::vector<DynFwdEntry> v;
+    add_dyn_fwd_w<Op, 8>(v);
+    add_dyn_fwd_w<Op, 4>(v);
+    add_dyn_fwd_w<Op, 2>(v);
+    add_dyn_fwd_w<Op, 1>(v);
+    return v;
+}
+
+}  // namespace rownorm

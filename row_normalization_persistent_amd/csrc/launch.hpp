@@ -61,6 +61,75 @@ const std::vector<FwdEntry>& layernorm_fwd_table();
 const std::vector<BwdEntry>& layernorm_bwd_table();
 const std::vector<BwdEntry>& rmsnorm_bwd_table();
 
+// ---- run-time-hidden path -------------------------------------------------------
+// Leading dimensions (row strides) are in elements; every pointer is aligned
+// to the access width (2*elems bytes) and hidden % elems == 0.
+struct DynFwdArgs {
+    void* out;             // fused/rms: out; layernorm: y
+    void* residual;        // fused only (in/out)
+    const void* x;
+    const void* weight;
+    const void* bias;      // layernorm only
+    float* mean;           // layernorm only (may be null together with rstd)
+    float* rstd;
+    int64_t ld_out, ld_res, ld_x;
+    int64_t rows;
+    int32_t hidden;
+    float eps;
+};
+
+struct DynBwdArgs {
+    void* dx;
+    const void* dy;
+    const void* x;
+    const float* mean;     // LayerNorm only
+    const float* rstd;     // LayerNorm only
+    const void* dres;      // RMSNorm-fused only, or null
+    const void* weight;
+    float* workspace;      // [grid * walkers per workgroup][outs][padded hidden] fp32
+    float* dweight;
+    float* dbias;          // LayerNorm only
+    int64_t ld_dx, ld_dy, ld_x, ld_dres;
+    int64_t rows;
+    int32_t hidden;
+    int32_t grid;
+    float eps;             // RMSNorm only
+};
+
+using DynFwdLauncher = hipError_t (*)(const DynFwdArgs&, hipStream_t);
+using DynBwdLauncher = hipError_t (*)(const DynBwdArgs&, hipStream_t);
+
+struct DynFwdEntry {
+    int elems, lanes, vecs;  // access width W, lanes per row T, accesses per lane V
+    DynFwdLauncher launch;
+};
+
+struct DynBwdEntry {
+    int elems, lanes, vecs, depth;
+    DynBwdLauncher launch;
+};
+
+const std::vector<DynFwdEntry>& fused_add_rmsnorm_dyn_table();
+const std::vector<DynFwdEntry>& rmsnorm_fwd_dyn_table();
+const std::vector<DynFwdEntry>& layernorm_fwd_dyn_table();
+const std::vector<DynBwdEntry>& layernorm_bwd_dyn_table();
+const std::vector<DynBwdEntry>& rmsnorm_bwd_dyn_table();
+
+// Workgroup size of the run-time path for T lanes per row: rows narrower than
+// 256 lanes are packed 256 / T to a workgroup.
+constexpr int dyn_block_size(int lanes) { return lanes < 256 ? 256 : lanes; }
+constexpr int dyn_rows_per_block(int lanes) { return dyn_block_size(lanes) / lanes; }
+// Partial-sum slabs pad each output's hidden columns to a multiple of the
+// column reduce's 64-column tile.
+constexpr int64_t dyn_padded_hidden(int64_t hidden) { return (hidden + 63) / 64 * 64; }
+
+// Column reduce shared by both paths: out[o][j] = sum over slabs s of
+// ws[s][o][j] for j < hidden, o < outs (dweight, then dbias); slabs hold
+// `padded` floats per output.  Defined with the backward kernels.
+hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t hidden,
+                                 int32_t padded, int32_t outs, float* dweight, float* dbias,
+                                 hipStream_t stream);
+
 // Column-reduce geometry of LayerNorm backward.
 constexpr int kColReduceThreads = 256;
 constexpr int kColReduceCols = 64;  // flat [2][hidden] columns per workgroup

@@ -28,7 +28,10 @@ def test_header_declares_the_four_operations():
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
                "norm_layernorm_bwd", "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd"):
         assert op in names
-    assert len(names) == 20
+    for op in list(names):
+        if op.endswith("_ex"):
+            assert op[:-3] in names  # every strided variant has a plain form
+    assert len(names) == 26
 
 
 def test_library_exports_every_declared_symbol():
@@ -56,13 +59,49 @@ def test_status_strings():
 def test_compiled_shapes_cover_every_hidden_size():
     for op in rn.OPS:
         for h in rn.HIDDEN_SIZES:
-            cfgs = rn.list_configs(op, h)
+            cfgs = [c for c in rn.list_configs(op, h) if not c.runtime_hidden]
             assert cfgs, (op, h)
             for c in cfgs:
                 assert c.threads_per_row % 64 == 0
                 assert h % (8 * c.threads_per_row) == 0
                 assert c.threads_per_row * c.rows_per_block <= 1024
-        assert rn.list_configs(op, 3000) == []
+        assert rn.list_configs(op, 0) == []
+        assert rn.list_configs(op, 70000) == []
+
+
+def test_runtime_hidden_shapes():
+    # any hidden gets run-time shapes at the widest access the row allows
+    for op in rn.OPS:
+        for h, w in ((1, 1), (3000, 8), (4100, 4), (130, 2), (127, 1), (4096, 8), (5120, 8)):
+            cfgs = [c for c in rn.list_configs(op, h) if c.runtime_hidden]
+            assert cfgs, (op, h)
+            for c in cfgs:
+                t = c.threads_per_row
+                assert c.vector_elems == w
+                assert t in (8, 16, 32, 64, 128, 256, 512, 1024)
+                assert c.rows_per_block == max(1, 256 // t)
+                assert t // 2 < max(h // w, 1) or t == 8  # no shape with half its lanes idle
+            sel = rn.select_config(op, 4096, h, cu_count=256)
+            assert sel.runtime_hidden == (h not in rn.HIDDEN_SIZES)
+            if sel.runtime_hidden:
+                assert sel in cfgs or rn.OPS[op] >= 3, (op, h, sel)
+    # the widest rows each family holds
+    assert rn.select_config("fused_add_rmsnorm", 64, 65536, cu_count=256).threads_per_row == 1024
+    for op, h in (("layernorm_fwd", 49152 + 8), ("rmsnorm_fwd", 65536 + 8),
+                  ("layernorm_bwd", 16384 + 8), ("rmsnorm_bwd", 8193)):
+        with pytest.raises(rn.NormError) as e:
+            rn.select_config(op, 64, h, cu_count=256)
+        assert e.value.status == UNSUPPORTED
+    # small-batch rule on the run-time path: fewer rows -> more lanes per row
+    prev = 1 << 30
+    for rows in (1, 16, 256, 1024, 2048):  # (from 16 * CUs rows on, at most 4 accesses a lane)
+        c = rn.select_config("rmsnorm_fwd", rows, 5120, cu_count=256)
+        assert c.threads_per_row <= prev
+        prev = c.threads_per_row
+    # tiny rows share a wave; backward rows get one access per lane
+    assert rn.select_config("rmsnorm_fwd", 1 << 16, 64, cu_count=256).threads_per_row == 8
+    assert rn.select_config("rmsnorm_bwd", 8192, 128).threads_per_row == 16
+    assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 1024
 
 
 def test_select_config_small_batches_spread_rows_over_more_lanes():
@@ -86,7 +125,7 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
                 assert h // (8 * c.threads_per_row) <= 8  # at most 8 vectors per lane
     for h in rn.HIDDEN_SIZES:
         c = rn.select_config("layernorm_bwd", 8192, h)
-        assert rn.Cfg(c.threads_per_row, 1, 0) in rn.list_configs("layernorm_bwd", h)
+        assert rn.Cfg(c.threads_per_row, 1, 0, 0) in rn.list_configs("layernorm_bwd", h)
         assert c.grid == 256
         assert rn.select_config("layernorm_bwd", 5, h).grid == 5
 
@@ -98,7 +137,12 @@ def test_describe_config():
     d = rn.describe_config("layernorm_bwd", 8192, 4096, cu_count=256)
     assert "persistent grid of 256" in d and f"workspace {rn.workspace_bytes(8192, 4096)}" in d
     with pytest.raises(rn.NormError):
-        rn.describe_config("rmsnorm_fwd", 4, 1000, cu_count=256)
+        rn.describe_config("rmsnorm_fwd", 4, 70000, cu_count=256)
+    d = rn.describe_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
+    c = rn.select_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
+    assert f"rmsnorm_fwd_dyn_kernel<8,{c.threads_per_row}," in d
+    d = rn.describe_config("layernorm_bwd", 8192, 100)
+    assert "norm_bwd_dyn_rows_kernel<4," in d and f"workspace {rn.workspace_bytes(8192, 100)}" in d
     L = rn.lib()
     buf = ctypes.create_string_buffer(8)  # truncated, still NUL-terminated
     n = L.norm_describe_config(0, 16, 4096, 256, buf, 8)
@@ -109,14 +153,20 @@ def test_describe_config():
 def test_workspace_bytes():
     for h in rn.HIDDEN_SIZES:
         g = rn.select_config("rmsnorm_bwd", 8192, h).grid
-        assert rn.workspace_bytes(8192, h, op="rmsnorm_bwd") == g * h * 4  # one slab
-        assert rn.workspace_bytes(8192, h, op="fused_add_rmsnorm_bwd") == g * h * 4
+        # without a shape: enough for the compiled kernels and for the
+        # run-time kernels at any access width (strided or narrow-aligned rows)
+        assert rn.workspace_bytes(8192, h, op="rmsnorm_bwd") >= g * h * 4  # one slab
+        assert rn.workspace_bytes(8192, h, op="fused_add_rmsnorm_bwd") >= g * h * 4
         c = rn.select_config("layernorm_bwd", 8192, h)
-        assert rn.workspace_bytes(8192, h) == c.grid * 2 * h * 4
-        assert rn.workspace_bytes(3, h) == 3 * 2 * h * 4  # never more slabs than rows
+        assert rn.workspace_bytes(8192, h) >= c.grid * 2 * h * 4
+        assert rn.workspace_bytes(8192, h) == 2 * rn.workspace_bytes(8192, h, op="rmsnorm_bwd")
         assert rn.workspace_bytes(0, h) == 0
         assert rn.workspace_bytes(100, h, rn.Cfg(256, 1, 7)) == 7 * 2 * h * 4
-    assert rn.workspace_bytes(10, 1000) == 0
+    assert rn.workspace_bytes(3, 4096) == 3 * 2 * 4096 * 4  # never more slabs than rows
+    # run-time shapes: one slab per row group, each output padded to 64 columns
+    assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 16 * 2 * 1024 * 4
+    assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
+    assert rn.workspace_bytes(10, 70000) == 0
     assert rn.workspace_bytes(-1, 4096) == 0
 
 
@@ -135,15 +185,19 @@ def test_fused_validation():
     assert fused(eps=float("nan")) == INVALID
     assert fused(eps=float("inf")) == INVALID
     assert fused(eps=-1e-6) == INVALID
-    assert fused(hidden=4000) == UNSUPPORTED
+    assert fused(hidden=70000) == UNSUPPORTED
     assert fused(hidden=0) == UNSUPPORTED
     assert fused(out=0) == INVALID
     assert fused(res=0) == INVALID
     assert fused(x=0) == INVALID
     assert fused(w=0) == INVALID
-    assert fused(x=A + 2 * MB + 8) == MISALIGNED
-    assert fused(res=A + MB + 2) == MISALIGNED
-    assert fused(w=A + 3 * MB + 4) == MISALIGNED
+    assert fused(x=A + 2 * MB + 1) == MISALIGNED  # bf16 needs 2 bytes
+    assert fused(res=A + MB + 1) == MISALIGNED
+    assert fused(w=A + 3 * MB + 1) == MISALIGNED
+    compiled = ctypes.byref(rn.LaunchCfg(64, 4, 0, 0))  # compiled shapes need 16 bytes
+    assert fused(x=A + 2 * MB + 8, cfg=compiled) == MISALIGNED
+    assert fused(w=A + 3 * MB + 4, cfg=compiled) == MISALIGNED
+    assert fused(hidden=4000, cfg=compiled) == UNSUPPORTED
     assert fused(res=A + 2 * MB) == INVALID   # residual may alias nothing
     assert fused(out=A + MB) == INVALID       # out == residual
     assert fused(out=A + 2 * MB + 64) == INVALID  # partial overlap with x
@@ -152,6 +206,12 @@ def test_fused_validation():
     assert fused(cfg=ctypes.byref(bad)) == INVALID  # not a compiled shape
     assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 4, 3))) == INVALID  # grid is bwd-only
     assert fused(cfg=ctypes.byref(rn.LaunchCfg(0, 1, 0))) == INVALID
+    # run-time-hidden shapes
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 1, 0, 8))) == INVALID  # rows per block is 4
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 4, 0, 3))) == INVALID  # not an access width
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(8, 32, 0, 8))) == INVALID  # row too wide for it
+    assert fused(hidden=4100, cfg=ctypes.byref(rn.LaunchCfg(512, 1, 0, 8))) == INVALID
+    assert fused(x=A + 2 * MB + 8, cfg=ctypes.byref(rn.LaunchCfg(512, 1, 0, 8))) == MISALIGNED
 
 
 def rms(out=A, x=A + MB, w=A + 2 * MB, rows=4, hidden=2048, eps=1e-6):
@@ -160,9 +220,9 @@ def rms(out=A, x=A + MB, w=A + 2 * MB, rows=4, hidden=2048, eps=1e-6):
 
 def test_rmsnorm_validation():
     assert rms(rows=0) == SUCCESS
-    assert rms(hidden=2049) == UNSUPPORTED
+    assert rms(hidden=65544) == UNSUPPORTED
     assert rms(out=0) == INVALID
-    assert rms(out=A + 8) == MISALIGNED
+    assert rms(out=A + 1) == MISALIGNED
     assert rms(out=A + MB + 16) == INVALID  # partial overlap with x
     assert rms(w=A + 32) == INVALID
 
@@ -175,12 +235,13 @@ def lnf(y=A, mean=A + MB, rstd=A + MB + 65536, x=A + 2 * MB, w=A + 3 * MB, b=A +
 def test_layernorm_fwd_validation():
     assert lnf(rows=0) == SUCCESS
     assert lnf(eps=-1.0) == INVALID
-    assert lnf(hidden=1000) == UNSUPPORTED
+    assert lnf(hidden=70000) == UNSUPPORTED
+    assert lnf(hidden=49152 + 8) == UNSUPPORTED  # LayerNorm's run-time kernels stop at 49152
     assert lnf(b=0) == INVALID
     assert lnf(mean=0) == INVALID   # mean and rstd are both given or both null
     assert lnf(rstd=0) == INVALID
     assert lnf(mean=A + MB + 2) == MISALIGNED
-    assert lnf(b=A + 3 * MB + 65536 + 8) == MISALIGNED
+    assert lnf(b=A + 3 * MB + 65536 + 1) == MISALIGNED
     assert lnf(mean=A + MB, rstd=A + MB + 8) == INVALID  # mean/rstd overlap
 
 
@@ -201,12 +262,14 @@ def test_layernorm_bwd_validation():
     assert lnb() == WORKSPACE
     assert lnb(rows=-2) == INVALID
     assert lnb(eps=float("nan")) == INVALID
-    assert lnb(hidden=5000) == UNSUPPORTED
+    assert lnb(hidden=16392) == UNSUPPORTED
+    assert lnb(hidden=5000) == WORKSPACE  # run-time kernels (workspace sized for 4096)
     assert lnb(dw=0) == INVALID
     assert lnb(ws=0) == INVALID
     assert lnb(dy=0) == INVALID
     assert lnb(mean=0) == INVALID
-    assert lnb(dx=A + 4) == MISALIGNED
+    assert lnb(dx=A + 1) == MISALIGNED
+    assert lnb(dx=A + 4) == WORKSPACE  # 4-byte alignment: narrower accesses
     assert lnb(mean=A + 4 * GB + 2) == MISALIGNED
     assert lnb(ws=A + 6 * GB + 4) == MISALIGNED
     assert lnb(db=A + GB + 4 * 4096 - 8) == INVALID  # dweight overlaps dbias
@@ -247,11 +310,14 @@ def test_rmsnorm_bwd_validation():
     assert rmsb(rows=-1) == INVALID
     assert rmsb(eps=-1.0) == INVALID
     assert rmsb(eps=float("nan")) == INVALID
-    assert rmsb(hidden=4095) == UNSUPPORTED
+    assert rmsb(hidden=16392) == UNSUPPORTED
+    assert rmsb(hidden=8193) == UNSUPPORTED  # odd rows: 2-byte accesses, at most 8192
+    assert rmsb(hidden=4095) == WORKSPACE
     assert rmsb(dw=0) == INVALID
     assert rmsb(x=0) == INVALID
-    assert rmsb(dy=A + 2 * GB + 8) == MISALIGNED
-    assert rmsb(dres=A + 4 * GB + 8) == MISALIGNED
+    assert rmsb(dy=A + 2 * GB + 1) == MISALIGNED
+    assert rmsb(dres=A + 4 * GB + 1) == MISALIGNED
+    assert rmsb(dy=A + 2 * GB + 8) == WORKSPACE
     assert rmsb(dx=A + 2 * GB) == WORKSPACE                 # dx == dy allowed
     assert rmsb(dx=A + 4 * GB, dres=A + 4 * GB) == WORKSPACE  # ds == dres allowed
     assert rmsb(dx=A + 3 * GB) == INVALID                   # dx == x is not
@@ -259,3 +325,49 @@ def test_rmsnorm_bwd_validation():
     assert rmsb(ws=A + 1 * GB + 64) == INVALID              # workspace over dweight
     assert rmsb(cfg=ctypes.byref(rn.LaunchCfg(512, 1, 4)),
                 ws_bytes=4 * 4096 * 4 - 1) == WORKSPACE
+
+
+# ---- strided rows (the _ex entry points) ---------------------------------------------
+def rmsb_ex(dx=A, ld_dx=4096, dw=A + GB, dy=A + 2 * GB, ld_dy=4096, x=A + 3 * GB, ld_x=4096,
+            w=A + 5 * GB, ws=A + 6 * GB, rows=8192, hidden=4096, eps=1e-6, cfg=None):
+    ws_bytes = rn.workspace_bytes(rows, hidden, op="rmsnorm_bwd") - 4
+    return rn.lib().norm_rmsnorm_bwd_ex(dx, ld_dx, dw, dy, ld_dy, x, ld_x, w, ws, ws_bytes,
+                                        rows, hidden, eps, cfg, None)
+
+
+def test_strided_validation():
+    assert rmsb_ex() == WORKSPACE
+    assert rmsb_ex(ld_x=4095) == INVALID           # ld < hidden
+    assert rmsb_ex(ld_x=1 << 41) == INVALID        # absurd stride
+    assert rmsb_ex(ld_x=3 * 4096) == WORKSPACE     # a column slice of a wider matrix
+    # dx and dy as two column slices of one [rows, 2 * hidden] matrix: their rows
+    # interleave without sharing an element
+    assert rmsb_ex(dx=A + 2 * GB, ld_dx=8192, dy=A + 2 * GB + 8192, ld_dy=8192) == WORKSPACE
+    # ... but shifted by half a row they do share elements
+    assert rmsb_ex(dx=A + 2 * GB, ld_dx=8192, dy=A + 2 * GB + 4096, ld_dy=8192) == INVALID
+    # the exact alias dx == dy needs equal strides
+    assert rmsb_ex(dx=A + 2 * GB, ld_dx=4096, dy=A + 2 * GB, ld_dy=4096) == WORKSPACE
+    assert rmsb_ex(dx=A + 2 * GB, ld_dx=8192, dy=A + 2 * GB, ld_dy=4096) == INVALID
+    # odd strides force 2-byte accesses: still accepted
+    assert rmsb_ex(ld_x=4097) == WORKSPACE
+    compiled = ctypes.byref(rn.LaunchCfg(512, 1, 0, 0))
+    assert rmsb_ex(ld_x=8192, cfg=compiled) == INVALID  # compiled shapes need contiguous rows
+    L = rn.lib()
+    # forward: out overlapping a slice of x, and a bad ld (rejected before any HIP call)
+    assert L.norm_rmsnorm_fwd_ex(A, 4096, A + 2, 8192, A + GB, 4, 4096, 1e-6, None,
+                                 None) == INVALID
+    assert L.norm_rmsnorm_fwd_ex(A, 4000, A + GB, 4096, A + 2 * GB, 4, 4096, 1e-6, None,
+                                 None) == INVALID
+    assert L.norm_fused_add_rmsnorm_ex(A, 4096, A + GB, 4096, A + 2 * GB, 4096, A + 3 * GB, 4,
+                                       70000, 1e-6, None, None) == UNSUPPORTED
+    assert L.norm_layernorm_fwd_ex(A, 4096, None, None, A + GB, 4095, A + 2 * GB, A + 3 * GB, 4,
+                                   4096, 1e-5, None, None) == INVALID
+    assert L.norm_layernorm_bwd_ex(A, 4096, A + GB, A + GB + 65536, A + 2 * GB, 4096,
+                                   A + 3 * GB, 4096, A + 4 * GB, A + 4 * GB + 65536, A + 5 * GB,
+                                   A + 6 * GB, 0, 8192, 4096, 1e-5, None, None) == WORKSPACE
+    assert L.norm_fused_add_rmsnorm_bwd_ex(A, 4096, A + GB, A + 2 * GB, 4096, A + 4 * GB, 4095,
+                                           A + 3 * GB, 4096, A + 5 * GB, A + 6 * GB, 0, 8192,
+                                           4096, 1e-6, None, None) == INVALID  # ld_dres < hidden
+    assert L.norm_fused_add_rmsnorm_bwd_ex(A, 4096, A + GB, A + 2 * GB, 4096, None, 0,
+                                           A + 3 * GB, 4096, A + 5 * GB, A + 6 * GB, 0, 8192,
+                                           4096, 1e-6, None, None) == WORKSPACE  # ld ignored

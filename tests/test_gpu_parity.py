@@ -162,7 +162,8 @@ def test_layernorm_bwd_every_compiled_shape(hidden):
     inp = lnb_inputs(75, hidden, seed=5)
     for c in rn.list_configs("layernorm_bwd", hidden):
         for grid in (1, 7, 75, 200):  # one slab, ragged, one row each, idle workgroups
-            check_lnb(inp, cfg=rn.Cfg(c.threads_per_row, 1, grid),
+            check_lnb(inp,
+                      cfg=rn.Cfg(c.threads_per_row, c.rows_per_block, grid, c.vector_elems),
                       what=f"layernorm_bwd h={hidden} {c} grid={grid}")
     check_lnb(inp, what="layernorm_bwd dx==dy", dx_is_dy=True)
 
@@ -279,7 +280,8 @@ def test_no_write_outside_outputs_and_every_output_written(rows):
         dy = dev(linp["dy"])
         rn.layernorm_bwd(dy, dev(linp["x"]), torch.from_numpy(linp["mean"]).to(DEV),
                          torch.from_numpy(linp["rstd"]).to(DEV), dev(linp["w"]),
-                         dx=dx.view(rows, h), cfg=rn.Cfg(c.threads_per_row, 1, 0))
+                         dx=dx.view(rows, h),
+                         cfg=rn.Cfg(c.threads_per_row, c.rows_per_block, 0, c.vector_elems))
         torch.cuda.synchronize()
         assert _guards_intact(big_dx, n), c
         assert not torch.isnan(dx.float()).any().item(), c

@@ -68,7 +68,7 @@ def test_every_compiled_shape_and_grid(hidden):
     nodres = dict(inp, dres=None)
     for c in rn.list_configs("rmsnorm_bwd", hidden):
         for grid in (1, 7, 75, 200):
-            cfg = rn.Cfg(c.threads_per_row, 1, grid)
+            cfg = rn.Cfg(c.threads_per_row, c.rows_per_block, grid, c.vector_elems)
             check(inp, fused=False, cfg=cfg, what=f"rmsnorm_bwd h={hidden} {cfg}")
             check(inp, fused=True, cfg=cfg, what=f"fused bwd h={hidden} {cfg}")
             check(nodres, fused=True, cfg=cfg, what=f"fused bwd no dres h={hidden} {cfg}")
