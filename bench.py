@@ -25,7 +25,11 @@ Also reported, on the same line:
   other_ops     RMSNorm / LayerNorm forward / LayerNorm backward / RMSNorm
                 backward / fused add + RMSNorm backward at their largest
                 workload: one graph of back-to-back launches over
-                >= 1.2 GB of buffer sets (cold reads), time per launch
+                >= 1.2 GB of buffer sets (cold reads), time per launch; then
+                the run-time-hidden kernels: fused add + RMSNorm at hidden
+                5120 and at 4096 (forced, against the compiled kernel), an
+                in-place RMSNorm over 128-wide column slices (row stride
+                384), LayerNorm and RMSNorm backward at hidden 5120
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
@@ -437,6 +441,81 @@ def other_ops(torch, rn, wl, dev, stream, reps):
     out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, 8 * h * rows + 6 * h, t,
                        note="dout, dres, s read; ds written; workspace not counted"))
     del xs, dys, drs, dxs, x0, dy0, dr0
+    torch.cuda.synchronize()
+    out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps)
+    return out
+
+
+def runtime_hidden_ops(torch, rn, wl, dev, stream, reps):
+    """The run-time-hidden kernels on shapes the compiled set does not cover,
+    and on the headline fused shape for a like-for-like comparison with the
+    compiled kernel."""
+    out = []
+    # fused add + RMSNorm: hidden 5120 (run-time), and hidden 4096 forced onto
+    # the run-time kernels in the shape the compiled path uses there
+    for h, forced in ((5120, False), (4096, True)):
+        rows = 8192
+        i = wl.fused_inputs(rows, h, seed=0)
+        n = _n_sets(4 * rows * h * 2)
+        x0, r0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["r"], dev)
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        rs = [r0] + [r0.clone() for _ in range(n - 1)]
+        ys = [torch.empty_like(x0) for _ in range(n)]
+        w = wl.to_device_bf16(i["w"], dev)
+        cfg = None
+        if forced:
+            c = rn.select_config("fused_add_rmsnorm", rows, h)
+            cfg = rn.Cfg(c.threads_per_row, c.rows_per_block, 0, 8)
+        t = graph_time_per_launch(torch, stream, [
+            (lambda j=j: rn.fused_add_rmsnorm(xs[j], rs[j], w, i["eps"], out=ys[j], cfg=cfg,
+                                              stream=stream))
+            for j in range(n)], reps)
+        out.append(_op_rec("fused_add_rmsnorm", rows, h, 8 * h * rows + 2 * h, t,
+                           note="run-time-hidden kernel" + (
+                               f" forced at a compiled hidden ({cfg})" if forced else "")))
+        del xs, rs, ys, x0, r0
+    # RMSNorm over 128-wide head slices of a [rows, 3 * 128] projection (row
+    # stride 384): the query/key normalization of a fused QKV output
+    rows, h, ld = 131072, 128, 384
+    i = wl.rmsnorm_inputs(rows, h, seed=0)
+    n = _n_sets(rows * ld * 2)
+    base0 = torch.zeros(rows, ld, dtype=torch.bfloat16, device=dev)
+    base0[:, :h] = wl.to_device_bf16(i["x"], dev)
+    bases = [base0] + [base0.clone() for _ in range(n - 1)]
+    w = wl.to_device_bf16(i["w"], dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_fwd(bases[j][:, :h], w, i["eps"], out=bases[j][:, :h],
+                                    stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_fwd", rows, h, 4 * h * rows + 2 * h, t,
+                       note=f"in place on a column slice with row stride {ld}"))
+    del bases, base0
+    # backward at hidden 5120
+    rows, h = 8192, 5120
+    i = wl.layernorm_bwd_inputs(rows, h, seed=0)
+    n = _n_sets(3 * rows * h * 2)
+    x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
+    w = wl.to_device_bf16(i["w"], dev)
+    zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+    _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
+    dxs = [torch.empty_like(x0) for _ in range(n)]
+    dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    ws = torch.empty(rn.workspace_bytes(rows, h), dtype=torch.uint8, device=dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
+                                      dweight=dw, dbias=db, workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
+                       note="run-time-hidden rows kernel + column reduce"))
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
+                                    workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
+                       note="run-time-hidden rows kernel + column reduce"))
+    del xs, dys, dxs, x0, dy0
     torch.cuda.synchronize()
     return out
 
