@@ -217,7 +217,7 @@ def main():
     kname = f"fused_add_rmsnorm_kernel<{HIDDEN}, {dom_key[0]}, {dom_key[1]}>"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic(kname),
+                "traffic": load_traffic(kname, [SWEEP_ROWS[i] for i in dom["idx"]]),
                 "kernel": kname, "launches_per_step": len(dom["idx"]),
                 "rows_per_launch": [SWEEP_ROWS[i] for i in dom["idx"]],
                 "algorithmic_bytes_per_launch": round(dom["avg_bytes"]),
@@ -293,30 +293,32 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def load_traffic(kernel: str):
+def load_traffic(kernel: str, rows):
     """HBM bytes per launch of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (profiles/traffic.json, written by
-    `bench.py --summarize-pmc`), or None when absent or taken from a different
-    kernel source."""
+    `bench.py --summarize-profiles`), or None when absent, taken from a
+    different kernel source, or taken over a different mix of row counts
+    (the launch choice changed since)."""
     path = os.path.join(PROFILES, "traffic.json")
-    if not os.path.exists(path):
-        return None
     try:
         t = json.load(open(path))
         entry = t["kernels"][kernel]
-    except (KeyError, ValueError):
+    except (KeyError, ValueError, OSError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    if sorted(entry.get("rows", [])) != sorted(rows):
         return None
     return round(entry["hbm_bytes_per_launch"])
 
 
 def kernel_source_digest() -> str:
+    """Digest of the sources that make the compiled forward kernels' code."""
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "row_normalization_persistent_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("device_common.hpp", "kernels_fwd.hpp", "api.hip"):
+    for name in ("device_common.hpp", "kernels_fwd.hpp", "launch.hpp"):
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
@@ -701,7 +703,8 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
                       "rows": sorted(g["rows"])}
     lines += ["", "Per-launch averages over each kernel's dispatches (the mix of row counts "
               "the sweep gives it) are in `profiles/traffic.json`, which `bench.py` reports as "
-              "`roofline.traffic` while the kernel sources are unchanged."]
+              "`roofline.traffic` while the kernel sources and the kernel's mix of row counts are "
+              "unchanged."]
     open(os.path.join(out_dir, "fused_add_rmsnorm_h4096_sweep_hbm_traffic.md"), "w").write(
         "\n".join(lines) + "\n")
     json.dump({"kernel_source_sha256": kernel_source_digest(),

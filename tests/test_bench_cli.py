@@ -1,5 +1,6 @@
 """bench.py host-side behaviour (CPU only): the one-GPU guard and the
-rocprofv3 summary arithmetic (FETCH_SIZE / WRITE_SIZE calibration)."""
+rocprofv3 summary arithmetic (FETCH_SIZE / WRITE_SIZE calibration) and when the
+recorded traffic applies."""
 import csv
 import json
 import os
@@ -66,3 +67,19 @@ def test_profile_summary_calibrates_counters(tmp_path):
     assert k["algorithmic_bytes_per_launch"] == 8 * 4096 * 8192 + 2 * 4096
     md = open(out / "fused_add_rmsnorm_h4096_sweep_kernel_stats.md").read()
     assert "rocprofv3 --kernel-trace --stats" in md and "| 8192 | 2 | 40.00 |" in md
+
+
+def test_traffic_is_reported_only_for_the_profiled_kernel_and_row_mix(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    kname = "fused_add_rmsnorm_kernel<4096, 128, 2>"
+    rec = {"kernel_source_sha256": bench.kernel_source_digest(),
+           "kernels": {kname: {"hbm_bytes_per_launch": 1234.4, "rows": [512, 4096, 8192]}}}
+    json.dump(rec, open(tmp_path / "traffic.json", "w"))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.load_traffic(kname, [8192, 512, 4096]) == 1234
+    assert bench.load_traffic(kname, [4096, 8192]) is None        # launch choice changed
+    assert bench.load_traffic("fused_add_rmsnorm_kernel<4096, 64, 4>", [1024]) is None
+    rec["kernel_source_sha256"] = "0" * 64                       # kernel code changed
+    json.dump(rec, open(tmp_path / "traffic.json", "w"))
+    assert bench.load_traffic(kname, [512, 4096, 8192]) is None
