@@ -22,6 +22,7 @@ What each pin compares against:
                        the fused op's residual gradient); central finite
                        differences; fsum column sums; closed forms (constant
                        row, orthogonality to x at eps = 0).
+  * all operations  -- brute force: 50-digit decimal arithmetic on tiny rows.
 """
 from __future__ import annotations
 
@@ -463,6 +464,106 @@ def check_rmsb_sums_and_closed_forms(o):
     assert np.array_equal(fdx, dx + torch_bf16_to_f64(dres)), "dres must be added as is"
 
 
+# ---------------------------------------------------------------- brute force
+def _dec(a):
+    """float64 array -> nested lists of exact Decimals."""
+    import decimal
+    return [[decimal.Decimal(float(v)) for v in row] for row in np.atleast_2d(a)]
+
+
+def check_decimal_brute_force(o):
+    """Every operation on tiny rows recomputed with 50-digit decimal
+    arithmetic from the textbook formulas (RMSNorm: Zhang & Sennrich 2019,
+    eq. 4; LayerNorm: Ba, Kiros & Hinton 2016, eq. 4, and their gradients),
+    element by element; the fp64 oracle must agree to ~1e-13 relative."""
+    import decimal
+    ctx = decimal.Context(prec=50)
+    D = decimal.Decimal
+    rng = np.random.default_rng(53)
+    for rows, hidden in ((1, 8), (3, 16), (4, 24)):
+        eps_r, eps_l = float(np.float32(1e-6)), float(np.float32(1e-5))
+        x = rand_bf16(rng, (rows, hidden))
+        r = rand_bf16(rng, (rows, hidden))
+        dy = rand_bf16(rng, (rows, hidden))
+        dres = rand_bf16(rng, (rows, hidden))
+        w = rand_bf16(rng, (hidden,), 1.0, 0.1)
+        b = rand_bf16(rng, (hidden,), 0.0, 0.1)
+        X, R, DY, DR = (_dec(torch_bf16_to_f64(a)) for a in (x, r, dy, dres))
+        W, B = _dec(torch_bf16_to_f64(w))[0], _dec(torch_bf16_to_f64(b))[0]
+        H = D(hidden)
+        er, el = D(eps_r), D(eps_l)
+
+        def rms_rows(M):
+            outs, rstds = [], []
+            for row in M:
+                ms = ctx.divide(sum((ctx.multiply(v, v) for v in row), D(0)), H)
+                rs = ctx.divide(D(1), ctx.sqrt(ctx.add(ms, er)))
+                rstds.append(rs)
+                outs.append([ctx.multiply(ctx.multiply(v, rs), W[j]) for j, v in enumerate(row)])
+            return outs, rstds
+
+        def as_f64(M):
+            return np.array([[float(v) for v in row] for row in M])
+
+        # RMSNorm forward
+        ref, _ = rms_rows(X)
+        out, _ = o.rmsnorm_fwd(x, w, eps_r)
+        close(out, as_f64(ref), 1e-13, 1e-300, "rmsnorm vs decimal")
+        # fused: s = x + r exactly, then RMSNorm of s
+        S = [[ctx.add(a, c) for a, c in zip(ra, rc)] for ra, rc in zip(X, R)]
+        ref, _ = rms_rows(S)
+        out, _, _ = o.fused_add_rmsnorm(x, r, w, eps_r)
+        close(out, as_f64(ref), 1e-13, 1e-300, "fused out vs decimal")
+        # LayerNorm forward (statistics of the exact row)
+        ys, mus, rstds = [], [], []
+        for row in X:
+            mu = ctx.divide(sum(row, D(0)), H)
+            var = ctx.divide(sum((ctx.multiply(v - mu, v - mu) for v in row), D(0)), H)
+            rs = ctx.divide(D(1), ctx.sqrt(ctx.add(var, el)))
+            mus.append(mu)
+            rstds.append(rs)
+            ys.append([ctx.add(ctx.multiply(ctx.multiply(v - mu, rs), W[j]), B[j])
+                       for j, v in enumerate(row)])
+        y, mean, rstd = o.layernorm_fwd(x, w, b, eps_l)
+        scale = np.abs(as_f64(ys)).max()
+        close(y, as_f64(ys), 1e-13, 1e-14 * scale, "layernorm y vs decimal")
+        close(mean, [float(m) for m in mus], 1e-13, 1e-15, "layernorm mean vs decimal")
+        close(rstd, [float(v) for v in rstds], 1e-13, 0, "layernorm rstd vs decimal")
+        # LayerNorm backward with the given (fp64) statistics
+        MEAN, RSTD = [D(float(m)) for m in mean], [D(float(v)) for v in rstd]
+        dx_ref, dw_ref, db_ref = [], [D(0)] * hidden, [D(0)] * hidden
+        for i in range(rows):
+            xh = [ctx.multiply(X[i][j] - MEAN[i], RSTD[i]) for j in range(hidden)]
+            g = [ctx.multiply(DY[i][j], W[j]) for j in range(hidden)]
+            c1 = ctx.divide(sum(g, D(0)), H)
+            c2 = ctx.divide(sum((ctx.multiply(g[j], xh[j]) for j in range(hidden)), D(0)), H)
+            dx_ref.append([ctx.multiply(RSTD[i], g[j] - c1 - ctx.multiply(xh[j], c2))
+                           for j in range(hidden)])
+            for j in range(hidden):
+                dw_ref[j] = ctx.add(dw_ref[j], ctx.multiply(DY[i][j], xh[j]))
+                db_ref[j] = ctx.add(db_ref[j], DY[i][j])
+        dx, dw, db = o.layernorm_bwd(dy, x, mean, rstd, w)
+        scale = np.abs(as_f64(dx_ref)).max()
+        close(dx, as_f64(dx_ref), 1e-12, 1e-13 * scale, "layernorm dx vs decimal")
+        close(dw, [float(v) for v in dw_ref], 1e-12, 1e-13, "layernorm dweight vs decimal")
+        close(db, [float(v) for v in db_ref], 1e-13, 1e-14, "layernorm dbias vs decimal")
+        # RMSNorm backward (statistic recomputed), with the fused op's residual gradient
+        _, RS = rms_rows(X)
+        dx_ref, dw_ref = [], [D(0)] * hidden
+        for i in range(rows):
+            xh = [ctx.multiply(X[i][j], RS[i]) for j in range(hidden)]
+            g = [ctx.multiply(DY[i][j], W[j]) for j in range(hidden)]
+            c = ctx.divide(sum((ctx.multiply(g[j], xh[j]) for j in range(hidden)), D(0)), H)
+            dx_ref.append([ctx.add(ctx.multiply(RS[i], g[j] - ctx.multiply(xh[j], c)), DR[i][j])
+                           for j in range(hidden)])
+            for j in range(hidden):
+                dw_ref[j] = ctx.add(dw_ref[j], ctx.multiply(DY[i][j], xh[j]))
+        dx, dw, _ = o.rmsnorm_bwd(dy, x, w, eps_r, dres=dres)
+        scale = np.abs(as_f64(dx_ref)).max()
+        close(dx, as_f64(dx_ref), 1e-12, 1e-13 * scale, "rmsnorm bwd dx vs decimal")
+        close(dw, [float(v) for v in dw_ref], 1e-12, 1e-13, "rmsnorm bwd dweight vs decimal")
+
+
 ALL_CHECKS = [
     check_bf16_decode,
     check_bf16_encode,
@@ -478,5 +579,6 @@ ALL_CHECKS = [
     check_rmsb_autograd,
     check_rmsb_finite_differences,
     check_rmsb_sums_and_closed_forms,
+    check_decimal_brute_force,
     check_thread_count_independence,
 ]
