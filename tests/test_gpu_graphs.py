@@ -1,0 +1,79 @@
+"""The operations captured in a HIP graph (torch.cuda.CUDAGraph): every replay,
+with eager work and synchronizations between replays, gives exactly the
+eager results, for compiled-hidden and run-time-hidden kernels, forward and
+backward (the backward's column reduce runs from the workspace the capture
+recorded; nothing in the library records a memset).  Inputs are refreshed
+from pristine copies by captured device copies, so each replay recomputes
+the same outputs."""
+import numpy as np
+import pytest
+import torch
+
+import row_normalization_persistent_amd as rn
+from row_normalization_persistent_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def dev(bits):
+    return wl.to_device_bf16(bits, DEV)
+
+
+def bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().copy()
+
+
+@pytest.mark.parametrize("hidden", [4096, 5120, 100])
+def test_graph_replays_match_eager(hidden):
+    rows = 300
+    f = wl.fused_inputs(rows, hidden, seed=31)
+    b = wl.rmsnorm_bwd_inputs(rows, hidden, seed=32)
+    lnw = wl.layernorm_fwd_inputs(rows, hidden, seed=33)
+    x, r0, w = dev(f["x"]), dev(f["r"]), dev(f["w"])
+    dy, xb, dres, wb = dev(b["dy"]), dev(b["x"]), dev(b["dres"]), dev(b["w"])
+    xl, wl_, bl = dev(lnw["x"]), dev(lnw["w"]), dev(lnw["b"])
+    res = torch.empty_like(r0)
+    out, ds, y = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    dxl = torch.empty_like(x)
+    mean = torch.empty(rows, device=DEV)
+    rstd = torch.empty(rows, device=DEV)
+    dw1 = torch.empty(hidden, device=DEV)
+    dw2, db2 = torch.empty(hidden, device=DEV), torch.empty(hidden, device=DEV)
+    ws1 = torch.empty(rn.workspace_bytes(rows, hidden, op="fused_add_rmsnorm_bwd"),
+                      dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(rn.workspace_bytes(rows, hidden), dtype=torch.uint8, device=DEV)
+
+    def step(stream):
+        res.copy_(r0)  # the fused op updates its residual in place
+        rn.fused_add_rmsnorm(x, res, w, f["eps"], out=out, stream=stream)
+        rn.fused_add_rmsnorm_bwd(dy, xb, wb, b["eps"], dres=dres, ds=ds, dweight=dw1,
+                                 workspace=ws1, stream=stream)
+        rn.layernorm_fwd(xl, wl_, bl, lnw["eps"], y=y, mean=mean, rstd=rstd, stream=stream)
+        rn.layernorm_bwd(dy, xl, mean, rstd, wl_, dx=dxl, dweight=dw2, dbias=db2,
+                         workspace=ws2, stream=stream)
+
+    outputs = (out, res, ds, dw1, y, mean, rstd, dxl, dw2, db2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.synchronize()
+    eager = [bits(t) for t in outputs]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(s)  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        for t in outputs:  # poison every output between replays, eagerly
+            t.view(torch.int16).fill_(0x7FC1) if t.dtype == torch.bfloat16 else t.fill_(
+                float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, t in enumerate(outputs):
+            assert np.array_equal(bits(t), eager[k]), f"replay {replay}: output {k} differs"
