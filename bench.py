@@ -286,7 +286,9 @@ def main():
     }
 
     if not args.no_other_ops:
-        result["other_ops"] = other_ops(torch, rn, wl, dev, stream, max(3, min(args.steps, 50) // 5))
+        result["other_ops"] = other_ops(torch, rn, wl, dev, stream,
+                                        max(3, min(args.steps, 50) // 5),
+                                        None if args.no_cpu_baseline else 1.0)
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -361,7 +363,7 @@ def _n_sets(per_set_bytes: int) -> int:
     return max(3, -(-int(1.2e9) // per_set_bytes))
 
 
-def other_ops(torch, rn, wl, dev, stream, reps):
+def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     """The other three operations at their largest workload: back-to-back
     launches over enough buffer sets that every launch reads cold data,
     replayed from one graph; time per launch."""
@@ -377,7 +379,9 @@ def other_ops(torch, rn, wl, dev, stream, reps):
     t = graph_time_per_launch(torch, stream, [
         (lambda j=j: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("rmsnorm_fwd", rows, h, 4 * h * rows + 2 * h, t))
+    nb = 4 * h * rows + 2 * h
+    out.append(_op_rec("rmsnorm_fwd", rows, h, nb, t,
+                       cpu=oracle_beside("rmsnorm_fwd", i, rows, h, nb, cpu_seconds)))
     del xs, ys, x0
     # LayerNorm forward, hidden 16384, rows 2048
     h, rows = 16384, 2048
@@ -392,7 +396,9 @@ def other_ops(torch, rn, wl, dev, stream, reps):
         (lambda j=j: rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
                                       rstd=st[j, 1], stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("layernorm_fwd", rows, h, (4 * h + 8) * rows + 4 * h, t))
+    nb = (4 * h + 8) * rows + 4 * h
+    out.append(_op_rec("layernorm_fwd", rows, h, nb, t,
+                       cpu=oracle_beside("layernorm_fwd", i, rows, h, nb, cpu_seconds)))
     del xs, ys, x0
     # LayerNorm backward, hidden 4096 and 8192, rows 8192
     for h in (4096, 8192):
@@ -414,8 +420,10 @@ def other_ops(torch, rn, wl, dev, stream, reps):
             (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
                                           dweight=dw, dbias=db, workspace=ws, stream=stream))
             for j in range(n)], reps)
-        out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
-                           note="rows kernel + column-reduce kernel; workspace not counted"))
+        nb = (6 * h + 8) * rows + 10 * h
+        out.append(_op_rec("layernorm_bwd", rows, h, nb, t,
+                           note="rows kernel + column-reduce kernel; workspace not counted",
+                           cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
         del xs, dys, dxs, x0, dy0
     # RMSNorm backward and the fused residual-add + RMSNorm backward, hidden 4096, rows 8192
     h, rows = 4096, 8192
@@ -433,22 +441,27 @@ def other_ops(torch, rn, wl, dev, stream, reps):
         (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, i["eps"], dx=dxs[j], dweight=dw,
                                     workspace=ws, stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
-                       note="rows kernel + column-reduce kernel; workspace not counted"))
+    nb = 6 * h * rows + 6 * h
+    out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t,
+                       note="rows kernel + column-reduce kernel; workspace not counted",
+                       cpu=oracle_beside("rmsnorm_bwd", i, rows, h, nb, cpu_seconds)))
     t = graph_time_per_launch(torch, stream, [
         (lambda j=j: rn.fused_add_rmsnorm_bwd(dys[j], xs[j], w, i["eps"], dres=drs[j],
                                               ds=dxs[j], dweight=dw, workspace=ws,
                                               stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, 8 * h * rows + 6 * h, t,
-                       note="dout, dres, s read; ds written; workspace not counted"))
+    nb = 8 * h * rows + 6 * h
+    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, nb, t,
+                       note="dout, dres, s read; ds written; workspace not counted",
+                       cpu=oracle_beside("fused_add_rmsnorm_bwd", i, rows, h, nb,
+                                         cpu_seconds)))
     del xs, dys, drs, dxs, x0, dy0, dr0
     torch.cuda.synchronize()
-    out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps)
+    out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds)
     return out
 
 
-def runtime_hidden_ops(torch, rn, wl, dev, stream, reps):
+def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     """The run-time-hidden kernels on shapes the compiled set does not cover,
     and on the headline fused shape for a like-for-like comparison with the
     compiled kernel."""
@@ -472,9 +485,12 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps):
             (lambda j=j: rn.fused_add_rmsnorm(xs[j], rs[j], w, i["eps"], out=ys[j], cfg=cfg,
                                               stream=stream))
             for j in range(n)], reps)
-        out.append(_op_rec("fused_add_rmsnorm", rows, h, 8 * h * rows + 2 * h, t,
+        nb = 8 * h * rows + 2 * h
+        out.append(_op_rec("fused_add_rmsnorm", rows, h, nb, t,
                            note="run-time-hidden kernel" + (
-                               f" forced at a compiled hidden ({cfg})" if forced else "")))
+                               f" forced at a compiled hidden ({cfg})" if forced else ""),
+                           cpu=oracle_beside("fused_add_rmsnorm", i, rows, h, nb,
+                                             cpu_seconds)))
         del xs, rs, ys, x0, r0
     # RMSNorm over 128-wide head slices of a [rows, 3 * 128] projection (row
     # stride 384): the query/key normalization of a fused QKV output
@@ -489,8 +505,10 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps):
         (lambda j=j: rn.rmsnorm_fwd(bases[j][:, :h], w, i["eps"], out=bases[j][:, :h],
                                     stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("rmsnorm_fwd", rows, h, 4 * h * rows + 2 * h, t,
-                       note=f"in place on a column slice with row stride {ld}"))
+    nb = 4 * h * rows + 2 * h
+    out.append(_op_rec("rmsnorm_fwd", rows, h, nb, t,
+                       note=f"in place on a column slice with row stride {ld}",
+                       cpu=oracle_beside("rmsnorm_fwd", i, rows, h, nb, cpu_seconds)))
     del bases, base0
     # backward at hidden 5120
     rows, h = 8192, 5120
@@ -509,27 +527,84 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps):
         (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
                                       dweight=dw, dbias=db, workspace=ws, stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
-                       note="run-time-hidden rows kernel + column reduce"))
+    nb = (6 * h + 8) * rows + 10 * h
+    out.append(_op_rec("layernorm_bwd", rows, h, nb, t,
+                       note="run-time-hidden rows kernel + column reduce",
+                       cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
     t = graph_time_per_launch(torch, stream, [
         (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
                                     workspace=ws, stream=stream))
         for j in range(n)], reps)
-    out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
-                       note="run-time-hidden rows kernel + column reduce"))
+    nb = 6 * h * rows + 6 * h
+    out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t,
+                       note="run-time-hidden rows kernel + column reduce",
+                       cpu=oracle_beside("rmsnorm_bwd", dict(i, eps=wl.EPS_RMS), rows, h, nb,
+                                         cpu_seconds)))
     del xs, dys, dxs, x0, dy0
     torch.cuda.synchronize()
     return out
 
 
-def _op_rec(op, rows, hidden, nbytes, us, note=None):
+def _cores() -> int:
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return max(1, min(cores, 16))
+
+
+def oracle_beside(op, inp, rows, hidden, nbytes, seconds):
+    """The oracle on the first rows of the same workload, repeated for about
+    `seconds`, as GB/s on the operation's algorithmic bytes (scaled to the
+    rows timed).  Returns None when `seconds` is falsy."""
+    if not seconds:
+        return None
+    import oracle
+    cores = _cores()
+    k = max(1, min(rows, (1 << 22) // hidden))  # about 4 Mi elements per pass
+    sl = slice(0, k)
+    if op == "layernorm_bwd":
+        _, mean, rstd = oracle.layernorm_fwd(inp["x"][sl], inp["w"], np.zeros(hidden, np.uint16),
+                                             inp["eps"], cores)
+    calls = {
+        "fused_add_rmsnorm": lambda: oracle.fused_add_rmsnorm(inp["x"][sl], inp["r"][sl],
+                                                              inp["w"], inp["eps"], cores),
+        "rmsnorm_fwd": lambda: oracle.rmsnorm_fwd(inp["x"][sl], inp["w"], inp["eps"], cores),
+        "layernorm_fwd": lambda: oracle.layernorm_fwd(inp["x"][sl], inp["w"], inp["b"],
+                                                      inp["eps"], cores),
+        "layernorm_bwd": lambda: oracle.layernorm_bwd(inp["dy"][sl], inp["x"][sl], mean, rstd,
+                                                      inp["w"], cores),
+        "rmsnorm_bwd": lambda: oracle.rmsnorm_bwd(inp["dy"][sl], inp["x"][sl], inp["w"],
+                                                  inp["eps"], nthreads=cores),
+        "fused_add_rmsnorm_bwd": lambda: oracle.rmsnorm_bwd(inp["dy"][sl], inp["x"][sl],
+                                                            inp["w"], inp["eps"],
+                                                            dres=inp["dres"][sl],
+                                                            nthreads=cores),
+    }
+    fn = calls[op]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= seconds or reps >= 1000:
+            break
+    gbps = nbytes * (reps * k / rows) / t / 1e9
+    return {"GBps": round(gbps, 3), "cores": cores, "kind": "oracle",
+            "sample": f"{reps} pass(es) over the first {k} of {rows} rows in {t:.2f} s"}
+
+
+def _op_rec(op, rows, hidden, nbytes, us, note=None, cpu=None):
     gbps = nbytes / (us * 1e-6) / 1e9
     rec = {"op": op, "rows": rows, "hidden": hidden, "algorithmic_bytes": nbytes,
            "us_per_launch": round(us, 3), "GBps": round(gbps, 1),
            "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
     if note:
         rec["note"] = note
-    log(f"  {op} {rows}x{hidden}: {us:.2f} us, {gbps:.0f} GB/s")
+    if cpu:
+        rec["cpu_oracle"] = cpu
+    log(f"  {op} {rows}x{hidden}: {us:.2f} us, {gbps:.0f} GB/s"
+        + (f" (oracle {cpu['GBps']} GB/s)" if cpu else ""))
     return rec
 
 
@@ -613,6 +688,34 @@ def _alg_bytes(name: str, rows):
     if short.startswith("layernorm_fwd_kernel"):
         return (4 * h + 8) * rows + 4 * h
     return None
+
+
+# The other operations bench.py times: (op, rows, hidden, algorithmic bytes of
+# the kernel that moves the rows; the backward's workspace round trip and its
+# column reduce are not counted).
+OTHER_WORKLOADS = [
+    ("rmsnorm_fwd", 4096, 16384, lambda r, h: 4 * h * r + 2 * h),
+    ("layernorm_fwd", 2048, 16384, lambda r, h: (4 * h + 8) * r + 4 * h),
+    ("layernorm_bwd", 8192, 4096, lambda r, h: (6 * h + 8) * r + 2 * h),
+    ("layernorm_bwd", 8192, 8192, lambda r, h: (6 * h + 8) * r + 2 * h),
+    ("rmsnorm_bwd", 8192, 4096, lambda r, h: 6 * h * r + 2 * h),
+    ("fused_add_rmsnorm_bwd", 8192, 4096, lambda r, h: 8 * h * r + 2 * h),
+    ("fused_add_rmsnorm", 8192, 5120, lambda r, h: 8 * h * r + 2 * h),
+    ("rmsnorm_fwd", 131072, 128, lambda r, h: 4 * h * r + 2 * h),
+    ("layernorm_bwd", 8192, 5120, lambda r, h: (6 * h + 8) * r + 2 * h),
+    ("rmsnorm_bwd", 8192, 5120, lambda r, h: 6 * h * r + 2 * h),
+]
+
+
+def _row_kernel_name(op, rows, hidden):
+    """Kernel instantiation (rocprofv3's spelling, spaces removed) that moves
+    the rows of (op, rows, hidden) with the library's own launch choice."""
+    import row_normalization_persistent_amd as rn
+    desc = rn.describe_config(op, rows, hidden, cu_count=256)
+    k = desc.split(": ", 1)[1].split(" (", 1)[0]
+    dres = "true" if op == "fused_add_rmsnorm_bwd" else "false"
+    return (k.replace(",layernorm>", ",true,false>").replace(",rmsnorm,dres?>", f",false,{dres}>")
+             .replace(",dres?>", f",{dres}>"))
 
 
 def summarize_profiles(d: str, out_dir: str = PROFILES):
@@ -701,6 +804,28 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
         kernels[k] = {"hbm_bytes_per_launch": float(np.mean(g["hbm"])),
                       "algorithmic_bytes_per_launch": float(np.mean(g["alg"])),
                       "rows": sorted(g["rows"])}
+    lines += ["", "The other operations (`other_ops`), kernel that moves the rows, algorithmic bytes "
+              "without the backward workspace (its round trip shows as the excess):", "",
+              "| op | rows x hidden | kernel | dispatches | read MiB | written MiB | "
+              "algorithmic MiB | HBM / algorithmic |", "|---|---|---|---:|---:|---:|---:|---:|"]
+    by_name = collections.defaultdict(lambda: ([], []))
+    for (k, _rows), v in fetch.items():
+        by_name[k.replace(" ", "")][0].extend(v)
+    for (k, _rows), v in write.items():
+        by_name[k.replace(" ", "")][1].extend(v)
+    for op, rows, h, alg_fn in OTHER_WORKLOADS:
+        try:
+            kname = _row_kernel_name(op, rows, h)
+        except Exception:  # the library is not built here: skip the table
+            break
+        f_v, w_v = by_name.get(kname, ([], []))
+        if not f_v or not w_v:
+            continue
+        rd = float(np.mean(f_v)) * f_scale
+        wr = float(np.mean(w_v)) * w_scale
+        alg = alg_fn(rows, h)
+        lines.append(f"| {op} | {rows} x {h} | `{kname}` | {len(f_v)} | {rd / 2**20:.2f} | "
+                     f"{wr / 2**20:.2f} | {alg / 2**20:.2f} | {(rd + wr) / alg:.4f} |")
     lines += ["", "Per-launch averages over each kernel's dispatches (the mix of row counts "
               "the sweep gives it) are in `profiles/traffic.json`, which `bench.py` reports as "
               "`roofline.traffic` while the kernel sources and the kernel's mix of row counts are "
