@@ -111,10 +111,13 @@ typedef enum {
  *   rows_per_block  : rows handled side by side by one workgroup.  Run-time
  *                     shapes: max(1, 256 / threads_per_row), workgroups of
  *                     max(256, threads_per_row) lanes.
- *   grid            : backward ops only: number of persistent workgroups; 0
- *                     lets the library choose.  Each row group of a workgroup
- *                     writes one partial column-sum slab.  Must be 0 for the
- *                     forward ops.
+ *   grid            : number of persistent workgroups that walk the rows.
+ *                     Backward ops: 0 lets the library choose; each row group
+ *                     of a workgroup writes one partial column-sum slab.
+ *                     LayerNorm forward: 0 runs one row per lane group, > 0
+ *                     runs the persistent ring kernel of that lane count
+ *                     (compiled-hidden shapes, rows_per_block 1) on that many
+ *                     workgroups.  Must be 0 for the other forward ops.
  *   vector_elems    : 0 for a compiled-hidden shape; 1, 2, 4 or 8 for a
  *                     run-time-hidden shape whose accesses move that many
  *                     bf16 elements (hidden, every ld and every bf16 pointer

@@ -128,11 +128,19 @@ const std::vector<DynBwdEntry>& dyn_bwd_table(norm_op op) {
     return op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_dyn_table() : rmsnorm_bwd_dyn_table();
 }
 
-const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb) {
+// A compiled forward shape: one row per lane group (ring false) or the
+// persistent ring kernel (ring true, LayerNorm only).
+const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb, bool ring = false) {
     for (const FwdEntry& e : fwd_table(op))
-        if (e.hidden == hidden && e.lanes == lanes && e.rows_per_block == rpb) return &e;
+        if (e.hidden == hidden && e.lanes == lanes && e.rows_per_block == rpb &&
+            (e.depth > 0) == ring)
+            return &e;
     return nullptr;
 }
+
+// Largest persistent grid of a forward ring kernel (a sanity bound; the ring
+// kernels handle any grid from 1 up, idle workgroups included).
+constexpr int32_t kMaxFwdRingGrid = 1 << 20;
 
 const BwdEntry* find_bwd(norm_op op, int64_t hidden, int lanes) {
     for (const BwdEntry& e : bwd_table(op))
@@ -198,11 +206,30 @@ int pointer_width(std::initializer_list<const void*> ptrs) {
 //    per-lane buffers plus the weight/bias vectors cost occupancy), and from
 //    4096 rows up the RMS kernels run best at 4 vectors per lane.
 //  * Rows per workgroup: 4 for one-wave rows, 2 for two-wave rows, else 1.
+// LayerNorm forward from 512 rows (4096 at hidden 4096) runs on the persistent
+// ring kernel (measured on MI355X, 2048 rows: 6-8 % faster at hidden 8192-16384;
+// below those row counts the launch is latency-bound and the plain kernels
+// win): lanes and grid per hidden size from the same sweep.
+norm_launch_cfg choose_ln_ring(int64_t rows, int64_t hidden) {
+    int lanes = 0, grid = 0;
+    if (hidden == 16384 && rows >= 512) lanes = 1024, grid = 256;
+    if (hidden == 12288 && rows >= 512) lanes = 256, grid = 256;
+    if (hidden == 8192 && rows >= 512) lanes = 512, grid = 256;
+    if (hidden == 4096 && rows >= 4096) lanes = 64, grid = 1024;
+    if (lanes == 0 || !find_fwd(NORM_OP_LAYERNORM_FWD, hidden, lanes, 1, true))
+        return norm_launch_cfg{0, 0, 0, 0};
+    return norm_launch_cfg{lanes, 1, (int32_t)std::min<int64_t>(grid, rows), 0};
+}
+
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
+    if (op == NORM_OP_LAYERNORM_FWD) {
+        const norm_launch_cfg ring = choose_ln_ring(rows, hidden);
+        if (ring.threads_per_row) return ring;
+    }
     const int64_t target_waves = 4 * (int64_t)cu;
     auto valid = [&](int l) {
         for (const FwdEntry& e : fwd_table(op))
-            if (e.hidden == hidden && e.lanes == l) return true;
+            if (e.hidden == hidden && e.lanes == l && e.depth == 0) return true;
         return false;
     };
     const int max_vecs = (op != NORM_OP_LAYERNORM_FWD && rows >= 16 * (int64_t)cu) ? 4 : 8;
@@ -308,7 +335,10 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
     const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
     const bool ln = op == NORM_OP_LAYERNORM_FWD;
     if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
-    if (cfg && (cfg->grid != 0 || cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
+    // grid > 0 names a persistent ring shape: LayerNorm's compiled kernels only
+    if (cfg && (cfg->grid < 0 || cfg->grid > kMaxFwdRingGrid ||
+                (cfg->grid > 0 && (!ln || cfg->vector_elems != 0 || cfg->rows_per_block != 1)) ||
+                cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
                 !valid_elems(cfg->vector_elems)))
         return NORM_ERROR_INVALID_VALUE;
     if (c.rows == 0) return NORM_SUCCESS;
@@ -370,13 +400,15 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
     }
 
     if (k.vector_elems == 0) {
-        const FwdEntry* e = find_fwd(op, c.hidden, k.threads_per_row, k.rows_per_block);
+        const FwdEntry* e =
+            find_fwd(op, c.hidden, k.threads_per_row, k.rows_per_block, k.grid > 0);
         if (!e) return NORM_ERROR_INVALID_VALUE;
-        const int64_t groups = ceil_div(c.rows, k.rows_per_block);
+        const int64_t groups = k.grid > 0 ? k.grid : ceil_div(c.rows, k.rows_per_block);
         if (groups > INT32_MAX ||
             groups * k.threads_per_row * k.rows_per_block > (int64_t)UINT32_MAX)
             return NORM_ERROR_INVALID_VALUE;
-        const FwdArgs a{c.out, c.residual, c.x, c.weight, c.bias, c.mean, c.rstd, c.rows, c.eps};
+        const FwdArgs a{c.out, c.residual, c.x,    c.weight, c.bias,
+                        c.mean, c.rstd,    c.rows, c.eps,    k.grid};
         return from_hip(e->launch(a, stream));
     }
     if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row)) {
@@ -818,20 +850,33 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                            : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd"
                                                            : "layernorm_fwd";
         char inst[96];
+        const FwdEntry* ring = c.grid > 0 ? find_fwd(op, hidden, c.threads_per_row, 1, true)
+                                          : nullptr;
         if (dyn)
             std::snprintf(inst, sizeof inst, "%s_dyn_kernel<%d,%d,%d>", kern, w,
                           c.threads_per_row, vecs);
+        else if (ring)
+            std::snprintf(inst, sizeof inst, "%s_ring_kernel<%lld,%d,%d>", kern,
+                          (long long)hidden, c.threads_per_row, ring->depth);
         else
             std::snprintf(inst, sizeof inst, "%s_kernel<%lld,%d,%d>", kern, (long long)hidden,
                           c.threads_per_row, c.rows_per_block);
         const int block = dyn ? dyn_block_size(c.threads_per_row)
                               : c.threads_per_row * c.rows_per_block;
-        n = std::snprintf(tmp, sizeof tmp,
-                          "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
-                          "workgroup of %d, %d %d-byte accesses per lane), grid %lld",
-                          kNames[op], (long long)rows, (long long)hidden, inst,
-                          c.threads_per_row, c.rows_per_block, block, vecs, 2 * w,
-                          (long long)ceil_div(rows, c.rows_per_block));
+        if (ring)
+            n = std::snprintf(tmp, sizeof tmp,
+                              "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d 16-byte "
+                              "accesses per lane, ring of %d rows) on a persistent grid of %d "
+                              "workgroups",
+                              kNames[op], (long long)rows, (long long)hidden, inst,
+                              c.threads_per_row, vecs, ring->depth, c.grid);
+        else
+            n = std::snprintf(tmp, sizeof tmp,
+                              "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
+                              "workgroup of %d, %d %d-byte accesses per lane), grid %lld",
+                              kNames[op], (long long)rows, (long long)hidden, inst,
+                              c.threads_per_row, c.rows_per_block, block, vecs, 2 * w,
+                              (long long)ceil_div(rows, c.rows_per_block));
     }
     if (n < 0) return -1;
     if (buf && len > 0) {
@@ -854,7 +899,9 @@ int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int3
             if (e.hidden == hidden) put(norm_launch_cfg{e.lanes, 1, 0, 0});
     } else {
         for (const FwdEntry& e : fwd_table(op))
-            if (e.hidden == hidden) put(norm_launch_cfg{e.lanes, e.rows_per_block, 0, 0});
+            if (e.hidden == hidden)
+                put(norm_launch_cfg{e.lanes, e.rows_per_block, e.depth > 0 ? kFwdRingGrid : 0,
+                                    0});
     }
     // run-time-hidden shapes at the widest access a contiguous row allows
     const int w = shape_width(hidden, {});

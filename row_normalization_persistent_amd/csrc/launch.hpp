@@ -23,6 +23,7 @@ struct FwdArgs {
     float* rstd;
     int64_t rows;
     float eps;
+    int32_t grid;          // ring kernels: persistent workgroups; 0 otherwise
 };
 
 struct BwdArgs {
@@ -47,7 +48,12 @@ using BwdLauncher = hipError_t (*)(const BwdArgs&, hipStream_t);
 struct FwdEntry {
     int hidden, lanes, rows_per_block;
     FwdLauncher launch;
+    int depth;  // 0: one row per lane group; > 0: persistent ring of that many rows
 };
+
+// Default persistent grid of the forward ring kernels (one workgroup per CU of
+// the largest part).
+constexpr int kFwdRingGrid = 256;
 
 struct BwdEntry {
     int hidden, lanes, depth;  // depth: rows kept in flight per workgroup

@@ -123,8 +123,22 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
         for h in rn.HIDDEN_SIZES:
             for rows in (1, 64, 1024, 2048, 4096, 8192, 1 << 20):
                 c = rn.select_config(op, rows, h, cu_count=256)
-                assert c in rn.list_configs(op, h), (op, h, rows, c)
+                listed = [(k.threads_per_row, k.rows_per_block, k.grid > 0)
+                          for k in rn.list_configs(op, h)]
+                assert (c.threads_per_row, c.rows_per_block, c.grid > 0) in listed, \
+                    (op, h, rows, c)
                 assert h // (8 * c.threads_per_row) <= 8  # at most 8 vectors per lane
+    # LayerNorm forward: the persistent ring kernel from 512 rows at hidden >= 8192
+    for h, rows in ((16384, 2048), (12288, 512), (8192, 8192), (4096, 8192)):
+        c = rn.select_config("layernorm_fwd", rows, h, cu_count=256)
+        assert c.grid > 0 and c.rows_per_block == 1, (h, rows, c)
+        assert (c.threads_per_row, 1) in [(k.threads_per_row, k.rows_per_block)
+                                          for k in rn.list_configs("layernorm_fwd", h)
+                                          if k.grid > 0]
+        assert "layernorm_fwd_ring_kernel" in rn.describe_config("layernorm_fwd", rows, h, 256)
+    for h, rows in ((16384, 256), (4096, 2048), (2048, 8192), (1024, 8192)):
+        assert rn.select_config("layernorm_fwd", rows, h, cu_count=256).grid == 0
+    assert rn.select_config("layernorm_fwd", 600, 16384, cu_count=256).grid == 256
     for h in rn.HIDDEN_SIZES:
         c = rn.select_config("layernorm_bwd", 8192, h)
         assert rn.Cfg(c.threads_per_row, 1, 0, 0) in rn.list_configs("layernorm_bwd", h)
@@ -206,7 +220,8 @@ def test_fused_validation():
     assert fused(w=A + 16) == INVALID         # weight inside out
     bad = rn.LaunchCfg(96, 1, 0)
     assert fused(cfg=ctypes.byref(bad)) == INVALID  # not a compiled shape
-    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 4, 3))) == INVALID  # grid is bwd-only
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 4, 3))) == INVALID  # no ring kernel here
+    assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 1, -1))) == INVALID
     assert fused(cfg=ctypes.byref(rn.LaunchCfg(0, 1, 0))) == INVALID
     # run-time-hidden shapes
     assert fused(cfg=ctypes.byref(rn.LaunchCfg(64, 1, 0, 8))) == INVALID  # rows per block is 4
@@ -245,6 +260,13 @@ def test_layernorm_fwd_validation():
     assert lnf(mean=A + MB + 2) == MISALIGNED
     assert lnf(b=A + 3 * MB + 65536 + 1) == MISALIGNED
     assert lnf(mean=A + MB, rstd=A + MB + 8) == INVALID  # mean/rstd overlap
+    L = rn.lib()
+    ring = lambda c: L.norm_layernorm_fwd_cfg(A, A + MB, A + MB + 65536, A + 2 * MB, A + 3 * MB,
+                                              A + 3 * MB + 65536, 4, 1024, 1e-5, ctypes.byref(c),
+                                              None)
+    assert ring(rn.LaunchCfg(128, 1, 4, 0)) == INVALID   # no ring kernel at hidden 1024
+    assert ring(rn.LaunchCfg(128, 2, 4, 0)) == INVALID   # ring shapes hold one row a group
+    assert ring(rn.LaunchCfg(128, 1, 4, 8)) == INVALID   # rings are compiled-hidden only
 
 
 GB = 1 << 30

@@ -119,6 +119,38 @@ def test_layernorm_fwd_every_compiled_shape(hidden):
     check_lnf(inp, what="layernorm_fwd without stats", with_stats=False)
 
 
+@pytest.mark.parametrize("hidden", [2048, 4096, 8192, 12288, 16384])
+def test_layernorm_fwd_ring_shapes_and_grids(hidden):
+    """The persistent ring kernels: every compiled lane count, grids of one
+    workgroup, ragged walks (75 rows over 7 or 37 workgroups leave partial
+    ring steps) and idle workgroups (300 > rows); in place too."""
+    inp = wl.layernorm_fwd_inputs(75, hidden, seed=14)
+    rings = [c for c in rn.list_configs("layernorm_fwd", hidden) if c.grid > 0]
+    assert rings
+    for c in rings:
+        for grid in (1, 7, 37, 300):
+            cfg = rn.Cfg(c.threads_per_row, 1, grid, 0)
+            check_lnf(inp, cfg=cfg, what=f"layernorm ring h={hidden} {cfg}")
+        check_lnf(inp, cfg=c, what=f"layernorm ring h={hidden} no stats", with_stats=False)
+    ref, _, _ = oracle.layernorm_fwd(inp["x"], inp["w"], inp["b"], inp["eps"], NT)
+    x = dev(inp["x"])
+    rn.layernorm_fwd(x, dev(inp["w"]), dev(inp["b"]), inp["eps"], y=x,
+                     cfg=rn.Cfg(rings[0].threads_per_row, 1, 7, 0))
+    xd = P.bits_to_f64(inp["x"])
+    _, mean_ref, rstd_ref = oracle.layernorm_fwd(inp["x"], inp["w"], inp["b"], inp["eps"], NT)
+    scale = P.layernorm_y_scale(xd, mean_ref, rstd_ref, P.bits_to_f64(inp["w"]),
+                                P.bits_to_f64(inp["b"]))
+    P.assert_bf16_close(host(x), ref, "layernorm ring in place", floor_scale=scale)
+
+
+@pytest.mark.parametrize("rows,hidden", [(2048, 16384), (600, 12288), (8192, 4096)])
+def test_layernorm_fwd_ring_in_library_choice(rows, hidden):
+    """Sizes where the library picks the ring kernel by itself."""
+    assert rn.select_config("layernorm_fwd", rows, hidden).grid > 0
+    check_lnf(wl.layernorm_fwd_inputs(rows, hidden, seed=15),
+              what=f"layernorm_fwd ring {rows}x{hidden}")
+
+
 # ------------------------------------------------------------------ layernorm bwd
 def lnb_inputs(rows, hidden, seed=0):
     inp = wl.layernorm_bwd_inputs(rows, hidden, seed)
