@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "norm.h"
@@ -152,13 +153,19 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The run-time-hidden instantiation with access width w and `lanes` lanes
 // whose per-lane access count is the smallest compiled one covering the row.
+// Forward entries also match K, the rows per lane group.
 template <class Entry>
-const Entry* find_dyn(const std::vector<Entry>& table, int64_t hidden, int w, int lanes) {
+const Entry* find_dyn(const std::vector<Entry>& table, int64_t hidden, int w, int lanes,
+                      int k = 1) {
     const int64_t need = ceil_div(hidden / w, lanes);
     const Entry* best = nullptr;
-    for (const Entry& e : table)
+    for (const Entry& e : table) {
+        if constexpr (std::is_same_v<Entry, DynFwdEntry>) {
+            if (e.rows_per_group != k) continue;
+        }
         if (e.elems == w && e.lanes == lanes && e.vecs >= need && (!best || e.vecs < best->vecs))
             best = &e;
+    }
     return best;
 }
 
@@ -247,7 +254,15 @@ norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
 // so each load instruction of a wave covers whole rows: measured 1.5x faster
 // than two accesses per lane for 128-wide rows.  Returns lanes 0 when no
 // compiled instantiation holds the row.
-norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, int cu) {
+// Rows narrower than a wave are addressed through one descriptor per set of
+// `rows_per_set` rows; its byte extent must stay below the out-of-range
+// offset used for masked accesses.
+bool row_set_fits(int lanes, int64_t rows_per_set, int64_t ld_max, int64_t hidden) {
+    return lanes >= 64 || ((rows_per_set - 1) * ld_max + hidden) * 2 < 0x7ffffff0;
+}
+
+norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, int cu,
+                               int64_t ld_max) {
     const int64_t nacc = hidden / w;
     const int64_t target_lanes = 4 * (int64_t)cu * 64;
     const int64_t vcap = (op != NORM_OP_LAYERNORM_FWD && rows >= 16 * (int64_t)cu) ? 4 : 8;
@@ -255,9 +270,19 @@ norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, 
     while (lanes < 64 && lanes < nacc) lanes *= 2;
     while (lanes < 1024 && ceil_div(nacc, lanes) > vcap) lanes *= 2;
     while (lanes < 1024 && lanes < nacc && rows * lanes < target_lanes) lanes *= 2;
-    for (; lanes <= 1024; lanes *= 2)
-        if (find_dyn(dyn_fwd_table(op), hidden, w, lanes))
-            return norm_launch_cfg{lanes, dyn_rows_per_block(lanes), 0, w};
+    while (lanes < 64 && !row_set_fits(lanes, dyn_rows_per_block(lanes), ld_max, hidden))
+        lanes *= 2;
+    for (; lanes <= 1024; lanes *= 2) {
+        if (!find_dyn(dyn_fwd_table(op), hidden, w, lanes)) continue;
+        const int r = dyn_rows_per_block(lanes);
+        // rows narrower than a wave: two rows per lane group while that still
+        // leaves 8 workgroups per CU (3-6 % faster at 64k-256k rows of 64-256)
+        if (lanes < 64 && ceil_div(rows, 2 * r) >= 8 * (int64_t)cu &&
+            row_set_fits(lanes, 2 * r, ld_max, hidden) &&
+            find_dyn(dyn_fwd_table(op), hidden, w, lanes, 2))
+            return norm_launch_cfg{lanes, 2 * r, 0, w};
+        return norm_launch_cfg{lanes, r, 0, w};
+    }
     return norm_launch_cfg{0, 0, 0, w};
 }
 
@@ -282,15 +307,20 @@ norm_launch_cfg choose_bwd(norm_op op, int64_t rows, int64_t hidden) {
     return norm_launch_cfg{best, 1, default_bwd_grid(rows), 0};
 }
 
-// Run-time-hidden backward: the fewest lanes that give each lane one access
-// (at most 1024), falling back to fewer lanes with more accesses each where
-// that shape is not compiled.
-norm_launch_cfg choose_dyn_bwd(norm_op op, int64_t rows, int64_t hidden, int w) {
+// Run-time-hidden backward: one access per lane up to 256 lanes, then up to
+// 4 accesses per lane on 256 lanes before going wider (measured at hidden
+// 5120: 256 lanes x 3 accesses 13-16 % faster than 1024 lanes x 1, which
+// leaves lanes idle and caps a lane at 128 VGPRs, a shallower ring).
+norm_launch_cfg choose_dyn_bwd(norm_op op, int64_t rows, int64_t hidden, int w,
+                               int64_t ld_max) {
     const int64_t nacc = hidden / w;
     int lanes = 8;
-    while (lanes < 1024 && lanes < nacc) lanes *= 2;
-    for (; lanes >= 8; lanes /= 2)
-        if (find_dyn(dyn_bwd_table(op), hidden, w, lanes)) {
+    while (lanes < 256 && lanes < nacc) lanes *= 2;
+    while (lanes < 64 && !row_set_fits(lanes, dyn_rows_per_block(lanes), ld_max, hidden))
+        lanes *= 2;
+    for (; lanes <= 1024; lanes *= 2)
+        if (row_set_fits(lanes, dyn_rows_per_block(lanes), ld_max, hidden) &&
+            find_dyn(dyn_bwd_table(op), hidden, w, lanes)) {
             const int r = dyn_rows_per_block(lanes);
             return norm_launch_cfg{lanes, r, default_bwd_grid(rows, r), w};
         }
@@ -395,7 +425,8 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         const norm_status st = current_cu_count(&cu);
         if (st != NORM_SUCCESS) return st;
         k = compiled_ok ? choose_fwd(op, c.rows, c.hidden, cu)
-                        : choose_dyn_fwd(op, c.rows, c.hidden, w_max, cu);
+                        : choose_dyn_fwd(op, c.rows, c.hidden, w_max, cu,
+                                         std::max({c.ld_out, c.ld_x, ld_res}));
         if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     }
 
@@ -411,11 +442,14 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
                         c.mean, c.rstd,    c.rows, c.eps,    k.grid};
         return from_hip(e->launch(a, stream));
     }
-    if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row)) {
+    // rows per workgroup = R lane groups x K rows per group
+    const int r = dyn_rows_per_block(k.threads_per_row);
+    if (k.rows_per_block % r != 0 ||
+        !row_set_fits(k.threads_per_row, k.rows_per_block, std::max({c.ld_out, c.ld_x, ld_res}),
+                      c.hidden))
         return NORM_ERROR_INVALID_VALUE;
-    }
-    const DynFwdEntry* e =
-        find_dyn(dyn_fwd_table(op), c.hidden, k.vector_elems, k.threads_per_row);
+    const DynFwdEntry* e = find_dyn(dyn_fwd_table(op), c.hidden, k.vector_elems,
+                                    k.threads_per_row, k.rows_per_block / r);
     if (!e) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
     const int64_t groups = ceil_div(c.rows, k.rows_per_block);
     if (groups > INT32_MAX || groups * dyn_block_size(k.threads_per_row) > (int64_t)UINT32_MAX)
@@ -492,12 +526,15 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         if (cfg->vector_elems > ws_w) return NORM_ERROR_INVALID_VALUE;
         if (cfg->vector_elems > wp) return NORM_ERROR_MISALIGNED;
         k = *cfg;
-        if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row))
+        if (k.rows_per_block != dyn_rows_per_block(k.threads_per_row) ||
+            !row_set_fits(k.threads_per_row, k.rows_per_block,
+                          std::max({c.ld_dx, c.ld_dy, c.ld_x, ld_dres}), c.hidden))
             return NORM_ERROR_INVALID_VALUE;
         if (k.grid == 0) k.grid = default_bwd_grid(c.rows, k.rows_per_block);
     } else {
         k = compiled_ok ? choose_bwd(op, c.rows, c.hidden)
-                        : choose_dyn_bwd(op, c.rows, c.hidden, w_max);
+                        : choose_dyn_bwd(op, c.rows, c.hidden, w_max,
+                                         std::max({c.ld_dx, c.ld_dy, c.ld_x, ld_dres}));
         if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     }
 
@@ -569,7 +606,7 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         need = static_ws_bytes(op, hidden, choose_bwd(op, rows, hidden).grid);
     for (int w : {8, 4, 2, 1}) {
         if (hidden % w) continue;
-        const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w);
+        const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w, hidden);
         if (k.threads_per_row)
             need = std::max(need, dyn_ws_bytes(op, hidden, (int64_t)k.grid * k.rows_per_block));
     }
@@ -584,7 +621,7 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
     norm_launch_cfg k;
     if (is_bwd(op)) {
         k = hidden_compiled(hidden) ? choose_bwd(op, rows, hidden)
-                                    : choose_dyn_bwd(op, rows, hidden, w);
+                                    : choose_dyn_bwd(op, rows, hidden, w, hidden);
     } else {
         int cu = cu_count;
         if (cu <= 0) {
@@ -592,7 +629,7 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
             if (st != NORM_SUCCESS) return st;
         }
         k = hidden_compiled(hidden) ? choose_fwd(op, rows, hidden, cu)
-                                    : choose_dyn_fwd(op, rows, hidden, w, cu);
+                                    : choose_dyn_fwd(op, rows, hidden, w, cu, hidden);
     }
     if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     *cfg = k;
@@ -815,7 +852,9 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         vecs = e->vecs;
         depth = e->depth;
     } else if (dyn) {
-        vecs = find_dyn(dyn_fwd_table(op), hidden, w, c.threads_per_row)->vecs;
+        vecs = find_dyn(dyn_fwd_table(op), hidden, w, c.threads_per_row,
+                        c.rows_per_block / dyn_rows_per_block(c.threads_per_row))
+                   ->vecs;
     } else if (is_bwd(op)) {
         depth = find_bwd(op, hidden, c.threads_per_row)->depth;
     }
@@ -841,7 +880,8 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                           "(%lld workgroups of %d) over %lld slabs; workspace %zu bytes",
                           kNames[op], (long long)rows, (long long)hidden, kern,
                           c.threads_per_row, c.rows_per_block, vecs, 2 * w, depth, c.grid,
-                          (long long)(bwd_outs(op) * padded / kColReduceCols), kColReduceThreads,
+                          (long long)(bwd_outs(op) * padded / colreduce_cols(slabs)),
+                          kColReduceThreads,
                           (long long)slabs,
                           dyn ? dyn_ws_bytes(op, hidden, rows > 0 ? slabs : 0)
                               : static_ws_bytes(op, hidden, rows > 0 ? c.grid : 0));
@@ -853,8 +893,9 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         const FwdEntry* ring = c.grid > 0 ? find_fwd(op, hidden, c.threads_per_row, 1, true)
                                           : nullptr;
         if (dyn)
-            std::snprintf(inst, sizeof inst, "%s_dyn_kernel<%d,%d,%d>", kern, w,
-                          c.threads_per_row, vecs);
+            std::snprintf(inst, sizeof inst, "%s_dyn_kernel<%d,%d,%d,%d>", kern, w,
+                          c.threads_per_row, vecs,
+                          c.rows_per_block / dyn_rows_per_block(c.threads_per_row));
         else if (ring)
             std::snprintf(inst, sizeof inst, "%s_ring_kernel<%lld,%d,%d>", kern,
                           (long long)hidden, c.threads_per_row, ring->depth);
@@ -907,9 +948,14 @@ int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int3
     const int w = shape_width(hidden, {});
     for (int lanes = 8; lanes <= 1024; lanes *= 2) {
         if (lanes > 8 && lanes / 2 >= hidden / w) break;
-        const bool ok = is_bwd(op) ? find_dyn(dyn_bwd_table(op), hidden, w, lanes) != nullptr
-                                   : find_dyn(dyn_fwd_table(op), hidden, w, lanes) != nullptr;
-        if (ok) put(norm_launch_cfg{lanes, dyn_rows_per_block(lanes), 0, w});
+        const int r = dyn_rows_per_block(lanes);
+        if (is_bwd(op)) {
+            if (find_dyn(dyn_bwd_table(op), hidden, w, lanes)) put(norm_launch_cfg{lanes, r, 0, w});
+            continue;
+        }
+        for (int k : {1, 2, 4})
+            if (find_dyn(dyn_fwd_table(op), hidden, w, lanes, k))
+                put(norm_launch_cfg{lanes, r * k, 0, w});
     }
     return n;
 }

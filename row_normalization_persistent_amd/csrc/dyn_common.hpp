@@ -86,6 +86,56 @@ __device__ __forceinline__ rsrc_t row_rsrc_ld(const void* base, int64_t row, int
                                              row < rows ? row_bytes : 0, kRsrcWord3);
 }
 
+// ---- addressing a set of rows -------------------------------------------------------
+// Buffer descriptors are scalar: every lane of a wave must use the same one, or
+// the compiler serializes the access over the distinct values.  A row of at
+// least 64 lanes is uniform over its waves, so it gets a descriptor of its own
+// (sized to the row: accesses past its end are range-checked to zero).  Rows
+// narrower than a wave share one descriptor per set of consecutive rows (the
+// rows of a workgroup, or of one backward ring step), and each lane adds its
+// row's offset; an access past its row's end gets an offset beyond the range.
+// The host keeps such a set's extent below 2^31 bytes.
+constexpr int kOutOfRange = 0x7ffffff0;
+
+template <int T>
+__device__ __forceinline__ int uniform_group(int g) {
+    if constexpr (T >= kWave) return __builtin_amdgcn_readfirstlane(g);
+    else return g;
+}
+
+// Descriptor of rows [first, first + span) of a matrix (rows past `rows` are
+// left out; an empty set gets size 0).  For T >= 64 the set is one row.
+template <int T>
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* base, int64_t first, int64_t span,
+                                            int64_t rows, int64_t ld, int hidden, int elem) {
+    const char* p = static_cast<const char*>(base) + first * ld * elem;
+    int bytes;
+    if constexpr (T >= kWave) {
+        bytes = first < rows ? hidden * elem : 0;
+    } else {
+        const int64_t n = rows - first < span ? rows - first : span;
+        bytes = n > 0 ? (int)(((n - 1) * ld + hidden) * elem) : 0;
+    }
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, kRsrcWord3);
+}
+
+// An optimization barrier for a wave-uniform row index: the compiler may not
+// precompute values derived from it for several loop iterations at once
+// (which, for every matrix and ring slot, would hold scalar registers for
+// the whole loop).  Emits no instruction.
+__device__ __forceinline__ int64_t opaque_row(int64_t r) {
+    asm volatile("" : "+s"(r));
+    return r;
+}
+
+// Byte offset of a lane's access at column `col` of row `local` of a set
+// (T >= 64: the set's only row, masked by the descriptor's size).
+template <int T>
+__device__ __forceinline__ int set_off(int local, int col, int64_t ld, int hidden, int elem) {
+    if constexpr (T >= kWave) return col * elem;
+    else return col < hidden ? (int)((local * ld + col) * elem) : kOutOfRange;
+}
+
 // ---- workgroup shape ---------------------------------------------------------------
 // Rows narrower than 256 lanes are packed 256 / T to a workgroup (four waves),
 // wider rows take a workgroup each.

@@ -274,25 +274,28 @@ __global__ __launch_bounds__(T) void rmsnorm_bwd_rows_kernel(
     }
 }
 
-// Column reduce.  A workgroup owns kColReduceCols = 64 consecutive columns of
-// the flat [outs][padded] slab (dweight columns, then dbias columns; padded is
-// a multiple of 64, so a workgroup never straddles two outputs); its 256 lanes
-// form 16 column groups of 4 columns x 16 slab streams.  Stream s adds the
-// slabs s, s + 16, s + 32, ... (16 independent loads in flight per pass, so
-// the default 256 slabs take one memory round trip; slabs past the last are
-// range-checked to zero by the workspace descriptor), then the 16 stream sums
-// of each column are added in stream order.  The summation order is fixed,
-// so the result is bit-reproducible.  Columns in the padding (hidden <= j <
-// padded) are summed but not stored.
+// Column reduce.  A workgroup owns C consecutive columns of the flat
+// [outs][padded] slab (dweight columns, then dbias columns; padded is a
+// multiple of 64, so a workgroup never straddles two outputs); its 256 lanes
+// form C/4 column groups of 4 columns x 1024/C slab streams.  Stream s adds
+// the slabs s, s + S, s + 2S, ... (S streams, 16 independent loads in flight
+// per pass; slabs past the last are range-checked to zero by the workspace
+// descriptor), then the S stream sums of each column are added as a fixed
+// pairwise tree.  C = 64 for up to 256 slabs (one pass), 16 for up to 1024 and 4
+// beyond, so many slabs spread over more workgroups instead of more passes.
+// The summation order is fixed for a given (slabs, hidden), so the result is
+// bit-reproducible.  Columns in the padding (hidden <= j < padded) are
+// summed but not stored.
+template <int C>
 __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
     const float* __restrict__ workspace, int32_t grid_slabs, int32_t hidden, int32_t padded,
     int32_t outs, float* __restrict__ dweight, float* __restrict__ dbias) {
-    constexpr int kGroups = kColReduceCols / 4;                // 16 groups of 4 columns
-    constexpr int kStreams = kColReduceThreads / kGroups;      // 16 slab streams
+    constexpr int kGroups = C / 4;                              // column groups of 4
+    constexpr int kStreams = kColReduceThreads / kGroups;       // slab streams
     constexpr int kUnroll = 16;
     const int cg = threadIdx.x % kGroups;
     const int stream = threadIdx.x / kGroups;
-    const int flat = blockIdx.x * kColReduceCols + cg * 4;     // < outs * padded
+    const int flat = blockIdx.x * C + cg * 4;                   // < outs * padded
     const int slab_bytes = outs * padded * 4;
     const rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(workspace), (short)0, grid_slabs * slab_bytes, kRsrcWord3);
@@ -308,13 +311,17 @@ __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc += v[u];
     }
+    // the S stream sums of each column, added as a fixed pairwise tree
     __shared__ f32x4 part[kStreams][kGroups];
     part[stream][cg] = acc;
     __syncthreads();
-    if (threadIdx.x < kGroups) {
-        f32x4 s = part[0][cg];
 #pragma unroll
-        for (int i = 1; i < kStreams; ++i) s += part[i][cg];
+    for (int half = kStreams / 2; half >= 1; half /= 2) {
+        if (stream < half) part[stream][cg] += part[stream + half][cg];
+        __syncthreads();
+    }
+    if (threadIdx.x < kGroups) {
+        const f32x4 s = part[0][cg];
         const int o = flat / padded;
         const int col = flat - o * padded;
         float* dst = (o == 0 ? dweight : dbias) + col;
@@ -328,9 +335,17 @@ __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
 hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t hidden,
                                  int32_t padded, int32_t outs, float* dweight, float* dbias,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(norm_bwd_colreduce_kernel, dim3(outs * padded / kColReduceCols),
-                       dim3(kColReduceThreads), 0, stream, workspace, slabs, hidden, padded, outs,
-                       dweight, dbias);
+    const int cols = colreduce_cols(slabs);
+    const dim3 grid(outs * padded / cols), block(kColReduceThreads);
+    if (cols == 64)
+        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<64>, grid, block, 0, stream, workspace,
+                           slabs, hidden, padded, outs, dweight, dbias);
+    else if (cols == 16)
+        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<16>, grid, block, 0, stream, workspace,
+                           slabs, hidden, padded, outs, dweight, dbias);
+    else
+        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<4>, grid, block, 0, stream, workspace,
+                           slabs, hidden, padded, outs, dweight, dbias);
     return hipGetLastError();
 }
 

@@ -39,25 +39,50 @@ struct DynRow {
     float mean, rstd;  // LayerNorm only
 };
 
+// The rows one ring step of a workgroup touches: for rows of >= 64 lanes each
+// lane group's own row (one descriptor per row, uniform over its waves); for
+// narrower rows the R consecutive rows of all the workgroup's groups (one
+// descriptor, each lane at its row's offset).  See rows_rsrc / set_off.
+struct WalkRows {
+    int64_t first;  // first row of the set
+    int span;       // rows in the set
+    int local;      // this lane group's row within the set
+    __device__ __forceinline__ int64_t row() const { return first + local; }
+};
+
+template <int T>
+__device__ __forceinline__ WalkRows walk_rows(int64_t wg_first, int g, int64_t step) {
+    if constexpr (T < kWave) return WalkRows{opaque_row(wg_first + step), dyn_block<T>() / T, g};
+    else return WalkRows{opaque_row(wg_first + g + step), 1, 0};
+}
+
+template <int W, int T>
+__device__ __forceinline__ int walk_off(const WalkRows& w, int b, int lane, int64_t ld, int h) {
+    return set_off<T>(w.local, (b * T + lane) * W, ld, h, 2);
+}
+
 template <int W, int T, int V, bool LN, bool DRES>
 __device__ __forceinline__ void dyn_load_row(DynRow<W, V, LN, DRES>& r, const DynBwdArgs& a,
-                                             int64_t row, int lane) {
-    const int rb = a.hidden * 2;
-    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
-    const rsrc_t rd = row_rsrc_ld(a.dy, row, a.rows, a.ld_dy * 2, rb);
+                                             const WalkRows& w, int lane) {
+    const int h = a.hidden;
+    const rsrc_t rx = rows_rsrc<T>(a.x, w.first, w.span, a.rows, a.ld_x, h, 2);
+    const rsrc_t rd = rows_rsrc<T>(a.dy, w.first, w.span, a.rows, a.ld_dy, h, 2);
 #pragma unroll
-    for (int b = 0; b < V; ++b) r.x[b] = aload<W, kCachePolicyNT>(rx, dyn_boff<W, T>(b, lane));
+    for (int b = 0; b < V; ++b)
+        r.x[b] = aload<W, kCachePolicyNT>(rx, walk_off<W, T>(w, b, lane, a.ld_x, h));
 #pragma unroll
-    for (int b = 0; b < V; ++b) r.dy[b] = aload<W, kCachePolicyNT>(rd, dyn_boff<W, T>(b, lane));
+    for (int b = 0; b < V; ++b)
+        r.dy[b] = aload<W, kCachePolicyNT>(rd, walk_off<W, T>(w, b, lane, a.ld_dy, h));
     if constexpr (DRES) {
-        const rsrc_t rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * 2, rb);
+        const rsrc_t rr = rows_rsrc<T>(a.dres, w.first, w.span, a.rows, a.ld_dres, h, 2);
 #pragma unroll
         for (int b = 0; b < V; ++b)
-            r.dres[b] = aload<W, kCachePolicyNT>(rr, dyn_boff<W, T>(b, lane));
+            r.dres[b] = aload<W, kCachePolicyNT>(rr, walk_off<W, T>(w, b, lane, a.ld_dres, h));
     }
     if constexpr (LN) {
-        r.mean = rload_f32(row_rsrc(a.mean, row, a.rows, 4), 0);
-        r.rstd = rload_f32(row_rsrc(a.rstd, row, a.rows, 4), 0);
+        const int off = set_off<T>(w.local, 0, 1, 1, 4);
+        r.mean = rload_f32(rows_rsrc<T>(a.mean, w.first, w.span, a.rows, 1, 1, 4), off);
+        r.rstd = rload_f32(rows_rsrc<T>(a.rstd, w.first, w.span, a.rows, 1, 1, 4), off);
     }
 }
 
@@ -68,7 +93,7 @@ template <int W, int T, int V>
 __device__ __forceinline__ void dyn_ln_row(const DynRow<W, V, true, false>& cur,
                                            const float (&wf)[V][W], float (&pw)[V][W],
                                            float (&pb)[V][W], const DynBwdArgs& a, float inv_h,
-                                           float* slot, int64_t row, int lane) {
+                                           float* slot, const WalkRows& w, int lane) {
     float xh[V][W], g[V][W];
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
@@ -89,13 +114,14 @@ __device__ __forceinline__ void dyn_ln_row(const DynRow<W, V, true, false>& cur,
     dyn_row_sum2<T>(s1, s2, slot, lane);
     const float c1 = s1 * inv_h;
     const float c2 = s2 * inv_h;
-    const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, a.hidden * 2);
+    const rsrc_t rdx = rows_rsrc<T>(a.dx, w.first, w.span, a.rows, a.ld_dx, a.hidden, 2);
 #pragma unroll
     for (int b = 0; b < V; ++b) {
         float o[W];
 #pragma unroll
         for (int k = 0; k < W; ++k) o[k] = cur.rstd * (g[b][k] - c1 - xh[b][k] * c2);
-        astore<W, kCachePolicyNT>(rdx, dyn_boff<W, T>(b, lane), apack<W>(o));
+        astore<W, kCachePolicyNT>(rdx, walk_off<W, T>(w, b, lane, a.ld_dx, a.hidden),
+                                  apack<W>(o));
     }
 }
 
@@ -105,7 +131,7 @@ template <int W, int T, int V, bool DRES>
 __device__ __forceinline__ void dyn_rms_row(const DynRow<W, V, false, DRES>& cur,
                                             const float (&wf)[V][W], float (&pw)[V][W],
                                             const DynBwdArgs& a, float inv_h, float* slot,
-                                            int64_t row, int lane) {
+                                            const WalkRows& w, int lane) {
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int b = 0; b < V; ++b) {
@@ -120,9 +146,9 @@ __device__ __forceinline__ void dyn_rms_row(const DynRow<W, V, false, DRES>& cur
     }
     dyn_row_sum2<T>(s1, s2, slot, lane);
     // a row past the end must add exactly nothing, also at eps = 0
-    const float rstd = row < a.rows ? fast_rsqrt(s1 * inv_h + a.eps) : 0.0f;
+    const float rstd = w.row() < a.rows ? fast_rsqrt(s1 * inv_h + a.eps) : 0.0f;
     const float coef = rstd * rstd * rstd * s2 * inv_h;
-    const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, a.hidden * 2);
+    const rsrc_t rdx = rows_rsrc<T>(a.dx, w.first, w.span, a.rows, a.ld_dx, a.hidden, 2);
 #pragma unroll
     for (int b = 0; b < V; ++b) {
         float xf[W], df[W], o[W];
@@ -139,7 +165,8 @@ __device__ __forceinline__ void dyn_rms_row(const DynRow<W, V, false, DRES>& cur
 #pragma unroll
             for (int k = 0; k < W; ++k) o[k] += rf[k];
         }
-        astore<W, kCachePolicyNT>(rdx, dyn_boff<W, T>(b, lane), apack<W>(o));
+        astore<W, kCachePolicyNT>(rdx, walk_off<W, T>(w, b, lane, a.ld_dx, a.hidden),
+                                  apack<W>(o));
     }
 }
 
@@ -164,7 +191,7 @@ __global__ __launch_bounds__(dyn_block<T>()) void norm_bwd_dyn_rows_kernel(DynBw
     constexpr int kSlot = 2 * dyn_red_floats<T>();  // one two-value reduction of the workgroup
     __shared__ float red[2 * kSlot];
     const int lane = threadIdx.x % T;
-    const int g = threadIdx.x / T;
+    const int g = uniform_group<T>(threadIdx.x / T);
     const float inv_h = 1.0f / (float)a.hidden;
 
     float wf[V][W];
@@ -193,22 +220,23 @@ __global__ __launch_bounds__(dyn_block<T>()) void norm_bwd_dyn_rows_kernel(DynBw
     // fences keep each slot's loads in slot order (precise memory-counter waits)
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        dyn_load_row<W, T, V, LN, DRES>(buf[d], a, me + d * P, lane);
+        dyn_load_row<W, T, V, LN, DRES>(buf[d], a, walk_rows<T>(first, g, d * P), lane);
         issue_fence();
     }
     int parity = 0;
     for (int64_t i = 0; i < n; i += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int64_t r = me + (i + d) * P;
+            const WalkRows w = walk_rows<T>(first, g, (i + d) * P);
             float* slot = red + parity * kSlot + g * (2 * (T / kWave));
             if constexpr (LN)
-                dyn_ln_row<W, T, V>(buf[d], wf, pw, pb, a, inv_h, slot, r, lane);
+                dyn_ln_row<W, T, V>(buf[d], wf, pw, pb, a, inv_h, slot, w, lane);
             else
-                dyn_rms_row<W, T, V, DRES>(buf[d], wf, pw, a, inv_h, slot, r, lane);
+                dyn_rms_row<W, T, V, DRES>(buf[d], wf, pw, a, inv_h, slot, w, lane);
             parity ^= 1;
             issue_fence();
-            dyn_load_row<W, T, V, LN, DRES>(buf[d], a, r + D * P, lane);
+            dyn_load_row<W, T, V, LN, DRES>(buf[d], a, walk_rows<T>(first, g, (i + d + D) * P),
+                                            lane);
             issue_fence();
         }
     }

@@ -6,8 +6,8 @@
 // strides and 1/hidden are kernel arguments instead of constants.
 //
 // Template parameters: W elements per access, T lanes per row, V accesses per
-// lane.  A workgroup of dyn_block<T>() lanes holds R = block / T rows; row
-// group g of workgroup k normalizes row k*R + g.
+// lane, K rows per lane group.  A workgroup of dyn_block<T>() lanes holds
+// R = block / T lane groups and R*K rows.
 #pragma once
 
 #include <type_traits>
@@ -21,152 +21,212 @@ namespace rownorm {
 template <int W, int T>
 __device__ __forceinline__ int dyn_off(int b, int lane) { return (b * T + lane) * (2 * W); }
 
-template <int W, int T, int V>
-__global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(DynFwdArgs a) {
-    constexpr int R = dyn_block<T>() / T;
-    __shared__ float red[dyn_red_floats<T>()];
-    const int lane = threadIdx.x % T;
-    const int g = threadIdx.x / T;
-    const int64_t row = (int64_t)blockIdx.x * R + g;
-    const int rb = a.hidden * 2;
-    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
-    const rsrc_t rr = row_rsrc_ld(a.residual, row, a.rows, a.ld_res * 2, rb);
-    const rsrc_t ro = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
-    raw_t<W> xv[V], rv[V], wv[V];
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-        xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
-        rv[b] = aload<W, kCachePolicyNT>(rr, dyn_off<W, T>(b, lane));
-    }
-#pragma unroll
-    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
-    issue_fence();
-    float acc = 0.0f;
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W], rf[W], sv[W];
-        aunpack<W>(xv[b], xf);
-        aunpack<W>(rv[b], rf);
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-            sv[k] = xf[k] + rf[k];
-            acc += sv[k] * sv[k];  // accesses past the row's end are 0 + 0
+// K rows per lane group (K > 1 only for rows narrower than a wave, which
+// reduce without LDS): the group issues the loads of all K rows before the
+// first reduction.  Rows of workgroup k: k*R*K + j*R + g for j < K
+// (consecutive groups take consecutive rows).  Addressing: one descriptor per
+// row for rows of >= 64 lanes, one per workgroup for narrower rows
+// (dyn_common.hpp, rows_rsrc / set_off).
+template <int T, int K>
+struct RowSet {
+    static constexpr int R = dyn_block<T>() / T;
+    static_assert(K == 1 || T < kWave, "several rows per lane group only without LDS");
+    int64_t first, span;
+    __device__ __forceinline__ explicit RowSet(int g) {
+        if constexpr (T < kWave) {
+            first = (int64_t)blockIdx.x * (R * K);
+            span = R * K;
+        } else {
+            first = (int64_t)blockIdx.x * R + g;
+            span = 1;
         }
-        astore<W, kCachePolicyNT>(rr, dyn_off<W, T>(b, lane), apack<W>(sv));
     }
-    const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
-    const float rstd = fast_rsqrt(ss / (float)a.hidden + a.eps);
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W], rf[W], wf[W], o[W];
-        aunpack<W>(xv[b], xf);
-        aunpack<W>(rv[b], rf);
-        aunpack<W>(wv[b], wf);
-#pragma unroll
-        for (int k = 0; k < W; ++k) o[k] = (xf[k] + rf[k]) * rstd * wf[k];
-        astore<W, kCachePolicyNT>(ro, dyn_off<W, T>(b, lane), apack<W>(o));
+    __device__ __forceinline__ int local(int j, int g) const {
+        if constexpr (T < kWave) return j * R + g;
+        else return 0;
     }
+    __device__ __forceinline__ int64_t row(int j, int g) const { return first + local(j, g); }
+    __device__ __forceinline__ rsrc_t rsrc(const void* base, int64_t rows, int64_t ld,
+                                           int hidden) const {
+        return rows_rsrc<T>(base, first, span, rows, ld, hidden, 2);
+    }
+};
+
+template <int W, int T>
+__device__ __forceinline__ int acc_off(int local, int b, int lane, int64_t ld, int hidden) {
+    return set_off<T>(local, (b * T + lane) * W, ld, hidden, 2);
 }
 
-template <int W, int T, int V>
-__global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdArgs a) {
-    constexpr int R = dyn_block<T>() / T;
+template <int W, int T, int V, int K>
+__global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(DynFwdArgs a) {
     __shared__ float red[dyn_red_floats<T>()];
     const int lane = threadIdx.x % T;
-    const int g = threadIdx.x / T;
-    const int64_t row = (int64_t)blockIdx.x * R + g;
-    const int rb = a.hidden * 2;
-    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
-    const rsrc_t ro = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
-    raw_t<W> xv[V], wv[V];
+    const int g = uniform_group<T>(threadIdx.x / T);
+    const RowSet<T, K> set(g);
+    const int h = a.hidden;
+    const rsrc_t rx = set.rsrc(a.x, a.rows, a.ld_x, h);
+    const rsrc_t rr = set.rsrc(a.residual, a.rows, a.ld_res, h);
+    const rsrc_t ro = set.rsrc(a.out, a.rows, a.ld_out, h);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    raw_t<W> xv[K][V], rv[K][V], wv[V];
 #pragma unroll
-    for (int b = 0; b < V; ++b) xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            xv[j][b] = aload<W, kCachePolicyNT>(rx, acc_off<W, T>(l, b, lane, a.ld_x, h));
+            rv[j][b] = aload<W, kCachePolicyNT>(rr, acc_off<W, T>(l, b, lane, a.ld_res, h));
+        }
+    }
 #pragma unroll
     for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
     issue_fence();
-    float acc = 0.0f;
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W];
-        aunpack<W>(xv[b], xf);
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+        float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < W; ++k) acc += xf[k] * xf[k];
-    }
-    const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
-    const float rstd = fast_rsqrt(ss / (float)a.hidden + a.eps);
+        for (int b = 0; b < V; ++b) {
+            float xf[W], rf[W], sv[W];
+            aunpack<W>(xv[j][b], xf);
+            aunpack<W>(rv[j][b], rf);
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W], wf[W], o[W];
-        aunpack<W>(xv[b], xf);
-        aunpack<W>(wv[b], wf);
+            for (int k = 0; k < W; ++k) {
+                sv[k] = xf[k] + rf[k];
+                acc += sv[k] * sv[k];  // accesses past the row's end are 0 + 0
+            }
+            astore<W, kCachePolicyNT>(rr, acc_off<W, T>(l, b, lane, a.ld_res, h), apack<W>(sv));
+        }
+        const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
+        const float rstd = fast_rsqrt(ss / (float)h + a.eps);
 #pragma unroll
-        for (int k = 0; k < W; ++k) o[k] = xf[k] * rstd * wf[k];
-        astore<W, kCachePolicyNT>(ro, dyn_off<W, T>(b, lane), apack<W>(o));
+        for (int b = 0; b < V; ++b) {
+            float xf[W], rf[W], wf[W], o[W];
+            aunpack<W>(xv[j][b], xf);
+            aunpack<W>(rv[j][b], rf);
+            aunpack<W>(wv[b], wf);
+#pragma unroll
+            for (int k = 0; k < W; ++k) o[k] = (xf[k] + rf[k]) * rstd * wf[k];
+            astore<W, kCachePolicyNT>(ro, acc_off<W, T>(l, b, lane, a.ld_out, h), apack<W>(o));
+        }
     }
 }
 
-template <int W, int T, int V>
+template <int W, int T, int V, int K>
+__global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdArgs a) {
+    __shared__ float red[dyn_red_floats<T>()];
+    const int lane = threadIdx.x % T;
+    const int g = uniform_group<T>(threadIdx.x / T);
+    const RowSet<T, K> set(g);
+    const int h = a.hidden;
+    const rsrc_t rx = set.rsrc(a.x, a.rows, a.ld_x, h);
+    const rsrc_t ro = set.rsrc(a.out, a.rows, a.ld_out, h);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    raw_t<W> xv[K][V], wv[V];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+#pragma unroll
+        for (int b = 0; b < V; ++b)
+            xv[j][b] = aload<W, kCachePolicyNT>(rx, acc_off<W, T>(l, b, lane, a.ld_x, h));
+    }
+#pragma unroll
+    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+    issue_fence();
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+        float acc = 0.0f;
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            float xf[W];
+            aunpack<W>(xv[j][b], xf);
+#pragma unroll
+            for (int k = 0; k < W; ++k) acc += xf[k] * xf[k];
+        }
+        const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
+        const float rstd = fast_rsqrt(ss / (float)h + a.eps);
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            float xf[W], wf[W], o[W];
+            aunpack<W>(xv[j][b], xf);
+            aunpack<W>(wv[b], wf);
+#pragma unroll
+            for (int k = 0; k < W; ++k) o[k] = xf[k] * rstd * wf[k];
+            astore<W, kCachePolicyNT>(ro, acc_off<W, T>(l, b, lane, a.ld_out, h), apack<W>(o));
+        }
+    }
+}
+
+template <int W, int T, int V, int K>
 __global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFwdArgs a) {
-    constexpr int R = dyn_block<T>() / T;
     constexpr int kRed = dyn_red_floats<T>();
     __shared__ float red[2 * kRed];  // mean and variance use different slots: one barrier each
     const int lane = threadIdx.x % T;
-    const int g = threadIdx.x / T;
-    const int64_t row = (int64_t)blockIdx.x * R + g;
-    const int rb = a.hidden * 2;
-    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, rb);
-    const rsrc_t ry = row_rsrc_ld(a.out, row, a.rows, a.ld_out * 2, rb);
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, rb);
-    const rsrc_t rbias = row_rsrc_ld(a.bias, 0, 1, 0, rb);
-    raw_t<W> xv[V], wv[V], bv[V];
+    const int g = uniform_group<T>(threadIdx.x / T);
+    const RowSet<T, K> set(g);
+    const int h = a.hidden;
+    const rsrc_t rx = set.rsrc(a.x, a.rows, a.ld_x, h);
+    const rsrc_t ry = set.rsrc(a.out, a.rows, a.ld_out, h);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    const rsrc_t rbias = row_rsrc_ld(a.bias, 0, 1, 0, h * 2);
+    raw_t<W> xv[K][V], wv[V], bv[V];
 #pragma unroll
-    for (int b = 0; b < V; ++b) xv[b] = aload<W, kCachePolicyNT>(rx, dyn_off<W, T>(b, lane));
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+#pragma unroll
+        for (int b = 0; b < V; ++b)
+            xv[j][b] = aload<W, kCachePolicyNT>(rx, acc_off<W, T>(l, b, lane, a.ld_x, h));
+    }
 #pragma unroll
     for (int b = 0; b < V; ++b) {
         wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
         bv[b] = aload<W, 0>(rbias, dyn_off<W, T>(b, lane));
     }
     issue_fence();
-    const float inv_h = 1.0f / (float)a.hidden;
-    float acc = 0.0f;
+    const float inv_h = 1.0f / (float)h;
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W];
-        aunpack<W>(xv[b], xf);
+    for (int j = 0; j < K; ++j) {
+        const int l = set.local(j, g);
+        const int64_t row = set.row(j, g);
+        float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < W; ++k) acc += xf[k];
-    }
-    const float mu = dyn_row_sum<T>(acc, red + g * (T / kWave), lane) * inv_h;
-    float acc2 = 0.0f;
+        for (int b = 0; b < V; ++b) {
+            float xf[W];
+            aunpack<W>(xv[j][b], xf);
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        // an access past the row's end holds zeros, but (0 - mu)^2 must not count
-        const bool in_row = (b * T + lane) * W < a.hidden;
-        float xf[W];
-        aunpack<W>(xv[b], xf);
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-            const float d = in_row ? xf[k] - mu : 0.0f;
-            acc2 += d * d;
+            for (int k = 0; k < W; ++k) acc += xf[k];
         }
-    }
-    const float var = dyn_row_sum<T>(acc2, red + kRed + g * (T / kWave), lane) * inv_h;
-    const float rstd = fast_rsqrt(var + a.eps);
-    if (a.mean != nullptr && lane == 0 && row < a.rows) {
-        a.mean[row] = mu;
-        a.rstd[row] = rstd;
-    }
+        const float mu = dyn_row_sum<T>(acc, red + g * (T / kWave), lane) * inv_h;
+        float acc2 = 0.0f;
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        float xf[W], wf[W], bf[W], o[W];
-        aunpack<W>(xv[b], xf);
-        aunpack<W>(wv[b], wf);
-        aunpack<W>(bv[b], bf);
+        for (int b = 0; b < V; ++b) {
+            // an access past the row's end holds zeros, but (0 - mu)^2 must not count
+            const bool in_row = (b * T + lane) * W < h;
+            float xf[W];
+            aunpack<W>(xv[j][b], xf);
 #pragma unroll
-        for (int k = 0; k < W; ++k) o[k] = (xf[k] - mu) * rstd * wf[k] + bf[k];
-        astore<W, kCachePolicyNT>(ry, dyn_off<W, T>(b, lane), apack<W>(o));
+            for (int k = 0; k < W; ++k) {
+                const float d = in_row ? xf[k] - mu : 0.0f;
+                acc2 += d * d;
+            }
+        }
+        const float var = dyn_row_sum<T>(acc2, red + kRed + g * (T / kWave), lane) * inv_h;
+        const float rstd = fast_rsqrt(var + a.eps);
+        if (a.mean != nullptr && lane == 0 && row < a.rows) {
+            a.mean[row] = mu;
+            a.rstd[row] = rstd;
+        }
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            float xf[W], wf[W], bf[W], o[W];
+            aunpack<W>(xv[j][b], xf);
+            aunpack<W>(wv[b], wf);
+            aunpack<W>(bv[b], bf);
+#pragma unroll
+            for (int k = 0; k < W; ++k) o[k] = (xf[k] - mu) * rstd * wf[k] + bf[k];
+            astore<W, kCachePolicyNT>(ry, acc_off<W, T>(l, b, lane, a.ld_out, h), apack<W>(o));
+        }
     }
 }
 
@@ -174,17 +234,17 @@ struct OpFusedDyn {};
 struct OpRmsDyn {};
 struct OpLnFwdDyn {};
 
-template <class Op, int W, int T, int V>
+template <class Op, int W, int T, int V, int K>
 hipError_t launch_fwd_dyn(const DynFwdArgs& a, hipStream_t stream) {
-    constexpr int R = dyn_block<T>() / T;
-    const dim3 grid((unsigned)((a.rows + R - 1) / R));
+    constexpr int RK = dyn_block<T>() / T * K;
+    const dim3 grid((unsigned)((a.rows + RK - 1) / RK));
     const dim3 block(dyn_block<T>());
     if constexpr (std::is_same_v<Op, OpFusedDyn>)
-        hipLaunchKernelGGL((fused_add_rmsnorm_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((fused_add_rmsnorm_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
     else if constexpr (std::is_same_v<Op, OpRmsDyn>)
-        hipLaunchKernelGGL((rmsnorm_fwd_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((rmsnorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((layernorm_fwd_dyn_kernel<W, T, V>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((layernorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
@@ -202,9 +262,18 @@ constexpr bool dyn_fwd_fits() {
     return !(std::is_same_v<Op, OpLnFwdDyn> && T == 1024 && V * W > 48);
 }
 
+// Rows per lane group compiled: 1 everywhere; also 2 and 4 for rows of at
+// most two accesses a lane on fewer than 64 lanes (small rows, whose workgroups
+// would otherwise keep too few bytes in flight).
 template <class Op, int W, int T, int V>
 void add_dyn_fwd_one(std::vector<DynFwdEntry>& v) {
-    if constexpr (dyn_fwd_fits<Op, W, T, V>()) v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V>});
+    if constexpr (dyn_fwd_fits<Op, W, T, V>()) {
+        v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 1>, 1});
+        if constexpr (T < kWave && V <= 2) {
+            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 2>, 2});
+            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 4>, 4});
+        }
+    }
 }
 
 template <class Op, int W, int T, int... Vs>

@@ -108,6 +108,7 @@ using DynBwdLauncher = hipError_t (*)(const DynBwdArgs&, hipStream_t);
 struct DynFwdEntry {
     int elems, lanes, vecs;  // access width W, lanes per row T, accesses per lane V
     DynFwdLauncher launch;
+    int rows_per_group;      // K rows per lane group (workgroup rows = R * K)
 };
 
 struct DynBwdEntry {
@@ -136,9 +137,12 @@ hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t 
                                  int32_t padded, int32_t outs, float* dweight, float* dbias,
                                  hipStream_t stream);
 
-// Column-reduce geometry of LayerNorm backward.
+// Column-reduce geometry of the backward ops: 256 lanes a workgroup, 64
+// columns a workgroup for up to 256 partial-sum slabs (one pass), 16 for up
+// to 1024 and 4 beyond (more workgroups instead of more passes).
 constexpr int kColReduceThreads = 256;
-constexpr int kColReduceCols = 64;  // flat [2][hidden] columns per workgroup
+constexpr int kColReduceCols = 64;
+constexpr int colreduce_cols(int64_t slabs) { return slabs <= 256 ? 64 : (slabs <= 1024 ? 16 : 4); }
 // Largest persistent grid for a hidden size: the workspace ([grid][2][hidden]
 // fp32) must stay addressable by one 32-bit buffer descriptor, with room for
 // the column reduce's range-checked reads one pass past the last slab.

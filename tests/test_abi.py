@@ -79,7 +79,8 @@ def test_runtime_hidden_shapes():
                 t = c.threads_per_row
                 assert c.vector_elems == w
                 assert t in (8, 16, 32, 64, 128, 256, 512, 1024)
-                assert c.rows_per_block == max(1, 256 // t)
+                r = max(1, 256 // t)  # lane groups a workgroup; narrow rows: 1, 2 or 4 rows each
+                assert c.rows_per_block in ((r, 2 * r, 4 * r) if t < 64 else (r,))
                 assert t // 2 < max(h // w, 1) or t == 8  # no shape with half its lanes idle
             sel = rn.select_config(op, 4096, h, cu_count=256)
             assert sel.runtime_hidden == (h not in rn.HIDDEN_SIZES)
@@ -100,10 +101,15 @@ def test_runtime_hidden_shapes():
         prev = c.threads_per_row
     # tiny rows share a wave; backward rows get one access per lane
     assert rn.select_config("rmsnorm_fwd", 1 << 16, 64, cu_count=256).threads_per_row == 8
+    # two rows per lane group from 8 workgroups per CU up
+    assert rn.select_config("rmsnorm_fwd", 1 << 17, 128, cu_count=256).rows_per_block == 32
+    assert rn.select_config("rmsnorm_fwd", 8192, 128, cu_count=256).rows_per_block == 16
     assert rn.select_config("rmsnorm_fwd", 1 << 17, 128, cu_count=256).threads_per_row == 16
     assert rn.select_config("layernorm_fwd", 2048, 1000, cu_count=256).threads_per_row == 64
     assert rn.select_config("rmsnorm_bwd", 8192, 128).threads_per_row == 16
-    assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 1024
+    assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 256
+    assert rn.select_config("layernorm_bwd", 8192, 1000).threads_per_row == 128
+    assert rn.select_config("rmsnorm_bwd", 64, 16376).threads_per_row == 512
 
 
 def test_select_config_small_batches_spread_rows_over_more_lanes():
