@@ -112,8 +112,8 @@ typedef enum {
  *                     shapes: max(1, 256 / threads_per_row), workgroups of
  *                     max(256, threads_per_row) lanes.
  *   grid            : number of persistent workgroups that walk the rows.
- *                     Backward ops: 0 lets the library choose; each row group
- *                     of a workgroup writes one partial column-sum slab.
+ *                     Backward ops: 0 lets the library choose; each
+ *                     workgroup writes one partial column-sum slab.
  *                     LayerNorm forward: 0 runs one row per lane group, > 0
  *                     runs the persistent ring kernel of that lane count
  *                     (compiled-hidden shapes, rows_per_block 1) on that many

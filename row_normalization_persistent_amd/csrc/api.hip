@@ -337,9 +337,9 @@ size_t dyn_ws_bytes(norm_op op, int64_t hidden, int64_t slabs) {
 }
 
 // The column reduce addresses the workspace with 32-bit byte offsets and
-// reads up to 255 slabs past the last one (range-checked to zero).
+// reads at most one slab past the last one (clamped, range-checked to zero).
 bool dyn_slabs_fit(norm_op op, int64_t hidden, int64_t slabs) {
-    return (slabs + 256) * bwd_outs(op) * dyn_padded_hidden(hidden) * 4 <= INT32_MAX;
+    return (slabs + 1) * bwd_outs(op) * dyn_padded_hidden(hidden) * 4 <= INT32_MAX;
 }
 
 norm_status from_hip(hipError_t e) { return e == hipSuccess ? NORM_SUCCESS : NORM_ERROR_LAUNCH; }
@@ -548,7 +548,7 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
     } else {
         de = find_dyn(dyn_bwd_table(op), c.hidden, k.vector_elems, k.threads_per_row);
         if (!de) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
-        const int64_t slabs = (int64_t)k.grid * k.rows_per_block;
+        const int64_t slabs = k.grid;  // one slab per workgroup
         if (!dyn_slabs_fit(op, c.hidden, slabs)) return NORM_ERROR_INVALID_VALUE;
         ws_need = dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
     }
@@ -599,7 +599,7 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         if (!valid_elems(cfg->vector_elems) || cfg->threads_per_row <= 0) return 0;
         const int r = dyn_rows_per_block(cfg->threads_per_row);
         const int64_t g = cfg->grid > 0 ? cfg->grid : default_bwd_grid(rows, r);
-        return dyn_ws_bytes(op, hidden, g * r);
+        return dyn_ws_bytes(op, hidden, g);
     }
     size_t need = 0;
     if (hidden_compiled(hidden))
@@ -608,7 +608,7 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         if (hidden % w) continue;
         const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w, hidden);
         if (k.threads_per_row)
-            need = std::max(need, dyn_ws_bytes(op, hidden, (int64_t)k.grid * k.rows_per_block));
+            need = std::max(need, dyn_ws_bytes(op, hidden, k.grid));
     }
     return need;
 }
@@ -861,7 +861,7 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     char tmp[640];
     int n;
     if (is_bwd(op)) {
-        const int64_t slabs = (int64_t)c.grid * c.rows_per_block;
+        const int64_t slabs = c.grid;
         const int64_t padded = dyn ? dyn_padded_hidden(hidden) : hidden;
         char kern[96];
         if (dyn)

@@ -279,10 +279,10 @@ __global__ __launch_bounds__(T) void rmsnorm_bwd_rows_kernel(
 // multiple of 64, so a workgroup never straddles two outputs); its 256 lanes
 // form C/4 column groups of 4 columns x 1024/C slab streams.  Stream s adds
 // the slabs s, s + S, s + 2S, ... (S streams, 16 independent loads in flight
-// per pass; slabs past the last are range-checked to zero by the workspace
-// descriptor), then the S stream sums of each column are added as a fixed
-// pairwise tree.  C = 64 for up to 256 slabs (one pass), 16 for up to 1024 and 4
-// beyond, so many slabs spread over more workgroups instead of more passes.
+// per pass; a slab index past the last is clamped to the slab count, whose
+// offset the workspace descriptor range-checks to zero), then the S stream
+// sums of each column are added as a fixed pairwise tree.  C = 64 for up to
+// 256 slabs (one pass), 16 beyond, so many slabs spread over more workgroups.
 // The summation order is fixed for a given (slabs, hidden), so the result is
 // bit-reproducible.  Columns in the padding (hidden <= j < padded) are
 // summed but not stored.
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kColReduceThreads) void norm_bwd_colreduce_kernel(
         f32x4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int g = g0 + stream + u * kStreams;
+            const int g = min(g0 + stream + u * kStreams, grid_slabs);
             v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  ws, g * slab_bytes + flat * 4, 0, 0));
         }
@@ -340,11 +340,8 @@ hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t 
     if (cols == 64)
         hipLaunchKernelGGL(norm_bwd_colreduce_kernel<64>, grid, block, 0, stream, workspace,
                            slabs, hidden, padded, outs, dweight, dbias);
-    else if (cols == 16)
-        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<16>, grid, block, 0, stream, workspace,
-                           slabs, hidden, padded, outs, dweight, dbias);
     else
-        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<4>, grid, block, 0, stream, workspace,
+        hipLaunchKernelGGL(norm_bwd_colreduce_kernel<16>, grid, block, 0, stream, workspace,
                            slabs, hidden, padded, outs, dweight, dbias);
     return hipGetLastError();
 }

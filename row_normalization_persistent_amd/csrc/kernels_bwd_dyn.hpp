@@ -8,10 +8,11 @@
 //
 // A workgroup of dyn_block<T>() lanes runs R = block / T row "walkers" (one
 // per lane group); walker w of P = grid * R walks the rows w, w + P, w + 2P, ...
-// with a ring of D rows in flight, accumulates the column sums of its lanes'
-// columns in registers, and at the end writes them to its own slab of the
-// workspace: [P][outs][padded] fp32, padded = hidden rounded up to 64.  The
-// shared column-reduce kernel then sums the P slabs in a fixed order.
+// with a ring of D rows in flight and accumulates the column sums of its
+// lanes' columns in registers.  At the end the workgroup adds its R walkers'
+// sums in LDS (walker order) and writes one slab of the workspace:
+// [grid][outs][padded] fp32, padded = hidden rounded up to 64.  The shared
+// column-reduce kernel then sums the grid slabs in a fixed order.
 //
 // Every walker of a workgroup runs as many ring steps as the workgroup's
 // first walker (which has the most rows); the extra rows are past the end,
@@ -170,17 +171,44 @@ __device__ __forceinline__ void dyn_rms_row(const DynRow<W, V, false, DRES>& cur
     }
 }
 
-// Writes a lane's column sums to its walker's slab (columns past hidden are
-// skipped; they hold zeros anyway).
+// Writes the workgroup's column sums to its slab (columns past hidden are
+// skipped; they hold zeros anyway).  One walker (R == 1): each lane stores its
+// own.  Several: per access b, every lane puts its W sums in LDS, then the
+// workgroup's lanes take the access's T * W columns in turn, add each over
+// the R walkers in walker order and store it; `stage` holds R * T * W floats.
+// Uniform control flow required.
 template <int W, int T, int V>
 __device__ __forceinline__ void dyn_store_partials(float* slab, const float (&p)[V][W],
-                                                   int hidden, int lane) {
+                                                   int hidden, int lane, int g, float* stage) {
+    constexpr int R = dyn_block<T>() / T;
+    if constexpr (R == 1) {
 #pragma unroll
-    for (int b = 0; b < V; ++b) {
-        const int col = (b * T + lane) * W;
-        if (col < hidden) {
+        for (int b = 0; b < V; ++b) {
+            const int col = (b * T + lane) * W;
+            if (col < hidden) {
 #pragma unroll
-            for (int k = 0; k < W; ++k) slab[col + k] = p[b][k];
+                for (int k = 0; k < W; ++k) slab[col + k] = p[b][k];
+            }
+        }
+    } else {
+        constexpr int kCols = T * W;  // columns of one access
+        constexpr int kBlock = dyn_block<T>();
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+#pragma unroll
+            for (int k = 0; k < W; ++k) stage[(g * T + lane) * W + k] = p[b][k];
+            __syncthreads();
+#pragma unroll
+            for (int c0 = 0; c0 < kCols; c0 += kBlock) {
+                const int c = c0 + (int)threadIdx.x;
+                if (c < kCols && b * kCols + c < hidden) {
+                    float s = stage[c];
+#pragma unroll
+                    for (int r = 1; r < R; ++r) s += stage[r * kCols + c];
+                    slab[b * kCols + c] = s;
+                }
+            }
+            __syncthreads();
         }
     }
 }
@@ -214,7 +242,6 @@ __global__ __launch_bounds__(dyn_block<T>()) void norm_bwd_dyn_rows_kernel(DynBw
 
     const int64_t P = (int64_t)gridDim.x * R;
     const int64_t first = (int64_t)blockIdx.x * R;  // the workgroup's first walker
-    const int64_t me = first + g;
     const int64_t n = first < a.rows ? (a.rows - 1 - first) / P + 1 : 0;
     DynRow<W, V, LN, DRES> buf[D];
     // fences keep each slot's loads in slot order (precise memory-counter waits)
@@ -242,9 +269,10 @@ __global__ __launch_bounds__(dyn_block<T>()) void norm_bwd_dyn_rows_kernel(DynBw
     }
 
     const int64_t padded = dyn_padded_hidden(a.hidden);
-    float* slab = a.workspace + me * (LN ? 2 : 1) * padded;
-    dyn_store_partials<W, T, V>(slab, pw, a.hidden, lane);
-    if constexpr (LN) dyn_store_partials<W, T, V>(slab + padded, pb, a.hidden, lane);
+    float* slab = a.workspace + (int64_t)blockIdx.x * (LN ? 2 : 1) * padded;
+    __shared__ float stage[R > 1 ? dyn_block<T>() * W : 1];
+    dyn_store_partials<W, T, V>(slab, pw, a.hidden, lane, g, stage);
+    if constexpr (LN) dyn_store_partials<W, T, V>(slab + padded, pb, a.hidden, lane, g, stage);
 }
 
 // Ring depth: as deep as the register budget allows without spills (the
@@ -268,7 +296,6 @@ constexpr bool dyn_bwd_fits() {
 
 template <int W, int T, int V, bool LN>
 hipError_t launch_bwd_dyn(const DynBwdArgs& a, hipStream_t stream) {
-    constexpr int R = dyn_block<T>() / T;
     constexpr int D = dyn_bwd_depth<W, T, V>();
     const int outs = LN ? 2 : 1;
     if (a.rows > 0) {
@@ -286,7 +313,7 @@ hipError_t launch_bwd_dyn(const DynBwdArgs& a, hipStream_t stream) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    return launch_norm_colreduce(a.workspace, a.rows > 0 ? a.grid * R : 0, a.hidden,
+    return launch_norm_colreduce(a.workspace, a.rows > 0 ? a.grid : 0, a.hidden,
                                  (int32_t)dyn_padded_hidden(a.hidden), outs, a.dweight, a.dbias,
                                  stream);
 }

@@ -142,10 +142,23 @@ hipError_t launch_norm_colreduce(const float* workspace, int32_t slabs, int32_t 
 // to 1024 and 4 beyond (more workgroups instead of more passes).
 constexpr int kColReduceThreads = 256;
 constexpr int kColReduceCols = 64;
-constexpr int colreduce_cols(int64_t slabs) { return slabs <= 256 ? 64 : (slabs <= 1024 ? 16 : 4); }
+// Columns per column-reduce workgroup: 64 (16 slab streams, one pass of 256
+// slabs) up to 256 slabs, else 16 (64 streams, passes of 1024 slabs).
+// Narrower workgroups read 16 bytes of each 128-byte line of a slab row, so
+// the line is fetched once per workgroup; measured slower at every slab count.
+#ifndef ROWNORM_COLREDUCE_COLS
+#define ROWNORM_COLREDUCE_COLS 0  // build-time override of the choice below (64 or 16)
+#endif
+static_assert(ROWNORM_COLREDUCE_COLS == 0 || ROWNORM_COLREDUCE_COLS == 16 ||
+                  ROWNORM_COLREDUCE_COLS == 64,
+              "the column reduce is compiled for 64 and 16 columns per workgroup");
+constexpr int colreduce_cols(int64_t slabs) {
+    if constexpr (ROWNORM_COLREDUCE_COLS > 0) return ROWNORM_COLREDUCE_COLS;
+    return slabs <= 256 ? 64 : 16;
+}
 // Largest persistent grid for a hidden size: the workspace ([grid][2][hidden]
 // fp32) must stay addressable by one 32-bit buffer descriptor, with room for
-// the column reduce's range-checked reads one pass past the last slab.
+// the column reduce's clamped, range-checked reads one slab past the last.
 constexpr int64_t max_bwd_grid(int64_t hidden) {
     return ((int64_t(1) << 31) - 1) / (8 * hidden) - 128;
 }

@@ -186,7 +186,8 @@ def test_workspace_bytes():
         assert rn.workspace_bytes(100, h, rn.Cfg(256, 1, 7)) == 7 * 2 * h * 4
     assert rn.workspace_bytes(3, 4096) == 3 * 2 * 4096 * 4  # never more slabs than rows
     # run-time shapes: one slab per row group, each output padded to 64 columns
-    assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 16 * 2 * 1024 * 4
+    # run-time shapes: one slab per workgroup, whatever its rows per workgroup
+    assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 2 * 1024 * 4
     assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
     assert rn.workspace_bytes(10, 70000) == 0
     assert rn.workspace_bytes(-1, 4096) == 0
