@@ -29,7 +29,9 @@ Also reported, on the same line:
                 the run-time-hidden kernels: fused add + RMSNorm at hidden
                 5120 and at 4096 (forced, against the compiled kernel), an
                 in-place RMSNorm over 128-wide column slices (row stride
-                384), LayerNorm and RMSNorm backward at hidden 5120
+                384), LayerNorm and RMSNorm backward at hidden 5120; then
+                few wide rows through the row-split forward (one row over
+                several workgroups) beside one workgroup per row
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
@@ -458,6 +460,57 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     del xs, dys, drs, dxs, x0, dy0, dr0
     torch.cuda.synchronize()
     out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds)
+    out += split_ops(torch, rn, wl, dev, stream, reps)
+    return out
+
+
+def split_ops(torch, rn, wl, dev, stream, reps):
+    """Few wide rows: the row-split forward (the library's choice of chunks)
+    beside one workgroup per row, back to back from one graph over 32 buffer
+    sets (a few MB: these launches are latency-bound, not bandwidth-bound)."""
+    out = []
+    n = 32
+    ws = torch.zeros(rn.split_workspace_bytes(64), dtype=torch.uint8, device=dev)
+    for op, rows, h in (("fused_add_rmsnorm", 1, 65536), ("fused_add_rmsnorm", 16, 65536),
+                        ("rmsnorm_fwd", 1, 65536), ("layernorm_fwd", 1, 49152),
+                        ("layernorm_fwd", 8, 65536)):
+        i = (wl.fused_inputs if op == "fused_add_rmsnorm" else
+             wl.rmsnorm_inputs if op == "rmsnorm_fwd" else wl.layernorm_fwd_inputs)(rows, h, 0)
+        xs = [wl.to_device_bf16(i["x"], dev) for _ in range(n)]
+        ys = [torch.empty_like(xs[0]) for _ in range(n)]
+        w = wl.to_device_bf16(i["w"], dev)
+        if op == "fused_add_rmsnorm":
+            rs = [wl.to_device_bf16(i["r"], dev) for _ in range(n)]
+            call = lambda j, k: rn.fused_add_rmsnorm(xs[j], rs[j], w, i["eps"], out=ys[j],
+                                                     stream=stream, workspace=ws, split=k)
+            nb = 8 * h * rows + 2 * h
+        elif op == "rmsnorm_fwd":
+            call = lambda j, k: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream,
+                                               workspace=ws, split=k)
+            nb = 4 * h * rows + 2 * h
+        else:
+            bb = wl.to_device_bf16(i["b"], dev)
+            st = torch.empty(n, 2, rows, device=dev)
+            call = lambda j, k: rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
+                                                 rstd=st[j, 1], stream=stream, workspace=ws,
+                                                 split=k)
+            nb = (4 * h + 8) * rows + 4 * h
+        k, v = rn.select_split(op, rows, h)
+        plain = None
+        if not (op == "layernorm_fwd" and h > 49152):  # one workgroup per row holds it
+            plain = graph_time_per_launch(torch, stream, [
+                (lambda j=j: call(j, 1)) for j in range(n)], reps)
+        t = graph_time_per_launch(torch, stream, [(lambda j=j: call(j, 0)) for j in range(n)],
+                                  reps)
+        note = f"row split into {k} chunks of {256 * v * 8} columns"
+        if plain is not None:
+            note += f"; one workgroup per row: {plain:.2f} us"
+        rec = _op_rec(op, rows, h, nb, t, note=note)
+        rec["split"] = k
+        rec["us_one_workgroup_per_row"] = None if plain is None else round(plain, 3)
+        out.append(rec)
+        del xs, ys
+    torch.cuda.synchronize()
     return out
 
 

@@ -308,6 +308,70 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_ex(void* ds, int64_t ld_ds, floa
                                                    const norm_launch_cfg* cfg,
                                                    hipStream_t stream);
 
+/* Row-split forward ("Llu/ln bwd", author note: the grid-parallel inner
+ * normalization the pages list as missing).  With few rows one workgroup per
+ * row leaves most CUs idle and moves a wide row at the rate of one CU; these
+ * entry points may instead cut each row into `k` contiguous chunks, one
+ * workgroup each, whose partial sums meet in `workspace` (the workgroups of
+ * a row wait for each other there; LayerNorm combines the chunks' sums and
+ * centered sums of squares exactly).  Results equal the operation's
+ * definition within the same tolerances as the other entry points, with a
+ * different summation order, and are bitwise reproducible run to run.
+ *   split = 0: the library's choice (norm_select_split; rows it does not
+ *              split run the operation's usual kernels and leave the
+ *              workspace untouched, which may then be NULL);
+ *   split = 1: never split;
+ *   split = k >= 2: about k workgroups per row (the chunk count that covers
+ *              the row with the fewest 16-byte accesses per lane, at most 8);
+ *              needs 16-byte-aligned pointers (else MISALIGNED), hidden a
+ *              multiple of 8, rows <= 512 and rows * k <= the device's CU
+ *              count (else INVALID_VALUE).
+ * Through these entry points LayerNorm forward also takes rows of up to 65536
+ * (wider than its one-workgroup-per-row kernels hold) when they are split.
+ * Arguments, aliasing rules and errors are otherwise the operation's own;
+ * rows are contiguous.  workspace: device memory of at least
+ * norm_split_workspace_bytes(rows) bytes, 16-byte aligned, overlapping no
+ * other argument, ZERO-FILLED before its first use; every call that finishes
+ * leaves it zero-filled again, so one workspace serves any number of calls
+ * in stream order (calls that overlap in time on one workspace race).  Its
+ * first 32-bit word stays 0 unless a workgroup gave up waiting for its row's
+ * partners (about a second; only possible when other work keeps the launch
+ * from being resident at once): then that call's results are invalid and
+ * the workspace must be zero-filled again.  Ownership: the caller's. */
+NORM_API norm_status norm_fused_add_rmsnorm_split(void* out, void* residual, const void* x,
+                                                  const void* weight, int64_t rows,
+                                                  int64_t hidden, float eps, void* workspace,
+                                                  size_t workspace_bytes, int32_t split,
+                                                  hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_fwd_split(void* out, const void* x, const void* weight,
+                                            int64_t rows, int64_t hidden, float eps,
+                                            void* workspace, size_t workspace_bytes,
+                                            int32_t split, hipStream_t stream);
+NORM_API norm_status norm_layernorm_fwd_split(void* y, float* mean, float* rstd, const void* x,
+                                              const void* weight, const void* bias,
+                                              int64_t rows, int64_t hidden, float eps,
+                                              void* workspace, size_t workspace_bytes,
+                                              int32_t split, hipStream_t stream);
+
+/* Workspace bytes the row-split entry points need for `rows` rows (0 for
+ * rows <= 0; constant above 512 rows, which are never split). */
+NORM_API size_t norm_split_workspace_bytes(int64_t rows);
+
+/* The row split the library would choose for a forward op (fused, RMSNorm or
+ * LayerNorm forward) on contiguous 16-byte-aligned rows with `cu_count` CUs
+ * (<= 0: the current device): *split = workgroups per row (1: no split) and
+ * *vecs = 16-byte accesses per lane (0 when not split).  Rows are split when
+ * hidden is a multiple of 8 and either up to 8 rows move >= 256 KiB each
+ * (fused op: 8 * hidden bytes) or >= 192 KiB each (the others: 4 * hidden
+ * bytes), 9 to 32 rows
+ * move >= 384 KiB each, or no one-workgroup-per-row kernel holds the row
+ * (LayerNorm above 49152; up to 64 rows).  Chunks aim at about 64 KiB of
+ * traffic (8192 columns fused, 16384 RMSNorm, 12288 LayerNorm), at most
+ * max(4, 64 / rows) a row and rows * k <= cu_count.  Pure host logic when
+ * cu_count > 0. */
+NORM_API norm_status norm_select_split(norm_op op, int64_t rows, int64_t hidden,
+                                       int32_t cu_count, int32_t* split, int32_t* vecs);
+
 /* The library's launch choice for (op, rows, hidden) on a device with
  * `cu_count` compute units (the small-batch rule of "optimize inner
  * persistent scheduler for static fusion", author description: when the

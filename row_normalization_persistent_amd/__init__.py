@@ -91,6 +91,7 @@ _lib = None
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
+_i32 = ctypes.c_int32
 _cfgp = ctypes.POINTER(LaunchCfg)
 
 
@@ -136,6 +137,12 @@ def lib() -> ctypes.CDLL:
                                 _f32, _cfgp, _vp],
         "norm_fused_add_rmsnorm_bwd_ex": [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                           _vp, _sz, _i64, _i64, _f32, _cfgp, _vp],
+        # row-split forward: workspace, workspace bytes, workgroups per row
+        "norm_fused_add_rmsnorm_split": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _sz, _i32,
+                                         _vp],
+        "norm_rmsnorm_fwd_split": [_vp, _vp, _vp, _i64, _i64, _f32, _vp, _sz, _i32, _vp],
+        "norm_layernorm_fwd_split": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _sz,
+                                     _i32, _vp],
     }
     for n, args in sigs.items():
         fn = getattr(L, n)
@@ -149,6 +156,11 @@ def lib() -> ctypes.CDLL:
     L.norm_layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.norm_layernorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
     L.norm_layernorm_bwd_workspace_bytes_cfg.restype = ctypes.c_size_t
+    L.norm_split_workspace_bytes.argtypes = [_i64]
+    L.norm_split_workspace_bytes.restype = ctypes.c_size_t
+    L.norm_select_split.argtypes = [ctypes.c_int, _i64, _i64, _i32, ctypes.POINTER(_i32),
+                                    ctypes.POINTER(_i32)]
+    L.norm_select_split.restype = ctypes.c_int
     L.norm_select_config.argtypes = [ctypes.c_int, _i64, _i64, ctypes.c_int32, _cfgp]
     L.norm_select_config.restype = ctypes.c_int
     L.norm_list_configs.argtypes = [ctypes.c_int, _i64, _cfgp, ctypes.c_int32]
@@ -247,9 +259,52 @@ def _like(t, out, name):
     return out
 
 
-def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, stream=None):
+def split_workspace_bytes(rows: int) -> int:
+    """Bytes of workspace the row-split forward needs for `rows` rows."""
+    return int(lib().norm_split_workspace_bytes(rows))
+
+
+def select_split(op, rows: int, hidden: int, cu_count: int = 0):
+    """(workgroups per row, 16-byte accesses per lane) the library would use
+    for a row-split forward; (1, 0) means no split."""
+    k, v = _i32(), _i32()
+    _check(lib().norm_select_split(int(OPS.get(op, op)), rows, hidden, cu_count,
+                                   ctypes.byref(k), ctypes.byref(v)), "norm_select_split")
+    return k.value, v.value
+
+
+def _split_ws(workspace):
+    """(pointer, bytes) of a row-split workspace (a zero-filled uint8 device
+    tensor), or (None, 0)."""
+    if workspace is None:
+        return None, 0
+    _mat(workspace, "workspace", torch.uint8)
+    return workspace.data_ptr(), workspace.numel()
+
+
+def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, stream=None,
+                      workspace=None, split=None):
     """residual <- bf16(x + residual) in place; returns (out, residual).
-    x, residual and out may be row-strided views (e.g. column slices)."""
+    x, residual and out may be row-strided views (e.g. column slices).  With
+    `workspace` (zero-filled uint8, split_workspace_bytes(rows)) or `split`,
+    runs the row-split entry point on contiguous rows (split None/0: the
+    library's choice, 1: never, k: about k workgroups a row)."""
+    if workspace is not None or split is not None:
+        if cfg is not None:
+            raise ValueError("cfg does not apply to the row-split entry point")
+        rows, hidden = _rows_hidden(_mat(x, "x"))
+        _mat(residual, "residual")
+        if residual.shape != x.shape:
+            raise ValueError("residual must have x's shape")
+        _vec(weight, hidden, "weight")
+        out = _mat(_like(x, out, "out"), "out")
+        wp, wb = _split_ws(workspace)
+        _check(lib().norm_fused_add_rmsnorm_split(out.data_ptr(), residual.data_ptr(),
+                                                  x.data_ptr(), weight.data_ptr(), rows, hidden,
+                                                  float(eps), wp, wb, int(split or 0),
+                                                  _stream(stream)),
+               "norm_fused_add_rmsnorm_split")
+        return out, residual
     rows, hidden, ld_x = _rows(x, "x")
     if residual.shape != x.shape:
         raise ValueError("residual must have x's shape")
@@ -264,7 +319,21 @@ def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, strea
     return out, residual
 
 
-def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None):
+def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspace=None,
+                split=None):
+    """workspace / split: the row-split entry point, as for fused_add_rmsnorm."""
+    if workspace is not None or split is not None:
+        if cfg is not None:
+            raise ValueError("cfg does not apply to the row-split entry point")
+        rows, hidden = _rows_hidden(_mat(x, "x"))
+        _vec(weight, hidden, "weight")
+        out = _mat(_like(x, out, "out"), "out")
+        wp, wb = _split_ws(workspace)
+        _check(lib().norm_rmsnorm_fwd_split(out.data_ptr(), x.data_ptr(), weight.data_ptr(),
+                                            rows, hidden, float(eps), wp, wb, int(split or 0),
+                                            _stream(stream)),
+               "norm_rmsnorm_fwd_split")
+        return out
     rows, hidden, ld_x = _rows(x, "x")
     _vec(weight, hidden, "weight")
     out = _like(x, out, "out")
@@ -276,8 +345,14 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None):
 
 
 def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
-                  with_stats: bool = True, cfg=None, stream=None):
-    """Returns (y, mean, rstd); mean/rstd are None when with_stats is False."""
+                  with_stats: bool = True, cfg=None, stream=None, workspace=None, split=None):
+    """Returns (y, mean, rstd); mean/rstd are None when with_stats is False.
+    workspace / split: the row-split entry point, as for fused_add_rmsnorm."""
+    use_split = workspace is not None or split is not None
+    if use_split:
+        if cfg is not None:
+            raise ValueError("cfg does not apply to the row-split entry point")
+        _mat(x, "x")
     rows, hidden, ld_x = _rows(x, "x")
     _vec(weight, hidden, "weight")
     _vec(bias, hidden, "bias")
@@ -294,6 +369,15 @@ def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
     else:
         mean = rstd = None
         mp = rp = None
+    if use_split:
+        _mat(y, "y")
+        wp, wb = _split_ws(workspace)
+        _check(lib().norm_layernorm_fwd_split(y.data_ptr(), mp, rp, x.data_ptr(),
+                                              weight.data_ptr(), bias.data_ptr(), rows, hidden,
+                                              float(eps), wp, wb, int(split or 0),
+                                              _stream(stream)),
+               "norm_layernorm_fwd_split")
+        return y, mean, rstd
     _check(lib().norm_layernorm_fwd_ex(y.data_ptr(), ld_y, mp, rp, x.data_ptr(), ld_x,
                                        weight.data_ptr(), bias.data_ptr(), rows, hidden,
                                        float(eps), _cfg_ptr(cfg), _stream(stream)),

@@ -34,6 +34,7 @@ SOURCES = [
     "k_layernorm_fwd_dyn.hip",
     "k_layernorm_bwd_dyn.hip",
     "k_rmsnorm_bwd_dyn.hip",
+    "k_split.hip",
 ]
 
 HIPCC_FLAGS = [

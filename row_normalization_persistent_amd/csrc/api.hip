@@ -360,17 +360,21 @@ struct FwdCall {
     float eps;
 };
 
-norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
-                    hipStream_t stream) {
+// What the checks of a forward call found out about its layout.
+struct FwdLayout {
+    int64_t ld_res;    // the residual's stride (hidden for the unfused ops)
+    int ws, wp;        // widest access the shape / the pointers allow
+    int w_max;         // min(ws, wp)
+    bool contiguous;   // every matrix has ld == hidden
+    bool compiled_ok;  // a compiled-hidden kernel can run it
+};
+
+// Argument checks every forward entry shares (cfg aside).  NORM_SUCCESS with
+// rows == 0 means: nothing to launch.
+norm_status check_fwd(norm_op op, const FwdCall& c, FwdLayout* L) {
     const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
     const bool ln = op == NORM_OP_LAYERNORM_FWD;
     if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
-    // grid > 0 names a persistent ring shape: LayerNorm's compiled kernels only
-    if (cfg && (cfg->grid < 0 || cfg->grid > kMaxFwdRingGrid ||
-                (cfg->grid > 0 && (!ln || cfg->vector_elems != 0 || cfg->rows_per_block != 1)) ||
-                cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
-                !valid_elems(cfg->vector_elems)))
-        return NORM_ERROR_INVALID_VALUE;
     if (c.rows == 0) return NORM_SUCCESS;
     if (c.hidden < 1 || c.hidden > kMaxHidden) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     if (!c.out || !c.x || !c.weight || (fused && !c.residual) || (ln && !c.bias))
@@ -399,12 +403,32 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         conflict(rstd, b, false))
         return NORM_ERROR_INVALID_VALUE;
 
-    const int ws = shape_width(c.hidden, {c.ld_out, c.ld_x, ld_res});
-    const int wp = pointer_width({c.out, c.x, c.weight, fused ? c.residual : nullptr,
-                                  ln ? c.bias : nullptr});
-    const int w_max = std::min(ws, wp);
-    const bool contiguous = c.ld_out == c.hidden && c.ld_x == c.hidden && ld_res == c.hidden;
-    const bool compiled_ok = hidden_compiled(c.hidden) && contiguous && w_max == 8;
+    L->ld_res = ld_res;
+    L->ws = shape_width(c.hidden, {c.ld_out, c.ld_x, ld_res});
+    L->wp = pointer_width({c.out, c.x, c.weight, fused ? c.residual : nullptr,
+                           ln ? c.bias : nullptr});
+    L->w_max = std::min(L->ws, L->wp);
+    L->contiguous = c.ld_out == c.hidden && c.ld_x == c.hidden && ld_res == c.hidden;
+    L->compiled_ok = hidden_compiled(c.hidden) && L->contiguous && L->w_max == 8;
+    return NORM_SUCCESS;
+}
+
+norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
+                    hipStream_t stream) {
+    const bool ln = op == NORM_OP_LAYERNORM_FWD;
+    if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
+    // grid > 0 names a persistent ring shape: LayerNorm's compiled kernels only
+    if (cfg && (cfg->grid < 0 || cfg->grid > kMaxFwdRingGrid ||
+                (cfg->grid > 0 && (!ln || cfg->vector_elems != 0 || cfg->rows_per_block != 1)) ||
+                cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
+                !valid_elems(cfg->vector_elems)))
+        return NORM_ERROR_INVALID_VALUE;
+    FwdLayout L;
+    const norm_status chk = check_fwd(op, c, &L);
+    if (chk != NORM_SUCCESS || c.rows == 0) return chk;
+    const int64_t ld_res = L.ld_res;
+    const int ws = L.ws, wp = L.wp, w_max = L.w_max;
+    const bool contiguous = L.contiguous, compiled_ok = L.compiled_ok;
 
     if (!compiled_ok && !(cfg && cfg->vector_elems == 0) &&
         c.hidden > max_dyn_hidden(dyn_fwd_table(op), cfg ? cfg->vector_elems : w_max))
@@ -458,6 +482,130 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
                        c.rstd,    c.ld_out,   ld_res, c.ld_x,  c.rows,   (int32_t)c.hidden,
                        c.eps};
     return from_hip(e->launch(a, stream));
+}
+
+// ---- row-split forward entry ---------------------------------------------------
+// Splitting costs ~1 us (the partners' round trip through the workspace) and
+// pays only where one workgroup is slow to move its row.  Measured (one MI355X,
+// graph-timed, us; "plain" = one workgroup per row):
+//   fused 1 x 16384 (128 KiB a row): plain 3.0, best split 3.3   -> not split
+//   fused 8 x 24576 (192 KiB):       plain 4.7, k = 3 4.8         -> not split
+//   fused 1 x 32768 (256 KiB):       plain 5.4, k = 4 3.7
+//   RMSNorm 1 x 49152 (192 KiB):     plain 4.4, k = 4 3.7
+//   fused 16 x 49152 (384 KiB):      plain 9.2, k = 4 7.1; 16 x 32768: 6.6 vs 6.4
+//   fused 32 x 65536:                plain 12.3, k = 4 10.2; 64 rows: plain wins
+// So: up to 8 rows, rows moving >= 256 KiB (fused) or 192 KiB (the others);
+// 9-32 rows, >= 384 KiB; chunks of
+// ~64 KiB of traffic (8192 columns fused, 16384 RMSNorm, 12288 LayerNorm);
+// at most max(4, 64 / rows) chunks a row (16 x 65536 fused: k = 4 7.7 us,
+// k = 8 9.0 us).  Rows that no one-workgroup-per-row kernel holds (LayerNorm
+// above 49152) are split whenever a shape exists, up to 64 rows.
+constexpr int64_t kSplitMaxRows = 512;
+
+size_t split_ws_bytes(int64_t rows) {
+    if (rows <= 0) return 0;
+    return (size_t)kSplitHeaderWords * 4 +
+           (size_t)std::min(rows, kSplitMaxRows) * kSplitRowQwords * 8;
+}
+
+struct SplitShape {
+    int k;     // workgroups per row (1: no split)
+    int vecs;  // 16-byte accesses per lane
+};
+
+// The (k, V) of an explicit request of `split` workgroups per row: V is the
+// fewest accesses a lane that covers the row in `split` chunks, k the chunks
+// that V then needs (no empty chunk).  vecs = 0 when no such shape exists.
+SplitShape split_shape(int64_t hidden, int64_t split) {
+    if (split < 1) return {1, 0};
+    const int64_t acc = hidden / 8;
+    const int64_t v = ceil_div(acc, (int64_t)kSplitLanes * split);
+    if (v < 1 || v > kSplitMaxVecs) return {1, 0};
+    return {(int)ceil_div(acc, (int64_t)kSplitLanes * v), (int)v};
+}
+
+// Whether a one-workgroup-per-row kernel holds contiguous 16-byte rows of
+// this hidden size.
+bool fwd_plain_holds(norm_op op, int64_t hidden) {
+    return hidden_compiled(hidden) || hidden <= max_dyn_hidden(dyn_fwd_table(op), 8);
+}
+
+SplitShape choose_split(norm_op op, int64_t rows, int64_t hidden, int cu) {
+    if (rows < 1 || rows > kSplitMaxRows || hidden % 8) return {1, 0};
+    const bool plain = fwd_plain_holds(op, hidden);
+    const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
+    if (plain) {
+        const int64_t row_bytes = (fused ? 8 : 4) * hidden;
+        const int64_t min_bytes = rows > 8 ? (384 << 10) : (fused ? (256 << 10) : (192 << 10));
+        if (rows > 32 || row_bytes < min_bytes) return {1, 0};
+    }
+    const int64_t kcap = std::min<int64_t>({(int64_t)kSplitMax, std::max<int64_t>(4, 64 / rows),
+                                            cu / rows});
+    if (kcap < 2) return {1, 0};
+    const int64_t target = fused ? 8192 : (op == NORM_OP_LAYERNORM_FWD ? 12288 : 16384);
+    const int64_t want = std::max<int64_t>(2, ceil_div(hidden, target));
+    SplitShape sh = split_shape(hidden, std::min(kcap, want));
+    if (sh.vecs == 0 && !plain) sh = split_shape(hidden, kcap);  // needs more, smaller chunks
+    return sh.vecs == 0 || sh.k < 2 ? SplitShape{1, 0} : sh;
+}
+
+// The workspace of a row-split call: big enough, 16-byte aligned, apart from
+// every other argument.
+norm_status check_split_ws(norm_op op, const FwdCall& c, const FwdLayout& L, void* workspace,
+                           size_t ws_bytes) {
+    if (!workspace || ws_bytes < split_ws_bytes(c.rows)) return NORM_ERROR_WORKSPACE;
+    if (!aligned(workspace, 16)) return NORM_ERROR_MISALIGNED;
+    const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
+    const bool ln = op == NORM_OP_LAYERNORM_FWD;
+    const Region wsr = vec_region(workspace, (int64_t)split_ws_bytes(c.rows), 1);
+    for (const Region& r : {Region{c.out, c.rows, c.ld_out, c.hidden, 2},
+                            Region{c.x, c.rows, c.ld_x, c.hidden, 2},
+                            Region{fused ? c.residual : nullptr, c.rows, L.ld_res, c.hidden, 2},
+                            vec_region(c.weight, c.hidden, 2),
+                            vec_region(ln ? c.bias : nullptr, c.hidden, 2),
+                            vec_region(ln ? c.mean : nullptr, c.rows, 4),
+                            vec_region(ln ? c.rstd : nullptr, c.rows, 4)})
+        if (conflict(wsr, r, false)) return NORM_ERROR_INVALID_VALUE;
+    return NORM_SUCCESS;
+}
+
+norm_status run_fwd_split(norm_op op, const FwdCall& c, void* workspace, size_t ws_bytes,
+                          int32_t split, hipStream_t stream) {
+    if (split < 0 || split > kSplitMax) return NORM_ERROR_INVALID_VALUE;
+    if (split == 1) return run_fwd(op, c, nullptr, stream);
+    FwdLayout L;
+    norm_status st = check_fwd(op, c, &L);
+    if (st != NORM_SUCCESS || c.rows == 0) return st;
+    SplitShape sh;
+    int cu = 0;
+    if (split >= 2) {  // everything but the CU count is checked before any HIP call
+        if (!L.contiguous || L.ws < 8 || c.rows > kSplitMaxRows) return NORM_ERROR_INVALID_VALUE;
+        if (L.wp < 8) return NORM_ERROR_MISALIGNED;
+        sh = split_shape(c.hidden, split);
+        if (sh.vecs == 0) return NORM_ERROR_INVALID_VALUE;
+        if ((st = check_split_ws(op, c, L, workspace, ws_bytes)) != NORM_SUCCESS) return st;
+        if ((st = current_cu_count(&cu)) != NORM_SUCCESS) return st;
+        if (c.rows * sh.k > cu) return NORM_ERROR_INVALID_VALUE;
+    } else {
+        if (!L.contiguous || L.w_max < 8) return run_fwd(op, c, nullptr, stream);
+        if ((st = current_cu_count(&cu)) != NORM_SUCCESS) return st;
+        sh = choose_split(op, c.rows, c.hidden, cu);
+        if (sh.k == 1) return run_fwd(op, c, nullptr, stream);
+        if ((st = check_split_ws(op, c, L, workspace, ws_bytes)) != NORM_SUCCESS) return st;
+    }
+
+    const int sop = op == NORM_OP_FUSED_ADD_RMSNORM ? kSplitFused
+                    : op == NORM_OP_LAYERNORM_FWD   ? kSplitLn
+                                                    : kSplitRms;
+    for (const SplitEntry& e : split_table())
+        if (e.op == sop && e.vecs == sh.vecs) {
+            const SplitArgs a{c.out,     c.residual, c.x,      c.weight, c.bias,
+                              c.mean,    c.rstd,     static_cast<uint32_t*>(workspace),
+                              c.ld_out,  L.ld_res,   c.ld_x,   c.rows,   (int32_t)c.hidden,
+                              sh.k,      c.eps};
+            return from_hip(e.launch(a, stream));
+        }
+    return NORM_ERROR_INVALID_VALUE;
 }
 
 // ---- backward entry ------------------------------------------------------------
@@ -722,6 +870,53 @@ norm_status norm_layernorm_fwd(void* y, float* mean, float* rstd, const void* x,
                                float eps, hipStream_t stream) {
     return norm_layernorm_fwd_cfg(y, mean, rstd, x, weight, bias, rows, hidden, eps, nullptr,
                                   stream);
+}
+
+// ---- row-split forward --------------------------------------------------------------
+norm_status norm_fused_add_rmsnorm_split(void* out, void* residual, const void* x,
+                                         const void* weight, int64_t rows, int64_t hidden,
+                                         float eps, void* workspace, size_t workspace_bytes,
+                                         int32_t split, hipStream_t stream) {
+    const FwdCall c{out,    hidden,  residual, hidden, x,      hidden, weight,
+                    nullptr, nullptr, nullptr, rows,   hidden, eps};
+    return run_fwd_split(NORM_OP_FUSED_ADD_RMSNORM, c, workspace, workspace_bytes, split,
+                         stream);
+}
+
+norm_status norm_rmsnorm_fwd_split(void* out, const void* x, const void* weight, int64_t rows,
+                                   int64_t hidden, float eps, void* workspace,
+                                   size_t workspace_bytes, int32_t split, hipStream_t stream) {
+    const FwdCall c{out,    hidden,  nullptr, hidden, x,      hidden, weight,
+                    nullptr, nullptr, nullptr, rows,  hidden, eps};
+    return run_fwd_split(NORM_OP_RMSNORM_FWD, c, workspace, workspace_bytes, split, stream);
+}
+
+norm_status norm_layernorm_fwd_split(void* y, float* mean, float* rstd, const void* x,
+                                     const void* weight, const void* bias, int64_t rows,
+                                     int64_t hidden, float eps, void* workspace,
+                                     size_t workspace_bytes, int32_t split, hipStream_t stream) {
+    const FwdCall c{y, hidden, nullptr, hidden, x, hidden, weight, bias, mean, rstd, rows,
+                    hidden, eps};
+    return run_fwd_split(NORM_OP_LAYERNORM_FWD, c, workspace, workspace_bytes, split, stream);
+}
+
+size_t norm_split_workspace_bytes(int64_t rows) { return split_ws_bytes(rows); }
+
+norm_status norm_select_split(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
+                              int32_t* split, int32_t* vecs) {
+    if (!split || !vecs || rows < 0 || hidden < 1 ||
+        (op != NORM_OP_FUSED_ADD_RMSNORM && op != NORM_OP_RMSNORM_FWD &&
+         op != NORM_OP_LAYERNORM_FWD))
+        return NORM_ERROR_INVALID_VALUE;
+    int cu = cu_count;
+    if (cu <= 0) {
+        const norm_status st = current_cu_count(&cu);
+        if (st != NORM_SUCCESS) return st;
+    }
+    const SplitShape sh = choose_split(op, rows, hidden, cu);
+    *split = sh.k;
+    *vecs = sh.vecs;
+    return NORM_SUCCESS;
 }
 
 // ---- backward -----------------------------------------------------------------------

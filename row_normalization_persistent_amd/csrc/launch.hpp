@@ -122,6 +122,49 @@ const std::vector<DynFwdEntry>& layernorm_fwd_dyn_table();
 const std::vector<DynBwdEntry>& layernorm_bwd_dyn_table();
 const std::vector<DynBwdEntry>& rmsnorm_bwd_dyn_table();
 
+// ---- row-split forward (few rows: one row over k workgroups) ------------------
+// Workspace: kSplitHeaderWords 32-bit words (word 0: error bits), then per
+// row kSplitRowQwords 64-bit words: [kSplitDepart] the count of workgroups
+// done with the row, [kSplitP0 + j] and [kSplitP1 + j] chunk j's two partial
+// sums (fp32 bits in the high half, 1 in the low half once written).  Zero
+// at rest.
+constexpr int kSplitLanes = 256;        // lanes per workgroup
+constexpr int kSplitMax = 64;           // workgroups per row at most (one wave polls them)
+constexpr int kSplitMaxVecs = 8;        // 16-byte accesses per lane at most
+constexpr int kSplitHeaderWords = 64;
+constexpr int kSplitDepart = 0;
+constexpr int kSplitP0 = 1;
+constexpr int kSplitP1 = kSplitP0 + kSplitMax;
+constexpr int kSplitRowQwords = 144;    // >= kSplitP1 + kSplitMax, 128-byte multiple
+constexpr uint32_t kSplitSpinLimit = 1u << 20;
+enum SplitOp : int { kSplitFused = 0, kSplitRms = 1, kSplitLn = 2 };
+
+struct SplitArgs {
+    void* out;             // fused/rms: out; layernorm: y
+    void* residual;        // fused only (in/out)
+    const void* x;
+    const void* weight;
+    const void* bias;      // layernorm only
+    float* mean;           // layernorm only (may be null together with rstd)
+    float* rstd;
+    uint32_t* ws;
+    int64_t ld_out, ld_res, ld_x;
+    int64_t rows;
+    int32_t hidden;
+    int32_t split;         // k workgroups per row
+    float eps;
+};
+
+using SplitLauncher = hipError_t (*)(const SplitArgs&, hipStream_t);
+
+struct SplitEntry {
+    int op;    // kSplitFused / kSplitRms / kSplitLn
+    int vecs;  // V 16-byte accesses per lane: a chunk is kSplitLanes * V * 8 columns
+    SplitLauncher launch;
+};
+
+const std::vector<SplitEntry>& split_table();
+
 // Workgroup size of the run-time path for T lanes per row: rows narrower than
 // 256 lanes are packed 256 / T to a workgroup.
 constexpr int dyn_block_size(int lanes) { return lanes < 256 ? 256 : lanes; }

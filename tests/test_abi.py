@@ -31,7 +31,9 @@ def test_header_declares_the_four_operations():
     for op in list(names):
         if op.endswith("_ex"):
             assert op[:-3] in names  # every strided variant has a plain form
-    assert len(names) == 26
+    for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd"):
+        assert op + "_split" in names  # the row-split forward
+    assert len(names) == 31
 
 
 def test_library_exports_every_declared_symbol():
@@ -402,3 +404,99 @@ def test_strided_validation():
     assert L.norm_fused_add_rmsnorm_bwd_ex(A, 4096, A + GB, A + 2 * GB, 4096, None, 0,
                                            A + 3 * GB, 4096, A + 5 * GB, A + 6 * GB, 0, 8192,
                                            4096, 1e-6, None, None) == WORKSPACE  # ld ignored
+
+
+# ---- row-split forward --------------------------------------------------------------
+def test_select_split():
+    """Rows are split only when few and heavy: up to 8 rows that move >= 256
+    KiB (fused, 8 * hidden bytes) or 192 KiB (4 * hidden) each, 9 to 32 rows
+    that move >= 384 KiB, or up to 64 rows that no one-workgroup-per-row
+    kernel holds (LayerNorm above 49152).  Chunks aim at ~64 KiB of traffic
+    (8192 columns fused, 16384 RMSNorm, 12288 LayerNorm), at most
+    max(4, 64 / rows) a row; hidden must be a multiple of 8."""
+    sel = lambda op, rows, h, cu=256: rn.select_split(op, rows, h, cu_count=cu)
+    F, R, L = "fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"
+    assert sel(F, 1, 65536) == (8, 4)       # 8 chunks of 8192 columns
+    assert sel(F, 1, 32768) == (4, 4)
+    assert sel(F, 1, 24576) == (1, 0)       # 192 KiB a row: a tie for the fused op
+    assert sel(F, 1, 40960) == (5, 4)
+    assert sel(F, 1, 16384) == (1, 0)       # 128 KiB a row: one workgroup is faster
+    assert sel(F, 9, 32768) == (1, 0)       # 9-32 rows need 384 KiB a row
+    assert sel(F, 16, 65536) == (4, 8)      # at most max(4, 64 / rows) chunks
+    assert sel(F, 32, 49152) == (4, 6)
+    assert sel(F, 33, 65536) == (1, 0)
+    assert sel(F, 1, 65528) == (8, 4)       # the last chunk holds 8184 columns
+    assert sel(R, 1, 65536) == (4, 8)       # 4 chunks of 16384 columns
+    assert sel(R, 1, 49152) == (3, 8)
+    assert sel(R, 1, 32768) == (1, 0)       # 128 KiB a row
+    assert sel(R, 16, 65536) == (1, 0)      # 256 KiB < 384 KiB
+    assert sel(L, 1, 49152) == (4, 6)       # 12288 columns a chunk
+    assert sel(L, 9, 49152) == (1, 0)
+    assert sel(L, 9, 57344) == (5, 6)       # no one-workgroup kernel holds it: split
+    assert sel(L, 64, 65536) == (4, 8)      # ... up to 64 rows
+    assert sel(L, 65, 65536) == (1, 0)
+    assert sel(L, 2, 57344, cu=8) == (4, 7)
+    assert sel(F, 1, 65540) == (1, 0)       # not a multiple of 8
+    assert sel(F, 4, 65536, cu=4) == (1, 0)
+    for op in (F, R, L):
+        for rows in (1, 2, 3, 5, 8, 9, 17, 32, 64, 128, 512):
+            for h in (8192, 8200, 12288, 16384, 24576, 30000, 32768, 49152, 57344, 65536):
+                k, v = sel(op, rows, h)
+                if k > 1:
+                    chunk = 256 * v * 8
+                    assert 1 <= v <= 8 and 2 <= k <= 64 and rows * k <= 256
+                    assert (k - 1) * chunk < h <= k * chunk  # no empty chunk
+    with pytest.raises(rn.NormError):
+        rn.select_split("layernorm_bwd", 1, 16384, cu_count=256)
+
+
+def test_split_workspace_bytes():
+    assert rn.split_workspace_bytes(0) == 0
+    assert rn.split_workspace_bytes(-3) == 0
+    assert rn.split_workspace_bytes(1) == 256 + 144 * 8
+    assert rn.split_workspace_bytes(512) == 256 + 512 * 144 * 8
+    assert rn.split_workspace_bytes(10 ** 6) == rn.split_workspace_bytes(512)
+
+
+WS = A + 8 * MB  # a workspace away from every other argument
+
+
+def fused_split(out=A, res=A + MB, x=A + 2 * MB, w=A + 3 * MB, rows=4, hidden=16384, eps=1e-6,
+                ws=WS, ws_bytes=1 << 20, split=2):
+    return rn.lib().norm_fused_add_rmsnorm_split(out, res, x, w, rows, hidden, eps, ws, ws_bytes,
+                                                 split, None)
+
+
+def test_split_validation():
+    """Checks that return before any HIP call (the CU count is the last one)."""
+    assert fused_split(rows=0) == SUCCESS
+    assert fused_split(split=-1) == INVALID
+    assert fused_split(split=65) == INVALID
+    assert fused_split(rows=-1) == INVALID
+    assert fused_split(eps=float("nan")) == INVALID
+    assert fused_split(hidden=70000) == UNSUPPORTED
+    assert fused_split(x=0) == INVALID
+    assert fused_split(res=A + 2 * MB) == INVALID              # residual aliases x
+    assert fused_split(x=A + 2 * MB + 1) == MISALIGNED
+    # explicit k: contiguous 16-byte rows of a multiple-of-8 hidden, <= 512 rows
+    assert fused_split(x=A + 2 * MB + 8) == MISALIGNED
+    assert fused_split(hidden=16380) == INVALID
+    assert fused_split(rows=513) == INVALID
+    assert fused_split(hidden=8192 * 8 + 8, split=2) == UNSUPPORTED
+    assert fused_split(hidden=65536, split=2) == INVALID        # 16 accesses a lane
+    assert fused_split(ws=0) == WORKSPACE
+    assert fused_split(ws_bytes=rn.split_workspace_bytes(4) - 1) == WORKSPACE
+    assert fused_split(ws=WS + 4) == MISALIGNED
+    assert fused_split(ws=A + 2 * MB + 4096) == INVALID         # workspace inside x
+    assert fused_split(ws=A + 3 * MB - 16) == INVALID           # overlaps the weight
+    L = rn.lib()
+    assert L.norm_rmsnorm_fwd_split(A, A + MB, A + 2 * MB, 4, 16384, 1e-6, 0, 0, 3,
+                                    None) == WORKSPACE
+    assert L.norm_rmsnorm_fwd_split(A, A, A + 2 * MB, 4, 16384, 1e-6, WS, 1 << 20, -2,
+                                    None) == INVALID
+    assert L.norm_layernorm_fwd_split(A, A + MB, A + MB + 8, A + 2 * MB, A + 3 * MB,
+                                      A + 3 * MB + 65536, 4, 16384, 1e-5, WS, 1 << 20, 2,
+                                      None) == INVALID  # rstd overlaps mean
+    assert L.norm_layernorm_fwd_split(A, A + MB, A + MB + 65536, A + 2 * MB, A + 3 * MB,
+                                      A + 3 * MB + 65536, 4, 16384, 1e-5, A + MB + 8, 1 << 20,
+                                      2, None) == MISALIGNED
