@@ -35,6 +35,7 @@ SOURCES = [
     "k_layernorm_bwd_dyn.hip",
     "k_rmsnorm_bwd_dyn.hip",
     "k_split.hip",
+    "k_bwd_wide.hip",
 ]
 
 HIPCC_FLAGS = [

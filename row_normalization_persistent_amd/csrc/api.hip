@@ -129,6 +129,10 @@ const std::vector<DynBwdEntry>& dyn_bwd_table(norm_op op) {
     return op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_dyn_table() : rmsnorm_bwd_dyn_table();
 }
 
+// The LDS-staged backward for rows wider than the register-resident run-time
+// kernels hold: 512 lanes, 16-byte accesses, V = ceil(hidden / 4096).
+const WideBwdEntry* find_wide(norm_op op, int64_t hidden, int lanes, int w);
+
 // A compiled forward shape: one row per lane group (ring false) or the
 // persistent ring kernel (ring true, LayerNorm only).
 const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb, bool ring = false) {
@@ -175,6 +179,30 @@ int64_t max_dyn_hidden(const std::vector<Entry>& table, int w) {
     int64_t m = 0;
     for (const Entry& e : table)
         if (e.elems == w) m = std::max<int64_t>(m, (int64_t)e.lanes * e.vecs * w);
+    return m;
+}
+
+const WideBwdEntry* find_wide(norm_op op, int64_t hidden, int lanes, int w) {
+    if (lanes != kWideBwdLanes || w != 8 || hidden % 8 ||
+        hidden <= max_dyn_hidden(dyn_bwd_table(op), 8))
+        return nullptr;
+    const int64_t v = ceil_div(hidden, (int64_t)8 * kWideBwdLanes);
+    const auto& t = op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_wide_table()
+                                                : rmsnorm_bwd_wide_table();
+    for (const WideBwdEntry& e : t)
+        if (e.vecs == v) return &e;
+    return nullptr;
+}
+
+// Widest backward row for accesses of w elements (the wide kernels take over
+// above the run-time kernels' widest row at 16-byte accesses).
+int64_t max_bwd_hidden(norm_op op, int w) {
+    int64_t m = max_dyn_hidden(dyn_bwd_table(op), w);
+    if (w == 8) {
+        const auto& t = op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_wide_table()
+                                                    : rmsnorm_bwd_wide_table();
+        for (const WideBwdEntry& e : t) m = std::max<int64_t>(m, (int64_t)e.vecs * 8 * kWideBwdLanes);
+    }
     return m;
 }
 
@@ -324,6 +352,8 @@ norm_launch_cfg choose_dyn_bwd(norm_op op, int64_t rows, int64_t hidden, int w,
             const int r = dyn_rows_per_block(lanes);
             return norm_launch_cfg{lanes, r, default_bwd_grid(rows, r), w};
         }
+    if (find_wide(op, hidden, kWideBwdLanes, w))
+        return norm_launch_cfg{kWideBwdLanes, 1, default_bwd_grid(rows), w};
     return norm_launch_cfg{0, 0, 0, w};
 }
 
@@ -659,7 +689,7 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
     const bool compiled_ok = hidden_compiled(c.hidden) && contiguous && w_max == 8;
 
     if (!compiled_ok && !(cfg && cfg->vector_elems == 0) &&
-        c.hidden > max_dyn_hidden(dyn_bwd_table(op), cfg ? cfg->vector_elems : w_max))
+        c.hidden > max_bwd_hidden(op, cfg ? cfg->vector_elems : w_max))
         return NORM_ERROR_UNSUPPORTED_HIDDEN;
 
     norm_launch_cfg k;
@@ -687,15 +717,20 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
     }
 
     const BwdEntry* se = nullptr;
-    const DynBwdEntry* de = nullptr;
+    DynBwdLauncher dyn_launch = nullptr;
     size_t ws_need = 0;
     if (k.vector_elems == 0) {
         se = find_bwd(op, c.hidden, k.threads_per_row);
         if (!se) return NORM_ERROR_INVALID_VALUE;
         ws_need = static_ws_bytes(op, c.hidden, any ? k.grid : 0);
     } else {
-        de = find_dyn(dyn_bwd_table(op), c.hidden, k.vector_elems, k.threads_per_row);
-        if (!de) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
+        if (const DynBwdEntry* de =
+                find_dyn(dyn_bwd_table(op), c.hidden, k.vector_elems, k.threads_per_row))
+            dyn_launch = de->launch;
+        else if (const WideBwdEntry* we =
+                     find_wide(op, c.hidden, k.threads_per_row, k.vector_elems))
+            dyn_launch = we->launch;
+        if (!dyn_launch) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
         const int64_t slabs = k.grid;  // one slab per workgroup
         if (!dyn_slabs_fit(op, c.hidden, slabs)) return NORM_ERROR_INVALID_VALUE;
         ws_need = dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
@@ -731,7 +766,7 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
                        c.dres,  c.weight, (float*)c.workspace, c.dweight, c.dbias,
                        c.ld_dx, c.ld_dy,  c.ld_x,    ld_dres, c.rows,
                        (int32_t)c.hidden, k.grid, c.eps};
-    return from_hip(de->launch(a, stream));
+    return from_hip(dyn_launch(a, stream));
 }
 
 // Workspace for (op, rows, hidden): the given shape's, or with cfg == NULL the
@@ -794,7 +829,8 @@ const char* norm_status_string(norm_status status) {
         case NORM_ERROR_INVALID_VALUE: return "NORM_ERROR_INVALID_VALUE: invalid argument";
         case NORM_ERROR_UNSUPPORTED_HIDDEN:
             return "NORM_ERROR_UNSUPPORTED_HIDDEN: no kernel holds a row of this hidden size "
-                   "(forward: up to 65536, backward: up to 16384, less for narrow accesses)";
+                   "(forward: up to 65536, LayerNorm 49152; backward: up to 32768 with 16-byte "
+                   "accesses, 16384 with 8-byte, less for narrower ones)";
         case NORM_ERROR_MISALIGNED:
             return "NORM_ERROR_MISALIGNED: bf16 pointers need 2-byte (compiled shapes: 16-byte) "
                    "alignment, fp32 pointers 4-byte, the workspace 16-byte";
@@ -1042,7 +1078,12 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     const int w = dyn ? c.vector_elems : 8;
     int vecs = (int)(hidden / (w * c.threads_per_row));
     int depth = 0;
-    if (dyn && is_bwd(op)) {
+    const WideBwdEntry* wide = dyn && is_bwd(op) ? find_wide(op, hidden, c.threads_per_row, w)
+                                                  : nullptr;
+    if (wide) {
+        vecs = wide->vecs;
+        depth = 1;
+    } else if (dyn && is_bwd(op)) {
         const DynBwdEntry* e = find_dyn(dyn_bwd_table(op), hidden, w, c.threads_per_row);
         vecs = e->vecs;
         depth = e->depth;
@@ -1059,7 +1100,10 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         const int64_t slabs = c.grid;
         const int64_t padded = dyn ? dyn_padded_hidden(hidden) : hidden;
         char kern[96];
-        if (dyn)
+        if (wide)
+            std::snprintf(kern, sizeof kern, "norm_bwd_wide_kernel<%d,%s> (x, dy staged in LDS)",
+                          vecs, op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?");
+        else if (dyn)
             std::snprintf(kern, sizeof kern, "norm_bwd_dyn_rows_kernel<%d,%d,%d,%d,%s>", w,
                           c.threads_per_row, vecs, depth,
                           op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?");
@@ -1145,7 +1189,8 @@ int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int3
         if (lanes > 8 && lanes / 2 >= hidden / w) break;
         const int r = dyn_rows_per_block(lanes);
         if (is_bwd(op)) {
-            if (find_dyn(dyn_bwd_table(op), hidden, w, lanes)) put(norm_launch_cfg{lanes, r, 0, w});
+            if (find_dyn(dyn_bwd_table(op), hidden, w, lanes) || find_wide(op, hidden, lanes, w))
+                put(norm_launch_cfg{lanes, r, 0, w});
             continue;
         }
         for (int k : {1, 2, 4})

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
 #include <vector>
 
 namespace rownorm {
@@ -121,6 +122,18 @@ const std::vector<DynFwdEntry>& rmsnorm_fwd_dyn_table();
 const std::vector<DynFwdEntry>& layernorm_fwd_dyn_table();
 const std::vector<DynBwdEntry>& layernorm_bwd_dyn_table();
 const std::vector<DynBwdEntry>& rmsnorm_bwd_dyn_table();
+
+// ---- backward for rows wider than the registers hold (x staged in LDS) ---------
+// 512 lanes, 16-byte accesses, V accesses a lane: hidden <= 4096 V.
+constexpr int kWideBwdLanes = 512;
+struct WideBwdEntry {
+    int vecs;
+    DynBwdLauncher launch;
+};
+using WideVecsLn = std::integer_sequence<int, 5, 6, 7, 8>;
+using WideVecsRms = std::integer_sequence<int, 5, 6, 7, 8>;
+const std::vector<WideBwdEntry>& layernorm_bwd_wide_table();
+const std::vector<WideBwdEntry>& rmsnorm_bwd_wide_table();
 
 // ---- row-split forward (few rows: one row over k workgroups) ------------------
 // Workspace: kSplitHeaderWords 32-bit words (word 0: error bits), then per

@@ -91,7 +91,7 @@ def test_runtime_hidden_shapes():
     # the widest rows each family holds
     assert rn.select_config("fused_add_rmsnorm", 64, 65536, cu_count=256).threads_per_row == 1024
     for op, h in (("layernorm_fwd", 49152 + 8), ("rmsnorm_fwd", 65536 + 8),
-                  ("layernorm_bwd", 16384 + 8), ("rmsnorm_bwd", 8193)):
+                  ("layernorm_bwd", 32768 + 8), ("rmsnorm_bwd", 8193)):
         with pytest.raises(rn.NormError) as e:
             rn.select_config(op, 64, h, cu_count=256)
         assert e.value.status == UNSUPPORTED
@@ -295,7 +295,7 @@ def test_layernorm_bwd_validation():
     assert lnb() == WORKSPACE
     assert lnb(rows=-2) == INVALID
     assert lnb(eps=float("nan")) == INVALID
-    assert lnb(hidden=16392) == UNSUPPORTED
+    assert lnb(hidden=32776) == UNSUPPORTED
     assert lnb(hidden=5000) == WORKSPACE  # run-time kernels (workspace sized for 4096)
     assert lnb(dw=0) == INVALID
     assert lnb(ws=0) == INVALID
@@ -343,7 +343,7 @@ def test_rmsnorm_bwd_validation():
     assert rmsb(rows=-1) == INVALID
     assert rmsb(eps=-1.0) == INVALID
     assert rmsb(eps=float("nan")) == INVALID
-    assert rmsb(hidden=16392) == UNSUPPORTED
+    assert rmsb(hidden=32776) == UNSUPPORTED
     assert rmsb(hidden=8193) == UNSUPPORTED  # odd rows: 2-byte accesses, at most 8192
     assert rmsb(hidden=4095) == WORKSPACE
     assert rmsb(dw=0) == INVALID
@@ -500,3 +500,27 @@ def test_split_validation():
     assert L.norm_layernorm_fwd_split(A, A + MB, A + MB + 65536, A + 2 * MB, A + 3 * MB,
                                       A + 3 * MB + 65536, 4, 16384, 1e-5, A + MB + 8, 1 << 20,
                                       2, None) == MISALIGNED
+
+
+def test_wide_backward_host_logic():
+    """Backward rows above 16384 run on 512-lane workgroups with the row
+    staged in LDS (5 to 8 16-byte accesses a lane, up to 32768); narrower
+    accesses stop at the register-resident kernels' widest rows."""
+    for op in ("layernorm_bwd", "rmsnorm_bwd", "fused_add_rmsnorm_bwd"):
+        for h in (16392, 20000, 24576, 32768):
+            c = rn.select_config(op, 8192, h)
+            assert (c.threads_per_row, c.rows_per_block, c.grid, c.vector_elems) == \
+                (512, 1, 256, 8), (op, h, c)
+            v = -(-h // 4096)
+            assert f"norm_bwd_wide_kernel<{v}," in rn.describe_config(op, 8192, h)
+            assert rn.list_configs(op, h) == [rn.Cfg(512, 1, 0, 8)]
+            outs = 2 if op == "layernorm_bwd" else 1
+            padded = -(-h // 64) * 64
+            assert rn.workspace_bytes(8192, h, op=op) == 256 * outs * padded * 4
+            assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4
+        with pytest.raises(rn.NormError):
+            rn.select_config(op, 8192, 32776)   # 9 accesses a lane
+        with pytest.raises(rn.NormError):
+            rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels
+        assert rn.select_config(op, 8192, 16384 - 8).threads_per_row != 512 or \
+            rn.select_config(op, 8192, 16384 - 8).rows_per_block == 1

@@ -313,6 +313,37 @@ def test_bwd_widest_rows():
             check_bwd(op, bwd_inputs(op, 40, h, seed=6))
 
 
+@pytest.mark.parametrize("h", [16392, 20000, 24576, 32768])
+def test_bwd_wide_rows_staged_in_lds(h):
+    """Rows wider than the register-resident backward holds (16392 ... 32768):
+    512-lane workgroups with x and dy staged in LDS, 5 to 8 accesses a lane;
+    one row, a ragged 37 and 300 rows over the 256-workgroup grid."""
+    for op in BWD_OPS:
+        c = rn.select_config(op, 300, h)
+        assert (c.threads_per_row, c.rows_per_block, c.vector_elems) == (512, 1, 8), (op, c)
+        assert "norm_bwd_wide_kernel" in rn.describe_config(op, 300, h)
+        for rows in (1, 37, 300):
+            check_bwd(op, bwd_inputs(op, rows, h, seed=h + rows))
+        if op == "fused_add_rmsnorm_bwd":
+            check_bwd(op, dict(bwd_inputs(op, 37, h, seed=3), dres=None), what="no dres")
+
+
+def test_bwd_wide_grids_strides_alias_and_determinism():
+    h = 20000
+    for op in BWD_OPS:
+        inp = bwd_inputs(op, 75, h, seed=12)
+        for grid in (1, 7, 0):
+            check_bwd(op, inp, cfg=rn.Cfg(512, 1, grid, 8), what=f"grid {grid}")
+        first = check_bwd(op, inp)
+        again = check_bwd(op, inp)
+        for x, y in zip(first, again):
+            assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+        # rows of a wider matrix (ld = 2h + 8), and dx written over dy
+        check_bwd(op, bwd_inputs(op, 40, h, seed=13), layout=(2, 8), what="strided")
+        check_bwd(op, bwd_inputs(op, 40, h, seed=14), layout=(2, 8), alias=True,
+                  what="dx==dy strided")
+
+
 def test_bwd_runtime_deterministic():
     for op in BWD_OPS:
         inp = bwd_inputs(op, 2000, 5120, seed=10)
