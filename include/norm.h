@@ -17,7 +17,11 @@
  *     widest access (16, 8, 4 or 2 bytes) that hidden, every row stride and
  *     every bf16 pointer allow.  Largest hidden: forward 65536 (LayerNorm
  *     49152) with 16-byte accesses, 8192 * (access elements) otherwise;
- *     backward 16384 with 16- or 8-byte accesses, 8192 otherwise.
+ *     backward 32768 with 16-byte accesses (above 16384 the row is staged
+ *     in LDS: "TMA inner persistent scheduler", description summary, the
+ *     shared-memory persistent buffer), 16384 with 8-byte accesses, 8192
+ *     otherwise.  The row-split forward entry points below take LayerNorm
+ *     rows up to 65536 too.
  * The library picks the family; the arithmetic and results (within rounding)
  * are the same.
  *
