@@ -29,7 +29,8 @@ Also reported, on the same line:
                 the run-time-hidden kernels: fused add + RMSNorm at hidden
                 5120 and at 4096 (forced, against the compiled kernel), an
                 in-place RMSNorm over 128-wide column slices (row stride
-                384), LayerNorm and RMSNorm backward at hidden 5120; then
+                384), LayerNorm and RMSNorm backward at hidden 5120 and at
+                32768 (rows staged in LDS); then
                 few wide rows through the row-split forward (one row over
                 several workgroups) beside one workgroup per row
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
@@ -563,38 +564,38 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                        note=f"in place on a column slice with row stride {ld}",
                        cpu=oracle_beside("rmsnorm_fwd", i, rows, h, nb, cpu_seconds)))
     del bases, base0
-    # backward at hidden 5120
-    rows, h = 8192, 5120
-    i = wl.layernorm_bwd_inputs(rows, h, seed=0)
-    n = _n_sets(3 * rows * h * 2)
-    x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
-    w = wl.to_device_bf16(i["w"], dev)
-    zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
-    _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
-    xs = [x0] + [x0.clone() for _ in range(n - 1)]
-    dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
-    dxs = [torch.empty_like(x0) for _ in range(n)]
-    dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
-    ws = torch.empty(rn.workspace_bytes(rows, h), dtype=torch.uint8, device=dev)
-    t = graph_time_per_launch(torch, stream, [
-        (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
-                                      dweight=dw, dbias=db, workspace=ws, stream=stream))
-        for j in range(n)], reps)
-    nb = (6 * h + 8) * rows + 10 * h
-    out.append(_op_rec("layernorm_bwd", rows, h, nb, t,
-                       note="run-time-hidden rows kernel + column reduce",
-                       cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
-    t = graph_time_per_launch(torch, stream, [
-        (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
-                                    workspace=ws, stream=stream))
-        for j in range(n)], reps)
-    nb = 6 * h * rows + 6 * h
-    out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t,
-                       note="run-time-hidden rows kernel + column reduce",
-                       cpu=oracle_beside("rmsnorm_bwd", dict(i, eps=wl.EPS_RMS), rows, h, nb,
-                                         cpu_seconds)))
-    del xs, dys, dxs, x0, dy0
-    torch.cuda.synchronize()
+    # backward at hidden 5120 (register-resident run-time kernels) and 32768
+    # (rows staged in LDS)
+    for rows, h, kind in ((8192, 5120, "run-time-hidden rows kernel"),
+                          (4096, 32768, "LDS-staged wide-row kernel")):
+        i = wl.layernorm_bwd_inputs(rows, h, seed=0)
+        n = _n_sets(3 * rows * h * 2)
+        x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
+        w = wl.to_device_bf16(i["w"], dev)
+        zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+        _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
+        dxs = [torch.empty_like(x0) for _ in range(n)]
+        dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
+        ws = torch.empty(rn.workspace_bytes(rows, h), dtype=torch.uint8, device=dev)
+        t = graph_time_per_launch(torch, stream, [
+            (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
+                                          dweight=dw, dbias=db, workspace=ws, stream=stream))
+            for j in range(n)], reps)
+        nb = (6 * h + 8) * rows + 10 * h
+        out.append(_op_rec("layernorm_bwd", rows, h, nb, t, note=kind + " + column reduce",
+                           cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
+        t = graph_time_per_launch(torch, stream, [
+            (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
+                                        workspace=ws, stream=stream))
+            for j in range(n)], reps)
+        nb = 6 * h * rows + 6 * h
+        out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t, note=kind + " + column reduce",
+                           cpu=oracle_beside("rmsnorm_bwd", dict(i, eps=wl.EPS_RMS), rows, h,
+                                             nb, cpu_seconds)))
+        del xs, dys, dxs, x0, dy0, ws
+        torch.cuda.synchronize()
     return out
 
 
@@ -757,6 +758,8 @@ OTHER_WORKLOADS = [
     ("rmsnorm_fwd", 131072, 128, lambda r, h: 4 * h * r + 2 * h),
     ("layernorm_bwd", 8192, 5120, lambda r, h: (6 * h + 8) * r + 2 * h),
     ("rmsnorm_bwd", 8192, 5120, lambda r, h: 6 * h * r + 2 * h),
+    ("layernorm_bwd", 4096, 32768, lambda r, h: (6 * h + 8) * r + 2 * h),
+    ("rmsnorm_bwd", 4096, 32768, lambda r, h: 6 * h * r + 2 * h),
 ]
 
 
