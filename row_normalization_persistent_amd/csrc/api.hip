@@ -256,7 +256,78 @@ norm_launch_cfg choose_ln_ring(int64_t rows, int64_t hidden) {
     return norm_launch_cfg{lanes, 1, (int32_t)std::min<int64_t>(grid, rows), 0};
 }
 
+// Launch shapes measured faster than the rules below on one MI355X (256 CUs):
+// every compiled and run-time shape of each (op, compiled hidden) at 1, 16, 64,
+// 256, 1024, 2048, 4096 and 8192 rows, back-to-back launches from a graph over
+// cold buffer sets, kept where the best shape beat the rules' choice by >= 4 %
+// and >= 0.1 us, then timed again against the rules' shape, interleaved (the
+// figures below; kept where >= 3 % faster), and at row counts between the
+// measured ones (entries that lost there were dropped or narrowed: shapes that
+// win at 1024-4096 rows only by giving exactly one workgroup per CU lose 6-19 %
+// at 600, 1200 or 3000 rows, since their gain comes from a whole number of
+// workgroup waves).  An entry measured at R < 1024 rows covers the rows between
+// the geometric midpoints of its neighbours, one measured at R >= 1024 the rows
+// from the midpoint below up to R; counted on a 256-CU part (rows * 256 / CUs).
+// A run-time shape (vector_elems 8) here runs the run-time kernel on rows the
+// compiled kernels also hold.
+#ifndef ROWNORM_NO_TUNED_TABLE
+#define ROWNORM_NO_TUNED_TABLE 0  // build-time switch: 1 = the rules alone
+#endif
+struct TunedFwd {
+    norm_op op;
+    int32_t hidden;
+    int64_t rows_lo, rows_hi;  // [lo, hi) rows on a 256-CU part
+    norm_launch_cfg cfg;
+};
+constexpr TunedFwd kTunedFwd[] = {
+    {NORM_OP_RMSNORM_FWD, 1024, 128, 512, {64, 1, 0, 0}},  // 256 rows: 2.50 -> 1.97 us (21 %)
+    {NORM_OP_RMSNORM_FWD, 2048, 128, 512, {256, 1, 0, 8}},  // 256 rows: 2.62 -> 2.27 us (13 %)
+    {NORM_OP_RMSNORM_FWD, 2048, 1449, 2049, {256, 1, 0, 8}},  // 2048 rows: 4.64 -> 3.88 us (16 %)
+    {NORM_OP_RMSNORM_FWD, 4096, 32, 128, {256, 1, 0, 0}},  // 64 rows: 2.59 -> 2.24 us (14 %)
+    {NORM_OP_RMSNORM_FWD, 8192, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.07 -> 2.54 us (17 %)
+    {NORM_OP_RMSNORM_FWD, 12288, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.08 -> 2.79 us (9 %)
+    {NORM_OP_RMSNORM_FWD, 12288, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 11.07 -> 9.61 us (13 %)
+    {NORM_OP_RMSNORM_FWD, 16384, 16, 32, {256, 1, 0, 0}},  // 16 rows: 3.21 -> 3.05 us (5 %)
+    {NORM_OP_RMSNORM_FWD, 16384, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.46 -> 3.28 us (5 %)
+    {NORM_OP_RMSNORM_FWD, 16384, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 14.08 -> 12.32 us (12 %)
+    {NORM_OP_LAYERNORM_FWD, 1024, 4, 32, {64, 4, 0, 0}},  // 16 rows: 2.52 -> 2.29 us (9 %)
+    {NORM_OP_LAYERNORM_FWD, 1024, 32, 128, {64, 4, 0, 0}},  // 64 rows: 2.56 -> 2.32 us (9 %)
+    {NORM_OP_LAYERNORM_FWD, 1024, 128, 512, {64, 1, 0, 0}},  // 256 rows: 2.97 -> 2.28 us (23 %)
+    {NORM_OP_LAYERNORM_FWD, 1024, 2897, 4097, {64, 1, 0, 0}},  // 4096 rows: 4.97 -> 4.26 us (14 %)
+    {NORM_OP_LAYERNORM_FWD, 2048, 128, 512, {64, 1, 0, 0}},  // 256 rows: 3.09 -> 2.58 us (17 %)
+    {NORM_OP_LAYERNORM_FWD, 2048, 1449, 2049, {64, 1, 0, 0}},  // 2048 rows: 4.81 -> 4.25 us (12 %)
+    {NORM_OP_LAYERNORM_FWD, 2048, 5793, 8193, {128, 1, 0, 0}},  // 8192 rows: 13.81 -> 13.38 us (3 %)
+    {NORM_OP_LAYERNORM_FWD, 4096, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.09 -> 2.64 us (15 %)
+    {NORM_OP_LAYERNORM_FWD, 8192, 1, 4, {512, 1, 0, 0}},  // 1 rows: 2.76 -> 2.64 us (4 %)
+    {NORM_OP_LAYERNORM_FWD, 8192, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.88 -> 3.03 us (22 %)
+    {NORM_OP_LAYERNORM_FWD, 12288, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.70 -> 3.44 us (7 %)
+    {NORM_OP_LAYERNORM_FWD, 12288, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 11.68 -> 11.19 us (4 %)
+    {NORM_OP_LAYERNORM_FWD, 12288, 5793, 8193, {512, 1, 256, 0}},  // 8192 rows: 71.65 -> 68.60 us (4 %)
+    {NORM_OP_LAYERNORM_FWD, 16384, 4, 32, {512, 1, 0, 0}},  // 16 rows: 4.13 -> 3.83 us (7 %)
+    {NORM_OP_LAYERNORM_FWD, 16384, 32, 128, {512, 1, 0, 0}},  // 64 rows: 4.31 -> 4.06 us (6 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 1024, 128, 512, {64, 1, 0, 0}},  // 256 rows: 2.58 -> 2.19 us (15 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 2048, 32, 128, {256, 1, 0, 8}},  // 64 rows: 2.47 -> 2.25 us (9 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 2048, 128, 512, {256, 1, 0, 8}},  // 256 rows: 2.88 -> 2.57 us (11 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 2048, 512, 1025, {64, 4, 0, 8}},  // 1024 rows: 4.15 -> 3.84 us (7 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 2048, 1449, 2049, {64, 1, 0, 0}},  // 2048 rows: 6.84 -> 6.38 us (7 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 4096, 32, 128, {512, 1, 0, 8}},  // 64 rows: 2.71 -> 2.50 us (8 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 8192, 16, 32, {256, 1, 0, 0}},  // 16 rows: 3.17 -> 2.93 us (8 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 8192, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.38 -> 3.16 us (7 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 8192, 512, 1025, {64, 1, 0, 0}},  // 1024 rows: 12.23 -> 11.25 us (8 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 8192, 1449, 2049, {512, 2, 0, 0}},  // 2048 rows: 24.76 -> 23.38 us (6 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 12288, 1, 4, {512, 1, 0, 8}},  // 1 rows: 3.20 -> 3.09 us (3 %)
+};
+
+norm_launch_cfg tuned_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
+    if (ROWNORM_NO_TUNED_TABLE || cu <= 0) return norm_launch_cfg{0, 0, 0, 0};
+    const int64_t r = std::max<int64_t>(1, rows * 256 / cu);
+    for (const TunedFwd& t : kTunedFwd)
+        if (t.op == op && t.hidden == hidden && r >= t.rows_lo && r < t.rows_hi) return t.cfg;
+    return norm_launch_cfg{0, 0, 0, 0};
+}
+
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
+    if (const norm_launch_cfg t = tuned_fwd(op, rows, hidden, cu); t.threads_per_row) return t;
     if (op == NORM_OP_LAYERNORM_FWD) {
         const norm_launch_cfg ring = choose_ln_ring(rows, hidden);
         if (ring.threads_per_row) return ring;

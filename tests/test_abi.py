@@ -135,9 +135,11 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
                           for k in rn.list_configs(op, h)]
                 assert (c.threads_per_row, c.rows_per_block, c.grid > 0) in listed, \
                     (op, h, rows, c)
-                assert h // (8 * c.threads_per_row) <= 8  # at most 8 vectors per lane
+                # at most 8 vectors per lane by the rules, 16 (the compiled cap)
+                # for shapes from the measured table
+                assert h // (8 * c.threads_per_row) <= 16
     # LayerNorm forward: the persistent ring kernel from 512 rows at hidden >= 8192
-    for h, rows in ((16384, 2048), (12288, 512), (8192, 8192), (4096, 8192)):
+    for h, rows in ((16384, 2048), (12288, 2048), (8192, 8192), (4096, 8192)):
         c = rn.select_config("layernorm_fwd", rows, h, cu_count=256)
         assert c.grid > 0 and c.rows_per_block == 1, (h, rows, c)
         assert (c.threads_per_row, 1) in [(k.threads_per_row, k.rows_per_block)
@@ -524,3 +526,29 @@ def test_wide_backward_host_logic():
             rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels
         assert rn.select_config(op, 8192, 16384 - 8).threads_per_row != 512 or \
             rn.select_config(op, 8192, 16384 - 8).rows_per_block == 1
+
+
+def test_tuned_forward_table():
+    """Measured launch shapes override the rules for some (op, compiled
+    hidden, rows) cells, counted on a 256-CU part: entries measured at >= 1024
+    rows stop at their row count (their gain needs whole workgroup waves)."""
+    sel = lambda op, rows, h, cu=256: rn.select_config(op, rows, h, cu_count=cu)
+    assert sel("rmsnorm_fwd", 1024, 16384) == rn.Cfg(128, 4, 0, 0)
+    assert sel("rmsnorm_fwd", 600, 16384) == rn.Cfg(128, 4, 0, 0)
+    assert sel("rmsnorm_fwd", 1025, 16384) != rn.Cfg(128, 4, 0, 0)   # 257 workgroups
+    assert sel("rmsnorm_fwd", 512, 16384, cu=128) == rn.Cfg(128, 4, 0, 0)  # = 1024 on 256 CUs
+    assert sel("fused_add_rmsnorm", 64, 4096) == rn.Cfg(512, 1, 0, 8)  # the run-time kernel
+    assert sel("fused_add_rmsnorm", 8192, 4096) == rn.Cfg(128, 2, 0, 0)  # the rules
+    assert sel("layernorm_fwd", 64, 8192) == rn.Cfg(256, 1, 0, 0)
+    assert sel("layernorm_fwd", 8192, 12288) == rn.Cfg(512, 1, 256, 0)  # a ring shape
+    assert sel("layernorm_fwd", 9000, 12288) == rn.Cfg(256, 1, 256, 0)
+    # every table choice runs: a listed shape of its (op, hidden)
+    for op in ("fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"):
+        for h in rn.HIDDEN_SIZES:
+            listed = rn.list_configs(op, h)
+            for rows in (1, 3, 16, 40, 64, 100, 256, 300, 700, 1024, 1500, 2048, 3000, 4096,
+                         6000, 8192):
+                c = sel(op, rows, h)
+                assert rn.Cfg(c.threads_per_row, c.rows_per_block, 0, c.vector_elems) in \
+                    [rn.Cfg(k.threads_per_row, k.rows_per_block, 0, k.vector_elems)
+                     for k in listed], (op, h, rows, c)
