@@ -709,6 +709,10 @@ PROFILE_COMMANDS = [
     "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $DIR/write -o bench -- "
     "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc MeanOccupancyPerCU --output-format csv -d $DIR/occ -o bench -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc LdsBankConflict --output-format csv -d $DIR/lds -o bench -- "
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
     "python3 bench.py --summarize-profiles $DIR",
 ]
 CALIBRATION_BYTES = 1 << 30  # the 1 GiB device copy of the copy_ceiling pass
@@ -891,6 +895,43 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
     json.dump({"kernel_source_sha256": kernel_source_digest(),
                "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels},
               open(os.path.join(out_dir, "traffic.json"), "w"), indent=1)
+
+    # -- occupancy and LDS bank conflicts (rocprofv3 derived counters), when collected
+    if os.path.isdir(os.path.join(d, "occ")) and os.path.isdir(os.path.join(d, "lds")):
+        res = {}  # kernel -> (VGPRs per lane, LDS bytes per workgroup, workgroup size)
+
+        def derived(sub, name):
+            out = collections.defaultdict(list)
+            for r in csv.DictReader(open(os.path.join(d, sub, "bench_counter_collection.csv"))):
+                if r["Counter_Name"] == name:
+                    k = _short(r["Kernel_Name"])
+                    out[k].append(float(r["Counter_Value"]))
+                    res[k] = (r["VGPR_Count"], r["LDS_Block_Size"], r["Workgroup_Size"])
+            return out
+        occ = derived("occ", "MeanOccupancyPerCU")
+        lds = derived("lds", "LdsBankConflict")
+        lines = ["# Occupancy and LDS bank conflicts per kernel", "",
+                 "Produced on one MI355X (gfx950, 256 CUs) by:", "", cmds, "",
+                 "`MeanOccupancyPerCU` is rocprofv3's derived counter: resident waves summed "
+                 "over the dispatch's busy cycles, divided by those cycles and by the CU count "
+                 "(a CU holds at most 32 waves here: 8 per SIMD).  `LdsBankConflict` is "
+                 "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT): cycles lost "
+                 "to bank conflicts per conflict-free LDS cycle (0 = none).  Averages over each "
+                 "kernel's dispatches in the profiled command; short launches are dominated by "
+                 "their ramp, so their occupancy reads low.", "",
+                 "| kernel | workgroup | VGPR_Count (as rocprofv3 reports it) | LDS bytes | "
+                 "dispatches | mean waves per CU | "
+                 "LDS conflict cycles per LDS cycle |", "|---|---:|---:|---:|---:|---:|---:|"]
+        for k in sorted(set(occ) | set(lds)):
+            if not k.startswith(("fused_add", "rmsnorm", "layernorm", "norm_", "split_")):
+                continue
+            o = f"{np.mean(occ[k]):.2f}" if occ.get(k) else "-"
+            c = f"{np.mean(lds[k]):.4f}" if lds.get(k) else "-"
+            wg, vg, lb = res[k][2], res[k][0], res[k][1]
+            lines.append(f"| `{k}` | {wg} | {vg} | {lb} | "
+                         f"{max(len(occ.get(k, [])), len(lds.get(k, [])))} | {o} | {c} |")
+        open(os.path.join(out_dir, "fused_add_rmsnorm_h4096_sweep_occupancy_lds.md"), "w").write(
+            "\n".join(lines) + "\n")
     print(f"wrote summaries to {out_dir}")
 
 
