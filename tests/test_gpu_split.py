@@ -143,6 +143,29 @@ def test_split_not_chosen_runs_usual_kernels():
             check(op, inp, run(op, inp, None, 0), f"{op} {rows}x{h} no workspace")
 
 
+def test_split_in_place():
+    """out == x (and y == x): each workgroup reads its chunk before any
+    workgroup writes, and the chunks are disjoint, so in-place calls work."""
+    rows, h = 3, 65536
+    for op in ("fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"):
+        assert rn.select_split(op, rows, h)[0] > 1
+        inp = inputs(op, rows, h, seed=21)
+        x, w = dev(inp["x"]), dev(inp["w"])
+        ws = workspace(rows)
+        if op == "fused_add_rmsnorm":
+            r = dev(inp["r"])
+            rn.fused_add_rmsnorm(x, r, w, inp["eps"], out=x, workspace=ws)
+            got = {"out": host(x), "res": host(r)}
+        elif op == "rmsnorm_fwd":
+            rn.rmsnorm_fwd(x, w, inp["eps"], out=x, workspace=ws)
+            got = {"out": host(x)}
+        else:
+            _, mean, rstd = rn.layernorm_fwd(x, w, dev(inp["b"]), inp["eps"], y=x, workspace=ws)
+            got = {"out": host(x), "mean": mean.cpu().numpy(), "rstd": rstd.cpu().numpy()}
+        check(op, inp, got, f"{op} in place")
+        assert int(torch.count_nonzero(ws)) == 0
+
+
 def test_split_stats_optional():
     rows, h = 2, 57344
     assert rn.select_split("layernorm_fwd", rows, h)[0] > 1
