@@ -15,6 +15,10 @@ Operations (names as in the C ABI):
   * ``rmsnorm_bwd``        -- dx (bf16), dweight (fp32) from dy, x, w (rstd recomputed)
   * ``fused_add_rmsnorm_bwd`` -- ds = RMSNorm backward of dout at s, plus dres;
                               the gradient of both the x and residual inputs
+
+The three forward ops also take ``workspace=`` (a zero-filled uint8 device
+tensor of ``split_workspace_bytes(rows)``) and ``split=``: the row-split entry
+points, which may spread each of few wide rows over several workgroups.
 """
 from __future__ import annotations
 
