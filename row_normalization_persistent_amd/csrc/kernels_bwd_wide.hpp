@@ -21,9 +21,13 @@
 // write 64 consecutive 16-byte slots, which are exactly the slots those lanes
 // read back, so no barrier is needed) and never occupy registers; the weights
 // stay in registers packed as bf16 (4 per access); dres (fused op) is loaded
-// after the reduction.  One two-value reduction over the 16 waves (LDS, one
-// barrier) per row.  A single wide row keeps 2 V x 8 KiB of loads in flight
-// per workgroup, enough to cover the memory latency without a ring of rows.
+// after the reduction.  One two-value reduction over the 8 waves (LDS, one
+// barrier) per row.  There is room in LDS for one row only, so the walk is
+// pipelined by access instead of by row: in the second pass over row i each
+// lane, once it has read access b of x and dy, issues row i+1's loads into
+// the same two slots, and row i+1 streams in while row i is finished and
+// stored (without this the memory pipe idled through every row's two passes
+// and reduction).
 // At the end each workgroup writes one slab of [G][outs][padded] column sums
 // for the shared column-reduce kernel.
 #pragma once
@@ -37,9 +41,45 @@
 namespace rownorm {
 
 constexpr int kWideLanes = kWideBwdLanes;
-// s_waitcnt operand (gfx9 encoding: vmcnt bits 15:14 and 3:0, expcnt 6:4,
-// lgkmcnt 11:8) waiting for LDS operations only: vmcnt 63, expcnt 7, lgkmcnt 0.
-constexpr int kWaitLdsOnly = 0xC07F;
+// Waits written as volatile asm with a memory clobber, so that the compiler
+// moves no LDS access across them: every counter to zero (the row's
+// buffer-to-LDS loads have landed), and the LDS / scalar counter alone (this
+// wave's LDS reads of a slot are done before a load may overwrite it).
+__device__ __forceinline__ void wait_all_counters() {
+    asm volatile("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// A row's buffer descriptor as four scalar words: base address (48 bits, no
+// stride), size in bytes (0 past the matrix's last row), format word.
+typedef uint32_t desc4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ desc4 row_desc(const void* base, int64_t row, int64_t rows,
+                                          int64_t ld_bytes, int row_bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(static_cast<const char*>(base) + row * ld_bytes);
+    desc4 d;
+    d.x = (uint32_t)p;
+    d.y = (uint32_t)(p >> 32) & 0xffffu;
+    d.z = row < rows ? (uint32_t)row_bytes : 0u;
+    d.w = (uint32_t)kRsrcWord3;
+    return d;
+}
+
+// One 16-byte-per-lane buffer load straight into LDS (non-temporal): lane i
+// of the wave writes bytes [16 i, 16 i + 16) past LDS address `lds` (wave
+// uniform) with the 16 bytes at byte `voff` of the descriptor's range (zeros,
+// from no memory, past its end).  Issued from asm so that the compiler does
+// not track it: it would otherwise make every later LDS read of the wave wait
+// for it, the reads of other slots included.  The caller orders it: LDS reads
+// of the slots before it (wait_lds), and its landing before any read of them
+// (wait_all_counters).
+__device__ __forceinline__ void lds_load16(desc4 d, int voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+        :
+        : "v"(voff), "s"(d), "s"(lds)
+        : "memory", "m0");
+}
 
 // The value of v, opaque to the optimizer (emits no instruction).
 __device__ __forceinline__ int opaque_lane(int v) {
@@ -74,33 +114,47 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
             for (int k = 0; k < 8; ++k) pb[b][k] = 0.0f;
     }
 
+    // access b of lane t of a row: x and dy from HBM into their LDS slots
+    // (slot b*T + t; the wave's 64 lanes write its 64 consecutive slots)
+    // LDS byte addresses of the wave's first slot of access 0, wave uniform
+    const uint32_t wave_slot = (uint32_t)__builtin_amdgcn_readfirstlane(wave_base) * 16u;
+    const uint32_t xs_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)xs + wave_slot;
+    const uint32_t ds_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ds + wave_slot;
+    auto stage = [&](desc4 rx, desc4 rd, int b, int t) {
+        lds_load16(rx, (b * T + t) * 16, xs_lds + b * T * 16);
+        lds_load16(rd, (b * T + t) * 16, ds_lds + b * T * 16);
+    };
+    auto x_rsrc = [&](int64_t row) { return row_desc(a.x, row, a.rows, a.ld_x * 2, h * 2); };
+    auto dy_rsrc = [&](int64_t row) { return row_desc(a.dy, row, a.rows, a.ld_dy * 2, h * 2); };
+
     const int64_t G = gridDim.x;
     const int64_t first = blockIdx.x;
     const int64_t n = first < a.rows ? (a.rows - 1 - first) / G + 1 : 0;
+    // The walk is software-pipelined by access: the second pass over a row
+    // hands each access's LDS slots, once read, to the next row's loads, so
+    // the next row streams in while this one is finished and stored.
+    float mean_nx = 0.0f, rstd_nx = 0.0f;
+    if (n > 0) {
+        const desc4 rx = x_rsrc(first), rd = dy_rsrc(first);
+#pragma unroll
+        for (int b = 0; b < V; ++b) stage(rx, rd, b, lane);
+        if constexpr (LN) {
+            mean_nx = rload_f32(row_rsrc_ld(a.mean, first, a.rows, 4, 4), 0);
+            rstd_nx = rload_f32(row_rsrc_ld(a.rstd, first, a.rows, 4, 4), 0);
+        }
+    }
     int parity = 0;
     for (int64_t i = 0; i < n; ++i) {
         const int64_t row = opaque_row(first + i * G);
+        const int64_t next = row + G;  // past the end (size-0 descriptors) after the last
+        const float mean = mean_nx, rstd_in = rstd_nx;
+        // the row's loads (its LDS writes included); no LDS read may move above
+        wait_all_counters();
         // lane offsets recomputed every row (an opaque lane index), not hoisted
         // out of the loop into registers held for the whole walk
         const int l = opaque_lane(lane);
-        const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, h * 2);
-        const rsrc_t rd = row_rsrc_ld(a.dy, row, a.rows, a.ld_dy * 2, h * 2);
-        // x, dy -> LDS (lane t's slot b is [b*T + t]; the wave writes its 64 slots)
-#pragma unroll
-        for (int b = 0; b < V; ++b) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)&xs[b * T + wave_base], 16,
-                (b * T + l) * 16, 0, 0, kCachePolicyNT);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rd, (__attribute__((address_space(3))) void*)&ds[b * T + wave_base], 16,
-                (b * T + l) * 16, 0, 0, kCachePolicyNT);
-        }
-        float mean = 0.0f, rstd_in = 0.0f;
-        if constexpr (LN) {
-            mean = rload_f32(row_rsrc_ld(a.mean, row, a.rows, 4, 4), 0);
-            rstd_in = rload_f32(row_rsrc_ld(a.rstd, row, a.rows, 4, 4), 0);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // the row's loads, the LDS writes included
 
         // the row's two sums (an access past the row's end, in the last b, is
         // left out whatever its LDS slot holds; hidden is a multiple of 8, so
@@ -133,63 +187,64 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         }
         row_sum2<T>(s1, s2, red + parity * (2 * (T / kWave)), lane);
         parity ^= 1;
-        // the second pass re-reads x, dy (LDS) and the weights (cache) instead
-        // of keeping the first pass's values live across the reduction: an
-        // opaque copy of the lane index keeps the compiler from merging them
+        if constexpr (LN) {  // past the walk's last row: zeros, never used
+            mean_nx = rload_f32(row_rsrc_ld(a.mean, next, a.rows, 4, 4), 0);
+            rstd_nx = rload_f32(row_rsrc_ld(a.rstd, next, a.rows, 4, 4), 0);
+        }
+        // the second pass re-reads x, dy (LDS) and the weights (registers)
+        // instead of keeping the first pass's values live across the
+        // reduction: an opaque copy of the lane index keeps the compiler from
+        // merging them
         const int t = opaque_lane(lane);
+        const desc4 nrx = x_rsrc(next), nrd = dy_rsrc(next);
 
         const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, h * 2);
         rsrc_t rr = rdx;
         if constexpr (DRES) rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * 2, h * 2);
+        float c1 = 0.0f, c2 = 0.0f, rstd = 0.0f, coef = 0.0f;
         if constexpr (LN) {
-            const float c1 = s1 * inv_h, c2 = s2 * inv_h;
+            c1 = s1 * inv_h;
+            c2 = s2 * inv_h;
+        } else {
+            // a row past the end must add exactly nothing, also at eps = 0
+            rstd = row < a.rows ? fast_rsqrt(s1 * inv_h + a.eps) : 0.0f;
+            coef = rstd * rstd * rstd * s2 * inv_h;
+        }
+        u32x4 dr[DRES ? V : 1];
+        if constexpr (DRES) {
 #pragma unroll
-            for (int b = 0; b < V; ++b) {
-                float xf[8], df[8], wf[8], o[8];
-                unpack8(xs[b * T + t], xf);
-                unpack8(ds[b * T + t], df);
-                unpack8(wv[b], wf);
+            for (int b = 0; b < V; ++b) dr[b] = aload<8, kCachePolicyNT>(rr, (b * T + lane) * 16);
+        }
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
+        for (int b = 0; b < V; ++b) {
+            float xf[8], df[8], wf[8], o[8];
+            unpack8(xs[b * T + t], xf);
+            unpack8(ds[b * T + t], df);
+            // this access's slots are read: hand them to the next row (past
+            // the walk's last row the descriptors are empty: nothing is read)
+            wait_lds();
+            stage(nrx, nrd, b, t);
+            unpack8(wv[b], wf);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if constexpr (LN) {
                     const float xh = (xf[k] - mean) * rstd_in;
                     o[k] = rstd_in * (df[k] * wf[k] - c1 - xh * c2);
                     pw[b][k] += df[k] * xh;
                     pb[b][k] += df[k];
-                }
-                astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack8(o));
-            }
-        } else {
-            // a row past the end must add exactly nothing, also at eps = 0
-            const float rstd = row < a.rows ? fast_rsqrt(s1 * inv_h + a.eps) : 0.0f;
-            const float coef = rstd * rstd * rstd * s2 * inv_h;
-            u32x4 dr[DRES ? V : 1];
-            if constexpr (DRES) {
-#pragma unroll
-                for (int b = 0; b < V; ++b) dr[b] = aload<8, kCachePolicyNT>(rr, (b * T + lane) * 16);
-            }
-#pragma unroll
-            for (int b = 0; b < V; ++b) {
-                float xf[8], df[8], wf[8], o[8];
-                unpack8(xs[b * T + t], xf);
-                unpack8(ds[b * T + t], df);
-                unpack8(wv[b], wf);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
+                } else {
                     o[k] = rstd * (df[k] * wf[k]) - coef * xf[k];
                     pw[b][k] += df[k] * (xf[k] * rstd);
                 }
-                if constexpr (DRES) {
-                    float rf[8];
-                    unpack8(dr[b], rf);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) o[k] += rf[k];
-                }
-                astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack8(o));
             }
+            if constexpr (DRES) {
+                float rf[8];
+                unpack8(dr[b], rf);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) o[k] += rf[k];
+            }
+            astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack8(o));
         }
-        // the next row's x may land in LDS only after this row's reads of it
-        // are done (the dx stores may still be in flight)
-        __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
     }
 
     const int64_t padded = dyn_padded_hidden(h);
