@@ -183,7 +183,7 @@ def main():
     # kernel is the instantiation with the most GPU time per step
     groups = {}
     for i, c in enumerate(cfgs):
-        key = (c.threads_per_row, c.rows_per_block)
+        key = _fwd_kernel_name("fused_add_rmsnorm", SWEEP_ROWS[i], HIDDEN)
         g = groups.setdefault(key, {"idx": [], "bytes": 0})
         g["idx"].append(i)
         g["bytes"] += fused_bytes(SWEEP_ROWS[i])
@@ -217,7 +217,7 @@ def main():
     dom_key = max(groups, key=lambda k: groups[k]["us_per_step"])
     dom = groups[dom_key]
     achieved = dom["GBps"]
-    kname = f"fused_add_rmsnorm_kernel<{HIDDEN}, {dom_key[0]}, {dom_key[1]}>"
+    kname = dom_key
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": load_traffic(kname, [SWEEP_ROWS[i] for i in dom["idx"]]),
@@ -226,7 +226,7 @@ def main():
                 "algorithmic_bytes_per_launch": round(dom["avg_bytes"]),
                 "avg_launch_us": round(dom["avg_launch_us"], 3)}
     log(f"dominant kernel {kname}: {dom['avg_launch_us']:.2f} us/launch avg, {achieved:.0f} GB/s")
-    kernels = [{"kernel": f"fused_add_rmsnorm_kernel<{HIDDEN}, {k[0]}, {k[1]}>",
+    kernels = [{"kernel": k,
                 "rows": [SWEEP_ROWS[i] for i in g["idx"]],
                 "us_per_step": round(g["us_per_step"], 3),
                 "avg_launch_us": round(g["avg_launch_us"], 3), "GBps": round(g["GBps"], 1)}
@@ -743,14 +743,14 @@ def _tpl(name: str):
 
 def _rows_of(name: str, grid: int):
     """Rows processed by a dispatch of one of our kernels (grid in work-items)."""
-    short = _short(name)
+    short = _short(name).replace("_lw_kernel", "_kernel")
     if short.startswith(("fused_add_rmsnorm_kernel", "rmsnorm_fwd_kernel", "layernorm_fwd_kernel")):
         return grid // _tpl(short)[1]
     return None
 
 
 def _alg_bytes(name: str, rows):
-    short = _short(name)
+    short = _short(name).replace("_lw_kernel", "_kernel")
     if rows is None:
         return None
     h = _tpl(short)[0]
@@ -780,6 +780,14 @@ OTHER_WORKLOADS = [
     ("layernorm_bwd", 4096, 32768, lambda r, h: (6 * h + 8) * r + 2 * h),
     ("rmsnorm_bwd", 4096, 32768, lambda r, h: 6 * h * r + 2 * h),
 ]
+
+
+def _fwd_kernel_name(op, rows, hidden):
+    """The forward kernel instantiation the library launches for (op, rows,
+    hidden) on this device, in rocprofv3's spelling."""
+    import row_normalization_persistent_amd as rn
+    desc = rn.describe_config(op, rows, hidden)
+    return desc.split(": ", 1)[1].split(" (", 1)[0].replace(",", ", ")
 
 
 def _row_kernel_name(op, rows, hidden):

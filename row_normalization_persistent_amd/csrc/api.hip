@@ -326,6 +326,53 @@ norm_launch_cfg tuned_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     return norm_launch_cfg{0, 0, 0, 0};
 }
 
+// Weight-load variant of the one-row-per-lane-group forward kernels
+// (kernels_fwd.hpp: `*_kernel` loads the weight, and bias, with the row;
+// `*_lw_kernel` after the row's statistics).  The early variant is the
+// default; the late one runs for the shapes and row ranges below, where it
+// measured faster (graph-timed, cold buffers, A/B in one process).  Rows are
+// counted on a 256-CU part as in the table above.  Build-time switch for
+// measurement: 1 = early everywhere, 2 = late everywhere.
+#ifndef ROWNORM_FWD_LATE_WEIGHTS
+#define ROWNORM_FWD_LATE_WEIGHTS 0
+#endif
+struct LateFwd {
+    norm_op op;
+    int32_t hidden, lanes, rows_per_block;
+    int64_t rows_lo, rows_hi;  // [lo, hi) rows on a 256-CU part
+};
+constexpr LateFwd kLateFwd[] = {
+    {NORM_OP_LAYERNORM_FWD, 4096, 64, 4, 1449, 2897},       // 2048 rows: 8.22 -> 6.52 us (26 %)
+    {NORM_OP_RMSNORM_FWD, 1024, 64, 4, 2897, 5793},         // 4096 rows: 3.93 -> 3.77 us (4 %)
+    {NORM_OP_RMSNORM_FWD, 2048, 64, 4, 2897, 5793},         // 4096 rows: 7.35 -> 6.25 us (18 %)
+    {NORM_OP_RMSNORM_FWD, 8192, 128, 2, 725, 1449},         // 1024 rows: 6.59 -> 6.35 us (4 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 1024, 64, 4, 1449, 5793},   // 2048 / 4096 rows: 8 % / 9 %
+    {NORM_OP_FUSED_ADD_RMSNORM, 4096, 64, 4, 1449, 2897},   // 2048 rows: 12.11 -> 11.74 us (3 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 8192, 1024, 1, 1, 8},       // 1 / 4 rows: 5 % / 5 %
+    {NORM_OP_FUSED_ADD_RMSNORM, 12288, 256, 1, 363, 725},   // 512 rows: 9.38 -> 8.97 us (5 %)
+    {NORM_OP_FUSED_ADD_RMSNORM, 16384, 1024, 1, 1, 91},     // 1-64 rows: 4-7 %
+    {NORM_OP_FUSED_ADD_RMSNORM, 16384, 256, 1, 363, 725},   // 512 rows: 12.45 -> 11.47 us (9 %)
+};
+
+bool late_listed(norm_op op, int64_t hidden, int lanes, int rpb) {
+    if (ROWNORM_FWD_LATE_WEIGHTS != 0) return ROWNORM_FWD_LATE_WEIGHTS == 2;
+    for (const LateFwd& t : kLateFwd)
+        if (t.op == op && t.hidden == hidden && t.lanes == lanes && t.rows_per_block == rpb)
+            return true;
+    return false;
+}
+
+bool late_weights(norm_op op, int64_t rows, int64_t hidden, int lanes, int rpb, int cu) {
+    if (ROWNORM_FWD_LATE_WEIGHTS != 0) return ROWNORM_FWD_LATE_WEIGHTS == 2;
+    if (cu <= 0) return false;
+    const int64_t r = std::max<int64_t>(1, rows * 256 / cu);
+    for (const LateFwd& t : kLateFwd)
+        if (t.op == op && t.hidden == hidden && t.lanes == lanes && t.rows_per_block == rpb &&
+            r >= t.rows_lo && r < t.rows_hi)
+            return true;
+    return false;
+}
+
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     if (const norm_launch_cfg t = tuned_fwd(op, rows, hidden, cu); t.threads_per_row) return t;
     if (op == NORM_OP_LAYERNORM_FWD) {
@@ -536,6 +583,7 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         return NORM_ERROR_UNSUPPORTED_HIDDEN;
 
     norm_launch_cfg k;
+    int cu = 0;  // queried only where a choice needs it
     if (cfg && cfg->vector_elems == 0) {  // a compiled-hidden shape was asked for
         if (!hidden_compiled(c.hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
         if (!contiguous) return NORM_ERROR_INVALID_VALUE;
@@ -546,7 +594,6 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         if (cfg->vector_elems > wp) return NORM_ERROR_MISALIGNED;
         k = *cfg;
     } else {
-        int cu = 0;
         const norm_status st = current_cu_count(&cu);
         if (st != NORM_SUCCESS) return st;
         k = compiled_ok ? choose_fwd(op, c.rows, c.hidden, cu)
@@ -565,7 +612,16 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
             return NORM_ERROR_INVALID_VALUE;
         const FwdArgs a{c.out, c.residual, c.x,    c.weight, c.bias,
                         c.mean, c.rstd,    c.rows, c.eps,    k.grid};
-        return from_hip(e->launch(a, stream));
+        FwdLauncher launch = e->launch;
+        if (e->launch_late && late_listed(op, c.hidden, k.threads_per_row, k.rows_per_block)) {
+            if (cu == 0) {
+                const norm_status st = current_cu_count(&cu);
+                if (st != NORM_SUCCESS) return st;
+            }
+            if (late_weights(op, c.rows, c.hidden, k.threads_per_row, k.rows_per_block, cu))
+                launch = e->launch_late;
+        }
+        return from_hip(launch(a, stream));
     }
     // rows per workgroup = R lane groups x K rows per group
     const int r = dyn_rows_per_block(k.threads_per_row);
@@ -1209,9 +1265,17 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         else if (ring)
             std::snprintf(inst, sizeof inst, "%s_ring_kernel<%lld,%d,%d>", kern,
                           (long long)hidden, c.threads_per_row, ring->depth);
-        else
-            std::snprintf(inst, sizeof inst, "%s_kernel<%lld,%d,%d>", kern, (long long)hidden,
-                          c.threads_per_row, c.rows_per_block);
+        else {
+            int cu = cu_count;
+            if (cu <= 0 && late_listed(op, hidden, c.threads_per_row, c.rows_per_block) &&
+                current_cu_count(&cu) != NORM_SUCCESS)
+                return -1;
+            const bool late =
+                late_weights(op, rows, hidden, c.threads_per_row, c.rows_per_block, cu);
+            std::snprintf(inst, sizeof inst, "%s%s<%lld,%d,%d>", kern,
+                          late ? "_lw_kernel" : "_kernel", (long long)hidden, c.threads_per_row,
+                          c.rows_per_block);
+        }
         const int block = dyn ? dyn_block_size(c.threads_per_row)
                               : c.threads_per_row * c.rows_per_block;
         if (ring)

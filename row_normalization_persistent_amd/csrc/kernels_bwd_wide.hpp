@@ -72,13 +72,19 @@ __device__ __forceinline__ desc4 row_desc(const void* base, int64_t row, int64_t
 // for it, the reads of other slots included.  The caller orders it: LDS reads
 // of the slots before it (wait_lds), and its landing before any read of them
 // (wait_all_counters).
+// M0 (which the load takes its LDS address from) is saved and restored inside
+// the asm, since the compiler does not allocate M0 and may not expect an asm
+// statement to change it.
 __device__ __forceinline__ void lds_load16(desc4 d, int voff, uint32_t lds) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
-        :
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
         : "v"(voff), "s"(d), "s"(lds)
-        : "memory", "m0");
+        : "memory");
 }
 
 // The value of v, opaque to the optimizer (emits no instruction).

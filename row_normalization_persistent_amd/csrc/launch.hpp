@@ -50,6 +50,7 @@ struct FwdEntry {
     int hidden, lanes, rows_per_block;
     FwdLauncher launch;
     int depth;  // 0: one row per lane group; > 0: persistent ring of that many rows
+    FwdLauncher launch_late;  // the late-weights variant (one row per lane group only)
 };
 
 // Default persistent grid of the forward ring kernels (one workgroup per CU of

@@ -160,6 +160,18 @@ def test_describe_config():
     d = rn.describe_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
     c = rn.select_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
     assert f"fused_add_rmsnorm_kernel<4096,{c.threads_per_row},{c.rows_per_block}>" in d
+    # the late-weights variant where it measured faster, the early one around it
+    assert "layernorm_fwd_lw_kernel<4096,64,4>" in rn.describe_config("layernorm_fwd", 2048,
+                                                                      4096, cu_count=256)
+    assert "layernorm_fwd_kernel<4096,64,4>" in rn.describe_config("layernorm_fwd", 1024, 4096,
+                                                                   cu_count=256)
+    assert "rmsnorm_fwd_lw_kernel<2048,64,4>" in rn.describe_config("rmsnorm_fwd", 4096, 2048,
+                                                                    cu_count=256)
+    # rows are counted on a 256-CU part: half the rows on a 128-CU part
+    assert "rmsnorm_fwd_lw_kernel<2048,64,4>" in rn.describe_config("rmsnorm_fwd", 2048, 2048,
+                                                                    cu_count=128)
+    assert "fused_add_rmsnorm_lw_kernel<4096,64,4>" in rn.describe_config(
+        "fused_add_rmsnorm", 2048, 4096, cu_count=256)
     d = rn.describe_config("layernorm_bwd", 8192, 4096, cu_count=256)
     assert "persistent grid of 256" in d and f"workspace {rn.workspace_bytes(8192, 4096)}" in d
     with pytest.raises(rn.NormError):

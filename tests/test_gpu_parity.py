@@ -66,6 +66,31 @@ def test_fused_in_place_out():
     check_fused(wl.fused_inputs(64, 4096, seed=2), out_is_x=True, what="fused out==x")
 
 
+# (op, rows, hidden) where the library runs the late-weights variant of the
+# forward kernels on a 256-CU part (weight and bias loaded after the row's
+# statistics), with ragged row counts where the bucket allows
+LATE_WEIGHT_CASES = [("layernorm_fwd", 2047, 4096), ("rmsnorm_fwd", 4095, 1024),
+                     ("rmsnorm_fwd", 4093, 2048), ("rmsnorm_fwd", 1023, 8192),
+                     ("fused_add_rmsnorm", 2047, 1024), ("fused_add_rmsnorm", 4095, 1024),
+                     ("fused_add_rmsnorm", 2046, 4096), ("fused_add_rmsnorm", 3, 8192),
+                     ("fused_add_rmsnorm", 501, 12288), ("fused_add_rmsnorm", 1, 16384),
+                     ("fused_add_rmsnorm", 61, 16384), ("fused_add_rmsnorm", 501, 16384)]
+
+
+@pytest.mark.parametrize("op,rows,hidden", LATE_WEIGHT_CASES)
+def test_fwd_late_weight_variant(op, rows, hidden):
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if cu != 256:
+        pytest.skip(f"the late-weights buckets are given for 256 CUs; this part has {cu}")
+    assert "_lw_kernel<" in rn.describe_config(op, rows, hidden), (op, rows, hidden)
+    if op == "layernorm_fwd":
+        check_lnf(wl.layernorm_fwd_inputs(rows, hidden, seed=21), what=f"late {rows}x{hidden}")
+    elif op == "rmsnorm_fwd":
+        check_rms(wl.rmsnorm_inputs(rows, hidden, seed=21), what=f"late {rows}x{hidden}")
+    else:
+        check_fused(wl.fused_inputs(rows, hidden, seed=21), what=f"late {rows}x{hidden}")
+
+
 # ------------------------------------------------------------------ rmsnorm
 def check_rms(inp, cfg=None, what="rmsnorm", in_place=False):
     ref, _ = oracle.rmsnorm_fwd(inp["x"], inp["w"], inp["eps"], NT)
