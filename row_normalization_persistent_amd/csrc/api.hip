@@ -373,6 +373,18 @@ bool late_weights(norm_op op, int64_t rows, int64_t hidden, int lanes, int rpb, 
     return false;
 }
 
+// The run-time-hidden forward kernels (hidden is not a compile-time constant,
+// so no per-hidden table): late weights when the grid is one wave of 2 to 4
+// workgroups per CU that all start together, for rows of at least one wave.
+// Measured (fused, RMSNorm and LayerNorm at hidden 2560 ... 7168, 16 ... 8192
+// rows): late was 3-25 % faster at every such grid, e.g. RMSNorm 2048 x 6144
+// 10.7 -> 8.6 us, LayerNorm 1024 x 7168 7.8 -> 6.3 us; with one workgroup per
+// CU it lost up to 4 %, and from 8 per CU on it was level (+-2 %).
+bool late_weights_dyn(int64_t groups, int lanes, int cu) {
+    if (ROWNORM_FWD_LATE_WEIGHTS != 0) return ROWNORM_FWD_LATE_WEIGHTS == 2;
+    return cu > 0 && lanes >= 64 && groups >= 2 * (int64_t)cu && groups <= 4 * (int64_t)cu;
+}
+
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     if (const norm_launch_cfg t = tuned_fwd(op, rows, hidden, cu); t.threads_per_row) return t;
     if (op == NORM_OP_LAYERNORM_FWD) {
@@ -638,7 +650,12 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
     const DynFwdArgs a{c.out,     c.residual, c.x,   c.weight, c.bias,   c.mean,
                        c.rstd,    c.ld_out,   ld_res, c.ld_x,  c.rows,   (int32_t)c.hidden,
                        c.eps};
-    return from_hip(e->launch(a, stream));
+    if (cu == 0) {
+        const norm_status st = current_cu_count(&cu);
+        if (st != NORM_SUCCESS) return st;
+    }
+    return from_hip((late_weights_dyn(groups, k.threads_per_row, cu) ? e->launch_late
+                                                                      : e->launch)(a, stream));
 }
 
 // ---- row-split forward entry ---------------------------------------------------
@@ -1258,10 +1275,15 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         char inst[96];
         const FwdEntry* ring = c.grid > 0 ? find_fwd(op, hidden, c.threads_per_row, 1, true)
                                           : nullptr;
-        if (dyn)
-            std::snprintf(inst, sizeof inst, "%s_dyn_kernel<%d,%d,%d,%d>", kern, w,
-                          c.threads_per_row, vecs,
+        if (dyn) {
+            int cu = cu_count;
+            if (cu <= 0 && current_cu_count(&cu) != NORM_SUCCESS) return -1;
+            const bool late =
+                late_weights_dyn(ceil_div(rows, c.rows_per_block), c.threads_per_row, cu);
+            std::snprintf(inst, sizeof inst, "%s%s<%d,%d,%d,%d>", kern,
+                          late ? "_dyn_lw_kernel" : "_dyn_kernel", w, c.threads_per_row, vecs,
                           c.rows_per_block / dyn_rows_per_block(c.threads_per_row));
+        }
         else if (ring)
             std::snprintf(inst, sizeof inst, "%s_ring_kernel<%lld,%d,%d>", kern,
                           (long long)hidden, c.threads_per_row, ring->depth);

@@ -21,6 +21,13 @@ namespace rownorm {
 template <int W, int T>
 __device__ __forceinline__ int dyn_off(int b, int lane) { return (b * T + lane) * (2 * W); }
 
+// The lane's V accesses of a per-column parameter (weight or bias).
+template <int W, int T, int V>
+__device__ __forceinline__ void dyn_load_params(raw_t<W> (&v)[V], rsrc_t r, int lane) {
+#pragma unroll
+    for (int b = 0; b < V; ++b) v[b] = aload<W, 0>(r, dyn_off<W, T>(b, lane));
+}
+
 // K rows per lane group (K > 1 only for rows narrower than a wave, which
 // reduce without LDS): the group issues the loads of all K rows before the
 // first reduction.  Rows of workgroup k: k*R*K + j*R + g for j < K
@@ -57,8 +64,11 @@ __device__ __forceinline__ int acc_off(int local, int b, int lane, int64_t ld, i
     return set_off<T>(local, (b * T + lane) * W, ld, hidden, 2);
 }
 
-template <int W, int T, int V, int K>
-__global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(DynFwdArgs a) {
+// LATE: the weight (and bias) loads are issued once the first row's
+// statistics are known instead of right behind the rows' loads (the
+// `*_lw_kernel` variants; kernels_fwd.hpp describes the trade-off).
+template <int W, int T, int V, int K, bool LATE>
+__device__ __forceinline__ void fused_add_rmsnorm_dyn_body(const DynFwdArgs& a) {
     __shared__ float red[dyn_red_floats<T>()];
     const int lane = threadIdx.x % T;
     const int g = uniform_group<T>(threadIdx.x / T);
@@ -78,8 +88,7 @@ __global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(D
             rv[j][b] = aload<W, kCachePolicyNT>(rr, acc_off<W, T>(l, b, lane, a.ld_res, h));
         }
     }
-#pragma unroll
-    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+    if constexpr (!LATE) dyn_load_params<W, T, V>(wv, rw, lane);
     issue_fence();
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -99,6 +108,7 @@ __global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(D
         }
         const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
         const float rstd = fast_rsqrt(ss / (float)h + a.eps);
+        if (LATE && j == 0) dyn_load_params<W, T, V>(wv, rw, lane);
 #pragma unroll
         for (int b = 0; b < V; ++b) {
             float xf[W], rf[W], wf[W], o[W];
@@ -112,8 +122,8 @@ __global__ __launch_bounds__(dyn_block<T>()) void fused_add_rmsnorm_dyn_kernel(D
     }
 }
 
-template <int W, int T, int V, int K>
-__global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdArgs a) {
+template <int W, int T, int V, int K, bool LATE>
+__device__ __forceinline__ void rmsnorm_fwd_dyn_body(const DynFwdArgs& a) {
     __shared__ float red[dyn_red_floats<T>()];
     const int lane = threadIdx.x % T;
     const int g = uniform_group<T>(threadIdx.x / T);
@@ -130,8 +140,7 @@ __global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdA
         for (int b = 0; b < V; ++b)
             xv[j][b] = aload<W, kCachePolicyNT>(rx, acc_off<W, T>(l, b, lane, a.ld_x, h));
     }
-#pragma unroll
-    for (int b = 0; b < V; ++b) wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
+    if constexpr (!LATE) dyn_load_params<W, T, V>(wv, rw, lane);
     issue_fence();
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -146,6 +155,7 @@ __global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdA
         }
         const float ss = dyn_row_sum<T>(acc, red + g * (T / kWave), lane);
         const float rstd = fast_rsqrt(ss / (float)h + a.eps);
+        if (LATE && j == 0) dyn_load_params<W, T, V>(wv, rw, lane);
 #pragma unroll
         for (int b = 0; b < V; ++b) {
             float xf[W], wf[W], o[W];
@@ -158,8 +168,8 @@ __global__ __launch_bounds__(dyn_block<T>()) void rmsnorm_fwd_dyn_kernel(DynFwdA
     }
 }
 
-template <int W, int T, int V, int K>
-__global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFwdArgs a) {
+template <int W, int T, int V, int K, bool LATE>
+__device__ __forceinline__ void layernorm_fwd_dyn_body(const DynFwdArgs& a) {
     constexpr int kRed = dyn_red_floats<T>();
     __shared__ float red[2 * kRed];  // mean and variance use different slots: one barrier each
     const int lane = threadIdx.x % T;
@@ -178,10 +188,9 @@ __global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFw
         for (int b = 0; b < V; ++b)
             xv[j][b] = aload<W, kCachePolicyNT>(rx, acc_off<W, T>(l, b, lane, a.ld_x, h));
     }
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-        wv[b] = aload<W, 0>(rw, dyn_off<W, T>(b, lane));
-        bv[b] = aload<W, 0>(rbias, dyn_off<W, T>(b, lane));
+    if constexpr (!LATE) {
+        dyn_load_params<W, T, V>(wv, rw, lane);
+        dyn_load_params<W, T, V>(bv, rbias, lane);
     }
     issue_fence();
     const float inv_h = 1.0f / (float)h;
@@ -213,6 +222,10 @@ __global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFw
         }
         const float var = dyn_row_sum<T>(acc2, red + kRed + g * (T / kWave), lane) * inv_h;
         const float rstd = fast_rsqrt(var + a.eps);
+        if (LATE && j == 0) {
+            dyn_load_params<W, T, V>(wv, rw, lane);
+            dyn_load_params<W, T, V>(bv, rbias, lane);
+        }
         if (a.mean != nullptr && lane == 0 && row < a.rows) {
             a.mean[row] = mu;
             a.rstd[row] = rstd;
@@ -230,21 +243,48 @@ __global__ __launch_bounds__(dyn_block<T>()) void layernorm_fwd_dyn_kernel(DynFw
     }
 }
 
+#define ROWNORM_DYN_FWD_KERNELS(name)                                                  \
+    template <int W, int T, int V, int K>                                               \
+    __global__ __launch_bounds__(dyn_block<T>()) void name##_dyn_kernel(DynFwdArgs a) {   \
+        name##_dyn_body<W, T, V, K, false>(a);                                          \
+    }                                                                                   \
+    template <int W, int T, int V, int K>                                               \
+    __global__ __launch_bounds__(dyn_block<T>()) void name##_dyn_lw_kernel(DynFwdArgs a) { \
+        name##_dyn_body<W, T, V, K, true>(a);                                           \
+    }
+ROWNORM_DYN_FWD_KERNELS(fused_add_rmsnorm)
+ROWNORM_DYN_FWD_KERNELS(rmsnorm_fwd)
+ROWNORM_DYN_FWD_KERNELS(layernorm_fwd)
+#undef ROWNORM_DYN_FWD_KERNELS
+
 struct OpFusedDyn {};
 struct OpRmsDyn {};
 struct OpLnFwdDyn {};
 
-template <class Op, int W, int T, int V, int K>
+template <class Op, int W, int T, int V, int K, bool LATE>
 hipError_t launch_fwd_dyn(const DynFwdArgs& a, hipStream_t stream) {
     constexpr int RK = dyn_block<T>() / T * K;
     const dim3 grid((unsigned)((a.rows + RK - 1) / RK));
     const dim3 block(dyn_block<T>());
-    if constexpr (std::is_same_v<Op, OpFusedDyn>)
-        hipLaunchKernelGGL((fused_add_rmsnorm_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
-    else if constexpr (std::is_same_v<Op, OpRmsDyn>)
-        hipLaunchKernelGGL((rmsnorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((layernorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
+    if constexpr (std::is_same_v<Op, OpFusedDyn>) {
+        if constexpr (LATE)
+            hipLaunchKernelGGL((fused_add_rmsnorm_dyn_lw_kernel<W, T, V, K>), grid, block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((fused_add_rmsnorm_dyn_kernel<W, T, V, K>), grid, block, 0, stream,
+                               a);
+    } else if constexpr (std::is_same_v<Op, OpRmsDyn>) {
+        if constexpr (LATE)
+            hipLaunchKernelGGL((rmsnorm_fwd_dyn_lw_kernel<W, T, V, K>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((rmsnorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
+    } else {
+        if constexpr (LATE)
+            hipLaunchKernelGGL((layernorm_fwd_dyn_lw_kernel<W, T, V, K>), grid, block, 0, stream,
+                               a);
+        else
+            hipLaunchKernelGGL((layernorm_fwd_dyn_kernel<W, T, V, K>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -268,10 +308,13 @@ constexpr bool dyn_fwd_fits() {
 template <class Op, int W, int T, int V>
 void add_dyn_fwd_one(std::vector<DynFwdEntry>& v) {
     if constexpr (dyn_fwd_fits<Op, W, T, V>()) {
-        v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 1>, 1});
+        v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 1, false>, 1,
+                     &launch_fwd_dyn<Op, W, T, V, 1, true>});
         if constexpr (T < kWave && V <= 2) {
-            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 2>, 2});
-            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 4>, 4});
+            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 2, false>, 2,
+                         &launch_fwd_dyn<Op, W, T, V, 2, true>});
+            v.push_back({W, T, V, &launch_fwd_dyn<Op, W, T, V, 4, false>, 4,
+                         &launch_fwd_dyn<Op, W, T, V, 4, true>});
         }
     }
 }

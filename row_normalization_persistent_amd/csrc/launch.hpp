@@ -110,7 +110,8 @@ using DynBwdLauncher = hipError_t (*)(const DynBwdArgs&, hipStream_t);
 struct DynFwdEntry {
     int elems, lanes, vecs;  // access width W, lanes per row T, accesses per lane V
     DynFwdLauncher launch;
-    int rows_per_group;      // K rows per lane group (workgroup rows = R * K)
+    int rows_per_group;        // K rows per lane group (workgroup rows = R * K)
+    DynFwdLauncher launch_late;  // the late-weights variant
 };
 
 struct DynBwdEntry {

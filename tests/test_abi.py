@@ -172,6 +172,15 @@ def test_describe_config():
                                                                     cu_count=128)
     assert "fused_add_rmsnorm_lw_kernel<4096,64,4>" in rn.describe_config(
         "fused_add_rmsnorm", 2048, 4096, cu_count=256)
+    # run-time hidden: late weights exactly when the grid is 2 to 4 workgroups per CU
+    seen = set()
+    for rows in (256, 1024, 2048, 4096, 8192):
+        d = rn.describe_config("rmsnorm_fwd", rows, 2560, cu_count=256)
+        c = rn.select_config("rmsnorm_fwd", rows, 2560, cu_count=256)
+        late = 512 <= -(-rows // c.rows_per_block) <= 1024
+        assert ("rmsnorm_fwd_dyn_lw_kernel<" in d) == late, d
+        seen.add(late)
+    assert seen == {True, False}
     d = rn.describe_config("layernorm_bwd", 8192, 4096, cu_count=256)
     assert "persistent grid of 256" in d and f"workspace {rn.workspace_bytes(8192, 4096)}" in d
     with pytest.raises(rn.NormError):

@@ -74,7 +74,11 @@ LATE_WEIGHT_CASES = [("layernorm_fwd", 2047, 4096), ("rmsnorm_fwd", 4095, 1024),
                      ("fused_add_rmsnorm", 2047, 1024), ("fused_add_rmsnorm", 4095, 1024),
                      ("fused_add_rmsnorm", 2046, 4096), ("fused_add_rmsnorm", 3, 8192),
                      ("fused_add_rmsnorm", 501, 12288), ("fused_add_rmsnorm", 1, 16384),
-                     ("fused_add_rmsnorm", 61, 16384), ("fused_add_rmsnorm", 501, 16384)]
+                     ("fused_add_rmsnorm", 61, 16384), ("fused_add_rmsnorm", 501, 16384),
+                     # run-time hidden: 2 to 4 workgroups per CU
+                     ("rmsnorm_fwd", 2047, 6144), ("layernorm_fwd", 1023, 7168),
+                     ("fused_add_rmsnorm", 2045, 5120), ("rmsnorm_fwd", 1001, 5118),
+                     ("layernorm_fwd", 999, 3070), ("fused_add_rmsnorm", 1001, 6142)]
 
 
 @pytest.mark.parametrize("op,rows,hidden", LATE_WEIGHT_CASES)
