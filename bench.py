@@ -33,6 +33,9 @@ Also reported, on the same line:
                 32768 (rows staged in LDS); then
                 few wide rows through the row-split forward (one row over
                 several workgroups) beside one workgroup per row
+  config_points every RMSNorm-forward and LayerNorm-forward workload point
+                (hidden x rows grids of those workloads) with the kernel
+                the library runs, graph-timed on cold buffers
   copy_ceiling  torch's device copy of 1 GiB, as context for the peak
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 """
@@ -292,6 +295,8 @@ def main():
         result["other_ops"] = other_ops(torch, rn, wl, dev, stream,
                                         max(3, min(args.steps, 50) // 5),
                                         None if args.no_cpu_baseline else 1.0)
+        result["config_points"] = config_points(torch, rn, wl, dev, stream,
+                                                max(3, min(args.steps, 50) // 5))
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -462,6 +467,45 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     torch.cuda.synchronize()
     out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds)
     out += split_ops(torch, rn, wl, dev, stream, reps)
+    return out
+
+
+def config_points(torch, rn, wl, dev, stream, reps):
+    """Every point of the RMSNorm-forward (hidden 2048 / 8192 / 16384 x rows
+    1 / 64 / 1024 / 4096, 1 % outlier channels) and LayerNorm-forward (2048 rows
+    x hidden 1024 / 4096 / 12288 / 16384) workloads, on their seeded inputs,
+    with the library's launch choice: graph-timed over cold buffer sets, time
+    per launch, and the kernel that runs."""
+    out = []
+    pts = [("rmsnorm_fwd", r, h) for h in wl.RMSNORM_HIDDEN for r in wl.RMSNORM_ROWS]
+    pts += [("layernorm_fwd", wl.LAYERNORM_FWD_ROWS, h) for h in wl.LAYERNORM_FWD_HIDDEN]
+    for op, rows, h in pts:
+        if op == "rmsnorm_fwd":
+            i = wl.rmsnorm_inputs(rows, h, seed=0)
+            nb = 4 * h * rows + 2 * h
+        else:
+            i = wl.layernorm_fwd_inputs(rows, h, seed=0)
+            nb = (4 * h + 8) * rows + 4 * h
+        n = _n_sets(2 * rows * h * 2) if rows * h * 4 >= (1 << 20) else 16
+        x0 = wl.to_device_bf16(i["x"], dev)
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        ys = [torch.empty_like(x0) for _ in range(n)]
+        st = torch.empty(n, 2, rows, device=dev)
+        w = wl.to_device_bf16(i["w"], dev)
+        if op == "rmsnorm_fwd":
+            fns = [(lambda j=j: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream))
+                   for j in range(n)]
+        else:
+            bb = wl.to_device_bf16(i["b"], dev)
+            fns = [(lambda j=j: rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
+                                                 rstd=st[j, 1], stream=stream))
+                   for j in range(n)]
+        t = graph_time_per_launch(torch, stream, fns, reps if nb > (16 << 20) else 10 * reps)
+        rec = _op_rec(op, rows, h, nb, t)
+        rec["kernel"] = _fwd_kernel_name(op, rows, h)
+        out.append(rec)
+        del xs, ys, x0
+    torch.cuda.synchronize()
     return out
 
 

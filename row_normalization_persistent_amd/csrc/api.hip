@@ -345,7 +345,7 @@ constexpr LateFwd kLateFwd[] = {
     {NORM_OP_LAYERNORM_FWD, 4096, 64, 4, 1449, 2897},       // 2048 rows: 8.22 -> 6.52 us (26 %)
     {NORM_OP_RMSNORM_FWD, 1024, 64, 4, 2897, 5793},         // 4096 rows: 3.93 -> 3.77 us (4 %)
     {NORM_OP_RMSNORM_FWD, 2048, 64, 4, 2897, 5793},         // 4096 rows: 7.35 -> 6.25 us (18 %)
-    {NORM_OP_RMSNORM_FWD, 8192, 128, 2, 725, 1449},         // 1024 rows: 6.59 -> 6.35 us (4 %)
+    {NORM_OP_RMSNORM_FWD, 8192, 128, 2, 725, 2897},         // 1024 / 2048 rows: 4 % / 21 %
     {NORM_OP_FUSED_ADD_RMSNORM, 1024, 64, 4, 1449, 5793},   // 2048 / 4096 rows: 8 % / 9 %
     {NORM_OP_FUSED_ADD_RMSNORM, 4096, 64, 4, 1449, 2897},   // 2048 rows: 12.11 -> 11.74 us (3 %)
     {NORM_OP_FUSED_ADD_RMSNORM, 8192, 1024, 1, 1, 8},       // 1 / 4 rows: 5 % / 5 %
