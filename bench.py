@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-ops", action="store_true")
+    ap.add_argument("--no-config-points", action="store_true",
+                    help="skip the config_points leg (the counter-collection profile runs do: "
+                         "rocprofv3 --pmc crashed in that leg's many graph-replayed dispatches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="turn rocprofv3 CSV output under DIR/{stats,fetch,write} into the "
@@ -295,8 +298,9 @@ def main():
         result["other_ops"] = other_ops(torch, rn, wl, dev, stream,
                                         max(3, min(args.steps, 50) // 5),
                                         None if args.no_cpu_baseline else 1.0)
-        result["config_points"] = config_points(torch, rn, wl, dev, stream,
-                                                max(3, min(args.steps, 50) // 5))
+        if not args.no_config_points:
+            result["config_points"] = config_points(torch, rn, wl, dev, stream,
+                                                    max(3, min(args.steps, 50) // 5))
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -765,13 +769,13 @@ PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d $DIR/stats -o bench -- "
     "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $DIR/fetch -o bench -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-config-points",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $DIR/write -o bench -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-config-points",
     "rocprofv3 --pmc MeanOccupancyPerCU --output-format csv -d $DIR/occ -o bench -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-config-points",
     "rocprofv3 --pmc LdsBankConflict --output-format csv -d $DIR/lds -o bench -- "
-    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-config-points",
     "python3 bench.py --summarize-profiles $DIR",
 ]
 CALIBRATION_BYTES = 1 << 30  # the 1 GiB device copy of the copy_ceiling pass
