@@ -101,6 +101,32 @@ def rmsnorm_bwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
             "eps": EPS_RMS}
 
 
+def device_normal_bf16(rows: int, hidden: int, mean: float, std: float, seed: int,
+                       device="cuda", ld: int | None = None) -> torch.Tensor:
+    """A [rows, hidden] bf16 matrix ~ N(mean, std) drawn on the device from a
+    seeded torch generator, for matrices too large to draw on the host: fp32
+    draws in chunks of rows, rounded to bf16 by torch.  With ``ld`` > hidden the
+    matrix is the first ``hidden`` columns of a [rows, ld] allocation whose
+    other columns hold draws of the same distribution."""
+    cols = hidden if ld is None else ld
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    full = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
+    chunk = max(1, (1 << 26) // cols)
+    for a in range(0, rows, chunk):
+        b = min(rows, a + chunk)
+        z = torch.randn((b - a, cols), generator=g, device=device, dtype=torch.float32)
+        full[a:b] = (z * std + mean).to(torch.bfloat16)
+    return full if ld is None else full[:, :hidden]
+
+
+def device_normal_f32(n: int, mean: float, std: float, seed: int, device="cuda") -> torch.Tensor:
+    """n fp32 values ~ N(mean, std) drawn on the device from a seeded torch generator."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(n, generator=g, device=device, dtype=torch.float32) * std + mean
+
+
 def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     """bf16 bit patterns (uint16) -> torch.bfloat16 tensor on `device`."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)

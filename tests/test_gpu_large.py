@@ -1,0 +1,251 @@
+"""GPU parity past 4 GiB per matrix: every kernel family's 64-bit row
+addressing (row offsets beyond 2^31 and 2^32 bytes), through the C ABI.
+
+The matrices are drawn on the device from seeded generators
+(workloads.device_normal_bf16); the oracle recomputes sampled rows: the first
+rows, the rows on either side of the 2^31- and 2^32-byte offsets, the ragged
+last rows and a few seeded random rows.  Outputs are filled with NaN before
+each call, so an element the kernels never wrote fails the all-finite check
+on the whole output.  Column sums (dweight, dbias) cover every row and are
+checked against their definition summed in fp64 on the device.  Rules in
+parity.py."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as P
+import row_normalization_persistent_amd as rn
+from row_normalization_persistent_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+NT = min(16, os.cpu_count() or 1)
+DEV = "cuda"
+GIB4 = 1 << 32
+
+
+def rows_past_4gib(hidden: int, extra: int, ld: int | None = None) -> int:
+    """Rows of a bf16 matrix with row stride ld (default hidden) whose last
+    rows lie past 2^32 bytes."""
+    return GIB4 // (2 * (ld or hidden)) + extra
+
+
+def sample_rows(rows: int, row_bytes: int, seed: int) -> np.ndarray:
+    picks = {0, 1, rows - 2, rows - 1}
+    for edge in (1 << 31, 1 << 32):
+        r = edge // row_bytes
+        picks.update({r - 1, r, r + 1})
+    picks.update(np.random.default_rng(seed).integers(0, rows, 6).tolist())
+    return np.array(sorted(p for p in picks if 0 <= p < rows), np.int64)
+
+
+def take(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    """Rows idx of a bf16 device matrix as host bf16 bits."""
+    sel = t.index_select(0, torch.from_numpy(idx).to(t.device))
+    return wl.from_device_bf16(sel)
+
+
+def assert_all_finite(t: torch.Tensor, what: str):
+    bad = int((~torch.isfinite(t.float() if t.dtype == torch.bfloat16 else t)).sum().item())
+    assert bad == 0, f"{what}: {bad} elements not written (still NaN) or not finite"
+
+
+def nan_like(t: torch.Tensor) -> torch.Tensor:
+    return torch.full(t.shape, float("nan"), dtype=t.dtype, device=t.device)
+
+
+def free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def weight(hidden, seed, mean=1.0, std=0.1):
+    rng = np.random.default_rng(seed)
+    bits = wl.bf16_bits((rng.standard_normal(hidden) * std + mean).astype(np.float32))
+    return bits, wl.to_device_bf16(bits, DEV)
+
+
+def colsums_f64(n_rows, hidden, term, chunk=1 << 16):
+    """(sum_i t_ij, sum_i t_ij^2) in fp64 on the device, t = term(a, b) for row chunks."""
+    s = torch.zeros(hidden, dtype=torch.float64, device=DEV)
+    q = torch.zeros(hidden, dtype=torch.float64, device=DEV)
+    for a in range(0, n_rows, chunk):
+        t = term(a, min(n_rows, a + chunk))
+        s += t.sum(0)
+        q += (t * t).sum(0)
+    return s.cpu().numpy(), q.cpu().numpy()
+
+
+def test_fused_add_rmsnorm_past_4gib():
+    """hidden 4096 (compiled kernels): x, residual, out of 4 GiB + 77 rows each."""
+    h = 4096
+    rows = rows_past_4gib(h, 77)
+    idx = sample_rows(rows, 2 * h, seed=1)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=101)
+    r = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=102)
+    w_bits, w = weight(h, 103)
+    xs, rs = take(x, idx), take(r, idx)
+    out = nan_like(x)
+    rn.fused_add_rmsnorm(x, r, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, res_ref, _ = oracle.fused_add_rmsnorm(xs, rs, w_bits, wl.EPS_RMS, NT)
+    P.assert_bits_equal(take(r, idx), res_ref, "fused past 4 GiB: residual")
+    P.assert_bf16_close(take(out, idx), ref, "fused past 4 GiB: out")
+    assert_all_finite(out, "fused past 4 GiB: out")
+    del x, r, out
+    free()
+
+
+def test_fused_add_rmsnorm_runtime_hidden_past_4gib():
+    """hidden 5120 (run-time-hidden kernels): 4 GiB + 3 rows each."""
+    h = 5120
+    rows = rows_past_4gib(h, 3)
+    idx = sample_rows(rows, 2 * h, seed=2)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=201)
+    r = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=202)
+    w_bits, w = weight(h, 203)
+    xs, rs = take(x, idx), take(r, idx)
+    out = nan_like(x)
+    rn.fused_add_rmsnorm(x, r, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, res_ref, _ = oracle.fused_add_rmsnorm(xs, rs, w_bits, wl.EPS_RMS, NT)
+    P.assert_bits_equal(take(r, idx), res_ref, "run-time fused past 4 GiB: residual")
+    P.assert_bf16_close(take(out, idx), ref, "run-time fused past 4 GiB: out")
+    assert_all_finite(out, "run-time fused past 4 GiB: out")
+    del x, r, out
+    free()
+
+
+def test_rmsnorm_fwd_past_4gib():
+    """hidden 2048: 2^20 + 3 rows (4 GiB + 12 KiB per matrix)."""
+    h = 2048
+    rows = rows_past_4gib(h, 3)
+    idx = sample_rows(rows, 2 * h, seed=3)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=301)
+    w_bits, w = weight(h, 302)
+    out = nan_like(x)
+    rn.rmsnorm_fwd(x, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.rmsnorm_fwd(take(x, idx), w_bits, wl.EPS_RMS, NT)
+    P.assert_bf16_close(take(out, idx), ref, "rmsnorm past 4 GiB")
+    assert_all_finite(out, "rmsnorm past 4 GiB")
+    del x, out
+    free()
+
+
+def test_rmsnorm_fwd_column_slice_past_4gib():
+    """In place on the first 128 columns of a [rows, 384] matrix of 4 GiB + 5
+    rows (narrow rows share one buffer descriptor per set of rows)."""
+    h, ld = 128, 384
+    rows = rows_past_4gib(h, 5, ld)
+    idx = sample_rows(rows, 2 * ld, seed=4)
+    xv = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=401, ld=ld)
+    w_bits, w = weight(h, 402)
+    xs = take(xv, idx)
+    full = xv.as_strided((rows, ld), (ld, 1))
+    rest = full[:, h:].clone()
+    rn.rmsnorm_fwd(xv, w, wl.EPS_RMS, out=xv)
+    torch.cuda.synchronize()
+    ref, _ = oracle.rmsnorm_fwd(xs, w_bits, wl.EPS_RMS, NT)
+    P.assert_bf16_close(take(xv, idx), ref, "rmsnorm slice past 4 GiB")
+    assert torch.equal(full[:, h:], rest), "columns outside the slice changed"
+    del xv, full, rest
+    free()
+
+
+def test_layernorm_fwd_past_4gib():
+    """hidden 16384 (the persistent ring kernel): 4 GiB + 5 rows per matrix."""
+    h = 16384
+    rows = rows_past_4gib(h, 5)
+    idx = sample_rows(rows, 2 * h, seed=5)
+    x = wl.device_normal_bf16(rows, h, 0.5, 2.0, seed=501)
+    w_bits, w = weight(h, 502)
+    b_bits, b = weight(h, 503, mean=0.0, std=0.1)
+    y = nan_like(x)
+    mean = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    rstd = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    assert "ring" in rn.describe_config("layernorm_fwd", rows, h)
+    rn.layernorm_fwd(x, w, b, wl.EPS_LN, y=y, mean=mean, rstd=rstd)
+    torch.cuda.synchronize()
+    xs = take(x, idx)
+    ref, mean_ref, rstd_ref = oracle.layernorm_fwd(xs, w_bits, b_bits, wl.EPS_LN, NT)
+    xd, wd, bd = P.bits_to_f64(xs), P.bits_to_f64(w_bits), P.bits_to_f64(b_bits)
+    scale = P.layernorm_y_scale(xd, mean_ref, rstd_ref, wd, bd)
+    P.assert_bf16_close(take(y, idx), ref, "layernorm past 4 GiB: y", floor_scale=scale)
+    ti = torch.from_numpy(idx).to(DEV)
+    P.assert_f32_close(mean[ti].cpu().numpy(), mean_ref, "layernorm past 4 GiB: mean")
+    P.assert_f32_close(rstd[ti].cpu().numpy(), rstd_ref, "layernorm past 4 GiB: rstd")
+    assert_all_finite(y, "layernorm past 4 GiB: y")
+    assert_all_finite(mean, "layernorm past 4 GiB: mean")
+    assert_all_finite(rstd, "layernorm past 4 GiB: rstd")
+    del x, y, mean, rstd
+    free()
+
+
+def test_layernorm_bwd_past_4gib():
+    """hidden 4096: x, dy, dx of 4 GiB + 77 rows.  mean and rstd are drawn
+    (inputs of the backward, used as given by both sides), not computed from x."""
+    h = 4096
+    rows = rows_past_4gib(h, 77)
+    idx = sample_rows(rows, 2 * h, seed=6)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=601)
+    dy = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=602)
+    mean = wl.device_normal_f32(rows, 0.0, 0.02, seed=603)
+    rstd = wl.device_normal_f32(rows, 1.0, 0.05, seed=604)
+    w_bits, w = weight(h, 605)
+    dx = nan_like(x)
+    dw = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    db = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    rn.layernorm_bwd(dy, x, mean, rstd, w, dx=dx, dweight=dw, dbias=db)
+    torch.cuda.synchronize()
+    ti = torch.from_numpy(idx).to(DEV)
+    xs, dys = take(x, idx), take(dy, idx)
+    ms, rs = mean[ti].cpu().numpy(), rstd[ti].cpu().numpy()
+    dx_ref, _, _ = oracle.layernorm_bwd(dys, xs, ms, rs, w_bits, NT)
+    xd, dyd, wd = P.bits_to_f64(xs), P.bits_to_f64(dys), P.bits_to_f64(w_bits)
+    scale = P.layernorm_dx_scale(xd, dyd, wd, ms.astype(np.float64), rs.astype(np.float64))
+    P.assert_bf16_close(take(dx, idx), dx_ref, "layernorm bwd past 4 GiB: dx", floor_scale=scale)
+    assert_all_finite(dx, "layernorm bwd past 4 GiB: dx")
+    m64, r64 = mean.double(), rstd.double()
+    db_ref, db_q = colsums_f64(rows, h, lambda a, b: dy[a:b].double())
+    dw_ref, dw_q = colsums_f64(
+        rows, h, lambda a, b: dy[a:b].double() * (x[a:b].double() - m64[a:b, None]) * r64[a:b, None])
+    P.assert_colsum_close(dw.cpu().numpy(), dw_ref, dw_q, "layernorm bwd past 4 GiB: dweight")
+    P.assert_colsum_close(db.cpu().numpy(), db_ref, db_q, "layernorm bwd past 4 GiB: dbias")
+    del x, dy, dx, mean, rstd, m64, r64
+    free()
+
+
+def test_fused_add_rmsnorm_bwd_past_4gib():
+    """hidden 4096, with the residual gradient: s, dout, dres, ds of 4 GiB + 7 rows."""
+    h = 4096
+    rows = rows_past_4gib(h, 7)
+    idx = sample_rows(rows, 2 * h, seed=7)
+    s = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=701)
+    dout = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=702)
+    dres = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=703)
+    w_bits, w = weight(h, 704)
+    ds = nan_like(s)
+    dw = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    rn.fused_add_rmsnorm_bwd(dout, s, w, wl.EPS_RMS, dres=dres, ds=ds, dweight=dw)
+    torch.cuda.synchronize()
+    ss, dos, drs = take(s, idx), take(dout, idx), take(dres, idx)
+    dx_ref, _, rstd = oracle.rmsnorm_bwd(dos, ss, w_bits, wl.EPS_RMS, dres=drs, nthreads=NT)
+    xd, dyd, wd = P.bits_to_f64(ss), P.bits_to_f64(dos), P.bits_to_f64(w_bits)
+    scale = P.rmsnorm_dx_scale(xd, dyd, wd, rstd, P.bits_to_f64(drs))
+    P.assert_bf16_close(take(ds, idx), dx_ref, "fused bwd past 4 GiB: ds", floor_scale=scale)
+    assert_all_finite(ds, "fused bwd past 4 GiB: ds")
+    eps = float(wl.EPS_RMS)
+
+    def term(a, b):
+        sd = s[a:b].double()
+        r = torch.rsqrt((sd * sd).mean(1, keepdim=True) + eps)
+        return dout[a:b].double() * sd * r
+
+    dw_ref, dw_q = colsums_f64(rows, h, term)
+    P.assert_colsum_close(dw.cpu().numpy(), dw_ref, dw_q, "fused bwd past 4 GiB: dweight")
+    del s, dout, dres, ds
+    free()
