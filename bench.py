@@ -22,6 +22,9 @@ Also reported, on the same line:
   kernels       the same for every instantiation the sweep uses
   sweep         per-rows GB/s, % of the 8 TB/s peak, rows/s (eager launches,
                 an event pair around each, so dispatch overhead is included)
+  sweep_graph   the same rows, each graph-timed on its own over enough cold
+                buffer sets (time per launch includes only the GPU's gap
+                between dependent launches)
   other_ops     RMSNorm / LayerNorm forward / LayerNorm backward / RMSNorm
                 backward / fused add + RMSNorm backward at their largest
                 workload: one graph of back-to-back launches over
@@ -69,8 +72,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-ops", action="store_true")
     ap.add_argument("--no-config-points", action="store_true",
-                    help="skip the config_points leg (the counter-collection profile runs do: "
-                         "rocprofv3 --pmc crashed in that leg's many graph-replayed dispatches)")
+                    help="skip the sweep_graph and config_points legs (the counter-collection "
+                         "profile runs do: rocprofv3 --pmc crashed in config_points' many "
+                         "graph-replayed dispatches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="turn rocprofv3 CSV output under DIR/{stats,fetch,write} into the "
@@ -299,6 +303,8 @@ def main():
                                         max(3, min(args.steps, 50) // 5),
                                         None if args.no_cpu_baseline else 1.0)
         if not args.no_config_points:
+            result["sweep_graph"] = sweep_graph(torch, rn, dev, stream, sets[0], w, eps, offs,
+                                                max(3, min(args.steps, 50) // 5))
             result["config_points"] = config_points(torch, rn, wl, dev, stream,
                                                     max(3, min(args.steps, 50) // 5))
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
@@ -474,6 +480,36 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     return out
 
 
+def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
+    """Each rows value of the sweep on its own: its seeded slice of x and
+    residual cloned into enough buffer sets that the graph's launches cycle
+    through >= 1.2 GB, at most 512 sets (below 1 MiB a set: 256 sets, so the
+    graph's submission cost is spread as thinly as at the large points; those
+    few MB stay cache-resident, which latency-bound launches barely notice),
+    graph-timed per launch.  The kernel-level view of the sweep (no host
+    dispatch cost)."""
+    out = []
+    for i, rows in enumerate(SWEEP_ROWS):
+        a, b = int(offs[i]), int(offs[i + 1])
+        per_set = 8 * rows * HIDDEN
+        n = min(512, _n_sets(per_set)) if per_set >= (1 << 20) else 256
+        xs = [s0["x"][a:b].clone() for _ in range(n)]
+        rs = [s0["r"][a:b].clone() for _ in range(n)]
+        os_ = [torch.empty_like(xs[0]) for _ in range(n)]
+        fns = [(lambda j=j: rn.fused_add_rmsnorm(xs[j], rs[j], w, eps, out=os_[j], stream=stream))
+               for j in range(n)]
+        nb = fused_bytes(rows)
+        t = graph_time_per_launch(torch, stream, fns,
+                                  max(2, min(reps if nb > (16 << 20) else 10 * reps, 3000 // n)))
+        rec = _op_rec("fused_add_rmsnorm", rows, HIDDEN, nb, t)
+        rec["rows_per_s"] = round(rows / (t * 1e-6))
+        rec["kernel"] = _fwd_kernel_name("fused_add_rmsnorm", rows, HIDDEN)
+        out.append(rec)
+        del xs, rs, os_
+    torch.cuda.synchronize()
+    return out
+
+
 def config_points(torch, rn, wl, dev, stream, reps):
     """Every point of the RMSNorm-forward (hidden 2048 / 8192 / 16384 x rows
     1 / 64 / 1024 / 4096, 1 % outlier channels) and LayerNorm-forward (2048 rows
@@ -490,7 +526,7 @@ def config_points(torch, rn, wl, dev, stream, reps):
         else:
             i = wl.layernorm_fwd_inputs(rows, h, seed=0)
             nb = (4 * h + 8) * rows + 4 * h
-        n = min(512, _n_sets(2 * rows * h * 2)) if rows * h * 4 >= (1 << 20) else 16
+        n = min(512, _n_sets(2 * rows * h * 2)) if rows * h * 4 >= (1 << 20) else 256
         x0 = wl.to_device_bf16(i["x"], dev)
         xs = [x0] + [x0.clone() for _ in range(n - 1)]
         ys = [torch.empty_like(x0) for _ in range(n)]
