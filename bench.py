@@ -805,7 +805,7 @@ def cpu_baseline(inp, seconds):
 # ---------------------------------------------------------------------------
 PROFILE_COMMANDS = [
     "rocprofv3 --kernel-trace --stats --output-format csv -d $DIR/stats -o bench -- "
-    "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+    "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-config-points",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $DIR/fetch -o bench -- "
     "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-config-points",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $DIR/write -o bench -- "
@@ -905,10 +905,11 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
     lines = ["# Kernel durations: fused residual-add + RMSNorm, hidden 4096, rows 1-8192 sweep",
              "", "Produced on one MI355X (gfx950, 256 CUs) by:", "", cmds, "",
              "`bench.py` runs the sweep from HIP graphs, then the per-instantiation graph pass "
-             "behind `roofline`, the eager per-rows pass, the other operations, the "
-             "RMSNorm / LayerNorm forward workload points (config_points; the counter runs "
-             "skip them) and the 1 GiB copy.  `--stats` summary (all dispatches of the "
-             "command):", "",
+             "behind `roofline`, the eager per-rows pass, the other operations and the "
+             "1 GiB copy (every profile run skips the graph-timed per-rows sweep and the "
+             "RMSNorm / LayerNorm forward workload points: they would add thousands of "
+             "dispatches of the same instantiations at other row counts to the averages "
+             "below).  `--stats` summary (all dispatches of the command):", "",
              "| kernel | calls | average us | min us | max us |", "|---|---:|---:|---:|---:|"]
     for r in stats:
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
