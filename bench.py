@@ -18,7 +18,10 @@ Also reported, on the same line:
                 GPU time in a step): its launches of a step over every buffer
                 set, captured in one graph and replayed for about K steps
                 between two HIP events on the launch stream; achieved =
-                algorithmic bytes per launch / average launch time
+                algorithmic bytes per launch / average launch time; beside
+                it the same launches through a kernel with the same memory
+                traffic and no arithmetic (libnormceiling.so): the practical
+                ceiling of this traffic on the part
   kernels       the same for every instantiation the sweep uses
   sweep         per-rows GB/s, % of the 8 TB/s peak, rows/s (eager launches,
                 an event pair around each, so dispatch overhead is included)
@@ -197,17 +200,18 @@ def main():
         g = groups.setdefault(key, {"idx": [], "bytes": 0})
         g["idx"].append(i)
         g["bytes"] += fused_bytes(SWEEP_ROWS[i])
-    for key, g in groups.items():
-        # one graph walks the instantiation's launches over all buffer sets in
-        # turn, so each replay is N_SETS steps' worth and the per-replay launch
-        # cost is spread over N_SETS * len(idx) kernels
+    def group_us_per_step(launch_fn, idx):
+        """One graph walks the launches `idx` of a step over all buffer sets
+        in turn (each replay is N_SETS steps' worth, so the per-replay cost is
+        spread over N_SETS * len(idx) kernels), replayed about K steps' worth
+        between two events on the launch stream: GPU time per step."""
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             cg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(cg, stream=stream):
                 for k in range(N_SETS):
-                    for i in g["idx"]:
-                        launch(sets[k], i)
+                    for i in idx:
+                        launch_fn(sets[k], i)
             cg.replay()
         reps = max(1, args.steps // N_SETS)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -219,11 +223,14 @@ def main():
                 cg.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        g["us_per_step"] = e0.elapsed_time(e1) * 1e3 / (reps * N_SETS)
+        del cg
+        return e0.elapsed_time(e1) * 1e3 / (reps * N_SETS)
+
+    for key, g in groups.items():
+        g["us_per_step"] = group_us_per_step(launch, g["idx"])
         g["avg_launch_us"] = g["us_per_step"] / len(g["idx"])
         g["avg_bytes"] = g["bytes"] / len(g["idx"])
         g["GBps"] = g["avg_bytes"] / (g["avg_launch_us"] * 1e-6) / 1e9
-        del cg
     dom_key = max(groups, key=lambda k: groups[k]["us_per_step"])
     dom = groups[dom_key]
     achieved = dom["GBps"]
@@ -236,6 +243,31 @@ def main():
                 "algorithmic_bytes_per_launch": round(dom["avg_bytes"]),
                 "avg_launch_us": round(dom["avg_launch_us"], 3)}
     log(f"dominant kernel {kname}: {dom['avg_launch_us']:.2f} us/launch avg, {achieved:.0f} GB/s")
+
+    # ---- same-traffic ceiling: the dominant kernel's launches (same rows,
+    # launch shapes, buffers and graph) through a kernel with its exact
+    # memory traffic and no arithmetic (libnormceiling.so)
+    ceil = _ceiling_fn()
+    if ceil is not None and all(cfgs[i].vector_elems == 0 for i in dom["idx"]):
+        def copy_launch(s, i):
+            a, b = int(offs[i]), int(offs[i + 1])
+            c = cfgs[i]
+            st = ceil(s["out"][a:b].data_ptr(), s["r"][a:b].data_ptr(), s["x"][a:b].data_ptr(),
+                      b - a, c.threads_per_row, c.rows_per_block, sid)
+            if st != 0:
+                raise RuntimeError(f"same-traffic kernel failed ({st}) at rows {b - a}")
+
+        c_us = group_us_per_step(copy_launch, dom["idx"]) / len(dom["idx"])
+        c_gbps = dom["avg_bytes"] / (c_us * 1e-6) / 1e9
+        roofline["same_traffic_ceiling"] = {
+            "kernel": "same-traffic copy: x and residual read, two outputs written, no arithmetic, "
+                      "in the dominant kernel's launch shapes and row mix",
+            "avg_launch_us": round(c_us, 3), "GBps": round(c_gbps, 1),
+            "frac_of_peak": round(c_gbps / HBM_PEAK_GBPS, 4),
+            "kernel_time_over_ceiling_time": round(dom["avg_launch_us"] / c_us, 3)}
+        log(f"same-traffic ceiling: {c_us:.2f} us/launch avg, {c_gbps:.0f} GB/s")
+    else:
+        roofline["same_traffic_ceiling"] = None
     kernels = [{"kernel": k,
                 "rows": [SWEEP_ROWS[i] for i in g["idx"]],
                 "us_per_step": round(g["us_per_step"], 3),
@@ -480,6 +512,21 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     return out
 
 
+def _ceiling_fn():
+    """normceil_same_traffic_h4096 from libnormceiling.so (built with the
+    package), or None when it was not built."""
+    import ctypes
+    import row_normalization_persistent_amd as rn
+    path = os.path.join(os.path.dirname(os.path.abspath(rn.__file__)), "libnormceiling.so")
+    if not os.path.exists(path):
+        return None
+    f = ctypes.CDLL(path).normceil_same_traffic_h4096
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    return f
+
+
 def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
     """Each rows value of the sweep on its own: its seeded slice of x and
     residual cloned into enough buffer sets that the graph's launches cycle
@@ -504,6 +551,18 @@ def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
         rec = _op_rec("fused_add_rmsnorm", rows, HIDDEN, nb, t)
         rec["rows_per_s"] = round(rows / (t * 1e-6))
         rec["kernel"] = _fwd_kernel_name("fused_add_rmsnorm", rows, HIDDEN)
+        c = rn.select_config("fused_add_rmsnorm", rows, HIDDEN)
+        ceil = _ceiling_fn()
+        if ceil is not None and rows >= 512 and c.vector_elems == 0:
+            sid = stream.cuda_stream
+            cfns = [(lambda j=j: ceil(os_[j].data_ptr(), rs[j].data_ptr(), xs[j].data_ptr(), rows,
+                                      c.threads_per_row, c.rows_per_block, sid))
+                    for j in range(n)]
+            tc = graph_time_per_launch(torch, stream, cfns,
+                                       max(2, min(reps if nb > (16 << 20) else 10 * reps,
+                                                  3000 // n)))
+            rec["same_traffic_us"] = round(tc, 3)
+            rec["time_over_same_traffic"] = round(t / tc, 3)
         out.append(rec)
         del xs, rs, os_
     torch.cuda.synchronize()

@@ -38,6 +38,11 @@ SOURCES = [
     "k_bwd_wide.hip",
 ]
 
+# Benchmark-only measurement kernel (not part of the normalization library):
+# its own shared library, loaded by bench.py alone.
+CEILING_SOURCES = ["ceiling.hip"]
+CEILING_LIB_PATH = os.path.join(PKG, "libnormceiling.so")
+
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -95,5 +100,20 @@ def build(extra_flags=(), jobs: int | None = None, out_path: str | None = None,
     return out_path
 
 
+def build_ceiling() -> str:
+    """Compile and link libnormceiling.so (the benchmark's same-traffic
+    measurement kernel).  Always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = [_compile(src, []) for src in CEILING_SOURCES]
+    tmp = CEILING_LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, CEILING_LIB_PATH)
+    return CEILING_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_ceiling())
