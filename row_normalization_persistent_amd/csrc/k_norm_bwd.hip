@@ -35,19 +35,29 @@ struct BwdRow {
 };
 
 // Loads one row (predicated: a row index past the end loads zeros, from no
-// memory, and its mean/rstd load as 0, so it contributes nothing below).
+// memory, and its mean/rstd are 0, so it contributes nothing below).  The
+// row's mean and rstd are the same for every lane of the workgroup, so they
+// come in by scalar loads from a clamped row index (rows >= 1 whenever the
+// kernel runs) instead of a buffer load in every lane: at one 16-byte access
+// per lane that halves a row's vector memory instructions.  Measured on
+// MI355X: 8192 x 2048 / 4096 / 8192 rows kernel 5 / 2 / 1 % faster, output
+// bitwise unchanged.
 template <int H, int T, int V>
 __device__ __forceinline__ void load_bwd_row(BwdRow<V>& r, const u32x4* x, const u32x4* dy,
-                                             const float* mean, const float* rstd,
-                                             int64_t row, int64_t rows, int lane) {
+                                             const float* __restrict__ mean,
+                                             const float* __restrict__ rstd, int64_t row,
+                                             int64_t rows, int lane) {
     const rsrc_t rx = row_rsrc(x, row, rows, H * 2);
     const rsrc_t rd = row_rsrc(dy, row, rows, H * 2);
 #pragma unroll
     for (int b = 0; b < V; ++b) r.x[b] = rload_stream(rx, (b * T + lane) * 16);
 #pragma unroll
     for (int b = 0; b < V; ++b) r.dy[b] = rload_stream(rd, (b * T + lane) * 16);
-    r.mean = rload_f32(row_rsrc(mean, row, rows, 4), 0);
-    r.rstd = rload_f32(row_rsrc(rstd, row, rows, 4), 0);
+    const int64_t rc = row < rows ? row : rows - 1;
+    const float m = __builtin_nontemporal_load(mean + rc);
+    const float q = __builtin_nontemporal_load(rstd + rc);
+    r.mean = row < rows ? m : 0.0f;
+    r.rstd = row < rows ? q : 0.0f;
 }
 
 // RMSNorm row: x, dy and (fused op) the residual-output gradient dres.
