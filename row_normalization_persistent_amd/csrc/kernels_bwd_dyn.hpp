@@ -81,9 +81,23 @@ __device__ __forceinline__ void dyn_load_row(DynRow<W, V, LN, DRES>& r, const Dy
             r.dres[b] = aload<W, kCachePolicyNT>(rr, walk_off<W, T>(w, b, lane, a.ld_dres, h));
     }
     if constexpr (LN) {
-        const int off = set_off<T>(w.local, 0, 1, 1, 4);
-        r.mean = rload_f32(rows_rsrc<T>(a.mean, w.first, w.span, a.rows, 1, 1, 4), off);
-        r.rstd = rload_f32(rows_rsrc<T>(a.rstd, w.first, w.span, a.rows, 1, 1, 4), off);
+        if constexpr (T >= kWave) {
+            // one row per lane group: its mean and rstd are wave-uniform, so
+            // scalar loads (through the constant address space: the kernel
+            // never writes them) from a clamped row index replace a buffer
+            // load in every lane (rows >= 1 whenever the kernel runs)
+            typedef const __attribute__((address_space(4))) float cfloat;
+            const int64_t row = w.first;
+            const int64_t rc = row < a.rows ? row : a.rows - 1;
+            const float m = ((const cfloat*)(uintptr_t)a.mean)[rc];
+            const float q = ((const cfloat*)(uintptr_t)a.rstd)[rc];
+            r.mean = row < a.rows ? m : 0.0f;
+            r.rstd = row < a.rows ? q : 0.0f;
+        } else {
+            const int off = set_off<T>(w.local, 0, 1, 1, 4);
+            r.mean = rload_f32(rows_rsrc<T>(a.mean, w.first, w.span, a.rows, 1, 1, 4), off);
+            r.rstd = rload_f32(rows_rsrc<T>(a.rstd, w.first, w.span, a.rows, 1, 1, 4), off);
+        }
     }
 }
 
