@@ -121,7 +121,9 @@ typedef enum {
  *                     LayerNorm forward: 0 runs one row per lane group, > 0
  *                     runs the persistent ring kernel of that lane count
  *                     (compiled-hidden shapes, rows_per_block 1) on that many
- *                     workgroups.  Must be 0 for the other forward ops.
+ *                     workgroups; the library picks the ring depth (rows in
+ *                     flight per workgroup) from the walk, ceil(rows / grid)
+ *                     rows.  Must be 0 for the other forward ops.
  *   vector_elems    : 0 for a compiled-hidden shape; 1, 2, 4 or 8 for a
  *                     run-time-hidden shape whose accesses move that many
  *                     bf16 elements (hidden, every ld and every bf16 pointer

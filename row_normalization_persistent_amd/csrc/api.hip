@@ -143,6 +143,24 @@ const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb, bool ri
     return nullptr;
 }
 
+// The LayerNorm ring kernel a call runs: the shallowest compiled depth that
+// holds a workgroup's whole walk (ceil(rows / grid) rows), else the deepest
+// compiled.  Measured on MI355X (2048 rows at hidden 8192 / 12288 / 16384,
+// one workgroup per CU): loading the whole walk at once beats a shallower
+// ring by 6-16 %; with walks longer than the deepest ring the depths are
+// within 1-2 % of each other.
+const FwdEntry* ring_entry(norm_op op, int64_t hidden, int lanes, int64_t rows, int64_t grid) {
+    const int64_t walk = grid > 0 ? std::max<int64_t>(1, (rows + grid - 1) / grid) : 1;
+    const FwdEntry *fit = nullptr, *deepest = nullptr;
+    for (const FwdEntry& e : fwd_table(op)) {
+        if (e.hidden != hidden || e.lanes != lanes || e.rows_per_block != 1 || e.depth == 0)
+            continue;
+        if (!deepest || e.depth > deepest->depth) deepest = &e;
+        if (e.depth >= walk && (!fit || e.depth < fit->depth)) fit = &e;
+    }
+    return fit ? fit : deepest;
+}
+
 // Largest persistent grid of a forward ring kernel (a sanity bound; the ring
 // kernels handle any grid from 1 up, idle workgroups included).
 constexpr int32_t kMaxFwdRingGrid = 1 << 20;
@@ -242,13 +260,15 @@ int pointer_width(std::initializer_list<const void*> ptrs) {
 //    4096 rows up the RMS kernels run best at 4 vectors per lane.
 //  * Rows per workgroup: 4 for one-wave rows, 2 for two-wave rows, else 1.
 // LayerNorm forward from 512 rows (4096 at hidden 4096) runs on the persistent
-// ring kernel (measured on MI355X, 2048 rows: 6-8 % faster at hidden 8192-16384;
-// below those row counts the launch is latency-bound and the plain kernels
-// win): lanes and grid per hidden size from the same sweep.
+// ring kernel (measured on MI355X, 2048 rows: 6-8 % faster at hidden 8192-16384
+// with a fixed ring depth, 12-16 % with the depth picked per walk; below those
+// row counts the launch is latency-bound and the plain kernels win): lanes and
+// grid per hidden size from the same sweeps (512 lanes beat 1024 at hidden
+// 16384 and 256 at 12288 by 2-10 % at 512-8192 rows).
 norm_launch_cfg choose_ln_ring(int64_t rows, int64_t hidden) {
     int lanes = 0, grid = 0;
-    if (hidden == 16384 && rows >= 512) lanes = 1024, grid = 256;
-    if (hidden == 12288 && rows >= 512) lanes = 256, grid = 256;
+    if (hidden == 16384 && rows >= 512) lanes = 512, grid = 256;
+    if (hidden == 12288 && rows >= 512) lanes = 512, grid = 256;
     if (hidden == 8192 && rows >= 512) lanes = 512, grid = 256;
     if (hidden == 4096 && rows >= 4096) lanes = 64, grid = 1024;
     if (lanes == 0 || !find_fwd(NORM_OP_LAYERNORM_FWD, hidden, lanes, 1, true))
@@ -301,8 +321,6 @@ constexpr TunedFwd kTunedFwd[] = {
     {NORM_OP_LAYERNORM_FWD, 8192, 1, 4, {512, 1, 0, 0}},  // 1 rows: 2.76 -> 2.64 us (4 %)
     {NORM_OP_LAYERNORM_FWD, 8192, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.88 -> 3.03 us (22 %)
     {NORM_OP_LAYERNORM_FWD, 12288, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.70 -> 3.44 us (7 %)
-    {NORM_OP_LAYERNORM_FWD, 12288, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 11.68 -> 11.19 us (4 %)
-    {NORM_OP_LAYERNORM_FWD, 12288, 5793, 8193, {512, 1, 256, 0}},  // 8192 rows: 71.65 -> 68.60 us (4 %)
     {NORM_OP_LAYERNORM_FWD, 16384, 4, 32, {512, 1, 0, 0}},  // 16 rows: 4.13 -> 3.83 us (7 %)
     {NORM_OP_LAYERNORM_FWD, 16384, 32, 128, {512, 1, 0, 0}},  // 64 rows: 4.31 -> 4.06 us (6 %)
     {NORM_OP_FUSED_ADD_RMSNORM, 1024, 128, 512, {64, 1, 0, 0}},  // 256 rows: 2.58 -> 2.19 us (15 %)
@@ -616,7 +634,10 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
 
     if (k.vector_elems == 0) {
         const FwdEntry* e =
-            find_fwd(op, c.hidden, k.threads_per_row, k.rows_per_block, k.grid > 0);
+            k.grid > 0 ? (k.rows_per_block == 1 ? ring_entry(op, c.hidden, k.threads_per_row,
+                                                             c.rows, k.grid)
+                                                : nullptr)
+                       : find_fwd(op, c.hidden, k.threads_per_row, k.rows_per_block);
         if (!e) return NORM_ERROR_INVALID_VALUE;
         const int64_t groups = k.grid > 0 ? k.grid : ceil_div(c.rows, k.rows_per_block);
         if (groups > INT32_MAX ||
@@ -1273,8 +1294,8 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                            : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd"
                                                            : "layernorm_fwd";
         char inst[96];
-        const FwdEntry* ring = c.grid > 0 ? find_fwd(op, hidden, c.threads_per_row, 1, true)
-                                          : nullptr;
+        const FwdEntry* ring =
+            c.grid > 0 ? ring_entry(op, hidden, c.threads_per_row, rows, c.grid) : nullptr;
         if (dyn) {
             int cu = cu_count;
             if (cu <= 0 && current_cu_count(&cu) != NORM_SUCCESS) return -1;
@@ -1335,10 +1356,16 @@ int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int3
         for (const BwdEntry& e : bwd_table(op))
             if (e.hidden == hidden) put(norm_launch_cfg{e.lanes, 1, 0, 0});
     } else {
-        for (const FwdEntry& e : fwd_table(op))
-            if (e.hidden == hidden)
-                put(norm_launch_cfg{e.lanes, e.rows_per_block, e.depth > 0 ? kFwdRingGrid : 0,
-                                    0});
+        int ring_lanes_seen = 0;  // bit k: a ring shape of 64 << k lanes listed already
+        for (const FwdEntry& e : fwd_table(op)) {
+            if (e.hidden != hidden) continue;
+            if (e.depth > 0) {  // one shape per lane count (the depth follows the walk)
+                const int bit = 1 << __builtin_ctz((unsigned)(e.lanes / 64));
+                if (ring_lanes_seen & bit) continue;
+                ring_lanes_seen |= bit;
+            }
+            put(norm_launch_cfg{e.lanes, e.rows_per_block, e.depth > 0 ? kFwdRingGrid : 0, 0});
+        }
     }
     // run-time-hidden shapes at the widest access a contiguous row allows
     const int w = shape_width(hidden, {});

@@ -418,17 +418,16 @@ hipError_t launch_ln_ring(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Ring depth of the LayerNorm ring kernels: as deep as the lane's registers
-// allow without spills (weight and bias, held and unpacked, cost 24 VGPRs per
-// 16-byte vector; each ring row 4).
-template <int H, int T>
-constexpr int ln_ring_depth() {
+// Ring depths of the LayerNorm ring kernels: each ring shape is compiled at
+// depths 2, 4 and 8, where the lane's registers hold that depth without
+// spills (from gfx950's resource report: about 20 VGPRs per 16-byte vector
+// for the held weight and bias and the arithmetic, 4 per vector for each ring
+// row, 24 besides; 128 VGPRs a lane in 1024-lane workgroups, 256 otherwise).
+// The launch picks a depth per call from the length of a workgroup's walk.
+template <int H, int T, int D>
+constexpr bool ln_ring_fits() {
     constexpr int V = H / (8 * T);
-    if constexpr (T >= 1024) return V <= 2 ? 2 : 0;
-    if constexpr (V <= 2) return 4;
-    if constexpr (V <= 4) return 3;
-    if constexpr (V <= 8) return 2;
-    return 0;
+    return 20 * V + 4 * V * D + 24 <= (T >= 1024 ? 128 : 256);
 }
 
 // (lanes per row, rows per workgroup) pairs tried for every hidden size;
@@ -444,11 +443,15 @@ template <class Op, int H, int T, int R>
 void add_fwd_entry(std::vector<FwdEntry>& v, LR<T, R>) {
     if constexpr (shape_ok<Op, H, T, R>())
         v.push_back({H, T, R, &launch_fwd<Op, H, T, R, false>, 0, &launch_fwd<Op, H, T, R, true>});
-    // LayerNorm also gets a persistent ring kernel per lane count
+    // LayerNorm also gets persistent ring kernels per lane count, one per depth
     if constexpr (std::is_same_v<Op, OpLnFwd> && R == 1 && H % (8 * T) == 0 && T % kWave == 0 &&
                   H >= 2048) {
-        constexpr int D = ln_ring_depth<H, T>();
-        if constexpr (D > 0) v.push_back({H, T, 1, &launch_ln_ring<H, T, D>, D, nullptr});
+        if constexpr (ln_ring_fits<H, T, 2>())
+            v.push_back({H, T, 1, &launch_ln_ring<H, T, 2>, 2, nullptr});
+        if constexpr (ln_ring_fits<H, T, 4>())
+            v.push_back({H, T, 1, &launch_ln_ring<H, T, 4>, 4, nullptr});
+        if constexpr (ln_ring_fits<H, T, 8>())
+            v.push_back({H, T, 1, &launch_ln_ring<H, T, 8>, 8, nullptr});
     }
 }
 

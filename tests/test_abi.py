@@ -561,8 +561,9 @@ def test_tuned_forward_table():
     assert sel("fused_add_rmsnorm", 64, 4096) == rn.Cfg(512, 1, 0, 8)  # the run-time kernel
     assert sel("fused_add_rmsnorm", 8192, 4096) == rn.Cfg(128, 2, 0, 0)  # the rules
     assert sel("layernorm_fwd", 64, 8192) == rn.Cfg(256, 1, 0, 0)
-    assert sel("layernorm_fwd", 8192, 12288) == rn.Cfg(512, 1, 256, 0)  # a ring shape
-    assert sel("layernorm_fwd", 9000, 12288) == rn.Cfg(256, 1, 256, 0)
+    assert sel("layernorm_fwd", 8192, 12288) == rn.Cfg(512, 1, 256, 0)  # the ring rule
+    assert sel("layernorm_fwd", 1024, 12288) == rn.Cfg(512, 1, 256, 0)
+    assert sel("layernorm_fwd", 64, 12288) == rn.Cfg(256, 1, 0, 0)  # an entry below the ring
     # every table choice runs: a listed shape of its (op, hidden)
     for op in ("fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"):
         for h in rn.HIDDEN_SIZES:
