@@ -118,12 +118,12 @@ typedef enum {
  *   grid            : number of persistent workgroups that walk the rows.
  *                     Backward ops: 0 lets the library choose; each
  *                     workgroup writes one partial column-sum slab.
- *                     LayerNorm forward: 0 runs one row per lane group, > 0
- *                     runs the persistent ring kernel of that lane count
- *                     (compiled-hidden shapes, rows_per_block 1) on that many
- *                     workgroups; the library picks the ring depth (rows in
- *                     flight per workgroup) from the walk, ceil(rows / grid)
- *                     rows.  Must be 0 for the other forward ops.
+ *                     LayerNorm and RMSNorm forward: 0 runs one row per lane
+ *                     group, > 0 runs the persistent ring kernel of that lane
+ *                     count (compiled-hidden shapes, rows_per_block 1) on that
+ *                     many workgroups; the library picks the ring depth (rows
+ *                     in flight per workgroup) from the walk, ceil(rows /
+ *                     grid) rows.  Must be 0 for the fused op.
  *   vector_elems    : 0 for a compiled-hidden shape; 1, 2, 4 or 8 for a
  *                     run-time-hidden shape whose accesses move that many
  *                     bf16 elements (hidden, every ld and every bf16 pointer

@@ -143,7 +143,7 @@ const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb, bool ri
     return nullptr;
 }
 
-// The LayerNorm ring kernel a call runs: the shallowest compiled depth that
+// The ring kernel (LayerNorm or RMSNorm) a call runs: the shallowest compiled depth that
 // holds a workgroup's whole walk (ceil(rows / grid) rows), else the deepest
 // compiled.  Measured on MI355X (2048 rows at hidden 8192 / 12288 / 16384,
 // one workgroup per CU): loading the whole walk at once beats a shallower
@@ -306,10 +306,8 @@ constexpr TunedFwd kTunedFwd[] = {
     {NORM_OP_RMSNORM_FWD, 4096, 32, 128, {256, 1, 0, 0}},  // 64 rows: 2.59 -> 2.24 us (14 %)
     {NORM_OP_RMSNORM_FWD, 8192, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.07 -> 2.54 us (17 %)
     {NORM_OP_RMSNORM_FWD, 12288, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.08 -> 2.79 us (9 %)
-    {NORM_OP_RMSNORM_FWD, 12288, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 11.07 -> 9.61 us (13 %)
     {NORM_OP_RMSNORM_FWD, 16384, 16, 32, {256, 1, 0, 0}},  // 16 rows: 3.21 -> 3.05 us (5 %)
     {NORM_OP_RMSNORM_FWD, 16384, 32, 128, {256, 1, 0, 0}},  // 64 rows: 3.46 -> 3.28 us (5 %)
-    {NORM_OP_RMSNORM_FWD, 16384, 512, 1025, {128, 4, 0, 0}},  // 1024 rows: 14.08 -> 12.32 us (12 %)
     {NORM_OP_LAYERNORM_FWD, 1024, 4, 32, {64, 4, 0, 0}},  // 16 rows: 2.52 -> 2.29 us (9 %)
     {NORM_OP_LAYERNORM_FWD, 1024, 32, 128, {64, 4, 0, 0}},  // 64 rows: 2.56 -> 2.32 us (9 %)
     {NORM_OP_LAYERNORM_FWD, 1024, 128, 512, {64, 1, 0, 0}},  // 256 rows: 2.97 -> 2.28 us (23 %)
@@ -403,10 +401,26 @@ bool late_weights_dyn(int64_t groups, int lanes, int cu) {
     return cu > 0 && lanes >= 64 && groups >= 2 * (int64_t)cu && groups <= 4 * (int64_t)cu;
 }
 
+// RMSNorm forward on the persistent ring kernel: 512 lanes, 256 workgroups,
+// from 512 rows at hidden 12288 and 16384 and from 2048 rows at hidden 8192.
+// Measured on MI355X against the one-row-per-lane-group choice (ring depth
+// picked per walk): hidden 16384 at 512 / 1024 / 2048 / 4096 / 8192 rows 0.82 /
+// 0.90 / 0.88 / 0.94 / 0.99 of its time, hidden 12288 at 1024 / 2048 / 4096
+// rows 0.89 / 0.85 / 0.94, hidden 8192 at 2048 / 4096 / 8192 rows 0.97 / 0.95 /
+// 0.98 (at 1024 rows 1.04: not used there).
+norm_launch_cfg choose_rms_ring(int64_t rows, int64_t hidden) {
+    const bool on = ((hidden == 16384 || hidden == 12288) && rows >= 512) ||
+                    (hidden == 8192 && rows >= 2048);
+    if (!on || !find_fwd(NORM_OP_RMSNORM_FWD, hidden, 512, 1, true))
+        return norm_launch_cfg{0, 0, 0, 0};
+    return norm_launch_cfg{512, 1, (int32_t)std::min<int64_t>(256, rows), 0};
+}
+
 norm_launch_cfg choose_fwd(norm_op op, int64_t rows, int64_t hidden, int cu) {
     if (const norm_launch_cfg t = tuned_fwd(op, rows, hidden, cu); t.threads_per_row) return t;
-    if (op == NORM_OP_LAYERNORM_FWD) {
-        const norm_launch_cfg ring = choose_ln_ring(rows, hidden);
+    if (op == NORM_OP_LAYERNORM_FWD || op == NORM_OP_RMSNORM_FWD) {
+        const norm_launch_cfg ring = op == NORM_OP_LAYERNORM_FWD ? choose_ln_ring(rows, hidden)
+                                                                 : choose_rms_ring(rows, hidden);
         if (ring.threads_per_row) return ring;
     }
     const int64_t target_waves = 4 * (int64_t)cu;
@@ -593,11 +607,13 @@ norm_status check_fwd(norm_op op, const FwdCall& c, FwdLayout* L) {
 
 norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
                     hipStream_t stream) {
-    const bool ln = op == NORM_OP_LAYERNORM_FWD;
+    const bool has_ring = op == NORM_OP_LAYERNORM_FWD || op == NORM_OP_RMSNORM_FWD;
     if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
-    // grid > 0 names a persistent ring shape: LayerNorm's compiled kernels only
+    // grid > 0 names a persistent ring shape: LayerNorm's and RMSNorm's
+    // compiled kernels only
     if (cfg && (cfg->grid < 0 || cfg->grid > kMaxFwdRingGrid ||
-                (cfg->grid > 0 && (!ln || cfg->vector_elems != 0 || cfg->rows_per_block != 1)) ||
+                (cfg->grid > 0 &&
+                 (!has_ring || cfg->vector_elems != 0 || cfg->rows_per_block != 1)) ||
                 cfg->threads_per_row <= 0 || cfg->rows_per_block <= 0 ||
                 !valid_elems(cfg->vector_elems)))
         return NORM_ERROR_INVALID_VALUE;

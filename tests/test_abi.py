@@ -554,10 +554,12 @@ def test_tuned_forward_table():
     hidden, rows) cells, counted on a 256-CU part: entries measured at >= 1024
     rows stop at their row count (their gain needs whole workgroup waves)."""
     sel = lambda op, rows, h, cu=256: rn.select_config(op, rows, h, cu_count=cu)
-    assert sel("rmsnorm_fwd", 1024, 16384) == rn.Cfg(128, 4, 0, 0)
-    assert sel("rmsnorm_fwd", 600, 16384) == rn.Cfg(128, 4, 0, 0)
-    assert sel("rmsnorm_fwd", 1025, 16384) != rn.Cfg(128, 4, 0, 0)   # 257 workgroups
-    assert sel("rmsnorm_fwd", 512, 16384, cu=128) == rn.Cfg(128, 4, 0, 0)  # = 1024 on 256 CUs
+    assert sel("rmsnorm_fwd", 2048, 2048) == rn.Cfg(256, 1, 0, 8)  # a run-time shape
+    assert sel("rmsnorm_fwd", 1500, 2048) == rn.Cfg(256, 1, 0, 8)
+    assert sel("rmsnorm_fwd", 2049, 2048) != rn.Cfg(256, 1, 0, 8)   # past the measured row count
+    assert sel("rmsnorm_fwd", 1024, 2048, cu=128) == rn.Cfg(256, 1, 0, 8)  # = 2048 on 256 CUs
+    assert sel("rmsnorm_fwd", 1024, 16384) == rn.Cfg(512, 1, 256, 0)  # the RMSNorm ring rule
+    assert sel("rmsnorm_fwd", 1024, 8192) != rn.Cfg(512, 1, 256, 0)   # not below 2048 rows there
     assert sel("fused_add_rmsnorm", 64, 4096) == rn.Cfg(512, 1, 0, 8)  # the run-time kernel
     assert sel("fused_add_rmsnorm", 8192, 4096) == rn.Cfg(128, 2, 0, 0)  # the rules
     assert sel("layernorm_fwd", 64, 8192) == rn.Cfg(256, 1, 0, 0)

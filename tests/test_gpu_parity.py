@@ -110,6 +110,34 @@ def test_rmsnorm_config(hidden, rows):
     check_rms(wl.rmsnorm_inputs(rows, hidden, seed=0), what=f"rmsnorm {rows}x{hidden}")
 
 
+@pytest.mark.parametrize("hidden", [8192, 12288, 16384])
+def test_rmsnorm_fwd_ring_shapes_and_grids(hidden):
+    """The RMSNorm persistent ring kernels: every compiled lane count, one
+    workgroup, walks of 11, 8, 4 and 3 rows (75 rows over 7, 10, 19 or 37
+    workgroups: every compiled ring depth, full and partial ring steps), idle
+    workgroups (300 > rows); in place too.  Outlier channels as in the RMSNorm
+    workload."""
+    inp = wl.rmsnorm_inputs(75, hidden, seed=16)
+    rings = [c for c in rn.list_configs("rmsnorm_fwd", hidden) if c.grid > 0]
+    assert rings
+    assert len({c.threads_per_row for c in rings}) == len(rings)
+    for c in rings:
+        for grid in (1, 7, 10, 19, 37, 300):
+            cfg = rn.Cfg(c.threads_per_row, 1, grid, 0)
+            check_rms(inp, cfg=cfg, what=f"rmsnorm ring h={hidden} {cfg}")
+        check_rms(inp, cfg=rn.Cfg(c.threads_per_row, 1, 7, 0), in_place=True,
+                  what=f"rmsnorm ring h={hidden} lanes={c.threads_per_row} in place")
+
+
+@pytest.mark.parametrize("rows,hidden", [(1024, 16384), (2048, 12288), (4096, 8192),
+                                         (1100, 16384)])
+def test_rmsnorm_fwd_ring_in_library_choice(rows, hidden):
+    """Sizes where the library picks the RMSNorm ring kernel by itself."""
+    assert rn.select_config("rmsnorm_fwd", rows, hidden).grid > 0
+    assert "rmsnorm_fwd_ring_kernel" in rn.describe_config("rmsnorm_fwd", rows, hidden)
+    check_rms(wl.rmsnorm_inputs(rows, hidden, seed=17), what=f"rmsnorm ring {rows}x{hidden}")
+
+
 @pytest.mark.parametrize("hidden", rn.HIDDEN_SIZES)
 def test_rmsnorm_every_compiled_shape(hidden):
     inp = wl.rmsnorm_inputs(37, hidden, seed=3)
