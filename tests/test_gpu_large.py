@@ -136,6 +136,24 @@ def test_rmsnorm_fwd_past_4gib():
     free()
 
 
+def test_rmsnorm_fwd_ring_past_4gib():
+    """hidden 16384 (the persistent ring kernel, deepest ring): 4 GiB + 5 rows."""
+    h = 16384
+    rows = rows_past_4gib(h, 5)
+    idx = sample_rows(rows, 2 * h, seed=8)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=801)
+    w_bits, w = weight(h, 802)
+    assert "rmsnorm_fwd_ring_kernel" in rn.describe_config("rmsnorm_fwd", rows, h)
+    out = nan_like(x)
+    rn.rmsnorm_fwd(x, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.rmsnorm_fwd(take(x, idx), w_bits, wl.EPS_RMS, NT)
+    P.assert_bf16_close(take(out, idx), ref, "rmsnorm ring past 4 GiB")
+    assert_all_finite(out, "rmsnorm ring past 4 GiB")
+    del x, out
+    free()
+
+
 def test_rmsnorm_fwd_column_slice_past_4gib():
     """In place on the first 128 columns of a [rows, 384] matrix of 4 GiB + 5
     rows (narrow rows share one buffer descriptor per set of rows)."""
