@@ -25,9 +25,9 @@ def bits(t):
     return t.detach().contiguous().view(torch.int16).cpu().numpy().copy()
 
 
-@pytest.mark.parametrize("hidden", [4096, 5120, 100])
-def test_graph_replays_match_eager(hidden):
-    rows = 300
+@pytest.mark.parametrize("hidden,rows", [(4096, 300), (5120, 300), (100, 300), (16384, 600)])
+def test_graph_replays_match_eager(hidden, rows):
+    """(16384, 600): LayerNorm and RMSNorm forward on their ring kernels."""
     f = wl.fused_inputs(rows, hidden, seed=31)
     b = wl.rmsnorm_bwd_inputs(rows, hidden, seed=32)
     lnw = wl.layernorm_fwd_inputs(rows, hidden, seed=33)
@@ -36,6 +36,7 @@ def test_graph_replays_match_eager(hidden):
     xl, wl_, bl = dev(lnw["x"]), dev(lnw["w"]), dev(lnw["b"])
     res = torch.empty_like(r0)
     out, ds, y = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    yr = torch.empty_like(x)
     dxl = torch.empty_like(x)
     mean = torch.empty(rows, device=DEV)
     rstd = torch.empty(rows, device=DEV)
@@ -51,10 +52,11 @@ def test_graph_replays_match_eager(hidden):
         rn.fused_add_rmsnorm_bwd(dy, xb, wb, b["eps"], dres=dres, ds=ds, dweight=dw1,
                                  workspace=ws1, stream=stream)
         rn.layernorm_fwd(xl, wl_, bl, lnw["eps"], y=y, mean=mean, rstd=rstd, stream=stream)
+        rn.rmsnorm_fwd(xl, wl_, f["eps"], out=yr, stream=stream)
         rn.layernorm_bwd(dy, xl, mean, rstd, wl_, dx=dxl, dweight=dw2, dbias=db2,
                          workspace=ws2, stream=stream)
 
-    outputs = (out, res, ds, dw1, y, mean, rstd, dxl, dw2, db2)
+    outputs = (out, res, ds, dw1, y, mean, rstd, yr, dxl, dw2, db2)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         step(s)
