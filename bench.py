@@ -512,9 +512,14 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     return out
 
 
+_CEILING = []
+
+
 def _ceiling_fn():
     """normceil_same_traffic_h4096 from libnormceiling.so (built with the
-    package), or None when it was not built."""
+    package), or None when it was not built.  Loaded once."""
+    if _CEILING:
+        return _CEILING[0]
     import ctypes
     import row_normalization_persistent_amd as rn
     path = os.path.join(os.path.dirname(os.path.abspath(rn.__file__)), "libnormceiling.so")
@@ -524,6 +529,7 @@ def _ceiling_fn():
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     f.restype = ctypes.c_int
+    _CEILING.append(f)
     return f
 
 
