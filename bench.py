@@ -59,6 +59,7 @@ HBM_PEAK_GBPS = 8000.0
 HIDDEN = 4096
 SWEEP_ROWS = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192)
 N_SETS = 3  # 3 x 402 MB of x/residual/out buffers: no step reuses cached data
+MIN_GRAPH_LAUNCHES = 18  # per-instantiation timing graphs hold at least this many launches
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
 
@@ -202,16 +203,19 @@ def main():
         g["bytes"] += fused_bytes(SWEEP_ROWS[i])
     def group_us_per_step(launch_fn, idx):
         """One graph walks the launches `idx` of a step over all buffer sets
-        in turn (each replay is N_SETS steps' worth, so the per-replay cost is
-        spread over N_SETS * len(idx) kernels), replayed about K steps' worth
-        between two events on the launch stream: GPU time per step."""
+        in turn, repeated until it holds at least MIN_GRAPH_LAUNCHES launches
+        (so every group's per-replay cost is spread about as thinly), replayed
+        about K steps' worth between two events on the launch stream: GPU
+        time per step."""
+        copies = max(1, -(-MIN_GRAPH_LAUNCHES // (N_SETS * len(idx))))
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             cg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(cg, stream=stream):
-                for k in range(N_SETS):
-                    for i in idx:
-                        launch_fn(sets[k], i)
+                for _ in range(copies):
+                    for k in range(N_SETS):
+                        for i in idx:
+                            launch_fn(sets[k], i)
             cg.replay()
         reps = max(1, args.steps // N_SETS)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -224,7 +228,7 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         del cg
-        return e0.elapsed_time(e1) * 1e3 / (reps * N_SETS)
+        return e0.elapsed_time(e1) * 1e3 / (reps * N_SETS * copies)
 
     for key, g in groups.items():
         g["us_per_step"] = group_us_per_step(launch, g["idx"])
