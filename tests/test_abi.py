@@ -299,6 +299,14 @@ def test_layernorm_fwd_validation():
     assert ring(rn.LaunchCfg(128, 1, 4, 0)) == INVALID   # no ring kernel at hidden 1024
     assert ring(rn.LaunchCfg(128, 2, 4, 0)) == INVALID   # ring shapes hold one row a group
     assert ring(rn.LaunchCfg(128, 1, 4, 8)) == INVALID   # rings are compiled-hidden only
+    rms_ring = lambda c, h: L.norm_rmsnorm_fwd_cfg(A, A + 2 * GB, A + 4 * GB, 4, h, 1e-6,
+                                                   ctypes.byref(c), None)
+    assert rms_ring(rn.LaunchCfg(512, 1, 4, 0), 2048) == INVALID   # RMSNorm rings from 8192 only
+    assert rms_ring(rn.LaunchCfg(64, 1, 4, 0), 16384) == INVALID   # no ring of 64 lanes there
+    assert rms_ring(rn.LaunchCfg(512, 2, 4, 0), 16384) == INVALID  # one row a group
+    fused_ring = lambda c: L.norm_fused_add_rmsnorm_cfg(A, A + 2 * GB, A + 4 * GB, A + 6 * GB, 4,
+                                                        16384, 1e-6, ctypes.byref(c), None)
+    assert fused_ring(rn.LaunchCfg(512, 1, 4, 0)) == INVALID      # the fused op has no ring
 
 
 GB = 1 << 30
