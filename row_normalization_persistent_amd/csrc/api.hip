@@ -143,12 +143,12 @@ const FwdEntry* find_fwd(norm_op op, int64_t hidden, int lanes, int rpb, bool ri
     return nullptr;
 }
 
-// The ring kernel (LayerNorm or RMSNorm) a call runs: the shallowest compiled depth that
-// holds a workgroup's whole walk (ceil(rows / grid) rows), else the deepest
-// compiled.  Measured on MI355X (2048 rows at hidden 8192 / 12288 / 16384,
-// one workgroup per CU): loading the whole walk at once beats a shallower
-// ring by 6-16 %; with walks longer than the deepest ring the depths are
-// within 1-2 % of each other.
+// The ring kernel (LayerNorm or RMSNorm) a call runs: the shallowest compiled
+// depth that holds a workgroup's whole walk (ceil(rows / grid) rows), else the
+// deepest compiled.  Measured on MI355X (2048 rows at hidden 8192 / 12288 /
+// 16384, one workgroup per CU): loading the whole walk at once beats a
+// shallower ring by 6-16 %; with walks longer than the deepest ring the depths
+// are within 1-2 % of each other.
 const FwdEntry* ring_entry(norm_op op, int64_t hidden, int lanes, int64_t rows, int64_t grid) {
     const int64_t walk = grid > 0 ? std::max<int64_t>(1, (rows + grid - 1) / grid) : 1;
     const FwdEntry *fit = nullptr, *deepest = nullptr;
