@@ -156,6 +156,30 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
         assert rn.select_config("layernorm_bwd", 5, h).grid == 5
 
 
+def test_ring_depth_follows_the_walk():
+    """The ring kernels (LayerNorm, RMSNorm forward) run the shallowest compiled
+    depth that holds a workgroup's walk, ceil(rows / grid) rows, else the
+    deepest; the same rows and grid always give the same kernel."""
+    import re
+
+    def depth(op, rows, h, cfg=None):
+        d = rn.describe_config(op, rows, h, cu_count=256)
+        m = re.search(r"ring of (\d+) rows", d)
+        return int(m.group(1)) if m else None
+
+    for op in ("layernorm_fwd", "rmsnorm_fwd"):
+        # 256 workgroups: walks of 2, 3, 4, 8, 9, 32 rows
+        assert depth(op, 512, 16384) == 2
+        assert depth(op, 513, 16384) == 4
+        assert depth(op, 1024, 16384) == 4
+        assert depth(op, 2048, 16384) == 8
+        assert depth(op, 2049, 16384) == 8   # past the deepest ring: the deepest
+        assert depth(op, 8192, 16384) == 8
+        assert depth(op, 1024, 12288) == 4
+    assert depth("layernorm_fwd", 8192, 4096) == 2   # 64 lanes hold only depth 2
+    assert depth("rmsnorm_fwd", 1024, 8192) is None  # not a ring below 2048 rows there
+
+
 def test_describe_config():
     d = rn.describe_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)
     c = rn.select_config("fused_add_rmsnorm", 8192, 4096, cu_count=256)

@@ -113,8 +113,9 @@ def test_rmsnorm_config(hidden, rows):
 @pytest.mark.parametrize("hidden", [8192, 12288, 16384])
 def test_rmsnorm_fwd_ring_shapes_and_grids(hidden):
     """The RMSNorm persistent ring kernels: every compiled lane count, one
-    workgroup, walks of 11, 8, 4 and 3 rows (75 rows over 7, 10, 19 or 37
-    workgroups: every compiled ring depth, full and partial ring steps), idle
+    workgroup, walks of 11, 8, 5, 4, 3 and 2 rows (75 rows over 7, 10, 15, 19,
+    37 or 38 workgroups: every compiled ring depth, full and partial ring
+    steps), idle
     workgroups (300 > rows); in place too.  Outlier channels as in the RMSNorm
     workload."""
     inp = wl.rmsnorm_inputs(75, hidden, seed=16)
@@ -122,7 +123,7 @@ def test_rmsnorm_fwd_ring_shapes_and_grids(hidden):
     assert rings
     assert len({c.threads_per_row for c in rings}) == len(rings)
     for c in rings:
-        for grid in (1, 7, 10, 19, 37, 300):
+        for grid in (1, 7, 10, 15, 19, 37, 38, 300):
             cfg = rn.Cfg(c.threads_per_row, 1, grid, 0)
             check_rms(inp, cfg=cfg, what=f"rmsnorm ring h={hidden} {cfg}")
         check_rms(inp, cfg=rn.Cfg(c.threads_per_row, 1, 7, 0), in_place=True,
@@ -179,15 +180,15 @@ def test_layernorm_fwd_every_compiled_shape(hidden):
 @pytest.mark.parametrize("hidden", [2048, 4096, 8192, 12288, 16384])
 def test_layernorm_fwd_ring_shapes_and_grids(hidden):
     """The persistent ring kernels: every compiled lane count, grids of one
-    workgroup, ragged walks (75 rows over 7, 10, 19 or 37 workgroups: walks of
-    11, 8, 4 and 3 rows, so every compiled ring depth runs, with full and
-    partial ring steps) and idle workgroups (300 > rows); in place too."""
+    workgroup, ragged walks (75 rows over 7, 10, 15, 19, 37 or 38 workgroups:
+    walks of 11, 8, 5, 4, 3 and 2 rows, so every compiled ring depth runs, with
+    full and partial ring steps) and idle workgroups (300 > rows); in place too."""
     inp = wl.layernorm_fwd_inputs(75, hidden, seed=14)
     rings = [c for c in rn.list_configs("layernorm_fwd", hidden) if c.grid > 0]
     assert rings
     assert len({c.threads_per_row for c in rings}) == len(rings)  # one entry per lane count
     for c in rings:
-        for grid in (1, 7, 10, 19, 37, 300):
+        for grid in (1, 7, 10, 15, 19, 37, 38, 300):
             cfg = rn.Cfg(c.threads_per_row, 1, grid, 0)
             check_lnf(inp, cfg=cfg, what=f"layernorm ring h={hidden} {cfg}")
         check_lnf(inp, cfg=c, what=f"layernorm ring h={hidden} no stats", with_stats=False)
