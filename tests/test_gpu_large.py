@@ -22,6 +22,18 @@ from row_normalization_persistent_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+# The largest case holds about 20 GiB at once (three or four 4 GiB matrices
+# and fp64 column-sum chunks).
+NEED_BYTES = 24 << 30
+
+
+@pytest.fixture(autouse=True)
+def _enough_device_memory():
+    total = torch.cuda.get_device_properties(0).total_memory
+    if total < NEED_BYTES:
+        pytest.skip(f"needs {NEED_BYTES >> 30} GiB of device memory, the device has "
+                    f"{total >> 30} GiB")
+
 NT = min(16, os.cpu_count() or 1)
 DEV = "cuda"
 GIB4 = 1 << 32
