@@ -1,0 +1,59 @@
+"""Seeded randomized parity sweep: random (operation, rows, hidden) cases, each
+through the library's own launch choice, against the oracle with the rules of
+parity.py.  The draw favours the places where the choice logic branches:
+compiled and run-time hidden sizes, the ring kernels' row ranges (ragged
+walks over 256 workgroups), the table's row buckets and narrow rows.  The
+case list is fixed by the seed, so a failure names a reproducible case."""
+import numpy as np
+import pytest
+
+import test_gpu_parity as TP
+import test_gpu_rmsnorm_bwd as TR
+from row_normalization_persistent_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+COMPILED = (1024, 2048, 4096, 8192, 12288, 16384)
+RUNTIME = (8, 96, 264, 1000, 3080, 5120, 6144, 7168, 9000)
+OPS = ("fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd", "layernorm_bwd", "rmsnorm_bwd",
+       "fused_add_rmsnorm_bwd")
+MAX_ELEMS = 18 << 20  # keeps each case's oracle pass short
+
+
+def _cases(n=48, seed=20240611):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        op = OPS[k % len(OPS)]
+        if op in ("rmsnorm_fwd", "layernorm_fwd") and rng.random() < 0.5:
+            # the ring kernels' ranges: ragged walks over 256 workgroups
+            h = int(rng.choice((8192, 12288, 16384)))
+            lo = 2048 if (op == "rmsnorm_fwd" and h == 8192) else 512
+            rows = int(rng.integers(lo, lo + 600))
+        else:
+            h = int(rng.choice(COMPILED)) if rng.random() < 0.6 else int(rng.choice(RUNTIME))
+            rows = int(np.exp(rng.uniform(0.0, np.log(3000.0))))
+        rows = max(1, min(rows, MAX_ELEMS // h))
+        out.append((op, rows, h, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("op,rows,hidden,seed", CASES,
+                         ids=[f"{o}-{r}x{h}" for o, r, h, _ in CASES])
+def test_random_case(op, rows, hidden, seed):
+    what = f"random {op} {rows}x{hidden} seed {seed}"
+    if op == "fused_add_rmsnorm":
+        TP.check_fused(wl.fused_inputs(rows, hidden, seed=seed), what=what)
+    elif op == "rmsnorm_fwd":
+        TP.check_rms(wl.rmsnorm_inputs(rows, hidden, seed=seed), what=what)
+    elif op == "layernorm_fwd":
+        TP.check_lnf(wl.layernorm_fwd_inputs(rows, hidden, seed=seed), what=what)
+    elif op == "layernorm_bwd":
+        TP.check_lnb(TP.lnb_inputs(rows, hidden, seed=seed), what=what)
+    elif op == "rmsnorm_bwd":
+        TR.check(wl.rmsnorm_bwd_inputs(rows, hidden, seed=seed), fused=False, what=what)
+    else:
+        TR.check(wl.rmsnorm_bwd_inputs(rows, hidden, seed=seed), fused=True, what=what)
