@@ -259,15 +259,17 @@ int pointer_width(std::initializer_list<const void*> ptrs) {
 //    per-lane buffers plus the weight/bias vectors cost occupancy), and from
 //    4096 rows up the RMS kernels run best at 4 vectors per lane.
 //  * Rows per workgroup: 4 for one-wave rows, 2 for two-wave rows, else 1.
-// LayerNorm forward from 512 rows (4096 at hidden 4096) runs on the persistent
-// ring kernel (measured on MI355X, 2048 rows: 6-8 % faster at hidden 8192-16384
-// with a fixed ring depth, 12-16 % with the depth picked per walk; below those
-// row counts the launch is latency-bound and the plain kernels win): lanes and
-// grid per hidden size from the same sweeps (512 lanes beat 1024 at hidden
-// 16384 and 256 at 12288 by 2-10 % at 512-8192 rows).
+// LayerNorm forward from 512 rows (320 at hidden 16384, 4096 at hidden 4096)
+// runs on the persistent ring kernel (measured on MI355X, 2048 rows: 6-8 %
+// faster at hidden 8192-16384 with a fixed ring depth, 12-16 % with the depth
+// picked per walk; at 384 / 511 rows of hidden 16384 0.97 / 0.94 of the plain
+// kernel's time, but 1.05-1.09 at hidden 8192 and 12288; with walks of one row
+// the launch is latency-bound and the plain kernels win): lanes and grid per
+// hidden size from the same sweeps (512 lanes beat 1024 at hidden 16384 and
+// 256 at 12288 by 2-10 % at 512-8192 rows).
 norm_launch_cfg choose_ln_ring(int64_t rows, int64_t hidden) {
     int lanes = 0, grid = 0;
-    if (hidden == 16384 && rows >= 512) lanes = 512, grid = 256;
+    if (hidden == 16384 && rows >= 320) lanes = 512, grid = 256;
     if (hidden == 12288 && rows >= 512) lanes = 512, grid = 256;
     if (hidden == 8192 && rows >= 512) lanes = 512, grid = 256;
     if (hidden == 4096 && rows >= 4096) lanes = 64, grid = 1024;
@@ -402,15 +404,17 @@ bool late_weights_dyn(int64_t groups, int lanes, int cu) {
 }
 
 // RMSNorm forward on the persistent ring kernel: 512 lanes, 256 workgroups,
-// from 512 rows at hidden 12288 and 16384 and from 2048 rows at hidden 8192.
-// Measured on MI355X against the one-row-per-lane-group choice (ring depth
-// picked per walk): hidden 16384 at 512 / 1024 / 2048 / 4096 / 8192 rows 0.82 /
-// 0.90 / 0.88 / 0.94 / 0.99 of its time, hidden 12288 at 1024 / 2048 / 4096
-// rows 0.89 / 0.85 / 0.94, hidden 8192 at 2048 / 4096 / 8192 rows 0.97 / 0.95 /
-// 0.98 (at 1024 rows 1.04: not used there).
+// from 320 rows at hidden 12288 and 16384; at hidden 8192 for 320-511 rows
+// and from 2048 rows.  Measured on MI355X against the one-row-per-lane-group
+// choice (ring depth picked per walk): hidden 16384 at 384 / 512 / 1024 / 2048
+// / 4096 / 8192 rows 0.85 / 0.82 / 0.90 / 0.88 / 0.94 / 0.99 of its time,
+// hidden 12288 at 384 / 1024 / 2048 / 4096 rows 0.87 / 0.89 / 0.85 / 0.94,
+// hidden 8192 at 384 / 511 / 2048 / 4096 / 8192 rows 0.95 / 0.90 / 0.97 / 0.95
+// / 0.98 (at 1024 rows 1.04, where the late-weights kernel runs; at 256 rows
+// and fewer, a walk of one row, 1.14-1.21).
 norm_launch_cfg choose_rms_ring(int64_t rows, int64_t hidden) {
-    const bool on = ((hidden == 16384 || hidden == 12288) && rows >= 512) ||
-                    (hidden == 8192 && rows >= 2048);
+    const bool on = ((hidden == 16384 || hidden == 12288) && rows >= 320) ||
+                    (hidden == 8192 && ((rows >= 320 && rows < 512) || rows >= 2048));
     if (!on || !find_fwd(NORM_OP_RMSNORM_FWD, hidden, 512, 1, true))
         return norm_launch_cfg{0, 0, 0, 0};
     return norm_launch_cfg{512, 1, (int32_t)std::min<int64_t>(256, rows), 0};
