@@ -138,7 +138,7 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
                 # at most 8 vectors per lane by the rules, 16 (the compiled cap)
                 # for shapes from the measured table
                 assert h // (8 * c.threads_per_row) <= 16
-    # LayerNorm forward: the persistent ring kernel from 512 rows at hidden >= 8192
+    # LayerNorm forward: the persistent ring kernel at hidden >= 8192 for large batches
     for h, rows in ((16384, 2048), (12288, 2048), (8192, 8192), (4096, 8192)):
         c = rn.select_config("layernorm_fwd", rows, h, cu_count=256)
         assert c.grid > 0 and c.rows_per_block == 1, (h, rows, c)
@@ -149,6 +149,17 @@ def test_select_config_small_batches_spread_rows_over_more_lanes():
     for h, rows in ((16384, 256), (4096, 2048), (2048, 8192), (1024, 8192)):
         assert rn.select_config("layernorm_fwd", rows, h, cu_count=256).grid == 0
     assert rn.select_config("layernorm_fwd", 600, 16384, cu_count=256).grid == 256
+    # the switches where walks of two rows start to win: 320 rows (LayerNorm at
+    # hidden 16384; RMSNorm at 12288 and 16384, and at 8192 up to 511 rows, then
+    # again from 2048)
+    sel = lambda op, rows, h: rn.select_config(op, rows, h, cu_count=256).grid
+    assert sel("layernorm_fwd", 319, 16384) == 0 and sel("layernorm_fwd", 320, 16384) == 256
+    assert sel("layernorm_fwd", 320, 12288) == 0 and sel("layernorm_fwd", 320, 8192) == 0
+    for h in (16384, 12288):
+        assert sel("rmsnorm_fwd", 319, h) == 0 and sel("rmsnorm_fwd", 320, h) == 256
+    assert sel("rmsnorm_fwd", 319, 8192) == 0 and sel("rmsnorm_fwd", 320, 8192) == 256
+    assert sel("rmsnorm_fwd", 511, 8192) == 256 and sel("rmsnorm_fwd", 512, 8192) == 0
+    assert sel("rmsnorm_fwd", 2047, 8192) == 0 and sel("rmsnorm_fwd", 2048, 8192) == 256
     for h in rn.HIDDEN_SIZES:
         c = rn.select_config("layernorm_bwd", 8192, h)
         assert rn.Cfg(c.threads_per_row, 1, 0, 0) in rn.list_configs("layernorm_bwd", h)
@@ -177,7 +188,9 @@ def test_ring_depth_follows_the_walk():
         assert depth(op, 8192, 16384) == 8
         assert depth(op, 1024, 12288) == 4
     assert depth("layernorm_fwd", 8192, 4096) == 2   # 64 lanes hold only depth 2
-    assert depth("rmsnorm_fwd", 1024, 8192) is None  # not a ring below 2048 rows there
+    assert depth("rmsnorm_fwd", 1024, 8192) is None  # not a ring for 512-2047 rows there
+    assert depth("rmsnorm_fwd", 400, 8192) == 2
+    assert depth("layernorm_fwd", 320, 16384) == 2
 
 
 def test_describe_config():

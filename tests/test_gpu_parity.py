@@ -131,7 +131,8 @@ def test_rmsnorm_fwd_ring_shapes_and_grids(hidden):
 
 
 @pytest.mark.parametrize("rows,hidden", [(1024, 16384), (2048, 12288), (4096, 8192),
-                                         (1100, 16384)])
+                                         (1100, 16384), (320, 16384), (401, 12288),
+                                         (511, 8192)])
 def test_rmsnorm_fwd_ring_in_library_choice(rows, hidden):
     """Sizes where the library picks the RMSNorm ring kernel by itself."""
     assert rn.select_config("rmsnorm_fwd", rows, hidden).grid > 0
@@ -203,7 +204,8 @@ def test_layernorm_fwd_ring_shapes_and_grids(hidden):
     P.assert_bf16_close(host(x), ref, "layernorm ring in place", floor_scale=scale)
 
 
-@pytest.mark.parametrize("rows,hidden", [(2048, 16384), (1100, 12288), (8192, 4096)])
+@pytest.mark.parametrize("rows,hidden", [(2048, 16384), (1100, 12288), (8192, 4096),
+                                         (320, 16384), (479, 16384)])
 def test_layernorm_fwd_ring_in_library_choice(rows, hidden):
     """Sizes where the library picks the ring kernel by itself."""
     assert rn.select_config("layernorm_fwd", rows, hidden).grid > 0

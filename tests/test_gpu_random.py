@@ -26,10 +26,10 @@ def _cases(n=48, seed=20240611):
     for k in range(n):
         op = OPS[k % len(OPS)]
         if op in ("rmsnorm_fwd", "layernorm_fwd") and rng.random() < 0.5:
-            # the ring kernels' ranges: ragged walks over 256 workgroups
+            # around and inside the ring kernels' ranges: walks of one to eleven
+            # rows over 256 workgroups, ragged, across the 320/512/2048-row switches
             h = int(rng.choice((8192, 12288, 16384)))
-            lo = 2048 if (op == "rmsnorm_fwd" and h == 8192) else 512
-            rows = int(rng.integers(lo, lo + 600))
+            rows = int(rng.integers(250, 560) if rng.random() < 0.5 else rng.integers(560, 2800))
         else:
             h = int(rng.choice(COMPILED)) if rng.random() < 0.6 else int(rng.choice(RUNTIME))
             rows = int(np.exp(rng.uniform(0.0, np.log(3000.0))))
