@@ -48,7 +48,9 @@
  *   any HIP call, in this order: rows < 0 / bad eps / bad config ->
  *   INVALID_VALUE; then, for the forward ops, rows == 0 -> SUCCESS with
  *   nothing enqueued; hidden < 1 or beyond every kernel -> UNSUPPORTED_HIDDEN;
- *   null pointer or ld < hidden -> INVALID_VALUE; misaligned pointer ->
+ *   null pointer, ld < hidden, ld > 2^40 or a matrix spanning more than
+ *   2^47 bytes ((rows - 1) * ld + hidden elements) -> INVALID_VALUE;
+ *   misaligned pointer ->
  *   MISALIGNED; buffers that overlap other than by an allowed exact alias ->
  *   INVALID_VALUE (two matrices with the same ld whose rows interleave
  *   without sharing an element, such as two column slices of one wider

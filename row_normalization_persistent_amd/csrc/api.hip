@@ -40,6 +40,16 @@ constexpr int64_t kMaxHidden = 65536;
 
 bool valid_elems(int32_t w) { return w == 0 || w == 1 || w == 2 || w == 4 || w == 8; }
 
+// A strided matrix may span at most 2^47 bytes, far past any device
+// allocation: with it, (rows - 1) * ld + cols and every row offset a kernel
+// forms stay inside int64.  `ld` >= 1.
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 47;
+bool span_ok(int64_t rows, int64_t ld, int64_t cols, int elem) {
+    if (rows <= 0) return true;
+    const int64_t lim = kMaxSpanBytes / elem;  // elements
+    return cols <= lim && rows - 1 <= (lim - cols) / ld;
+}
+
 // ---- memory regions and overlap ---------------------------------------------------
 // A [rows, cols] matrix of `elem`-byte values whose rows start `ld` elements
 // apart (a vector is one row).
@@ -578,7 +588,8 @@ norm_status check_fwd(norm_op op, const FwdCall& c, FwdLayout* L) {
     if (ln && ((c.mean == nullptr) != (c.rstd == nullptr))) return NORM_ERROR_INVALID_VALUE;
     const int64_t ld_res = fused ? c.ld_res : c.hidden;
     for (int64_t ld : {c.ld_out, c.ld_x, ld_res})
-        if (ld < c.hidden || ld > kMaxLd) return NORM_ERROR_INVALID_VALUE;
+        if (ld < c.hidden || ld > kMaxLd || !span_ok(c.rows, ld, c.hidden, 2))
+            return NORM_ERROR_INVALID_VALUE;
     if (!aligned(c.out, 2) || !aligned(c.x, 2) || !aligned(c.weight, 2) ||
         (fused && !aligned(c.residual, 2)) || (ln && !aligned(c.bias, 2)) ||
         (ln && c.mean && (!aligned(c.mean, 4) || !aligned(c.rstd, 4))))
@@ -858,7 +869,8 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         return NORM_ERROR_INVALID_VALUE;
     const int64_t ld_dres = c.dres ? c.ld_dres : c.hidden;
     for (int64_t ld : {c.ld_dx, c.ld_dy, c.ld_x, ld_dres})
-        if (ld < c.hidden || ld > kMaxLd) return NORM_ERROR_INVALID_VALUE;
+        if (ld < c.hidden || ld > kMaxLd || !span_ok(c.rows, ld, c.hidden, 2))
+            return NORM_ERROR_INVALID_VALUE;
     if (!aligned(c.dweight, 4) || (ln && !aligned(c.dbias, 4)) || !aligned(c.workspace, 16))
         return NORM_ERROR_MISALIGNED;
     if (any && (!aligned(c.dx, 2) || !aligned(c.dy, 2) || !aligned(c.x, 2) ||

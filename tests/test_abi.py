@@ -440,6 +440,10 @@ def test_strided_validation():
     assert rmsb_ex() == WORKSPACE
     assert rmsb_ex(ld_x=4095) == INVALID           # ld < hidden
     assert rmsb_ex(ld_x=1 << 41) == INVALID        # absurd stride
+    # a legal stride whose span over all rows passes 2^47 bytes (offsets would
+    # leave int64 long before an address could be that far)
+    assert rmsb_ex(ld_x=1 << 40, rows=(1 << 31) - 1) == INVALID
+    assert rmsb_ex(x=A + 7 * GB, ld_x=1 << 40, rows=64) == WORKSPACE  # just inside
     assert rmsb_ex(ld_x=3 * 4096) == WORKSPACE     # a column slice of a wider matrix
     # dx and dy as two column slices of one [rows, 2 * hidden] matrix: their rows
     # interleave without sharing an element
@@ -459,6 +463,8 @@ def test_strided_validation():
                                  None) == INVALID
     assert L.norm_rmsnorm_fwd_ex(A, 4000, A + GB, 4096, A + 2 * GB, 4, 4096, 1e-6, None,
                                  None) == INVALID
+    assert L.norm_rmsnorm_fwd_ex(A, 4096, A + GB, 1 << 40, A + 2 * GB, (1 << 31) - 1, 4096,
+                                 1e-6, None, None) == INVALID  # x spans past 2^47 bytes
     assert L.norm_fused_add_rmsnorm_ex(A, 4096, A + GB, 4096, A + 2 * GB, 4096, A + 3 * GB, 4,
                                        70000, 1e-6, None, None) == UNSUPPORTED
     assert L.norm_layernorm_fwd_ex(A, 4096, None, None, A + GB, 4095, A + 2 * GB, A + 3 * GB, 4,
