@@ -198,10 +198,17 @@ _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 _current_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
-def _stream(stream) -> int:
+def _stream(stream, *tensors) -> int:
+    """The stream handle to launch on.  The library launches on the current
+    HIP device, so every tensor of the call must live there."""
+    cur = _current_device() if _current_device is not None else torch.cuda.current_device()
+    for t in tensors:
+        if t is not None and t.get_device() != cur:
+            raise ValueError(f"every tensor must be on the current device cuda:{cur}; "
+                             f"got one on {t.device}")
     if stream is None:
-        if _raw_stream is not None and _current_device is not None:
-            return _raw_stream(_current_device())
+        if _raw_stream is not None:
+            return _raw_stream(cur)
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -314,7 +321,8 @@ def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, strea
         _check(lib().norm_fused_add_rmsnorm_split(out.data_ptr(), residual.data_ptr(),
                                                   x.data_ptr(), weight.data_ptr(), rows, hidden,
                                                   float(eps), wp, wb, int(split or 0),
-                                                  _stream(stream)),
+                                                  _stream(stream, x, residual, weight, out,
+                                                          workspace)),
                "norm_fused_add_rmsnorm_split")
         return out, residual
     rows, hidden, ld_x = _rows(x, "x")
@@ -326,7 +334,8 @@ def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, strea
     _, _, ld_o = _rows(out, "out")
     _check(lib().norm_fused_add_rmsnorm_ex(out.data_ptr(), ld_o, residual.data_ptr(), ld_r,
                                            x.data_ptr(), ld_x, weight.data_ptr(), rows, hidden,
-                                           float(eps), _cfg_ptr(cfg), _stream(stream)),
+                                           float(eps), _cfg_ptr(cfg),
+                                           _stream(stream, x, residual, weight, out)),
            "norm_fused_add_rmsnorm")
     return out, residual
 
@@ -343,7 +352,7 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspac
         wp, wb = _split_ws(workspace)
         _check(lib().norm_rmsnorm_fwd_split(out.data_ptr(), x.data_ptr(), weight.data_ptr(),
                                             rows, hidden, float(eps), wp, wb, int(split or 0),
-                                            _stream(stream)),
+                                            _stream(stream, x, weight, out, workspace)),
                "norm_rmsnorm_fwd_split")
         return out
     rows, hidden, ld_x = _rows(x, "x")
@@ -351,7 +360,8 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspac
     out = _like(x, out, "out")
     _, _, ld_o = _rows(out, "out")
     _check(lib().norm_rmsnorm_fwd_ex(out.data_ptr(), ld_o, x.data_ptr(), ld_x, weight.data_ptr(),
-                                     rows, hidden, float(eps), _cfg_ptr(cfg), _stream(stream)),
+                                     rows, hidden, float(eps), _cfg_ptr(cfg),
+                                     _stream(stream, x, weight, out)),
            "norm_rmsnorm_fwd")
     return out
 
@@ -387,12 +397,14 @@ def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
         _check(lib().norm_layernorm_fwd_split(y.data_ptr(), mp, rp, x.data_ptr(),
                                               weight.data_ptr(), bias.data_ptr(), rows, hidden,
                                               float(eps), wp, wb, int(split or 0),
-                                              _stream(stream)),
+                                              _stream(stream, x, weight, bias, y, mean, rstd,
+                                                      workspace)),
                "norm_layernorm_fwd_split")
         return y, mean, rstd
     _check(lib().norm_layernorm_fwd_ex(y.data_ptr(), ld_y, mp, rp, x.data_ptr(), ld_x,
                                        weight.data_ptr(), bias.data_ptr(), rows, hidden,
-                                       float(eps), _cfg_ptr(cfg), _stream(stream)),
+                                       float(eps), _cfg_ptr(cfg),
+                                       _stream(stream, x, weight, bias, y, mean, rstd)),
            "norm_layernorm_fwd")
     return y, mean, rstd
 
@@ -446,7 +458,9 @@ def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=
                                        dbias.data_ptr(), dy.data_ptr(), ld_dy, x.data_ptr(), ld_x,
                                        mean.data_ptr(), rstd.data_ptr(), weight.data_ptr(),
                                        workspace.data_ptr(), wsb, rows, hidden, float(eps),
-                                       _cfg_ptr(cfg), _stream(stream)),
+                                       _cfg_ptr(cfg),
+                                       _stream(stream, dy, x, mean, rstd, weight, dx, dweight,
+                                               dbias, workspace)),
            "norm_layernorm_bwd")
     return dx, dweight, dbias
 
@@ -459,7 +473,8 @@ def rmsnorm_bwd(dy, x, weight, eps: float, dx=None, dweight=None, workspace=None
     _check(lib().norm_rmsnorm_bwd_ex(dx.data_ptr(), ld_dx, dweight.data_ptr(), dy.data_ptr(),
                                      ld_dy, x.data_ptr(), ld_x, weight.data_ptr(),
                                      workspace.data_ptr(), wsb, rows, hidden, float(eps),
-                                     _cfg_ptr(cfg), _stream(stream)),
+                                     _cfg_ptr(cfg),
+                                     _stream(stream, dy, x, weight, dx, dweight, workspace)),
            "norm_rmsnorm_bwd")
     return dx, dweight
 
@@ -480,7 +495,9 @@ def fused_add_rmsnorm_bwd(dout, s, weight, eps: float, dres=None, ds=None, dweig
                                                dres.data_ptr() if dres is not None else None,
                                                ld_dres, s.data_ptr(), ld_s, weight.data_ptr(),
                                                workspace.data_ptr(), wsb, rows, hidden,
-                                               float(eps), _cfg_ptr(cfg), _stream(stream)),
+                                               float(eps), _cfg_ptr(cfg),
+                                               _stream(stream, dout, dres, s, weight, ds,
+                                                       dweight, workspace)),
            "norm_fused_add_rmsnorm_bwd")
     return ds, dweight
 

@@ -379,3 +379,23 @@ def test_no_write_outside_outputs_and_every_output_written(rows):
         torch.cuda.synchronize()
         assert _guards_intact(big_dx, n), c
         assert not torch.isnan(dx.float()).any().item(), c
+
+
+def test_binding_refuses_tensors_off_the_current_device(monkeypatch):
+    """The library launches on the current device: the binding refuses a call
+    whose tensors live elsewhere, before anything is enqueued (the current
+    device is stubbed to another index, as a one-GPU machine has no second)."""
+    x = torch.zeros(4, 4096, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(4096, dtype=torch.bfloat16, device=DEV)
+    out = torch.full_like(x, 3.0)
+    rn.rmsnorm_fwd(x, w, 1e-6, out=out)  # accepted on the current device
+    torch.cuda.synchronize()
+    assert bool((out == 0).all())
+    out.fill_(3.0)
+    monkeypatch.setattr(rn, "_current_device", lambda: x.get_device() + 1)
+    with pytest.raises(ValueError, match="current device"):
+        rn.rmsnorm_fwd(x, w, 1e-6, out=out)
+    with pytest.raises(ValueError, match="current device"):
+        rn.layernorm_bwd(x, x, torch.zeros(4, device=DEV), torch.ones(4, device=DEV), w)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())  # nothing ran
