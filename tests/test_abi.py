@@ -627,3 +627,27 @@ def test_tuned_forward_table():
                 assert rn.Cfg(c.threads_per_row, c.rows_per_block, 0, c.vector_elems) in \
                     [rn.Cfg(k.threads_per_row, k.rows_per_block, 0, k.vector_elems)
                      for k in listed], (op, h, rows, c)
+
+
+def test_missing_library_raises_and_product_never_touches_the_oracle(monkeypatch, tmp_path):
+    """No fallback: without librownorm.so every entry of the binding raises,
+    and no module of the package imports the oracle."""
+    import ast
+    import glob
+    import os
+
+    monkeypatch.setattr(rn, "_lib", None)
+    monkeypatch.setattr(rn, "LIB_PATH", str(tmp_path / "librownorm.so"))
+    with pytest.raises(ImportError, match="missing"):
+        rn.lib()
+    with pytest.raises(ImportError):
+        rn.select_config("fused_add_rmsnorm", 8, 4096)
+    pkg = os.path.dirname(os.path.abspath(rn.__file__))
+    for path in glob.glob(os.path.join(pkg, "**", "*.py"), recursive=True):
+        tree = ast.parse(open(path).read())
+        for node in ast.walk(tree):
+            names = [a.name for a in node.names] if isinstance(node, (ast.Import,
+                                                                      ast.ImportFrom)) else []
+            if isinstance(node, ast.ImportFrom) and node.module:
+                names.append(node.module)
+            assert not any(n == "oracle" or n.startswith("oracle.") for n in names), path
