@@ -1,8 +1,9 @@
 """Parity on both sides of every switch in the library's own launch choice.
 
-For each forward operation and compiled hidden size, the row counts where the
-chosen kernel changes (another launch shape, the late-weights variant, the
-persistent ring or another ring depth) are found from the library's
+For each forward operation and hidden size (compiled and run-time), the row
+counts where the chosen kernel changes (another launch shape, the
+late-weights variant, the persistent ring or another ring depth) are found
+from the library's
 description of its choice on this device, and the rows just below and at each
 switch run through the library's choice against the oracle.  Switches past
 17 M elements are left to the large-matrix and random tests."""
@@ -44,7 +45,11 @@ CHECK = {
 }
 
 
-@pytest.mark.parametrize("hidden", rn.HIDDEN_SIZES)
+# compiled hidden sizes, then run-time ones (not multiples of 64: 1000, 3080; wide: 5120, 7168)
+HIDDEN = tuple(rn.HIDDEN_SIZES) + (1000, 3080, 5120, 7168)
+
+
+@pytest.mark.parametrize("hidden", HIDDEN)
 @pytest.mark.parametrize("op", sorted(CHECK))
 def test_both_sides_of_every_switch(op, hidden):
     switches = switch_rows(op, hidden)
