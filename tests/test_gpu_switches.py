@@ -3,10 +3,10 @@
 For each forward operation and hidden size (compiled and run-time), the row
 counts where the chosen kernel changes (another launch shape, the
 late-weights variant, the persistent ring or another ring depth) are found
-from the library's
-description of its choice on this device, and the rows just below and at each
-switch run through the library's choice against the oracle.  Switches past
-17 M elements are left to the large-matrix and random tests."""
+from the library's description of its choice on this device, and the rows
+just below and at each switch run through the library's choice against the
+oracle.  Switches past 17 M elements are left to the large-matrix and random
+tests."""
 import pytest
 
 import row_normalization_persistent_amd as rn
