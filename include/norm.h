@@ -343,9 +343,14 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_ex(void* ds, int64_t ld_ds, floa
  * leaves it zero-filled again, so one workspace serves any number of calls
  * in stream order (calls that overlap in time on one workspace race).  Its
  * first 32-bit word stays 0 unless a workgroup gave up waiting for its row's
- * partners (about a second; only possible when other work keeps the launch
- * from being resident at once): then that call's results are invalid and
- * the workspace must be zero-filled again.  Ownership: the caller's. */
+ * partners (about a second, see norm_split_set_spin_limit; only possible
+ * when other work keeps the launch from being resident at once): then bit 0
+ * is set, and every chunk whose workgroup gave up is written as NaN (its
+ * out or y elements, and for a row's first chunk that row's mean and rstd),
+ * never as wrong finite values; the fused op's residual is still correct.
+ * The bit stays set until norm_split_status clears it; the rest of the
+ * workspace is zero-filled again as after any call.  Ownership: the
+ * caller's. */
 NORM_API norm_status norm_fused_add_rmsnorm_split(void* out, void* residual, const void* x,
                                                   const void* weight, int64_t rows,
                                                   int64_t hidden, float eps, void* workspace,
@@ -364,6 +369,25 @@ NORM_API norm_status norm_layernorm_fwd_split(void* y, float* mean, float* rstd,
 /* Workspace bytes the row-split entry points need for `rows` rows (0 for
  * rows <= 0; constant above 512 rows, which are never split). */
 NORM_API size_t norm_split_workspace_bytes(int64_t rows);
+
+/* Error word of a row-split workspace: waits for `stream` (every call
+ * enqueued on it so far has finished), then stores the workspace's first
+ * 32-bit word in *status (0: no workgroup of any call since the word was
+ * last cleared gave up; bit 0 set: at least one did, and that call's NaN
+ * chunks mark the rows affected).  clear != 0 resets a nonzero word to 0.
+ * Synchronizes the host with `stream`, so it cannot be called while the
+ * stream is being captured into a graph.  Errors: INVALID_VALUE for a NULL
+ * workspace or status, MISALIGNED for a workspace not 16-byte aligned,
+ * LAUNCH when the copy or the synchronization fails. */
+NORM_API norm_status norm_split_status(void* workspace, int32_t clear, uint32_t* status,
+                                       hipStream_t stream);
+
+/* Polls a row-split partner wait makes before it gives up (default 2^20,
+ * about a second; 0: give up at once without polling, which makes every
+ * split workgroup write NaN and set the error bit).  Process-wide, read
+ * when a split call is enqueued; returns the previous value.  For tests and
+ * diagnostics of the give-up path. */
+NORM_API uint32_t norm_split_set_spin_limit(uint32_t polls);
 
 /* The row split the library would choose for a forward op (fused, RMSNorm or
  * LayerNorm forward) on contiguous 16-byte-aligned rows with `cu_count` CUs

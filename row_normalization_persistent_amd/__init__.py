@@ -165,6 +165,10 @@ def lib() -> ctypes.CDLL:
     L.norm_select_split.argtypes = [ctypes.c_int, _i64, _i64, _i32, ctypes.POINTER(_i32),
                                     ctypes.POINTER(_i32)]
     L.norm_select_split.restype = ctypes.c_int
+    L.norm_split_status.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_uint32), _vp]
+    L.norm_split_status.restype = ctypes.c_int
+    L.norm_split_set_spin_limit.argtypes = [ctypes.c_uint32]
+    L.norm_split_set_spin_limit.restype = ctypes.c_uint32
     L.norm_select_config.argtypes = [ctypes.c_int, _i64, _i64, ctypes.c_int32, _cfgp]
     L.norm_select_config.restype = ctypes.c_int
     L.norm_list_configs.argtypes = [ctypes.c_int, _i64, _cfgp, ctypes.c_int32]
@@ -292,6 +296,36 @@ def select_split(op, rows: int, hidden: int, cu_count: int = 0):
     return k.value, v.value
 
 
+class SplitGaveUpError(NormError):
+    """A row-split call's workgroup gave up waiting for its row's partners:
+    the chunks it owned were written as NaN."""
+
+
+def split_status(workspace, clear: bool = True, stream=None) -> int:
+    """The row-split workspace's error word after every call enqueued on the
+    stream so far (synchronizes with it): 0, or bit 0 set when a workgroup
+    gave up waiting for its row's partners.  clear: reset it to 0."""
+    _mat(workspace, "workspace", torch.uint8)
+    st = ctypes.c_uint32()
+    _check(lib().norm_split_status(workspace.data_ptr(), int(bool(clear)), ctypes.byref(st),
+                                   _stream(stream, workspace)), "norm_split_status")
+    return st.value
+
+
+def set_split_spin_limit(polls: int) -> int:
+    """Polls a row-split partner wait makes before giving up (process-wide;
+    0 makes every split workgroup give up at once).  Returns the previous
+    value.  For tests and diagnostics."""
+    return int(lib().norm_split_set_spin_limit(int(polls)))
+
+
+def _split_check(workspace, stream, what: str) -> None:
+    """check_split=True: wait for the call and raise if any workgroup gave up."""
+    if workspace is not None and split_status(workspace, True, stream) != 0:
+        raise SplitGaveUpError(6, f"{what}: a workgroup gave up waiting for its row's "
+                                  "partners; the chunks it owned are NaN")
+
+
 def _split_ws(workspace):
     """(pointer, bytes) of a row-split workspace (a zero-filled uint8 device
     tensor), or (None, 0)."""
@@ -302,12 +336,13 @@ def _split_ws(workspace):
 
 
 def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, stream=None,
-                      workspace=None, split=None):
+                      workspace=None, split=None, check_split: bool = False):
     """residual <- bf16(x + residual) in place; returns (out, residual).
     x, residual and out may be row-strided views (e.g. column slices).  With
     `workspace` (zero-filled uint8, split_workspace_bytes(rows)) or `split`,
     runs the row-split entry point on contiguous rows (split None/0: the
-    library's choice, 1: never, k: about k workgroups a row)."""
+    library's choice, 1: never, k: about k workgroups a row).  check_split:
+    wait for the call and raise SplitGaveUpError if a workgroup gave up."""
     if workspace is not None or split is not None:
         if cfg is not None:
             raise ValueError("cfg does not apply to the row-split entry point")
@@ -324,6 +359,8 @@ def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, strea
                                                   _stream(stream, x, residual, weight, out,
                                                           workspace)),
                "norm_fused_add_rmsnorm_split")
+        if check_split:
+            _split_check(workspace, stream, "norm_fused_add_rmsnorm_split")
         return out, residual
     rows, hidden, ld_x = _rows(x, "x")
     if residual.shape != x.shape:
@@ -341,8 +378,9 @@ def fused_add_rmsnorm(x, residual, weight, eps: float, out=None, cfg=None, strea
 
 
 def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspace=None,
-                split=None):
-    """workspace / split: the row-split entry point, as for fused_add_rmsnorm."""
+                split=None, check_split: bool = False):
+    """workspace / split / check_split: the row-split entry point, as for
+    fused_add_rmsnorm."""
     if workspace is not None or split is not None:
         if cfg is not None:
             raise ValueError("cfg does not apply to the row-split entry point")
@@ -354,6 +392,8 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspac
                                             rows, hidden, float(eps), wp, wb, int(split or 0),
                                             _stream(stream, x, weight, out, workspace)),
                "norm_rmsnorm_fwd_split")
+        if check_split:
+            _split_check(workspace, stream, "norm_rmsnorm_fwd_split")
         return out
     rows, hidden, ld_x = _rows(x, "x")
     _vec(weight, hidden, "weight")
@@ -367,9 +407,11 @@ def rmsnorm_fwd(x, weight, eps: float, out=None, cfg=None, stream=None, workspac
 
 
 def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
-                  with_stats: bool = True, cfg=None, stream=None, workspace=None, split=None):
+                  with_stats: bool = True, cfg=None, stream=None, workspace=None, split=None,
+                  check_split: bool = False):
     """Returns (y, mean, rstd); mean/rstd are None when with_stats is False.
-    workspace / split: the row-split entry point, as for fused_add_rmsnorm."""
+    workspace / split / check_split: the row-split entry point, as for
+    fused_add_rmsnorm."""
     use_split = workspace is not None or split is not None
     if use_split:
         if cfg is not None:
@@ -400,6 +442,8 @@ def layernorm_fwd(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
                                               _stream(stream, x, weight, bias, y, mean, rstd,
                                                       workspace)),
                "norm_layernorm_fwd_split")
+        if check_split:
+            _split_check(workspace, stream, "norm_layernorm_fwd_split")
         return y, mean, rstd
     _check(lib().norm_layernorm_fwd_ex(y.data_ptr(), ld_y, mp, rp, x.data_ptr(), ld_x,
                                        weight.data_ptr(), bias.data_ptr(), rows, hidden,

@@ -728,6 +728,10 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
 // above 49152) are split whenever a shape exists, up to 64 rows.
 constexpr int64_t kSplitMaxRows = 512;
 
+// Polls a partner wait makes before it gives up; process-wide, changed only by
+// norm_split_set_spin_limit (tests and diagnostics force a give-up with 0).
+std::atomic<uint32_t> g_split_spin_limit{kSplitSpinLimit};
+
 size_t split_ws_bytes(int64_t rows) {
     if (rows <= 0) return 0;
     return (size_t)kSplitHeaderWords * 4 +
@@ -828,7 +832,7 @@ norm_status run_fwd_split(norm_op op, const FwdCall& c, void* workspace, size_t 
             const SplitArgs a{c.out,     c.residual, c.x,      c.weight, c.bias,
                               c.mean,    c.rstd,     static_cast<uint32_t*>(workspace),
                               c.ld_out,  L.ld_res,   c.ld_x,   c.rows,   (int32_t)c.hidden,
-                              sh.k,      c.eps};
+                              sh.k,      c.eps,      g_split_spin_limit.load()};
             return from_hip(e.launch(a, stream));
         }
     return NORM_ERROR_INVALID_VALUE;
@@ -1134,6 +1138,28 @@ norm_status norm_layernorm_fwd_split(void* y, float* mean, float* rstd, const vo
 }
 
 size_t norm_split_workspace_bytes(int64_t rows) { return split_ws_bytes(rows); }
+
+norm_status norm_split_status(void* workspace, int32_t clear, uint32_t* status,
+                              hipStream_t stream) {
+    if (!workspace || !status) return NORM_ERROR_INVALID_VALUE;
+    if (!aligned(workspace, 16)) return NORM_ERROR_MISALIGNED;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return NORM_ERROR_LAUNCH;
+    if (word != 0 && clear) {
+        static const uint32_t zero = 0;
+        if (hipMemcpyAsync(workspace, &zero, sizeof zero, hipMemcpyHostToDevice, stream) !=
+                hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return NORM_ERROR_LAUNCH;
+    }
+    *status = word;
+    return NORM_SUCCESS;
+}
+
+uint32_t norm_split_set_spin_limit(uint32_t polls) { return g_split_spin_limit.exchange(polls); }
 
 norm_status norm_select_split(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
                               int32_t* split, int32_t* vecs) {

@@ -27,11 +27,15 @@
 //      the next call.
 //
 // Every workgroup of a launch must be resident at once (the waits); the host
-// keeps rows * k at or below the CU count, one workgroup per CU.  A wait gives
-// up after kSplitSpinLimit polls (about a second), sets bit 0 of the
-// workspace's first word, and goes on with whatever partials it sees; that
-// can only happen when other work keeps this launch's workgroups off the
-// CUs.
+// keeps rows * k at or below the CU count, one workgroup per CU.  A wait polls
+// at most SplitArgs::spin_limit times (kSplitSpinLimit, about a second, unless
+// the host set another limit; 0: give up without polling).  A workgroup that
+// gives up sets bit 0 of the workspace's first word and takes NaN for every
+// partial it has not seen, so its chunk's outputs (and, for chunk 0, the
+// row's mean and rstd) are NaN rather than wrong finite values; it still
+// departs the row, so the workspace's row words end zero-filled.  Giving up
+// can only happen when other work keeps this launch's workgroups off the CUs
+// (or the host asked for it).
 #pragma once
 
 #include "dyn_common.hpp"
@@ -43,10 +47,13 @@ namespace rownorm {
 // word (value bits << 32 | 1): its nonzero low half says it is there, so the
 // data and its ready flag arrive together and no fence is needed on this
 // path.  Lane i < k polls chunk i's word(s) (one round trip per poll for the
-// whole row) and puts the values in q0[i], q1[i] (LDS).
+// whole row), at most `limit` times, and puts the values in q0[i], q1[i]
+// (LDS); a lane that runs out of polls records the give-up in *err and
+// writes NaN there instead.
 __device__ __forceinline__ void split_publish_and_gather(uint64_t* slot, uint32_t* err, int j,
                                                          int k, bool two, float p0, float p1,
-                                                         float* q0, float* q1, int lane) {
+                                                         float* q0, float* q1, int lane,
+                                                         uint32_t limit) {
     if (lane == 0) {
         __hip_atomic_store(&slot[kSplitP0 + j], ((uint64_t)__float_as_uint(p0) << 32) | 1u,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -56,20 +63,24 @@ __device__ __forceinline__ void split_publish_and_gather(uint64_t* slot, uint32_
     }
     if (lane < k) {
         uint64_t a = 0, b = two ? 0 : 1;
-        uint32_t polls = 0;
-        for (;;) {
+        bool seen = false;
+        for (uint32_t polls = 0; polls < limit; ++polls) {
             if (!(a & 1u))
                 a = __hip_atomic_load(&slot[kSplitP0 + lane], __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
             if (!(b & 1u))
                 b = __hip_atomic_load(&slot[kSplitP1 + lane], __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
-            if ((a & b & 1u) != 0) break;
-            if (++polls > kSplitSpinLimit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((a & b & 1u) != 0) {
+                seen = true;
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
+        }
+        if (!seen) {
+            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a = (uint64_t)__float_as_uint(__builtin_nanf("")) << 32;
+            b = a;
         }
         q0[lane] = __uint_as_float((uint32_t)(a >> 32));
         q1[lane] = __uint_as_float((uint32_t)(b >> 32));
@@ -186,7 +197,8 @@ __global__ __launch_bounds__(kSplitLanes) void split_norm_kernel(SplitArgs a) {
     // step 3: meet the row's other chunks
     uint64_t* slot = reinterpret_cast<uint64_t*>(a.ws + kSplitHeaderWords) + row * kSplitRowQwords;
     if (lane < kWave)
-        split_publish_and_gather(slot, a.ws, j, k, OP == kSplitLn, p0, p1, q0, q1, lane);
+        split_publish_and_gather(slot, a.ws, j, k, OP == kSplitLn, p0, p1, q0, q1, lane,
+                                 a.spin_limit);
     __syncthreads();
 
     const float inv_h = 1.0f / (float)h;

@@ -151,7 +151,7 @@ constexpr int kSplitDepart = 0;
 constexpr int kSplitP0 = 1;
 constexpr int kSplitP1 = kSplitP0 + kSplitMax;
 constexpr int kSplitRowQwords = 144;    // >= kSplitP1 + kSplitMax, 128-byte multiple
-constexpr uint32_t kSplitSpinLimit = 1u << 20;
+constexpr uint32_t kSplitSpinLimit = 1u << 20;  // default polls per wait (about a second)
 enum SplitOp : int { kSplitFused = 0, kSplitRms = 1, kSplitLn = 2 };
 
 struct SplitArgs {
@@ -168,6 +168,7 @@ struct SplitArgs {
     int32_t hidden;
     int32_t split;         // k workgroups per row
     float eps;
+    uint32_t spin_limit;   // polls a partner wait makes before giving up
 };
 
 using SplitLauncher = hipError_t (*)(const SplitArgs&, hipStream_t);

@@ -33,7 +33,7 @@ def test_header_declares_the_four_operations():
             assert op[:-3] in names  # every strided variant has a plain form
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd"):
         assert op + "_split" in names  # the row-split forward
-    assert len(names) == 31
+    assert len(names) == 33
 
 
 def test_library_exports_every_declared_symbol():
@@ -574,6 +574,24 @@ def test_split_validation():
     assert L.norm_layernorm_fwd_split(A, A + MB, A + MB + 65536, A + 2 * MB, A + 3 * MB,
                                       A + 3 * MB + 65536, 4, 16384, 1e-5, A + MB + 8, 1 << 20,
                                       2, None) == MISALIGNED
+
+
+def test_split_status_and_spin_limit_host_side():
+    """The error-word query rejects bad arguments before any HIP call; the
+    spin limit is process-wide and returns the previous value."""
+    L = rn.lib()
+    st = ctypes.c_uint32(7)
+    assert L.norm_split_status(None, 1, ctypes.byref(st), None) == INVALID
+    assert L.norm_split_status(WS, 1, None, None) == INVALID
+    assert L.norm_split_status(WS + 4, 1, ctypes.byref(st), None) == MISALIGNED
+    assert st.value == 7  # untouched on error
+    prev = rn.set_split_spin_limit(5)
+    try:
+        assert prev == 1 << 20
+        assert rn.set_split_spin_limit(0) == 5
+    finally:
+        rn.set_split_spin_limit(prev)
+    assert rn.set_split_spin_limit(prev) == prev
 
 
 def test_wide_backward_host_logic():

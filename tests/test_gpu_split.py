@@ -275,3 +275,75 @@ def test_split_errors_that_need_the_device():
     with pytest.raises(rn.NormError) as e:  # the library splits these rows: a workspace is needed
         rn.rmsnorm_fwd(x64, w64, 1e-6, workspace=None, split=0)
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("op,rows,h,split", [("fused_add_rmsnorm", 2, 32768, 4),
+                                             ("rmsnorm_fwd", 3, 65536, 4),
+                                             ("layernorm_fwd", 2, 57344, 5)])
+def test_split_give_up_is_visible(op, rows, h, split):
+    """A partner wait that gives up (forced from the host: a spin limit of 0
+    polls, so every split workgroup gives up at once and every kernel still
+    exits) writes NaN for its chunk, never a wrong finite value; the fused
+    op's residual is still exact; the error word reports it until cleared,
+    the rest of the workspace is zero again, and the next call on the same
+    workspace is correct."""
+    inp = inputs(op, rows, h, seed=5 + rows)
+    ws = workspace(rows)
+    prev = rn.set_split_spin_limit(0)
+    try:
+        got = run(op, inp, ws, split)
+        assert rn.set_split_spin_limit(0) == 0
+        with pytest.raises(rn.SplitGaveUpError):
+            if op == "rmsnorm_fwd":
+                rn.rmsnorm_fwd(dev(inp["x"]), dev(inp["w"]), inp["eps"], workspace=ws,
+                               split=split, check_split=True)
+            elif op == "fused_add_rmsnorm":
+                rn.fused_add_rmsnorm(dev(inp["x"]), dev(inp["r"]), dev(inp["w"]), inp["eps"],
+                                     workspace=ws, split=split, check_split=True)
+            else:
+                rn.layernorm_fwd(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]), inp["eps"],
+                                 workspace=ws, split=split, check_split=True)
+    finally:
+        rn.set_split_spin_limit(prev)
+    assert prev == 1 << 20
+    out = P.bits_to_f64(got["out"])
+    assert np.isnan(out).all(), f"{op}: a chunk that gave up holds finite values"
+    if op == "fused_add_rmsnorm":
+        _, res_ref, _ = oracle.fused_add_rmsnorm(inp["x"], inp["r"], inp["w"], inp["eps"], NT)
+        P.assert_bits_equal(got["res"], res_ref, f"{op}: residual after a give-up")
+    if op == "layernorm_fwd":
+        assert np.isnan(got["mean"]).all() and np.isnan(got["rstd"]).all()
+    # check_split cleared the word of the second call; the first call's bit was
+    # the same bit, so the word is 0 now and the row words were zeroed
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    assert rn.split_status(ws) == 0
+    # a give-up without check_split: the word reports it, clear=False keeps it
+    prev = rn.set_split_spin_limit(0)
+    try:
+        run(op, inp, ws, split)
+    finally:
+        rn.set_split_spin_limit(prev)
+    assert rn.split_status(ws, clear=False) == 1
+    assert int(torch.count_nonzero(ws[4:])) == 0
+    assert rn.split_status(ws) == 1
+    assert rn.split_status(ws) == 0
+    # the same workspace, default limit: correct, and no error reported
+    got = run(op, inp, ws, split)
+    check(op, inp, got, f"{op} {rows}x{h} after a give-up")
+    assert rn.split_status(ws) == 0
+
+
+def test_split_status_untouched_when_not_split():
+    """Rows the library does not split leave the workspace (and its error
+    word) alone, whatever the spin limit."""
+    inp = inputs("fused_add_rmsnorm", 64, 4096, seed=3)
+    assert rn.select_split("fused_add_rmsnorm", 64, 4096)[0] == 1
+    ws = workspace(64)
+    prev = rn.set_split_spin_limit(0)
+    try:
+        got = run("fused_add_rmsnorm", inp, ws, 0)
+    finally:
+        rn.set_split_spin_limit(prev)
+    check("fused_add_rmsnorm", inp, got, "not split, spin limit 0")
+    assert rn.split_status(ws) == 0
