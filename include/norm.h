@@ -192,6 +192,33 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
                                int64_t rows, int64_t hidden, float eps,
                                hipStream_t stream);
 
+/* norm_layernorm_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments, launch choice, kernels and
+ * errors, with the per-workgroup partial sums kept in a scratch array the
+ * library holds in every device's memory (NORM_NOALLOC_SCRATCH_BYTES per
+ * device, set up on the first call on a device and kept until the process
+ * ends) instead of a caller-given workspace.  Allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library call.  Returns
+ * NORM_ERROR_WORKSPACE when the launch's partial sums (2 * 4 * hidden bytes,
+ * hidden rounded up to 64 off the compiled sizes, for each of its up to 256
+ * workgroups) would exceed NORM_NOALLOC_SCRATCH_BYTES: every hidden up to
+ * 16384 fits, wider rows fit only with fewer rows (32768: up to 128 rows).
+ * NORM_ERROR_DEVICE when the
+ * scratch array's address cannot be found on the current device.  All calls
+ * on one device share its scratch array: calls that overlap in time on that
+ * device (different streams, or different host threads, without ordering
+ * between them) race and give wrong column sums; calls in one stream's order
+ * are safe.  Nothing in the array needs to start at any value (every slab a
+ * launch reads it writes first).  Results are bitwise those of
+ * norm_layernorm_bwd. */
+#define NORM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+NORM_API norm_status norm_layernorm_bwd_noalloc(void* dx, float* dweight, float* dbias,
+                                                const void* dy, const void* x,
+                                                const float* mean, const float* rstd,
+                                                const void* weight, int64_t rows,
+                                                int64_t hidden, float eps, hipStream_t stream);
+
 /* RMSNorm backward with the same combined inner + outer reduction ("Llu/ln
  * bwd", author note and review thread, applied to RMSNorm), the per-row
  * statistic recomputed from x with `eps` (no saved statistic is needed):

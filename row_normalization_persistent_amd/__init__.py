@@ -147,6 +147,9 @@ def lib() -> ctypes.CDLL:
         "norm_rmsnorm_fwd_split": [_vp, _vp, _vp, _i64, _i64, _f32, _vp, _sz, _i32, _vp],
         "norm_layernorm_fwd_split": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _sz,
                                      _i32, _vp],
+        # LayerNorm backward with the library's per-device scratch (no workspace)
+        "norm_layernorm_bwd_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32,
+                                       _vp],
     }
     for n, args in sigs.items():
         fn = getattr(L, n)
@@ -506,6 +509,42 @@ def layernorm_bwd(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=
                                        _stream(stream, dy, x, mean, rstd, weight, dx, dweight,
                                                dbias, workspace)),
            "norm_layernorm_bwd")
+    return dx, dweight, dbias
+
+
+# bytes of the per-device scratch array norm_layernorm_bwd_noalloc uses
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def layernorm_bwd_noalloc(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
+                          dbias=None, stream=None):
+    """layernorm_bwd through the entry point that allocates nothing: its
+    partial sums go to the library's per-device scratch array, so calls that
+    overlap in time on one device race.  Contiguous tensors; pass dx, dweight
+    and dbias to keep the binding from allocating them.  Returns (dx,
+    dweight, dbias)."""
+    rows, hidden = _rows_hidden(_mat(x, "x"))
+    _mat(dy, "dy")
+    if dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    _vec(weight, hidden, "weight")
+    _mat(mean, "mean", torch.float32)
+    _mat(rstd, "rstd", torch.float32)
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must hold one value per row")
+    dx = _mat(_like(x, dx, "dx"), "dx")
+    dweight = torch.empty(hidden, dtype=torch.float32, device=x.device) if dweight is None \
+        else dweight
+    dbias = torch.empty(hidden, dtype=torch.float32, device=x.device) if dbias is None else dbias
+    _vec(dweight, hidden, "dweight", torch.float32)
+    _vec(dbias, hidden, "dbias", torch.float32)
+    _check(lib().norm_layernorm_bwd_noalloc(dx.data_ptr(), dweight.data_ptr(), dbias.data_ptr(),
+                                            dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
+                                            rstd.data_ptr(), weight.data_ptr(), rows, hidden,
+                                            float(eps),
+                                            _stream(stream, dy, x, mean, rstd, weight, dx,
+                                                    dweight, dbias)),
+           "norm_layernorm_bwd_noalloc")
     return dx, dweight, dbias
 
 

@@ -16,6 +16,9 @@
 
 using namespace rownorm;
 
+// Partial-sum slabs of norm_layernorm_bwd_noalloc (see current_scratch).
+static __device__ __align__(256) unsigned char scratch[NORM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 bool hidden_compiled(int64_t hidden) {
@@ -106,6 +109,30 @@ norm_status current_cu_count(int* cu) {
         return NORM_ERROR_DEVICE;
     if (dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
     *cu = c;
+    return NORM_SUCCESS;
+}
+
+// ---- scratch of the allocation-free backward entry -------------------------
+// norm_layernorm_bwd_noalloc keeps its partial-sum slabs here instead of in a
+// caller-given workspace.  Each device that runs it holds its own copy of this
+// array for the life of the process; host code never uses the array's name
+// (a host-side stand-in, not a device address) but the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept in g_scratch.
+constexpr size_t kScratchBytes = NORM_NOALLOC_SCRATCH_BYTES;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+norm_status current_scratch(void** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return NORM_ERROR_DEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return NORM_ERROR_DEVICE;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
     return NORM_SUCCESS;
 }
 
@@ -857,6 +884,9 @@ struct BwdCall {
     float* dbias;
     int64_t rows, hidden;
     float eps;
+    // workspace == NULL and workspace_bytes == kScratchBytes: the slabs go to
+    // this device's scratch array, looked up after every argument check
+    bool use_scratch = false;
 };
 
 norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
@@ -868,14 +898,16 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         return NORM_ERROR_INVALID_VALUE;
     if (c.hidden < 1 || c.hidden > kMaxHidden) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     const bool any = c.rows > 0;
-    if (!c.dweight || (ln && !c.dbias) || !c.workspace) return NORM_ERROR_INVALID_VALUE;
+    if (!c.dweight || (ln && !c.dbias) || (!c.workspace && !c.use_scratch))
+        return NORM_ERROR_INVALID_VALUE;
     if (any && (!c.dx || !c.dy || !c.x || !c.weight || (ln && (!c.mean || !c.rstd))))
         return NORM_ERROR_INVALID_VALUE;
     const int64_t ld_dres = c.dres ? c.ld_dres : c.hidden;
     for (int64_t ld : {c.ld_dx, c.ld_dy, c.ld_x, ld_dres})
         if (ld < c.hidden || ld > kMaxLd || !span_ok(c.rows, ld, c.hidden, 2))
             return NORM_ERROR_INVALID_VALUE;
-    if (!aligned(c.dweight, 4) || (ln && !aligned(c.dbias, 4)) || !aligned(c.workspace, 16))
+    if (!aligned(c.dweight, 4) || (ln && !aligned(c.dbias, 4)) ||
+        (!c.use_scratch && !aligned(c.workspace, 16)))
         return NORM_ERROR_MISALIGNED;
     if (any && (!aligned(c.dx, 2) || !aligned(c.dy, 2) || !aligned(c.x, 2) ||
                 !aligned(c.weight, 2) || (c.dres && !aligned(c.dres, 2)) ||
@@ -958,13 +990,18 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         return NORM_ERROR_INVALID_VALUE;
     if (c.workspace_bytes < ws_need) return NORM_ERROR_WORKSPACE;
 
+    void* ws = c.workspace;
+    if (c.use_scratch) {
+        const norm_status st = current_scratch(&ws);
+        if (st != NORM_SUCCESS) return st;
+    }
     if (se) {
         const BwdArgs a{c.dx,     c.dy,      c.x,    c.mean, c.rstd,    c.dres, c.weight,
-                        (float*)c.workspace, c.dweight, c.dbias, c.rows, k.grid, c.eps};
+                        (float*)ws, c.dweight, c.dbias, c.rows, k.grid, c.eps};
         return from_hip(se->launch(a, stream));
     }
     const DynBwdArgs a{c.dx,    c.dy,     c.x,       c.mean,  c.rstd,
-                       c.dres,  c.weight, (float*)c.workspace, c.dweight, c.dbias,
+                       c.dres,  c.weight, (float*)ws, c.dweight, c.dbias,
                        c.ld_dx, c.ld_dy,  c.ld_x,    ld_dres, c.rows,
                        (int32_t)c.hidden, k.grid, c.eps};
     return from_hip(dyn_launch(a, stream));
@@ -1207,6 +1244,17 @@ norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias, const voi
                                int64_t rows, int64_t hidden, float eps, hipStream_t stream) {
     return norm_layernorm_bwd_cfg(dx, dweight, dbias, dy, x, mean, rstd, weight, workspace,
                                   workspace_bytes, rows, hidden, eps, nullptr, stream);
+}
+
+norm_status norm_layernorm_bwd_noalloc(void* dx, float* dweight, float* dbias, const void* dy,
+                                       const void* x, const float* mean, const float* rstd,
+                                       const void* weight, int64_t rows, int64_t hidden,
+                                       float eps, hipStream_t stream) {
+    BwdCall c{dx,     hidden,  dy,      hidden, x,       hidden,       mean,
+              rstd,   nullptr, hidden,  weight, nullptr, kScratchBytes, dweight,
+              dbias,  rows,    hidden,  eps};
+    c.use_scratch = true;
+    return run_bwd(NORM_OP_LAYERNORM_BWD, c, nullptr, stream);
 }
 
 norm_status norm_rmsnorm_bwd_ex(void* dx, int64_t ld_dx, float* dweight, const void* dy,

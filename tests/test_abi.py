@@ -33,7 +33,7 @@ def test_header_declares_the_four_operations():
             assert op[:-3] in names  # every strided variant has a plain form
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd"):
         assert op + "_split" in names  # the row-split forward
-    assert len(names) == 33
+    assert len(names) == 34
 
 
 def test_library_exports_every_declared_symbol():
@@ -592,6 +592,38 @@ def test_split_status_and_spin_limit_host_side():
     finally:
         rn.set_split_spin_limit(prev)
     assert rn.set_split_spin_limit(prev) == prev
+
+
+def test_noalloc_validation():
+    """The allocation-free LayerNorm backward validates like
+    norm_layernorm_bwd and refuses launches whose partial sums exceed its
+    scratch array, all before any HIP call."""
+    L = rn.lib()
+    f = L.norm_layernorm_bwd_noalloc
+    f.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                          ctypes.c_void_p]
+
+    def call(dx=A, dw=A + MB, db=A + 2 * MB, dy=A + 3 * MB, x=A + 4 * MB, m=A + 5 * MB,
+             r=A + 6 * MB, w=A + 7 * MB, rows=8, hidden=4096, eps=1e-5):
+        return f(dx, dw, db, dy, x, m, r, w, rows, hidden, eps, None)
+
+    assert call(rows=-1) == INVALID
+    assert call(dw=0) == INVALID
+    assert call(db=0) == INVALID
+    assert call(x=0) == INVALID
+    assert call(m=0) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(hidden=0) == UNSUPPORTED
+    assert call(dw=A + MB + 2) == MISALIGNED
+    assert call(dx=A + 3 * MB + 64) == INVALID      # dx overlaps dy without equalling it
+    assert call(dw=A + 5 * MB) == INVALID           # dweight aliases mean
+    # 256 rows of 32768 columns: 256 slabs of 2 x 32768 fp32 = 64 MiB > 32 MiB
+    big = 1 << 30
+    assert call(dx=A, dy=A + big, x=A + 2 * big, m=A + 3 * big, r=A + 3 * big + MB,
+                w=A + 3 * big + 2 * MB, dw=A + 3 * big + 3 * MB, db=A + 3 * big + 4 * MB,
+                rows=256, hidden=32768) == WORKSPACE
+    assert rn.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert rn.workspace_bytes(512, 16384) == rn.NOALLOC_SCRATCH_BYTES  # the largest that fits
 
 
 def test_wide_backward_host_logic():
