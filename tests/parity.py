@@ -5,11 +5,16 @@
   fp32 sum rounded once for every finite input).
 * bf16 normalized outputs: |gpu - ref| <= 2 ulp_bf16(ref), ref the unrounded
   fp64 oracle value; ulp_bf16(v) = 2^max(floor(log2|v|) - 7, -133).
-  For the outputs formed by cancellation (LayerNorm y, LayerNorm dx) a floor
-  of 2^-16 * M is added, M the magnitude of the terms that cancel (fp32 sums
-  over the row leave errors of order 2^-24 * sum|terms|; 2^-16 is 256x that
-  and is at most 1/256 bf16 ulp at scale M, so it only matters for outputs
-  cancelled far below the row's scale).
+  For the outputs formed by cancellation (LayerNorm y and dx, RMSNorm and
+  fused residual-add + RMSNorm dx, where rstd * (g - xhat * c) subtracts two
+  terms of the row's scale) a floor of 2^-16 * M is added, M the magnitude of
+  the terms that cancel (fp32 sums over the row leave errors of order
+  2^-24 * sum|terms|; 2^-16 is 256x that and is at most 1/256 bf16 ulp at
+  scale M, so it only matters for outputs cancelled far below the row's
+  scale).  Every element that passes only by the floor must be such an
+  output: |ref| <= 2^-6 * M (there 2 ulp are at most 2^-13 * M, so the floor
+  can add a real share of the budget); a floor-only pass at a larger |ref|
+  fails, since the floor is not meant to cover it.
 * fp32 statistics (LayerNorm mean, rstd): |gpu - ref| <= 1e-6 + 1e-5 |ref|.
 * fp32 column sums (dweight, dbias): |gpu - ref| <= 1e-3 |ref| + 1e-3 sqrt(sum_i t_i^2),
   t the summed terms (dy * xhat or dy): relative 1e-3, with the column's RMS
@@ -21,6 +26,7 @@ import numpy as np
 import torch
 
 FLOOR = 2.0 ** -16
+CANCELLED = 2.0 ** -6  # floor-only passes must have |ref| <= CANCELLED * M
 
 
 def bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -62,10 +68,30 @@ def assert_bf16_close(got_bits: np.ndarray, ref: np.ndarray, what: str, ulps: fl
                              f"first at {idx}: got {got[idx]!r} ref {ref[idx]!r}")
     with np.errstate(invalid="ignore", divide="ignore"):
         e = err / ulp_bf16(ref)
-    only_floor = 0
+    only_floor, ratio = 0, 0.0
     if floor_scale is not None:
-        only_floor = int((err > ulps * ulp_bf16(ref)).sum())
-    return {"max_err_ulp": float(np.nanmax(e)), "passed_only_by_floor": only_floor}
+        only = err > ulps * ulp_bf16(ref)
+        only_floor = int(only.sum())
+        if only_floor:
+            m = np.broadcast_to(floor_scale, ref.shape)[only]
+            r = np.abs(ref[only]) / m
+            ratio = float(r.max())
+            if ratio > CANCELLED:
+                k = int(np.argmax(r))
+                raise AssertionError(
+                    f"{what}: an element passed only by the cancellation floor although its "
+                    f"value is not cancelled: |ref| = {abs(ref[only][k])!r} is "
+                    f"{r[k]:.3g} x its term scale M (limit {CANCELLED})")
+    return {"max_err_ulp": float(np.nanmax(e)), "passed_only_by_floor": only_floor,
+            "elements": int(ref.size), "floor_max_ref_over_m": ratio}
+
+
+def report_floor(what: str, stats: dict) -> None:
+    """One line per checked output with the floor's use (shown with -s)."""
+    print(f"FLOOR {what}: {stats['passed_only_by_floor']} of {stats['elements']} elements "
+          f"passed only by the cancellation floor (max |ref|/M among them "
+          f"{stats['floor_max_ref_over_m']:.3g}); max error {stats['max_err_ulp']:.3f} bf16 ulp",
+          flush=True)
 
 
 def assert_f32_close(got: np.ndarray, ref: np.ndarray, what: str, rtol=1e-5, atol=1e-6):

@@ -166,8 +166,9 @@ def check_lnf(inp, cfg=None, what="layernorm_fwd", with_stats=True):
 @pytest.mark.parametrize("hidden", wl.LAYERNORM_FWD_HIDDEN)
 def test_layernorm_fwd_config(hidden):
     """rows=2048, x ~ N(0.5,2), w ~ N(1,0.1), b ~ N(0,0.1), eps 1e-5."""
-    check_lnf(wl.layernorm_fwd_inputs(wl.LAYERNORM_FWD_ROWS, hidden, seed=0),
-              what=f"layernorm_fwd h={hidden}")
+    stats = check_lnf(wl.layernorm_fwd_inputs(wl.LAYERNORM_FWD_ROWS, hidden, seed=0),
+                      what=f"layernorm_fwd h={hidden}")
+    P.report_floor(f"layernorm_fwd {wl.LAYERNORM_FWD_ROWS}x{hidden} y", stats)
 
 
 @pytest.mark.parametrize("hidden", rn.HIDDEN_SIZES)
@@ -248,7 +249,9 @@ def check_lnb(inp, cfg=None, what="layernorm_bwd", dx_is_dy=False):
 @pytest.mark.parametrize("hidden", wl.LAYERNORM_BWD_HIDDEN)
 def test_layernorm_bwd_config(hidden):
     """rows=8192, x, dy ~ N(0,1), w ~ N(1,0.1), mean/rstd from x with eps 1e-5."""
-    check_lnb(lnb_inputs(wl.LAYERNORM_BWD_ROWS, hidden, seed=0), what=f"layernorm_bwd h={hidden}")
+    stats, _ = check_lnb(lnb_inputs(wl.LAYERNORM_BWD_ROWS, hidden, seed=0),
+                         what=f"layernorm_bwd h={hidden}")
+    P.report_floor(f"layernorm_bwd {wl.LAYERNORM_BWD_ROWS}x{hidden} dx", stats)
 
 
 @pytest.mark.parametrize("hidden", rn.HIDDEN_SIZES)

@@ -52,14 +52,16 @@ def check(inp, fused, cfg=None, alias=None, what="rmsnorm_bwd"):
 def test_rmsnorm_bwd_config(hidden):
     """rows=8192, x, dy ~ N(0,1), w ~ N(1,0.1), eps 1e-6."""
     inp = wl.rmsnorm_bwd_inputs(wl.RMSNORM_BWD_ROWS, hidden, seed=0)
-    check(inp, fused=False, what=f"rmsnorm_bwd h={hidden}")
+    stats, _ = check(inp, fused=False, what=f"rmsnorm_bwd h={hidden}")
+    P.report_floor(f"rmsnorm_bwd {wl.RMSNORM_BWD_ROWS}x{hidden} dx", stats)
 
 
 @pytest.mark.parametrize("hidden", wl.RMSNORM_BWD_HIDDEN)
 def test_fused_add_rmsnorm_bwd_config(hidden):
     """The fused op's backward at its residual output, with the residual gradient."""
     inp = wl.rmsnorm_bwd_inputs(wl.RMSNORM_BWD_ROWS, hidden, seed=1)
-    check(inp, fused=True, what=f"fused_add_rmsnorm_bwd h={hidden}")
+    stats, _ = check(inp, fused=True, what=f"fused_add_rmsnorm_bwd h={hidden}")
+    P.report_floor(f"fused_add_rmsnorm_bwd {wl.RMSNORM_BWD_ROWS}x{hidden} ds", stats)
 
 
 @pytest.mark.parametrize("hidden", rn.HIDDEN_SIZES)
