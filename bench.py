@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-ops", action="store_true")
+    ap.add_argument("--no-hbm-ceilings", action="store_true",
+                    help="skip the streaming read/write-mix ceilings (1 GiB buffers)")
     ap.add_argument("--no-config-points", action="store_true",
                     help="skip the sweep_graph and config_points legs (the counter-collection "
                          "profile runs do: rocprofv3 --pmc crashed in config_points' many "
@@ -343,6 +345,8 @@ def main():
                                                 max(3, min(args.steps, 50) // 5))
             result["config_points"] = config_points(torch, rn, wl, dev, stream,
                                                     max(3, min(args.steps, 50) // 5))
+    if not args.no_hbm_ceilings:
+        result["hbm_ceilings"] = hbm_ceilings(torch, dev, stream, 10)
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
@@ -434,7 +438,9 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
         (lambda j=j: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream))
         for j in range(n)], reps)
     nb = 4 * h * rows + 2 * h
-    out.append(_op_rec("rmsnorm_fwd", rows, h, nb, t,
+    ceil = op_ceilings(torch, stream, [[xs[j]] for j in range(n)], ys, rows, h,
+                       launch_shape(rn, "rmsnorm_fwd", rows, h), reps, t)
+    out.append(_op_rec("rmsnorm_fwd", rows, h, nb, t, ceil=ceil,
                        cpu=oracle_beside("rmsnorm_fwd", i, rows, h, nb, cpu_seconds)))
     del xs, ys, x0
     # LayerNorm forward, hidden 16384, rows 2048
@@ -451,7 +457,9 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                       rstd=st[j, 1], stream=stream))
         for j in range(n)], reps)
     nb = (4 * h + 8) * rows + 4 * h
-    out.append(_op_rec("layernorm_fwd", rows, h, nb, t,
+    ceil = op_ceilings(torch, stream, [[xs[j]] for j in range(n)], ys, rows, h,
+                       launch_shape(rn, "layernorm_fwd", rows, h), reps, t)
+    out.append(_op_rec("layernorm_fwd", rows, h, nb, t, ceil=ceil,
                        cpu=oracle_beside("layernorm_fwd", i, rows, h, nb, cpu_seconds)))
     del xs, ys, x0
     # LayerNorm backward, hidden 4096 and 8192, rows 8192
@@ -475,7 +483,9 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                           dweight=dw, dbias=db, workspace=ws, stream=stream))
             for j in range(n)], reps)
         nb = (6 * h + 8) * rows + 10 * h
-        out.append(_op_rec("layernorm_bwd", rows, h, nb, t,
+        ceil = op_ceilings(torch, stream, [[xs[j], dys[j]] for j in range(n)], dxs, rows, h,
+                           launch_shape(rn, "layernorm_bwd", rows, h), reps, t)
+        out.append(_op_rec("layernorm_bwd", rows, h, nb, t, ceil=ceil,
                            note="rows kernel + column-reduce kernel; workspace not counted",
                            cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
         del xs, dys, dxs, x0, dy0
@@ -496,7 +506,9 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                     workspace=ws, stream=stream))
         for j in range(n)], reps)
     nb = 6 * h * rows + 6 * h
-    out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t,
+    ceil = op_ceilings(torch, stream, [[xs[j], dys[j]] for j in range(n)], dxs, rows, h,
+                       launch_shape(rn, "rmsnorm_bwd", rows, h), reps, t)
+    out.append(_op_rec("rmsnorm_bwd", rows, h, nb, t, ceil=ceil,
                        note="rows kernel + column-reduce kernel; workspace not counted",
                        cpu=oracle_beside("rmsnorm_bwd", i, rows, h, nb, cpu_seconds)))
     t = graph_time_per_launch(torch, stream, [
@@ -505,7 +517,9 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                               stream=stream))
         for j in range(n)], reps)
     nb = 8 * h * rows + 6 * h
-    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, nb, t,
+    ceil = op_ceilings(torch, stream, [[dys[j], drs[j], xs[j]] for j in range(n)], dxs, rows, h,
+                       launch_shape(rn, "fused_add_rmsnorm_bwd", rows, h), reps, t)
+    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, nb, t, ceil=ceil,
                        note="dout, dres, s read; ds written; workspace not counted",
                        cpu=oracle_beside("fused_add_rmsnorm_bwd", i, rows, h, nb,
                                          cpu_seconds)))
@@ -516,25 +530,146 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     return out
 
 
-_CEILING = []
+_CEIL_LIB = []
 
 
-def _ceiling_fn():
-    """normceil_same_traffic_h4096 from libnormceiling.so (built with the
-    package), or None when it was not built.  Loaded once."""
-    if _CEILING:
-        return _CEILING[0]
+def _ceil_lib():
+    """libnormceiling.so (the benchmark's measurement kernels, built with the
+    package) with its argument types, or None when it was not built.  Loaded
+    once."""
+    if _CEIL_LIB:
+        return _CEIL_LIB[0]
     import ctypes
     import row_normalization_persistent_amd as rn
     path = os.path.join(os.path.dirname(os.path.abspath(rn.__file__)), "libnormceiling.so")
     if not os.path.exists(path):
         return None
-    f = ctypes.CDLL(path).normceil_same_traffic_h4096
-    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
-    f.restype = ctypes.c_int
-    _CEILING.append(f)
-    return f
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.normceil_same_traffic_h4096.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+    L.normceil_same_traffic_h4096.restype = ctypes.c_int
+    L.normceil_stream.argtypes = [ctypes.POINTER(vp), i32, ctypes.POINTER(vp), i32, i64, i32,
+                                  i32, vp]
+    L.normceil_stream.restype = ctypes.c_int
+    L.normceil_rows.argtypes = [ctypes.POINTER(vp), i32, vp, i64, i64, i32, i32, i64, i32, vp]
+    L.normceil_rows.restype = ctypes.c_int
+    _CEIL_LIB.append(L)
+    return L
+
+
+def _ceiling_fn():
+    """normceil_same_traffic_h4096 from libnormceiling.so, or None."""
+    L = _ceil_lib()
+    return None if L is None else L.normceil_same_traffic_h4096
+
+
+def launch_shape(rn, op, rows, hidden):
+    """(lanes per row, 16-byte accesses per lane, persistent grid or 0, ring
+    depth) of the library's launch, from its own description."""
+    import re
+    d = rn.describe_config(op, rows, hidden)
+    lanes = int(re.search(r"\((\d+) lanes per row", d).group(1))
+    vecs = int(re.search(r"(\d+) 16-byte accesses per lane", d).group(1))
+    g = re.search(r"persistent grid of (\d+) workgroups", d)
+    ring = re.search(r"ring of (\d+) rows", d)
+    return lanes, vecs, int(g.group(1)) if g else 0, int(ring.group(1)) if ring else 1
+
+
+def op_ceilings(torch, stream, ins, outs, rows, hidden, shape, reps, op_us):
+    """The operation's row traffic (len(ins[j]) input matrices read, outs[j]
+    written, no arithmetic) through libnormceiling.so's row kernel over the
+    same buffer sets: one row per workgroup in the operation's lane layout,
+    and the operation's own persistent walk (grid and ring depth) when it has
+    one.  Time per launch, graph-timed like the operation; None when the
+    library is not built or the layout is not compiled there."""
+    import ctypes
+    L = _ceil_lib()
+    lanes, vecs, grid, depth = shape
+    if L is None or vecs not in (1, 2, 4, 8):
+        return None
+    n_in = len(ins[0])
+    sid = stream.cuda_stream
+    ptrs = [(ctypes.c_void_p * 3)(*([t.data_ptr() for t in ins[j]] + [None] * (3 - n_in)))
+            for j in range(len(outs))]
+    traffic = (n_in + 1) * rows * hidden * 2
+
+    def timed(g, d):
+        def one(j):
+            st = L.normceil_rows(ptrs[j], n_in, outs[j].data_ptr(), rows, hidden, lanes, vecs, g,
+                                 d, sid)
+            if st != 0:
+                raise RuntimeError(f"normceil_rows failed ({st}) at {rows}x{hidden} "
+                                   f"lanes {lanes} vecs {vecs} grid {g} depth {d}")
+        one(0)  # refuses a layout it does not compile before any capture
+        torch.cuda.synchronize()
+        us = graph_time_per_launch(torch, stream, [(lambda j=j: one(j)) for j in
+                                                   range(len(outs))], reps)
+        return {"us_per_launch": round(us, 3), "GBps": round(traffic / (us * 1e-6) / 1e9, 1),
+                "op_time_over_this": round(op_us / us, 3)}
+
+    res = {"traffic_bytes": traffic,
+           "reads_writes": f"{n_in} input row(s) read, 1 written, {lanes} lanes x {vecs} "
+                           "16-byte accesses a row"}
+    try:
+        res["one_row_per_workgroup"] = timed(0, 1)
+        if grid > 0:
+            res["persistent_walk"] = dict(timed(grid, depth), grid=grid, depth=depth)
+    except RuntimeError as e:
+        log(f"  ceiling skipped: {e}")
+        return None
+    log(f"  same traffic: one row a workgroup {res['one_row_per_workgroup']['us_per_launch']} us"
+        + (f", walk {res['persistent_walk']['us_per_launch']} us" if grid > 0 else ""))
+    return res
+
+
+STREAM_MIXES = (("read only", 1, 0), ("write only", 0, 1), ("copy, 1 read : 1 write", 1, 1),
+                ("2 reads : 1 write", 2, 1), ("2 reads : 2 writes", 2, 2),
+                ("3 reads : 1 write", 3, 1))
+
+
+def hbm_ceilings(torch, dev, stream, reps):
+    """The part's streaming rate for each read/write mix of the operations:
+    normceil_stream over 1 GiB per buffer (so every launch streams >= 1 GiB
+    through the 256 MB Infinity Cache), 16-byte non-temporal accesses, a grid
+    of {1024, 2048, 4096, 8192} workgroups x {1, 2, 4, 8} accesses in flight a
+    lane; the best of them per mix, time per launch over `reps` back-to-back
+    launches between two events on the launch stream."""
+    import ctypes
+    L = _ceil_lib()
+    if L is None:
+        return None
+    nbytes = 1 << 30
+    bufs = [torch.full((nbytes // 4,), k + 1, dtype=torch.int32, device=dev) for k in range(5)]
+    sink = torch.zeros(16 * 8192, dtype=torch.uint8, device=dev)
+    sid = stream.cuda_stream
+    out = []
+    for name, nr, nw in STREAM_MIXES:
+        ins = (ctypes.c_void_p * 3)(*([b.data_ptr() for b in bufs[:nr]] + [None] * (3 - nr)))
+        o = [b.data_ptr() for b in bufs[3:3 + nw]] or [sink.data_ptr()]
+        outs = (ctypes.c_void_p * 2)(*(o + [None] * (2 - len(o))))
+        trials = []
+        for grid in (1024, 2048, 4096, 8192):
+            for unroll in (1, 2, 4, 8):
+                def fn(k, grid=grid, unroll=unroll):
+                    st = L.normceil_stream(ins, nr, outs, nw, nbytes, grid, unroll, sid)
+                    if st != 0:
+                        raise RuntimeError(f"normceil_stream failed ({st})")
+                fn(0)
+                d = timed_events(torch, stream, fn, reps)
+                us = float(np.median(d))
+                trials.append((us, grid, unroll))
+        us, grid, unroll = min(trials)
+        gbps = (nr + nw) * nbytes / (us * 1e-6) / 1e9
+        out.append({"mix": name, "bytes_per_launch": (nr + nw) * nbytes, "best_grid": grid,
+                    "best_accesses_in_flight": unroll, "us_median": round(us, 1),
+                    "GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                    "GBps_range_over_shapes": [
+                        round((nr + nw) * nbytes / (max(t[0] for t in trials) * 1e-6) / 1e9, 1),
+                        round(gbps, 1)]})
+        log(f"  stream {name}: {gbps:.0f} GB/s (grid {grid}, {unroll} in flight)")
+    del bufs, sink
+    torch.cuda.synchronize()
+    return out
 
 
 def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
@@ -739,7 +874,10 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                           dweight=dw, dbias=db, workspace=ws, stream=stream))
             for j in range(n)], reps)
         nb = (6 * h + 8) * rows + 10 * h
+        ceil = op_ceilings(torch, stream, [[xs[j], dys[j]] for j in range(n)], dxs, rows, h,
+                           launch_shape(rn, "layernorm_bwd", rows, h), reps, t)
         out.append(_op_rec("layernorm_bwd", rows, h, nb, t, note=kind + " + column reduce",
+                           ceil=ceil,
                            cpu=oracle_beside("layernorm_bwd", i, rows, h, nb, cpu_seconds)))
         t = graph_time_per_launch(torch, stream, [
             (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
@@ -754,12 +892,18 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     return out
 
 
-def _cores() -> int:
+def _cores():
+    """(threads the oracle runs on, cores this process may run on).  The
+    threads are every core in sched_getaffinity(0), capped by the host's
+    per-GPU CPU share when the environment states one (OMP_NUM_THREADS: a
+    one-GPU machine allots 16 cores whatever the affinity mask shows)."""
     try:
-        cores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    return max(1, min(cores, 16))
+        avail = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    used = min(avail, int(share)) if share.isdigit() and int(share) > 0 else avail
+    return max(1, used), max(1, avail)
 
 
 def oracle_beside(op, inp, rows, hidden, nbytes, seconds):
@@ -769,7 +913,7 @@ def oracle_beside(op, inp, rows, hidden, nbytes, seconds):
     if not seconds:
         return None
     import oracle
-    cores = _cores()
+    cores, avail = _cores()
     k = max(1, min(rows, (1 << 22) // hidden))  # about 4 Mi elements per pass
     sl = slice(0, k)
     if op == "layernorm_bwd":
@@ -799,17 +943,19 @@ def oracle_beside(op, inp, rows, hidden, nbytes, seconds):
         if t >= seconds or reps >= 1000:
             break
     gbps = nbytes * (reps * k / rows) / t / 1e9
-    return {"GBps": round(gbps, 3), "cores": cores, "kind": "oracle",
+    return {"GBps": round(gbps, 3), "cores": cores, "cores_available": avail, "kind": "oracle",
             "sample": f"{reps} pass(es) over the first {k} of {rows} rows in {t:.2f} s"}
 
 
-def _op_rec(op, rows, hidden, nbytes, us, note=None, cpu=None):
+def _op_rec(op, rows, hidden, nbytes, us, note=None, cpu=None, ceil=None):
     gbps = nbytes / (us * 1e-6) / 1e9
     rec = {"op": op, "rows": rows, "hidden": hidden, "algorithmic_bytes": nbytes,
            "us_per_launch": round(us, 3), "GBps": round(gbps, 1),
            "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 1)}
     if note:
         rec["note"] = note
+    if ceil:
+        rec["same_traffic_ceiling"] = ceil
     if cpu:
         rec["cpu_oracle"] = cpu
     log(f"  {op} {rows}x{hidden}: {us:.2f} us, {gbps:.0f} GB/s"
@@ -832,11 +978,7 @@ def cpu_baseline(inp, seconds):
     """The oracle (fp64 loops, C) over the same workload, repeated for about
     `seconds`; rows are split over the host cores."""
     import oracle
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
+    cores, avail = _cores()
     x, r, w, eps = inp["x"], inp["r"], inp["w"], inp["eps"]
     offs = np.cumsum((0,) + SWEEP_ROWS)
     reps, t = 0, 0.0
@@ -861,6 +1003,9 @@ def cpu_baseline(inp, seconds):
         t1 = time.perf_counter() - t0
     nbytes1 = reps1 * sum(fused_bytes(rr) for rr in one_rows)
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": cores,
+            "cores_available": avail,
+            "cores_note": "threads = the cores in sched_getaffinity(0), capped by the per-GPU "
+                          "CPU share the host states in OMP_NUM_THREADS",
             "kind": "oracle",
             "sample": f"{reps} pass(es) of the full rows 1..8192 sweep at hidden 4096 "
                       f"({reps * sum(SWEEP_ROWS)} rows) in {t:.1f} s",

@@ -1,11 +1,25 @@
-// Measurement kernel for the benchmark only (not part of the normalization
-// library or its C ABI): the fused residual-add + RMSNorm forward's exact
-// memory traffic at hidden 4096 without its arithmetic.  Each row's x and
-// residual vectors are read with the same lane layout, launch shape and
-// non-temporal hints as fused_add_rmsnorm_kernel<4096, T, R>, and two outputs
-// are written (x to `residual`, the old residual to `out`); no reduction, no
-// barrier.  Its time is a same-traffic ceiling for the fused kernel on the
-// part it runs on.  Built into libnormceiling.so, loaded by bench.py.
+// Measurement kernels for the benchmark only (not part of the normalization
+// library or its C ABI), built into libnormceiling.so and loaded by bench.py:
+//
+//  * normceil_same_traffic_h4096: the fused residual-add + RMSNorm forward's
+//    exact memory traffic at hidden 4096 without its arithmetic.  Each row's x
+//    and residual vectors are read with the same lane layout, launch shape
+//    and non-temporal hints as fused_add_rmsnorm_kernel<4096, T, R>, and two
+//    outputs are written (x to `residual`, the old residual to `out`); no
+//    reduction, no barrier.
+//  * normceil_stream: grid-stride streaming over whole buffers, NR inputs read
+//    and NW outputs written (read-only, write-only, 1:1, 2:1, 2:2, 3:1): the
+//    part's practical HBM rate for each read/write mix, apart from any row
+//    structure.
+//  * normceil_rows: the memory traffic of a row-normalization operation in its
+//    own row layout (T lanes a row, V 16-byte accesses a lane, one row a
+//    workgroup at a time): NR input rows read, one output row written (the
+//    XOR of the inputs, so no load is dead), no arithmetic and no barrier;
+//    either one row per workgroup (grid = rows) or the persistent walk of the
+//    backward and ring kernels (G workgroups walk rows g, g + G, ..., with D
+//    rows in flight in a register ring).
+// Their times are same-traffic ceilings for the library's kernels on the part
+// they run on.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,5 +84,275 @@ extern "C" __attribute__((visibility("default"))) int normceil_same_traffic_h409
         e = launch<512, 1>(out, residual, x, rows, stream);
     else
         return 1;
+    return e == hipSuccess ? 0 : 2;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming probes.
+namespace {
+
+struct StreamArgs {
+    const u32x4* in[3];
+    u32x4* out[2];
+    int64_t n;  // 16-byte vectors per buffer
+};
+
+// Every lane handles vectors i = base + u * L (u < U, L = lanes in the grid)
+// per pass, base stepping by U * L: U independent accesses per buffer in
+// flight.  With no input, outputs get the vector index; with no output, the
+// inputs' XOR is kept and stored (to out[0] = a 16-byte sink per workgroup)
+// only if it equals a value the data never produces, so no load is dead and
+// no store is made.
+template <int NR, int NW, int U>
+__global__ __launch_bounds__(256) void stream_kernel(StreamArgs a) {
+    const int64_t lanes = (int64_t)gridDim.x * 256;
+    const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    u32x4 keep = {0u, 0u, 0u, 0u};
+    for (int64_t base = first; base < a.n; base += U * lanes) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * lanes;
+            u32x4 acc = {(uint32_t)i, (uint32_t)(i >> 32), 0u, 0u};
+            if (i < a.n) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const u32x4 t = rownorm::load_stream(a.in[r] + i);
+                    acc = r == 0 ? t : (acc ^ t);
+                }
+            }
+            v[u] = acc;
+        }
+        rownorm::issue_fence();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = base + u * lanes;
+            if constexpr (NW == 0) {
+                keep ^= v[u];
+            } else if (i < a.n) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) rownorm::store_stream(a.out[w] + i, v[u]);
+            }
+        }
+    }
+    if constexpr (NW == 0) {
+        if (keep.x == 0x9e3779b9u && keep.y == 0x7f4a7c15u && keep.z == 0xf39cc060u &&
+            keep.w == 0x5ced1a2bu)
+            a.out[0][blockIdx.x] = keep;
+    }
+}
+
+template <int NR, int NW, int U>
+hipError_t launch_stream(const StreamArgs& a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((stream_kernel<NR, NW, U>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int NR, int NW>
+hipError_t stream_by_unroll(const StreamArgs& a, int grid, int unroll, hipStream_t stream) {
+    switch (unroll) {
+        case 1: return launch_stream<NR, NW, 1>(a, grid, stream);
+        case 2: return launch_stream<NR, NW, 2>(a, grid, stream);
+        case 4: return launch_stream<NR, NW, 4>(a, grid, stream);
+        case 8: return launch_stream<NR, NW, 8>(a, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-layout traffic.
+struct RowArgs {
+    const void* in[3];
+    void* out;
+    int64_t rows;
+    int32_t row_bytes;
+};
+
+template <int NR, int V>
+struct RowSlot {
+    u32x4 v[NR][V];
+};
+
+template <int NR, int V>
+__device__ __forceinline__ void load_row_slot(RowSlot<NR, V>& s, const RowArgs& a, int64_t row,
+                                              int T, int lane) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const rownorm::rsrc_t rs = rownorm::row_rsrc(a.in[r], row, a.rows, a.row_bytes);
+#pragma unroll
+        for (int b = 0; b < V; ++b) s.v[r][b] = rownorm::rload_stream(rs, (b * T + lane) * 16);
+    }
+}
+
+template <int NR, int V>
+__device__ __forceinline__ void store_row_slot(const RowSlot<NR, V>& s, const RowArgs& a,
+                                               int64_t row, int T, int lane) {
+    const rownorm::rsrc_t ro = rownorm::row_rsrc(a.out, row, a.rows, a.row_bytes);
+#pragma unroll
+    for (int b = 0; b < V; ++b) {
+        u32x4 o = s.v[0][b];
+#pragma unroll
+        for (int r = 1; r < NR; ++r) o ^= s.v[r][b];
+        rownorm::rstore_stream(ro, (b * T + lane) * 16, o);
+    }
+}
+
+// Workgroup g walks rows g, g + G, ... with D rows in flight: the structure
+// of the backward rows kernels (buffer accesses through per-row descriptors,
+// rows past the end load zeros and store nothing, no branch in the loop).
+template <int NR, int V, int D, int LB>
+__global__ __launch_bounds__(LB) void row_traffic_kernel(RowArgs a) {
+    const int T = blockDim.x;
+    const int lane = threadIdx.x;
+    const int64_t G = gridDim.x;
+    const int64_t first = blockIdx.x;
+    const int64_t n = first < a.rows ? (a.rows - 1 - first) / G + 1 : 0;
+    RowSlot<NR, V> buf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        load_row_slot<NR, V>(buf[d], a, first + d * G, T, lane);
+        rownorm::issue_fence();
+    }
+    for (int64_t i = 0; i < n; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t r = first + (i + d) * G;
+            store_row_slot<NR, V>(buf[d], a, r, T, lane);
+            rownorm::issue_fence();
+            load_row_slot<NR, V>(buf[d], a, r + D * G, T, lane);
+            rownorm::issue_fence();
+        }
+    }
+}
+
+// The ring takes NR * V * D * 4 VGPRs a lane and NR * D row descriptors
+// (4 SGPRs each); only rings that leave room in the lane's share of the
+// register file (256 VGPRs up to 512 lanes, 128 at 1024) and hold at most 12
+// descriptors are compiled, so no instantiation spills.
+template <int NR, int V, int D, int LB>
+constexpr bool ring_fits() {
+    return NR * V * D * 4 <= (LB > 512 ? 96 : 192) && NR * D <= 12;
+}
+
+template <int NR, int V, int D>
+hipError_t launch_rows(const RowArgs& a, int lanes, int64_t grid, hipStream_t stream) {
+    if (lanes > 512) {
+        if constexpr (ring_fits<NR, V, D, 1024>())
+            hipLaunchKernelGGL((row_traffic_kernel<NR, V, D, 1024>), dim3((unsigned)grid),
+                               dim3(lanes), 0, stream, a);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        if constexpr (ring_fits<NR, V, D, 512>())
+            hipLaunchKernelGGL((row_traffic_kernel<NR, V, D, 512>), dim3((unsigned)grid),
+                               dim3(lanes), 0, stream, a);
+        else
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int NR, int V>
+hipError_t rows_by_depth(const RowArgs& a, int lanes, int64_t grid, int depth,
+                         hipStream_t stream) {
+    switch (depth) {
+        case 1: return launch_rows<NR, V, 1>(a, lanes, grid, stream);
+        case 2: return launch_rows<NR, V, 2>(a, lanes, grid, stream);
+        case 3: return launch_rows<NR, V, 3>(a, lanes, grid, stream);
+        case 4: return launch_rows<NR, V, 4>(a, lanes, grid, stream);
+        case 8: return launch_rows<NR, V, 8>(a, lanes, grid, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int NR>
+hipError_t rows_by_vecs(const RowArgs& a, int lanes, int vecs, int64_t grid, int depth,
+                        hipStream_t stream) {
+    switch (vecs) {
+        case 1: return rows_by_depth<NR, 1>(a, lanes, grid, depth, stream);
+        case 2: return rows_by_depth<NR, 2>(a, lanes, grid, depth, stream);
+        case 4: return rows_by_depth<NR, 4>(a, lanes, grid, depth, stream);
+        case 8: return rows_by_depth<NR, 8>(a, lanes, grid, depth, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool bad_ptr(const void* p) { return !p || reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
+}  // namespace
+
+// Streams NR in {0..3} input buffers and NW in {0..2} output buffers of
+// `bytes` bytes each (a multiple of 16; at least one buffer; when NW == 0,
+// outs[0] must hold 16 bytes per workgroup of `grid`, a sink that is never
+// written in practice).  grid in [1, 2^20] workgroups of 256 lanes; unroll in
+// {1, 2, 4, 8}.  Returns 0 on success, 1 for invalid arguments, 2 when the
+// launch fails.
+extern "C" __attribute__((visibility("default"))) int normceil_stream(
+    const void* const* ins, int32_t n_in, void* const* outs, int32_t n_out, int64_t bytes,
+    int32_t grid, int32_t unroll, hipStream_t stream) {
+    if (n_in < 0 || n_in > 3 || n_out < 0 || n_out > 2 || n_in + n_out == 0) return 1;
+    if (bytes < 0 || bytes % 16 || grid < 1 || grid > (1 << 20)) return 1;
+    if (n_out == 0 && (!outs || bad_ptr(outs[0]))) return 1;
+    StreamArgs a{};
+    for (int r = 0; r < n_in; ++r) {
+        if (!ins || bad_ptr(ins[r])) return 1;
+        a.in[r] = static_cast<const u32x4*>(ins[r]);
+    }
+    for (int w = 0; w < n_out; ++w) {
+        if (bad_ptr(outs[w])) return 1;
+        a.out[w] = static_cast<u32x4*>(outs[w]);
+    }
+    if (n_out == 0) a.out[0] = static_cast<u32x4*>(outs[0]);
+    a.n = bytes / 16;
+    if (a.n == 0) return 0;
+    hipError_t e = hipErrorInvalidValue;
+    const int mix = n_in * 4 + n_out;
+    switch (mix) {
+        case 1 * 4 + 0: e = stream_by_unroll<1, 0>(a, grid, unroll, stream); break;
+        case 0 * 4 + 1: e = stream_by_unroll<0, 1>(a, grid, unroll, stream); break;
+        case 1 * 4 + 1: e = stream_by_unroll<1, 1>(a, grid, unroll, stream); break;
+        case 2 * 4 + 1: e = stream_by_unroll<2, 1>(a, grid, unroll, stream); break;
+        case 2 * 4 + 2: e = stream_by_unroll<2, 2>(a, grid, unroll, stream); break;
+        case 3 * 4 + 1: e = stream_by_unroll<3, 1>(a, grid, unroll, stream); break;
+        default: return 1;
+    }
+    if (e == hipErrorInvalidValue) return 1;
+    return e == hipSuccess ? 0 : 2;
+}
+
+// Row-layout traffic of an operation: n_in in {1, 2, 3} input matrices and one
+// output matrix, contiguous [rows, hidden] bf16, hidden = vecs * 8 * lanes,
+// lanes a multiple of 64 in [64, 1024], vecs in {1, 2, 4, 8}, every matrix under
+// 2^31 bytes.  grid = 0: one row per workgroup (grid = rows, depth must be
+// 1); else grid workgroups walk the rows with `depth` in {1, 2, 3, 4, 8} rows
+// in flight, where n_in * vecs * depth <= 48 (24 above 512 lanes) and
+// n_in * depth <= 12.  The output may not overlap an input.  Returns 0 on success, 1
+// for invalid arguments, 2 when the launch fails.
+extern "C" __attribute__((visibility("default"))) int normceil_rows(
+    const void* const* ins, int32_t n_in, void* out, int64_t rows, int64_t hidden,
+    int32_t lanes, int32_t vecs, int64_t grid, int32_t depth, hipStream_t stream) {
+    if (n_in < 1 || n_in > 3 || !ins || bad_ptr(out)) return 1;
+    if (rows < 0 || lanes < 64 || lanes > 1024 || lanes % 64) return 1;
+    if (vecs != 1 && vecs != 2 && vecs != 4 && vecs != 8) return 1;
+    if (hidden != (int64_t)vecs * 8 * lanes) return 1;
+    if (rows * hidden * 2 >= (int64_t(1) << 31)) return 1;
+    if (grid < 0 || grid > (int64_t(1) << 31) - 1 || (grid == 0 && depth != 1)) return 1;
+    RowArgs a{};
+    for (int r = 0; r < n_in; ++r) {
+        if (bad_ptr(ins[r])) return 1;
+        a.in[r] = ins[r];
+    }
+    a.out = out;
+    a.rows = rows;
+    a.row_bytes = (int32_t)(hidden * 2);
+    if (rows == 0) return 0;
+    const int64_t g = grid == 0 ? rows : grid;
+    hipError_t e = hipErrorInvalidValue;
+    switch (n_in) {
+        case 1: e = rows_by_vecs<1>(a, lanes, vecs, g, depth, stream); break;
+        case 2: e = rows_by_vecs<2>(a, lanes, vecs, g, depth, stream); break;
+        case 3: e = rows_by_vecs<3>(a, lanes, vecs, g, depth, stream); break;
+    }
+    if (e == hipErrorInvalidValue) return 1;
     return e == hipSuccess ? 0 : 2;
 }

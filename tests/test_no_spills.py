@@ -23,7 +23,7 @@ def _report(src):
                     reason="hipcc not available")
 def test_no_kernel_spills_registers():
     with cf.ThreadPoolExecutor(max_workers=len(B.SOURCES)) as ex:
-        reports = list(ex.map(_report, B.SOURCES))
+        reports = list(ex.map(_report, B.SOURCES + B.CEILING_SOURCES))
     kernels = 0
     for src, text in reports:
         name = None
