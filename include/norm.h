@@ -15,13 +15,19 @@
  *     same page, reviewer guide, split logic): any hidden >= 1, row strides,
  *     and bf16 pointers aligned to 2 bytes or more.  Rows are read with the
  *     widest access (16, 8, 4 or 2 bytes) that hidden, every row stride and
- *     every bf16 pointer allow.  Largest hidden: forward 65536 (LayerNorm
- *     49152) with 16-byte accesses, 8192 * (access elements) otherwise;
- *     backward 32768 with 16-byte accesses (above 16384 the row is staged
- *     in LDS: "TMA inner persistent scheduler", description summary, the
- *     shared-memory persistent buffer), 16384 with 8-byte accesses, 8192
- *     otherwise.  The row-split forward entry points below take LayerNorm
- *     rows up to 65536 too.
+ *     every bf16 pointer allow.  One workgroup holds the row on chip up to
+ *     hidden 65536 forward (LayerNorm 49152) with 16-byte accesses, 8192 *
+ *     (access elements) otherwise; backward 32768 with 16-byte accesses
+ *     (above 16384 the row is staged in LDS: "TMA inner persistent
+ *     scheduler", description summary, the shared-memory persistent
+ *     buffer), 16384 with 8-byte accesses, 8192 otherwise.  Wider rows with
+ *     16-byte accesses (hidden a multiple of 8, up to 2^20) run on streamed
+ *     kernels that read the row twice: forward, one pass for the statistic
+ *     and one, mostly from the Infinity Cache, to normalize; backward, a
+ *     per-row reduction kernel, then workgroups over 16384-column tiles
+ *     (the two reductions per row go to the workspace).  Wider rows with
+ *     narrower accesses are unsupported.  The row-split forward entry
+ *     points below spread few wide rows over several workgroups instead.
  * The library picks the family; the arithmetic and results (within rounding)
  * are the same.
  *
@@ -200,10 +206,14 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
  * device, set up on the first call on a device and kept until the process
  * ends) instead of a caller-given workspace.  Allocates nothing: no
  * hipMalloc, no hipFree, no allocating library call.  Returns
- * NORM_ERROR_WORKSPACE when the launch's partial sums (2 * 4 * hidden bytes,
- * hidden rounded up to 64 off the compiled sizes, for each of its up to 256
- * workgroups) would exceed NORM_NOALLOC_SCRATCH_BYTES: every hidden up to
- * 16384 fits, wider rows fit only with fewer rows (32768: up to 128 rows).
+ * NORM_ERROR_WORKSPACE when the launch's workspace
+ * (norm_layernorm_bwd_workspace_bytes for contiguous rows: 2 * 4 * hidden
+ * bytes, hidden rounded up to 64 off the compiled sizes, for each of its up
+ * to 256 workgroups; rows past 32768 columns: for each of its up to
+ * 255 / ceil(hidden / 16384) row walkers, plus 8 bytes a row) would exceed
+ * NORM_NOALLOC_SCRATCH_BYTES: every hidden up to 16384 fits, rows of
+ * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows), and
+ * wider rows fit up to at least 16384 rows.
  * NORM_ERROR_DEVICE when the
  * scratch array's address cannot be found on the current device.  All calls
  * on one device share its scratch array: calls that overlap in time on that
@@ -423,8 +433,8 @@ NORM_API uint32_t norm_split_set_spin_limit(uint32_t polls);
  * hidden is a multiple of 8 and either up to 8 rows move >= 256 KiB each
  * (fused op: 8 * hidden bytes) or >= 192 KiB each (the others: 4 * hidden
  * bytes), 9 to 32 rows
- * move >= 384 KiB each, or no one-workgroup-per-row kernel holds the row
- * (LayerNorm above 49152; up to 64 rows).  Chunks aim at about 64 KiB of
+ * move >= 384 KiB each, or no one-workgroup-per-row kernel holds the row on
+ * chip (above 65536, LayerNorm above 49152; up to 64 rows).  Chunks aim at about 64 KiB of
  * traffic (8192 columns fused, 16384 RMSNorm, 12288 LayerNorm), at most
  * max(4, 64 / rows) a row and rows * k <= cu_count.  Pure host logic when
  * cu_count > 0. */

@@ -36,6 +36,7 @@ SOURCES = [
     "k_rmsnorm_bwd_dyn.hip",
     "k_split.hip",
     "k_bwd_wide.hip",
+    "k_stream.hip",
 ]
 
 # Benchmark-only measurement kernel (not part of the normalization library):

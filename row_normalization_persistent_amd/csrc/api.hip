@@ -39,7 +39,7 @@ constexpr int64_t kMaxLd = int64_t(1) << 40;  // elements
 // Largest hidden any kernel family can hold in registers (the run-time path,
 // 16-byte accesses, 1024 lanes x 8 accesses); the exact limit depends on the
 // operation and the access width (see the tables).
-constexpr int64_t kMaxHidden = 65536;
+constexpr int64_t kMaxHidden = kStreamMaxHidden;  // 2^20: the streamed kernels' limit
 
 bool valid_elems(int32_t w) { return w == 0 || w == 1 || w == 2 || w == 4 || w == 8; }
 
@@ -249,9 +249,10 @@ const WideBwdEntry* find_wide(norm_op op, int64_t hidden, int lanes, int w) {
     return nullptr;
 }
 
-// Widest backward row for accesses of w elements (the wide kernels take over
-// above the run-time kernels' widest row at 16-byte accesses).
-int64_t max_bwd_hidden(norm_op op, int w) {
+// Widest backward row one workgroup holds on chip for accesses of w elements
+// (the LDS-staged kernels take over above the run-time kernels' widest row at
+// 16-byte accesses).
+int64_t max_bwd_resident(norm_op op, int w) {
     int64_t m = max_dyn_hidden(dyn_bwd_table(op), w);
     if (w == 8) {
         const auto& t = op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_wide_table()
@@ -259,6 +260,31 @@ int64_t max_bwd_hidden(norm_op op, int w) {
         for (const WideBwdEntry& e : t) m = std::max<int64_t>(m, (int64_t)e.vecs * 8 * kWideBwdLanes);
     }
     return m;
+}
+
+// Streamed rows (kernels_stream.hpp): wider than every on-chip kernel holds,
+// 16-byte accesses, up to kStreamMaxHidden.
+bool stream_fwd_ok(norm_op op, int64_t hidden, int w) {
+    return w == 8 && hidden % 8 == 0 && hidden <= kStreamMaxHidden &&
+           hidden > max_dyn_hidden(dyn_fwd_table(op), 8);
+}
+
+bool stream_bwd_ok(norm_op op, int64_t hidden, int w) {
+    return w == 8 && hidden % 8 == 0 && hidden <= kStreamMaxHidden &&
+           hidden > max_bwd_resident(op, 8);
+}
+
+// Widest backward row for accesses of w elements.
+int64_t max_bwd_hidden(norm_op op, int w) {
+    return w == 8 ? kStreamMaxHidden : max_bwd_resident(op, w);
+}
+
+// Column tiles of a streamed backward row, and its default row walkers: one
+// 512-lane workgroup per (walker, tile), at most 255 in all (one per CU,
+// leaving the partial sums of any width under 32 MiB).
+int32_t stream_tiles(int64_t hidden) { return (int32_t)ceil_div(hidden, kStreamTileCols); }
+int32_t stream_walkers(int64_t rows, int64_t hidden) {
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles(hidden)));
 }
 
 // partial-sum slabs per walker: dweight and dbias for LayerNorm, dweight for RMSNorm
@@ -514,6 +540,7 @@ norm_launch_cfg choose_dyn_fwd(norm_op op, int64_t rows, int64_t hidden, int w, 
             return norm_launch_cfg{lanes, 2 * r, 0, w};
         return norm_launch_cfg{lanes, r, 0, w};
     }
+    if (stream_fwd_ok(op, hidden, w)) return norm_launch_cfg{kStreamFwdLanes, 1, 0, 8};
     return norm_launch_cfg{0, 0, 0, w};
 }
 
@@ -557,6 +584,8 @@ norm_launch_cfg choose_dyn_bwd(norm_op op, int64_t rows, int64_t hidden, int w,
         }
     if (find_wide(op, hidden, kWideBwdLanes, w))
         return norm_launch_cfg{kWideBwdLanes, 1, default_bwd_grid(rows), w};
+    if (stream_bwd_ok(op, hidden, w))
+        return norm_launch_cfg{kStreamTileLanes, 1, stream_walkers(rows, hidden), 8};
     return norm_launch_cfg{0, 0, 0, w};
 }
 
@@ -567,6 +596,11 @@ size_t static_ws_bytes(norm_op op, int64_t hidden, int64_t grid) {
 size_t dyn_ws_bytes(norm_op op, int64_t hidden, int64_t slabs) {
     return (size_t)slabs * (size_t)bwd_outs(op) * (size_t)dyn_padded_hidden(hidden) *
            sizeof(float);
+}
+
+// Streamed backward: the walkers' slabs, then two fp32 per row.
+size_t stream_ws_bytes(norm_op op, int64_t hidden, int64_t walkers, int64_t rows) {
+    return dyn_ws_bytes(op, hidden, walkers) + (size_t)std::max<int64_t>(rows, 0) * 8;
 }
 
 // The column reduce addresses the workspace with 32-bit byte offsets and
@@ -667,7 +701,8 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
     const bool contiguous = L.contiguous, compiled_ok = L.compiled_ok;
 
     if (!compiled_ok && !(cfg && cfg->vector_elems == 0) &&
-        c.hidden > max_dyn_hidden(dyn_fwd_table(op), cfg ? cfg->vector_elems : w_max))
+        c.hidden > max_dyn_hidden(dyn_fwd_table(op), cfg ? cfg->vector_elems : w_max) &&
+        !stream_fwd_ok(op, c.hidden, cfg ? cfg->vector_elems : w_max))
         return NORM_ERROR_UNSUPPORTED_HIDDEN;
 
     norm_launch_cfg k;
@@ -722,6 +757,17 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         return NORM_ERROR_INVALID_VALUE;
     const DynFwdEntry* e = find_dyn(dyn_fwd_table(op), c.hidden, k.vector_elems,
                                     k.threads_per_row, k.rows_per_block / r);
+    if (!e && k.vector_elems == 8 && k.threads_per_row == kStreamFwdLanes &&
+        k.rows_per_block == 1 && stream_fwd_ok(op, c.hidden, 8)) {
+        // a row no workgroup holds on chip: the streamed two-pass kernel
+        const DynFwdArgs a{c.out,     c.residual, c.x,   c.weight, c.bias,   c.mean,
+                           c.rstd,    c.ld_out,   ld_res, c.ld_x,  c.rows,   (int32_t)c.hidden,
+                           c.eps};
+        const int sop = op == NORM_OP_FUSED_ADD_RMSNORM ? kSplitFused
+                        : op == NORM_OP_LAYERNORM_FWD   ? kSplitLn
+                                                        : kSplitRms;
+        return from_hip(launch_stream_fwd(sop, a, stream));
+    }
     if (!e) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
     const int64_t groups = ceil_div(c.rows, k.rows_per_block);
     if (groups > INT32_MAX || groups * dyn_block_size(k.threads_per_row) > (int64_t)UINT32_MAX)
@@ -941,7 +987,11 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
             !row_set_fits(k.threads_per_row, k.rows_per_block,
                           std::max({c.ld_dx, c.ld_dy, c.ld_x, ld_dres}), c.hidden))
             return NORM_ERROR_INVALID_VALUE;
-        if (k.grid == 0) k.grid = default_bwd_grid(c.rows, k.rows_per_block);
+        if (k.grid == 0)
+            k.grid = k.vector_elems == 8 && k.threads_per_row == kStreamTileLanes &&
+                             stream_bwd_ok(op, c.hidden, 8)
+                         ? stream_walkers(c.rows, c.hidden)
+                         : default_bwd_grid(c.rows, k.rows_per_block);
     } else {
         k = compiled_ok ? choose_bwd(op, c.rows, c.hidden)
                         : choose_dyn_bwd(op, c.rows, c.hidden, w_max,
@@ -951,6 +1001,7 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
 
     const BwdEntry* se = nullptr;
     DynBwdLauncher dyn_launch = nullptr;
+    bool streamed = false;
     size_t ws_need = 0;
     if (k.vector_elems == 0) {
         se = find_bwd(op, c.hidden, k.threads_per_row);
@@ -963,10 +1014,17 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         else if (const WideBwdEntry* we =
                      find_wide(op, c.hidden, k.threads_per_row, k.vector_elems))
             dyn_launch = we->launch;
-        if (!dyn_launch) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
-        const int64_t slabs = k.grid;  // one slab per workgroup
-        if (!dyn_slabs_fit(op, c.hidden, slabs)) return NORM_ERROR_INVALID_VALUE;
-        ws_need = dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
+        else if (k.vector_elems == 8 && k.threads_per_row == kStreamTileLanes &&
+                 stream_bwd_ok(op, c.hidden, 8))
+            streamed = true;  // row statistics, then column tiles (kernels_stream.hpp)
+        if (!dyn_launch && !streamed)
+            return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
+        const int64_t slabs = k.grid;  // one slab per workgroup (streamed: per walker)
+        if (!dyn_slabs_fit(op, c.hidden, slabs) ||
+            (streamed && slabs * stream_tiles(c.hidden) > INT32_MAX))
+            return NORM_ERROR_INVALID_VALUE;
+        ws_need = streamed ? stream_ws_bytes(op, c.hidden, any ? slabs : 0, any ? c.rows : 0)
+                           : dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
     }
 
     const int64_t mrows = any ? c.rows : 0;
@@ -1004,6 +1062,9 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
                        c.dres,  c.weight, (float*)ws, c.dweight, c.dbias,
                        c.ld_dx, c.ld_dy,  c.ld_x,    ld_dres, c.rows,
                        (int32_t)c.hidden, k.grid, c.eps};
+    if (streamed)
+        return from_hip(launch_stream_bwd(op == NORM_OP_LAYERNORM_BWD, a,
+                                          stream_tiles(c.hidden), k.grid, stream));
     return from_hip(dyn_launch(a, stream));
 }
 
@@ -1019,6 +1080,10 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         }
         if (!valid_elems(cfg->vector_elems) || cfg->threads_per_row <= 0) return 0;
         const int r = dyn_rows_per_block(cfg->threads_per_row);
+        if (cfg->vector_elems == 8 && cfg->threads_per_row == kStreamTileLanes &&
+            stream_bwd_ok(op, hidden, 8))
+            return stream_ws_bytes(op, hidden,
+                                   cfg->grid > 0 ? cfg->grid : stream_walkers(rows, hidden), rows);
         const int64_t g = cfg->grid > 0 ? cfg->grid : default_bwd_grid(rows, r);
         return dyn_ws_bytes(op, hidden, g);
     }
@@ -1029,7 +1094,9 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         if (hidden % w) continue;
         const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w, hidden);
         if (k.threads_per_row)
-            need = std::max(need, dyn_ws_bytes(op, hidden, k.grid));
+            need = std::max(need, stream_bwd_ok(op, hidden, w) && w == 8
+                                      ? stream_ws_bytes(op, hidden, k.grid, rows)
+                                      : dyn_ws_bytes(op, hidden, k.grid));
     }
     return need;
 }
@@ -1351,7 +1418,12 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     int depth = 0;
     const WideBwdEntry* wide = dyn && is_bwd(op) ? find_wide(op, hidden, c.threads_per_row, w)
                                                   : nullptr;
-    if (wide) {
+    const bool streamed = dyn && (is_bwd(op) ? !wide && stream_bwd_ok(op, hidden, w)
+                                             : stream_fwd_ok(op, hidden, w));
+    if (streamed) {
+        vecs = is_bwd(op) ? kStreamTileVecs : 0;
+        depth = is_bwd(op) ? (op == NORM_OP_FUSED_ADD_RMSNORM_BWD ? 2 : 3) : 0;
+    } else if (wide) {
         vecs = wide->vecs;
         depth = 1;
     } else if (dyn && is_bwd(op)) {
@@ -1370,8 +1442,22 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     if (is_bwd(op)) {
         const int64_t slabs = c.grid;
         const int64_t padded = dyn ? dyn_padded_hidden(hidden) : hidden;
-        char kern[96];
-        if (wide)
+        char grid_text[64];
+        if (streamed)
+            std::snprintf(grid_text, sizeof grid_text, "%d row walkers x %d column tiles = %lld",
+                          c.grid, stream_tiles(hidden),
+                          (long long)c.grid * stream_tiles(hidden));
+        else
+            std::snprintf(grid_text, sizeof grid_text, "%d", c.grid);
+        char kern[160];
+        if (streamed)
+            std::snprintf(kern, sizeof kern,
+                          "stream_bwd_stats_kernel<%s> (1024 lanes a row), then "
+                          "stream_bwd_tile_kernel<%d,%s,%d> over %d column tiles of %d",
+                          op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm", vecs,
+                          op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?", depth,
+                          stream_tiles(hidden), kStreamTileCols);
+        else if (wide)
             std::snprintf(kern, sizeof kern, "norm_bwd_wide_kernel<%d,%s> (x, dy staged in LDS)",
                           vecs, op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?");
         else if (dyn)
@@ -1386,15 +1472,16 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         n = std::snprintf(tmp, sizeof tmp,
                           "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
                           "workgroup, %d %d-byte accesses per lane, ring of %d rows) on a "
-                          "persistent grid of %d workgroups, then norm_bwd_colreduce_kernel "
+                          "persistent grid of %s workgroups, then norm_bwd_colreduce_kernel "
                           "(%lld workgroups of %d) over %lld slabs; workspace %zu bytes",
                           kNames[op], (long long)rows, (long long)hidden, kern,
-                          c.threads_per_row, c.rows_per_block, vecs, 2 * w, depth, c.grid,
+                          c.threads_per_row, c.rows_per_block, vecs, 2 * w, depth, grid_text,
                           (long long)(bwd_outs(op) * padded / colreduce_cols(slabs)),
                           kColReduceThreads,
                           (long long)slabs,
-                          dyn ? dyn_ws_bytes(op, hidden, rows > 0 ? slabs : 0)
-                              : static_ws_bytes(op, hidden, rows > 0 ? c.grid : 0));
+                          streamed ? stream_ws_bytes(op, hidden, rows > 0 ? slabs : 0, rows)
+                          : dyn    ? dyn_ws_bytes(op, hidden, rows > 0 ? slabs : 0)
+                                   : static_ws_bytes(op, hidden, rows > 0 ? c.grid : 0));
     } else {
         const char* kern = op == NORM_OP_FUSED_ADD_RMSNORM ? "fused_add_rmsnorm"
                            : op == NORM_OP_RMSNORM_FWD     ? "rmsnorm_fwd"
@@ -1402,7 +1489,10 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         char inst[96];
         const FwdEntry* ring =
             c.grid > 0 ? ring_entry(op, hidden, c.threads_per_row, rows, c.grid) : nullptr;
-        if (dyn) {
+        if (streamed) {
+            std::snprintf(inst, sizeof inst, "stream_fwd_kernel<%s> (two passes over the row)",
+                          kern);
+        } else if (dyn) {
             int cu = cu_count;
             if (cu <= 0 && current_cu_count(&cu) != NORM_SUCCESS) return -1;
             const bool late =
@@ -1427,7 +1517,16 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         }
         const int block = dyn ? dyn_block_size(c.threads_per_row)
                               : c.threads_per_row * c.rows_per_block;
-        if (ring)
+        if (streamed)
+            n = std::snprintf(tmp, sizeof tmp,
+                              "%s rows=%lld hidden=%lld: %s (%d lanes per row, 1 rows per "
+                              "workgroup of %d, %lld 16-byte accesses per lane in passes of %d), "
+                              "grid %lld",
+                              kNames[op], (long long)rows, (long long)hidden, inst,
+                              c.threads_per_row, c.threads_per_row,
+                              (long long)ceil_div(hidden / 8, c.threads_per_row), 4,
+                              (long long)std::min<int64_t>(rows, kStreamMaxGrid));
+        else if (ring)
             n = std::snprintf(tmp, sizeof tmp,
                               "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d 16-byte "
                               "accesses per lane, ring of %d rows) on a persistent grid of %d "
@@ -1487,6 +1586,10 @@ int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out, int3
             if (find_dyn(dyn_fwd_table(op), hidden, w, lanes, k))
                 put(norm_launch_cfg{lanes, r * k, 0, w});
     }
+    // streamed rows (wider than the on-chip kernels hold)
+    if (is_bwd(op) ? stream_bwd_ok(op, hidden, w) : stream_fwd_ok(op, hidden, w))
+        put(is_bwd(op) ? norm_launch_cfg{kStreamTileLanes, 1, 0, 8}
+                       : norm_launch_cfg{kStreamFwdLanes, 1, 0, 8});
     return n;
 }
 

@@ -181,6 +181,25 @@ struct SplitEntry {
 
 const std::vector<SplitEntry>& split_table();
 
+// ---- streamed rows (wider than registers and LDS hold; kernels_stream.hpp) ------
+// Forward: 1024-lane workgroups walk the rows, each row read twice.  Backward:
+// a 1024-lane per-row reduction kernel, then 512-lane workgroups over tiles of
+// kStreamTileVecs * 8 * 512 columns.  16-byte accesses only.
+constexpr int kStreamFwdLanes = 1024;
+constexpr int kStreamTileLanes = 512;
+constexpr int kStreamTileVecs = 4;
+constexpr int kStreamTileCols = kStreamTileLanes * kStreamTileVecs * 8;  // 16384
+constexpr int64_t kStreamMaxGrid = 65536;  // workgroups of the row-walking kernels
+constexpr int64_t kStreamMaxHidden = int64_t(1) << 20;
+
+// op: kSplitFused / kSplitRms / kSplitLn (the row-split numbering)
+hipError_t launch_stream_fwd(int op, const DynFwdArgs& a, hipStream_t stream);
+// Stats kernel, tile kernel and column reduce.  ln: LayerNorm, else RMSNorm
+// (with a.dres: the fused op).  The workspace holds `walkers` slabs of
+// [outs][padded] fp32, then two fp32 per row.
+hipError_t launch_stream_bwd(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t walkers,
+                             hipStream_t stream);
+
 // Workgroup size of the run-time path for T lanes per row: rows narrower than
 // 256 lanes are packed 256 / T to a workgroup.
 constexpr int dyn_block_size(int lanes) { return lanes < 256 ? 256 : lanes; }

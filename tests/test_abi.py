@@ -68,7 +68,11 @@ def test_compiled_shapes_cover_every_hidden_size():
                 assert h % (8 * c.threads_per_row) == 0
                 assert c.threads_per_row * c.rows_per_block <= 1024
         assert rn.list_configs(op, 0) == []
-        assert rn.list_configs(op, 70000) == []
+        assert rn.list_configs(op, (1 << 20) + 8) == []
+        # rows wider than the on-chip kernels hold: the streamed shape only
+        stream = rn.Cfg(512 if rn.OPS[op] >= 3 else 1024, 1, 0, 8)
+        assert rn.list_configs(op, 70000) == [stream]
+        assert rn.list_configs(op, 1 << 20) == [stream]
 
 
 def test_runtime_hidden_shapes():
@@ -88,10 +92,19 @@ def test_runtime_hidden_shapes():
             assert sel.runtime_hidden == (h not in rn.HIDDEN_SIZES)
             if sel.runtime_hidden:
                 assert sel in cfgs or rn.OPS[op] >= 3, (op, h, sel)
-    # the widest rows each family holds
+    # the widest rows each family holds on chip; past them the streamed kernels
+    # take 16-byte rows up to 2^20, and narrower accesses stay unsupported
     assert rn.select_config("fused_add_rmsnorm", 64, 65536, cu_count=256).threads_per_row == 1024
+    assert "stream" not in rn.describe_config("fused_add_rmsnorm", 64, 65536, cu_count=256)
     for op, h in (("layernorm_fwd", 49152 + 8), ("rmsnorm_fwd", 65536 + 8),
-                  ("layernorm_bwd", 32768 + 8), ("rmsnorm_bwd", 8193)):
+                  ("fused_add_rmsnorm", 65536 + 8), ("layernorm_bwd", 32768 + 8),
+                  ("rmsnorm_bwd", 32768 + 8), ("fused_add_rmsnorm_bwd", 1 << 20)):
+        c = rn.select_config(op, 64, h, cu_count=256)
+        assert c.vector_elems == 8 and c.threads_per_row == (512 if "bwd" in op else 1024), op
+        assert "stream_" in rn.describe_config(op, 64, h, cu_count=256)
+    for op, h in (("layernorm_fwd", 49152 + 4), ("rmsnorm_fwd", 65536 + 2),
+                  ("layernorm_bwd", 32768 + 4), ("rmsnorm_bwd", 8193),
+                  ("fused_add_rmsnorm", (1 << 20) + 8)):
         with pytest.raises(rn.NormError) as e:
             rn.select_config(op, 64, h, cu_count=256)
         assert e.value.status == UNSUPPORTED
@@ -221,7 +234,10 @@ def test_describe_config():
     d = rn.describe_config("layernorm_bwd", 8192, 4096, cu_count=256)
     assert "persistent grid of 256" in d and f"workspace {rn.workspace_bytes(8192, 4096)}" in d
     with pytest.raises(rn.NormError):
-        rn.describe_config("rmsnorm_fwd", 4, 70000, cu_count=256)
+        rn.describe_config("rmsnorm_fwd", 4, 70002, cu_count=256)
+    d = rn.describe_config("layernorm_bwd", 1000, 65536, cu_count=256)
+    assert "63 row walkers x 4 column tiles" in d and \
+        f"workspace {rn.workspace_bytes(1000, 65536)}" in d
     d = rn.describe_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     c = rn.select_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     assert f"rmsnorm_fwd_dyn_kernel<8,{c.threads_per_row}," in d
@@ -251,7 +267,13 @@ def test_workspace_bytes():
     # run-time shapes: one slab per workgroup, whatever its rows per workgroup
     assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 2 * 1024 * 4
     assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
-    assert rn.workspace_bytes(10, 70000) == 0
+    assert rn.workspace_bytes(10, (1 << 20) + 8) == 0
+    # streamed rows: one slab per row walker (255 // column tiles of 16384, at
+    # most the rows), then two fp32 per row
+    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 8
+    assert rn.workspace_bytes(1000, 65536) == 63 * 2 * 65536 * 4 + 1000 * 8
+    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 63 * 65536 * 4 + 1000 * 8
+    assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == 5 * 2 * 65536 * 4 + 8000
     assert rn.workspace_bytes(-1, 4096) == 0
 
 
@@ -270,7 +292,8 @@ def test_fused_validation():
     assert fused(eps=float("nan")) == INVALID
     assert fused(eps=float("inf")) == INVALID
     assert fused(eps=-1e-6) == INVALID
-    assert fused(hidden=70000) == UNSUPPORTED
+    assert fused(hidden=(1 << 20) + 8) == UNSUPPORTED
+    assert fused(hidden=70002) == UNSUPPORTED  # 4-byte accesses stop at 16384
     assert fused(hidden=0) == UNSUPPORTED
     assert fused(out=0) == INVALID
     assert fused(res=0) == INVALID
@@ -306,7 +329,7 @@ def rms(out=A, x=A + MB, w=A + 2 * MB, rows=4, hidden=2048, eps=1e-6):
 
 def test_rmsnorm_validation():
     assert rms(rows=0) == SUCCESS
-    assert rms(hidden=65544) == UNSUPPORTED
+    assert rms(hidden=65546) == UNSUPPORTED
     assert rms(out=0) == INVALID
     assert rms(out=A + 1) == MISALIGNED
     assert rms(out=A + MB + 16) == INVALID  # partial overlap with x
@@ -321,8 +344,8 @@ def lnf(y=A, mean=A + MB, rstd=A + MB + 65536, x=A + 2 * MB, w=A + 3 * MB, b=A +
 def test_layernorm_fwd_validation():
     assert lnf(rows=0) == SUCCESS
     assert lnf(eps=-1.0) == INVALID
-    assert lnf(hidden=70000) == UNSUPPORTED
-    assert lnf(hidden=49152 + 8) == UNSUPPORTED  # LayerNorm's run-time kernels stop at 49152
+    assert lnf(hidden=(1 << 20) + 8) == UNSUPPORTED
+    assert lnf(hidden=49152 + 4) == UNSUPPORTED  # past 49152 only 16-byte rows (streamed)
     assert lnf(b=0) == INVALID
     assert lnf(mean=0) == INVALID   # mean and rstd are both given or both null
     assert lnf(rstd=0) == INVALID
@@ -363,7 +386,8 @@ def test_layernorm_bwd_validation():
     assert lnb() == WORKSPACE
     assert lnb(rows=-2) == INVALID
     assert lnb(eps=float("nan")) == INVALID
-    assert lnb(hidden=32776) == UNSUPPORTED
+    assert lnb(hidden=32778) == UNSUPPORTED  # past 32768 only 16-byte rows (streamed)
+    assert lnb(hidden=(1 << 20) + 8) == UNSUPPORTED
     assert lnb(hidden=5000) == WORKSPACE  # run-time kernels (workspace sized for 4096)
     assert lnb(dw=0) == INVALID
     assert lnb(ws=0) == INVALID
@@ -411,7 +435,7 @@ def test_rmsnorm_bwd_validation():
     assert rmsb(rows=-1) == INVALID
     assert rmsb(eps=-1.0) == INVALID
     assert rmsb(eps=float("nan")) == INVALID
-    assert rmsb(hidden=32776) == UNSUPPORTED
+    assert rmsb(hidden=32778) == UNSUPPORTED
     assert rmsb(hidden=8193) == UNSUPPORTED  # odd rows: 2-byte accesses, at most 8192
     assert rmsb(hidden=4095) == WORKSPACE
     assert rmsb(dw=0) == INVALID
@@ -466,7 +490,7 @@ def test_strided_validation():
     assert L.norm_rmsnorm_fwd_ex(A, 4096, A + GB, 1 << 40, A + 2 * GB, (1 << 31) - 1, 4096,
                                  1e-6, None, None) == INVALID  # x spans past 2^47 bytes
     assert L.norm_fused_add_rmsnorm_ex(A, 4096, A + GB, 4096, A + 2 * GB, 4096, A + 3 * GB, 4,
-                                       70000, 1e-6, None, None) == UNSUPPORTED
+                                       (1 << 20) + 8, 1e-6, None, None) == UNSUPPORTED
     assert L.norm_layernorm_fwd_ex(A, 4096, None, None, A + GB, 4095, A + 2 * GB, A + 3 * GB, 4,
                                    4096, 1e-5, None, None) == INVALID
     assert L.norm_layernorm_bwd_ex(A, 4096, A + GB, A + GB + 65536, A + 2 * GB, 4096,
@@ -548,7 +572,7 @@ def test_split_validation():
     assert fused_split(split=65) == INVALID
     assert fused_split(rows=-1) == INVALID
     assert fused_split(eps=float("nan")) == INVALID
-    assert fused_split(hidden=70000) == UNSUPPORTED
+    assert fused_split(hidden=(1 << 20) + 8) == UNSUPPORTED
     assert fused_split(x=0) == INVALID
     assert fused_split(res=A + 2 * MB) == INVALID              # residual aliases x
     assert fused_split(x=A + 2 * MB + 1) == MISALIGNED
@@ -556,7 +580,7 @@ def test_split_validation():
     assert fused_split(x=A + 2 * MB + 8) == MISALIGNED
     assert fused_split(hidden=16380) == INVALID
     assert fused_split(rows=513) == INVALID
-    assert fused_split(hidden=8192 * 8 + 8, split=2) == UNSUPPORTED
+    assert fused_split(hidden=8192 * 8 + 8, split=2) == INVALID  # 2 chunks of 17 accesses
     assert fused_split(hidden=65536, split=2) == INVALID        # 16 accesses a lane
     assert fused_split(ws=0) == WORKSPACE
     assert fused_split(ws_bytes=rn.split_workspace_bytes(4) - 1) == WORKSPACE
@@ -628,8 +652,9 @@ def test_noalloc_validation():
 
 def test_wide_backward_host_logic():
     """Backward rows above 16384 run on 512-lane workgroups with the row
-    staged in LDS (5 to 8 16-byte accesses a lane, up to 32768); narrower
-    accesses stop at the register-resident kernels' widest rows."""
+    staged in LDS (5 to 8 16-byte accesses a lane, up to 32768), then on the
+    streamed kernels; narrower accesses stop at the register-resident
+    kernels' widest rows."""
     for op in ("layernorm_bwd", "rmsnorm_bwd", "fused_add_rmsnorm_bwd"):
         for h in (16392, 20000, 24576, 32768):
             c = rn.select_config(op, 8192, h)
@@ -642,8 +667,10 @@ def test_wide_backward_host_logic():
             padded = -(-h // 64) * 64
             assert rn.workspace_bytes(8192, h, op=op) == 256 * outs * padded * 4
             assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4
-        with pytest.raises(rn.NormError):
-            rn.select_config(op, 8192, 32776)   # 9 accesses a lane
+        # 9 accesses a lane: past the LDS-staged kernel, the streamed kernels
+        c = rn.select_config(op, 8192, 32776)
+        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 85, 8)  # 255 // 3 tiles
+        assert "stream_bwd_tile_kernel" in rn.describe_config(op, 8192, 32776)
         with pytest.raises(rn.NormError):
             rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels
         assert rn.select_config(op, 8192, 16384 - 8).threads_per_row != 512 or \
