@@ -345,6 +345,8 @@ def main():
                                                 max(3, min(args.steps, 50) // 5))
             result["config_points"] = config_points(torch, rn, wl, dev, stream,
                                                     max(3, min(args.steps, 50) // 5))
+            result["fixed_cost"] = fixed_cost(torch, rn, dev, stream, sets[0], w, eps, offs,
+                                              max(3, min(args.steps, 50) // 5))
     if not args.no_hbm_ceilings:
         result["hbm_ceilings"] = hbm_ceilings(torch, dev, stream, 10)
     result["copy_ceiling"] = copy_ceiling(torch, dev, stream)
@@ -714,6 +716,78 @@ def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
     return out
 
 
+FIXED_COST_ROWS = (1024, 2048, 4096, 8192)
+
+
+def fixed_cost(torch, rn, dev, stream, s0, w, eps, offs, reps):
+    """Where a fused hidden-4096 launch's time goes at 1024 ... 8192 rows: the
+    library's launch beside the same launch shape (lanes per row, rows per
+    workgroup, grid) doing nothing, only its reads (x and residual), only its
+    writes (out and residual) and both as a plain copy (libnormceiling.so),
+    each graph-timed per launch over the same cold buffer sets as sweep_graph.
+    The empty grid's time is the launch's floor in a graph (dispatch and
+    completion); each other figure over it is the data movement's."""
+    import ctypes
+    L = _ceil_lib()
+    if L is None:
+        return None
+    L.normceil_fused_shape_part.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_void_p]
+    L.normceil_fused_shape_part.restype = ctypes.c_int
+    sid = stream.cuda_stream
+    out = []
+    for rows in FIXED_COST_ROWS:
+        i = SWEEP_ROWS.index(rows)
+        a, b = int(offs[i]), int(offs[i + 1])
+        n = min(512, _n_sets(8 * rows * HIDDEN))
+        xs = [s0["x"][a:b].clone() for _ in range(n)]
+        rs0 = [s0["r"][a:b].clone() for _ in range(n)]
+        os_ = [torch.empty_like(xs[0]) for _ in range(n)]
+        c = rn.select_config("fused_add_rmsnorm", rows, HIDDEN)
+        if c.vector_elems != 0:
+            continue
+        nrep = max(2, min(reps, 3000 // n))
+
+        def part(mode):
+            def one(j):
+                st = L.normceil_fused_shape_part(os_[j].data_ptr(), rs0[j].data_ptr(),
+                                                 xs[j].data_ptr(), rows, c.threads_per_row,
+                                                 c.rows_per_block, mode, sid)
+                if st != 0:
+                    raise RuntimeError(f"normceil_fused_shape_part failed ({st})")
+            return graph_time_per_launch(torch, stream, [(lambda j=j: one(j)) for j in range(n)],
+                                         nrep)
+
+        t_empty, t_read, t_write = part(3), part(1), part(2)
+        t_copy = graph_time_per_launch(torch, stream, [
+            (lambda j=j: L.normceil_same_traffic_h4096(os_[j].data_ptr(), rs0[j].data_ptr(),
+                                                       xs[j].data_ptr(), rows, c.threads_per_row,
+                                                       c.rows_per_block, sid))
+            for j in range(n)], nrep)
+        t_op = graph_time_per_launch(torch, stream, [
+            (lambda j=j: rn.fused_add_rmsnorm(xs[j], rs0[j], w, eps, out=os_[j], stream=stream))
+            for j in range(n)], nrep)
+        half = 4 * rows * HIDDEN
+        rec = {"rows": rows, "kernel": _fwd_kernel_name("fused_add_rmsnorm", rows, HIDDEN),
+               "lanes_per_row": c.threads_per_row, "rows_per_workgroup": c.rows_per_block,
+               "us_empty_grid": round(t_empty, 3), "us_reads_only": round(t_read, 3),
+               "us_writes_only": round(t_write, 3), "us_copy": round(t_copy, 3),
+               "us_fused": round(t_op, 3),
+               "GBps_reads_over_empty": round(half / ((t_read - t_empty) * 1e-6) / 1e9, 1)
+               if t_read > t_empty else None,
+               "GBps_writes_over_empty": round(half / ((t_write - t_empty) * 1e-6) / 1e9, 1)
+               if t_write > t_empty else None,
+               "pct_peak_fused": round(100 * fused_bytes(rows) / (t_op * 1e-6) / 1e9
+                                       / HBM_PEAK_GBPS, 1)}
+        log(f"  fixed cost {rows} rows: empty {t_empty:.2f}, reads {t_read:.2f}, writes "
+            f"{t_write:.2f}, copy {t_copy:.2f}, fused {t_op:.2f} us")
+        out.append(rec)
+        del xs, rs0, os_
+    torch.cuda.synchronize()
+    return out
+
+
 def config_points(torch, rn, wl, dev, stream, reps):
     """Every point of the RMSNorm-forward (hidden 2048 / 8192 / 16384 x rows
     1 / 64 / 1024 / 4096, 1 % outlier channels) and LayerNorm-forward (2048 rows
@@ -889,6 +963,74 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
                                              nb, cpu_seconds)))
         del xs, dys, dxs, x0, dy0, ws
         torch.cuda.synchronize()
+    out += streamed_ops(torch, rn, wl, dev, stream, reps)
+    return out
+
+
+def streamed_ops(torch, rn, wl, dev, stream, reps):
+    """Rows no workgroup holds on chip (the streamed kernels, each row read
+    twice): fused add + RMSNorm 2048 x 131072, LayerNorm forward 2048 x 65536,
+    LayerNorm and RMSNorm backward 4096 x 65536; time per launch over cold
+    buffer sets, algorithmic bytes as for the on-chip kernels (one read and
+    one write of each matrix)."""
+    out = []
+    h, rows = 131072, 2048
+    i = wl.fused_inputs(rows, h, seed=0)
+    n = _n_sets(4 * rows * h * 2)
+    x0, r0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["r"], dev)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    rs = [r0] + [r0.clone() for _ in range(n - 1)]
+    ys = [torch.empty_like(x0) for _ in range(n)]
+    w = wl.to_device_bf16(i["w"], dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.fused_add_rmsnorm(xs[j], rs[j], w, i["eps"], out=ys[j], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("fused_add_rmsnorm", rows, h, 8 * h * rows + 2 * h, t,
+                       note="streamed kernel: the row is read twice"))
+    del xs, rs, ys, x0, r0
+    h, rows = 65536, 2048
+    i = wl.layernorm_fwd_inputs(rows, h, seed=0)
+    n = _n_sets(2 * rows * h * 2)
+    x0 = wl.to_device_bf16(i["x"], dev)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    ys = [torch.empty_like(x0) for _ in range(n)]
+    st = torch.empty(n, 2, rows, device=dev)
+    w, bb = wl.to_device_bf16(i["w"], dev), wl.to_device_bf16(i["b"], dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_fwd(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
+                                      rstd=st[j, 1], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_fwd", rows, h, (4 * h + 8) * rows + 4 * h, t,
+                       note="streamed kernel: the row is read twice"))
+    del xs, ys, x0
+    h, rows = 65536, 4096
+    i = wl.layernorm_bwd_inputs(rows, h, seed=0)
+    n = _n_sets(3 * rows * h * 2)
+    x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
+    w = wl.to_device_bf16(i["w"], dev)
+    zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+    _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
+    dxs = [torch.empty_like(x0) for _ in range(n)]
+    dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    ws = torch.empty(rn.workspace_bytes(rows, h), dtype=torch.uint8, device=dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_bwd(dys[j], xs[j], mean, rstd, w, i["eps"], dx=dxs[j],
+                                      dweight=dw, dbias=db, workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
+                       note="streamed kernels: row reductions, then column tiles (x and dy "
+                            "read twice) + column reduce"))
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
+                                    workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
+                       note="streamed kernels: row reductions, then column tiles (x and dy "
+                            "read twice) + column reduce"))
+    del xs, dys, dxs, x0, dy0, ws
+    torch.cuda.synchronize()
     return out
 
 

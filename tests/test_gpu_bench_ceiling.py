@@ -138,3 +138,37 @@ def test_row_traffic_kernel_moves_exactly_its_rows(nr, lanes, vecs, grid, depth)
                            stream) == 1
     assert L.normceil_rows(_ptrs(ins, 3), 3, out.data_ptr(), rows, 4 * 8 * 512, 512, 4, 256, 8,
                            stream) == 1  # a ring that would not fit the registers
+
+
+@pytest.mark.parametrize("lanes,rpb", [(64, 4), (128, 2), (256, 1), (512, 1)])
+def test_fused_shape_parts(lanes, rpb):
+    """Reads-only launches write nothing, writes-only launches write exactly
+    out and the residual (the vector index) for the rows given, and the empty
+    grid touches nothing."""
+    L = ctypes.CDLL(PATH)
+    f = L.normceil_fused_shape_part
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    h = 4096
+    stream = torch.cuda.current_stream().cuda_stream
+    for rows in (1, 37, 1001):
+        x = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows + 1, h // 2), dtype=torch.int32,
+                          device="cuda")
+        r0 = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows + 1, h // 2), dtype=torch.int32,
+                           device="cuda")
+        for mode in (1, 3):
+            r, out = r0.clone(), torch.full_like(x, 7)
+            assert f(out.data_ptr(), r.data_ptr(), x.data_ptr(), rows, lanes, rpb, mode,
+                     stream) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(r, r0) and bool((out == 7).all()), mode
+        r, out = r0.clone(), torch.full_like(x, 7)
+        assert f(out.data_ptr(), r.data_ptr(), x.data_ptr(), rows, lanes, rpb, 2, stream) == 0
+        torch.cuda.synchronize()
+        idx = torch.arange(rows * h // 8, dtype=torch.int32, device="cuda")
+        exp = idx.repeat_interleave(4).view(rows, h // 2)
+        assert torch.equal(out[:rows], exp) and torch.equal(r[:rows], exp)
+        assert torch.equal(r[rows], r0[rows]) and bool((out[rows] == 7).all())
+    assert f(out.data_ptr(), r.data_ptr(), x.data_ptr(), 4, lanes, rpb, 0, stream) == 1
+    assert f(out.data_ptr(), r.data_ptr(), x.data_ptr(), 4, 96, 1, 1, stream) == 1
