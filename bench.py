@@ -1176,7 +1176,8 @@ CALIBRATION_BYTES = 1 << 30  # the 1 GiB device copy of the copy_ceiling pass
 
 
 def _short(name: str) -> str:
-    return name.split("(")[0].replace("void ", "").replace("rownorm::", "")
+    return (name.replace("void ", "").replace("(anonymous namespace)::", "")
+            .replace("rownorm::", "").split("(")[0])
 
 
 def _tpl(name: str):
@@ -1354,6 +1355,27 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
         alg = alg_fn(rows, h)
         lines.append(f"| {op} | {rows} x {h} | `{kname}` | {len(f_v)} | {rd / 2**20:.2f} | "
                      f"{wr / 2**20:.2f} | {alg / 2**20:.2f} | {(rd + wr) / alg:.4f} |")
+    # the streaming ceilings move known bytes (1 GiB per buffer): their scaled
+    # counters check the calibration and the kernels' own traffic
+    import re as _re
+    stream_rows = []
+    for (k, _rows), v in sorted(fetch.items()):
+        m = _re.search(r"stream_kernel<(\d+), (\d+), (\d+)>", k)
+        if not m or (k, _rows) not in write:
+            continue
+        nr, nw, u = (int(g) for g in m.groups())
+        rd = float(np.mean(v)) * f_scale
+        wr = float(np.mean(write[(k, _rows)])) * w_scale
+        exp_r, exp_w = nr * CALIBRATION_BYTES, nw * CALIBRATION_BYTES
+        stream_rows.append(f"| {nr} : {nw} | {u} | {len(v)} | {rd / 2**20:.1f} | "
+                           f"{exp_r / 2**20:.0f} | {wr / 2**20:.1f} | {exp_w / 2**20:.0f} |")
+    if stream_rows:
+        lines += ["", "The streaming ceilings (`hbm_ceilings`, `normceil_stream` over 1 GiB "
+                  "buffers: reads : writes, accesses in flight a lane) against the bytes they "
+                  "touch, averaged over their dispatches (every grid size of the sweep):", "",
+                  "| reads : writes | in flight | dispatches | read MiB (scaled) | buffers read "
+                  "MiB | written MiB (scaled) | buffers written MiB |",
+                  "|---|---:|---:|---:|---:|---:|---:|"] + stream_rows
     lines += ["", "Per-launch averages over each kernel's dispatches (the mix of row counts "
               "the sweep gives it) are in `profiles/traffic.json`, which `bench.py` reports as "
               "`roofline.traffic` while the kernel sources and the kernel's mix of row counts are "
