@@ -299,3 +299,70 @@ def test_fused_add_rmsnorm_bwd_past_4gib():
     P.assert_colsum_close(dw.cpu().numpy(), dw_ref, dw_q, "fused bwd past 4 GiB: dweight")
     del s, dout, dres, ds
     free()
+
+
+def test_streamed_fused_add_rmsnorm_past_4gib():
+    """hidden 131072 (the streamed two-pass kernel): x, residual, out of 4 GiB
+    + 3 rows each."""
+    h = 131072
+    rows = rows_past_4gib(h, 3)
+    idx = sample_rows(rows, 2 * h, seed=9)
+    assert "stream_fwd_kernel" in rn.describe_config("fused_add_rmsnorm", rows, h)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=901)
+    r = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=902)
+    w_bits, w = weight(h, 903)
+    xs, rs = take(x, idx), take(r, idx)
+    out = nan_like(x)
+    rn.fused_add_rmsnorm(x, r, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, res_ref, _ = oracle.fused_add_rmsnorm(xs, rs, w_bits, wl.EPS_RMS, NT)
+    P.assert_bits_equal(take(r, idx), res_ref, "streamed fused past 4 GiB: residual")
+    P.assert_bf16_close(take(out, idx), ref, "streamed fused past 4 GiB: out")
+    assert_all_finite(out, "streamed fused past 4 GiB: out")
+    del x, r, out
+    free()
+
+
+def test_streamed_layernorm_bwd_past_4gib():
+    """hidden 65536 (row reductions, then column tiles): x, dy, dx of 4 GiB + 5
+    rows; column sums over every row against chunked oracle calls."""
+    h = 65536
+    rows = rows_past_4gib(h, 5)
+    idx = sample_rows(rows, 2 * h, seed=10)
+    assert "stream_bwd_tile_kernel" in rn.describe_config("layernorm_bwd", rows, h)
+    x = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=1001)
+    dy = wl.device_normal_bf16(rows, h, 0.0, 1.0, seed=1002)
+    mean = wl.device_normal_f32(rows, 0.0, 0.02, seed=1003)
+    rstd = wl.device_normal_f32(rows, 1.0, 0.05, seed=1004)
+    w_bits, w = weight(h, 1005)
+    dx = nan_like(x)
+    dw = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    db = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    rn.layernorm_bwd(dy, x, mean, rstd, w, dx=dx, dweight=dw, dbias=db)
+    torch.cuda.synchronize()
+    ti = torch.from_numpy(idx).to(DEV)
+    xs, dys = take(x, idx), take(dy, idx)
+    ms, rs = mean[ti].cpu().numpy(), rstd[ti].cpu().numpy()
+    dx_ref, _, _ = oracle.layernorm_bwd(dys, xs, ms, rs, w_bits, NT)
+    xd, dyd, wd = P.bits_to_f64(xs), P.bits_to_f64(dys), P.bits_to_f64(w_bits)
+    scale = P.layernorm_dx_scale(xd, dyd, wd, ms.astype(np.float64), rs.astype(np.float64))
+    P.assert_bf16_close(take(dx, idx), dx_ref, "streamed layernorm bwd past 4 GiB: dx",
+                        floor_scale=scale)
+    assert_all_finite(dx, "streamed layernorm bwd past 4 GiB: dx")
+
+    def chunk(a, b):
+        xc, dc = wl.from_device_bf16(x[a:b]), wl.from_device_bf16(dy[a:b])
+        mc, rc = mean[a:b].cpu().numpy(), rstd[a:b].cpu().numpy()
+        _, cdw, cdb = oracle.layernorm_bwd(dc, xc, mc, rc, w_bits, NT)
+        dyt = f64_rows(dc)
+        xhat = (f64_rows(xc) - torch.from_numpy(mc).double()[:, None]) * \
+            torch.from_numpy(rc).double()[:, None]
+        return [(cdw, ((dyt * xhat) ** 2).sum(0).numpy()), (cdb, (dyt * dyt).sum(0).numpy())]
+
+    (dw_ref, dw_q), (db_ref, db_q) = oracle_colsums(rows, chunk, chunk=1 << 12)
+    P.assert_colsum_close(dw.cpu().numpy(), dw_ref, dw_q,
+                          "streamed layernorm bwd past 4 GiB: dweight")
+    P.assert_colsum_close(db.cpu().numpy(), db_ref, db_q,
+                          "streamed layernorm bwd past 4 GiB: dbias")
+    del x, dy, dx, mean, rstd
+    free()
