@@ -4,8 +4,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The HIP library never imports it and
 shares no code with it.
 
-The arithmetic lives in ``oracle.c`` (plain fp64 loops, built with gcc -O2 and
-no fast-math); this module only marshals numpy arrays into it.  Definitions:
+The arithmetic lives in ``oracle.c`` (plain fp64 loops over bf16 operands, built
+with gcc -O2 and no fast-math) and ``oracle_f32.c`` (the same definitions over
+binary32 operands, for the fp32-activation entry points); this module only
+marshals numpy arrays into them.  Definitions:
 
 * fused residual-add + RMSNorm forward -- "optimize inner persistent scheduler
   for static fusion" (nvFuser PR 5281), author description and changes
@@ -30,7 +32,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_SOURCES = [os.path.join(_HERE, "oracle.c")]
+_SOURCES = [os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "oracle_f32.c")]
+F32_SOURCE = _SOURCES[1]
 
 def build(force: bool = True, sources=None, out_path: str | None = None,
           defines=()) -> str:
@@ -49,6 +52,7 @@ def build(force: bool = True, sources=None, out_path: str | None = None,
 
 
 _u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64
 
@@ -75,6 +79,21 @@ def _bind(lib):
     for name in ("orc_fused_add_rmsnorm", "orc_rmsnorm_fwd", "orc_layernorm_fwd",
                  "orc_layernorm_bwd", "orc_rmsnorm_bwd"):
         getattr(lib, name).restype = ctypes.c_int
+    if hasattr(lib, "orc_fused_add_rmsnorm_f32"):  # builds without oracle_f32.c lack them
+        lib.orc_fused_add_rmsnorm_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64,
+                                                  ctypes.c_double, _f64p, _f32p, _f64p,
+                                                  ctypes.c_int]
+        lib.orc_rmsnorm_fwd_f32.argtypes = [_f32p, _f32p, _i64, _i64, ctypes.c_double, _f64p,
+                                            _f64p, ctypes.c_int]
+        lib.orc_layernorm_fwd_f32.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, ctypes.c_double,
+                                              _f64p, _f64p, _f64p, ctypes.c_int]
+        lib.orc_layernorm_bwd_f32.argtypes = [_f32p, _f32p, _f64p, _f64p, _f32p, _i64, _i64,
+                                              _f64p, _f64p, _f64p, ctypes.c_int]
+        lib.orc_rmsnorm_bwd_f32.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64,
+                                            ctypes.c_double, _f64p, _f64p, _f64p, ctypes.c_int]
+        for name in ("orc_fused_add_rmsnorm_f32", "orc_rmsnorm_fwd_f32",
+                     "orc_layernorm_fwd_f32", "orc_layernorm_bwd_f32", "orc_rmsnorm_bwd_f32"):
+            getattr(lib, name).restype = ctypes.c_int
     return lib
 
 
@@ -95,6 +114,17 @@ def _p16(a):
 
 def _p64(a):
     return a.ctypes.data_as(_f64p)
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"expected float32 values, got {a.dtype}")
+    return a
+
+
+def _p32(a):
+    return a.ctypes.data_as(_f32p)
 
 
 def _check(rc: int, name: str) -> None:
@@ -206,6 +236,79 @@ class Oracle:
         return dx, dw, rstd
 
 
+    # ---- fp32 activations (oracle_f32.c) ------------------------------------
+    def fused_add_rmsnorm_f32(self, x, r, w, eps: float, nthreads: int = 1):
+        """float32 x, r, w.  Returns (out_f64, residual_f32, rstd_f64)."""
+        x, r, w = _f32(x), _f32(r), _f32(w)
+        rows, hidden = _shape(x)
+        assert r.shape == x.shape and w.shape == (hidden,)
+        out = np.empty((rows, hidden), np.float64)
+        res = np.empty((rows, hidden), np.float32)
+        rstd = np.empty((rows,), np.float64)
+        _check(self.lib.orc_fused_add_rmsnorm_f32(_p32(x), _p32(r), _p32(w), rows, hidden,
+                                                  float(eps), _p64(out), _p32(res), _p64(rstd),
+                                                  nthreads), "fused_add_rmsnorm_f32")
+        return out, res, rstd
+
+    def rmsnorm_fwd_f32(self, x, w, eps: float, nthreads: int = 1):
+        """Returns (out_f64, rstd_f64)."""
+        x, w = _f32(x), _f32(w)
+        rows, hidden = _shape(x)
+        assert w.shape == (hidden,)
+        out = np.empty((rows, hidden), np.float64)
+        rstd = np.empty((rows,), np.float64)
+        _check(self.lib.orc_rmsnorm_fwd_f32(_p32(x), _p32(w), rows, hidden, float(eps),
+                                            _p64(out), _p64(rstd), nthreads), "rmsnorm_fwd_f32")
+        return out, rstd
+
+    def layernorm_fwd_f32(self, x, w, b, eps: float, nthreads: int = 1):
+        """Returns (y_f64, mean_f64, rstd_f64)."""
+        x, w, b = _f32(x), _f32(w), _f32(b)
+        rows, hidden = _shape(x)
+        assert w.shape == (hidden,) and b.shape == (hidden,)
+        y = np.empty((rows, hidden), np.float64)
+        mean = np.empty((rows,), np.float64)
+        rstd = np.empty((rows,), np.float64)
+        _check(self.lib.orc_layernorm_fwd_f32(_p32(x), _p32(w), _p32(b), rows, hidden,
+                                              float(eps), _p64(y), _p64(mean), _p64(rstd),
+                                              nthreads), "layernorm_fwd_f32")
+        return y, mean, rstd
+
+    def layernorm_bwd_f32(self, dy, x, mean, rstd, w, nthreads: int = 1):
+        """mean/rstd: the given statistics, widened exactly to float64.
+        Returns (dx_f64, dweight_f64, dbias_f64)."""
+        dy, x, w = _f32(dy), _f32(x), _f32(w)
+        rows, hidden = _shape(x)
+        assert dy.shape == x.shape and w.shape == (hidden,)
+        mean, rstd = _f64(mean), _f64(rstd)
+        assert mean.shape == (rows,) and rstd.shape == (rows,)
+        dx = np.empty((rows, hidden), np.float64)
+        dw = np.empty((hidden,), np.float64)
+        db = np.empty((hidden,), np.float64)
+        _check(self.lib.orc_layernorm_bwd_f32(_p32(dy), _p32(x), _p64(mean), _p64(rstd), _p32(w),
+                                              rows, hidden, _p64(dx), _p64(dw), _p64(db),
+                                              nthreads), "layernorm_bwd_f32")
+        return dx, dw, db
+
+    def rmsnorm_bwd_f32(self, dy, x, w, eps: float, dres=None, nthreads: int = 1):
+        """Returns (dx_f64, dweight_f64, rstd_f64); dres (float32) is added to dx."""
+        dy, x, w = _f32(dy), _f32(x), _f32(w)
+        rows, hidden = _shape(x)
+        assert dy.shape == x.shape and w.shape == (hidden,)
+        dres_p = None
+        if dres is not None:
+            dres = _f32(dres)
+            assert dres.shape == x.shape
+            dres_p = _p32(dres)
+        dx = np.empty((rows, hidden), np.float64)
+        dw = np.empty((hidden,), np.float64)
+        rstd = np.empty((rows,), np.float64)
+        _check(self.lib.orc_rmsnorm_bwd_f32(_p32(dy), _p32(x), _p32(w), dres_p, rows, hidden,
+                                            float(eps), _p64(dx), _p64(dw), _p64(rstd), nthreads),
+               "rmsnorm_bwd_f32")
+        return dx, dw, rstd
+
+
 _default: Oracle | None = None
 
 
@@ -242,3 +345,23 @@ def layernorm_bwd(dy, x, mean, rstd, w, nthreads=1):
 
 def rmsnorm_bwd(dy, x, w, eps, dres=None, nthreads=1):
     return default().rmsnorm_bwd(dy, x, w, eps, dres, nthreads)
+
+
+def fused_add_rmsnorm_f32(x, r, w, eps, nthreads=1):
+    return default().fused_add_rmsnorm_f32(x, r, w, eps, nthreads)
+
+
+def rmsnorm_fwd_f32(x, w, eps, nthreads=1):
+    return default().rmsnorm_fwd_f32(x, w, eps, nthreads)
+
+
+def layernorm_fwd_f32(x, w, b, eps, nthreads=1):
+    return default().layernorm_fwd_f32(x, w, b, eps, nthreads)
+
+
+def layernorm_bwd_f32(dy, x, mean, rstd, w, nthreads=1):
+    return default().layernorm_bwd_f32(dy, x, mean, rstd, w, nthreads)
+
+
+def rmsnorm_bwd_f32(dy, x, w, eps, dres=None, nthreads=1):
+    return default().rmsnorm_bwd_f32(dy, x, w, eps, dres, nthreads)

@@ -88,6 +88,24 @@ int orc_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w,
                     const uint16_t* dres, int64_t rows, int64_t hidden, double eps,
                     double* dx, double* dweight, double* rstd_out, int nthreads);
 
+/* fp32 activations (oracle_f32.c): the same five definitions with every
+ * operand an IEEE-754 binary32 value, widened to double exactly.  The fused
+ * op's res_out is the exact sum x + r rounded once to binary32. */
+int orc_fused_add_rmsnorm_f32(const float* x, const float* r, const float* w, int64_t rows,
+                              int64_t hidden, double eps, double* out, float* res_out,
+                              double* rstd_out, int nthreads);
+int orc_rmsnorm_fwd_f32(const float* x, const float* w, int64_t rows, int64_t hidden,
+                        double eps, double* out, double* rstd_out, int nthreads);
+int orc_layernorm_fwd_f32(const float* x, const float* w, const float* b, int64_t rows,
+                          int64_t hidden, double eps, double* y, double* mean, double* rstd,
+                          int nthreads);
+int orc_layernorm_bwd_f32(const float* dy, const float* x, const double* mean,
+                          const double* rstd, const float* w, int64_t rows, int64_t hidden,
+                          double* dx, double* dweight, double* dbias, int nthreads);
+int orc_rmsnorm_bwd_f32(const float* dy, const float* x, const float* w, const float* dres,
+                        int64_t rows, int64_t hidden, double eps, double* dx, double* dweight,
+                        double* rstd_out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

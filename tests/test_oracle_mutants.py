@@ -99,3 +99,59 @@ def test_pins_catch_mutant(workdir, name, old, new):
         except AssertionError:
             caught.append(check.__name__)
     assert caught, f"no pin catches the planted mistake '{name}'"
+
+
+# ---- the fp32-activation functions (oracle_f32.c) against oracle_checks_f32
+import oracle_checks_f32  # noqa: E402
+
+SRC_F32 = oracle.F32_SOURCE
+
+MUTANTS_F32 = [
+    ("f32_residual_subtract", "if (c->r) v += (double)c->r[base + j];",
+     "if (c->r) v -= (double)c->r[base + j];"),
+    ("f32_residual_biased_rounding", "c->res_out[base + j] = (float)s[j];",
+     "c->res_out[base + j] = (float)(s[j] * (1.0 + 0x1p-30));"),
+    ("f32_rms_eps_outside", "const double rstd = 1.0 / sqrt(ss / (double)H + c->eps);\n        if",
+     "const double rstd = 1.0 / (sqrt(ss / (double)H) + c->eps);\n        if"),
+    ("f32_rms_no_weight", "c->out[base + j] = s[j] * rstd * (double)c->w[j];",
+     "c->out[base + j] = s[j] * rstd;"),
+    ("f32_ln_unbiased", "sqrt(sq / (double)H + c->eps)", "sqrt(sq / (double)(H - 1) + c->eps)"),
+    ("f32_ln_no_bias", "* (double)c->w[j] + (double)c->b[j];", "* (double)c->w[j];"),
+    ("f32_ln_mean_sign", "c->y[i * H + j] = ((double)xr[j] - mu)",
+     "c->y[i * H + j] = ((double)xr[j] + mu)"),
+    ("f32_lnb_drop_c1", "(g - c1 - lnb32_xhat(c, i, j) * c2)", "(g - lnb32_xhat(c, i, j) * c2)"),
+    ("f32_lnb_xhat_sign", "((double)c->x[i * c->hidden + j] - c->mean[i]) * c->rstd[i];",
+     "((double)c->x[i * c->hidden + j] + c->mean[i]) * c->rstd[i];"),
+    ("f32_lnb_dbias_scaled", "db += d;", "db += d * lnb32_xhat(c, i, j);"),
+    ("f32_rmsb_drop_c", "double v = rstd * (g - xhat * cc);", "double v = rstd * g;"),
+    ("f32_rmsb_dres_subtracted", "if (c->dres) v += (double)c->dres[i * H + j];",
+     "if (c->dres) v -= (double)c->dres[i * H + j];"),
+    ("f32_rmsb_dw_no_rstd", "((double)c->x[i * c->hidden + j] * c->rstd[i]);",
+     "(double)c->x[i * c->hidden + j];"),
+]
+
+
+def test_f32_mutant_list_applies_cleanly():
+    src = open(SRC_F32).read()
+    for name, old, _ in MUTANTS_F32:
+        assert src.count(old) >= 1, f"mutant {name}: text not found in oracle_f32.c"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_F32, ids=[m[0] for m in MUTANTS_F32])
+def test_f32_pins_catch_mutant(workdir, name, old, new):
+    src = open(SRC_F32).read()
+    d = workdir / name
+    d.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(SRC), "oracle.h"), d / "oracle.h")
+    shutil.copy(SRC, d / "oracle.c")
+    (d / "oracle_f32.c").write_text(src.replace(old, new))
+    lib = oracle.build(sources=[str(d / "oracle.c"), str(d / "oracle_f32.c")],
+                       out_path=str(d / "liboracle.so"))
+    o = oracle.Oracle(lib)
+    caught = []
+    for check in oracle_checks_f32.F32_CHECKS:
+        try:
+            check(o)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no fp32 pin catches the planted mistake '{name}'"
