@@ -529,6 +529,7 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
     torch.cuda.synchronize()
     out += runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds)
     out += split_ops(torch, rn, wl, dev, stream, reps)
+    out += f32_ops(torch, rn, wl, dev, stream, reps)
     return out
 
 
@@ -1030,6 +1031,87 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
                        note="streamed kernels: row reductions, then column tiles (x and dy "
                             "read twice) + column reduce"))
     del xs, dys, dxs, x0, dy0, ws
+    torch.cuda.synchronize()
+    return out
+
+
+def f32_ops(torch, rn, wl, dev, stream, reps):
+    """fp32 activations (the `_f32` entry points, the streamed kernels at
+    every width) at the bf16 operations' configured shapes: fused add +
+    RMSNorm 8192 x 4096, RMSNorm 4096 x 16384, LayerNorm forward 2048 x
+    16384, the three backward operations 8192 x 4096; time per launch over
+    cold buffer sets, algorithmic bytes at 4 bytes an element."""
+    out = []
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    def sets(a, n):
+        return [a] + [a.clone() for _ in range(n - 1)]
+
+    rows, h = 8192, 4096
+    i = wl.fused_inputs(rows, h, seed=0, f32=True)
+    n = _n_sets(4 * rows * h * 4)
+    xs, rs = sets(f(i["x"]), n), sets(f(i["r"]), n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
+    w = f(i["w"])
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.fused_add_rmsnorm_f32(xs[j], rs[j], w, i["eps"], out=ys[j],
+                                              stream=stream)) for j in range(n)], reps)
+    out.append(_op_rec("fused_add_rmsnorm_f32", rows, h, 16 * h * rows + 4 * h, t,
+                       note="fp32 activations: streamed kernel, row read once"))
+    del xs, rs, ys
+    rows, h = 4096, 16384
+    i = wl.rmsnorm_inputs(rows, h, seed=0, f32=True)
+    n = _n_sets(2 * rows * h * 4)
+    xs = sets(f(i["x"]), n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
+    w = f(i["w"])
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_fwd_f32(xs[j], w, i["eps"], out=ys[j], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_fwd_f32", rows, h, 8 * h * rows + 4 * h, t,
+                       note="fp32 activations: streamed kernel, row read once"))
+    del xs, ys
+    rows, h = 2048, 16384
+    i = wl.layernorm_fwd_inputs(rows, h, seed=0, f32=True)
+    n = _n_sets(2 * rows * h * 4)
+    xs = sets(f(i["x"]), n)
+    ys = [torch.empty_like(xs[0]) for _ in range(n)]
+    st = torch.empty(n, 2, rows, device=dev)
+    w, bb = f(i["w"]), f(i["b"])
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_fwd_f32(xs[j], w, bb, i["eps"], y=ys[j], mean=st[j, 0],
+                                          rstd=st[j, 1], stream=stream)) for j in range(n)],
+        reps)
+    out.append(_op_rec("layernorm_fwd_f32", rows, h, (8 * h + 8) * rows + 8 * h, t,
+                       note="fp32 activations: streamed kernel, row read once"))
+    del xs, ys
+    rows, h = 8192, 4096
+    i = wl.rmsnorm_bwd_inputs(rows, h, seed=0, f32=True)
+    n = _n_sets(4 * rows * h * 4)
+    xs, dys, drs = sets(f(i["x"]), n), sets(f(i["dy"]), n), sets(f(i["dres"]), n)
+    dxs = [torch.empty_like(xs[0]) for _ in range(n)]
+    w = f(i["w"])
+    _, mean, rstd = rn.layernorm_fwd_f32(xs[0], w, torch.zeros_like(w), wl.EPS_LN, stream=stream)
+    dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    ws = torch.empty(rn.workspace_bytes_f32("layernorm_bwd", rows, h), dtype=torch.uint8,
+                     device=dev)
+    note = "fp32 activations: streamed kernels (row reductions, column tiles) + column reduce"
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_bwd_f32(dys[j], xs[j], mean, rstd, w, dx=dxs[j], dweight=dw,
+                                          dbias=db, workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_bwd_f32", rows, h, (12 * h + 8) * rows + 12 * h, t, note=note))
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_bwd_f32(dys[j], xs[j], w, i["eps"], dx=dxs[j], dweight=dw,
+                                        workspace=ws, stream=stream)) for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_bwd_f32", rows, h, 12 * h * rows + 8 * h, t, note=note))
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.fused_add_rmsnorm_bwd_f32(dys[j], xs[j], w, i["eps"], dres=drs[j],
+                                                  ds=dxs[j], dweight=dw, workspace=ws,
+                                                  stream=stream)) for j in range(n)], reps)
+    out.append(_op_rec("fused_add_rmsnorm_bwd_f32", rows, h, 16 * h * rows + 8 * h, t,
+                       note=note))
+    del xs, dys, drs, dxs, ws
     torch.cuda.synchronize()
     return out
 

@@ -29,7 +29,9 @@
  *     narrower accesses are unsupported.  The row-split forward entry
  *     points below spread few wide rows over several workgroups instead.
  * The library picks the family; the arithmetic and results (within rounding)
- * are the same.
+ * are the same.  The `_f32` entry points take fp32 activations, weights and
+ * gradients instead (contiguous rows, hidden a multiple of 4 up to 2^20) and
+ * run the streamed kernels at every width.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -470,6 +472,60 @@ NORM_API int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden,
  * 0 for an unsupported hidden. */
 NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* out,
                           int32_t capacity);
+
+/* ---- fp32 activations ----------------------------------------------------
+ * The six operations above on fp32 matrices and fp32 weight / bias vectors:
+ * the same formulas, arguments and errors, with every bf16 store replaced by
+ * an fp32 store of the fp32 result (norm_fused_add_rmsnorm_f32's residual is
+ * the fp32 sum x + residual, rounded once).  The pages fix no activation
+ * precision ("TMA inner persistent scheduler" and "optimize inner persistent
+ * scheduler for static fusion" benchmark bf16); fp32 is the other activation
+ * type their schedulers take.  Restrictions: contiguous rows (ld = hidden),
+ * hidden a multiple of 4 from 4 up to 2^20 (else UNSUPPORTED_HIDDEN), the
+ * matrices and the weight / bias vectors 16-byte aligned, mean / rstd /
+ * dweight / dbias 4-byte aligned, the workspace 16-byte aligned (else
+ * MISALIGNED).  Aliasing as for the bf16 entry points: out (y) may equal x,
+ * dx (ds) may equal dy (dout) or dres, nothing else overlaps.
+ * Every row is handled by the streamed kernels: forward, a 1024-lane
+ * workgroup per row that keeps the first 16384 values of the row in
+ * registers between its two passes and reads the rest again; backward, the
+ * per-row reduction kernel, then 512-lane workgroups over 8192-column tiles
+ * and the fixed-order column reduce (column sums bitwise reproducible run to
+ * run).  workspace: at least norm_bwd_workspace_bytes_f32(op, rows, hidden)
+ * bytes, contents ignored on entry. */
+NORM_API norm_status norm_fused_add_rmsnorm_f32(float* out, float* residual, const float* x,
+                                                const float* weight, int64_t rows,
+                                                int64_t hidden, float eps, hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_fwd_f32(float* out, const float* x, const float* weight,
+                                          int64_t rows, int64_t hidden, float eps,
+                                          hipStream_t stream);
+NORM_API norm_status norm_layernorm_fwd_f32(float* y, float* mean, float* rstd, const float* x,
+                                            const float* weight, const float* bias,
+                                            int64_t rows, int64_t hidden, float eps,
+                                            hipStream_t stream);
+NORM_API norm_status norm_layernorm_bwd_f32(float* dx, float* dweight, float* dbias,
+                                            const float* dy, const float* x, const float* mean,
+                                            const float* rstd, const float* weight,
+                                            void* workspace, size_t workspace_bytes,
+                                            int64_t rows, int64_t hidden, float eps,
+                                            hipStream_t stream);
+NORM_API norm_status norm_rmsnorm_bwd_f32(float* dx, float* dweight, const float* dy,
+                                          const float* x, const float* weight, void* workspace,
+                                          size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                          float eps, hipStream_t stream);
+NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, const float* dout,
+                                                    const float* dres, const float* s,
+                                                    const float* weight, void* workspace,
+                                                    size_t workspace_bytes, int64_t rows,
+                                                    int64_t hidden, float eps,
+                                                    hipStream_t stream);
+/* Workspace bytes of an fp32 backward op (NORM_OP_LAYERNORM_BWD,
+ * NORM_OP_RMSNORM_BWD or NORM_OP_FUSED_ADD_RMSNORM_BWD): 4 * padded hidden
+ * (hidden rounded up to 64) per partial-sum slab and output column sum, for
+ * each of its max(1, min(rows, 255 / ceil(hidden / 8192))) row walkers, plus
+ * 8 bytes a row.  Pure host arithmetic; 0 for another op, an unsupported
+ * hidden or rows <= 0. */
+NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,9 @@ Operations (names as in the C ABI):
   * ``fused_add_rmsnorm_bwd`` -- ds = RMSNorm backward of dout at s, plus dres;
                               the gradient of both the x and residual inputs
 
+Each op has an fp32 twin with the suffix ``_f32`` (fp32 activations, weights
+and gradients; contiguous rows, hidden a multiple of 4 up to 2^20).
+
 The three forward ops also take ``workspace=`` (a zero-filled uint8 device
 tensor of ``split_workspace_bytes(rows)``) and ``split=``: the row-split entry
 points, which may spread each of few wide rows over several workgroups.
@@ -150,6 +153,15 @@ def lib() -> ctypes.CDLL:
         # LayerNorm backward with the library's per-device scratch (no workspace)
         "norm_layernorm_bwd_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32,
                                        _vp],
+        # fp32 activations (contiguous rows)
+        "norm_fused_add_rmsnorm_f32": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_rmsnorm_fwd_f32": [_vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_layernorm_fwd_f32": [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+        "norm_layernorm_bwd_f32": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64,
+                                   _f32, _vp],
+        "norm_rmsnorm_bwd_f32": [_vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _f32, _vp],
+        "norm_fused_add_rmsnorm_bwd_f32": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64,
+                                           _f32, _vp],
     }
     for n, args in sigs.items():
         fn = getattr(L, n)
@@ -163,6 +175,8 @@ def lib() -> ctypes.CDLL:
     L.norm_layernorm_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.norm_layernorm_bwd_workspace_bytes_cfg.argtypes = [_i64, _i64, _cfgp]
     L.norm_layernorm_bwd_workspace_bytes_cfg.restype = ctypes.c_size_t
+    L.norm_bwd_workspace_bytes_f32.argtypes = [ctypes.c_int, _i64, _i64]
+    L.norm_bwd_workspace_bytes_f32.restype = ctypes.c_size_t
     L.norm_split_workspace_bytes.argtypes = [_i64]
     L.norm_split_workspace_bytes.restype = ctypes.c_size_t
     L.norm_select_split.argtypes = [ctypes.c_int, _i64, _i64, _i32, ctypes.POINTER(_i32),
@@ -610,3 +624,154 @@ def list_configs(op, hidden: int):
     arr = (LaunchCfg * max(n, 1))()
     lib().norm_list_configs(int(op), hidden, arr, n)
     return [Cfg(*arr[i].astuple()) for i in range(n)]
+
+
+# ---- fp32 activations -----------------------------------------------------------
+# Contiguous fp32 tensors throughout; the library requires hidden % 4 == 0 and
+# 16-byte-aligned matrices and weight / bias vectors (it reports a violation).
+def _f32_rows(x, name):
+    _mat(x, name, torch.float32)
+    return _rows_hidden(x)
+
+
+def _f32_same(t, ref, name):
+    _mat(t, name, torch.float32)
+    if t.shape != ref.shape:
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    return t
+
+
+def _f32_out(t, ref, name):
+    return _f32_same(torch.empty_like(ref) if t is None else t, ref, name)
+
+
+def _f32_colsum(t, hidden, name, device):
+    t = torch.empty(hidden, dtype=torch.float32, device=device) if t is None else t
+    return _vec(t, hidden, name, torch.float32)
+
+
+def fused_add_rmsnorm_f32(x, residual, weight, eps: float, out=None, stream=None):
+    """fp32 fused_add_rmsnorm: residual <- x + residual (fp32) in place;
+    returns (out, residual)."""
+    rows, hidden = _f32_rows(x, "x")
+    _f32_same(residual, x, "residual")
+    _vec(weight, hidden, "weight", torch.float32)
+    out = _f32_out(out, x, "out")
+    _check(lib().norm_fused_add_rmsnorm_f32(out.data_ptr(), residual.data_ptr(), x.data_ptr(),
+                                            weight.data_ptr(), rows, hidden, float(eps),
+                                            _stream(stream, x, residual, weight, out)),
+           "norm_fused_add_rmsnorm_f32")
+    return out, residual
+
+
+def rmsnorm_fwd_f32(x, weight, eps: float, out=None, stream=None):
+    rows, hidden = _f32_rows(x, "x")
+    _vec(weight, hidden, "weight", torch.float32)
+    out = _f32_out(out, x, "out")
+    _check(lib().norm_rmsnorm_fwd_f32(out.data_ptr(), x.data_ptr(), weight.data_ptr(), rows,
+                                      hidden, float(eps), _stream(stream, x, weight, out)),
+           "norm_rmsnorm_fwd_f32")
+    return out
+
+
+def layernorm_fwd_f32(x, weight, bias, eps: float, y=None, mean=None, rstd=None,
+                      with_stats: bool = True, stream=None):
+    """Returns (y, mean, rstd); mean/rstd are None when with_stats is False."""
+    rows, hidden = _f32_rows(x, "x")
+    _vec(weight, hidden, "weight", torch.float32)
+    _vec(bias, hidden, "bias", torch.float32)
+    y = _f32_out(y, x, "y")
+    if with_stats:
+        mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+        _mat(mean, "mean", torch.float32)
+        _mat(rstd, "rstd", torch.float32)
+        if mean.numel() != rows or rstd.numel() != rows:
+            raise ValueError("mean/rstd must hold one value per row")
+        mp, rp = mean.data_ptr(), rstd.data_ptr()
+    else:
+        mean = rstd = None
+        mp = rp = None
+    _check(lib().norm_layernorm_fwd_f32(y.data_ptr(), mp, rp, x.data_ptr(), weight.data_ptr(),
+                                        bias.data_ptr(), rows, hidden, float(eps),
+                                        _stream(stream, x, weight, bias, y, mean, rstd)),
+           "norm_layernorm_fwd_f32")
+    return y, mean, rstd
+
+
+def workspace_bytes_f32(op, rows: int, hidden: int) -> int:
+    """Workspace bytes of an fp32 backward op."""
+    return int(lib().norm_bwd_workspace_bytes_f32(int(OPS.get(op, op)), rows, hidden))
+
+
+def _f32_ws(workspace, op, rows, hidden, device):
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes_f32(op, rows, hidden), 16),
+                                dtype=torch.uint8, device=device)
+    _mat(workspace, "workspace", workspace.dtype)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def layernorm_bwd_f32(dy, x, mean, rstd, weight, eps: float = 0.0, dx=None, dweight=None,
+                      dbias=None, workspace=None, stream=None):
+    """Returns (dx, dweight, dbias)."""
+    rows, hidden = _f32_rows(x, "x")
+    _f32_same(dy, x, "dy")
+    _vec(weight, hidden, "weight", torch.float32)
+    _mat(mean, "mean", torch.float32)
+    _mat(rstd, "rstd", torch.float32)
+    if mean.numel() != rows or rstd.numel() != rows:
+        raise ValueError("mean/rstd must hold one value per row")
+    dx = _f32_out(dx, x, "dx")
+    dweight = _f32_colsum(dweight, hidden, "dweight", x.device)
+    dbias = _f32_colsum(dbias, hidden, "dbias", x.device)
+    workspace, wsb = _f32_ws(workspace, "layernorm_bwd", rows, hidden, x.device)
+    _check(lib().norm_layernorm_bwd_f32(dx.data_ptr(), dweight.data_ptr(), dbias.data_ptr(),
+                                        dy.data_ptr(), x.data_ptr(), mean.data_ptr(),
+                                        rstd.data_ptr(), weight.data_ptr(), workspace.data_ptr(),
+                                        wsb, rows, hidden, float(eps),
+                                        _stream(stream, dy, x, mean, rstd, weight, dx, dweight,
+                                                dbias, workspace)),
+           "norm_layernorm_bwd_f32")
+    return dx, dweight, dbias
+
+
+def rmsnorm_bwd_f32(dy, x, weight, eps: float, dx=None, dweight=None, workspace=None,
+                    stream=None):
+    """Returns (dx, dweight); rstd is recomputed from x with eps."""
+    rows, hidden = _f32_rows(x, "x")
+    _f32_same(dy, x, "dy")
+    _vec(weight, hidden, "weight", torch.float32)
+    dx = _f32_out(dx, x, "dx")
+    dweight = _f32_colsum(dweight, hidden, "dweight", x.device)
+    workspace, wsb = _f32_ws(workspace, "rmsnorm_bwd", rows, hidden, x.device)
+    _check(lib().norm_rmsnorm_bwd_f32(dx.data_ptr(), dweight.data_ptr(), dy.data_ptr(),
+                                      x.data_ptr(), weight.data_ptr(), workspace.data_ptr(), wsb,
+                                      rows, hidden, float(eps),
+                                      _stream(stream, dy, x, weight, dx, dweight, workspace)),
+           "norm_rmsnorm_bwd_f32")
+    return dx, dweight
+
+
+def fused_add_rmsnorm_bwd_f32(dout, s, weight, eps: float, dres=None, ds=None, dweight=None,
+                              workspace=None, stream=None):
+    """Backward of fused_add_rmsnorm_f32 at its residual output s: returns
+    (ds, dweight)."""
+    rows, hidden = _f32_rows(s, "s")
+    _f32_same(dout, s, "dout")
+    if dres is not None:
+        _f32_same(dres, s, "dres")
+    _vec(weight, hidden, "weight", torch.float32)
+    ds = _f32_out(ds, s, "ds")
+    dweight = _f32_colsum(dweight, hidden, "dweight", s.device)
+    workspace, wsb = _f32_ws(workspace, "fused_add_rmsnorm_bwd", rows, hidden, s.device)
+    _check(lib().norm_fused_add_rmsnorm_bwd_f32(ds.data_ptr(), dweight.data_ptr(),
+                                                dout.data_ptr(),
+                                                dres.data_ptr() if dres is not None else None,
+                                                s.data_ptr(), weight.data_ptr(),
+                                                workspace.data_ptr(), wsb, rows, hidden,
+                                                float(eps),
+                                                _stream(stream, dout, dres, s, weight, ds,
+                                                        dweight, workspace)),
+           "norm_fused_add_rmsnorm_bwd_f32")
+    return ds, dweight

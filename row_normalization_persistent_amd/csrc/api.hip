@@ -766,7 +766,7 @@ norm_status run_fwd(norm_op op, const FwdCall& c, const norm_launch_cfg* cfg,
         const int sop = op == NORM_OP_FUSED_ADD_RMSNORM ? kSplitFused
                         : op == NORM_OP_LAYERNORM_FWD   ? kSplitLn
                                                         : kSplitRms;
-        return from_hip(launch_stream_fwd(sop, a, stream));
+        return from_hip(launch_stream_fwd(sop, false, a, stream));
     }
     if (!e) return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
     const int64_t groups = ceil_div(c.rows, k.rows_per_block);
@@ -1063,7 +1063,7 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
                        c.ld_dx, c.ld_dy,  c.ld_x,    ld_dres, c.rows,
                        (int32_t)c.hidden, k.grid, c.eps};
     if (streamed)
-        return from_hip(launch_stream_bwd(op == NORM_OP_LAYERNORM_BWD, a,
+        return from_hip(launch_stream_bwd(op == NORM_OP_LAYERNORM_BWD, false, a,
                                           stream_tiles(c.hidden), k.grid, stream));
     return from_hip(dyn_launch(a, stream));
 }
@@ -1122,6 +1122,111 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
     if (k.threads_per_row == 0) return NORM_ERROR_UNSUPPORTED_HIDDEN;
     *cfg = k;
     return NORM_SUCCESS;
+}
+
+// ---- fp32 activations ------------------------------------------------------------
+// Every fp32 call runs the streamed kernels (kernels_stream.hpp) with four fp32
+// values a 16-byte access: contiguous rows, hidden a multiple of 4 up to
+// kStreamMaxHidden, the matrices and weight / bias vectors 16-byte aligned,
+// mean / rstd 4-byte aligned.  The forward reads a row of up to 16384 values
+// once and a wider one twice; the backward is the streamed pair of kernels
+// plus the column reduce at every width.
+int32_t stream_tiles_f32(int64_t hidden) {
+    return (int32_t)ceil_div(hidden, kStreamTileColsF32);
+}
+int32_t stream_walkers_f32(int64_t rows, int64_t hidden) {
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles_f32(hidden)));
+}
+bool f32_hidden_ok(int64_t hidden) {
+    return hidden >= 4 && hidden % 4 == 0 && hidden <= kStreamMaxHidden;
+}
+
+norm_status run_fwd_f32(norm_op op, const FwdCall& c, hipStream_t stream) {
+    const bool fused = op == NORM_OP_FUSED_ADD_RMSNORM;
+    const bool ln = op == NORM_OP_LAYERNORM_FWD;
+    if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
+    if (c.rows == 0) return NORM_SUCCESS;
+    if (!f32_hidden_ok(c.hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    if (!c.out || !c.x || !c.weight || (fused && !c.residual) || (ln && !c.bias))
+        return NORM_ERROR_INVALID_VALUE;
+    if (ln && ((c.mean == nullptr) != (c.rstd == nullptr))) return NORM_ERROR_INVALID_VALUE;
+    if (!span_ok(c.rows, c.hidden, c.hidden, 4)) return NORM_ERROR_INVALID_VALUE;
+    if (!aligned(c.out, 16) || !aligned(c.x, 16) || !aligned(c.weight, 16) ||
+        (fused && !aligned(c.residual, 16)) || (ln && !aligned(c.bias, 16)) ||
+        (ln && c.mean && (!aligned(c.mean, 4) || !aligned(c.rstd, 4))))
+        return NORM_ERROR_MISALIGNED;
+    const Region out{c.out, c.rows, c.hidden, c.hidden, 4}, x{c.x, c.rows, c.hidden, c.hidden, 4};
+    const Region res{fused ? c.residual : nullptr, c.rows, c.hidden, c.hidden, 4};
+    const Region w = vec_region(c.weight, c.hidden, 4);
+    const Region b = vec_region(ln ? c.bias : nullptr, c.hidden, 4);
+    const Region mean = vec_region(ln ? c.mean : nullptr, c.rows, 4);
+    const Region rstd = vec_region(ln ? c.rstd : nullptr, c.rows, 4);
+    // outputs must not overlap anything, except out == x exactly
+    if (conflict(out, x, true) || conflict(out, w, false) || conflict(out, res, false) ||
+        conflict(out, b, false) || conflict(out, mean, false) || conflict(out, rstd, false) ||
+        conflict(res, x, false) || conflict(res, w, false) || conflict(res, b, false) ||
+        conflict(mean, x, false) || conflict(mean, w, false) || conflict(mean, b, false) ||
+        conflict(mean, rstd, false) || conflict(rstd, x, false) || conflict(rstd, w, false) ||
+        conflict(rstd, b, false))
+        return NORM_ERROR_INVALID_VALUE;
+    const DynFwdArgs a{c.out,    c.residual, c.x,      c.weight, c.bias,
+                       c.mean,   c.rstd,     c.hidden, c.hidden, c.hidden,
+                       c.rows,   (int32_t)c.hidden,   c.eps};
+    const int sop = fused ? kSplitFused : ln ? kSplitLn : kSplitRms;
+    return from_hip(launch_stream_fwd(sop, true, a, stream));
+}
+
+size_t ws_query_f32(norm_op op, int64_t rows, int64_t hidden) {
+    if (rows <= 0 || !f32_hidden_ok(hidden)) return 0;
+    return stream_ws_bytes(op, hidden, stream_walkers_f32(rows, hidden), rows);
+}
+
+norm_status run_bwd_f32(norm_op op, const BwdCall& c, hipStream_t stream) {
+    const bool ln = op == NORM_OP_LAYERNORM_BWD;
+    if (c.rows < 0 || c.rows > kMaxRows || !eps_ok(c.eps)) return NORM_ERROR_INVALID_VALUE;
+    if (!f32_hidden_ok(c.hidden)) return NORM_ERROR_UNSUPPORTED_HIDDEN;
+    const bool any = c.rows > 0;
+    if (!c.dweight || (ln && !c.dbias) || !c.workspace) return NORM_ERROR_INVALID_VALUE;
+    if (any && (!c.dx || !c.dy || !c.x || !c.weight || (ln && (!c.mean || !c.rstd))))
+        return NORM_ERROR_INVALID_VALUE;
+    if (!span_ok(c.rows, c.hidden, c.hidden, 4)) return NORM_ERROR_INVALID_VALUE;
+    if (!aligned(c.dweight, 4) || (ln && !aligned(c.dbias, 4)) || !aligned(c.workspace, 16))
+        return NORM_ERROR_MISALIGNED;
+    if (any && (!aligned(c.dx, 16) || !aligned(c.dy, 16) || !aligned(c.x, 16) ||
+                !aligned(c.weight, 16) || (c.dres && !aligned(c.dres, 16)) ||
+                (ln && (!aligned(c.mean, 4) || !aligned(c.rstd, 4)))))
+        return NORM_ERROR_MISALIGNED;
+    const int32_t tiles = stream_tiles_f32(c.hidden);
+    const int32_t walkers = stream_walkers_f32(c.rows, c.hidden);
+    const size_t ws_need = stream_ws_bytes(op, c.hidden, any ? walkers : 0, any ? c.rows : 0);
+
+    const int64_t mrows = any ? c.rows : 0;
+    const int64_t h = c.hidden;
+    const Region dx{c.dx, mrows, h, h, 4}, dy{c.dy, mrows, h, h, 4}, x{c.x, mrows, h, h, 4},
+        dres{c.dres, mrows, h, h, 4};
+    const Region mean = vec_region(ln ? c.mean : nullptr, mrows, 4),
+                 rstd = vec_region(ln ? c.rstd : nullptr, mrows, 4),
+                 w = vec_region(any ? c.weight : nullptr, h, 4),
+                 dw = vec_region(c.dweight, h, 4),
+                 db = vec_region(ln ? c.dbias : nullptr, h, 4),
+                 wsr = vec_region(c.workspace, (int64_t)ws_need, 1);
+    // outputs overlap no input, except dx == dy (or dx == dres) exactly
+    for (const Region* in : {&dy, &x, &mean, &rstd, &dres, &w}) {
+        const bool alias_ok = in == &dy || in == &dres;
+        if (conflict(dx, *in, alias_ok) || conflict(dw, *in, false) ||
+            conflict(db, *in, false) || conflict(wsr, *in, false))
+            return NORM_ERROR_INVALID_VALUE;
+    }
+    if (conflict(dx, dw, false) || conflict(dx, db, false) || conflict(dx, wsr, false) ||
+        conflict(dw, db, false) || conflict(dw, wsr, false) || conflict(db, wsr, false))
+        return NORM_ERROR_INVALID_VALUE;
+    if (c.workspace_bytes < ws_need) return NORM_ERROR_WORKSPACE;
+
+    const DynBwdArgs a{c.dx,    c.dy,     c.x,       c.mean,    c.rstd,
+                       c.dres,  c.weight, (float*)c.workspace, c.dweight, c.dbias,
+                       h,       h,        h,         h,         c.rows,
+                       (int32_t)h, walkers, c.eps};
+    return from_hip(launch_stream_bwd(ln, true, a, tiles, walkers, stream));
 }
 
 }  // namespace
@@ -1379,6 +1484,65 @@ norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const void* dou
                                        int64_t hidden, float eps, hipStream_t stream) {
     return norm_fused_add_rmsnorm_bwd_cfg(ds, dweight, dout, dres, s, weight, workspace,
                                           workspace_bytes, rows, hidden, eps, nullptr, stream);
+}
+
+// ---- fp32 activations ---------------------------------------------------------------
+norm_status norm_fused_add_rmsnorm_f32(float* out, float* residual, const float* x,
+                                       const float* weight, int64_t rows, int64_t hidden,
+                                       float eps, hipStream_t stream) {
+    const FwdCall c{out,    hidden,  residual, hidden, x,      hidden, weight,
+                    nullptr, nullptr, nullptr, rows,   hidden, eps};
+    return run_fwd_f32(NORM_OP_FUSED_ADD_RMSNORM, c, stream);
+}
+
+norm_status norm_rmsnorm_fwd_f32(float* out, const float* x, const float* weight, int64_t rows,
+                                 int64_t hidden, float eps, hipStream_t stream) {
+    const FwdCall c{out,    hidden,  nullptr, hidden, x,      hidden, weight,
+                    nullptr, nullptr, nullptr, rows,  hidden, eps};
+    return run_fwd_f32(NORM_OP_RMSNORM_FWD, c, stream);
+}
+
+norm_status norm_layernorm_fwd_f32(float* y, float* mean, float* rstd, const float* x,
+                                   const float* weight, const float* bias, int64_t rows,
+                                   int64_t hidden, float eps, hipStream_t stream) {
+    const FwdCall c{y, hidden, nullptr, hidden, x, hidden, weight, bias, mean, rstd, rows,
+                    hidden, eps};
+    return run_fwd_f32(NORM_OP_LAYERNORM_FWD, c, stream);
+}
+
+norm_status norm_layernorm_bwd_f32(float* dx, float* dweight, float* dbias, const float* dy,
+                                   const float* x, const float* mean, const float* rstd,
+                                   const float* weight, void* workspace, size_t workspace_bytes,
+                                   int64_t rows, int64_t hidden, float eps, hipStream_t stream) {
+    const BwdCall c{dx,     hidden,  dy,        hidden, x,         hidden, mean,
+                    rstd,   nullptr, hidden,    weight, workspace, workspace_bytes,
+                    dweight, dbias,  rows,      hidden, eps};
+    return run_bwd_f32(NORM_OP_LAYERNORM_BWD, c, stream);
+}
+
+norm_status norm_rmsnorm_bwd_f32(float* dx, float* dweight, const float* dy, const float* x,
+                                 const float* weight, void* workspace, size_t workspace_bytes,
+                                 int64_t rows, int64_t hidden, float eps, hipStream_t stream) {
+    const BwdCall c{dx,      hidden,  dy,      hidden, x,         hidden, nullptr,
+                    nullptr, nullptr, hidden,  weight, workspace, workspace_bytes,
+                    dweight, nullptr, rows,    hidden, eps};
+    return run_bwd_f32(NORM_OP_RMSNORM_BWD, c, stream);
+}
+
+norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, const float* dout,
+                                           const float* dres, const float* s,
+                                           const float* weight, void* workspace,
+                                           size_t workspace_bytes, int64_t rows, int64_t hidden,
+                                           float eps, hipStream_t stream) {
+    const BwdCall c{ds,      hidden,  dout,   hidden, s,         hidden, nullptr,
+                    nullptr, dres,    hidden, weight, workspace, workspace_bytes,
+                    dweight, nullptr, rows,   hidden, eps};
+    return run_bwd_f32(NORM_OP_FUSED_ADD_RMSNORM_BWD, c, stream);
+}
+
+size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden) {
+    if (!is_bwd(op)) return 0;
+    return ws_query_f32(op, rows, hidden);
 }
 
 // ---- queries ---------------------------------------------------------------------------

@@ -1,5 +1,8 @@
 // Streamed rows (kernels_stream.hpp): the forward of each operation and the
-// backward's two kernels, ahead of the shared column reduce.
+// backward's two kernels, ahead of the shared column reduce, for bf16 and
+// fp32 activations.
+#include <type_traits>
+
 #include "kernels_stream.hpp"
 
 namespace rownorm {
@@ -9,46 +12,94 @@ namespace rownorm {
 template <bool LN, bool DRES>
 constexpr int tile_depth() { return DRES ? 2 : 3; }
 
-hipError_t launch_stream_fwd(int op, const DynFwdArgs& a, hipStream_t stream) {
+template <typename E, int T>
+hipError_t fwd_by_op(int op, const DynFwdArgs& a, hipStream_t stream) {
     switch (op) {
-        case kSplitFused: return launch_stream_fwd_op<kSplitFused>(a, stream);
-        case kSplitRms: return launch_stream_fwd_op<kSplitRms>(a, stream);
-        case kSplitLn: return launch_stream_fwd_op<kSplitLn>(a, stream);
+        case kSplitFused: return launch_stream_fwd_op<E, kSplitFused, T>(a, stream);
+        case kSplitRms: return launch_stream_fwd_op<E, kSplitRms, T>(a, stream);
+        case kSplitLn: return launch_stream_fwd_op<E, kSplitLn, T>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool LN, bool DRES>
+hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t stream) {
+    if (!f32) return fwd_by_op<uint16_t, kStreamFwdLanes>(op, a, stream);
+    switch (stream_fwd_lanes_f32(a.hidden)) {
+        case 64: return fwd_by_op<float, 64>(op, a, stream);
+        case 128: return fwd_by_op<float, 128>(op, a, stream);
+        case 256: return fwd_by_op<float, 256>(op, a, stream);
+        case 512: return fwd_by_op<float, 512>(op, a, stream);
+        default: return fwd_by_op<float, kStreamFwdLanes>(op, a, stream);
+    }
+}
+
+template <typename E, bool LN, bool DRES>
 hipError_t launch_tiles(const DynBwdArgs& a, const float* stats, int32_t tiles, int32_t walkers,
                         hipStream_t stream) {
-    hipLaunchKernelGGL((stream_bwd_tile_kernel<kStreamTileVecs, LN, DRES, tile_depth<LN, DRES>()>),
-                       dim3((unsigned)(walkers * tiles)), dim3(kStreamTileLanes), 0, stream, a,
-                       stats, (int)tiles);
+    hipLaunchKernelGGL(
+        (stream_bwd_tile_kernel<E, kStreamTileVecs, LN, DRES, tile_depth<LN, DRES>()>),
+        dim3((unsigned)(walkers * tiles)), dim3(kStreamTileLanes), 0, stream, a, stats,
+        (int)tiles);
     return hipGetLastError();
 }
 
-hipError_t launch_stream_bwd(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t walkers,
-                             hipStream_t stream) {
+// One tile holds the whole fp32 row (hidden <= 8192): V accesses a lane, the
+// row reduced in the tile kernel, each row read once.  Ring depth: the
+// deepest without spills, fewer rows for wider tiles and with dres.
+template <int V, bool DRES>
+constexpr int inrow_depth() { return V == 4 ? (DRES ? 2 : 3) : V == 2 ? (DRES ? 3 : 4) : (DRES ? 6 : 8); }
+
+template <int V, bool LN, bool DRES>
+hipError_t launch_inrow(const DynBwdArgs& a, int32_t walkers, hipStream_t stream) {
+    hipLaunchKernelGGL(
+        (stream_bwd_tile_kernel<float, V, LN, DRES, inrow_depth<V, DRES>(), true>),
+        dim3((unsigned)walkers), dim3(kStreamTileLanes), 0, stream, a, nullptr, 1);
+    return hipGetLastError();
+}
+
+template <bool LN, bool DRES>
+hipError_t inrow_by_vecs(const DynBwdArgs& a, int32_t walkers, hipStream_t stream) {
+    switch (stream_inrow_vecs_f32(a.hidden)) {
+        case 1: return launch_inrow<1, LN, DRES>(a, walkers, stream);
+        case 2: return launch_inrow<2, LN, DRES>(a, walkers, stream);
+        default: return launch_inrow<4, LN, DRES>(a, walkers, stream);
+    }
+}
+
+template <typename E>
+hipError_t stream_bwd_typed(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t walkers,
+                            hipStream_t stream) {
     const int outs = ln ? 2 : 1;
     const int32_t padded = (int32_t)((a.hidden + 63) / 64 * 64);
-    if (a.rows > 0) {
+    if (a.rows > 0 && std::is_same_v<E, float> && tiles == 1) {
+        hipError_t e = ln              ? inrow_by_vecs<true, false>(a, walkers, stream)
+                       : a.dres        ? inrow_by_vecs<false, true>(a, walkers, stream)
+                                       : inrow_by_vecs<false, false>(a, walkers, stream);
+        if (e != hipSuccess) return e;
+    } else if (a.rows > 0) {
         float* stats = a.workspace + (int64_t)walkers * outs * padded;
         const int64_t grid = a.rows < kStreamMaxGrid ? a.rows : kStreamMaxGrid;
         if (ln)
-            hipLaunchKernelGGL((stream_bwd_stats_kernel<true>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((stream_bwd_stats_kernel<E, true>), dim3((unsigned)grid),
                                dim3(kStreamFwdLanes), 0, stream, a, stats);
         else
-            hipLaunchKernelGGL((stream_bwd_stats_kernel<false>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((stream_bwd_stats_kernel<E, false>), dim3((unsigned)grid),
                                dim3(kStreamFwdLanes), 0, stream, a, stats);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (ln) e = launch_tiles<true, false>(a, stats, tiles, walkers, stream);
-        else if (a.dres) e = launch_tiles<false, true>(a, stats, tiles, walkers, stream);
-        else e = launch_tiles<false, false>(a, stats, tiles, walkers, stream);
+        if (ln) e = launch_tiles<E, true, false>(a, stats, tiles, walkers, stream);
+        else if (a.dres) e = launch_tiles<E, false, true>(a, stats, tiles, walkers, stream);
+        else e = launch_tiles<E, false, false>(a, stats, tiles, walkers, stream);
         if (e != hipSuccess) return e;
     }
     return launch_norm_colreduce(a.workspace, a.rows > 0 ? walkers : 0, a.hidden, padded, outs,
                                  a.dweight, a.dbias, stream);
+}
+
+hipError_t launch_stream_bwd(bool ln, bool f32, const DynBwdArgs& a, int32_t tiles,
+                             int32_t walkers, hipStream_t stream) {
+    return f32 ? stream_bwd_typed<float>(ln, a, tiles, walkers, stream)
+               : stream_bwd_typed<uint16_t>(ln, a, tiles, walkers, stream);
 }
 
 }  // namespace rownorm

@@ -1,24 +1,29 @@
-// Rows too wide for one workgroup's registers and LDS: the streamed fallback
-// of the persistent buffer.  "TMA inner persistent scheduler" (description
-// summary) keeps the row in shared memory when registers cannot hold it; a row
-// of more than 65536 bf16 values (fused add + RMSNorm, RMSNorm), 49152
-// (LayerNorm forward) or 32768 (the backward operations, whose per-column
-// sums also live on chip) fits neither, so these kernels read it twice: once
-// for the row's reduction and once more, from the Infinity Cache while the
-// rows in flight fit there, for the normalized output.  16-byte accesses
-// only (hidden a multiple of 8, every row stride too, 16-byte-aligned
-// pointers), any such hidden up to 2^20.
+// Streamed rows: the rows of a [rows, hidden] matrix walked by workgroups that
+// read each row from memory twice instead of holding it on chip.  "TMA inner
+// persistent scheduler" (description summary) keeps the row in shared memory
+// when registers cannot hold it; a bf16 row of more than 65536 values (fused
+// add + RMSNorm, RMSNorm), 49152 (LayerNorm forward) or 32768 (the backward
+// operations, whose per-column sums also live on chip) fits neither, so
+// these kernels read it twice: once for the row's reduction and once more,
+// from the Infinity Cache while the rows in flight fit there, for the
+// normalized output.  The same kernels serve fp32 activations at every
+// width.  16-byte accesses only: E = uint16_t (bf16 patterns, 8 a 16-byte
+// access) or float (4), hidden a multiple of the access's element count,
+// every row stride too, 16-byte-aligned pointers, hidden up to 2^20.
 //
-// Forward (stream_fwd_kernel, 1024 lanes, workgroups walk the rows g, g + G,
-// ...): pass 1 streams the row for its statistic -- sum s^2 (s = x + r for
+// Forward (stream_fwd_kernel, T lanes a row -- 1024 for bf16; for fp32 as
+// many as give each lane at most 4 accesses of a row of up to 16384 values,
+// 1024 beyond -- workgroups walk the rows g, g + G, ...): pass 1 streams the row for its statistic -- sum s^2 (s = x + r for
 // the fused op), or for LayerNorm each lane's count, sum and centered sum of
 // squares, merged access by access with the pairwise update of a sum of
 // squared deviations (Chan, Golub & LeVeque), then combined over the lanes
 // exactly as the row split combines its chunks:
 //   mean = sum_l S_l / H,  M2 = sum_l M2_l + n_l (S_l / n_l - mean)^2;
-// pass 2 re-reads the row, normalizes and stores it (and the fused op's
-// residual, which pass 1 leaves untouched so that pass 2 still reads the
-// caller's residual).
+// pass 2 normalizes and stores the row (and the fused op's residual, which
+// pass 1 leaves untouched so that pass 2 still reads the caller's residual).
+// The row's first kStreamUnroll accesses a lane stay in registers from pass
+// 1 to pass 2; only the rest is read again (a row of up to 4 x T accesses is
+// read once: every fp32 row of up to 16384 values).
 //
 // Backward, two kernels before the shared column reduce:
 //  * stream_bwd_stats_kernel (1024 lanes, workgroups walk the rows): the
@@ -26,12 +31,15 @@
 //    RMSNorm rstd = rsqrt(mean_j x^2 + eps) and coef = rstd^3 mean_j g x --
 //    stored as two floats per row after the workspace's partial-sum slabs;
 //  * stream_bwd_tile_kernel (512 lanes): the columns are cut into tiles of
-//    512 * V * 8; workgroup (walker w, tile t) walks the rows w, w + P, ...
-//    of its tile with a ring of D rows in flight, writes dx of its columns
+//    512 * V accesses; workgroup (walker w, tile t) walks the rows w, w + P,
+//    ... of its tile with a ring of D rows in flight, writes dx of its columns
 //    and accumulates their column sums in registers (no reduction over the
 //    row, so no barrier in the loop), then writes them into slab w, columns
 //    of tile t: the same [P][outs][padded] layout as the other backward
-//    kernels.
+//    kernels.  When one tile holds the whole row (fp32 up to 8192 columns,
+//    V = 1, 2 or 4), the tile kernel forms the row's two reductions itself
+//    (INROW, one barrier a row) and the stats kernel is not launched: each
+//    row is then read once.
 #pragma once
 
 #include "dyn_common.hpp"
@@ -59,71 +67,168 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStreamUnroll = ROWNORM_STREAM_UNROLL;  // 16-byte accesses in flight per lane and matrix
 constexpr int kStreamPass1 = ROWNORM_STREAM_P1_POLICY;  // cache policy of the first read
 
+// ---- elements of a 16-byte access ------------------------------------------------
+template <typename E> struct Elems;
+template <> struct Elems<uint16_t> { static constexpr int kPer = 8; };  // bf16 patterns
+template <> struct Elems<float> { static constexpr int kPer = 4; };
+
+template <typename E>
+__device__ __forceinline__ void unpack16(const u32x4& v, float (&f)[Elems<E>::kPer]) {
+    if constexpr (Elems<E>::kPer == 8) {
+        unpack8(v, f);
+    } else {
+        f[0] = __uint_as_float(v.x);
+        f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z);
+        f[3] = __uint_as_float(v.w);
+    }
+}
+
+// bf16: round to nearest even; fp32: the values themselves
+template <typename E>
+__device__ __forceinline__ u32x4 pack16(const float (&f)[Elems<E>::kPer]) {
+    if constexpr (Elems<E>::kPer == 8) {
+        return pack8(f);
+    } else {
+        u32x4 v;
+        v.x = __float_as_uint(f[0]);
+        v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]);
+        v.w = __float_as_uint(f[3]);
+        return v;
+    }
+}
+
+template <int Aux>
+__device__ __forceinline__ u32x4 load16(rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, Aux);
+}
+__device__ __forceinline__ void store16(rsrc_t r, int byte_off, const u32x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kCachePolicyNT);
+}
+
 // ---- forward -------------------------------------------------------------------
-template <int OP>
-__global__ __launch_bounds__(kStreamFwdLanes) void stream_fwd_kernel(DynFwdArgs a) {
-    constexpr int T = kStreamFwdLanes;
+// One pass-1 step over accesses base + u * T (u < U) of the loaded chunk.
+template <typename E, int OP, int U, int T>
+__device__ __forceinline__ void stream_stat_step(const u32x4 (&xv)[U],
+                                                 const u32x4 (&rv)[OP == kSplitFused ? U : 1],
+                                                 int base, int n_acc, float& p0, float& p1,
+                                                 float& n_l) {
+    constexpr int EP = Elems<E>::kPer;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float s[EP];
+        unpack16<E>(xv[u], s);
+        if constexpr (OP == kSplitFused) {
+            float rf[EP];
+            unpack16<E>(rv[u], rf);
+#pragma unroll
+            for (int e = 0; e < EP; ++e) s[e] += rf[e];
+        }
+        if constexpr (OP == kSplitLn) {
+            if (base + u * T < n_acc) {  // an access past the row's end holds no data
+                float sg = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) sg += s[e];
+                const float mg = sg * (1.0f / EP);
+                float m2g = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EP; ++e) m2g += (s[e] - mg) * (s[e] - mg);
+                if (n_l == 0.0f) {
+                    p0 = sg;
+                    p1 = m2g;
+                } else {
+                    const float d = mg - p0 / n_l;
+                    p1 += m2g + d * d * (n_l * (float)EP / (n_l + (float)EP));
+                    p0 += sg;
+                }
+                n_l += (float)EP;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < EP; ++e) p0 += s[e] * s[e];  // past the end: zeros
+        }
+    }
+}
+
+// One pass-2 step: normalize and store the U accesses base + u * T.
+template <typename E, int OP, int U, int T>
+__device__ __forceinline__ void stream_norm_step(const u32x4 (&xv)[U],
+                                                 const u32x4 (&rv)[OP == kSplitFused ? U : 1],
+                                                 rsrc_t rw, rsrc_t rb, rsrc_t rr, rsrc_t ro,
+                                                 int base, float mu, float rstd) {
+    constexpr int EP = Elems<E>::kPer;
+    u32x4 wv[U], bv[OP == kSplitLn ? U : 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        wv[u] = load16<0>(rw, (base + u * T) * 16);
+        if constexpr (OP == kSplitLn) bv[u] = load16<0>(rb, (base + u * T) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int off = (base + u * T) * 16;
+        float s[EP], wf[EP], o[EP];
+        unpack16<E>(xv[u], s);
+        unpack16<E>(wv[u], wf);
+        if constexpr (OP == kSplitFused) {
+            float rf[EP];
+            unpack16<E>(rv[u], rf);
+#pragma unroll
+            for (int e = 0; e < EP; ++e) s[e] += rf[e];
+            store16(rr, off, pack16<E>(s));
+        }
+        if constexpr (OP == kSplitLn) {
+            float bf[EP];
+            unpack16<E>(bv[u], bf);
+#pragma unroll
+            for (int e = 0; e < EP; ++e) o[e] = (s[e] - mu) * rstd * wf[e] + bf[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < EP; ++e) o[e] = s[e] * rstd * wf[e];
+        }
+        store16(ro, off, pack16<E>(o));
+    }
+}
+
+template <typename E, int OP, int T>
+__global__ __launch_bounds__(T) void stream_fwd_kernel(DynFwdArgs a) {
     constexpr int U = kStreamUnroll;
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
     constexpr bool kFused = OP == kSplitFused, kLn = OP == kSplitLn;
     __shared__ float red[4 * (T / kWave)];
     const int lane = threadIdx.x;
     const int h = a.hidden;
-    const int n_acc = h / 8;
+    const int n_acc = h / EP;
     const float inv_h = 1.0f / (float)h;
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * ES);
     rsrc_t rb = rw;
-    if constexpr (kLn) rb = row_rsrc_ld(a.bias, 0, 1, 0, h * 2);
+    if constexpr (kLn) rb = row_rsrc_ld(a.bias, 0, 1, 0, h * ES);
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t r = opaque_row(row);
-        const rsrc_t rx = row_rsrc_ld(a.x, r, a.rows, a.ld_x * 2, h * 2);
-        const rsrc_t ro = row_rsrc_ld(a.out, r, a.rows, a.ld_out * 2, h * 2);
+        const rsrc_t rx = row_rsrc_ld(a.x, r, a.rows, a.ld_x * ES, h * ES);
+        const rsrc_t ro = row_rsrc_ld(a.out, r, a.rows, a.ld_out * ES, h * ES);
         rsrc_t rr = rx;
-        if constexpr (kFused) rr = row_rsrc_ld(a.residual, r, a.rows, a.ld_res * 2, h * 2);
+        if constexpr (kFused) rr = row_rsrc_ld(a.residual, r, a.rows, a.ld_res * ES, h * ES);
 
-        // pass 1: the row's statistic
+        // pass 1: the row's statistic; the first U accesses a lane are kept
         float p0 = 0.0f, p1 = 0.0f, n_l = 0.0f;
-        for (int base = lane; base < n_acc; base += U * T) {
+        u32x4 x0[U], r0[kFused ? U : 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x0[u] = load16<kStreamPass1>(rx, (lane + u * T) * 16);
+            if constexpr (kFused) r0[u] = load16<kStreamPass1>(rr, (lane + u * T) * 16);
+        }
+        stream_stat_step<E, OP, U, T>(x0, r0, lane, n_acc, p0, p1, n_l);
+        for (int base = lane + U * T; base < n_acc; base += U * T) {
             u32x4 xv[U], rv[kFused ? U : 1];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                xv[u] = aload<8, kStreamPass1>(rx, (base + u * T) * 16);
-                if constexpr (kFused) rv[u] = aload<8, kStreamPass1>(rr, (base + u * T) * 16);
+                xv[u] = load16<kStreamPass1>(rx, (base + u * T) * 16);
+                if constexpr (kFused) rv[u] = load16<kStreamPass1>(rr, (base + u * T) * 16);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float s[8];
-                unpack8(xv[u], s);
-                if constexpr (kFused) {
-                    float rf[8];
-                    unpack8(rv[u], rf);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] += rf[e];
-                }
-                if constexpr (kLn) {
-                    if (base + u * T < n_acc) {  // an access past the row's end holds no data
-                        float sg = 0.0f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) sg += s[e];
-                        const float mg = sg * 0.125f;
-                        float m2g = 0.0f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) m2g += (s[e] - mg) * (s[e] - mg);
-                        if (n_l == 0.0f) {
-                            p0 = sg;
-                            p1 = m2g;
-                        } else {
-                            const float d = mg - p0 / n_l;
-                            p1 += m2g + d * d * (n_l * 8.0f / (n_l + 8.0f));
-                            p0 += sg;
-                        }
-                        n_l += 8.0f;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) p0 += s[e] * s[e];  // past the end: zeros
-                }
-            }
+            stream_stat_step<E, OP, U, T>(xv, rv, base, n_acc, p0, p1, n_l);
         }
         float mu = 0.0f, rstd;
         if constexpr (kLn) {
@@ -140,73 +245,50 @@ __global__ __launch_bounds__(kStreamFwdLanes) void stream_fwd_kernel(DynFwdArgs 
             rstd = fast_rsqrt(row_sum<T>(p0, red, lane) * inv_h + a.eps);
         }
 
-        // pass 2: normalize (the row comes back from the caches while the rows
-        // in flight fit there)
-        for (int base = lane; base < n_acc; base += U * T) {
-            u32x4 xv[U], rv[kFused ? U : 1], wv[U], bv[kLn ? U : 1];
+        // pass 2: normalize; the rest of the row comes back from the caches
+        // while the rows in flight fit there
+        stream_norm_step<E, OP, U, T>(x0, r0, rw, rb, rr, ro, lane, mu, rstd);
+        for (int base = lane + U * T; base < n_acc; base += U * T) {
+            u32x4 xv[U], rv[kFused ? U : 1];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int off = (base + u * T) * 16;
-                xv[u] = aload<8, kCachePolicyNT>(rx, off);
-                if constexpr (kFused) rv[u] = aload<8, kCachePolicyNT>(rr, off);
-                wv[u] = aload<8, 0>(rw, off);
-                if constexpr (kLn) bv[u] = aload<8, 0>(rb, off);
+                xv[u] = load16<kCachePolicyNT>(rx, (base + u * T) * 16);
+                if constexpr (kFused) rv[u] = load16<kCachePolicyNT>(rr, (base + u * T) * 16);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int off = (base + u * T) * 16;
-                float s[8], wf[8], o[8];
-                unpack8(xv[u], s);
-                unpack8(wv[u], wf);
-                if constexpr (kFused) {
-                    float rf[8];
-                    unpack8(rv[u], rf);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s[e] += rf[e];
-                    astore<8, kCachePolicyNT>(rr, off, pack8(s));
-                }
-                if constexpr (kLn) {
-                    float bf[8];
-                    unpack8(bv[u], bf);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] = (s[e] - mu) * rstd * wf[e] + bf[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] = s[e] * rstd * wf[e];
-                }
-                astore<8, kCachePolicyNT>(ro, off, pack8(o));
-            }
+            stream_norm_step<E, OP, U, T>(xv, rv, rw, rb, rr, ro, base, mu, rstd);
         }
         // the next row's first reduction must not overwrite slots still being read
         __syncthreads();
     }
 }
 
-template <int OP>
+template <typename E, int OP, int T>
 hipError_t launch_stream_fwd_op(const DynFwdArgs& a, hipStream_t stream) {
     const int64_t grid = a.rows < kStreamMaxGrid ? a.rows : kStreamMaxGrid;
-    hipLaunchKernelGGL((stream_fwd_kernel<OP>), dim3((unsigned)grid), dim3(kStreamFwdLanes), 0,
-                       stream, a);
+    hipLaunchKernelGGL((stream_fwd_kernel<E, OP, T>), dim3((unsigned)grid), dim3(T), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
 // ---- backward: the rows' two reductions ------------------------------------------
-template <bool LN>
+template <typename E, bool LN>
 __global__ __launch_bounds__(kStreamFwdLanes) void stream_bwd_stats_kernel(DynBwdArgs a,
                                                                            float* stats) {
     constexpr int T = kStreamFwdLanes;
     constexpr int U = kStreamUnroll;
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
     __shared__ float red[2 * 2 * (T / kWave)];
     const int lane = threadIdx.x;
     const int h = a.hidden;
-    const int n_acc = h / 8;
+    const int n_acc = h / EP;
     const float inv_h = 1.0f / (float)h;
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * ES);
     int parity = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t r = opaque_row(row);
-        const rsrc_t rx = row_rsrc_ld(a.x, r, a.rows, a.ld_x * 2, h * 2);
-        const rsrc_t rd = row_rsrc_ld(a.dy, r, a.rows, a.ld_dy * 2, h * 2);
+        const rsrc_t rx = row_rsrc_ld(a.x, r, a.rows, a.ld_x * ES, h * ES);
+        const rsrc_t rd = row_rsrc_ld(a.dy, r, a.rows, a.ld_dy * ES, h * ES);
         float mean = 0.0f, q = 0.0f;
         if constexpr (LN) {
             mean = a.mean[r];
@@ -218,18 +300,18 @@ __global__ __launch_bounds__(kStreamFwdLanes) void stream_bwd_stats_kernel(DynBw
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int off = (base + u * T) * 16;
-                xv[u] = aload<8, kStreamPass1>(rx, off);
-                dv[u] = aload<8, kStreamPass1>(rd, off);
-                wv[u] = aload<8, 0>(rw, off);
+                xv[u] = load16<kStreamPass1>(rx, off);
+                dv[u] = load16<kStreamPass1>(rd, off);
+                wv[u] = load16<0>(rw, off);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float xf[8], df[8], wf[8];
-                unpack8(xv[u], xf);
-                unpack8(dv[u], df);
-                unpack8(wv[u], wf);
+                float xf[EP], df[EP], wf[EP];
+                unpack16<E>(xv[u], xf);
+                unpack16<E>(dv[u], df);
+                unpack16<E>(wv[u], wf);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < EP; ++e) {
                     const float g = df[e] * wf[e];
                     if constexpr (LN) {
                         s1 += g;
@@ -264,33 +346,40 @@ struct TileRow {
     u32x4 dres[DRES ? V : 1];
     float s0, s1;                  // LayerNorm: c1, c2; RMSNorm: rstd, coef
     float mean, rstd;              // LayerNorm only
+    bool in;                       // a row of the matrix (not past its end)
 };
 
-// Loads row `row` of tile columns [col0, ...) (a row past the end loads
-// zeros from no memory and statistics of zero, so it adds nothing).
-template <int V, bool LN, bool DRES>
+// Loads row `row` of the tile whose first access is acc0 (a row past the end
+// loads zeros from no memory and statistics of zero, so it adds nothing).
+// INROW: the tile is the whole row and its statistics are reduced from the
+// loaded row (tile_row), not read from the stats kernel's output.
+template <typename E, int V, bool LN, bool DRES, bool INROW>
 __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdArgs& a,
-                                              const float* stats, int64_t row, int col0,
+                                              const float* stats, int64_t row, int acc0,
                                               int lane) {
     constexpr int T = kStreamTileLanes;
+    constexpr int ES = (int)sizeof(E);
     const int h = a.hidden;
-    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * 2, h * 2);
-    const rsrc_t rd = row_rsrc_ld(a.dy, row, a.rows, a.ld_dy * 2, h * 2);
+    const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * ES, h * ES);
+    const rsrc_t rd = row_rsrc_ld(a.dy, row, a.rows, a.ld_dy * ES, h * ES);
 #pragma unroll
-    for (int b = 0; b < V; ++b) t.x[b] = aload<8, kCachePolicyNT>(rx, (col0 + (b * T + lane) * 8) * 2);
+    for (int b = 0; b < V; ++b) t.x[b] = load16<kCachePolicyNT>(rx, (acc0 + b * T + lane) * 16);
 #pragma unroll
-    for (int b = 0; b < V; ++b) t.dy[b] = aload<8, kCachePolicyNT>(rd, (col0 + (b * T + lane) * 8) * 2);
+    for (int b = 0; b < V; ++b) t.dy[b] = load16<kCachePolicyNT>(rd, (acc0 + b * T + lane) * 16);
     if constexpr (DRES) {
-        const rsrc_t rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * 2, h * 2);
+        const rsrc_t rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * ES, h * ES);
 #pragma unroll
         for (int b = 0; b < V; ++b)
-            t.dres[b] = aload<8, kCachePolicyNT>(rr, (col0 + (b * T + lane) * 8) * 2);
+            t.dres[b] = load16<kCachePolicyNT>(rr, (acc0 + b * T + lane) * 16);
     }
     const bool in = row < a.rows;
     const int64_t rc = in ? row : a.rows - 1;
-    const float s0 = stats[2 * rc], s1 = stats[2 * rc + 1];
-    t.s0 = in ? s0 : 0.0f;
-    t.s1 = in ? s1 : 0.0f;
+    t.in = in;
+    if constexpr (!INROW) {
+        const float s0 = stats[2 * rc], s1 = stats[2 * rc + 1];
+        t.s0 = in ? s0 : 0.0f;
+        t.s1 = in ? s1 : 0.0f;
+    }
     if constexpr (LN) {
         const float m = a.mean[rc], q = a.rstd[rc];
         t.mean = in ? m : 0.0f;
@@ -298,20 +387,60 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
     }
 }
 
-template <int V, bool LN, bool DRES>
-__device__ __forceinline__ void tile_row(const TileRow<V, DRES>& t, const u32x4 (&wv)[V],
-                                         float (&pw)[V][8], float (&pb)[LN ? V : 1][8],
-                                         const DynBwdArgs& a, int64_t row, int col0, int lane) {
+template <typename E, int V, bool LN, bool DRES, bool INROW>
+__device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[V],
+                                         float (&pw)[V][Elems<E>::kPer],
+                                         float (&pb)[LN ? V : 1][Elems<E>::kPer],
+                                         const DynBwdArgs& a, int64_t row, int acc0, int lane,
+                                         float* red) {
     constexpr int T = kStreamTileLanes;
-    const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, a.hidden * 2);
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
+    if constexpr (INROW) {
+        // the row's two reductions, as stream_bwd_stats_kernel forms them
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int b = 0; b < V; ++b) {
+            float xf[EP], df[EP], wf[EP];
+            unpack16<E>(t.x[b], xf);
+            unpack16<E>(t.dy[b], df);
+            unpack16<E>(wv[b], wf);
+#pragma unroll
+            for (int e = 0; e < EP; ++e) {
+                const float g = df[e] * wf[e];
+                if constexpr (LN) {
+                    s1 += g;
+                    s2 += g * ((xf[e] - t.mean) * t.rstd);
+                } else {
+                    s1 += xf[e] * xf[e];
+                    s2 += g * xf[e];
+                }
+            }
+        }
+        row_sum2<T>(s1, s2, red, lane);
+        const float inv_h = 1.0f / (float)a.hidden;
+        if constexpr (LN) {
+            t.s0 = s1 * inv_h;
+            t.s1 = s2 * inv_h;
+        } else {
+            const float rstd = fast_rsqrt(s1 * inv_h + a.eps);
+            t.s0 = rstd;
+            t.s1 = rstd * rstd * rstd * s2 * inv_h;
+        }
+        if (!t.in) {  // a row past the end adds nothing (rsqrt(eps) may be infinite)
+            t.s0 = 0.0f;
+            t.s1 = 0.0f;
+        }
+    }
+    const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * ES, a.hidden * ES);
 #pragma unroll
     for (int b = 0; b < V; ++b) {
-        float xf[8], df[8], wf[8], o[8];
-        unpack8(t.x[b], xf);
-        unpack8(t.dy[b], df);
-        unpack8(wv[b], wf);
+        float xf[EP], df[EP], wf[EP], o[EP];
+        unpack16<E>(t.x[b], xf);
+        unpack16<E>(t.dy[b], df);
+        unpack16<E>(wv[b], wf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < EP; ++e) {
             const float g = df[e] * wf[e];
             if constexpr (LN) {
                 const float xh = (xf[e] - t.mean) * t.rstd;
@@ -324,57 +453,67 @@ __device__ __forceinline__ void tile_row(const TileRow<V, DRES>& t, const u32x4 
             }
         }
         if constexpr (DRES) {
-            float rf[8];
-            unpack8(t.dres[b], rf);
+            float rf[EP];
+            unpack16<E>(t.dres[b], rf);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += rf[e];
+            for (int e = 0; e < EP; ++e) o[e] += rf[e];
         }
-        astore<8, kCachePolicyNT>(rdx, (col0 + (b * T + lane) * 8) * 2, pack8(o));
+        store16(rdx, (acc0 + b * T + lane) * 16, pack16<E>(o));
     }
 }
 
 // Grid: walkers * tiles workgroups; workgroup i is tile i % tiles of walker
 // i / tiles.  The stats of every row are complete (stream_bwd_stats_kernel
-// ran before on the same stream).
-template <int V, bool LN, bool DRES, int D>
+// ran before on the same stream), or, with INROW (one tile holds the whole
+// row), reduced here from the row in registers: each row is then read once.
+template <typename E, int V, bool LN, bool DRES, int D, bool INROW = false>
 __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(DynBwdArgs a,
                                                                            const float* stats,
                                                                            int tiles) {
     constexpr int T = kStreamTileLanes;
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
+    // two sums per wave, two sets used alternately so that a row's reduction
+    // never overwrites slots the previous row's lanes may still be reading
+    __shared__ float red[INROW ? 2 * 2 * (T / kWave) : 1];
+    int parity = 0;
     const int lane = threadIdx.x;
     const int tile = blockIdx.x % tiles;
     const int64_t walker = blockIdx.x / tiles;
     const int64_t P = gridDim.x / tiles;
-    const int col0 = tile * (T * V * 8);
+    const int acc0 = tile * (T * V);  // the tile's first 16-byte access
     const int h = a.hidden;
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * ES);
     u32x4 wv[V];
 #pragma unroll
-    for (int b = 0; b < V; ++b) wv[b] = aload<8, 0>(rw, (col0 + (b * T + lane) * 8) * 2);
-    float pw[V][8], pb[LN ? V : 1][8];
+    for (int b = 0; b < V; ++b) wv[b] = load16<0>(rw, (acc0 + b * T + lane) * 16);
+    float pw[V][EP], pb[LN ? V : 1][EP];
 #pragma unroll
     for (int b = 0; b < V; ++b)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pw[b][e] = 0.0f;
+        for (int e = 0; e < EP; ++e) pw[b][e] = 0.0f;
 #pragma unroll
     for (int b = 0; b < (LN ? V : 1); ++b)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[b][e] = 0.0f;
+        for (int e = 0; e < EP; ++e) pb[b][e] = 0.0f;
 
     const int64_t n = walker < a.rows ? (a.rows - 1 - walker) / P + 1 : 0;
     TileRow<V, DRES> buf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load_tile_row<V, LN, DRES>(buf[d], a, stats, opaque_row(walker + d * P), col0, lane);
+        load_tile_row<E, V, LN, DRES, INROW>(buf[d], a, stats, opaque_row(walker + d * P), acc0,
+                                             lane);
         issue_fence();
     }
     for (int64_t i = 0; i < n; i += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int64_t r = opaque_row(walker + (i + d) * P);
-            tile_row<V, LN, DRES>(buf[d], wv, pw, pb, a, r, col0, lane);
+            tile_row<E, V, LN, DRES, INROW>(buf[d], wv, pw, pb, a, r, acc0, lane,
+                                            red + parity * 2 * (T / kWave));
+            parity ^= 1;
             issue_fence();
-            load_tile_row<V, LN, DRES>(buf[d], a, stats, r + D * P, col0, lane);
+            load_tile_row<E, V, LN, DRES, INROW>(buf[d], a, stats, r + D * P, acc0, lane);
             issue_fence();
         }
     }
@@ -389,17 +528,18 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(DynBw
                                                         LN ? padded * 4 : 0, kRsrcWord3);
 #pragma unroll
     for (int b = 0; b < V; ++b) {
-        const int off = (col0 + (b * T + lane) * 8) * 4;
-        const f32x4 w0 = {pw[b][0], pw[b][1], pw[b][2], pw[b][3]};
-        const f32x4 w1 = {pw[b][4], pw[b][5], pw[b][6], pw[b][7]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w0), sw, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w1), sw, off + 16, 0, 0);
-        if constexpr (LN) {
-            const f32x4 b0 = {pb[b][0], pb[b][1], pb[b][2], pb[b][3]};
-            const f32x4 b1 = {pb[b][4], pb[b][5], pb[b][6], pb[b][7]};
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b0), sb, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b1), sb, off + 16, 0,
-                                                   0);
+        const int off = (acc0 + b * T + lane) * EP * 4;  // byte offset of the access's first column
+#pragma unroll
+        for (int q = 0; q < EP / 4; ++q) {
+            const f32x4 w4 = {pw[b][4 * q], pw[b][4 * q + 1], pw[b][4 * q + 2], pw[b][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w4), sw,
+                                                   off + 16 * q, 0, 0);
+            if constexpr (LN) {
+                const f32x4 b4 = {pb[b][4 * q], pb[b][4 * q + 1], pb[b][4 * q + 2],
+                                  pb[b][4 * q + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b4), sb,
+                                                       off + 16 * q, 0, 0);
+            }
         }
     }
 }

@@ -184,21 +184,39 @@ const std::vector<SplitEntry>& split_table();
 // ---- streamed rows (wider than registers and LDS hold; kernels_stream.hpp) ------
 // Forward: 1024-lane workgroups walk the rows, each row read twice.  Backward:
 // a 1024-lane per-row reduction kernel, then 512-lane workgroups over tiles of
-// kStreamTileVecs * 8 * 512 columns.  16-byte accesses only.
+// kStreamTileVecs * 512 16-byte accesses (16384 bf16 or 8192 fp32 columns).
+// 16-byte accesses only.  The same kernels run fp32 activations (the `_f32`
+// entry points) at every width; the DynFwdArgs / DynBwdArgs pointers then
+// point at fp32 matrices and vectors, row strides in fp32 elements.
 constexpr int kStreamFwdLanes = 1024;
 constexpr int kStreamTileLanes = 512;
 constexpr int kStreamTileVecs = 4;
-constexpr int kStreamTileCols = kStreamTileLanes * kStreamTileVecs * 8;  // 16384
+constexpr int kStreamTileCols = kStreamTileLanes * kStreamTileVecs * 8;  // bf16 columns: 16384
+constexpr int kStreamTileColsF32 = kStreamTileLanes * kStreamTileVecs * 4;  // fp32: 8192
 constexpr int64_t kStreamMaxGrid = 65536;  // workgroups of the row-walking kernels
 constexpr int64_t kStreamMaxHidden = int64_t(1) << 20;
 
+// fp32 forward: lanes a row so that 4 accesses a lane hold it (64 .. 1024; a
+// row of up to 16384 values is then read once).
+constexpr int stream_fwd_lanes_f32(int64_t hidden) {
+    return hidden <= 1024 ? 64 : hidden <= 2048 ? 128 : hidden <= 4096 ? 256
+           : hidden <= 8192 ? 512 : kStreamFwdLanes;
+}
+// fp32 backward with one tile (hidden <= kStreamTileColsF32): accesses a lane
+// of the 512-lane tile that hold the row (1, 2 or 4).
+constexpr int stream_inrow_vecs_f32(int64_t hidden) {
+    return hidden <= 2048 ? 1 : hidden <= 4096 ? 2 : 4;
+}
+
 // op: kSplitFused / kSplitRms / kSplitLn (the row-split numbering)
-hipError_t launch_stream_fwd(int op, const DynFwdArgs& a, hipStream_t stream);
+hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t stream);
 // Stats kernel, tile kernel and column reduce.  ln: LayerNorm, else RMSNorm
 // (with a.dres: the fused op).  The workspace holds `walkers` slabs of
-// [outs][padded] fp32, then two fp32 per row.
-hipError_t launch_stream_bwd(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t walkers,
-                             hipStream_t stream);
+// [outs][padded] fp32, then two fp32 per row.  fp32 rows of one tile skip the
+// stats kernel (the tile kernel reduces each row itself; the per-row floats
+// stay unused).
+hipError_t launch_stream_bwd(bool ln, bool f32, const DynBwdArgs& a, int32_t tiles,
+                             int32_t walkers, hipStream_t stream);
 
 // Workgroup size of the run-time path for T lanes per row: rows narrower than
 // 256 lanes are packed 256 / T to a workgroup.

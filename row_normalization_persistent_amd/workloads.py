@@ -18,7 +18,9 @@ a fixed order, then bf16 rounding):
   w ~ N(1, 0.1); dres ~ N(0, 1) (gradient of the fused op's residual output);
   eps = fp32(1e-6)
 
-``N(m, s)`` means mean m and standard deviation s.
+``N(m, s)`` means mean m and standard deviation s.  With ``f32=True`` a
+generator returns the same fp32 draws without the bf16 rounding (the inputs of
+the fp32-activation entry points).
 """
 from __future__ import annotations
 
@@ -47,17 +49,23 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def _keep_f32(a: np.ndarray) -> np.ndarray:
+    """The fp32 draws themselves (the generators' ``f32=True``)."""
+    return np.ascontiguousarray(a, dtype=np.float32).copy()
+
+
 def _normal(rng: np.random.Generator, shape, mean: float, std: float) -> np.ndarray:
     z = rng.standard_normal(shape, dtype=np.float32)
     return z * np.float32(std) + np.float32(mean)
 
 
-def fused_inputs(rows: int, hidden: int = FUSED_HIDDEN, seed: int = 0) -> dict:
+def fused_inputs(rows: int, hidden: int = FUSED_HIDDEN, seed: int = 0, f32: bool = False) -> dict:
+    q = _keep_f32 if f32 else bf16_bits
     rng = np.random.default_rng(seed)
     x = _normal(rng, (rows, hidden), 0.0, 1.0)
     r = _normal(rng, (rows, hidden), 0.0, 1.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
-    return {"x": bf16_bits(x), "r": bf16_bits(r), "w": bf16_bits(w), "eps": EPS_RMS}
+    return {"x": q(x), "r": q(r), "w": q(w), "eps": EPS_RMS}
 
 
 def outlier_columns(hidden: int, seed: int = 0) -> np.ndarray:
@@ -66,38 +74,42 @@ def outlier_columns(hidden: int, seed: int = 0) -> np.ndarray:
     return np.sort(rng.permutation(hidden)[:k])
 
 
-def rmsnorm_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
+def rmsnorm_inputs(rows: int, hidden: int, seed: int = 0, f32: bool = False) -> dict:
+    q = _keep_f32 if f32 else bf16_bits
     rng = np.random.default_rng(seed)
     x = _normal(rng, (rows, hidden), 0.0, 1.0)
     cols = outlier_columns(hidden, seed)
     x[:, cols] *= np.float32(50.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
-    return {"x": bf16_bits(x), "w": bf16_bits(w), "eps": EPS_RMS, "outlier_cols": cols}
+    return {"x": q(x), "w": q(w), "eps": EPS_RMS, "outlier_cols": cols}
 
 
-def layernorm_fwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
+def layernorm_fwd_inputs(rows: int, hidden: int, seed: int = 0, f32: bool = False) -> dict:
+    q = _keep_f32 if f32 else bf16_bits
     rng = np.random.default_rng(seed)
     x = _normal(rng, (rows, hidden), 0.5, 2.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
     b = _normal(rng, (hidden,), 0.0, 0.1)
-    return {"x": bf16_bits(x), "w": bf16_bits(w), "b": bf16_bits(b), "eps": EPS_LN}
+    return {"x": q(x), "w": q(w), "b": q(b), "eps": EPS_LN}
 
 
-def layernorm_bwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
+def layernorm_bwd_inputs(rows: int, hidden: int, seed: int = 0, f32: bool = False) -> dict:
+    q = _keep_f32 if f32 else bf16_bits
     rng = np.random.default_rng(seed)
     x = _normal(rng, (rows, hidden), 0.0, 1.0)
     dy = _normal(rng, (rows, hidden), 0.0, 1.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
-    return {"x": bf16_bits(x), "dy": bf16_bits(dy), "w": bf16_bits(w), "eps": EPS_LN}
+    return {"x": q(x), "dy": q(dy), "w": q(w), "eps": EPS_LN}
 
 
-def rmsnorm_bwd_inputs(rows: int, hidden: int, seed: int = 0) -> dict:
+def rmsnorm_bwd_inputs(rows: int, hidden: int, seed: int = 0, f32: bool = False) -> dict:
+    q = _keep_f32 if f32 else bf16_bits
     rng = np.random.default_rng(seed)
     x = _normal(rng, (rows, hidden), 0.0, 1.0)
     dy = _normal(rng, (rows, hidden), 0.0, 1.0)
     w = _normal(rng, (hidden,), 1.0, 0.1)
     dres = _normal(rng, (rows, hidden), 0.0, 1.0)
-    return {"x": bf16_bits(x), "dy": bf16_bits(dy), "w": bf16_bits(w), "dres": bf16_bits(dres),
+    return {"x": q(x), "dy": q(dy), "w": q(w), "dres": q(dres),
             "eps": EPS_RMS}
 
 

@@ -19,6 +19,23 @@
 * fp32 column sums (dweight, dbias): |gpu - ref| <= 1e-3 |ref| + 1e-3 sqrt(sum_i t_i^2),
   t the summed terms (dy * xhat or dy): relative 1e-3, with the column's RMS
   scale as the absolute floor for columns that cancel to near zero.
+* fp32 activations (the `_f32` entry points), from the arithmetic: every
+  output is a short formula over the row's fp32 sums, so its error is the
+  sums' relative error times the magnitude M of the terms it combines, plus a
+  few roundings.  The longest sequential fp32 sum one lane forms in a row
+  reduction is n(H) = max(16, 4 ceil(H / 4096)) values: a row of up to 16384
+  values is held by as many lanes as give each lane at most 4 16-byte accesses
+  (4 values each), a wider one by 1024 lanes; the lanes then meet in a tree of
+  at most 16 levels.  Bound:
+  |gpu - ref| <= (n(H) + 64) 2^-24 M, 64 covering the tree, the output
+  formula's roundings, the hardware rsqrt (1 ulp) and the rounding of
+  x + r to fp32 (the oracle normalizes the exact sum).  M: |ref| for the
+  pure products (fused and RMSNorm out), the cancellation scales below for
+  LayerNorm y and the dx of every backward, mean_j |x| for the LayerNorm mean,
+  rstd itself for rstd.  Column sums over rows: each of the P row walkers sums
+  ceil(rows / P) terms in order, then the walkers meet in a fixed pairwise
+  tree, and each term carries its row's statistic error:
+  |gpu - ref| <= (ceil(rows / P) + n(H) + 64) 2^-24 sum_i |t_i|.
 """
 from __future__ import annotations
 
@@ -145,3 +162,43 @@ def rmsnorm_dx_scale(xd, dyd, wd, rstd, dresd=None):
     if dresd is not None:
         m = m + np.abs(dresd)
     return m
+
+
+U32 = 2.0 ** -24
+
+
+def f32_seq(hidden: int) -> int:
+    """n(H): the longest sequential fp32 sum one lane of a row reduction forms."""
+    return max(16, 4 * -(-hidden // 4096))
+
+
+def assert_f32_scaled(got, ref, scale, hidden: int, what: str) -> float:
+    """|gpu - ref| <= (n(H) + 64) 2^-24 M; returns the largest err / (2^-24 M)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, what
+    m = np.broadcast_to(np.asarray(scale, np.float64), ref.shape)
+    err = np.abs(got - ref)
+    lim = (f32_seq(hidden) + 64) * U32 * m
+    bad = ~(err <= lim)
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside (n(H) + 64) "
+                             f"2^-24 M; first at {idx}: got {got[idx]!r} ref {ref[idx]!r} "
+                             f"(M {m[idx]!r})")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = np.where(m > 0, err / (U32 * m), 0.0)
+    return float(r.max()) if r.size else 0.0
+
+
+def assert_colsum_f32(got, ref, terms_abs_sum, rows: int, walkers: int, hidden: int,
+                      what: str) -> None:
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    lim = (-(-rows // walkers) + f32_seq(hidden) + 64) * U32 * np.asarray(terms_abs_sum)
+    bad = ~(err <= lim)
+    if bad.any():
+        j = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{what}: {int(bad.sum())} columns outside tolerance; first {j}: "
+                             f"{got[j]!r} vs {ref[j]!r} (limit {lim[j]!r})")
+

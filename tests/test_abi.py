@@ -33,7 +33,10 @@ def test_header_declares_the_four_operations():
             assert op[:-3] in names  # every strided variant has a plain form
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd"):
         assert op + "_split" in names  # the row-split forward
-    assert len(names) == 34
+    for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
+               "norm_layernorm_bwd", "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd"):
+        assert op + "_f32" in names  # fp32 activations
+    assert len(names) == 41
 
 
 def test_library_exports_every_declared_symbol():
@@ -648,6 +651,97 @@ def test_noalloc_validation():
                 rows=256, hidden=32768) == WORKSPACE
     assert rn.NOALLOC_SCRATCH_BYTES == 32 << 20
     assert rn.workspace_bytes(512, 16384) == rn.NOALLOC_SCRATCH_BYTES  # the largest that fits
+
+
+def test_f32_validation():
+    """The fp32 entry points: contiguous rows, hidden a multiple of 4 up to
+    2^20, 16-byte-aligned matrices and weight / bias vectors; every case here
+    returns before any HIP call."""
+    L = rn.lib()
+    fa = L.norm_fused_add_rmsnorm_f32
+
+    def fused(out=A, res=A + 4 * MB, x=A + 8 * MB, w=A + 12 * MB, rows=8, hidden=4096,
+              eps=1e-6):
+        return fa(out, res, x, w, rows, hidden, eps, None)
+
+    assert fused(rows=0) == SUCCESS             # nothing to launch
+    assert fused(rows=-1) == INVALID
+    assert fused(eps=float("nan")) == INVALID
+    assert fused(hidden=0) == UNSUPPORTED
+    assert fused(hidden=4098) == UNSUPPORTED    # not a multiple of 4
+    assert fused(hidden=2) == UNSUPPORTED
+    assert fused(hidden=(1 << 20) + 4) == UNSUPPORTED
+    assert fused(x=0) == INVALID
+    assert fused(res=0) == INVALID
+    assert fused(x=A + 8 * MB + 8) == MISALIGNED  # 8 bytes: fine for bf16, not here
+    assert fused(w=A + 12 * MB + 4) == MISALIGNED
+    assert fused(res=A + 8 * MB) == INVALID      # residual aliases x
+    assert fused(out=A + 12 * MB) == INVALID     # out overlaps the weight
+    assert fused(out=A + 8 * MB + 16) == INVALID  # out overlaps x without equalling it
+    rf = L.norm_rmsnorm_fwd_f32
+    assert rf(A, A + 4 * MB, A + 8 * MB, 8, 4102, 1e-6, None) == UNSUPPORTED
+    assert rf(A, A + 4 * MB, A + 8 * MB + 16, 8, 4096, -1.0, None) == INVALID
+    lf = L.norm_layernorm_fwd_f32
+    assert lf(A, A + 4 * MB, 0, A + 8 * MB, A + 12 * MB, A + 13 * MB, 8, 4096, 1e-5,
+              None) == INVALID                   # mean without rstd
+    assert lf(A, A + 4 * MB, A + 4 * MB + 16, A + 8 * MB, A + 12 * MB, A + 13 * MB + 8, 8,
+              4096, 1e-5, None) == MISALIGNED    # bias
+    assert lf(A, A + 4 * MB, A + 4 * MB + 16, A + 8 * MB, A + 12 * MB, A + 13 * MB, 8, 4096,
+              1e-5, None) == INVALID             # rstd overlaps mean (8 rows = 32 bytes)
+    assert lf(A, A + 4 * MB + 2, A + 5 * MB, A + 8 * MB, A + 12 * MB, A + 13 * MB, 8, 4096,
+              1e-5, None) == MISALIGNED          # mean 4-byte
+
+    lb = L.norm_layernorm_bwd_f32
+    WS = A + 64 * MB  # apart from every other argument below
+    ws_need = rn.workspace_bytes_f32("layernorm_bwd", 8, 4096)
+
+    def lbwd(dx=A, dw=A + 4 * MB, db=A + 5 * MB, dy=A + 8 * MB, x=A + 12 * MB, m=A + 16 * MB,
+             r=A + 17 * MB, w=A + 18 * MB, ws=WS, ws_bytes=1 << 20, rows=8, hidden=4096):
+        return lb(dx, dw, db, dy, x, m, r, w, ws, ws_bytes, rows, hidden, 0.0, None)
+
+    assert lbwd(rows=-1) == INVALID
+    assert lbwd(hidden=4094) == UNSUPPORTED
+    assert lbwd(ws=0) == INVALID
+    assert lbwd(db=0) == INVALID
+    assert lbwd(m=0) == INVALID
+    assert lbwd(dy=A + 8 * MB + 4) == MISALIGNED
+    assert lbwd(ws=WS + 8) == MISALIGNED
+    assert lbwd(dw=A + 4 * MB + 2) == MISALIGNED
+    assert lbwd(dx=A + 8 * MB + 16) == INVALID   # dx overlaps dy without equalling it
+    assert lbwd(dw=A + 16 * MB) == INVALID       # dweight aliases mean
+    assert lbwd(ws=A + 12 * MB) == INVALID       # workspace inside x
+    assert lbwd(ws_bytes=ws_need - 1) == WORKSPACE
+    rb = L.norm_rmsnorm_bwd_f32
+    assert rb(A, A + 4 * MB, A + 8 * MB, A + 12 * MB, A + 16 * MB, WS, 16, 8, 4096, 1e-6,
+              None) == WORKSPACE
+    assert rb(A, A + 4 * MB, A + 8 * MB, A + 12 * MB, A + 16 * MB + 8, WS, 1 << 20, 8, 4096,
+              1e-6, None) == MISALIGNED          # weight
+    fb = L.norm_fused_add_rmsnorm_bwd_f32
+    assert fb(A, A + 4 * MB, A + 8 * MB, A + 12 * MB + 4, A + 16 * MB, A + 20 * MB, WS,
+              1 << 20, 8, 4096, 1e-6, None) == MISALIGNED  # dres
+    assert fb(A + 12 * MB, A + 4 * MB, A + 8 * MB, A + 12 * MB, A + 16 * MB, A + 20 * MB, WS,
+              16, 8, 4096, 1e-6, None) == WORKSPACE  # ds == dres is allowed
+    assert fb(A + 16 * MB, A + 4 * MB, A + 8 * MB, None, A + 16 * MB, A + 20 * MB, WS,
+              1 << 20, 8, 4096, 1e-6, None) == INVALID   # ds aliases s
+
+
+def test_f32_workspace_sizes():
+    """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
+    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers),
+    plus 8 bytes a row."""
+    ws = rn.workspace_bytes_f32
+    pad = lambda h: -(-h // 64) * 64
+    assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4 + 8192 * 8
+    assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4 + 8192 * 8
+    assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4 + 3 * 8
+    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1000 * 8  # 128 tiles
+    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 1000 * 8  # 3 tiles
+    assert ws("layernorm_bwd", 0, 4096) == 0
+    assert ws("layernorm_bwd", 8, 4098) == 0
+    assert ws("layernorm_fwd", 8, 4096) == 0      # a forward op
+    # the largest any call needs stays under 32 MiB
+    assert max(ws("layernorm_bwd", 1 << 20, h) for h in (4096, 8192, 8196, 65536, 1 << 20)) \
+        < 32 << 20
 
 
 def test_wide_backward_host_logic():
