@@ -472,6 +472,7 @@ def other_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
         x0 = wl.to_device_bf16(i["x"], dev)
         w = wl.to_device_bf16(i["w"], dev)
         zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()  # inputs written on the current stream, used on `stream`
         _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
         dy0 = wl.to_device_bf16(i["dy"], dev)
         xs = [x0] + [x0.clone() for _ in range(n - 1)]
@@ -938,6 +939,7 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
         x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
         w = wl.to_device_bf16(i["w"], dev)
         zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()  # inputs written on the current stream, used on `stream`
         _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
         xs = [x0] + [x0.clone() for _ in range(n - 1)]
         dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
@@ -1010,6 +1012,7 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
     x0, dy0 = wl.to_device_bf16(i["x"], dev), wl.to_device_bf16(i["dy"], dev)
     w = wl.to_device_bf16(i["w"], dev)
     zb = torch.zeros(h, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()  # inputs written on the current stream, used on `stream`
     _, mean, rstd = rn.layernorm_fwd(x0, w, zb, i["eps"], stream=stream)
     xs = [x0] + [x0.clone() for _ in range(n - 1)]
     dys = [dy0] + [dy0.clone() for _ in range(n - 1)]
@@ -1091,6 +1094,7 @@ def f32_ops(torch, rn, wl, dev, stream, reps):
     xs, dys, drs = sets(f(i["x"]), n), sets(f(i["dy"]), n), sets(f(i["dres"]), n)
     dxs = [torch.empty_like(xs[0]) for _ in range(n)]
     w = f(i["w"])
+    torch.cuda.synchronize()  # inputs written on the current stream, used on `stream`
     _, mean, rstd = rn.layernorm_fwd_f32(xs[0], w, torch.zeros_like(w), wl.EPS_LN, stream=stream)
     dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
     ws = torch.empty(rn.workspace_bytes_f32("layernorm_bwd", rows, h), dtype=torch.uint8,

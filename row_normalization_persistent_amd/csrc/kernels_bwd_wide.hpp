@@ -49,6 +49,43 @@ __device__ __forceinline__ void wait_all_counters() {
     asm volatile("s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)" ::: "memory");
 }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// At most N vector-memory operations of this wave still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until access b's x and dy have landed, `later` = V - 1 - b accesses
+// (two loads each) having been issued after it (a constant once the caller's
+// loop over b is unrolled: one wait instruction).
+__device__ __forceinline__ void wait_access_landed(int later) {
+    switch (later) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<2>(); break;
+        case 2: wait_vm<4>(); break;
+        case 3: wait_vm<6>(); break;
+        case 4: wait_vm<8>(); break;
+        case 5: wait_vm<10>(); break;
+        case 6: wait_vm<12>(); break;
+        default: wait_vm<14>(); break;
+    }
+}
+
+// The first pass over a row starts on access b as soon as b's two loads have
+// landed instead of after the whole row (build-time switch for measurement).
+#ifndef ROWNORM_WIDE_STAGED
+#define ROWNORM_WIDE_STAGED 1
+#endif
+
+// p[i] through the scalar data cache (a wave-uniform index into a read-only
+// input of the kernel, so the load is a scalar one and no vector-memory wait
+// ever waits for it), or 0 for i >= n.
+__device__ __forceinline__ float uniform_load_f32(const float* p, int64_t i, int64_t n) {
+    const __attribute__((address_space(4))) float* q =
+        (const __attribute__((address_space(4))) float*)p;
+    return i < n ? q[i] : 0.0f;
+}
 
 // A row's buffer descriptor as four scalar words: base address (48 bits, no
 // stride), size in bytes (0 past the matrix's last row), format word.
@@ -147,8 +184,8 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
 #pragma unroll
         for (int b = 0; b < V; ++b) stage(rx, rd, b, lane);
         if constexpr (LN) {
-            mean_nx = rload_f32(row_rsrc_ld(a.mean, first, a.rows, 4, 4), 0);
-            rstd_nx = rload_f32(row_rsrc_ld(a.rstd, first, a.rows, 4, 4), 0);
+            mean_nx = uniform_load_f32(a.mean, first, a.rows);
+            rstd_nx = uniform_load_f32(a.rstd, first, a.rows);
         }
     }
     int parity = 0;
@@ -156,8 +193,15 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         const int64_t row = opaque_row(first + i * G);
         const int64_t next = row + G;  // past the end (size-0 descriptors) after the last
         const float mean = mean_nx, rstd_in = rstd_nx;
-        // the row's loads (its LDS writes included); no LDS read may move above
-        wait_all_counters();
+        // the row's loads (its LDS writes included); no LDS read may move above.
+        // Staged: access b is read once b's x and dy have landed.  The row's
+        // loads went out in access order (x then dy of access b, then this
+        // wave's dx store of the previous row's access b), so at most 2 (V - 1
+        // - b) operations after b's dy are loads; vector-memory operations
+        // retire in issue order, so once no more than that many are
+        // outstanding, b's two loads have landed whether or not the stores are
+        // counted.
+        if constexpr (!ROWNORM_WIDE_STAGED) wait_all_counters();
         // lane offsets recomputed every row (an opaque lane index), not hoisted
         // out of the loop into registers held for the whole walk
         const int l = opaque_lane(lane);
@@ -168,6 +212,7 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int b = 0; b < V; ++b) {
+            if constexpr (ROWNORM_WIDE_STAGED) wait_access_landed(V - 1 - b);
             const bool in_row = (b * T + l) * 8 < h;
             float xf[8], df[8], wf[8];
             unpack8(xs[b * T + l], xf);
@@ -194,8 +239,8 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         row_sum2<T>(s1, s2, red + parity * (2 * (T / kWave)), lane);
         parity ^= 1;
         if constexpr (LN) {  // past the walk's last row: zeros, never used
-            mean_nx = rload_f32(row_rsrc_ld(a.mean, next, a.rows, 4, 4), 0);
-            rstd_nx = rload_f32(row_rsrc_ld(a.rstd, next, a.rows, 4, 4), 0);
+            mean_nx = uniform_load_f32(a.mean, next, a.rows);
+            rstd_nx = uniform_load_f32(a.rstd, next, a.rows);
         }
         // the second pass re-reads x, dy (LDS) and the weights (registers)
         // instead of keeping the first pass's values live across the
