@@ -12,24 +12,45 @@ namespace rownorm {
 template <bool LN, bool DRES>
 constexpr int tile_depth() { return DRES ? 2 : 3; }
 
-template <typename E, int T>
-hipError_t fwd_by_op(int op, const DynFwdArgs& a, hipStream_t stream) {
-    switch (op) {
-        case kSplitFused: return launch_stream_fwd_op<E, kSplitFused, T>(a, stream);
-        case kSplitRms: return launch_stream_fwd_op<E, kSplitRms, T>(a, stream);
-        case kSplitLn: return launch_stream_fwd_op<E, kSplitLn, T>(a, stream);
-        default: return hipErrorInvalidValue;
+// Only the shapes stream_fwd_shape picks are instantiated.
+template <int OP>
+hipError_t fwd_f32_rms(const StreamFwdShape& sh, const DynFwdArgs& a, hipStream_t stream) {
+    switch (sh.lanes * 100 + sh.unroll) {
+        case 6404: return launch_stream_fwd_op<float, OP, 64, 4>(a, stream);
+        case 12804: return launch_stream_fwd_op<float, OP, 128, 4>(a, stream);
+        case 25604: return launch_stream_fwd_op<float, OP, 256, 4>(a, stream);
+        case 51204: return launch_stream_fwd_op<float, OP, 512, 4>(a, stream);
+        case 102404: return launch_stream_fwd_op<float, OP, 1024, 4>(a, stream);
+        default: return launch_stream_fwd_op<float, OP, 1024, 8>(a, stream);
+    }
+}
+
+hipError_t fwd_f32_ln(const StreamFwdShape& sh, const DynFwdArgs& a, hipStream_t stream) {
+    switch (sh.lanes * 100 + sh.unroll) {
+        case 6404: return launch_stream_fwd_op<float, kSplitLn, 64, 4>(a, stream);
+        case 6408: return launch_stream_fwd_op<float, kSplitLn, 64, 8>(a, stream);
+        case 12808: return launch_stream_fwd_op<float, kSplitLn, 128, 8>(a, stream);
+        case 25608: return launch_stream_fwd_op<float, kSplitLn, 256, 8>(a, stream);
+        case 51208: return launch_stream_fwd_op<float, kSplitLn, 512, 8>(a, stream);
+        default: return launch_stream_fwd_op<float, kSplitLn, 1024, 4>(a, stream);
     }
 }
 
 hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t stream) {
-    if (!f32) return fwd_by_op<uint16_t, kStreamFwdLanes>(op, a, stream);
-    switch (stream_fwd_lanes_f32(a.hidden)) {
-        case 64: return fwd_by_op<float, 64>(op, a, stream);
-        case 128: return fwd_by_op<float, 128>(op, a, stream);
-        case 256: return fwd_by_op<float, 256>(op, a, stream);
-        case 512: return fwd_by_op<float, 512>(op, a, stream);
-        default: return fwd_by_op<float, kStreamFwdLanes>(op, a, stream);
+    const StreamFwdShape sh = stream_fwd_shape(f32, op == kSplitLn, op == kSplitRms, a.hidden);
+    switch (op) {
+        case kSplitFused:
+            return f32 ? fwd_f32_rms<kSplitFused>(sh, a, stream)
+                       : launch_stream_fwd_op<uint16_t, kSplitFused, kStreamFwdLanes, 4>(a, stream);
+        case kSplitRms:
+            if (f32) return fwd_f32_rms<kSplitRms>(sh, a, stream);
+            return sh.unroll == 8
+                       ? launch_stream_fwd_op<uint16_t, kSplitRms, kStreamFwdLanes, 8>(a, stream)
+                       : launch_stream_fwd_op<uint16_t, kSplitRms, kStreamFwdLanes, 4>(a, stream);
+        case kSplitLn:
+            return f32 ? fwd_f32_ln(sh, a, stream)
+                       : launch_stream_fwd_op<uint16_t, kSplitLn, kStreamFwdLanes, 4>(a, stream);
+        default: return hipErrorInvalidValue;
     }
 }
 

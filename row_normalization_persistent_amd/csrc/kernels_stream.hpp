@@ -190,9 +190,8 @@ __device__ __forceinline__ void stream_norm_step(const u32x4 (&xv)[U],
     }
 }
 
-template <typename E, int OP, int T>
+template <typename E, int OP, int T, int U = kStreamUnroll>
 __global__ __launch_bounds__(T) void stream_fwd_kernel(DynFwdArgs a) {
-    constexpr int U = kStreamUnroll;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     constexpr bool kFused = OP == kSplitFused, kLn = OP == kSplitLn;
@@ -262,10 +261,10 @@ __global__ __launch_bounds__(T) void stream_fwd_kernel(DynFwdArgs a) {
     }
 }
 
-template <typename E, int OP, int T>
+template <typename E, int OP, int T, int U = kStreamUnroll>
 hipError_t launch_stream_fwd_op(const DynFwdArgs& a, hipStream_t stream) {
     const int64_t grid = a.rows < kStreamMaxGrid ? a.rows : kStreamMaxGrid;
-    hipLaunchKernelGGL((stream_fwd_kernel<E, OP, T>), dim3((unsigned)grid), dim3(T), 0, stream,
+    hipLaunchKernelGGL((stream_fwd_kernel<E, OP, T, U>), dim3((unsigned)grid), dim3(T), 0, stream,
                        a);
     return hipGetLastError();
 }

@@ -196,11 +196,43 @@ constexpr int kStreamTileColsF32 = kStreamTileLanes * kStreamTileVecs * 4;  // f
 constexpr int64_t kStreamMaxGrid = 65536;  // workgroups of the row-walking kernels
 constexpr int64_t kStreamMaxHidden = int64_t(1) << 20;
 
-// fp32 forward: lanes a row so that 4 accesses a lane hold it (64 .. 1024; a
-// row of up to 16384 values is then read once).
-constexpr int stream_fwd_lanes_f32(int64_t hidden) {
-    return hidden <= 1024 ? 64 : hidden <= 2048 ? 128 : hidden <= 4096 ? 256
-           : hidden <= 8192 ? 512 : kStreamFwdLanes;
+// Streamed forward launch shape: lanes a row and 16-byte accesses a lane
+// kept in registers from the statistic pass to the normalize pass (a row of
+// up to lanes x unroll accesses is read once, the rest twice).  Measured on
+// MI355X (graph-timed over cold buffers):
+//  * fp32 fused and RMSNorm: 64 .. 1024 lanes x 4 accesses up to 16384
+//    columns, 1024 x 8 beyond (2048 x 32768: fused 202 -> 190 us, RMSNorm
+//    97 -> 93 us; 1024 x 65536 4-5 % faster; 256 x 262144 even);
+//  * fp32 LayerNorm, whose two reductions cost a barrier each: half the lanes
+//    with 8 accesses from 1025 to 16384 columns (2048 x 16384 57.3 -> 51.6 us,
+//    2048 x 4096 16.3 -> 14.9 us; 4096 x 8192, 8192 x 4096, 16384 x 2048
+//    0.5-1.5 % faster, 8192 x 1536 1 % slower), 1024 x 4 beyond (8 accesses
+//    were 0-4 % slower there);
+//  * bf16 (rows past the on-chip kernels): 1024 x 4; RMSNorm 1024 x 8 up to
+//    73728 columns, where 8 accesses hold nearly the whole row (4096 x 65544
+//    214 -> 202 us; at 131072 and 262144 columns 1-6 % slower); the fused and
+//    LayerNorm forms spill at 8.
+#ifndef ROWNORM_STREAM_U8
+#define ROWNORM_STREAM_U8 1  // build-time switch for measurement: 0 = never 8 accesses past 16384 fp32 columns
+#endif
+struct StreamFwdShape {
+    int lanes, unroll;
+};
+constexpr StreamFwdShape stream_fwd_shape(bool f32, bool ln, bool rms, int64_t hidden) {
+    if (!f32) return {kStreamFwdLanes, rms && ROWNORM_STREAM_U8 && hidden <= 73728 ? 8 : 4};
+    if (hidden <= 1024) return {64, 4};
+    if (ln) {
+        if (hidden <= 2048) return {64, 8};
+        if (hidden <= 4096) return {128, 8};
+        if (hidden <= 8192) return {256, 8};
+        if (hidden <= 16384) return {512, 8};
+        return {kStreamFwdLanes, 4};
+    }
+    if (hidden <= 2048) return {128, 4};
+    if (hidden <= 4096) return {256, 4};
+    if (hidden <= 8192) return {512, 4};
+    if (hidden <= 16384) return {kStreamFwdLanes, 4};
+    return {kStreamFwdLanes, ROWNORM_STREAM_U8 ? 8 : 4};
 }
 // fp32 backward with one tile (hidden <= kStreamTileColsF32): accesses a lane
 // of the 512-lane tile that hold the row (1, 2 or 4).

@@ -23,9 +23,9 @@
   output is a short formula over the row's fp32 sums, so its error is the
   sums' relative error times the magnitude M of the terms it combines, plus a
   few roundings.  The longest sequential fp32 sum one lane forms in a row
-  reduction is n(H) = max(16, 4 ceil(H / 4096)) values: a row of up to 16384
-  values is held by as many lanes as give each lane at most 4 16-byte accesses
-  (4 values each), a wider one by 1024 lanes; the lanes then meet in a tree of
+  reduction is n(H) = max(32, 4 ceil(H / 4096)) values: up to 32768 columns
+  the launch shapes give a lane at most 8 16-byte accesses of a row (4 values
+  each), a wider row is walked by 1024 lanes; the lanes then meet in a tree of
   at most 16 levels.  Bound:
   |gpu - ref| <= (n(H) + 64) 2^-24 M, 64 covering the tree, the output
   formula's roundings, the hardware rsqrt (1 ulp) and the rounding of
@@ -169,7 +169,7 @@ U32 = 2.0 ** -24
 
 def f32_seq(hidden: int) -> int:
     """n(H): the longest sequential fp32 sum one lane of a row reduction forms."""
-    return max(16, 4 * -(-hidden // 4096))
+    return max(32, 4 * -(-hidden // 4096))
 
 
 def assert_f32_scaled(got, ref, scale, hidden: int, what: str) -> float:

@@ -41,8 +41,10 @@ def walkers(rows, h):
 
 
 # ------------------------------------------------------------------ forward
-FWD_SHAPES = [(4, 1), (12, 37), (1024, 300), (4096, 64), (4100, 37), (16384, 9), (16388, 5),
-              (65536, 17), (100004, 3), (1 << 20, 2)]
+# one shape per launch-shape bucket of the fp32 forward (lanes x accesses held:
+# up to 1024, 2048, 4096, 8192, 16384 columns, then 1024 lanes x 8 / x 4)
+FWD_SHAPES = [(4, 1), (12, 37), (1024, 300), (2048, 45), (4096, 64), (4100, 37), (8192, 11),
+              (16384, 9), (16388, 5), (32768, 7), (65536, 17), (100004, 3), (1 << 20, 2)]
 
 
 def check_fused(inp, out, res, h, what):
