@@ -1311,6 +1311,40 @@ OTHER_WORKLOADS = [
 ]
 
 
+# The streamed and fp32 kernels bench.py times (`streamed_ops`, `f32_ops`):
+# (op, rows, hidden, kernel in rocprofv3's spelling without spaces, algorithmic
+# bytes of that kernel: each matrix it reads or writes once, the vectors once,
+# the backward's per-row floats and partial-sum slabs not counted).
+STREAM_F32_WORKLOADS = [
+    ("fused_add_rmsnorm", 2048, 131072, "stream_fwd_kernel<unsignedshort,0,1024,4>",
+     lambda r, h: 8 * h * r + 2 * h),
+    ("layernorm_fwd", 2048, 65536, "stream_fwd_kernel<unsignedshort,2,1024,4>",
+     lambda r, h: (4 * h + 8) * r + 4 * h),
+    ("layernorm_bwd (row sums)", 4096, 65536, "stream_bwd_stats_kernel<unsignedshort,true>",
+     lambda r, h: (4 * h + 8) * r + 2 * h),
+    ("layernorm_bwd (column tiles)", 4096, 65536,
+     "stream_bwd_tile_kernel<unsignedshort,4,true,false,3,false>",
+     lambda r, h: (6 * h + 8) * r + 2 * h),
+    ("rmsnorm_bwd (row sums)", 4096, 65536, "stream_bwd_stats_kernel<unsignedshort,false>",
+     lambda r, h: 4 * h * r + 2 * h),
+    ("rmsnorm_bwd (column tiles)", 4096, 65536,
+     "stream_bwd_tile_kernel<unsignedshort,4,false,false,3,false>",
+     lambda r, h: 6 * h * r + 2 * h),
+    ("fused_add_rmsnorm_f32", 8192, 4096, "stream_fwd_kernel<float,0,256,4>",
+     lambda r, h: 16 * h * r + 4 * h),
+    ("rmsnorm_fwd_f32", 4096, 16384, "stream_fwd_kernel<float,1,1024,4>",
+     lambda r, h: 8 * h * r + 4 * h),
+    ("layernorm_fwd_f32", 2048, 16384, "stream_fwd_kernel<float,2,512,8>",
+     lambda r, h: (8 * h + 8) * r + 8 * h),
+    ("layernorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,true,false,4,true>",
+     lambda r, h: (12 * h + 8) * r + 4 * h),
+    ("rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,false,4,true>",
+     lambda r, h: 12 * h * r + 4 * h),
+    ("fused_add_rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,true,3,true>",
+     lambda r, h: 16 * h * r + 4 * h),
+]
+
+
 def _fwd_kernel_name(op, rows, hidden):
     """The forward kernel instantiation the library launches for (op, rows,
     hidden) on this device, in rocprofv3's spelling."""
@@ -1441,6 +1475,24 @@ def summarize_profiles(d: str, out_dir: str = PROFILES):
         alg = alg_fn(rows, h)
         lines.append(f"| {op} | {rows} x {h} | `{kname}` | {len(f_v)} | {rd / 2**20:.2f} | "
                      f"{wr / 2**20:.2f} | {alg / 2**20:.2f} | {(rd + wr) / alg:.4f} |")
+    stream_f32 = []
+    for op, rows, h, kname, alg_fn in STREAM_F32_WORKLOADS:
+        f_v, w_v = by_name.get(kname, ([], []))
+        if not f_v or not w_v:
+            continue
+        rd = float(np.mean(f_v)) * f_scale
+        wr = float(np.mean(w_v)) * w_scale
+        alg = alg_fn(rows, h)
+        stream_f32.append(f"| {op} | {rows} x {h} | `{kname}` | {len(f_v)} | {rd / 2**20:.2f} | "
+                          f"{wr / 2**20:.2f} | {alg / 2**20:.2f} | {(rd + wr) / alg:.4f} |")
+    if stream_f32:
+        lines += ["", "The streamed kernels (`streamed_ops`: rows past the on-chip kernels, each "
+                  "row read twice) and the fp32-activation kernels (`f32_ops`), algorithmic bytes "
+                  "counting each matrix once (a streamed row's second read shows as the excess "
+                  "when it misses the Infinity Cache):", "",
+                  "| op | rows x hidden | kernel | dispatches | read MiB | written MiB | "
+                  "algorithmic MiB | HBM / algorithmic |", "|---|---|---|---:|---:|---:|---:|---:|"]
+        lines += stream_f32
     # the streaming ceilings move known bytes (1 GiB per buffer): their scaled
     # counters check the calibration and the kernels' own traffic
     import re as _re
