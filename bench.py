@@ -683,7 +683,9 @@ def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
     graph's submission cost is spread as thinly as at the large points; those
     few MB stay cache-resident, which latency-bound launches barely notice),
     graph-timed per launch.  The kernel-level view of the sweep (no host
-    dispatch cost)."""
+    dispatch cost).  Each point also reports the same launch re-run on one
+    buffer set ("warm_mall": inputs resident in the Infinity Cache), as
+    context only."""
     out = []
     for i, rows in enumerate(SWEEP_ROWS):
         a, b = int(offs[i]), int(offs[i + 1])
@@ -700,6 +702,13 @@ def sweep_graph(torch, rn, dev, stream, s0, w, eps, offs, reps):
         rec = _op_rec("fused_add_rmsnorm", rows, HIDDEN, nb, t)
         rec["rows_per_s"] = round(rows / (t * 1e-6))
         rec["kernel"] = _fwd_kernel_name("fused_add_rmsnorm", rows, HIDDEN)
+        # warm (MALL): 16 launches on one buffer set, whose x, residual and out
+        # (at most 192 MiB) stay in the 256 MB Infinity Cache; context only,
+        # never the metric
+        tw = graph_time_per_launch(torch, stream, [fns[0]] * 16,
+                                   max(2, min(reps if nb > (16 << 20) else 10 * reps, 200)))
+        rec["warm_mall_us"] = round(tw, 3)
+        rec["warm_mall_GBps"] = round(nb / (tw * 1e-6) / 1e9, 1)
         c = rn.select_config("fused_add_rmsnorm", rows, HIDDEN)
         ceil = _ceiling_fn()
         if ceil is not None and rows >= 512 and c.vector_elems == 0:
