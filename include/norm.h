@@ -455,7 +455,8 @@ NORM_API norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden
                                int32_t cu_count, norm_launch_cfg* cfg);
 
 /* Human-readable description of the launch the library would make for
- * (op, rows, hidden) on a device with `cu_count` compute units (<= 0: the
+ * (op, rows, hidden) through the bf16 entry points (the `_f32` ones always
+ * run the streamed kernels) on a device with `cu_count` compute units (<= 0: the
  * current device): kernel instantiation, lanes per row, rows per workgroup,
  * 16-byte vectors per lane, workgroup size, grid, ring depth and workspace.
  * Writes a NUL-terminated string of at most `len` bytes to `buf` (which may be

@@ -1,5 +1,6 @@
 """GPU parity past 4 GiB per matrix: every kernel family's 64-bit row
-addressing (row offsets beyond 2^31 and 2^32 bytes), through the C ABI.
+addressing (row offsets beyond 2^31 and 2^32 bytes), through the C ABI,
+for bf16 and fp32 activations.
 
 The matrices are drawn on the device from seeded generators
 (workloads.device_normal_bf16); the oracle recomputes sampled rows: the first
@@ -84,9 +85,10 @@ def weight(hidden, seed, mean=1.0, std=0.1):
 def oracle_colsums(n_rows, chunk_fn, chunk=1 << 15):
     """Column sums over all rows from the oracle: chunk_fn(a, b) runs the
     oracle's backward on rows a..b (host copies) and returns, per output,
-    (its column sums, the column sums of the squared summed terms); both are
-    added over the chunks in fp64.  The squared terms scale the tolerance's
-    absolute part only."""
+    (its column sums, a per-column scale of the summed terms: their squares'
+    sums for the bf16 rule, their absolute values' sums for the fp32 one);
+    both are added over the chunks in fp64.  The scale enters the tolerance
+    only."""
     tot = None
     for k, a in enumerate(range(0, n_rows, chunk)):
         part = chunk_fn(a, min(n_rows, a + chunk))
@@ -364,5 +366,83 @@ def test_streamed_layernorm_bwd_past_4gib():
                           "streamed layernorm bwd past 4 GiB: dweight")
     P.assert_colsum_close(db.cpu().numpy(), db_ref, db_q,
                           "streamed layernorm bwd past 4 GiB: dbias")
+    del x, dy, dx, mean, rstd
+    free()
+
+
+# ------------------------------------------------------------- fp32 activations
+def device_normal_f32_rows(rows: int, hidden: int, mean: float, std: float,
+                           seed: int) -> torch.Tensor:
+    """A [rows, hidden] fp32 matrix ~ N(mean, std) drawn on the device."""
+    return wl.device_normal_f32(rows * hidden, mean, std, seed, DEV).view(rows, hidden)
+
+
+def take_f32(t: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    return t.index_select(0, torch.from_numpy(idx).to(t.device)).cpu().numpy()
+
+
+def test_f32_fused_add_rmsnorm_past_4gib():
+    """fp32 hidden 4096: x, residual, out of 4 GiB + 77 rows each."""
+    h = 4096
+    rows = GIB4 // (4 * h) + 77
+    idx = sample_rows(rows, 4 * h, seed=11)
+    x = device_normal_f32_rows(rows, h, 0.0, 1.0, seed=1101)
+    r = device_normal_f32_rows(rows, h, 0.0, 1.0, seed=1102)
+    w = wl.device_normal_f32(h, 1.0, 0.1, 1103, DEV)
+    xs, rs = take_f32(x, idx), take_f32(r, idx)
+    out = nan_like(x)
+    rn.fused_add_rmsnorm_f32(x, r, w, wl.EPS_RMS, out=out)
+    torch.cuda.synchronize()
+    ref, res_ref, _ = oracle.fused_add_rmsnorm_f32(xs, rs, w.cpu().numpy(), wl.EPS_RMS, NT)
+    assert np.array_equal(take_f32(r, idx).view(np.uint32), res_ref.view(np.uint32)), \
+        "fp32 fused past 4 GiB: residual"
+    P.assert_f32_scaled(take_f32(out, idx), ref, np.abs(ref), h, "fp32 fused past 4 GiB: out")
+    assert_all_finite(out, "fp32 fused past 4 GiB: out")
+    del x, r, out
+    free()
+
+
+def test_f32_layernorm_bwd_past_4gib():
+    """fp32 hidden 4096: x, dy, dx of 4 GiB + 77 rows (one-tile rows reduced
+    in the tile kernel); mean and rstd drawn (inputs used as given)."""
+    h = 4096
+    rows = GIB4 // (4 * h) + 77
+    idx = sample_rows(rows, 4 * h, seed=12)
+    x = device_normal_f32_rows(rows, h, 0.0, 1.0, seed=1201)
+    dy = device_normal_f32_rows(rows, h, 0.0, 1.0, seed=1202)
+    mean = wl.device_normal_f32(rows, 0.0, 0.02, 1203, DEV)
+    rstd = wl.device_normal_f32(rows, 1.0, 0.05, 1204, DEV)
+    w = wl.device_normal_f32(h, 1.0, 0.1, 1205, DEV)
+    w_h = w.cpu().numpy()
+    dx = nan_like(x)
+    dw = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    db = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    rn.layernorm_bwd_f32(dy, x, mean, rstd, w, dx=dx, dweight=dw, dbias=db)
+    torch.cuda.synchronize()
+    ti = torch.from_numpy(idx).to(DEV)
+    xs, dys = take_f32(x, idx), take_f32(dy, idx)
+    ms, rs = mean[ti].cpu().numpy(), rstd[ti].cpu().numpy()
+    dx_ref, _, _ = oracle.layernorm_bwd_f32(dys, xs, ms, rs, w_h, NT)
+    scale = P.layernorm_dx_scale(xs.astype(np.float64), dys.astype(np.float64),
+                                 w_h.astype(np.float64), ms.astype(np.float64),
+                                 rs.astype(np.float64))
+    P.assert_f32_scaled(take_f32(dx, idx), dx_ref, scale, h, "fp32 layernorm bwd past 4 GiB: dx")
+    assert_all_finite(dx, "fp32 layernorm bwd past 4 GiB: dx")
+
+    def chunk(a, b):
+        xc, dyc = x[a:b].cpu().numpy(), dy[a:b].cpu().numpy()
+        mc, rc = mean[a:b].cpu().numpy(), rstd[a:b].cpu().numpy()
+        _, cdw, cdb = oracle.layernorm_bwd_f32(dyc, xc, mc, rc, w_h, NT)
+        dyt = torch.from_numpy(dyc).double()
+        xhat = (torch.from_numpy(xc).double() - torch.from_numpy(mc).double()[:, None]) * \
+            torch.from_numpy(rc).double()[:, None]
+        return [(cdw, (dyt * xhat).abs().sum(0).numpy()), (cdb, dyt.abs().sum(0).numpy())]
+
+    (dw_ref, dw_a), (db_ref, db_a) = oracle_colsums(rows, chunk)
+    p = max(1, min(rows, 255))  # row walkers of a one-tile fp32 row
+    P.assert_colsum_f32(dw.cpu().numpy(), dw_ref, dw_a, rows, p, h,
+                        "fp32 layernorm bwd past 4 GiB: dweight")
+    P.assert_colsum_f32(db.cpu().numpy(), db_ref, db_a, rows, p, h,
+                        "fp32 layernorm bwd past 4 GiB: dbias")
     del x, dy, dx, mean, rstd
     free()
