@@ -56,9 +56,9 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Waits until access b's x and dy have landed, `later` = V - 1 - b accesses
-// (two loads each) having been issued after it (a constant once the caller's
-// loop over b is unrolled: one wait instruction).
+// Waits until an access's x and dy have landed, `later` accesses (two loads
+// each) having been issued after it (a constant once the caller's loop over
+// the accesses is unrolled: one wait instruction).
 __device__ __forceinline__ void wait_access_landed(int later) {
     switch (later) {
         case 0: wait_vm<0>(); break;
@@ -68,9 +68,25 @@ __device__ __forceinline__ void wait_access_landed(int later) {
         case 4: wait_vm<8>(); break;
         case 5: wait_vm<10>(); break;
         case 6: wait_vm<12>(); break;
-        default: wait_vm<14>(); break;
+        case 7: wait_vm<14>(); break;
+        default: wait_vm<16>(); break;
     }
 }
+
+// LDS access slots of the staged rows (LayerNorm): a ring of kWideSlots slots
+// (x and dy of one access of all 512 lanes each, 16 KiB), of which a row
+// takes V; row i's access b sits in slot (i V + b) mod kWideSlots, so the
+// kWideSlots - V slots a row leaves free take the next row's first accesses
+// before this row's first pass even starts.  Measured on MI355X (A/B in
+// alternating processes, bitwise-equal outputs): LayerNorm bwd 8192 x 20480
+// (4 accesses ahead) 191-196 -> 185-187 us, 8192 x 24576 223-229 -> 220-225
+// us, 4096 x 32768 (1 ahead) level; RMSNorm level (+-0.5 %); the fused op's
+// backward 2-2.5 % slower (its dres loads, issued after the head start, wait
+// for it), so RMSNorm keeps V slots.  Build-time switch: 0 = V slots always.
+#ifndef ROWNORM_WIDE_RING
+#define ROWNORM_WIDE_RING 1
+#endif
+constexpr int kWideSlots = 9;  // 9 x 16 KiB + the reduction slots fit the 160 KiB of LDS
 
 // The first pass over a row starts on access b as soon as b's two loads have
 // landed instead of after the whole row (build-time switch for measurement).
@@ -133,7 +149,10 @@ __device__ __forceinline__ int opaque_lane(int v) {
 template <int V, bool LN, bool DRES>
 __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a) {
     constexpr int T = kWideLanes;
-    __shared__ u32x4 xs[V * T], ds[V * T];      // the row's x and dy, 16 bytes per slot
+    constexpr int S = ROWNORM_WIDE_RING && LN ? kWideSlots : V;  // access slots in LDS
+    constexpr int HS = S - V;                               // next-row accesses issued early
+    static_assert(HS >= 0, "a row needs V slots");
+    __shared__ u32x4 xs[S * T], ds[S * T];      // x and dy of the slots, 16 bytes per lane
     __shared__ float red[2 * 2 * (T / kWave)];  // two alternating two-value slots
     const int lane = threadIdx.x;
     const int wave_base = lane & ~(kWave - 1);
@@ -165,9 +184,14 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)xs + wave_slot;
     const uint32_t ds_lds =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)ds + wave_slot;
-    auto stage = [&](desc4 rx, desc4 rd, int b, int t) {
-        lds_load16(rx, (b * T + t) * 16, xs_lds + b * T * 16);
-        lds_load16(rd, (b * T + t) * 16, ds_lds + b * T * 16);
+    // access b of a row into slot `slot`
+    auto stage = [&](desc4 rx, desc4 rd, int b, int t, int slot) {
+        lds_load16(rx, (b * T + t) * 16, xs_lds + slot * T * 16);
+        lds_load16(rd, (b * T + t) * 16, ds_lds + slot * T * 16);
+    };
+    auto slot_of = [&](int base, int b) {  // (base + b) mod S, base < S, b < S
+        const int sl = base + b;
+        return sl >= S ? sl - S : sl;
     };
     auto x_rsrc = [&](int64_t row) { return row_desc(a.x, row, a.rows, a.ld_x * 2, h * 2); };
     auto dy_rsrc = [&](int64_t row) { return row_desc(a.dy, row, a.rows, a.ld_dy * 2, h * 2); };
@@ -182,25 +206,35 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
     if (n > 0) {
         const desc4 rx = x_rsrc(first), rd = dy_rsrc(first);
 #pragma unroll
-        for (int b = 0; b < V; ++b) stage(rx, rd, b, lane);
+        for (int b = 0; b < V; ++b) stage(rx, rd, b, lane, b);
         if constexpr (LN) {
             mean_nx = uniform_load_f32(a.mean, first, a.rows);
             rstd_nx = uniform_load_f32(a.rstd, first, a.rows);
         }
     }
     int parity = 0;
+    int base = 0;  // slot of the row's access 0: (i V) mod S
     for (int64_t i = 0; i < n; ++i) {
         const int64_t row = opaque_row(first + i * G);
         const int64_t next = row + G;  // past the end (size-0 descriptors) after the last
         const float mean = mean_nx, rstd_in = rstd_nx;
+        const desc4 nrx = x_rsrc(next), nrd = dy_rsrc(next);
+        const int nbase = slot_of(base, V % S);  // the next row's access 0
+        if constexpr (HS > 0) {
+            // the next row's first HS accesses, into the slots the previous
+            // row's last HS accesses left (this wave's reads of them are done)
+            wait_lds();
+#pragma unroll
+            for (int b = 0; b < HS; ++b) stage(nrx, nrd, b, lane, slot_of(nbase, b));
+        }
         // the row's loads (its LDS writes included); no LDS read may move above.
         // Staged: access b is read once b's x and dy have landed.  The row's
-        // loads went out in access order (x then dy of access b, then this
-        // wave's dx store of the previous row's access b), so at most 2 (V - 1
-        // - b) operations after b's dy are loads; vector-memory operations
-        // retire in issue order, so once no more than that many are
-        // outstanding, b's two loads have landed whether or not the stores are
-        // counted.
+        // loads went out in access order (x then dy of each access; stores of
+        // the previous row's dx and its dres loads between them), and after
+        // them the next row's first HS accesses: 2 (V - 1 - b + HS) = 2 (S - 1
+        // - b) loads follow b's dy.  Vector-memory operations retire in issue
+        // order, so once no more than that many are outstanding, b's two loads
+        // have landed whether or not the stores are counted.
         if constexpr (!ROWNORM_WIDE_STAGED) wait_all_counters();
         // lane offsets recomputed every row (an opaque lane index), not hoisted
         // out of the loop into registers held for the whole walk
@@ -212,11 +246,12 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int b = 0; b < V; ++b) {
-            if constexpr (ROWNORM_WIDE_STAGED) wait_access_landed(V - 1 - b);
+            if constexpr (ROWNORM_WIDE_STAGED) wait_access_landed(S - 1 - b);
             const bool in_row = (b * T + l) * 8 < h;
+            const int sl = slot_of(base, b);
             float xf[8], df[8], wf[8];
-            unpack8(xs[b * T + l], xf);
-            unpack8(ds[b * T + l], df);
+            unpack8(xs[sl * T + l], xf);
+            unpack8(ds[sl * T + l], df);
             unpack8(wv[b], wf);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -247,7 +282,6 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         // reduction: an opaque copy of the lane index keeps the compiler from
         // merging them
         const int t = opaque_lane(lane);
-        const desc4 nrx = x_rsrc(next), nrd = dy_rsrc(next);
 
         const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, h * 2);
         rsrc_t rr = rdx;
@@ -269,12 +303,16 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
 #pragma unroll
         for (int b = 0; b < V; ++b) {
             float xf[8], df[8], wf[8], o[8];
-            unpack8(xs[b * T + t], xf);
-            unpack8(ds[b * T + t], df);
-            // this access's slots are read: hand them to the next row (past
-            // the walk's last row the descriptors are empty: nothing is read)
-            wait_lds();
-            stage(nrx, nrd, b, t);
+            const int sl = slot_of(base, b);
+            unpack8(xs[sl * T + t], xf);
+            unpack8(ds[sl * T + t], df);
+            // this access's slot is read: hand it to the next row's access b +
+            // HS (past the walk's last row the descriptors are empty: nothing
+            // is read); the last HS slots wait for the row after next
+            if (b + HS < V) {
+                wait_lds();
+                stage(nrx, nrd, b + HS, t, sl);
+            }
             unpack8(wv[b], wf);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -296,6 +334,7 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
             }
             astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack8(o));
         }
+        base = nbase;
     }
 
     const int64_t padded = dyn_padded_hidden(h);
