@@ -318,3 +318,57 @@ def test_f32_fused_8192_rows():
     x, r, w = dev(inp["x"]), dev(inp["r"]), dev(inp["w"])
     out, r = rn.fused_add_rmsnorm_f32(x, r, w, inp["eps"])
     check_fused(inp, host(out), r.cpu().numpy(), h, "fused f32 8192x4096")
+
+
+# ------------------------------------------------------------ seeded random sweep
+def _random_cases(n=36, seed=20251203):
+    """(op, rows, hidden, seed): hidden a multiple of 4 drawn log-uniformly
+    from 4 to 2^18 (every launch bucket of the fp32 kernels, one-tile and
+    tiled backward rows), rows log-uniform up to 4000, at most 8 Mi elements."""
+    rng = np.random.default_rng(seed)
+    ops = ("fused", "rms", "ln", "ln_bwd", "rms_bwd", "fused_bwd")
+    out = []
+    for k in range(n):
+        h = 4 * max(1, int(np.exp(rng.uniform(0.0, np.log(1 << 16)))))
+        rows = max(1, int(np.exp(rng.uniform(0.0, np.log(4000.0)))))
+        rows = max(1, min(rows, (8 << 20) // h))
+        out.append((ops[k % len(ops)], rows, h, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("op,rows,h,seed", RANDOM_CASES,
+                         ids=[f"{o}-{r}x{h}" for o, r, h, _ in RANDOM_CASES])
+def test_f32_random_case(op, rows, h, seed):
+    what = f"random fp32 {op} {rows}x{h} seed {seed}"
+    if op == "fused":
+        inp = wl.fused_inputs(rows, h, seed=seed, f32=True)
+        out, r = rn.fused_add_rmsnorm_f32(dev(inp["x"]), dev(inp["r"]), dev(inp["w"]), inp["eps"])
+        check_fused(inp, host(out), r.cpu().numpy(), h, what)
+    elif op == "rms":
+        inp = wl.rmsnorm_inputs(rows, h, seed=seed, f32=True)
+        out = rn.rmsnorm_fwd_f32(dev(inp["x"]), dev(inp["w"]), inp["eps"])
+        ref, _ = oracle.rmsnorm_fwd_f32(inp["x"], inp["w"], inp["eps"], NT)
+        P.assert_f32_scaled(host(out), ref, np.abs(ref), h, what)
+    elif op == "ln":
+        inp = wl.layernorm_fwd_inputs(rows, h, seed=seed, f32=True)
+        y, mean, rstd = rn.layernorm_fwd_f32(dev(inp["x"]), dev(inp["w"]), dev(inp["b"]),
+                                             inp["eps"])
+        check_ln_fwd(inp, host(y), host(mean), host(rstd), h, what)
+    elif op == "ln_bwd":
+        inp = wl.layernorm_bwd_inputs(rows, h, seed=seed, f32=True)
+        mean32, rstd32 = ln_stats_f32(inp["x"], inp["eps"])
+        dx, dw, db = rn.layernorm_bwd_f32(dev(inp["dy"]), dev(inp["x"]), dev(mean32),
+                                          dev(rstd32), dev(inp["w"]))
+        check_ln_bwd(inp, mean32, rstd32, host(dx), host(dw), host(db), what)
+    else:
+        inp = wl.rmsnorm_bwd_inputs(rows, h, seed=seed, f32=True)
+        fused = op == "fused_bwd"
+        if fused:
+            dx, dw = rn.fused_add_rmsnorm_bwd_f32(dev(inp["dy"]), dev(inp["x"]), dev(inp["w"]),
+                                                  inp["eps"], dres=dev(inp["dres"]))
+        else:
+            dx, dw = rn.rmsnorm_bwd_f32(dev(inp["dy"]), dev(inp["x"]), dev(inp["w"]), inp["eps"])
+        check_rms_bwd(inp, host(dx), host(dw), inp["dres"] if fused else None, what)
