@@ -487,13 +487,16 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * dweight / dbias 4-byte aligned, the workspace 16-byte aligned (else
  * MISALIGNED).  Aliasing as for the bf16 entry points: out (y) may equal x,
  * dx (ds) may equal dy (dout) or dres, nothing else overlaps.
- * Every row is handled by the streamed kernels: forward, a 1024-lane
- * workgroup per row that keeps the first 16384 values of the row in
- * registers between its two passes and reads the rest again; backward, the
- * per-row reduction kernel, then 512-lane workgroups over 8192-column tiles
- * and the fixed-order column reduce (column sums bitwise reproducible run to
- * run).  workspace: at least norm_bwd_workspace_bytes_f32(op, rows, hidden)
- * bytes, contents ignored on entry. */
+ * Forward: one workgroup per row (64 to 1024 lanes) holds up to 16384
+ * values of the row in registers between the statistic and the normalize
+ * step (32768 for the fused op and RMSNorm) and reads any rest again.
+ * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
+ * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
+ * (read once); wider rows take a per-row reduction kernel, then 512-lane
+ * workgroups over 8192-column tiles (read twice); then the fixed-order column
+ * reduce (column sums bitwise reproducible run to run).  workspace: at least
+ * norm_bwd_workspace_bytes_f32(op, rows, hidden) bytes, contents ignored on
+ * entry. */
 NORM_API norm_status norm_fused_add_rmsnorm_f32(float* out, float* residual, const float* x,
                                                 const float* weight, int64_t rows,
                                                 int64_t hidden, float eps, hipStream_t stream);
@@ -523,9 +526,9 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, c
 /* Workspace bytes of an fp32 backward op (NORM_OP_LAYERNORM_BWD,
  * NORM_OP_RMSNORM_BWD or NORM_OP_FUSED_ADD_RMSNORM_BWD): 4 * padded hidden
  * (hidden rounded up to 64) per partial-sum slab and output column sum, for
- * each of its max(1, min(rows, 255 / ceil(hidden / 8192))) row walkers, plus
- * 8 bytes a row.  Pure host arithmetic; 0 for another op, an unsupported
- * hidden or rows <= 0. */
+ * each row walker: min(rows, 256) of them at 8196 ... 16384 columns, else
+ * max(1, min(rows, 255 / ceil(hidden / 8192))) plus 8 bytes a row.  Pure
+ * host arithmetic; 0 for another op, an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);
 
 #ifdef __cplusplus

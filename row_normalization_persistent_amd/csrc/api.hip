@@ -1125,12 +1125,15 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
 }
 
 // ---- fp32 activations ------------------------------------------------------------
-// Every fp32 call runs the streamed kernels (kernels_stream.hpp) with four fp32
-// values a 16-byte access: contiguous rows, hidden a multiple of 4 up to
-// kStreamMaxHidden, the matrices and weight / bias vectors 16-byte aligned,
-// mean / rstd 4-byte aligned.  The forward reads a row of up to 16384 values
-// once and a wider one twice; the backward is the streamed pair of kernels
-// plus the column reduce at every width.
+// fp32 calls run the streamed kernels (kernels_stream.hpp) with four fp32
+// values a 16-byte access, and the backward's rows of 8196 ... 16384 columns
+// the LDS-staged kernel (kernels_bwd_wide.hpp): contiguous rows, hidden a
+// multiple of 4 up to kStreamMaxHidden, the matrices and weight / bias
+// vectors 16-byte aligned, mean / rstd 4-byte aligned.  The forward reads a
+// row of up to 16384 values (32768 for fused / RMSNorm) once and a wider one
+// twice; the backward reads a row of up to 16384 values once (one tile of the
+// tile kernel up to 8192, LDS above) and a wider one twice (the streamed
+// pair), then the column reduce.
 int32_t stream_tiles_f32(int64_t hidden) {
     return (int32_t)ceil_div(hidden, kStreamTileColsF32);
 }
@@ -1139,6 +1142,22 @@ int32_t stream_walkers_f32(int64_t rows, int64_t hidden) {
 }
 bool f32_hidden_ok(int64_t hidden) {
     return hidden >= 4 && hidden % 4 == 0 && hidden <= kStreamMaxHidden;
+}
+// fp32 backward rows the LDS-staged kernel holds (read once; one workgroup
+// per row walker, up to 256).  Build-time switch for measurement: 0 sends
+// them to the streamed pair.
+#ifndef ROWNORM_F32_WIDE_BWD
+#define ROWNORM_F32_WIDE_BWD 1
+#endif
+bool f32_wide(int64_t hidden) {
+    return ROWNORM_F32_WIDE_BWD && hidden >= kWideF32MinHidden && hidden <= kWideF32MaxHidden;
+}
+int32_t bwd_walkers_f32(int64_t rows, int64_t hidden) {
+    return f32_wide(hidden) ? default_bwd_grid(rows) : stream_walkers_f32(rows, hidden);
+}
+size_t bwd_ws_bytes_f32(norm_op op, int64_t hidden, int64_t walkers, int64_t rows) {
+    return f32_wide(hidden) ? dyn_ws_bytes(op, hidden, walkers)
+                            : stream_ws_bytes(op, hidden, walkers, rows);
 }
 
 norm_status run_fwd_f32(norm_op op, const FwdCall& c, hipStream_t stream) {
@@ -1178,7 +1197,7 @@ norm_status run_fwd_f32(norm_op op, const FwdCall& c, hipStream_t stream) {
 
 size_t ws_query_f32(norm_op op, int64_t rows, int64_t hidden) {
     if (rows <= 0 || !f32_hidden_ok(hidden)) return 0;
-    return stream_ws_bytes(op, hidden, stream_walkers_f32(rows, hidden), rows);
+    return bwd_ws_bytes_f32(op, hidden, bwd_walkers_f32(rows, hidden), rows);
 }
 
 norm_status run_bwd_f32(norm_op op, const BwdCall& c, hipStream_t stream) {
@@ -1197,8 +1216,8 @@ norm_status run_bwd_f32(norm_op op, const BwdCall& c, hipStream_t stream) {
                 (ln && (!aligned(c.mean, 4) || !aligned(c.rstd, 4)))))
         return NORM_ERROR_MISALIGNED;
     const int32_t tiles = stream_tiles_f32(c.hidden);
-    const int32_t walkers = stream_walkers_f32(c.rows, c.hidden);
-    const size_t ws_need = stream_ws_bytes(op, c.hidden, any ? walkers : 0, any ? c.rows : 0);
+    const int32_t walkers = bwd_walkers_f32(c.rows, c.hidden);
+    const size_t ws_need = bwd_ws_bytes_f32(op, c.hidden, any ? walkers : 0, any ? c.rows : 0);
 
     const int64_t mrows = any ? c.rows : 0;
     const int64_t h = c.hidden;
@@ -1226,6 +1245,7 @@ norm_status run_bwd_f32(norm_op op, const BwdCall& c, hipStream_t stream) {
                        c.dres,  c.weight, (float*)c.workspace, c.dweight, c.dbias,
                        h,       h,        h,         h,         c.rows,
                        (int32_t)h, walkers, c.eps};
+    if (f32_wide(h)) return from_hip(launch_bwd_wide_f32(ln, a, stream));
     return from_hip(launch_stream_bwd(ln, true, a, tiles, walkers, stream));
 }
 

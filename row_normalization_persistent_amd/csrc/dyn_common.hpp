@@ -181,4 +181,37 @@ __device__ __forceinline__ void dyn_row_sum2(float& a, float& b, float* slot, in
 template <int T>
 constexpr int dyn_red_floats() { return T > kWave ? (dyn_block<T>() / T) * (T / kWave) : 1; }
 
+// ---- elements of a 16-byte access ------------------------------------------------
+template <typename E> struct Elems;
+template <> struct Elems<uint16_t> { static constexpr int kPer = 8; };  // bf16 patterns
+template <> struct Elems<float> { static constexpr int kPer = 4; };
+
+template <typename E>
+__device__ __forceinline__ void unpack16(const u32x4& v, float (&f)[Elems<E>::kPer]) {
+    if constexpr (Elems<E>::kPer == 8) {
+        unpack8(v, f);
+    } else {
+        f[0] = __uint_as_float(v.x);
+        f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z);
+        f[3] = __uint_as_float(v.w);
+    }
+}
+
+// bf16: round to nearest even; fp32: the values themselves
+template <typename E>
+__device__ __forceinline__ u32x4 pack16(const float (&f)[Elems<E>::kPer]) {
+    if constexpr (Elems<E>::kPer == 8) {
+        return pack8(f);
+    } else {
+        u32x4 v;
+        v.x = __float_as_uint(f[0]);
+        v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]);
+        v.w = __float_as_uint(f[3]);
+        return v;
+    }
+}
+
+
 }  // namespace rownorm

@@ -30,6 +30,10 @@
 // and reduction).
 // At the end each workgroup writes one slab of [G][outs][padded] column sums
 // for the shared column-reduce kernel.
+// The element type E is uint16_t (bf16 patterns, 8 a 16-byte access: hidden
+// 16392 ... 32768) or float (4 an access: fp32 rows of 8196 ... 16384, whose
+// column sums take half the registers and whose LDS footprint is that of a
+// bf16 row twice as wide).
 #pragma once
 
 #include <type_traits>
@@ -146,9 +150,11 @@ __device__ __forceinline__ int opaque_lane(int v) {
     return v;
 }
 
-template <int V, bool LN, bool DRES>
+template <typename E, int V, bool LN, bool DRES>
 __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a) {
     constexpr int T = kWideLanes;
+    constexpr int EP = Elems<E>::kPer;     // values a 16-byte access
+    constexpr int ES = (int)sizeof(E);     // bytes a value
     constexpr int S = ROWNORM_WIDE_RING && LN ? kWideSlots : V;  // access slots in LDS
     constexpr int HS = S - V;                               // next-row accesses issued early
     static_assert(HS >= 0, "a row needs V slots");
@@ -159,21 +165,21 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
     const int h = a.hidden;
     const float inv_h = 1.0f / (float)h;
     // the weights stay in registers for the whole walk, packed (4 per access)
-    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 2);
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * ES);
     u32x4 wv[V];
 #pragma unroll
     for (int b = 0; b < V; ++b) wv[b] = aload<8, 0>(rw, (b * T + lane) * 16);
 
-    float pw[V][8], pb[LN ? V : 1][8];
+    float pw[V][EP], pb[LN ? V : 1][EP];
 #pragma unroll
     for (int b = 0; b < V; ++b)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pw[b][k] = 0.0f;
+        for (int k = 0; k < EP; ++k) pw[b][k] = 0.0f;
     if constexpr (LN) {
 #pragma unroll
         for (int b = 0; b < V; ++b)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pb[b][k] = 0.0f;
+            for (int k = 0; k < EP; ++k) pb[b][k] = 0.0f;
     }
 
     // access b of lane t of a row: x and dy from HBM into their LDS slots
@@ -193,8 +199,10 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         const int sl = base + b;
         return sl >= S ? sl - S : sl;
     };
-    auto x_rsrc = [&](int64_t row) { return row_desc(a.x, row, a.rows, a.ld_x * 2, h * 2); };
-    auto dy_rsrc = [&](int64_t row) { return row_desc(a.dy, row, a.rows, a.ld_dy * 2, h * 2); };
+    auto x_rsrc = [&](int64_t row) { return row_desc(a.x, row, a.rows, a.ld_x * ES, h * ES); };
+    auto dy_rsrc = [&](int64_t row) {
+        return row_desc(a.dy, row, a.rows, a.ld_dy * ES, h * ES);
+    };
 
     const int64_t G = gridDim.x;
     const int64_t first = blockIdx.x;
@@ -241,25 +249,25 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         const int l = opaque_lane(lane);
 
         // the row's two sums (an access past the row's end, in the last b, is
-        // left out whatever its LDS slot holds; hidden is a multiple of 8, so
+        // left out whatever its LDS slot holds; hidden is a multiple of EP, so
         // an access is wholly inside the row or wholly past it)
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int b = 0; b < V; ++b) {
             if constexpr (ROWNORM_WIDE_STAGED) wait_access_landed(S - 1 - b);
-            const bool in_row = (b * T + l) * 8 < h;
+            const bool in_row = (b * T + l) * EP < h;
             const int sl = slot_of(base, b);
-            float xf[8], df[8], wf[8];
-            unpack8(xs[sl * T + l], xf);
-            unpack8(ds[sl * T + l], df);
-            unpack8(wv[b], wf);
+            float xf[EP], df[EP], wf[EP];
+            unpack16<E>(xs[sl * T + l], xf);
+            unpack16<E>(ds[sl * T + l], df);
+            unpack16<E>(wv[b], wf);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < EP; ++k) {
                 xf[k] = in_row ? xf[k] : 0.0f;
                 df[k] = in_row ? df[k] : 0.0f;
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < EP; ++k) {
                 if constexpr (LN) {
                     const float xh = (xf[k] - mean) * rstd_in;
                     const float g = df[k] * wf[k];
@@ -283,9 +291,9 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         // merging them
         const int t = opaque_lane(lane);
 
-        const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * 2, h * 2);
+        const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * ES, h * ES);
         rsrc_t rr = rdx;
-        if constexpr (DRES) rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * 2, h * 2);
+        if constexpr (DRES) rr = row_rsrc_ld(a.dres, row, a.rows, a.ld_dres * ES, h * ES);
         float c1 = 0.0f, c2 = 0.0f, rstd = 0.0f, coef = 0.0f;
         if constexpr (LN) {
             c1 = s1 * inv_h;
@@ -302,10 +310,10 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
         }
 #pragma unroll
         for (int b = 0; b < V; ++b) {
-            float xf[8], df[8], wf[8], o[8];
+            float xf[EP], df[EP], wf[EP], o[EP];
             const int sl = slot_of(base, b);
-            unpack8(xs[sl * T + t], xf);
-            unpack8(ds[sl * T + t], df);
+            unpack16<E>(xs[sl * T + t], xf);
+            unpack16<E>(ds[sl * T + t], df);
             // this access's slot is read: hand it to the next row's access b +
             // HS (past the walk's last row the descriptors are empty: nothing
             // is read); the last HS slots wait for the row after next
@@ -313,9 +321,9 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
                 wait_lds();
                 stage(nrx, nrd, b + HS, t, sl);
             }
-            unpack8(wv[b], wf);
+            unpack16<E>(wv[b], wf);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < EP; ++k) {
                 if constexpr (LN) {
                     const float xh = (xf[k] - mean) * rstd_in;
                     o[k] = rstd_in * (df[k] * wf[k] - c1 - xh * c2);
@@ -327,12 +335,12 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
                 }
             }
             if constexpr (DRES) {
-                float rf[8];
-                unpack8(dr[b], rf);
+                float rf[EP];
+                unpack16<E>(dr[b], rf);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) o[k] += rf[k];
+                for (int k = 0; k < EP; ++k) o[k] += rf[k];
             }
-            astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack8(o));
+            astore<8, kCachePolicyNT>(rdx, (b * T + lane) * 16, pack16<E>(o));
         }
         base = nbase;
     }
@@ -341,10 +349,10 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
     float* slab = a.workspace + (int64_t)blockIdx.x * (LN ? 2 : 1) * padded;
 #pragma unroll
     for (int b = 0; b < V; ++b) {
-        const int col = (b * T + lane) * 8;
+        const int col = (b * T + lane) * EP;
         if (col < h) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < EP; ++k) {
                 slab[col + k] = pw[b][k];
                 if constexpr (LN) slab[padded + col + k] = pb[b][k];
             }
@@ -352,19 +360,19 @@ __global__ __launch_bounds__(kWideLanes) void norm_bwd_wide_kernel(DynBwdArgs a)
     }
 }
 
-template <int V, bool LN>
+template <int V, bool LN, typename E = uint16_t>
 hipError_t launch_bwd_wide(const DynBwdArgs& a, hipStream_t stream) {
     const int outs = LN ? 2 : 1;
     if (a.rows > 0) {
         if constexpr (LN) {
-            hipLaunchKernelGGL((norm_bwd_wide_kernel<V, true, false>), dim3(a.grid),
+            hipLaunchKernelGGL((norm_bwd_wide_kernel<E, V, true, false>), dim3(a.grid),
                                dim3(kWideLanes), 0, stream, a);
         } else {
             if (a.dres)
-                hipLaunchKernelGGL((norm_bwd_wide_kernel<V, false, true>), dim3(a.grid),
+                hipLaunchKernelGGL((norm_bwd_wide_kernel<E, V, false, true>), dim3(a.grid),
                                    dim3(kWideLanes), 0, stream, a);
             else
-                hipLaunchKernelGGL((norm_bwd_wide_kernel<V, false, false>), dim3(a.grid),
+                hipLaunchKernelGGL((norm_bwd_wide_kernel<E, V, false, false>), dim3(a.grid),
                                    dim3(kWideLanes), 0, stream, a);
         }
         const hipError_t e = hipGetLastError();

@@ -67,38 +67,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStreamUnroll = ROWNORM_STREAM_UNROLL;  // 16-byte accesses in flight per lane and matrix
 constexpr int kStreamPass1 = ROWNORM_STREAM_P1_POLICY;  // cache policy of the first read
 
-// ---- elements of a 16-byte access ------------------------------------------------
-template <typename E> struct Elems;
-template <> struct Elems<uint16_t> { static constexpr int kPer = 8; };  // bf16 patterns
-template <> struct Elems<float> { static constexpr int kPer = 4; };
-
-template <typename E>
-__device__ __forceinline__ void unpack16(const u32x4& v, float (&f)[Elems<E>::kPer]) {
-    if constexpr (Elems<E>::kPer == 8) {
-        unpack8(v, f);
-    } else {
-        f[0] = __uint_as_float(v.x);
-        f[1] = __uint_as_float(v.y);
-        f[2] = __uint_as_float(v.z);
-        f[3] = __uint_as_float(v.w);
-    }
-}
-
-// bf16: round to nearest even; fp32: the values themselves
-template <typename E>
-__device__ __forceinline__ u32x4 pack16(const float (&f)[Elems<E>::kPer]) {
-    if constexpr (Elems<E>::kPer == 8) {
-        return pack8(f);
-    } else {
-        u32x4 v;
-        v.x = __float_as_uint(f[0]);
-        v.y = __float_as_uint(f[1]);
-        v.z = __float_as_uint(f[2]);
-        v.w = __float_as_uint(f[3]);
-        return v;
-    }
-}
-
 template <int Aux>
 __device__ __forceinline__ u32x4 load16(rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, Aux);

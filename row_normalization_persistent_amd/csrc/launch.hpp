@@ -136,6 +136,13 @@ using WideVecsLn = std::integer_sequence<int, 5, 6, 7, 8>;
 using WideVecsRms = std::integer_sequence<int, 5, 6, 7, 8>;
 const std::vector<WideBwdEntry>& layernorm_bwd_wide_table();
 const std::vector<WideBwdEntry>& rmsnorm_bwd_wide_table();
+// fp32 rows of kWideF32MinHidden ... kWideF32MaxHidden columns (4 values an
+// access, V = ceil(hidden / 2048) = 5 ... 8): the same kernel, read once
+// instead of the streamed pair's twice.  Grid a.grid, workspace a.grid slabs.
+constexpr int64_t kWideF32MinHidden = 8196;
+constexpr int64_t kWideF32MaxHidden = 16384;
+constexpr int wide_vecs_f32(int64_t hidden) { return (int)((hidden + 2047) / 2048); }
+hipError_t launch_bwd_wide_f32(bool ln, const DynBwdArgs& a, hipStream_t stream);
 
 // ---- row-split forward (few rows: one row over k workgroups) ------------------
 // Workspace: kSplitHeaderWords 32-bit words (word 0: error bits), then per

@@ -727,8 +727,8 @@ def test_f32_validation():
 
 def test_f32_workspace_sizes():
     """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
-    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers),
-    plus 8 bytes a row."""
+    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers, plus
+    8 bytes a row; at 8196 ... 16384 columns min(rows, 256) walkers)."""
     ws = rn.workspace_bytes_f32
     pad = lambda h: -(-h // 64) * 64
     assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4 + 8192 * 8
@@ -736,6 +736,11 @@ def test_f32_workspace_sizes():
     assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4 + 3 * 8
     assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1000 * 8  # 128 tiles
     assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 1000 * 8  # 3 tiles
+    # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs, no per-row floats
+    assert ws("layernorm_bwd", 1000, 16384) == 256 * 2 * 16384 * 4
+    assert ws("rmsnorm_bwd", 3, 8196) == 3 * pad(8196) * 4
+    assert ws("fused_add_rmsnorm_bwd", 100, 12288) == 100 * 12288 * 4
+    assert ws("layernorm_bwd", 1000, 8192) == 255 * 2 * 8192 * 4 + 1000 * 8  # one tile
     assert ws("layernorm_bwd", 0, 4096) == 0
     assert ws("layernorm_bwd", 8, 4098) == 0
     assert ws("layernorm_fwd", 8, 4096) == 0      # a forward op
