@@ -40,7 +40,9 @@ hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t 
     const StreamFwdShape sh = stream_fwd_shape(f32, op == kSplitLn, op == kSplitRms, a.hidden);
     switch (op) {
         case kSplitFused:
-            return f32 ? fwd_f32_rms<kSplitFused>(sh, a, stream)
+            if (f32) return fwd_f32_rms<kSplitFused>(sh, a, stream);
+            return sh.unroll == 6
+                       ? launch_stream_fwd_op<uint16_t, kSplitFused, kStreamFwdLanes, 6>(a, stream)
                        : launch_stream_fwd_op<uint16_t, kSplitFused, kStreamFwdLanes, 4>(a, stream);
         case kSplitRms:
             if (f32) return fwd_f32_rms<kSplitRms>(sh, a, stream);

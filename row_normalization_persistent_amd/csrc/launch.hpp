@@ -217,16 +217,25 @@ constexpr int64_t kStreamMaxHidden = int64_t(1) << 20;
 //    were 0-4 % slower there);
 //  * bf16 (rows past the on-chip kernels): 1024 x 4; RMSNorm 1024 x 8 up to
 //    73728 columns, where 8 accesses hold nearly the whole row (4096 x 65544
-//    214 -> 202 us; at 131072 and 262144 columns 1-6 % slower); the fused and
-//    LayerNorm forms spill at 8.
+//    214 -> 202 us; at 131072 and 262144 columns 1-6 % slower); the fused op
+//    1024 x 6 up to 98304 columns (4096 x 65544 454 -> 440 us, 2048 x 81920
+//    263 -> 256 us, level at 98304); LayerNorm keeps 4 (6 was 4-12 % slower
+//    at 53248-65536 columns); the fused and LayerNorm forms spill at 8.
 #ifndef ROWNORM_STREAM_U8
 #define ROWNORM_STREAM_U8 1  // build-time switch for measurement: 0 = never 8 accesses past 16384 fp32 columns
 #endif
 struct StreamFwdShape {
     int lanes, unroll;
 };
+#ifndef ROWNORM_STREAM_U6
+#define ROWNORM_STREAM_U6 1
+#endif
 constexpr StreamFwdShape stream_fwd_shape(bool f32, bool ln, bool rms, int64_t hidden) {
-    if (!f32) return {kStreamFwdLanes, rms && ROWNORM_STREAM_U8 && hidden <= 73728 ? 8 : 4};
+    if (!f32) {
+        if (rms) return {kStreamFwdLanes, ROWNORM_STREAM_U8 && hidden <= 73728 ? 8 : 4};
+        if (!ln) return {kStreamFwdLanes, ROWNORM_STREAM_U6 && hidden <= 98304 ? 6 : 4};
+        return {kStreamFwdLanes, 4};
+    }
     if (hidden <= 1024) return {64, 4};
     if (ln) {
         if (hidden <= 2048) return {64, 8};

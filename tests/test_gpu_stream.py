@@ -45,7 +45,8 @@ FWD_CASES = [("fused_add_rmsnorm", 65544, 37), ("fused_add_rmsnorm", 131072, 300
              ("fused_add_rmsnorm", 1 << 20, 3), ("rmsnorm_fwd", 65544, 3), ("rmsnorm_fwd", 73728, 5),
              ("rmsnorm_fwd", 73736, 4),
              ("rmsnorm_fwd", 100000, 37), ("rmsnorm_fwd", 262144, 64),
-             ("layernorm_fwd", 49160, 37), ("layernorm_fwd", 65536, 300),
+             ("layernorm_fwd", 49160, 37), ("layernorm_fwd", 65536, 300), ("layernorm_fwd", 65544, 9),
+             ("fused_add_rmsnorm", 98304, 11), ("fused_add_rmsnorm", 98312, 5),
              ("layernorm_fwd", 100000, 1), ("layernorm_fwd", 1 << 20, 3)]
 
 
