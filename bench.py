@@ -375,13 +375,18 @@ def load_traffic(kernel: str, rows):
 
 
 def kernel_source_digest() -> str:
-    """Digest of the sources that make the compiled forward kernels' code."""
+    """Digest of the sources that make the compiled forward kernels' code,
+    comments and blank lines left out (a comment edit changes no kernel)."""
     import hashlib
+    import re
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "row_normalization_persistent_amd", "csrc")
     h = hashlib.sha256()
     for name in ("device_common.hpp", "kernels_fwd.hpp", "launch.hpp"):
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()
 
 

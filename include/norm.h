@@ -30,8 +30,9 @@
  *     points below spread few wide rows over several workgroups instead.
  * The library picks the family; the arithmetic and results (within rounding)
  * are the same.  The `_f32` entry points take fp32 activations, weights and
- * gradients instead (contiguous rows, hidden a multiple of 4 up to 2^20) and
- * run the streamed kernels at every width.
+ * gradients instead (contiguous rows, hidden a multiple of 4 up to 2^20):
+ * the streamed kernels at every width, and for backward rows of 8196 ...
+ * 16384 columns the LDS-staged kernel.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -455,10 +456,11 @@ NORM_API norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden
                                int32_t cu_count, norm_launch_cfg* cfg);
 
 /* Human-readable description of the launch the library would make for
- * (op, rows, hidden) through the bf16 entry points (the `_f32` ones always
- * run the streamed kernels) on a device with `cu_count` compute units (<= 0: the
- * current device): kernel instantiation, lanes per row, rows per workgroup,
- * 16-byte vectors per lane, workgroup size, grid, ring depth and workspace.
+ * (op, rows, hidden) through the bf16 entry points (the `_f32` ones choose
+ * by hidden alone, as their section below states) on a device with
+ * `cu_count` compute units (<= 0: the current device): kernel
+ * instantiation, lanes per row, rows per workgroup, 16-byte vectors per lane,
+ * workgroup size, grid, ring depth and workspace.
  * Writes a NUL-terminated string of at most `len` bytes to `buf` (which may be
  * NULL when len is 0) and returns the full length without the NUL, or -1 for
  * invalid arguments or an unsupported hidden.  Host logic only when

@@ -6,8 +6,9 @@
 // operations, whose per-column sums also live on chip) fits neither, so
 // these kernels read it twice: once for the row's reduction and once more,
 // from the Infinity Cache while the rows in flight fit there, for the
-// normalized output.  The same kernels serve fp32 activations at every
-// width.  16-byte accesses only: E = uint16_t (bf16 patterns, 8 a 16-byte
+// normalized output.  The same kernels serve fp32 activations (at every
+// width but the backward's 8196 ... 16384 columns, which the LDS-staged
+// kernel reads once).  16-byte accesses only: E = uint16_t (bf16 patterns, 8 a 16-byte
 // access) or float (4), hidden a multiple of the access's element count,
 // every row stride too, 16-byte-aligned pointers, hidden up to 2^20.
 //

@@ -193,7 +193,8 @@ const std::vector<SplitEntry>& split_table();
 // a 1024-lane per-row reduction kernel, then 512-lane workgroups over tiles of
 // kStreamTileVecs * 512 16-byte accesses (16384 bf16 or 8192 fp32 columns).
 // 16-byte accesses only.  The same kernels run fp32 activations (the `_f32`
-// entry points) at every width; the DynFwdArgs / DynBwdArgs pointers then
+// entry points; their backward rows of 8196 ... 16384 columns go to the
+// LDS-staged kernel instead); the DynFwdArgs / DynBwdArgs pointers then
 // point at fp32 matrices and vectors, row strides in fp32 elements.
 constexpr int kStreamFwdLanes = 1024;
 constexpr int kStreamTileLanes = 512;
