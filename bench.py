@@ -1053,11 +1053,11 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
 
 
 def f32_ops(torch, rn, wl, dev, stream, reps):
-    """fp32 activations (the `_f32` entry points, the streamed kernels at
-    every width) at the bf16 operations' configured shapes: fused add +
-    RMSNorm 8192 x 4096, RMSNorm 4096 x 16384, LayerNorm forward 2048 x
-    16384, the three backward operations 8192 x 4096; time per launch over
-    cold buffer sets, algorithmic bytes at 4 bytes an element."""
+    """fp32 activations (the `_f32` entry points) at the bf16 operations'
+    configured shapes: fused add + RMSNorm 8192 x 4096, RMSNorm 4096 x 16384,
+    LayerNorm forward 2048 x 16384, the three backward operations 8192 x 4096,
+    and LayerNorm backward 4096 x 16384 (the LDS-staged kernel); time per
+    launch over cold buffer sets, algorithmic bytes at 4 bytes an element."""
     out = []
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
@@ -1130,6 +1130,26 @@ def f32_ops(torch, rn, wl, dev, stream, reps):
     out.append(_op_rec("fused_add_rmsnorm_bwd_f32", rows, h, 16 * h * rows + 8 * h, t,
                        note=note))
     del xs, dys, drs, dxs, ws
+    # a row the LDS-staged backward holds (8196 ... 16384 fp32 columns)
+    rows, h = 4096, 16384
+    i = wl.layernorm_bwd_inputs(rows, h, seed=0, f32=True)
+    n = _n_sets(3 * rows * h * 4)
+    xs, dys = sets(f(i["x"]), n), sets(f(i["dy"]), n)
+    dxs = [torch.empty_like(xs[0]) for _ in range(n)]
+    w = f(i["w"])
+    torch.cuda.synchronize()  # inputs written on the current stream, used on `stream`
+    _, mean, rstd = rn.layernorm_fwd_f32(xs[0], w, torch.zeros_like(w), wl.EPS_LN, stream=stream)
+    dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
+    ws = torch.empty(rn.workspace_bytes_f32("layernorm_bwd", rows, h), dtype=torch.uint8,
+                     device=dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.layernorm_bwd_f32(dys[j], xs[j], mean, rstd, w, dx=dxs[j], dweight=dw,
+                                          dbias=db, workspace=ws, stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("layernorm_bwd_f32", rows, h, (12 * h + 8) * rows + 12 * h, t,
+                       note="fp32 activations: LDS-staged backward (row read once) + column "
+                            "reduce"))
+    del xs, dys, dxs, ws
     torch.cuda.synchronize()
     return out
 
@@ -1356,6 +1376,8 @@ STREAM_F32_WORKLOADS = [
      lambda r, h: 12 * h * r + 4 * h),
     ("fused_add_rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,true,3,true>",
      lambda r, h: 16 * h * r + 4 * h),
+    ("layernorm_bwd_f32 (LDS-staged)", 4096, 16384, "norm_bwd_wide_kernel<float,8,true,false>",
+     lambda r, h: (12 * h + 8) * r + 4 * h),
 ]
 
 
@@ -1374,6 +1396,7 @@ def _row_kernel_name(op, rows, hidden):
     desc = rn.describe_config(op, rows, hidden, cu_count=256)
     k = desc.split(": ", 1)[1].split(" (", 1)[0]
     dres = "true" if op == "fused_add_rmsnorm_bwd" else "false"
+    k = k.replace("norm_bwd_wide_kernel<", "norm_bwd_wide_kernel<unsignedshort,")  # element type
     return (k.replace(",layernorm>", ",true,false>").replace(",rmsnorm,dres?>", f",false,{dres}>")
              .replace(",dres?>", f",{dres}>"))
 
