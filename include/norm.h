@@ -489,9 +489,11 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * dweight / dbias 4-byte aligned, the workspace 16-byte aligned (else
  * MISALIGNED).  Aliasing as for the bf16 entry points: out (y) may equal x,
  * dx (ds) may equal dy (dout) or dres, nothing else overlaps.
- * Forward: one workgroup per row (64 to 1024 lanes) holds up to 16384
- * values of the row in registers between the statistic and the normalize
- * step (32768 for the fused op and RMSNorm) and reads any rest again.
+ * Forward: rows of up to 1024 values take 8 to 32 lanes each, 256 / lanes
+ * rows to a workgroup; wider rows take one workgroup each (64 to 1024
+ * lanes), which holds up to 16384 values of the row in registers between
+ * the statistic and the normalize step (32768 for the fused op and RMSNorm)
+ * and reads any rest again.
  * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
  * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
  * (read once); wider rows take a per-row reduction kernel, then 512-lane

@@ -36,7 +36,33 @@ hipError_t fwd_f32_ln(const StreamFwdShape& sh, const DynFwdArgs& a, hipStream_t
     }
 }
 
+// fp32 rows of up to 1024 values: G lanes a row, U accesses a lane, 256 / G
+// rows a workgroup (group_fwd_kernel).  Measured on MI355X with one row per
+// 64-lane workgroup instead: RMSNorm 262144 x 64 1.39 TB/s, 131072 x 128 2.43,
+// 65536 x 256 3.93, 32768 x 512 5.13, 16384 x 1024 5.35; with the group
+// kernel 5.74-5.77 up to 512 columns and 5.44 at 1024 (fused 5.62).
+template <int OP>
+hipError_t group_fwd_f32(int64_t hidden, const DynFwdArgs& a, hipStream_t stream) {
+    if (hidden <= 32) return launch_group_fwd<OP, 8, 1>(a, stream);
+    if (hidden <= 64) return launch_group_fwd<OP, 8, 2>(a, stream);
+    if (hidden <= 128) return launch_group_fwd<OP, 8, 4>(a, stream);
+    if (hidden <= 256) return launch_group_fwd<OP, 16, 4>(a, stream);
+    if (hidden <= 512) return launch_group_fwd<OP, 32, 4>(a, stream);
+    return launch_group_fwd<OP, 32, 8>(a, stream);
+}
+// (a whole wave a row, 8 accesses a lane, ran 4-9 % slower at 1536-2048
+// columns than the one-row streamed launch)
+constexpr int64_t kGroupFwdMaxHidden = 1024;
+
 hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t stream) {
+    if (f32 && a.hidden <= kGroupFwdMaxHidden) {
+        switch (op) {
+            case kSplitFused: return group_fwd_f32<kSplitFused>(a.hidden, a, stream);
+            case kSplitRms: return group_fwd_f32<kSplitRms>(a.hidden, a, stream);
+            case kSplitLn: return group_fwd_f32<kSplitLn>(a.hidden, a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     const StreamFwdShape sh = stream_fwd_shape(f32, op == kSplitLn, op == kSplitRms, a.hidden);
     switch (op) {
         case kSplitFused:

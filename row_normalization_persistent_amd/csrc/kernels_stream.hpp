@@ -8,13 +8,15 @@
 // from the Infinity Cache while the rows in flight fit there, for the
 // normalized output.  The same kernels serve fp32 activations (at every
 // width but the backward's 8196 ... 16384 columns, which the LDS-staged
-// kernel reads once).  16-byte accesses only: E = uint16_t (bf16 patterns, 8 a 16-byte
+// kernel reads once; forward rows of up to 1024 fp32 values go several to a
+// wave in group_fwd_kernel).  16-byte accesses only: E = uint16_t (bf16 patterns, 8 a 16-byte
 // access) or float (4), hidden a multiple of the access's element count,
 // every row stride too, 16-byte-aligned pointers, hidden up to 2^20.
 //
 // Forward (stream_fwd_kernel, T lanes a row -- 1024 for bf16; for fp32 as
 // many as give each lane at most 4 accesses of a row of up to 16384 values,
-// 1024 beyond -- workgroups walk the rows g, g + G, ...): pass 1 streams the row for its statistic -- sum s^2 (s = x + r for
+// 1024 beyond -- workgroups walk the rows g, g + G, ...): pass 1 streams the
+// row for its statistic -- sum s^2 (s = x + r for
 // the fused op), or for LayerNorm each lane's count, sum and centered sum of
 // squares, merged access by access with the pairwise update of a sum of
 // squared deviations (Chan, Golub & LeVeque), then combined over the lanes
@@ -235,6 +237,125 @@ hipError_t launch_stream_fwd_op(const DynFwdArgs& a, hipStream_t stream) {
     const int64_t grid = a.rows < kStreamMaxGrid ? a.rows : kStreamMaxGrid;
     hipLaunchKernelGGL((stream_fwd_kernel<E, OP, T, U>), dim3((unsigned)grid), dim3(T), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+// ---- forward, short fp32 rows: several rows a wave ---------------------------------
+// A row of up to 4 G U values (G lanes x U 16-byte accesses, G = 8, 16 or 32)
+// is held by a lane group of G lanes; a 256-lane workgroup holds 256 / G rows,
+// walking the row sets blockIdx.x, + gridDim.x, ...  One buffer descriptor
+// covers a workgroup's set of rows and each lane adds its row's offset (an
+// access past its row's end gets an offset past the descriptor's range: it
+// loads zeros and stores nothing).  The row's reductions stay inside its lane
+// group (DPP and one cross-lane swap, no LDS, no barrier).  LayerNorm takes
+// the two passes over the row in registers: mean, then the centered sum of
+// squares of the row's values (accesses past the end left out).
+constexpr int kGroupBlock = 256;
+
+template <int OP, int G, int U>
+__global__ __launch_bounds__(kGroupBlock) void group_fwd_kernel(DynFwdArgs a) {
+    static_assert(G == 8 || G == 16 || G == 32, "rows narrower than a wave");
+    constexpr int R = kGroupBlock / G;  // rows a workgroup
+    constexpr bool kFused = OP == kSplitFused, kLn = OP == kSplitLn;
+    const int lane = threadIdx.x;
+    const int g = lane / G, gl = lane % G;
+    const int h = a.hidden;
+    const float inv_h = 1.0f / (float)h;
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * 4);
+    rsrc_t rb = rw;
+    if constexpr (kLn) rb = row_rsrc_ld(a.bias, 0, 1, 0, h * 4);
+    u32x4 wv[U], bv[kLn ? U : 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int col = (gl + u * G) * 4;
+        const int off = col < h ? col * 4 : kOutOfRange;
+        wv[u] = load16<0>(rw, off);
+        if constexpr (kLn) bv[u] = load16<0>(rb, off);
+    }
+    for (int64_t first = (int64_t)blockIdx.x * R; first < a.rows;
+         first += (int64_t)gridDim.x * R) {
+        const int64_t r0 = opaque_row(first);
+        const rsrc_t rx = rows_rsrc<G>(a.x, r0, R, a.rows, a.ld_x, h, 4);
+        const rsrc_t ro = rows_rsrc<G>(a.out, r0, R, a.rows, a.ld_out, h, 4);
+        rsrc_t rr = rx;
+        if constexpr (kFused) rr = rows_rsrc<G>(a.residual, r0, R, a.rows, a.ld_res, h, 4);
+        int off_x[U], off_o[U], off_r[U];
+        float s[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int col = (gl + u * G) * 4;
+            off_x[u] = set_off<G>(g, col, a.ld_x, h, 4);
+            off_o[u] = set_off<G>(g, col, a.ld_out, h, 4);
+            off_r[u] = kFused ? set_off<G>(g, col, a.ld_res, h, 4) : 0;
+        }
+        u32x4 xv[U], rv[kFused ? U : 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xv[u] = load16<kCachePolicyNT>(rx, off_x[u]);
+            if constexpr (kFused) rv[u] = load16<kCachePolicyNT>(rr, off_r[u]);
+        }
+        float p0 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            unpack16<float>(xv[u], s[u]);
+            if constexpr (kFused) {
+                float rf[4];
+                unpack16<float>(rv[u], rf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[u][e] += rf[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p0 += kLn ? s[u][e] : s[u][e] * s[u][e];
+        }
+        p0 = group_sum<G>(p0);  // past the end: zeros, add nothing
+        float mu = 0.0f, rstd;
+        if constexpr (kLn) {
+            mu = p0 * inv_h;
+            float p1 = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = (gl + u * G) * 4 < h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float d = s[u][e] - mu;
+                    p1 += in ? d * d : 0.0f;
+                }
+            }
+            rstd = fast_rsqrt(group_sum<G>(p1) * inv_h + a.eps);
+            const int64_t row = r0 + g;
+            if (gl == 0 && row < a.rows && a.mean != nullptr) {
+                a.mean[row] = mu;
+                a.rstd[row] = rstd;
+            }
+        } else {
+            rstd = fast_rsqrt(p0 * inv_h + a.eps);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float wf[4], o[4];
+            unpack16<float>(wv[u], wf);
+            if constexpr (kFused) store16(rr, off_r[u], pack16<float>(s[u]));
+            if constexpr (kLn) {
+                float bf[4];
+                unpack16<float>(bv[u], bf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (s[u][e] - mu) * rstd * wf[e] + bf[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = s[u][e] * rstd * wf[e];
+            }
+            store16(ro, off_o[u], pack16<float>(o));
+        }
+    }
+}
+
+template <int OP, int G, int U>
+hipError_t launch_group_fwd(const DynFwdArgs& a, hipStream_t stream) {
+    constexpr int R = kGroupBlock / G;
+    const int64_t sets = (a.rows + R - 1) / R;
+    const int64_t grid = sets < kStreamMaxGrid ? sets : kStreamMaxGrid;
+    hipLaunchKernelGGL((group_fwd_kernel<OP, G, U>), dim3((unsigned)grid), dim3(kGroupBlock), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

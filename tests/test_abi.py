@@ -124,6 +124,10 @@ def test_runtime_hidden_shapes():
     assert rn.select_config("rmsnorm_fwd", 8192, 128, cu_count=256).rows_per_block == 16
     assert rn.select_config("rmsnorm_fwd", 1 << 17, 128, cu_count=256).threads_per_row == 16
     assert rn.select_config("layernorm_fwd", 2048, 1000, cu_count=256).threads_per_row == 64
+    # LayerNorm below a wave: about three accesses a lane, four rows a lane group
+    assert rn.select_config("layernorm_fwd", 1 << 15, 512, cu_count=256) == rn.Cfg(32, 32, 0, 8)
+    assert rn.select_config("layernorm_fwd", 1 << 17, 128, cu_count=256) == rn.Cfg(8, 128, 0, 8)
+    assert rn.select_config("layernorm_fwd", 1 << 14, 768, cu_count=256) == rn.Cfg(32, 8, 0, 8)
     assert rn.select_config("rmsnorm_bwd", 8192, 128).threads_per_row == 16
     assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 256
     assert rn.select_config("layernorm_bwd", 8192, 1000).threads_per_row == 128

@@ -43,10 +43,13 @@ def walkers(rows, h):
 
 
 # ------------------------------------------------------------------ forward
-# one shape per launch-shape bucket of the fp32 forward (lanes x accesses held:
-# up to 1024, 2048, 4096, 8192, 16384 columns, then 1024 lanes x 8 / x 4)
-FWD_SHAPES = [(4, 1), (12, 37), (1024, 300), (2048, 45), (4096, 64), (4100, 37), (8192, 11),
-              (16384, 9), (16388, 5), (32768, 7), (65536, 17), (100004, 3), (1 << 20, 2)]
+# one shape per launch-shape bucket of the fp32 forward (rows of up to 512
+# columns several to a wave; then lanes x accesses held: up to 1024, 2048,
+# 4096, 8192, 16384 columns, then 1024 lanes x 8 / x 4)
+FWD_SHAPES = [(4, 1), (12, 37), (32, 1000), (64, 517), (100, 33), (128, 300), (200, 77),
+              (256, 64), (500, 33), (512, 19), (516, 7), (1024, 300), (2048, 45), (4096, 64),
+              (4100, 37), (8192, 11), (16384, 9), (16388, 5), (32768, 7), (65536, 17),
+              (100004, 3), (1 << 20, 2)]
 
 
 def check_fused(inp, out, res, h, what):
