@@ -987,7 +987,8 @@ def runtime_hidden_ops(torch, rn, wl, dev, stream, reps, cpu_seconds=None):
 def streamed_ops(torch, rn, wl, dev, stream, reps):
     """Rows no workgroup holds on chip (the streamed kernels, each row read
     twice): fused add + RMSNorm 2048 x 131072, LayerNorm forward 2048 x 65536,
-    LayerNorm and RMSNorm backward 4096 x 65536; time per launch over cold
+    LayerNorm and RMSNorm backward 4096 x 65536; and RMSNorm 2048 x 98312 on
+    the LDS-staged forward (registers and LDS, read once); time per launch over cold
     buffer sets, algorithmic bytes as for the on-chip kernels (one read and
     one write of each matrix)."""
     out = []
@@ -1019,6 +1020,20 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
         for j in range(n)], reps)
     out.append(_op_rec("layernorm_fwd", rows, h, (4 * h + 8) * rows + 4 * h, t,
                        note="streamed kernel: the row is read twice"))
+    del xs, ys, x0
+    h, rows = 98312, 2048
+    i = wl.rmsnorm_inputs(rows, h, seed=0)
+    n = _n_sets(2 * rows * h * 2)
+    x0 = wl.to_device_bf16(i["x"], dev)
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    ys = [torch.empty_like(x0) for _ in range(n)]
+    w = wl.to_device_bf16(i["w"], dev)
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.rmsnorm_fwd(xs[j], w, i["eps"], out=ys[j], stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("rmsnorm_fwd", rows, h, 4 * h * rows + 2 * h, t,
+                       note="LDS-staged kernel: 5 accesses a lane in registers, the rest "
+                            "in LDS, the row read once"))
     del xs, ys, x0
     h, rows = 65536, 4096
     i = wl.layernorm_bwd_inputs(rows, h, seed=0)
@@ -1354,6 +1369,8 @@ STREAM_F32_WORKLOADS = [
      lambda r, h: 8 * h * r + 2 * h),
     ("layernorm_fwd", 2048, 65536, "stream_fwd_kernel<unsignedshort,2,1024,4>",
      lambda r, h: (4 * h + 8) * r + 4 * h),
+    ("rmsnorm_fwd (LDS-staged)", 2048, 98312, "stage_fwd_kernel<unsignedshort,1,5,9>",
+     lambda r, h: 4 * h * r + 2 * h),
     ("layernorm_bwd (row sums)", 4096, 65536, "stream_bwd_stats_kernel<unsignedshort,true>",
      lambda r, h: (4 * h + 8) * r + 2 * h),
     ("layernorm_bwd (column tiles)", 4096, 65536,

@@ -25,8 +25,11 @@
  *     kernels that read the row twice: forward, one pass for the statistic
  *     and one, mostly from the Infinity Cache, to normalize; backward, a
  *     per-row reduction kernel, then workgroups over 16384-column tiles
- *     (the two reductions per row go to the workspace).  Wider rows with
- *     narrower accesses are unsupported.  The row-split forward entry
+ *     (the two reductions per row go to the workspace).  Forward rows that
+ *     registers and LDS hold together are read once instead (the fused op
+ *     up to 81920, RMSNorm from 69912 up to 114688: the rest of the row
+ *     past the registers staged in LDS).  Wider rows with narrower accesses
+ *     are unsupported.  The row-split forward entry
  *     points below spread few wide rows over several workgroups instead.
  * The library picks the family; the arithmetic and results (within rounding)
  * are the same.  The `_f32` entry points take fp32 activations, weights and
@@ -493,7 +496,8 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * rows to a workgroup; wider rows take one workgroup each (64 to 1024
  * lanes), which holds up to 16384 values of the row in registers between
  * the statistic and the normalize step (32768 for the fused op and RMSNorm)
- * and reads any rest again.
+ * and reads any rest again, except fused rows of 34956 ... 40960 and
+ * RMSNorm rows of 34956 ... 69632, whose rest is staged in LDS (read once).
  * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
  * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
  * (read once); wider rows take a per-row reduction kernel, then 512-lane

@@ -13,6 +13,7 @@
 
 #include "launch.hpp"
 #include "norm.h"
+#include "stream_select.hpp"
 
 using namespace rownorm;
 
@@ -1683,7 +1684,13 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         char inst[96];
         const FwdEntry* ring =
             c.grid > 0 ? ring_entry(op, hidden, c.threads_per_row, rows, c.grid) : nullptr;
-        if (streamed) {
+        const int sop = op == NORM_OP_FUSED_ADD_RMSNORM ? kSplitFused
+                        : op == NORM_OP_LAYERNORM_FWD   ? kSplitLn
+                                                        : kSplitRms;
+        if (streamed && stage_fwd_holds(sop, false, hidden)) {
+            std::snprintf(inst, sizeof inst,
+                          "stage_fwd_kernel<%s> (registers and LDS, the row read once)", kern);
+        } else if (streamed) {
             std::snprintf(inst, sizeof inst, "stream_fwd_kernel<%s> (two passes over the row)",
                           kern);
         } else if (dyn) {
@@ -1711,15 +1718,28 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         }
         const int block = dyn ? dyn_block_size(c.threads_per_row)
                               : c.threads_per_row * c.rows_per_block;
-        if (streamed)
+        if (streamed && stage_fwd_holds(sop, false, hidden)) {
+            const StageShape st = stage_fwd_shape(sop, false);
             n = std::snprintf(tmp, sizeof tmp,
                               "%s rows=%lld hidden=%lld: %s (%d lanes per row, 1 rows per "
-                              "workgroup of %d, %lld 16-byte accesses per lane in passes of %d), "
-                              "grid %lld",
+                              "workgroup of %d, %lld 16-byte accesses per lane: up to %d in "
+                              "registers, up to %d in LDS), grid %lld",
                               kNames[op], (long long)rows, (long long)hidden, inst,
                               c.threads_per_row, c.threads_per_row,
-                              (long long)ceil_div(hidden / 8, c.threads_per_row), 4,
+                              (long long)ceil_div(hidden / 8, c.threads_per_row), st.u, st.l,
+                              (long long)std::min<int64_t>(rows, kStageGridRows));
+        } else if (streamed) {
+            const StreamFwdShape sh = stream_fwd_shape(false, sop == kSplitLn, sop == kSplitRms,
+                                                       hidden);
+            n = std::snprintf(tmp, sizeof tmp,
+                              "%s rows=%lld hidden=%lld: %s (%d lanes per row, 1 rows per "
+                              "workgroup of %d, %lld 16-byte accesses per lane, the first %d "
+                              "kept in registers), grid %lld",
+                              kNames[op], (long long)rows, (long long)hidden, inst,
+                              c.threads_per_row, c.threads_per_row,
+                              (long long)ceil_div(hidden / 8, c.threads_per_row), sh.unroll,
                               (long long)std::min<int64_t>(rows, kStreamMaxGrid));
+        }
         else if (ring)
             n = std::snprintf(tmp, sizeof tmp,
                               "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d 16-byte "

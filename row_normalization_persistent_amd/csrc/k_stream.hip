@@ -4,6 +4,7 @@
 #include <type_traits>
 
 #include "kernels_stream.hpp"
+#include "stream_select.hpp"
 
 namespace rownorm {
 
@@ -54,6 +55,21 @@ hipError_t group_fwd_f32(int64_t hidden, const DynFwdArgs& a, hipStream_t stream
 // columns than the one-row streamed launch)
 constexpr int64_t kGroupFwdMaxHidden = 1024;
 
+template <typename E, int OP>
+hipError_t launch_stage_op(const DynFwdArgs& a, hipStream_t stream) {
+    constexpr StageShape sh = stage_fwd_shape(OP, std::is_same_v<E, float>);
+    return launch_stage_fwd<E, OP, sh.u, sh.l>(a, stream);
+}
+
+template <typename E>
+hipError_t launch_stage_by_op(int op, const DynFwdArgs& a, hipStream_t stream) {
+    switch (op) {
+        case kSplitFused: return launch_stage_op<E, kSplitFused>(a, stream);
+        case kSplitRms: return launch_stage_op<E, kSplitRms>(a, stream);
+        default: return hipErrorInvalidValue;  // LayerNorm streams
+    }
+}
+
 hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t stream) {
     if (f32 && a.hidden <= kGroupFwdMaxHidden) {
         switch (op) {
@@ -63,6 +79,9 @@ hipError_t launch_stream_fwd(int op, bool f32, const DynFwdArgs& a, hipStream_t 
             default: return hipErrorInvalidValue;
         }
     }
+    if (stage_fwd_holds(op, f32, a.hidden))
+        return f32 ? launch_stage_by_op<float>(op, a, stream)
+                   : launch_stage_by_op<uint16_t>(op, a, stream);
     const StreamFwdShape sh = stream_fwd_shape(f32, op == kSplitLn, op == kSplitRms, a.hidden);
     switch (op) {
         case kSplitFused:

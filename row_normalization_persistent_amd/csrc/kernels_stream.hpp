@@ -47,6 +47,8 @@
 
 #include "dyn_common.hpp"
 #include "launch.hpp"
+#include "lds_stage.hpp"
+#include "stream_select.hpp"
 
 namespace rownorm {
 
@@ -237,6 +239,181 @@ hipError_t launch_stream_fwd_op(const DynFwdArgs& a, hipStream_t stream) {
     const int64_t grid = a.rows < kStreamMaxGrid ? a.rows : kStreamMaxGrid;
     hipLaunchKernelGGL((stream_fwd_kernel<E, OP, T, U>), dim3((unsigned)grid), dim3(T), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+// ---- forward, rows held in registers and LDS ----------------------------------------
+// For rows a little too wide for the registers (the LDS-staged persistent
+// buffer of "TMA inner persistent scheduler", description summary): lane t of
+// the 1024 holds accesses b*1024 + t, the first U in registers (as in
+// stream_fwd_kernel) and the next L in LDS slots, which buffer loads with the
+// LDS bit fill straight from HBM (x, and r for the fused op: 16 KiB a slot and
+// matrix); rows of up to (U + L) * 1024 accesses are read once.  One row at a
+// time (the LDS holds one): its slot loads, then its register loads, go out
+// at the start; the first pass reads slot k once at most as many loads are
+// outstanding as were issued after k's (the later slots' and the register
+// accesses; the buffer-to-LDS loads are invisible to the compiler, whose own
+// waits for the register accesses are exact because those go out last); the
+// weights (and LayerNorm's bias) of the whole row go out before the row's
+// reduction and land during it.  Measured against handing each slot to the
+// next row's load during the second pass (the walk pipelined by access, as
+// the LDS-staged backward does): that was 2-18 % slower at every shape.
+template <typename E, int OP>
+__device__ __forceinline__ void stage_norm_access(const u32x4& xv, const u32x4& rv,
+                                                  const u32x4& wv, const u32x4& bv, rsrc_t rr,
+                                                  rsrc_t ro, int off, float mu, float rstd) {
+    constexpr int EP = Elems<E>::kPer;
+    float s[EP], wf[EP], o[EP];
+    unpack16<E>(xv, s);
+    unpack16<E>(wv, wf);
+    if constexpr (OP == kSplitFused) {
+        float rf[EP];
+        unpack16<E>(rv, rf);
+#pragma unroll
+        for (int e = 0; e < EP; ++e) s[e] += rf[e];
+        store16(rr, off, pack16<E>(s));
+    }
+    if constexpr (OP == kSplitLn) {
+        float bf[EP];
+        unpack16<E>(bv, bf);
+#pragma unroll
+        for (int e = 0; e < EP; ++e) o[e] = (s[e] - mu) * rstd * wf[e] + bf[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < EP; ++e) o[e] = s[e] * rstd * wf[e];
+    }
+    store16(ro, off, pack16<E>(o));
+}
+
+template <typename E, int OP, int U, int L>
+__global__ __launch_bounds__(kStreamFwdLanes) void stage_fwd_kernel(DynFwdArgs a) {
+    constexpr int T = kStreamFwdLanes;
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
+    constexpr bool kFused = OP == kSplitFused, kLn = OP == kSplitLn;
+    constexpr int M = kFused ? 2 : 1;  // matrices staged an access: x (and r)
+    constexpr int NB = U + L;          // accesses a lane
+    static_assert(M * L * T * 16 + 4 * (T / kWave) * 4 <= 160 * 1024, "LDS of one workgroup");
+    __shared__ u32x4 st[L * M * T];  // slot (k, m) of lane t: st[(k M + m) T + t]
+    __shared__ float red[4 * (T / kWave)];
+    const int lane = threadIdx.x;
+    const int h = a.hidden;
+    const int n_acc = h / EP;
+    const float inv_h = 1.0f / (float)h;
+    const rsrc_t rw = row_rsrc_ld(a.weight, 0, 1, 0, h * ES);
+    rsrc_t rb = rw;
+    if constexpr (kLn) rb = row_rsrc_ld(a.bias, 0, 1, 0, h * ES);
+    // LDS byte address of this wave's 64 slots of slot (0, 0), wave uniform
+    const uint32_t st_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)st +
+        (uint32_t)__builtin_amdgcn_readfirstlane(lane & ~(kWave - 1)) * 16u;
+    // A lane's slots past the row's end (the same for every row) hold zeros
+    // for the whole walk, so that they add nothing to the row's sums: a
+    // buffer load past its range returns zeros, whether or not it then writes
+    // its LDS slot.
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        if ((U + k) * T + lane >= n_acc) {
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int m = 0; m < M; ++m) st[(k * M + m) * T + lane] = zero;
+        }
+    }
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t r = opaque_row(row);
+        const int t = opaque_lane(lane);
+        const rsrc_t rx = row_rsrc_ld(a.x, r, a.rows, a.ld_x * ES, h * ES);
+        const rsrc_t ro = row_rsrc_ld(a.out, r, a.rows, a.ld_out * ES, h * ES);
+        rsrc_t rr = rx;
+        if constexpr (kFused) rr = row_rsrc_ld(a.residual, r, a.rows, a.ld_res * ES, h * ES);
+        // the row's staged accesses, slot by slot, then its register accesses
+        {
+            const desc4 dx = row_desc(a.x, r, a.rows, a.ld_x * ES, h * ES);
+            desc4 dr = dx;
+            if constexpr (kFused) dr = row_desc(a.residual, r, a.rows, a.ld_res * ES, h * ES);
+#pragma unroll
+            for (int k = 0; k < L; ++k) {
+                lds_load16(dx, ((U + k) * T + t) * 16, st_lds + (uint32_t)(k * M) * T * 16u);
+                if constexpr (kFused)
+                    lds_load16(dr, ((U + k) * T + t) * 16,
+                               st_lds + (uint32_t)(k * M + 1) * T * 16u);
+            }
+        }
+        u32x4 x0[U], r0[kFused ? U : 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x0[u] = load16<kCachePolicyNT>(rx, (u * T + t) * 16);
+            if constexpr (kFused) r0[u] = load16<kCachePolicyNT>(rr, (u * T + t) * 16);
+        }
+
+        // pass 1: the staged accesses as they land (each slot's M loads are
+        // followed by M per later slot and the M U register loads), then the
+        // registers, pinned below the slots so that no use of them, and so no
+        // wait for them, moves above
+        float p0 = 0.0f, p1 = 0.0f, n_l = 0.0f;
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            wait_vm_at_most(M * (L - 1 - k) + M * U);
+            u32x4 xv[1] = {st[(k * M) * T + t]};
+            u32x4 rv[1] = {kFused ? st[(k * M + 1) * T + t] : xv[0]};
+            stream_stat_step<E, OP, 1, T>(xv, rv, (U + k) * T + t, n_acc, p0, p1, n_l);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            asm volatile("" : "+v"(x0[u]));
+            if constexpr (kFused) asm volatile("" : "+v"(r0[u]));
+        }
+        stream_stat_step<E, OP, U, T>(x0, r0, t, n_acc, p0, p1, n_l);
+        // the weights (and bias) of the whole row, packed, landing during the
+        // reduction
+        u32x4 wv[NB], bv[kLn ? NB : 1];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            wv[b] = load16<0>(rw, (b * T + t) * 16);
+            if constexpr (kLn) bv[b] = load16<0>(rb, (b * T + t) * 16);
+        }
+        float mu = 0.0f, rstd;
+        if constexpr (kLn) {
+            const float tot = row_sum<T>(p0, red, lane);
+            mu = tot * inv_h;
+            const float d = n_l > 0.0f ? p0 / n_l - mu : 0.0f;
+            const float m2 = row_sum<T>(p1 + n_l * d * d, red + (T / kWave), lane);
+            rstd = fast_rsqrt(m2 * inv_h + a.eps);
+            if (lane == 0 && a.mean != nullptr) {
+                a.mean[r] = mu;
+                a.rstd[r] = rstd;
+            }
+        } else {
+            rstd = fast_rsqrt(row_sum<T>(p0, red, lane) * inv_h + a.eps);
+        }
+
+        // pass 2: the register accesses, then the slots
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            stage_norm_access<E, OP>(x0[u], r0[kFused ? u : 0], wv[u], bv[kLn ? u : 0], rr, ro,
+                                     (u * T + t) * 16, mu, rstd);
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+            const u32x4 xv = st[(k * M) * T + t];
+            const u32x4 rv = kFused ? st[(k * M + 1) * T + t] : xv;
+            stage_norm_access<E, OP>(xv, rv, wv[U + k], bv[kLn ? U + k : 0], rr, ro,
+                                     ((U + k) * T + t) * 16, mu, rstd);
+        }
+        // this wave's reads of its slots are done before the next row's loads
+        // overwrite them; the next row's first reduction must not overwrite
+        // slots still being read
+        wait_lds();
+        __syncthreads();
+    }
+}
+
+template <typename E, int OP, int U, int L>
+hipError_t launch_stage_fwd(const DynFwdArgs& a, hipStream_t stream) {
+    const int64_t grid = a.rows < kStageGridRows ? a.rows : kStageGridRows;
+    if (grid > 0)
+        hipLaunchKernelGGL((stage_fwd_kernel<E, OP, U, L>), dim3((unsigned)grid),
+                           dim3(kStreamFwdLanes), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,0 +1,53 @@
+// Which streamed-row forward kernel takes a row (host side, shared by the
+// launcher and the launch description).
+#pragma once
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace rownorm {
+
+// Rows that the LDS-staged forward (stage_fwd_kernel) holds: U register and
+// L LDS accesses a lane of 1024 (16 KiB of LDS a slot and staged matrix, x
+// and for the fused op r; the weights of all U + L accesses sit in registers
+// during the second pass, which bounds U + L: bf16 RMSNorm spills at 6 + 9).
+// LayerNorm has none: staged (2 + 9 accesses) it ran 5-20 % slower than the
+// streamed kernel's second read from the Infinity Cache.
+struct StageShape {
+    int u, l;
+};
+constexpr StageShape stage_fwd_shape(int op, bool f32) {
+    if (op == kSplitFused) return {6, 4};
+    if (op == kSplitRms) return {f32 ? 8 : 5, 9};
+    return {0, 0};
+}
+
+// Workgroups of the staged kernel: one a compute unit of the largest part (its
+// LDS holds one row), each walking rows blockIdx.x, + 256, ...
+constexpr int64_t kStageGridRows = 256;
+
+#ifndef ROWNORM_STAGE_FWD
+#define ROWNORM_STAGE_FWD 1
+#endif
+
+// The staged kernel takes the rows of which the streamed kernel would read
+// at least 1/16 twice (the accesses past those its lanes keep in registers)
+// and that registers and LDS hold whole.  Measured on MI355X (graph-timed,
+// cold buffers, alternating processes): bf16 fused 2048 x 73736 252.5 ->
+// 249.5 us, 2048 x 81920 255.2 -> 252.5; bf16 RMSNorm 4096 x 73728 227.3 ->
+// 217.4, 2048 x 98312 165.6 -> 159.1, 2048 x 114688 179.9 -> 170.9; fp32
+// fused 4096 x 40960 493.2 -> 475.3, fp32 RMSNorm 2048 x 65536 202.4 -> 191.4;
+// level where the second read is short (bf16 RMSNorm 4096 x 69632, 11 of
+// 12 accesses a lane in registers), 6 % slower where it is one access in 9
+// (4096 x 65544).  op: kSplitFused / kSplitRms / kSplitLn.
+constexpr bool stage_fwd_holds(int op, bool f32, int64_t hidden) {
+    const StreamFwdShape sh = stream_fwd_shape(f32, op == kSplitLn, op == kSplitRms, hidden);
+    const StageShape st = stage_fwd_shape(op, f32);
+    const int64_t n_acc = hidden / (f32 ? 4 : 8);
+    const int64_t twice = n_acc - (int64_t)sh.lanes * sh.unroll;
+    return ROWNORM_STAGE_FWD && st.l > 0 && 16 * twice >= n_acc &&
+           n_acc <= (int64_t)kStreamFwdLanes * (st.u + st.l);
+}
+
+}  // namespace rownorm

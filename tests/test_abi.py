@@ -104,7 +104,8 @@ def test_runtime_hidden_shapes():
                   ("rmsnorm_bwd", 32768 + 8), ("fused_add_rmsnorm_bwd", 1 << 20)):
         c = rn.select_config(op, 64, h, cu_count=256)
         assert c.vector_elems == 8 and c.threads_per_row == (512 if "bwd" in op else 1024), op
-        assert "stream_" in rn.describe_config(op, 64, h, cu_count=256)
+        d = rn.describe_config(op, 64, h, cu_count=256)
+        assert "stream_" in d or "stage_fwd_kernel" in d, d
     for op, h in (("layernorm_fwd", 49152 + 4), ("rmsnorm_fwd", 65536 + 2),
                   ("layernorm_bwd", 32768 + 4), ("rmsnorm_bwd", 8193),
                   ("fused_add_rmsnorm", (1 << 20) + 8)):
@@ -132,6 +133,23 @@ def test_runtime_hidden_shapes():
     assert rn.select_config("layernorm_bwd", 8192, 5120).threads_per_row == 256
     assert rn.select_config("layernorm_bwd", 8192, 1000).threads_per_row == 128
     assert rn.select_config("rmsnorm_bwd", 64, 16376).threads_per_row == 512
+
+
+def test_describe_staged_forward_widths():
+    """Fused add + RMSNorm and RMSNorm rows past the on-chip forward kernels go
+    to the LDS-staged kernel while registers and LDS hold them whole, to the
+    streamed kernel past that; LayerNorm rows always stream."""
+    for op, first, last in (("fused_add_rmsnorm", 65544, 81920), ("rmsnorm_fwd", 69912, 114688)):
+        for h in (first, last):
+            d = rn.describe_config(op, 300, h, cu_count=256)
+            assert "stage_fwd_kernel" in d and d.endswith("grid 256"), d
+        assert "stage_fwd_kernel" in rn.describe_config(op, 7, first, cu_count=256)
+        assert rn.describe_config(op, 7, first, cu_count=256).endswith("grid 7")
+        assert "stream_fwd_kernel" in rn.describe_config(op, 300, last + 8, cu_count=256)
+    # RMSNorm rows that the streamed kernel reads once but for under 1/16
+    assert "stream_fwd_kernel" in rn.describe_config("rmsnorm_fwd", 300, 69904, cu_count=256)
+    for h in (49160, 65536, 90112, 131072):
+        assert "stream_fwd_kernel" in rn.describe_config("layernorm_fwd", 300, h, cu_count=256)
 
 
 def test_select_config_small_batches_spread_rows_over_more_lanes():

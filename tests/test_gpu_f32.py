@@ -43,13 +43,16 @@ def walkers(rows, h):
 
 
 # ------------------------------------------------------------------ forward
-# one shape per launch-shape bucket of the fp32 forward (rows of up to 512
-# columns several to a wave; then lanes x accesses held: up to 1024, 2048,
-# 4096, 8192, 16384 columns, then 1024 lanes x 8 / x 4)
+# one shape per launch-shape bucket of the fp32 forward (rows of up to 1024
+# columns several to a wave; then lanes x accesses held: up to 2048, 4096,
+# 8192, 16384 columns, then 1024 lanes x 8 / x 4; the LDS-staged rows past
+# those: fused 34956-40960, RMSNorm 34956-69632, with walks of two rows a
+# workgroup)
 FWD_SHAPES = [(4, 1), (12, 37), (32, 1000), (64, 517), (100, 33), (128, 300), (200, 77),
               (256, 64), (500, 33), (512, 19), (516, 7), (1024, 300), (2048, 45), (4096, 64),
-              (4100, 37), (8192, 11), (16384, 9), (16388, 5), (32768, 7), (65536, 17),
-              (100004, 3), (1 << 20, 2)]
+              (4100, 37), (8192, 11), (16384, 9), (16388, 5), (32768, 7), (32772, 5),
+              (34956, 4), (40960, 300), (45056, 257), (65536, 17), (69632, 3), (100004, 3),
+              (1 << 20, 2)]
 
 
 def check_fused(inp, out, res, h, what):

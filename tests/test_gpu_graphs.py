@@ -26,11 +26,12 @@ def bits(t):
 
 
 @pytest.mark.parametrize("hidden,rows", [(4096, 300), (5120, 300), (100, 300), (16384, 600),
-                                         (40000, 64), (65544, 40)])
+                                         (40000, 64), (65544, 300), (131080, 6)])
 def test_graph_replays_match_eager(hidden, rows):
     """(16384, 600): LayerNorm and RMSNorm forward on their ring kernels;
     (40000, 64): the backward on the streamed kernels (row reductions, column
-    tiles); (65544, 40): every operation on the streamed kernels."""
+    tiles); (65544, 300): the forward on the LDS-staged kernel (walks of two
+    rows), the backward streamed; (131080, 6): every operation streamed."""
     f = wl.fused_inputs(rows, hidden, seed=31)
     b = wl.rmsnorm_bwd_inputs(rows, hidden, seed=32)
     lnw = wl.layernorm_fwd_inputs(rows, hidden, seed=33)

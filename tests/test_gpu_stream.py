@@ -1,6 +1,8 @@
 """GPU parity of the streamed kernels (rows wider than one workgroup's
-registers and LDS hold: forward past 65536 columns, LayerNorm forward past
-49152, the backward operations past 32768; 16-byte rows up to 2^20 columns)
+registers hold: forward past 65536 columns, LayerNorm forward past 49152,
+the backward operations past 32768; 16-byte rows up to 2^20 columns) and of
+the LDS-staged forward (the fused op's and RMSNorm's rows of those that
+registers and LDS hold)
 against the CPU oracle, through the C ABI: the library's own choice over
 ragged widths and row counts, strided and in-place rows, explicit row-walker
 counts of the backward, bitwise run-to-run determinism, the row-split entry
@@ -95,14 +97,54 @@ def run_fwd(op, inp, ld=None, in_place=False, split=None):
 
 @pytest.mark.parametrize("op,h,rows", FWD_CASES)
 def test_stream_forward(op, h, rows):
-    assert "stream_fwd_kernel" in rn.describe_config(op, rows, h)
+    d = rn.describe_config(op, rows, h)
+    assert "stream_fwd_kernel" in d or "stage_fwd_kernel" in d, d
     inp = fwd_inputs(op, rows, h, seed=h + rows)
     check_fwd(op, inp, run_fwd(op, inp), f"{op} {rows}x{h}")
 
 
+# The LDS-staged forward (fused add + RMSNorm and RMSNorm rows past the
+# on-chip kernels that registers and LDS hold whole): each at its first width
+# (RMSNorm's: where the streamed kernel would read 1/16 of the row twice), a
+# ragged width and its widest, over one row, fewer rows than workgroups,
+# exactly as many, and walks of two and three rows; the widths just outside
+# the band go to the streamed kernel.
+STAGE_CASES = [("fused_add_rmsnorm", 65544, 300), ("fused_add_rmsnorm", 73736, 1),
+               ("fused_add_rmsnorm", 81920, 600), ("rmsnorm_fwd", 69912, 257),
+               ("rmsnorm_fwd", 98312, 37), ("rmsnorm_fwd", 114688, 513),
+               ("rmsnorm_fwd", 73736, 256)]
+
+
+@pytest.mark.parametrize("op,h,rows", STAGE_CASES)
+def test_staged_forward(op, h, rows):
+    assert "stage_fwd_kernel" in rn.describe_config(op, rows, h)
+    inp = fwd_inputs(op, rows, h, seed=2 * h + rows)
+    check_fwd(op, inp, run_fwd(op, inp), f"{op} staged {rows}x{h}")
+
+
+@pytest.mark.parametrize("op,h", [("fused_add_rmsnorm", 81928), ("rmsnorm_fwd", 114696),
+                                  ("rmsnorm_fwd", 69904)])
+def test_first_width_past_the_staged_forward(op, h):
+    assert "stream_fwd_kernel" in rn.describe_config(op, 300, h)
+    inp = fwd_inputs(op, 300, h, seed=h)
+    check_fwd(op, inp, run_fwd(op, inp), f"{op} streamed 300x{h}")
+
+
+@pytest.mark.parametrize("op", ["fused_add_rmsnorm", "rmsnorm_fwd"])
+def test_staged_forward_bitwise_run_to_run(op):
+    """Outputs of two calls are bitwise equal (no order-dependent arithmetic),
+    over a walk of several rows a workgroup."""
+    h, rows = 73736, 700
+    inp = fwd_inputs(op, rows, h, seed=11)
+    a, b = run_fwd(op, inp), run_fwd(op, inp)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), f"{op} {k}"
+
+
 @pytest.mark.parametrize("op", ["fused_add_rmsnorm", "rmsnorm_fwd", "layernorm_fwd"])
-def test_stream_forward_strided_and_in_place(op):
-    h, rows = 65536 + 64, 45
+@pytest.mark.parametrize("h", [65536 + 64, 131072 + 64])  # LDS-staged (not LayerNorm), streamed
+def test_stream_forward_strided_and_in_place(op, h):
+    rows = 45 if h < 100000 else 9
     inp = fwd_inputs(op, rows, h, seed=3)
     check_fwd(op, inp, run_fwd(op, inp, ld=h + 136), f"{op} strided")
     check_fwd(op, inp, run_fwd(op, inp, in_place=True), f"{op} in place")
