@@ -54,10 +54,11 @@ namespace rownorm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The first read of a row (the forward's statistic pass, the backward's
-// reduction kernel) takes the default cache policy, so the row stays in the
-// Infinity Cache for the second read, which is the row's last use and
-// streams (non-temporal).  Measured on MI355X against non-temporal first reads
+// The first read of the part of a row that is read twice (the forward's
+// statistic pass past the accesses it keeps in registers, the backward's
+// reduction kernel) takes the default cache policy, so that part stays in
+// the Infinity Cache for the second read, which is its last use and streams
+// (non-temporal).  Measured on MI355X against non-temporal first reads
 // (graph-timed over cold buffers, A/B in one process): fused add + RMSNorm
 // 2048 x 131072 560 -> 477 us, LayerNorm forward 2048 x 65536 155 -> 114 us,
 // LayerNorm backward 512 x 65536 78 -> 70 us and 4096 x 65536 468 -> 455 us;
@@ -71,6 +72,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kStreamUnroll = ROWNORM_STREAM_UNROLL;  // 16-byte accesses in flight per lane and matrix
 constexpr int kStreamPass1 = ROWNORM_STREAM_P1_POLICY;  // cache policy of the first read
+// The forward's accesses kept in registers from the first pass to the second
+// are never read again: non-temporal, so that they do not take Infinity Cache
+// lines from the rest of the row (measured on MI355X against the default
+// policy, graph-timed over cold buffers, alternating processes: fp32 fused
+// 8192 x 4096 100.8 -> 91.5 us and 4096 x 8192 107.6 -> 96.6, fp32 RMSNorm
+// 4096 x 16384 92.4 -> 87.9, fp32 LayerNorm 2048 x 16384 51.5 -> 49.2; bf16
+// fused 2048 x 131072 441 -> 432, LayerNorm 2048 x 65536 110.3 -> 106.9).
+#ifndef ROWNORM_STREAM_KEPT_NT
+#define ROWNORM_STREAM_KEPT_NT 1
+#endif
+constexpr int kStreamKept = ROWNORM_STREAM_KEPT_NT ? kCachePolicyNT : kStreamPass1;
 
 template <int Aux>
 __device__ __forceinline__ u32x4 load16(rsrc_t r, int byte_off) {
@@ -189,8 +201,8 @@ __global__ __launch_bounds__(T) void stream_fwd_kernel(DynFwdArgs a) {
         u32x4 x0[U], r0[kFused ? U : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            x0[u] = load16<kStreamPass1>(rx, (lane + u * T) * 16);
-            if constexpr (kFused) r0[u] = load16<kStreamPass1>(rr, (lane + u * T) * 16);
+            x0[u] = load16<kStreamKept>(rx, (lane + u * T) * 16);
+            if constexpr (kFused) r0[u] = load16<kStreamKept>(rr, (lane + u * T) * 16);
         }
         stream_stat_step<E, OP, U, T>(x0, r0, lane, n_acc, p0, p1, n_l);
         for (int base = lane + U * T; base < n_acc; base += U * T) {
