@@ -269,7 +269,10 @@ hipError_t launch_stream_fwd_op(const DynFwdArgs& a, hipStream_t stream) {
 // weights (and LayerNorm's bias) of the whole row go out before the row's
 // reduction and land during it.  Measured against handing each slot to the
 // next row's load during the second pass (the walk pipelined by access, as
-// the LDS-staged backward does): that was 2-18 % slower at every shape.
+// the LDS-staged backward does): that was 2-18 % slower at every shape.  The
+// launcher takes this kernel for the fused op and RMSNorm only (the rows it
+// takes: stage_fwd_holds); LayerNorm's rows stream.  A lane's slots past the
+// row's end are zeroed once for the walk.
 template <typename E, int OP>
 __device__ __forceinline__ void stage_norm_access(const u32x4& xv, const u32x4& rv,
                                                   const u32x4& wv, const u32x4& bv, rsrc_t rr,

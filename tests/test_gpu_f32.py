@@ -97,7 +97,7 @@ def test_layernorm_fwd_f32(h, rows):
     check_ln_fwd(inp, host(y), host(mean), host(rstd), h, f"layernorm f32 {rows}x{h}")
 
 
-@pytest.mark.parametrize("h", [4096, 20000])
+@pytest.mark.parametrize("h", [512, 4096, 20000, 40960])  # group, streamed, streamed, LDS-staged
 def test_forward_f32_in_place_and_without_stats(h):
     rows = 19
     inp = wl.fused_inputs(rows, h, seed=5, f32=True)
