@@ -34,8 +34,10 @@
  * The library picks the family; the arithmetic and results (within rounding)
  * are the same.  The `_f32` entry points take fp32 activations, weights and
  * gradients instead (contiguous rows, hidden a multiple of 4 up to 2^20):
- * the streamed kernels at every width, and for backward rows of 8196 ...
- * 16384 columns the LDS-staged kernel.
+ * rows of up to 1024 columns several to a wave, fused and RMSNorm forward
+ * rows of 34956 ... 40960 / 69632 columns staged partly in LDS, backward
+ * rows of 8196 ... 16384 columns staged in LDS, the streamed kernels
+ * everywhere else.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
