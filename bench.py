@@ -1053,15 +1053,15 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
                                       dweight=dw, dbias=db, workspace=ws, stream=stream))
         for j in range(n)], reps)
     out.append(_op_rec("layernorm_bwd", rows, h, (6 * h + 8) * rows + 10 * h, t,
-                       note="streamed kernels: row reductions, then column tiles (x and dy "
-                            "read twice) + column reduce"))
+                       note="streamed kernels: column tiles exchanging partial row sums "
+                            "(x and dy read once) + column reduce"))
     t = graph_time_per_launch(torch, stream, [
         (lambda j=j: rn.rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dx=dxs[j], dweight=dw,
                                     workspace=ws, stream=stream))
         for j in range(n)], reps)
     out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
-                       note="streamed kernels: row reductions, then column tiles (x and dy "
-                            "read twice) + column reduce"))
+                       note="streamed kernels: column tiles exchanging partial row sums "
+                            "(x and dy read once) + column reduce"))
     del xs, dys, dxs, x0, dy0, ws
     torch.cuda.synchronize()
     return out
@@ -1371,15 +1371,11 @@ STREAM_F32_WORKLOADS = [
      lambda r, h: (4 * h + 8) * r + 4 * h),
     ("rmsnorm_fwd (LDS-staged)", 2048, 98312, "stage_fwd_kernel<unsignedshort,1,5,9>",
      lambda r, h: 4 * h * r + 2 * h),
-    ("layernorm_bwd (row sums)", 4096, 65536, "stream_bwd_stats_kernel<unsignedshort,true>",
-     lambda r, h: (4 * h + 8) * r + 2 * h),
-    ("layernorm_bwd (column tiles)", 4096, 65536,
-     "stream_bwd_tile_kernel<unsignedshort,4,true,false,3,false>",
+    ("layernorm_bwd (tile exchange)", 4096, 65536,
+     "stream_bwd_tile_kernel<unsignedshort,2,true,false,3,false,true>",
      lambda r, h: (6 * h + 8) * r + 2 * h),
-    ("rmsnorm_bwd (row sums)", 4096, 65536, "stream_bwd_stats_kernel<unsignedshort,false>",
-     lambda r, h: 4 * h * r + 2 * h),
-    ("rmsnorm_bwd (column tiles)", 4096, 65536,
-     "stream_bwd_tile_kernel<unsignedshort,4,false,false,3,false>",
+    ("rmsnorm_bwd (tile exchange)", 4096, 65536,
+     "stream_bwd_tile_kernel<unsignedshort,2,false,false,3,false,true>",
      lambda r, h: 6 * h * r + 2 * h),
     ("fused_add_rmsnorm_f32", 8192, 4096, "stream_fwd_kernel<float,0,256,4>",
      lambda r, h: 16 * h * r + 4 * h),
@@ -1387,11 +1383,12 @@ STREAM_F32_WORKLOADS = [
      lambda r, h: 8 * h * r + 4 * h),
     ("layernorm_fwd_f32", 2048, 16384, "stream_fwd_kernel<float,2,512,8>",
      lambda r, h: (8 * h + 8) * r + 8 * h),
-    ("layernorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,true,false,4,true>",
+    ("layernorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,true,false,4,true,false>",
      lambda r, h: (12 * h + 8) * r + 4 * h),
-    ("rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,false,4,true>",
+    ("rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,false,4,true,false>",
      lambda r, h: 12 * h * r + 4 * h),
-    ("fused_add_rmsnorm_bwd_f32", 8192, 4096, "stream_bwd_tile_kernel<float,2,false,true,3,true>",
+    ("fused_add_rmsnorm_bwd_f32", 8192, 4096,
+     "stream_bwd_tile_kernel<float,2,false,true,3,true,false>",
      lambda r, h: 16 * h * r + 4 * h),
     ("layernorm_bwd_f32 (LDS-staged)", 4096, 16384, "norm_bwd_wide_kernel<float,8,true,false>",
      lambda r, h: (12 * h + 8) * r + 4 * h),

@@ -22,10 +22,10 @@
  *     scheduler", description summary, the shared-memory persistent
  *     buffer), 16384 with 8-byte accesses, 8192 otherwise.  Wider rows with
  *     16-byte accesses (hidden a multiple of 8, up to 2^20) run on streamed
- *     kernels that read the row twice: forward, one pass for the statistic
- *     and one, mostly from the Infinity Cache, to normalize; backward, a
- *     per-row reduction kernel, then workgroups over 16384-column tiles
- *     (the two reductions per row go to the workspace).  Forward rows that
+ *     kernels: forward, one pass for the statistic and one, mostly from the
+ *     Infinity Cache, to normalize (the row read twice); backward,
+ *     workgroups over 8192-column tiles that exchange each row's partial
+ *     sums through the workspace, so the row is read once.  Forward rows that
  *     registers and LDS hold together are read once instead (the fused op
  *     up to 81920, RMSNorm from 69912 up to 114688: the rest of the row
  *     past the registers staged in LDS).  Wider rows with narrower accesses
@@ -217,11 +217,12 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
  * NORM_ERROR_WORKSPACE when the launch's workspace
  * (norm_layernorm_bwd_workspace_bytes for contiguous rows: 2 * 4 * hidden
  * bytes, hidden rounded up to 64 off the compiled sizes, for each of its up
- * to 256 workgroups; rows past 32768 columns: for each of its up to
- * 255 / ceil(hidden / 16384) row walkers, plus 8 bytes a row) would exceed
+ * to 256 workgroups; rows past 32768 columns: the same for each of its up to
+ * 255 / ceil(hidden / 8192) row walkers, each with 128 bytes of partial-sum
+ * exchange slots per 8192-column tile) would exceed
  * NORM_NOALLOC_SCRATCH_BYTES: every hidden up to 16384 fits, rows of
  * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows), and
- * wider rows fit up to at least 16384 rows.
+ * wider rows fit at every row count.
  * NORM_ERROR_DEVICE when the
  * scratch array's address cannot be found on the current device.  All calls
  * on one device share its scratch array: calls that overlap in time on that
@@ -434,6 +435,17 @@ NORM_API norm_status norm_split_status(void* workspace, int32_t clear, uint32_t*
  * diagnostics of the give-up path. */
 NORM_API uint32_t norm_split_set_spin_limit(uint32_t polls);
 
+/* Polls a streamed-backward tile makes while it waits for the partial row
+ * sums of its row's other column tiles (default 2^14, about 16 ms; 0: never
+ * wait).  A tile that runs out stops waiting for the rest of its walk and
+ * reads the other tiles of each row itself instead, forming their partial
+ * sums exactly as their own workgroups do: the results are bitwise the same,
+ * only slower (two reads of those rows).  Process-wide, read when a call is
+ * enqueued; returns the previous value.  For tests and diagnostics of that
+ * path ("Llu/ln bwd", review thread: the grid-parallel inner reduction of
+ * the backward, here across a row's column tiles). */
+NORM_API uint32_t norm_bwd_set_spin_limit(uint32_t polls);
+
 /* The row split the library would choose for a forward op (fused, RMSNorm or
  * LayerNorm forward) on contiguous 16-byte-aligned rows with `cu_count` CUs
  * (<= 0: the current device): *split = workgroups per row (1: no split) and
@@ -502,9 +514,9 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * RMSNorm rows of 34956 ... 69632, whose rest is staged in LDS (read once).
  * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
  * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
- * (read once); wider rows take a per-row reduction kernel, then 512-lane
- * workgroups over 8192-column tiles (read twice); then the fixed-order column
- * reduce (column sums bitwise reproducible run to run).  workspace: at least
+ * (read once); wider rows take 512-lane workgroups over 8192-column tiles
+ * that exchange each row's partial sums (read once); then the fixed-order
+ * column reduce (column sums bitwise reproducible run to run).  workspace: at least
  * norm_bwd_workspace_bytes_f32(op, rows, hidden) bytes, contents ignored on
  * entry. */
 NORM_API norm_status norm_fused_add_rmsnorm_f32(float* out, float* residual, const float* x,
@@ -537,7 +549,8 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, c
  * NORM_OP_RMSNORM_BWD or NORM_OP_FUSED_ADD_RMSNORM_BWD): 4 * padded hidden
  * (hidden rounded up to 64) per partial-sum slab and output column sum, for
  * each row walker: min(rows, 256) of them at 8196 ... 16384 columns, else
- * max(1, min(rows, 255 / ceil(hidden / 8192))) plus 8 bytes a row.  Pure
+ * max(1, min(rows, 255 / ceil(hidden / 8192))), each with 128 bytes of
+ * partial-sum exchange slots per 8192-column tile.  Pure
  * host arithmetic; 0 for another op, an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);
 

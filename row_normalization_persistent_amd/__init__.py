@@ -186,6 +186,8 @@ def lib() -> ctypes.CDLL:
     L.norm_split_status.restype = ctypes.c_int
     L.norm_split_set_spin_limit.argtypes = [ctypes.c_uint32]
     L.norm_split_set_spin_limit.restype = ctypes.c_uint32
+    L.norm_bwd_set_spin_limit.argtypes = [ctypes.c_uint32]
+    L.norm_bwd_set_spin_limit.restype = ctypes.c_uint32
     L.norm_select_config.argtypes = [ctypes.c_int, _i64, _i64, ctypes.c_int32, _cfgp]
     L.norm_select_config.restype = ctypes.c_int
     L.norm_list_configs.argtypes = [ctypes.c_int, _i64, _cfgp, ctypes.c_int32]
@@ -334,6 +336,14 @@ def set_split_spin_limit(polls: int) -> int:
     0 makes every split workgroup give up at once).  Returns the previous
     value.  For tests and diagnostics."""
     return int(lib().norm_split_set_spin_limit(int(polls)))
+
+
+def set_bwd_spin_limit(polls: int) -> int:
+    """Polls a streamed-backward column tile makes waiting for its row's
+    other tiles before it re-reads them itself (process-wide; 0: never wait;
+    results are the same bits either way).  Returns the previous value.  For
+    tests and diagnostics."""
+    return int(lib().norm_bwd_set_spin_limit(int(polls)))
 
 
 def _split_check(workspace, stream, what: str) -> None:

@@ -17,6 +17,13 @@
 
 using namespace rownorm;
 
+namespace rownorm {
+// Polls a streamed-backward tile makes while it waits for its row's other
+// tiles; process-wide, changed only by norm_bwd_set_spin_limit.
+std::atomic<uint32_t> g_bwd_spin_limit{kBwdSpinLimit};
+uint32_t stream_bwd_spin_limit() { return g_bwd_spin_limit.load(std::memory_order_relaxed); }
+}  // namespace rownorm
+
 // Partial-sum slabs of norm_layernorm_bwd_noalloc (see current_scratch).
 static __device__ __align__(256) unsigned char scratch[NORM_NOALLOC_SCRATCH_BYTES];
 
@@ -283,7 +290,9 @@ int64_t max_bwd_hidden(norm_op op, int w) {
 // Column tiles of a streamed backward row, and its default row walkers: one
 // 512-lane workgroup per (walker, tile), at most 255 in all (one per CU,
 // leaving the partial sums of any width under 32 MiB).
-int32_t stream_tiles(int64_t hidden) { return (int32_t)ceil_div(hidden, kStreamTileCols); }
+int32_t stream_tiles(int64_t hidden) {
+    return (int32_t)ceil_div(hidden, ROWNORM_STREAM_BWD_XCH ? kXchTileColsBf16 : kStreamTileCols);
+}
 int32_t stream_walkers(int64_t rows, int64_t hidden) {
     return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles(hidden)));
 }
@@ -609,9 +618,14 @@ size_t dyn_ws_bytes(norm_op op, int64_t hidden, int64_t slabs) {
            sizeof(float);
 }
 
-// Streamed backward: the walkers' slabs, then two fp32 per row.
-size_t stream_ws_bytes(norm_op op, int64_t hidden, int64_t walkers, int64_t rows) {
-    return dyn_ws_bytes(op, hidden, walkers) + (size_t)std::max<int64_t>(rows, 0) * 8;
+// Streamed backward: the walkers' slabs, then the exchange area of the
+// tiles' partial sums (per walker kXchRing rows of `tiles` 16-byte slots;
+// none with one tile, which reduces its rows itself).
+size_t stream_ws_bytes(norm_op op, int64_t hidden, int64_t walkers, int64_t rows,
+                       int64_t tiles) {
+    if (!ROWNORM_STREAM_BWD_XCH)
+        return dyn_ws_bytes(op, hidden, walkers) + (size_t)std::max<int64_t>(rows, 0) * 8;
+    return dyn_ws_bytes(op, hidden, walkers) + (size_t)(rows > 0 ? xch_bytes(walkers, tiles) : 0);
 }
 
 // The column reduce addresses the workspace with 32-bit byte offsets and
@@ -1034,7 +1048,8 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
         if (!dyn_slabs_fit(op, c.hidden, slabs) ||
             (streamed && slabs * stream_tiles(c.hidden) > INT32_MAX))
             return NORM_ERROR_INVALID_VALUE;
-        ws_need = streamed ? stream_ws_bytes(op, c.hidden, any ? slabs : 0, any ? c.rows : 0)
+        ws_need = streamed ? stream_ws_bytes(op, c.hidden, any ? slabs : 0, any ? c.rows : 0,
+                                             stream_tiles(c.hidden))
                            : dyn_ws_bytes(op, c.hidden, any ? slabs : 0);
     }
 
@@ -1094,7 +1109,8 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         if (cfg->vector_elems == 8 && cfg->threads_per_row == kStreamTileLanes &&
             stream_bwd_ok(op, hidden, 8))
             return stream_ws_bytes(op, hidden,
-                                   cfg->grid > 0 ? cfg->grid : stream_walkers(rows, hidden), rows);
+                                   cfg->grid > 0 ? cfg->grid : stream_walkers(rows, hidden), rows,
+                                   stream_tiles(hidden));
         const int64_t g = cfg->grid > 0 ? cfg->grid : default_bwd_grid(rows, r);
         return dyn_ws_bytes(op, hidden, g);
     }
@@ -1106,7 +1122,8 @@ size_t ws_query(norm_op op, int64_t rows, int64_t hidden, const norm_launch_cfg*
         const norm_launch_cfg k = choose_dyn_bwd(op, rows, hidden, w, hidden);
         if (k.threads_per_row)
             need = std::max(need, stream_bwd_ok(op, hidden, w) && w == 8
-                                      ? stream_ws_bytes(op, hidden, k.grid, rows)
+                                      ? stream_ws_bytes(op, hidden, k.grid, rows,
+                                                        stream_tiles(hidden))
                                       : dyn_ws_bytes(op, hidden, k.grid));
     }
     return need;
@@ -1168,7 +1185,7 @@ int32_t bwd_walkers_f32(int64_t rows, int64_t hidden) {
 }
 size_t bwd_ws_bytes_f32(norm_op op, int64_t hidden, int64_t walkers, int64_t rows) {
     return f32_wide(hidden) ? dyn_ws_bytes(op, hidden, walkers)
-                            : stream_ws_bytes(op, hidden, walkers, rows);
+                            : stream_ws_bytes(op, hidden, walkers, rows, stream_tiles_f32(hidden));
 }
 
 norm_status run_fwd_f32(norm_op op, const FwdCall& c, hipStream_t stream) {
@@ -1401,6 +1418,8 @@ norm_status norm_split_status(void* workspace, int32_t clear, uint32_t* status,
 
 uint32_t norm_split_set_spin_limit(uint32_t polls) { return g_split_spin_limit.exchange(polls); }
 
+uint32_t norm_bwd_set_spin_limit(uint32_t polls) { return rownorm::g_bwd_spin_limit.exchange(polls); }
+
 norm_status norm_select_split(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
                               int32_t* split, int32_t* vecs) {
     if (!split || !vecs || rows < 0 || hidden < 1 ||
@@ -1616,8 +1635,11 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     const bool streamed = dyn && (is_bwd(op) ? !wide && stream_bwd_ok(op, hidden, w)
                                              : stream_fwd_ok(op, hidden, w));
     if (streamed) {
-        vecs = is_bwd(op) ? kStreamTileVecs : 0;
-        depth = is_bwd(op) ? (op == NORM_OP_FUSED_ADD_RMSNORM_BWD ? 2 : 3) : 0;
+        vecs = !is_bwd(op) ? 0 : ROWNORM_STREAM_BWD_XCH ? kXchVecsBf16 : kStreamTileVecs;
+        depth = !is_bwd(op)                          ? 0
+                : ROWNORM_STREAM_BWD_XCH             ? kXchDepthBf16
+                : op == NORM_OP_FUSED_ADD_RMSNORM_BWD ? 2
+                                                     : 3;
     } else if (wide) {
         vecs = wide->vecs;
         depth = 1;
@@ -1644,8 +1666,15 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                           (long long)c.grid * stream_tiles(hidden));
         else
             std::snprintf(grid_text, sizeof grid_text, "%d", c.grid);
-        char kern[160];
-        if (streamed)
+        char kern[256];
+        if (streamed && ROWNORM_STREAM_BWD_XCH)
+            std::snprintf(kern, sizeof kern,
+                          "stream_zero_kernel (the exchange area), then "
+                          "stream_bwd_tile_kernel<%d,%s,%d,exchange> over %d column tiles of %d "
+                          "exchanging partial row sums",
+                          vecs, op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm,dres?",
+                          depth, stream_tiles(hidden), kXchTileColsBf16);
+        else if (streamed)
             std::snprintf(kern, sizeof kern,
                           "stream_bwd_stats_kernel<%s> (1024 lanes a row), then "
                           "stream_bwd_tile_kernel<%d,%s,%d> over %d column tiles of %d",
@@ -1674,7 +1703,8 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                           (long long)(bwd_outs(op) * padded / colreduce_cols(slabs)),
                           kColReduceThreads,
                           (long long)slabs,
-                          streamed ? stream_ws_bytes(op, hidden, rows > 0 ? slabs : 0, rows)
+                          streamed ? stream_ws_bytes(op, hidden, rows > 0 ? slabs : 0, rows,
+                                                     stream_tiles(hidden))
                           : dyn    ? dyn_ws_bytes(op, hidden, rows > 0 ? slabs : 0)
                                    : static_ws_bytes(op, hidden, rows > 0 ? c.grid : 0));
     } else {

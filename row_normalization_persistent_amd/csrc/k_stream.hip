@@ -3,6 +3,8 @@
 // fp32 activations.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "kernels_stream.hpp"
 #include "stream_select.hpp"
 
@@ -107,7 +109,31 @@ hipError_t launch_tiles(const DynBwdArgs& a, const float* stats, int32_t tiles, 
     hipLaunchKernelGGL(
         (stream_bwd_tile_kernel<E, kStreamTileVecs, LN, DRES, tile_depth<LN, DRES>()>),
         dim3((unsigned)(walkers * tiles)), dim3(kStreamTileLanes), 0, stream, a, stats,
-        (int)tiles);
+        (int)tiles, (uint64_t*)nullptr, 0u);
+    return hipGetLastError();
+}
+
+// The tiles of each row exchange their partial sums (no statistics kernel):
+// the exchange area is zero-filled first.
+template <typename E, bool LN, bool DRES>
+hipError_t launch_tiles_xch(const DynBwdArgs& a, uint64_t* xch, int32_t tiles, int32_t walkers,
+                            hipStream_t stream) {
+    if (tiles < 2 || tiles > kXchMaxTiles) return hipErrorInvalidValue;  // the LDS slots
+    if (a.rows > INT32_MAX) return hipErrorInvalidValue;  // the walk counts rows in 32 bits
+    const int64_t words = xch_bytes(walkers, tiles) / 16;
+    const int64_t zgrid = std::min<int64_t>((words + 255) / 256, 1024);
+    hipLaunchKernelGGL(stream_zero_kernel, dim3((unsigned)zgrid), dim3(256), 0, stream,
+                       (u32x4*)xch, words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr bool kF32 = std::is_same_v<E, float>;
+    constexpr int V = kF32 ? kStreamTileVecs : kXchVecsBf16;
+    // fp32: the stats path's ring; bf16: 2 accesses a lane, a ring of kXchDepthBf16
+    constexpr int D = kF32 ? tile_depth<LN, DRES>() : kXchDepthBf16;
+    hipLaunchKernelGGL(
+        (stream_bwd_tile_kernel<E, V, LN, DRES, D, false, true>),
+        dim3((unsigned)(walkers * tiles)), dim3(kStreamTileLanes), 0, stream, a,
+        (const float*)nullptr, (int)tiles, xch, stream_bwd_spin_limit());
     return hipGetLastError();
 }
 
@@ -121,7 +147,8 @@ template <int V, bool LN, bool DRES>
 hipError_t launch_inrow(const DynBwdArgs& a, int32_t walkers, hipStream_t stream) {
     hipLaunchKernelGGL(
         (stream_bwd_tile_kernel<float, V, LN, DRES, inrow_depth<V, DRES>(), true>),
-        dim3((unsigned)walkers), dim3(kStreamTileLanes), 0, stream, a, nullptr, 1);
+        dim3((unsigned)walkers), dim3(kStreamTileLanes), 0, stream, a, nullptr, 1,
+        (uint64_t*)nullptr, 0u);
     return hipGetLastError();
 }
 
@@ -143,6 +170,12 @@ hipError_t stream_bwd_typed(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t
         hipError_t e = ln              ? inrow_by_vecs<true, false>(a, walkers, stream)
                        : a.dres        ? inrow_by_vecs<false, true>(a, walkers, stream)
                                        : inrow_by_vecs<false, false>(a, walkers, stream);
+        if (e != hipSuccess) return e;
+    } else if (a.rows > 0 && ROWNORM_STREAM_BWD_XCH) {
+        uint64_t* xch = (uint64_t*)(a.workspace + (int64_t)walkers * outs * padded);
+        hipError_t e = ln       ? launch_tiles_xch<E, true, false>(a, xch, tiles, walkers, stream)
+                       : a.dres ? launch_tiles_xch<E, false, true>(a, xch, tiles, walkers, stream)
+                                : launch_tiles_xch<E, false, false>(a, xch, tiles, walkers, stream);
         if (e != hipSuccess) return e;
     } else if (a.rows > 0) {
         float* stats = a.workspace + (int64_t)walkers * outs * padded;

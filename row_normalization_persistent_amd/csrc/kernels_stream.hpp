@@ -28,21 +28,26 @@
 // 1 to pass 2; only the rest is read again (a row of up to 4 x T accesses is
 // read once: every fp32 row of up to 16384 values).
 //
-// Backward, two kernels before the shared column reduce:
-//  * stream_bwd_stats_kernel (1024 lanes, workgroups walk the rows): the
-//    row's two reductions -- LayerNorm c1 = mean_j g, c2 = mean_j g * xhat;
-//    RMSNorm rstd = rsqrt(mean_j x^2 + eps) and coef = rstd^3 mean_j g x --
-//    stored as two floats per row after the workspace's partial-sum slabs;
-//  * stream_bwd_tile_kernel (512 lanes): the columns are cut into tiles of
-//    512 * V accesses; workgroup (walker w, tile t) walks the rows w, w + P,
-//    ... of its tile with a ring of D rows in flight, writes dx of its columns
-//    and accumulates their column sums in registers (no reduction over the
-//    row, so no barrier in the loop), then writes them into slab w, columns
-//    of tile t: the same [P][outs][padded] layout as the other backward
-//    kernels.  When one tile holds the whole row (fp32 up to 8192 columns,
-//    V = 1, 2 or 4), the tile kernel forms the row's two reductions itself
-//    (INROW, one barrier a row) and the stats kernel is not launched: each
-//    row is then read once.
+// Backward, before the shared column reduce: stream_bwd_tile_kernel (512
+// lanes) cuts the columns into tiles of 512 * V accesses; workgroup (walker
+// w, tile t) walks the rows w, w + P, ... of its tile with a ring of D rows in
+// flight, writes dx of its columns and accumulates their column sums in
+// registers, then writes them into slab w, columns of tile t: the same
+// [P][outs][padded] layout as the other backward kernels.  The row's two
+// reductions -- LayerNorm sum_j g and sum_j g * xhat; RMSNorm sum_j x^2 and
+// sum_j g x, giving rstd = rsqrt(mean_j x^2 + eps) and coef = rstd^3 mean_j
+// g x -- come from one of:
+//  * XCH (the default past one tile): the tiles of a row exchange their
+//    partial sums through 64-bit slots in the workspace, a group of D rows
+//    per round trip, with a bounded wait and a fallback that reads the other
+//    tiles' columns itself; each row is read once (stream_zero_kernel clears
+//    the slots first);
+//  * INROW (fp32 up to 8192 columns, one tile holds the row, V = 1, 2 or 4):
+//    the tile kernel reduces the row itself, one barrier a row;
+//  * stream_bwd_stats_kernel (1024 lanes, the path compiled with
+//    ROWNORM_STREAM_BWD_XCH=0): the two reductions of every row as two
+//    floats a row after the slabs, before the tile kernel, which then reads
+//    x and dy a second time.
 #pragma once
 
 #include "dyn_common.hpp"
@@ -634,7 +639,7 @@ struct TileRow {
 // loads zeros from no memory and statistics of zero, so it adds nothing).
 // INROW: the tile is the whole row and its statistics are reduced from the
 // loaded row (tile_row), not read from the stats kernel's output.
-template <typename E, int V, bool LN, bool DRES, bool INROW>
+template <typename E, int V, bool LN, bool DRES, bool INROW, bool XCH = false>
 __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdArgs& a,
                                               const float* stats, int64_t row, int acc0,
                                               int lane) {
@@ -656,7 +661,7 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
     const bool in = row < a.rows;
     const int64_t rc = in ? row : a.rows - 1;
     t.in = in;
-    if constexpr (!INROW) {
+    if constexpr (!INROW && !XCH) {
         const float s0 = stats[2 * rc], s1 = stats[2 * rc + 1];
         t.s0 = in ? s0 : 0.0f;
         t.s1 = in ? s1 : 0.0f;
@@ -665,6 +670,136 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
         const float m = a.mean[rc], q = a.rstd[rc];
         t.mean = in ? m : 0.0f;
         t.rstd = in ? q : 0.0f;
+    }
+}
+
+// The two per-lane sums of the row's backward over V accesses a lane (the
+// stats kernel's and INROW's terms: LayerNorm sum g and sum g xhat, RMSNorm
+// sum x^2 and sum g x; g = dy w).
+template <typename E, bool LN>
+__device__ __forceinline__ void accumulate_access(const u32x4& x, const u32x4& dy,
+                                                  const u32x4& w, float mean, float rstd,
+                                                  float& s1, float& s2) {
+    constexpr int EP = Elems<E>::kPer;
+    float xf[EP], df[EP], wf[EP];
+    unpack16<E>(x, xf);
+    unpack16<E>(dy, df);
+    unpack16<E>(w, wf);
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+        const float g = df[e] * wf[e];
+        if constexpr (LN) {
+            s1 += g;
+            s2 += g * ((xf[e] - mean) * rstd);
+        } else {
+            s1 += xf[e] * xf[e];
+            s2 += g * xf[e];
+        }
+    }
+}
+
+template <typename E, int V, bool LN>
+__device__ __forceinline__ void tile_sums(const u32x4 (&x)[V], const u32x4 (&dy)[V],
+                                          const u32x4 (&wv)[V], float mean, float rstd,
+                                          float& s1, float& s2) {
+    s1 = 0.0f;
+    s2 = 0.0f;
+#pragma unroll
+    for (int b = 0; b < V; ++b) accumulate_access<E, LN>(x[b], dy[b], wv[b], mean, rstd, s1, s2);
+}
+
+// ---- the column tiles of a row exchange their partial sums ---------------------------
+// Each (walker, tile) workgroup forms its tile's two sums for the D rows of
+// its ring at once (one reduction over the workgroup for all 2 D values) and
+// publishes them; a row's sums are the tiles' partials added in tile order,
+// so every tile of the row, and every run, gets the same bits.  A partial
+// goes out as one device-coherent 64-bit word (value bits << 32 | row + 1),
+// the tag naming the row, in slot (walk step mod kXchRing, tile, which) of
+// the walker's part of the exchange area, which the host zero-fills before
+// the launch (a tag of 0 names no row).  One round trip of polls covers the
+// group's D rows.  A tile publishes group g + 1 only after it has read every
+// partial of group g, and a partner publishes group g + 2 only after this
+// tile has published group g + 1, so slots of steps k and k + 2 D may share:
+// kXchRing >= 2 D.  Waits are bounded: a tile that runs out of polls (a
+// partner not resident, or the host's spin limit) stops waiting for the rest
+// of its walk and reads the other tiles of each row itself, forming their
+// partials exactly as their own workgroups do (same lanes, same order): the
+// same bits, from a second read of the row.
+
+// Sum over the workgroup of N values a lane (wave sums, then the waves' totals
+// added in wave order, as row_sum2 does for two): one barrier for all N.
+template <int T, int N>
+__device__ __forceinline__ void row_sum_n(float (&v)[N], float* slot, int lane) {
+    constexpr int kWaves = T / kWave;
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = wave_sum(v[j]);
+    const int w = lane / kWave;
+    if ((lane & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) slot[N * w + j] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        float t = slot[j];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) t += slot[N * i + j];
+        v[j] = t;
+    }
+}
+
+__device__ __forceinline__ uint64_t xch_word(float v, int64_t row) {
+    return ((uint64_t)__float_as_uint(v) << 32) | ((uint64_t)(row + 1) & 0xffffffffu);
+}
+
+// The row's sums from a re-read of the other tiles (this tile's own partials
+// s1, s2 as formed): tile by tile, each formed as its own workgroup forms it,
+// then added in tile order.  Plain loads (no buffer descriptors held in
+// scalar registers on this rare path).  Uniform control flow.
+template <typename E, int V, bool LN>
+__device__ __forceinline__ void xch_reread_row(const DynBwdArgs& a, int64_t row, int tiles,
+                                               int tile, float s1, float s2, float mean,
+                                               float rstd, float* redf, int lane, float& S1,
+                                               float& S2) {
+    constexpr int T = kStreamTileLanes;
+    constexpr int EP = Elems<E>::kPer;
+    constexpr int ES = (int)sizeof(E);
+    const int h = a.hidden;
+    // the row's byte offsets in vector registers (this path holds no more
+    // scalar registers than the walk around it)
+    int64_t xo = row * a.ld_x * ES, dyo = row * a.ld_dy * ES;
+    asm volatile("" : "+v"(xo));
+    asm volatile("" : "+v"(dyo));
+    const char* xr = static_cast<const char*>(a.x) + xo;
+    const char* dr = static_cast<const char*>(a.dy) + dyo;
+    const char* wr = static_cast<const char*>(a.weight);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int tp = 0; tp < tiles; ++tp) {
+        float p1 = s1, p2 = s2;  // this tile's own partials: the same bits
+        if (tp != tile) {
+            const int acc0 = tp * (T * V);
+            p1 = 0.0f;
+            p2 = 0.0f;
+#pragma unroll 1
+            for (int b = 0; b < V; ++b) {  // in the order tile_sums adds them
+                const int idx = acc0 + b * T + lane;
+                const bool in = idx * EP < h;  // past the row's end: zeros, as a buffer load
+                const int64_t off = (int64_t)idx * 16;
+                const u32x4 xv = in ? *reinterpret_cast<const u32x4*>(xr + off) : zero;
+                const u32x4 dv = in ? *reinterpret_cast<const u32x4*>(dr + off) : zero;
+                const u32x4 wv = in ? *reinterpret_cast<const u32x4*>(wr + off) : zero;
+                accumulate_access<E, LN>(xv, dv, wv, mean, rstd, p1, p2);
+            }
+            row_sum2<T>(p1, p2, redf, lane);
+            __syncthreads();  // the slots serve the next tile's reduction
+        }
+        if (tp == 0) {
+            S1 = p1;
+            S2 = p2;
+        } else {
+            S1 += p1;
+            S2 += p2;
+        }
     }
 }
 
@@ -743,20 +878,37 @@ __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[
     }
 }
 
+// Zero-fills n 16-byte words (the exchange area before an XCH launch).  A
+// kernel, not a memset, so that graphs capturing the call record no memset
+// node.
+__global__ __launch_bounds__(256) void stream_zero_kernel(u32x4* p, int64_t n) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = z;
+}
+
 // Grid: walkers * tiles workgroups; workgroup i is tile i % tiles of walker
-// i / tiles.  The stats of every row are complete (stream_bwd_stats_kernel
-// ran before on the same stream), or, with INROW (one tile holds the whole
-// row), reduced here from the row in registers: each row is then read once.
-template <typename E, int V, bool LN, bool DRES, int D, bool INROW = false>
-__global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(DynBwdArgs a,
-                                                                           const float* stats,
-                                                                           int tiles) {
+// i / tiles.  The row's two reductions: with XCH, exchanged between the row's
+// tiles through `xch` (zeroed before the launch; kXchRing walk steps of
+// `tiles` slot pairs per walker; a wait gives up after spin_limit polls);
+// with INROW (one tile holds the whole row), reduced here from the row in
+// registers; else read from `stats` (stream_bwd_stats_kernel ran before on
+// the same stream).
+template <typename E, int V, bool LN, bool DRES, int D, bool INROW = false, bool XCH = false>
+__global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
+    DynBwdArgs a, const float* stats, int tiles, uint64_t* xch, uint32_t spin_limit) {
     constexpr int T = kStreamTileLanes;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
+    static_assert(!(INROW && XCH), "one way to form the row's sums");
+    static_assert(!XCH || 2 * D <= kXchRing, "slots of a walker's last two groups");
     // two sums per wave, two sets used alternately so that a row's reduction
     // never overwrites slots the previous row's lanes may still be reading
-    __shared__ float red[INROW ? 2 * 2 * (T / kWave) : 1];
+    __shared__ float red[INROW ? 2 * 2 * (T / kWave) : XCH ? 2 * 2 * D * (T / kWave) : 1];
+    // XCH: the group's partials, row d of tile tp at [d * kXchMaxTiles + tp]
+    __shared__ float xq1[XCH ? D * kXchMaxTiles : 1], xq2[XCH ? D * kXchMaxTiles : 1];
+    __shared__ float redf[XCH ? 2 * (T / kWave) : 1];
+    __shared__ int xflag[XCH ? T / kWave : 1];
     int parity = 0;
     const int lane = threadIdx.x;
     const int tile = blockIdx.x % tiles;
@@ -782,20 +934,140 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(DynBw
     TileRow<V, DRES> buf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load_tile_row<E, V, LN, DRES, INROW>(buf[d], a, stats, opaque_row(walker + d * P), acc0,
-                                             lane);
+        load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, opaque_row(walker + d * P),
+                                                  acc0, lane);
         issue_fence();
     }
-    for (int64_t i = 0; i < n; i += D) {
+    if constexpr (XCH) {
+        // the ring's D rows are one group: their partials in one reduction,
+        // their exchange in one round trip of polls, then dx row by row
+        uint64_t* mine = xch + walker * kXchRing * tiles * 2;
+        bool sticky = false;  // a wait ran out: re-read rows for the rest of the walk
+        const float inv_h = 1.0f / (float)h;
+        const int nw = (int)n;  // a walker's rows: the host keeps rows below 2^31
+        for (int i = 0; i < nw; i += D) {
+            float v[2 * D];
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int64_t r = opaque_row(walker + (i + d) * P);
-            tile_row<E, V, LN, DRES, INROW>(buf[d], wv, pw, pb, a, r, acc0, lane,
-                                            red + parity * 2 * (T / kWave));
+            for (int d = 0; d < D; ++d)
+                tile_sums<E, V, LN>(buf[d].x, buf[d].dy, wv, buf[d].mean, buf[d].rstd, v[2 * d],
+                                    v[2 * d + 1]);
+            row_sum_n<T, 2 * D>(v, red + parity * 2 * D * (T / kWave), lane);
             parity ^= 1;
-            issue_fence();
-            load_tile_row<E, V, LN, DRES, INROW>(buf[d], a, stats, r + D * P, acc0, lane);
-            issue_fence();
+            const int64_t r0 = opaque_row(walker + i * P);
+            // rows of the group inside the matrix: d < nd (uniform)
+            const int nd = nw - i < D ? nw - i : D;
+            if (lane < nd) {  // lane d (of wave 0) publishes row d
+                float p1 = v[0], p2 = v[1];
+#pragma unroll
+                for (int d = 1; d < D; ++d) {
+                    p1 = lane == d ? v[2 * d] : p1;
+                    p2 = lane == d ? v[2 * d + 1] : p2;
+                }
+                const int64_t row = r0 + lane * P;
+                uint64_t* me = mine + (((i + lane) % kXchRing) * tiles + tile) * 2;
+                __hip_atomic_store(&me[0], xch_word(p1, row), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&me[1], xch_word(p2, row), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // every lane of the workgroup waits on its own slot pair (one pair
+            // a lane while nd * tiles <= T), so the group's polls are in
+            // flight together rather than one after another in one wave
+            bool seen = true;
+            if (!sticky) {
+                for (int p = lane; p < nd * tiles; p += T) {
+                    const int d = p / tiles, tp = p - d * tiles;
+                    const int64_t row = r0 + d * P;
+                    const uint64_t tag = (uint64_t)(row + 1) & 0xffffffffu;
+                    const uint64_t* slot = mine + (((i + d) % kXchRing) * tiles + tp) * 2;
+                    uint64_t u = 0, w = 0;
+                    bool ok = false;
+                    for (uint32_t polls = 0; polls < spin_limit; ++polls) {
+                        if ((u & 0xffffffffu) != tag)
+                            u = __hip_atomic_load(&slot[0], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                        if ((w & 0xffffffffu) != tag)
+                            w = __hip_atomic_load(&slot[1], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                        if ((u & 0xffffffffu) == tag && (w & 0xffffffffu) == tag) {
+                            ok = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    xq1[d * kXchMaxTiles + tp] = __uint_as_float((uint32_t)(u >> 32));
+                    xq2[d * kXchMaxTiles + tp] = __uint_as_float((uint32_t)(w >> 32));
+                    seen = seen && ok;
+                }
+            }
+            const bool wave_seen = __builtin_amdgcn_ballot_w64(!seen) == 0;
+            if ((lane & (kWave - 1)) == 0) xflag[lane / kWave] = wave_seen ? 1 : 0;
+            __syncthreads();
+            bool all = !sticky;
+#pragma unroll
+            for (int k = 0; k < T / kWave; ++k) all = all && xflag[k] != 0;
+            sticky = !all;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                float S1 = 0.0f, S2 = 0.0f;
+                if (d < nd) {
+                    if (all) {
+                        S1 = xq1[d * kXchMaxTiles];
+                        S2 = xq2[d * kXchMaxTiles];
+                        for (int tp = 1; tp < tiles; ++tp) {
+                            S1 += xq1[d * kXchMaxTiles + tp];
+                            S2 += xq2[d * kXchMaxTiles + tp];
+                        }
+                    } else {
+                        xch_reread_row<E, V, LN>(a, r0 + d * P, tiles, tile, v[2 * d],
+                                                 v[2 * d + 1], buf[d].mean, buf[d].rstd, redf,
+                                                 lane, S1, S2);
+                    }
+                }
+                TileRow<V, DRES>& t = buf[d];
+                if constexpr (LN) {
+                    t.s0 = S1 * inv_h;
+                    t.s1 = S2 * inv_h;
+                } else {
+                    const float rs = fast_rsqrt(S1 * inv_h + a.eps);
+                    t.s0 = rs;
+                    t.s1 = rs * rs * rs * S2 * inv_h;
+                }
+                if (!t.in) {  // a row past the end adds nothing
+                    t.s0 = 0.0f;
+                    t.s1 = 0.0f;
+                }
+                // dx unpacks the row again rather than keep the sums' unpacked
+                // values live across the exchange
+#pragma unroll
+                for (int b = 0; b < V; ++b) {
+                    asm volatile("" : "+v"(t.x[b]));
+                    asm volatile("" : "+v"(t.dy[b]));
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int64_t r = opaque_row(walker + (i + d) * P);
+                tile_row<E, V, LN, DRES, false>(buf[d], wv, pw, pb, a, r, acc0, lane, nullptr);
+                issue_fence();
+                load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, r + D * P, acc0,
+                                                          lane);
+                issue_fence();
+            }
+        }
+    } else {
+        for (int64_t i = 0; i < n; i += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int64_t r = opaque_row(walker + (i + d) * P);
+                tile_row<E, V, LN, DRES, INROW>(buf[d], wv, pw, pb, a, r, acc0, lane,
+                                                red + parity * 2 * (T / kWave));
+                parity ^= 1;
+                issue_fence();
+                load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, r + D * P, acc0,
+                                                          lane);
+                issue_fence();
+            }
         }
     }
 

@@ -50,4 +50,30 @@ constexpr bool stage_fwd_holds(int op, bool f32, int64_t hidden) {
            n_acc <= (int64_t)kStreamFwdLanes * (st.u + st.l);
 }
 
+// ---- streamed backward: the tiles of a row exchange their partial sums --------------
+// Exchange area after the walkers' slabs: per walker kXchRing walk steps of
+// `tiles` slots of two 64-bit words (16 bytes a slot), zero-filled by a
+// kernel before each launch.
+constexpr int kXchRing = 8;  // >= twice the ring rows of a group
+// bf16 tiles of the exchanging kernel: 512 lanes x 2 accesses (8192 columns;
+// at 4 accesses the exchange's registers push the kernel into spills)
+constexpr int kXchVecsBf16 = 2;
+constexpr int kXchTileColsBf16 = kStreamTileLanes * kXchVecsBf16 * 8;
+#ifndef ROWNORM_XCH_DEPTH
+#define ROWNORM_XCH_DEPTH 3
+#endif
+constexpr int kXchDepthBf16 = ROWNORM_XCH_DEPTH;  // ring rows
+constexpr int kXchMaxTiles = 128;  // 2^20 fp32 columns / 8192
+inline int64_t xch_bytes(int64_t walkers, int64_t tiles) {
+    return tiles > 1 ? walkers * kXchRing * tiles * 16 : 0;
+}
+#ifndef ROWNORM_STREAM_BWD_XCH
+#define ROWNORM_STREAM_BWD_XCH 1
+#endif
+// Polls a tile's wait for its partners makes before it re-reads the row
+// itself (norm_bwd_set_spin_limit): by default about 16 ms, which a tile
+// whose partners run beside it never needs.
+constexpr uint32_t kBwdSpinLimit = 1u << 14;
+uint32_t stream_bwd_spin_limit();
+
 }  // namespace rownorm

@@ -36,7 +36,7 @@ def test_header_declares_the_four_operations():
     for op in ("norm_fused_add_rmsnorm", "norm_rmsnorm_fwd", "norm_layernorm_fwd",
                "norm_layernorm_bwd", "norm_rmsnorm_bwd", "norm_fused_add_rmsnorm_bwd"):
         assert op + "_f32" in names  # fp32 activations
-    assert len(names) == 41
+    assert len(names) == 42
 
 
 def test_library_exports_every_declared_symbol():
@@ -261,7 +261,7 @@ def test_describe_config():
     with pytest.raises(rn.NormError):
         rn.describe_config("rmsnorm_fwd", 4, 70002, cu_count=256)
     d = rn.describe_config("layernorm_bwd", 1000, 65536, cu_count=256)
-    assert "63 row walkers x 4 column tiles" in d and \
+    assert "31 row walkers x 8 column tiles" in d and "exchanging partial row sums" in d and \
         f"workspace {rn.workspace_bytes(1000, 65536)}" in d
     d = rn.describe_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     c = rn.select_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
@@ -293,12 +293,14 @@ def test_workspace_bytes():
     assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 2 * 1024 * 4
     assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
     assert rn.workspace_bytes(10, (1 << 20) + 8) == 0
-    # streamed rows: one slab per row walker (255 // column tiles of 16384, at
-    # most the rows), then two fp32 per row
-    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 8
-    assert rn.workspace_bytes(1000, 65536) == 63 * 2 * 65536 * 4 + 1000 * 8
-    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 63 * 65536 * 4 + 1000 * 8
-    assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == 5 * 2 * 65536 * 4 + 8000
+    # streamed rows: one slab per row walker (255 // column tiles of 8192, at
+    # most the rows), then the tiles' exchange area: per walker 8 walk steps of
+    # 16 bytes a tile
+    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 8 * 9 * 16
+    assert rn.workspace_bytes(1000, 65536) == 31 * 2 * 65536 * 4 + 31 * 8 * 8 * 16
+    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 8 * 8 * 16
+    assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == \
+        5 * 2 * 65536 * 4 + 5 * 8 * 8 * 16
     assert rn.workspace_bytes(-1, 4096) == 0
 
 
@@ -749,20 +751,21 @@ def test_f32_validation():
 
 def test_f32_workspace_sizes():
     """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
-    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers, plus
-    8 bytes a row; at 8196 ... 16384 columns min(rows, 256) walkers)."""
+    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers), plus
+    with more than one column tile the tiles' exchange area (per walker 8 walk
+    steps of 16 bytes a tile); at 8196 ... 16384 columns min(rows, 256) walkers."""
     ws = rn.workspace_bytes_f32
     pad = lambda h: -(-h // 64) * 64
-    assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4 + 8192 * 8
-    assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4 + 8192 * 8
-    assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4 + 3 * 8
-    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1000 * 8  # 128 tiles
-    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 1000 * 8  # 3 tiles
-    # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs, no per-row floats
+    assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4
+    assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4
+    assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4
+    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1 * 8 * 128 * 16
+    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 85 * 8 * 3 * 16
+    # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs
     assert ws("layernorm_bwd", 1000, 16384) == 256 * 2 * 16384 * 4
     assert ws("rmsnorm_bwd", 3, 8196) == 3 * pad(8196) * 4
     assert ws("fused_add_rmsnorm_bwd", 100, 12288) == 100 * 12288 * 4
-    assert ws("layernorm_bwd", 1000, 8192) == 255 * 2 * 8192 * 4 + 1000 * 8  # one tile
+    assert ws("layernorm_bwd", 1000, 8192) == 255 * 2 * 8192 * 4  # one tile
     assert ws("layernorm_bwd", 0, 4096) == 0
     assert ws("layernorm_bwd", 8, 4098) == 0
     assert ws("layernorm_fwd", 8, 4096) == 0      # a forward op
@@ -790,7 +793,7 @@ def test_wide_backward_host_logic():
             assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4
         # 9 accesses a lane: past the LDS-staged kernel, the streamed kernels
         c = rn.select_config(op, 8192, 32776)
-        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 85, 8)  # 255 // 3 tiles
+        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 51, 8)  # 255 // 5 tiles
         assert "stream_bwd_tile_kernel" in rn.describe_config(op, 8192, 32776)
         with pytest.raises(rn.NormError):
             rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels

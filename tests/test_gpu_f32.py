@@ -274,6 +274,35 @@ def test_backward_f32_deterministic_and_dirty_workspace():
             assert torch.equal(a.view(torch.int32), c.view(torch.int32))
 
 
+def test_backward_f32_reread_path_is_bitwise_the_exchange():
+    """Rows of several column tiles: the tiles' exchanged partial row sums and
+    the re-read path (spin limit 0: no tile waits) give the same bits."""
+    rows, h = 300, 40004
+    inp = wl.layernorm_bwd_inputs(rows, h, seed=15, f32=True)
+    mean32, rstd32 = ln_stats_f32(inp["x"], inp["eps"])
+    args = (dev(inp["dy"]), dev(inp["x"]), dev(mean32), dev(rstd32), dev(inp["w"]))
+    rin = wl.rmsnorm_bwd_inputs(rows, h, seed=16, f32=True)
+    rargs = (dev(rin["dy"]), dev(rin["x"]), dev(rin["w"]), rin["eps"])
+
+    def run():
+        ln = rn.layernorm_bwd_f32(*args)
+        rms = rn.rmsnorm_bwd_f32(*rargs)
+        fused = rn.fused_add_rmsnorm_bwd_f32(*rargs, dres=dev(rin["dres"]))
+        torch.cuda.synchronize()
+        return [t.clone() for t in (*ln, *rms, *fused)]
+
+    fast = run()
+    old = rn.set_bwd_spin_limit(0)
+    try:
+        slow = run()
+    finally:
+        rn.set_bwd_spin_limit(old)
+    for k, (a, c) in enumerate(zip(fast, slow)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32)), f"output {k}"
+    check_ln_bwd(inp, mean32, rstd32, host(slow[0]), host(slow[1]), host(slow[2]),
+                 "layernorm bwd f32, re-read path")
+
+
 def test_f32_graph_replays_match_eager():
     """Forward and backward captured in one HIP graph: every replay bitwise
     equal to the eager calls (no memset nodes: the kernels write every slab

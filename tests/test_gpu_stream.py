@@ -258,6 +258,28 @@ def test_stream_bwd_walkers_aliasing_and_determinism():
     check_rmsb(rinp, False, run_rmsb(rinp, False, alias=True), "rmsnorm bwd dx == dy")
 
 
+@pytest.mark.parametrize("h,rows", [(40000, 300), (65544, 75), (1 << 20, 3)])
+def test_stream_bwd_reread_path_is_bitwise_the_exchange(h, rows):
+    """The column tiles of a row exchange their partial row sums; a tile that
+    stops waiting (spin limit 0: never wait) reads the other tiles of each
+    row itself and forms their partials as their own workgroups do.  Both
+    paths give the same bits, and agree with the oracle."""
+    inp = lnb_inputs(rows, h, seed=h + 3)
+    rinp = wl.rmsnorm_bwd_inputs(rows, h, seed=h + 4)
+    fast = (run_lnb(inp), run_rmsb(rinp, False), run_rmsb(rinp, True))
+    old = rn.set_bwd_spin_limit(0)
+    try:
+        slow = (run_lnb(inp), run_rmsb(rinp, False), run_rmsb(rinp, True))
+    finally:
+        rn.set_bwd_spin_limit(old)
+    for what, a, b in zip(("layernorm_bwd", "rmsnorm_bwd", "fused bwd"), fast, slow):
+        for k, (u, v) in enumerate(zip(a, b)):
+            assert np.array_equal(np.asarray(u).view(np.uint8), np.asarray(v).view(np.uint8)), \
+                f"{what} output {k}: re-read path differs from the exchange"
+    check_lnb(inp, slow[0], f"layernorm_bwd re-read {rows}x{h}")
+    check_rmsb(rinp, True, slow[2], f"fused bwd re-read {rows}x{h}")
+
+
 def test_stream_bwd_zero_rows_and_noalloc():
     h = 65536
     dw = torch.full((h,), float("nan"), device=DEV)
