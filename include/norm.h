@@ -218,7 +218,7 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
  * (norm_layernorm_bwd_workspace_bytes for contiguous rows: 2 * 4 * hidden
  * bytes, hidden rounded up to 64 off the compiled sizes, for each of its up
  * to 256 workgroups; rows past 32768 columns: the same for each of its up to
- * 255 / ceil(hidden / 8192) row walkers, each with 128 bytes of partial-sum
+ * 255 / ceil(hidden / 8192) row walkers, each with 192 bytes of partial-sum
  * exchange slots per 8192-column tile) would exceed
  * NORM_NOALLOC_SCRATCH_BYTES: every hidden up to 16384 fits, rows of
  * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows), and
@@ -549,7 +549,7 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, c
  * NORM_OP_RMSNORM_BWD or NORM_OP_FUSED_ADD_RMSNORM_BWD): 4 * padded hidden
  * (hidden rounded up to 64) per partial-sum slab and output column sum, for
  * each row walker: min(rows, 256) of them at 8196 ... 16384 columns, else
- * max(1, min(rows, 255 / ceil(hidden / 8192))), each with 128 bytes of
+ * max(1, min(rows, 255 / ceil(hidden / 8192))), each with 192 bytes of
  * partial-sum exchange slots per 8192-column tile.  Pure
  * host arithmetic; 0 for another op, an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);

@@ -39,9 +39,9 @@
 // g x -- come from one of:
 //  * XCH (the default past one tile): the tiles of a row exchange their
 //    partial sums through 64-bit slots in the workspace, a group of D rows
-//    per round trip, with a bounded wait and a fallback that reads the other
-//    tiles' columns itself; each row is read once (stream_zero_kernel clears
-//    the slots first);
+//    per round trip (bf16: two rings, one group published ahead), with a
+//    bounded wait and a fallback that reads the other tiles' columns itself;
+//    each row is read once (stream_zero_kernel clears the slots first);
 //  * INROW (fp32 up to 8192 columns, one tile holds the row, V = 1, 2 or 4):
 //    the tile kernel reduces the row itself, one barrier a row;
 //  * stream_bwd_stats_kernel (1024 lanes, the path compiled with
@@ -901,18 +901,24 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     static_assert(!(INROW && XCH), "one way to form the row's sums");
-    static_assert(!XCH || 2 * D <= kXchRing, "slots of a walker's last two groups");
     // two sums per wave, two sets used alternately so that a row's reduction
     // never overwrites slots the previous row's lanes may still be reading
     __shared__ float red[INROW ? 2 * 2 * (T / kWave) : XCH ? 2 * 2 * D * (T / kWave) : 1];
     // XCH: the group's partials, row d of tile tp at [d * kXchMaxTiles + tp]
     __shared__ float xq1[XCH ? D * kXchMaxTiles : 1], xq2[XCH ? D * kXchMaxTiles : 1];
     __shared__ float redf[XCH ? 2 * (T / kWave) : 1];
+    // XCH: the workgroup's own partials of each ring's group (for a re-read)
+    __shared__ float xown[XCH ? 2 * 2 * D : 1];
     __shared__ int xflag[XCH ? T / kWave : 1];
     int parity = 0;
     const int lane = threadIdx.x;
     const int tile = blockIdx.x % tiles;
     const int64_t walker = blockIdx.x / tiles;
+    // XCH: the workspace pointer waits in VGPRs through the walk (it is used
+    // once, at the end), leaving the scalar registers to the walk
+    uint32_t ws_lo = (uint32_t)(uintptr_t)a.workspace;
+    uint32_t ws_hi = (uint32_t)((uintptr_t)a.workspace >> 32);
+    if constexpr (XCH) asm volatile("" : "+v"(ws_lo), "+v"(ws_hi));
     const int64_t P = gridDim.x / tiles;
     const int acc0 = tile * (T * V);  // the tile's first 16-byte access
     const int h = a.hidden;
@@ -939,37 +945,61 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
         issue_fence();
     }
     if constexpr (XCH) {
-        // the ring's D rows are one group: their partials in one reduction,
-        // their exchange in one round trip of polls, then dx row by row
+        // The ring's D rows are one group: their partials in one reduction,
+        // their exchange in one round trip of polls, then dx row by row.
+        // AHEAD (bf16; fp32 rows are twice the registers): two rings, the
+        // group at i + D published before the group at i is waited on, so the
+        // round trip overlaps a group's loads and sums.
+        constexpr bool AHEAD = kXchAhead && ES == 2;
+        constexpr int kStep = AHEAD ? 2 * D : D;  // walk steps between a ring's groups
+        static_assert(AHEAD ? 4 * D <= kXchRing : 2 * D <= kXchRing,
+                      "slots of the groups other tiles may still read");
         uint64_t* mine = xch + walker * kXchRing * tiles * 2;
         bool sticky = false;  // a wait ran out: re-read rows for the rest of the walk
         const float inv_h = 1.0f / (float)h;
         const int nw = (int)n;  // a walker's rows: the host keeps rows below 2^31
-        for (int i = 0; i < nw; i += D) {
+
+        // the group at walk step i in ring k: partials of its rows (past the
+        // walk's end: zeros) reduced over the workgroup, rows < nw published
+        // and kept in xown; returns the group's first row
+        auto sums_publish = [&](TileRow<V, DRES>(&rb)[D], int k, int i)
+                                __attribute__((always_inline)) {
             float v[2 * D];
 #pragma unroll
             for (int d = 0; d < D; ++d)
-                tile_sums<E, V, LN>(buf[d].x, buf[d].dy, wv, buf[d].mean, buf[d].rstd, v[2 * d],
+                tile_sums<E, V, LN>(rb[d].x, rb[d].dy, wv, rb[d].mean, rb[d].rstd, v[2 * d],
                                     v[2 * d + 1]);
             row_sum_n<T, 2 * D>(v, red + parity * 2 * D * (T / kWave), lane);
             parity ^= 1;
             const int64_t r0 = opaque_row(walker + i * P);
-            // rows of the group inside the matrix: d < nd (uniform)
             const int nd = nw - i < D ? nw - i : D;
             if (lane < nd) {  // lane d (of wave 0) publishes row d
+                // an opaque lane: the lane == d masks are formed here, not
+                // hoisted to live across the walk
+                const int ld = opaque_lane(lane);
                 float p1 = v[0], p2 = v[1];
 #pragma unroll
                 for (int d = 1; d < D; ++d) {
-                    p1 = lane == d ? v[2 * d] : p1;
-                    p2 = lane == d ? v[2 * d + 1] : p2;
+                    p1 = ld == d ? v[2 * d] : p1;
+                    p2 = ld == d ? v[2 * d + 1] : p2;
                 }
                 const int64_t row = r0 + lane * P;
+                xown[k * 2 * D + 2 * lane] = p1;
+                xown[k * 2 * D + 2 * lane + 1] = p2;
                 uint64_t* me = mine + (((i + lane) % kXchRing) * tiles + tile) * 2;
                 __hip_atomic_store(&me[0], xch_word(p1, row), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(&me[1], xch_word(p2, row), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
+            return r0;
+        };
+
+        // the group at walk step i (i < nw, published): its row sums, dx of
+        // its rows, the ring reloaded with the rows kStep steps on
+        auto poll_finish = [&](TileRow<V, DRES>(&rb)[D], int k, int i, int64_t r0)
+                               __attribute__((always_inline)) {
+            const int nd = nw - i < D ? nw - i : D;
             // every lane of the workgroup waits on its own slot pair (one pair
             // a lane while nd * tiles <= T), so the group's polls are in
             // flight together rather than one after another in one wave
@@ -1012,19 +1042,24 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
                 float S1 = 0.0f, S2 = 0.0f;
                 if (d < nd) {
                     if (all) {
+                        // opaque here, so that the unrolled loop's trip-count
+                        // values are not hoisted to live across the whole walk
+                        int nt = tiles;
+                        asm volatile("" : "+s"(nt));
                         S1 = xq1[d * kXchMaxTiles];
                         S2 = xq2[d * kXchMaxTiles];
-                        for (int tp = 1; tp < tiles; ++tp) {
+                        for (int tp = 1; tp < nt; ++tp) {
                             S1 += xq1[d * kXchMaxTiles + tp];
                             S2 += xq2[d * kXchMaxTiles + tp];
                         }
                     } else {
-                        xch_reread_row<E, V, LN>(a, r0 + d * P, tiles, tile, v[2 * d],
-                                                 v[2 * d + 1], buf[d].mean, buf[d].rstd, redf,
-                                                 lane, S1, S2);
+                        xch_reread_row<E, V, LN>(a, r0 + d * P, tiles, tile,
+                                                 xown[k * 2 * D + 2 * d],
+                                                 xown[k * 2 * D + 2 * d + 1], rb[d].mean,
+                                                 rb[d].rstd, redf, lane, S1, S2);
                     }
                 }
-                TileRow<V, DRES>& t = buf[d];
+                TileRow<V, DRES>& t = rb[d];
                 if constexpr (LN) {
                     t.s0 = S1 * inv_h;
                     t.s1 = S2 * inv_h;
@@ -1048,11 +1083,33 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int64_t r = opaque_row(walker + (i + d) * P);
-                tile_row<E, V, LN, DRES, false>(buf[d], wv, pw, pb, a, r, acc0, lane, nullptr);
+                tile_row<E, V, LN, DRES, false>(rb[d], wv, pw, pb, a, r, acc0, lane, nullptr);
                 issue_fence();
-                load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, r + D * P, acc0,
+                load_tile_row<E, V, LN, DRES, INROW, XCH>(rb[d], a, stats, r + kStep * P, acc0,
                                                           lane);
                 issue_fence();
+            }
+        };
+
+        if constexpr (AHEAD) {
+            TileRow<V, DRES> buf2[D];
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                load_tile_row<E, V, LN, DRES, INROW, XCH>(
+                    buf2[d], a, stats, opaque_row(walker + (D + d) * P), acc0, lane);
+                issue_fence();
+            }
+            sums_publish(buf, 0, 0);
+            for (int i = 0; i < nw; i += 2 * D) {
+                sums_publish(buf2, 1, i + D);
+                poll_finish(buf, 0, i, opaque_row(walker + i * P));
+                if (i + D >= nw) break;
+                sums_publish(buf, 0, i + 2 * D);
+                poll_finish(buf2, 1, i + D, opaque_row(walker + (i + D) * P));
+            }
+        } else {
+            for (int i = 0; i < nw; i += D) {
+                poll_finish(buf, 0, i, sums_publish(buf, 0, i));
             }
         }
     } else {
@@ -1075,7 +1132,11 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     // padded width are dropped by the descriptors' range
     const int padded = (h + 63) / 64 * 64;
     const int outs = LN ? 2 : 1;
-    float* slab = a.workspace + walker * outs * (int64_t)padded;
+    float* ws = a.workspace;
+    if constexpr (XCH)
+        ws = (float*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)ws_hi) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)ws_lo));
+    float* slab = ws + walker * outs * (int64_t)padded;
     const rsrc_t sw = __builtin_amdgcn_make_buffer_rsrc(slab, (short)0, padded * 4, kRsrcWord3);
     const rsrc_t sb = __builtin_amdgcn_make_buffer_rsrc(slab + padded, (short)0,
                                                         LN ? padded * 4 : 0, kRsrcWord3);

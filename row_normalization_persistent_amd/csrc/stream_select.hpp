@@ -54,7 +54,17 @@ constexpr bool stage_fwd_holds(int op, bool f32, int64_t hidden) {
 // Exchange area after the walkers' slabs: per walker kXchRing walk steps of
 // `tiles` slots of two 64-bit words (16 bytes a slot), zero-filled by a
 // kernel before each launch.
-constexpr int kXchRing = 8;  // >= twice the ring rows of a group
+// bf16 walks keep two rings of D rows and publish one group ahead: a slot
+// is written again only after every tile has read the three groups before
+// it, so the ring covers 4D walk steps (D = 3: 12).
+#ifndef ROWNORM_XCH_RING
+#define ROWNORM_XCH_RING 12
+#endif
+constexpr int kXchRing = ROWNORM_XCH_RING;
+#ifndef ROWNORM_XCH_AHEAD
+#define ROWNORM_XCH_AHEAD 1
+#endif
+constexpr bool kXchAhead = ROWNORM_XCH_AHEAD != 0;
 // bf16 tiles of the exchanging kernel: 512 lanes x 2 accesses (8192 columns;
 // at 4 accesses the exchange's registers push the kernel into spills)
 constexpr int kXchVecsBf16 = 2;

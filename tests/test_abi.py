@@ -294,13 +294,13 @@ def test_workspace_bytes():
     assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
     assert rn.workspace_bytes(10, (1 << 20) + 8) == 0
     # streamed rows: one slab per row walker (255 // column tiles of 8192, at
-    # most the rows), then the tiles' exchange area: per walker 8 walk steps of
-    # 16 bytes a tile
-    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 8 * 9 * 16
-    assert rn.workspace_bytes(1000, 65536) == 31 * 2 * 65536 * 4 + 31 * 8 * 8 * 16
-    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 8 * 8 * 16
+    # most the rows), then the tiles' exchange area: per walker 12 walk steps
+    # of 16 bytes a tile
+    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 12 * 9 * 16
+    assert rn.workspace_bytes(1000, 65536) == 31 * 2 * 65536 * 4 + 31 * 12 * 8 * 16
+    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 12 * 8 * 16
     assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == \
-        5 * 2 * 65536 * 4 + 5 * 8 * 8 * 16
+        5 * 2 * 65536 * 4 + 5 * 12 * 8 * 16
     assert rn.workspace_bytes(-1, 4096) == 0
 
 
@@ -752,15 +752,15 @@ def test_f32_validation():
 def test_f32_workspace_sizes():
     """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
     column sum and row walker (at most 255 / ceil(hidden / 8192) walkers), plus
-    with more than one column tile the tiles' exchange area (per walker 8 walk
+    with more than one column tile the tiles' exchange area (per walker 12 walk
     steps of 16 bytes a tile); at 8196 ... 16384 columns min(rows, 256) walkers."""
     ws = rn.workspace_bytes_f32
     pad = lambda h: -(-h // 64) * 64
     assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4
     assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4
     assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4
-    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1 * 8 * 128 * 16
-    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 85 * 8 * 3 * 16
+    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1 * 12 * 128 * 16
+    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 85 * 12 * 3 * 16
     # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs
     assert ws("layernorm_bwd", 1000, 16384) == 256 * 2 * 16384 * 4
     assert ws("rmsnorm_bwd", 3, 8196) == 3 * pad(8196) * 4
