@@ -1128,7 +1128,8 @@ def f32_ops(torch, rn, wl, dev, stream, reps):
     dw, db = torch.empty(h, device=dev), torch.empty(h, device=dev)
     ws = torch.empty(rn.workspace_bytes_f32("layernorm_bwd", rows, h), dtype=torch.uint8,
                      device=dev)
-    note = "fp32 activations: streamed kernels (row reductions, column tiles) + column reduce"
+    note = ("fp32 activations: tile kernel, one 512-lane tile holds the row and reduces it "
+            "(row read once) + column reduce")
     t = graph_time_per_launch(torch, stream, [
         (lambda j=j: rn.layernorm_bwd_f32(dys[j], xs[j], mean, rstd, w, dx=dxs[j], dweight=dw,
                                           dbias=db, workspace=ws, stream=stream))
