@@ -41,7 +41,10 @@ struct BwdRow {
 // kernel runs) instead of a buffer load in every lane: at one 16-byte access
 // per lane that halves a row's vector memory instructions.  Measured on
 // MI355X: 8192 x 2048 / 4096 / 8192 rows kernel 5 / 2 / 1 % faster, output
-// bitwise unchanged.
+// bitwise unchanged.  The LDS waits of the row's reduction also wait for the
+// next row's scalar loads (one counter covers both); fetching a walk's 64
+// next pairs by one vector load instead and reading each with readlane was
+// 3-5 % slower still (8192 x 4096 / 8192, 16384 x 4096).
 template <int H, int T, int V>
 __device__ __forceinline__ void load_bwd_row(BwdRow<V>& r, const u32x4* x, const u32x4* dy,
                                              const float* __restrict__ mean,
