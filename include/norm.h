@@ -20,7 +20,8 @@
  *     (access elements) otherwise; backward 32768 with 16-byte accesses
  *     (above 16384 the row is staged in LDS: "TMA inner persistent
  *     scheduler", description summary, the shared-memory persistent
- *     buffer), 16384 with 8-byte accesses, 8192 otherwise.  Wider rows with
+ *     buffer; the fused op's backward up to 28672, wider rows streamed),
+ *     16384 with 8-byte accesses, 8192 otherwise.  Wider rows with
  *     16-byte accesses (hidden a multiple of 8, up to 2^20) run on streamed
  *     kernels: forward, one pass for the statistic and one, mostly from the
  *     Infinity Cache, to normalize (the row read twice); backward,
@@ -269,8 +270,9 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd(void* ds, float* dweight, const 
 
 /* Bytes of workspace the two RMSNorm backward ops need: with the library's
  * choice, enough for any layout (strides, alignment) of this hidden size; or
- * for a given shape.  Pure host arithmetic; 0 for an unsupported hidden or
- * rows <= 0. */
+ * for a given shape.  Enough for either op (their kernels differ at 28680 ...
+ * 32768 columns, where the fused op streams its rows).  Pure host
+ * arithmetic; 0 for an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden);
 NORM_API size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                                      const norm_launch_cfg* cfg);

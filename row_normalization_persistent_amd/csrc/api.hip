@@ -245,11 +245,21 @@ int64_t max_dyn_hidden(const std::vector<Entry>& table, int w) {
     return m;
 }
 
+// The fused op's LDS-staged backward stops at 7 accesses a lane: at 8 (rows of
+// 28680 ... 32768 columns) the streamed tiles were faster, 4096 x 32768
+// 199 -> 178 us, 8192 x 32768 398 -> 340 us (at 7, 4096 x 28672, 165 against
+// 175 us streamed).
+constexpr int kWideFusedMaxVecs = 7;
+bool wide_serves(norm_op op, int vecs) {
+    return op != NORM_OP_FUSED_ADD_RMSNORM_BWD || vecs <= kWideFusedMaxVecs;
+}
+
 const WideBwdEntry* find_wide(norm_op op, int64_t hidden, int lanes, int w) {
     if (lanes != kWideBwdLanes || w != 8 || hidden % 8 ||
         hidden <= max_dyn_hidden(dyn_bwd_table(op), 8))
         return nullptr;
     const int64_t v = ceil_div(hidden, (int64_t)8 * kWideBwdLanes);
+    if (!wide_serves(op, (int)v)) return nullptr;
     const auto& t = op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_wide_table()
                                                 : rmsnorm_bwd_wide_table();
     for (const WideBwdEntry& e : t)
@@ -265,7 +275,9 @@ int64_t max_bwd_resident(norm_op op, int w) {
     if (w == 8) {
         const auto& t = op == NORM_OP_LAYERNORM_BWD ? layernorm_bwd_wide_table()
                                                     : rmsnorm_bwd_wide_table();
-        for (const WideBwdEntry& e : t) m = std::max<int64_t>(m, (int64_t)e.vecs * 8 * kWideBwdLanes);
+        for (const WideBwdEntry& e : t)
+            if (wide_serves(op, e.vecs))
+                m = std::max<int64_t>(m, (int64_t)e.vecs * 8 * kWideBwdLanes);
     }
     return m;
 }
@@ -1605,13 +1617,17 @@ size_t norm_layernorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
     return ws_query(NORM_OP_LAYERNORM_BWD, rows, hidden, cfg);
 }
 
+// Shared by the two RMSNorm backward ops, whose kernel choice differs where
+// the fused op streams rows the plain op stages in LDS: enough for either.
 size_t norm_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t hidden) {
-    return ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, nullptr);
+    return std::max(ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, nullptr),
+                    ws_query(NORM_OP_FUSED_ADD_RMSNORM_BWD, rows, hidden, nullptr));
 }
 
 size_t norm_rmsnorm_bwd_workspace_bytes_cfg(int64_t rows, int64_t hidden,
                                             const norm_launch_cfg* cfg) {
-    return ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, cfg);
+    return std::max(ws_query(NORM_OP_RMSNORM_BWD, rows, hidden, cfg),
+                    ws_query(NORM_OP_FUSED_ADD_RMSNORM_BWD, rows, hidden, cfg));
 }
 
 norm_status norm_select_config(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,

@@ -776,11 +776,11 @@ def test_f32_workspace_sizes():
 
 def test_wide_backward_host_logic():
     """Backward rows above 16384 run on 512-lane workgroups with the row
-    staged in LDS (5 to 8 16-byte accesses a lane, up to 32768), then on the
-    streamed kernels; narrower accesses stop at the register-resident
-    kernels' widest rows."""
+    staged in LDS (5 to 8 16-byte accesses a lane, up to 32768; the fused op
+    up to 7, 28672), then on the streamed kernels; narrower accesses stop at
+    the register-resident kernels' widest rows."""
     for op in ("layernorm_bwd", "rmsnorm_bwd", "fused_add_rmsnorm_bwd"):
-        for h in (16392, 20000, 24576, 32768):
+        for h in (16392, 20000, 24576, 28672) + ((32768,) if op != "fused_add_rmsnorm_bwd" else ()):
             c = rn.select_config(op, 8192, h)
             assert (c.threads_per_row, c.rows_per_block, c.grid, c.vector_elems) == \
                 (512, 1, 256, 8), (op, h, c)
@@ -790,7 +790,9 @@ def test_wide_backward_host_logic():
             outs = 2 if op == "layernorm_bwd" else 1
             padded = -(-h // 64) * 64
             assert rn.workspace_bytes(8192, h, op=op) == 256 * outs * padded * 4
-            assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4
+            # (the RMSNorm query covers the fused op, which streams 32768)
+            xch = 3 * 12 * 4 * 16 if op == "rmsnorm_bwd" and h == 32768 else 0
+            assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4 + xch
         # 9 accesses a lane: past the LDS-staged kernel, the streamed kernels
         c = rn.select_config(op, 8192, 32776)
         assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 51, 8)  # 255 // 5 tiles
@@ -799,6 +801,24 @@ def test_wide_backward_host_logic():
             rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels
         assert rn.select_config(op, 8192, 16384 - 8).threads_per_row != 512 or \
             rn.select_config(op, 8192, 16384 - 8).rows_per_block == 1
+    # the fused op at 8 accesses a lane (28680 ... 32768): the streamed kernels,
+    # 4 column tiles at 32768, 255 // 4 walkers
+    for h, tiles in ((28680, 4), (32768, 4)):
+        c = rn.select_config("fused_add_rmsnorm_bwd", 8192, h)
+        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 255 // tiles, 8), (h, c)
+        d = rn.describe_config("fused_add_rmsnorm_bwd", 8192, h)
+        assert "stream_bwd_tile_kernel" in d and "norm_bwd_wide_kernel" not in d
+        assert rn.list_configs("fused_add_rmsnorm_bwd", h) == [rn.Cfg(512, 1, 0, 8)]
+        # the query the two RMSNorm backward ops share covers both choices: the
+        # plain op's 256 staged slabs, or (few rows) the fused op's walkers'
+        # slabs and exchange slots
+        padded = -(-h // 64) * 64
+        assert rn.workspace_bytes(8192, h, op="fused_add_rmsnorm_bwd") == 256 * padded * 4
+        assert rn.workspace_bytes(3, h, op="fused_add_rmsnorm_bwd") == \
+            3 * padded * 4 + 3 * 12 * tiles * 16
+        assert rn.workspace_bytes(3, h, op="rmsnorm_bwd") == \
+            rn.workspace_bytes(3, h, op="fused_add_rmsnorm_bwd")
+    assert "norm_bwd_wide_kernel<8," in rn.describe_config("rmsnorm_bwd", 8192, 32768)
 
 
 def test_tuned_forward_table():

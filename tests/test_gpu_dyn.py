@@ -313,15 +313,18 @@ def test_bwd_widest_rows():
             check_bwd(op, bwd_inputs(op, 40, h, seed=6))
 
 
-@pytest.mark.parametrize("h", [16392, 20000, 24576, 32768])
+@pytest.mark.parametrize("h", [16392, 20000, 24576, 28672, 28680, 32768])
 def test_bwd_wide_rows_staged_in_lds(h):
     """Rows wider than the register-resident backward holds (16392 ... 32768):
-    512-lane workgroups with x and dy staged in LDS, 5 to 8 accesses a lane;
+    512-lane workgroups with x and dy staged in LDS, 5 to 8 accesses a lane
+    (the fused op up to 7, 28672: its wider rows take the streamed tiles);
     one row, a ragged 37 and 300 rows over the 256-workgroup grid."""
     for op in BWD_OPS:
         c = rn.select_config(op, 300, h)
         assert (c.threads_per_row, c.rows_per_block, c.vector_elems) == (512, 1, 8), (op, c)
-        assert "norm_bwd_wide_kernel" in rn.describe_config(op, 300, h)
+        streamed = op == "fused_add_rmsnorm_bwd" and h > 28672
+        assert ("stream_bwd_tile_kernel" if streamed else "norm_bwd_wide_kernel") in \
+            rn.describe_config(op, 300, h)
         for rows in (1, 37, 300):
             check_bwd(op, bwd_inputs(op, rows, h, seed=h + rows))
         if op == "fused_add_rmsnorm_bwd":
