@@ -303,7 +303,7 @@ int64_t max_bwd_hidden(norm_op op, int w) {
 // 512-lane workgroup per (walker, tile), at most 255 in all (one per CU,
 // leaving the partial sums of any width under 32 MiB).
 int32_t stream_tiles(int64_t hidden) {
-    return (int32_t)ceil_div(hidden, ROWNORM_STREAM_BWD_XCH ? kXchTileColsBf16 : kStreamTileCols);
+    return (int32_t)ceil_div(hidden, stream_bwd_xch(hidden) ? kXchTileColsBf16 : kStreamTileCols);
 }
 int32_t stream_walkers(int64_t rows, int64_t hidden) {
     return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles(hidden)));
@@ -632,10 +632,11 @@ size_t dyn_ws_bytes(norm_op op, int64_t hidden, int64_t slabs) {
 
 // Streamed backward: the walkers' slabs, then the exchange area of the
 // tiles' partial sums (per walker kXchRing rows of `tiles` 16-byte slots;
-// none with one tile, which reduces its rows itself).
+// none with one tile, which reduces its rows itself), or past kXchMaxTiles
+// tiles two floats a row (the row sums kernel's output).
 size_t stream_ws_bytes(norm_op op, int64_t hidden, int64_t walkers, int64_t rows,
                        int64_t tiles) {
-    if (!ROWNORM_STREAM_BWD_XCH)
+    if (!stream_bwd_xch(hidden))
         return dyn_ws_bytes(op, hidden, walkers) + (size_t)std::max<int64_t>(rows, 0) * 8;
     return dyn_ws_bytes(op, hidden, walkers) + (size_t)(rows > 0 ? xch_bytes(walkers, tiles) : 0);
 }
@@ -1651,9 +1652,9 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
     const bool streamed = dyn && (is_bwd(op) ? !wide && stream_bwd_ok(op, hidden, w)
                                              : stream_fwd_ok(op, hidden, w));
     if (streamed) {
-        vecs = !is_bwd(op) ? 0 : ROWNORM_STREAM_BWD_XCH ? kXchVecsBf16 : kStreamTileVecs;
+        vecs = !is_bwd(op) ? 0 : stream_bwd_xch(hidden) ? kXchVecsBf16 : kStreamTileVecs;
         depth = !is_bwd(op)                          ? 0
-                : ROWNORM_STREAM_BWD_XCH             ? kXchDepthBf16
+                : stream_bwd_xch(hidden)             ? kXchDepthBf16
                 : op == NORM_OP_FUSED_ADD_RMSNORM_BWD ? 2
                                                      : 3;
     } else if (wide) {
@@ -1683,7 +1684,7 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
         else
             std::snprintf(grid_text, sizeof grid_text, "%d", c.grid);
         char kern[256];
-        if (streamed && ROWNORM_STREAM_BWD_XCH)
+        if (streamed && stream_bwd_xch(hidden))
             std::snprintf(kern, sizeof kern,
                           "stream_zero_kernel (the exchange area), then "
                           "stream_bwd_tile_kernel<%d,%s,%d,exchange> over %d column tiles of %d "

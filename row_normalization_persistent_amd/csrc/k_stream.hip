@@ -171,7 +171,7 @@ hipError_t stream_bwd_typed(bool ln, const DynBwdArgs& a, int32_t tiles, int32_t
                        : a.dres        ? inrow_by_vecs<false, true>(a, walkers, stream)
                                        : inrow_by_vecs<false, false>(a, walkers, stream);
         if (e != hipSuccess) return e;
-    } else if (a.rows > 0 && ROWNORM_STREAM_BWD_XCH) {
+    } else if (a.rows > 0 && stream_bwd_xch(a.hidden)) {
         uint64_t* xch = (uint64_t*)(a.workspace + (int64_t)walkers * outs * padded);
         hipError_t e = ln       ? launch_tiles_xch<E, true, false>(a, xch, tiles, walkers, stream)
                        : a.dres ? launch_tiles_xch<E, false, true>(a, xch, tiles, walkers, stream)

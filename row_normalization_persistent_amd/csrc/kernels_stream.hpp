@@ -37,17 +37,17 @@
 // reductions -- LayerNorm sum_j g and sum_j g * xhat; RMSNorm sum_j x^2 and
 // sum_j g x, giving rstd = rsqrt(mean_j x^2 + eps) and coef = rstd^3 mean_j
 // g x -- come from one of:
-//  * XCH (the default past one tile): the tiles of a row exchange their
+//  * XCH (2 to kXchMaxTiles tiles a row): the tiles of a row exchange their
 //    partial sums through 64-bit slots in the workspace, a group of D rows
 //    per round trip (bf16: two rings, one group published ahead), with a
 //    bounded wait and a fallback that reads the other tiles' columns itself;
 //    each row is read once (stream_zero_kernel clears the slots first);
 //  * INROW (fp32 up to 8192 columns, one tile holds the row, V = 1, 2 or 4):
 //    the tile kernel reduces the row itself, one barrier a row;
-//  * stream_bwd_stats_kernel (1024 lanes, the path compiled with
-//    ROWNORM_STREAM_BWD_XCH=0): the two reductions of every row as two
-//    floats a row after the slabs, before the tile kernel, which then reads
-//    x and dy a second time.
+//  * stream_bwd_stats_kernel (1024 lanes; rows of more than kXchMaxTiles
+//    tiles, whose all-to-all exchange would cost more than a second read):
+//    the two reductions of every row as two floats a row after the slabs,
+//    before the tile kernel, which then reads x and dy a second time.
 #pragma once
 
 #include "dyn_common.hpp"

@@ -73,13 +73,22 @@ constexpr int kXchTileColsBf16 = kStreamTileLanes * kXchVecsBf16 * 8;
 #define ROWNORM_XCH_DEPTH 3
 #endif
 constexpr int kXchDepthBf16 = ROWNORM_XCH_DEPTH;  // ring rows
-constexpr int kXchMaxTiles = 128;  // 2^20 fp32 columns / 8192
+// The tiles exchange partial row sums up to kXchMaxTiles tiles a row (262144
+// columns; the exchange tiles of both element types are 8192 columns): every
+// tile polls every other tile's slots, so the exchange's traffic grows with
+// the square of the tiles, and past 32 the two-kernel path (row sums, then
+// tiles reading the row again) was faster (256 x 2^19 / 2^20: 262 / 530 us
+// against 312 / 1058 us).
+constexpr int kXchMaxTiles = 32;
 inline int64_t xch_bytes(int64_t walkers, int64_t tiles) {
     return tiles > 1 ? walkers * kXchRing * tiles * 16 : 0;
 }
 #ifndef ROWNORM_STREAM_BWD_XCH
 #define ROWNORM_STREAM_BWD_XCH 1
 #endif
+inline bool stream_bwd_xch(int64_t hidden) {
+    return ROWNORM_STREAM_BWD_XCH && (hidden + 8191) / 8192 <= kXchMaxTiles;
+}
 // Polls a tile's wait for its partners makes before it re-reads the row
 // itself (norm_bwd_set_spin_limit): by default about 16 ms, which a tile
 // whose partners run beside it never needs.

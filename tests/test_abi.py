@@ -301,6 +301,13 @@ def test_workspace_bytes():
     assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 12 * 8 * 16
     assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == \
         5 * 2 * 65536 * 4 + 5 * 12 * 8 * 16
+    # up to 32 tiles (262144 columns) the tiles exchange their partial sums;
+    # wider rows take the row sums kernel (8 bytes a row) and 16384-column tiles
+    assert rn.workspace_bytes(1000, 262144) == 7 * 2 * 262144 * 4 + 7 * 12 * 32 * 16
+    assert rn.workspace_bytes(1000, 262152) == 15 * 2 * 262208 * 4 + 1000 * 8
+    assert "exchanging partial row sums" in rn.describe_config("layernorm_bwd", 1000, 262144)
+    d = rn.describe_config("rmsnorm_bwd", 1000, 262152)
+    assert "stream_bwd_stats_kernel" in d and "15 row walkers x 17 column tiles" in d, d
     assert rn.workspace_bytes(-1, 4096) == 0
 
 
@@ -752,14 +759,17 @@ def test_f32_validation():
 def test_f32_workspace_sizes():
     """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
     column sum and row walker (at most 255 / ceil(hidden / 8192) walkers), plus
-    with more than one column tile the tiles' exchange area (per walker 12 walk
-    steps of 16 bytes a tile); at 8196 ... 16384 columns min(rows, 256) walkers."""
+    with 2 to 32 column tiles the tiles' exchange area (per walker 12 walk
+    steps of 16 bytes a tile), with more 8 bytes a row (the row sums); at
+    8196 ... 16384 columns min(rows, 256) walkers."""
     ws = rn.workspace_bytes_f32
     pad = lambda h: -(-h // 64) * 64
     assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4
     assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4
     assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4
-    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1 * 12 * 128 * 16
+    assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1000 * 8
+    assert ws("layernorm_bwd", 1000, 1 << 18) == 7 * 2 * (1 << 18) * 4 + 7 * 12 * 32 * 16
+    assert ws("layernorm_bwd", 1000, (1 << 18) + 4) == 7 * 2 * pad((1 << 18) + 4) * 4 + 1000 * 8
     assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 85 * 12 * 3 * 16
     # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs
     assert ws("layernorm_bwd", 1000, 16384) == 256 * 2 * 16384 * 4
