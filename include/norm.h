@@ -26,7 +26,9 @@
  *     kernels: forward, one pass for the statistic and one, mostly from the
  *     Infinity Cache, to normalize (the row read twice); backward,
  *     workgroups over 8192-column tiles that exchange each row's partial
- *     sums through the workspace, so the row is read once.  Forward rows that
+ *     sums through the workspace, so the row is read once (up to 262144
+ *     columns; wider rows: a row-sums kernel, then 16384-column tiles that
+ *     read the row again).  Forward rows that
  *     registers and LDS hold together are read once instead (the fused op
  *     up to 81920, RMSNorm from 69912 up to 114688: the rest of the row
  *     past the registers staged in LDS).  Wider rows with narrower accesses
@@ -220,10 +222,12 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
  * bytes, hidden rounded up to 64 off the compiled sizes, for each of its up
  * to 256 workgroups; rows past 32768 columns: the same for each of its up to
  * 255 / ceil(hidden / 8192) row walkers, each with 192 bytes of partial-sum
- * exchange slots per 8192-column tile) would exceed
+ * exchange slots per 8192-column tile; past 262144 columns for each of up to
+ * 255 / ceil(hidden / 16384) walkers, plus 8 bytes a row) would exceed
  * NORM_NOALLOC_SCRATCH_BYTES: every hidden up to 16384 fits, rows of
- * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows), and
- * wider rows fit at every row count.
+ * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows),
+ * rows of 32776-262144 columns fit at every row count, and wider rows fit
+ * up to at least 16384 rows.
  * NORM_ERROR_DEVICE when the
  * scratch array's address cannot be found on the current device.  All calls
  * on one device share its scratch array: calls that overlap in time on that
@@ -517,8 +521,10 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
  * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
  * (read once); wider rows take 512-lane workgroups over 8192-column tiles
- * that exchange each row's partial sums (read once); then the fixed-order
- * column reduce (column sums bitwise reproducible run to run).  workspace: at least
+ * that exchange each row's partial sums (read once; up to 262144 columns,
+ * wider rows: a row-sums kernel first, then the tiles read the row again);
+ * then the fixed-order column reduce (column sums bitwise reproducible run
+ * to run).  workspace: at least
  * norm_bwd_workspace_bytes_f32(op, rows, hidden) bytes, contents ignored on
  * entry. */
 NORM_API norm_status norm_fused_add_rmsnorm_f32(float* out, float* residual, const float* x,
@@ -552,7 +558,8 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, c
  * (hidden rounded up to 64) per partial-sum slab and output column sum, for
  * each row walker: min(rows, 256) of them at 8196 ... 16384 columns, else
  * max(1, min(rows, 255 / ceil(hidden / 8192))), each with 192 bytes of
- * partial-sum exchange slots per 8192-column tile.  Pure
+ * partial-sum exchange slots per 8192-column tile (up to 262144 columns;
+ * wider: 8 bytes a row instead).  Pure
  * host arithmetic; 0 for another op, an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);
 
