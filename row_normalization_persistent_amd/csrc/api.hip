@@ -306,7 +306,8 @@ int32_t stream_tiles(int64_t hidden) {
     return (int32_t)ceil_div(hidden, stream_bwd_xch(hidden) ? kXchTileColsBf16 : kStreamTileCols);
 }
 int32_t stream_walkers(int64_t rows, int64_t hidden) {
-    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles(hidden)));
+    const int cap = stream_bwd_xch(hidden) ? kXchWgCap : 255;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, cap / stream_tiles(hidden)));
 }
 
 // partial-sum slabs per walker: dweight and dbias for LayerNorm, dweight for RMSNorm
@@ -1710,13 +1711,17 @@ int32_t norm_describe_config(norm_op op, int64_t rows, int64_t hidden, int32_t c
                           op == NORM_OP_LAYERNORM_BWD ? "layernorm" : "rmsnorm",
                           (long long)hidden, c.threads_per_row, depth,
                           op == NORM_OP_LAYERNORM_BWD ? "" : ",dres?");
+        // a streamed row spans its tiles: the text gives a tile's workgroup
+        const bool xch = streamed && stream_bwd_xch(hidden);
         n = std::snprintf(tmp, sizeof tmp,
-                          "%s rows=%lld hidden=%lld: %s (%d lanes per row, %d rows per "
+                          "%s rows=%lld hidden=%lld: %s (%d lanes per %s, %d rows per "
                           "workgroup, %d %d-byte accesses per lane, ring of %d rows) on a "
                           "persistent grid of %s workgroups, then norm_bwd_colreduce_kernel "
                           "(%lld workgroups of %d) over %lld slabs; workspace %zu bytes",
                           kNames[op], (long long)rows, (long long)hidden, kern,
-                          c.threads_per_row, c.rows_per_block, vecs, 2 * w, depth, grid_text,
+                          xch ? kXchLanesBf16 : c.threads_per_row,
+                          streamed ? "workgroup" : "row", c.rows_per_block, vecs, 2 * w,
+                          xch ? 2 * depth : depth, grid_text,
                           (long long)(bwd_outs(op) * padded / colreduce_cols(slabs)),
                           kColReduceThreads,
                           (long long)slabs,

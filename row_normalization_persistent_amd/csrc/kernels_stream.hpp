@@ -639,11 +639,10 @@ struct TileRow {
 // loads zeros from no memory and statistics of zero, so it adds nothing).
 // INROW: the tile is the whole row and its statistics are reduced from the
 // loaded row (tile_row), not read from the stats kernel's output.
-template <typename E, int V, bool LN, bool DRES, bool INROW, bool XCH = false>
+template <typename E, int V, bool LN, bool DRES, bool INROW, bool XCH, int T>
 __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdArgs& a,
                                               const float* stats, int64_t row, int acc0,
                                               int lane) {
-    constexpr int T = kStreamTileLanes;
     constexpr int ES = (int)sizeof(E);
     const int h = a.hidden;
     const rsrc_t rx = row_rsrc_ld(a.x, row, a.rows, a.ld_x * ES, h * ES);
@@ -756,12 +755,11 @@ __device__ __forceinline__ uint64_t xch_word(float v, int64_t row) {
 // s1, s2 as formed): tile by tile, each formed as its own workgroup forms it,
 // then added in tile order.  Plain loads (no buffer descriptors held in
 // scalar registers on this rare path).  Uniform control flow.
-template <typename E, int V, bool LN>
+template <typename E, int V, bool LN, int T>
 __device__ __forceinline__ void xch_reread_row(const DynBwdArgs& a, int64_t row, int tiles,
                                                int tile, float s1, float s2, float mean,
                                                float rstd, float* redf, int lane, float& S1,
                                                float& S2) {
-    constexpr int T = kStreamTileLanes;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     const int h = a.hidden;
@@ -803,13 +801,12 @@ __device__ __forceinline__ void xch_reread_row(const DynBwdArgs& a, int64_t row,
     }
 }
 
-template <typename E, int V, bool LN, bool DRES, bool INROW>
+template <typename E, int V, bool LN, bool DRES, bool INROW, int T>
 __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[V],
                                          float (&pw)[V][Elems<E>::kPer],
                                          float (&pb)[LN ? V : 1][Elems<E>::kPer],
                                          const DynBwdArgs& a, int64_t row, int acc0, int lane,
                                          float* red) {
-    constexpr int T = kStreamTileLanes;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     if constexpr (INROW) {
@@ -897,7 +894,8 @@ __global__ __launch_bounds__(256) void stream_zero_kernel(u32x4* p, int64_t n) {
 template <typename E, int V, bool LN, bool DRES, int D, bool INROW = false, bool XCH = false>
 __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     DynBwdArgs a, const float* stats, int tiles, uint64_t* xch, uint32_t spin_limit) {
-    constexpr int T = kStreamTileLanes;
+    // lanes: kXchLanesBf16 for the bf16 exchange, else kStreamTileLanes
+    constexpr int T = XCH && sizeof(E) == 2 ? kXchLanesBf16 : kStreamTileLanes;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     static_assert(!(INROW && XCH), "one way to form the row's sums");
@@ -940,7 +938,7 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     TileRow<V, DRES> buf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, opaque_row(walker + d * P),
+        load_tile_row<E, V, LN, DRES, INROW, XCH, T>(buf[d], a, stats, opaque_row(walker + d * P),
                                                   acc0, lane);
         issue_fence();
     }
@@ -1053,7 +1051,7 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
                             S2 += xq2[d * kXchMaxTiles + tp];
                         }
                     } else {
-                        xch_reread_row<E, V, LN>(a, r0 + d * P, tiles, tile,
+                        xch_reread_row<E, V, LN, T>(a, r0 + d * P, tiles, tile,
                                                  xown[k * 2 * D + 2 * d],
                                                  xown[k * 2 * D + 2 * d + 1], rb[d].mean,
                                                  rb[d].rstd, redf, lane, S1, S2);
@@ -1083,9 +1081,9 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int64_t r = opaque_row(walker + (i + d) * P);
-                tile_row<E, V, LN, DRES, false>(rb[d], wv, pw, pb, a, r, acc0, lane, nullptr);
+                tile_row<E, V, LN, DRES, false, T>(rb[d], wv, pw, pb, a, r, acc0, lane, nullptr);
                 issue_fence();
-                load_tile_row<E, V, LN, DRES, INROW, XCH>(rb[d], a, stats, r + kStep * P, acc0,
+                load_tile_row<E, V, LN, DRES, INROW, XCH, T>(rb[d], a, stats, r + kStep * P, acc0,
                                                           lane);
                 issue_fence();
             }
@@ -1095,7 +1093,7 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
             TileRow<V, DRES> buf2[D];
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                load_tile_row<E, V, LN, DRES, INROW, XCH>(
+                load_tile_row<E, V, LN, DRES, INROW, XCH, T>(
                     buf2[d], a, stats, opaque_row(walker + (D + d) * P), acc0, lane);
                 issue_fence();
             }
@@ -1117,11 +1115,11 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int64_t r = opaque_row(walker + (i + d) * P);
-                tile_row<E, V, LN, DRES, INROW>(buf[d], wv, pw, pb, a, r, acc0, lane,
+                tile_row<E, V, LN, DRES, INROW, T>(buf[d], wv, pw, pb, a, r, acc0, lane,
                                                 red + parity * 2 * (T / kWave));
                 parity ^= 1;
                 issue_fence();
-                load_tile_row<E, V, LN, DRES, INROW, XCH>(buf[d], a, stats, r + D * P, acc0,
+                load_tile_row<E, V, LN, DRES, INROW, XCH, T>(buf[d], a, stats, r + D * P, acc0,
                                                           lane);
                 issue_fence();
             }

@@ -65,21 +65,38 @@ constexpr int kXchRing = ROWNORM_XCH_RING;
 #define ROWNORM_XCH_AHEAD 1
 #endif
 constexpr bool kXchAhead = ROWNORM_XCH_AHEAD != 0;
-// bf16 tiles of the exchanging kernel: 512 lanes x 2 accesses (8192 columns;
-// at 4 accesses the exchange's registers push the kernel into spills)
+// bf16 tiles of the exchanging kernel: 256 lanes x 2 accesses (4096 columns;
+// at 4 accesses the exchange's registers push the kernel into spills).  Two
+// such workgroups fit a CU (at most 256 VGPRs a lane, the kernel's launch
+// bound), so one's barriers and waits overlap the other's loads: against one
+// 512-lane workgroup a CU, 4096 x 65536 fused 357 -> 322 us, RMSNorm
+// 324 -> 302, LayerNorm 360 -> 349, 8192 x 40000 416 -> 396.
 constexpr int kXchVecsBf16 = 2;
-constexpr int kXchTileColsBf16 = kStreamTileLanes * kXchVecsBf16 * 8;
+#ifndef ROWNORM_XCH_LANES
+#define ROWNORM_XCH_LANES 256
+#endif
+constexpr int kXchLanesBf16 = ROWNORM_XCH_LANES;
+constexpr int kXchTileColsBf16 = kXchLanesBf16 * kXchVecsBf16 * 8;
+// workgroups of a bf16 streamed backward with the exchange: two a CU, all
+// co-resident on 256 CUs
+#ifndef ROWNORM_XCH_WG_CAP
+#define ROWNORM_XCH_WG_CAP 511
+#endif
+constexpr int kXchWgCap = ROWNORM_XCH_WG_CAP;
 #ifndef ROWNORM_XCH_DEPTH
 #define ROWNORM_XCH_DEPTH 3
 #endif
 constexpr int kXchDepthBf16 = ROWNORM_XCH_DEPTH;  // ring rows
-// The tiles exchange partial row sums up to kXchMaxTiles tiles a row (262144
-// columns; the exchange tiles of both element types are 8192 columns): every
-// tile polls every other tile's slots, so the exchange's traffic grows with
-// the square of the tiles, and past 32 the two-kernel path (row sums, then
-// tiles reading the row again) was faster (256 x 2^19 / 2^20: 262 / 530 us
-// against 312 / 1058 us).
-constexpr int kXchMaxTiles = 32;
+// The tiles exchange partial row sums up to kXchMaxTiles bf16 tiles a row
+// (262144 columns; fp32 tiles are 8192 columns, so fp32 rows stop at 64
+// tiles' worth too): every tile polls every other tile's slots, so the
+// exchange's traffic grows with the square of the tiles, and past 262144
+// columns the two-kernel path (row sums, then tiles reading the row again)
+// was faster (256 x 2^19 / 2^20: 262 / 530 us against 312 / 1058 us).
+#ifndef ROWNORM_XCH_MAX_TILES
+#define ROWNORM_XCH_MAX_TILES 64
+#endif
+constexpr int kXchMaxTiles = ROWNORM_XCH_MAX_TILES;
 inline int64_t xch_bytes(int64_t walkers, int64_t tiles) {
     return tiles > 1 ? walkers * kXchRing * tiles * 16 : 0;
 }
@@ -87,7 +104,8 @@ inline int64_t xch_bytes(int64_t walkers, int64_t tiles) {
 #define ROWNORM_STREAM_BWD_XCH 1
 #endif
 inline bool stream_bwd_xch(int64_t hidden) {
-    return ROWNORM_STREAM_BWD_XCH && (hidden + 8191) / 8192 <= kXchMaxTiles;
+    return ROWNORM_STREAM_BWD_XCH &&
+           (hidden + kXchTileColsBf16 - 1) / kXchTileColsBf16 <= kXchMaxTiles;
 }
 // Polls a tile's wait for its partners makes before it re-reads the row
 // itself (norm_bwd_set_spin_limit): by default about 16 ms, which a tile

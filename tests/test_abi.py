@@ -261,7 +261,7 @@ def test_describe_config():
     with pytest.raises(rn.NormError):
         rn.describe_config("rmsnorm_fwd", 4, 70002, cu_count=256)
     d = rn.describe_config("layernorm_bwd", 1000, 65536, cu_count=256)
-    assert "31 row walkers x 8 column tiles" in d and "exchanging partial row sums" in d and \
+    assert "31 row walkers x 16 column tiles" in d and "exchanging partial row sums" in d and \
         f"workspace {rn.workspace_bytes(1000, 65536)}" in d
     d = rn.describe_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     c = rn.select_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
@@ -293,17 +293,18 @@ def test_workspace_bytes():
     assert rn.workspace_bytes(100, 1000, rn.Cfg(16, 16, 7, 8)) == 7 * 2 * 1024 * 4
     assert rn.workspace_bytes(8192, 1000) >= 256 * 2 * 1024 * 4
     assert rn.workspace_bytes(10, (1 << 20) + 8) == 0
-    # streamed rows: one slab per row walker (255 // column tiles of 8192, at
+    # streamed rows: one slab per row walker (511 // column tiles of 4096, at
     # most the rows), then the tiles' exchange area: per walker 12 walk steps
     # of 16 bytes a tile
-    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 12 * 9 * 16
-    assert rn.workspace_bytes(1000, 65536) == 31 * 2 * 65536 * 4 + 31 * 12 * 8 * 16
-    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 12 * 8 * 16
+    assert rn.workspace_bytes(10, 70000) == 10 * 2 * 70016 * 4 + 10 * 12 * 18 * 16
+    assert rn.workspace_bytes(1000, 65536) == 31 * 2 * 65536 * 4 + 31 * 12 * 16 * 16
+    assert rn.workspace_bytes(1000, 65536, op="rmsnorm_bwd") == 31 * 65536 * 4 + 31 * 12 * 16 * 16
     assert rn.workspace_bytes(1000, 65536, rn.Cfg(512, 1, 5, 8)) == \
-        5 * 2 * 65536 * 4 + 5 * 12 * 8 * 16
-    # up to 32 tiles (262144 columns) the tiles exchange their partial sums;
-    # wider rows take the row sums kernel (8 bytes a row) and 16384-column tiles
-    assert rn.workspace_bytes(1000, 262144) == 7 * 2 * 262144 * 4 + 7 * 12 * 32 * 16
+        5 * 2 * 65536 * 4 + 5 * 12 * 16 * 16
+    # up to 64 tiles (262144 columns) the tiles exchange their partial sums;
+    # wider rows take the row sums kernel (8 bytes a row) and 16384-column
+    # tiles, 255 // tiles walkers
+    assert rn.workspace_bytes(1000, 262144) == 7 * 2 * 262144 * 4 + 7 * 12 * 64 * 16
     assert rn.workspace_bytes(1000, 262152) == 15 * 2 * 262208 * 4 + 1000 * 8
     assert "exchanging partial row sums" in rn.describe_config("layernorm_bwd", 1000, 262144)
     d = rn.describe_config("rmsnorm_bwd", 1000, 262152)
@@ -801,21 +802,21 @@ def test_wide_backward_host_logic():
             padded = -(-h // 64) * 64
             assert rn.workspace_bytes(8192, h, op=op) == 256 * outs * padded * 4
             # (the RMSNorm query covers the fused op, which streams 32768)
-            xch = 3 * 12 * 4 * 16 if op == "rmsnorm_bwd" and h == 32768 else 0
+            xch = 3 * 12 * 8 * 16 if op == "rmsnorm_bwd" and h == 32768 else 0
             assert rn.workspace_bytes(3, h, op=op) == 3 * outs * padded * 4 + xch
         # 9 accesses a lane: past the LDS-staged kernel, the streamed kernels
         c = rn.select_config(op, 8192, 32776)
-        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 51, 8)  # 255 // 5 tiles
+        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 56, 8)  # 511 // 9 tiles
         assert "stream_bwd_tile_kernel" in rn.describe_config(op, 8192, 32776)
         with pytest.raises(rn.NormError):
             rn.select_config(op, 8192, 20002)   # 4-byte accesses: up to the run-time kernels
         assert rn.select_config(op, 8192, 16384 - 8).threads_per_row != 512 or \
             rn.select_config(op, 8192, 16384 - 8).rows_per_block == 1
     # the fused op at 8 accesses a lane (28680 ... 32768): the streamed kernels,
-    # 4 column tiles at 32768, 255 // 4 walkers
-    for h, tiles in ((28680, 4), (32768, 4)):
+    # 8 column tiles of 4096, 511 // 8 walkers
+    for h, tiles in ((28680, 8), (32768, 8)):
         c = rn.select_config("fused_add_rmsnorm_bwd", 8192, h)
-        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 255 // tiles, 8), (h, c)
+        assert (c.threads_per_row, c.grid, c.vector_elems) == (512, 511 // tiles, 8), (h, c)
         d = rn.describe_config("fused_add_rmsnorm_bwd", 8192, h)
         assert "stream_bwd_tile_kernel" in d and "norm_bwd_wide_kernel" not in d
         assert rn.list_configs("fused_add_rmsnorm_bwd", h) == [rn.Cfg(512, 1, 0, 8)]
