@@ -25,7 +25,7 @@
  *     16-byte accesses (hidden a multiple of 8, up to 2^20) run on streamed
  *     kernels: forward, one pass for the statistic and one, mostly from the
  *     Infinity Cache, to normalize (the row read twice); backward,
- *     workgroups over 8192-column tiles that exchange each row's partial
+ *     workgroups over 4096-column tiles that exchange each row's partial
  *     sums through the workspace, so the row is read once (up to 262144
  *     columns; wider rows: a row-sums kernel, then 16384-column tiles that
  *     read the row again).  Forward rows that
@@ -221,8 +221,8 @@ NORM_API norm_status norm_layernorm_bwd(void* dx, float* dweight, float* dbias,
  * (norm_layernorm_bwd_workspace_bytes for contiguous rows: 2 * 4 * hidden
  * bytes, hidden rounded up to 64 off the compiled sizes, for each of its up
  * to 256 workgroups; rows past 32768 columns: the same for each of its up to
- * 255 / ceil(hidden / 8192) row walkers, each with 192 bytes of partial-sum
- * exchange slots per 8192-column tile; past 262144 columns for each of up to
+ * 511 / ceil(hidden / 4096) row walkers, each with 192 bytes of partial-sum
+ * exchange slots per 4096-column tile; past 262144 columns for each of up to
  * 255 / ceil(hidden / 16384) walkers, plus 8 bytes a row) would exceed
  * NORM_NOALLOC_SCRATCH_BYTES: every hidden up to 16384 fits, rows of
  * 16392-32768 columns fit only with fewer rows (32768: up to 128 rows),
@@ -520,9 +520,10 @@ NORM_API int32_t norm_list_configs(norm_op op, int64_t hidden, norm_launch_cfg* 
  * RMSNorm rows of 34956 ... 69632, whose rest is staged in LDS (read once).
  * Backward: rows of up to 8192 columns are held by one 512-lane workgroup
  * that reduces the row itself; 8196 ... 16384 columns are staged in LDS
- * (read once); wider rows take 512-lane workgroups over 8192-column tiles
+ * (read once); wider rows take 256-lane workgroups over 4096-column tiles
  * that exchange each row's partial sums (read once; up to 262144 columns,
- * wider rows: a row-sums kernel first, then the tiles read the row again);
+ * wider rows: a row-sums kernel first, then 512-lane workgroups over
+ * 8192-column tiles read the row again);
  * then the fixed-order column reduce (column sums bitwise reproducible run
  * to run).  workspace: at least
  * norm_bwd_workspace_bytes_f32(op, rows, hidden) bytes, contents ignored on
@@ -556,10 +557,11 @@ NORM_API norm_status norm_fused_add_rmsnorm_bwd_f32(float* ds, float* dweight, c
 /* Workspace bytes of an fp32 backward op (NORM_OP_LAYERNORM_BWD,
  * NORM_OP_RMSNORM_BWD or NORM_OP_FUSED_ADD_RMSNORM_BWD): 4 * padded hidden
  * (hidden rounded up to 64) per partial-sum slab and output column sum, for
- * each row walker: min(rows, 256) of them at 8196 ... 16384 columns, else
- * max(1, min(rows, 255 / ceil(hidden / 8192))), each with 192 bytes of
- * partial-sum exchange slots per 8192-column tile (up to 262144 columns;
- * wider: 8 bytes a row instead).  Pure
+ * each row walker: min(rows, 255) of them up to 8192 columns, min(rows,
+ * 256) at 8196 ... 16384, max(1, min(rows, 511 / ceil(hidden / 4096))) at
+ * 16388 ... 262144, each with 192 bytes of partial-sum exchange slots per
+ * 4096-column tile, and past that max(1, min(rows, 255 / ceil(hidden /
+ * 8192))) plus 8 bytes a row.  Pure
  * host arithmetic; 0 for another op, an unsupported hidden or rows <= 0. */
 NORM_API size_t norm_bwd_workspace_bytes_f32(norm_op op, int64_t rows, int64_t hidden);
 

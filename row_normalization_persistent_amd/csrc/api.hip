@@ -1176,11 +1176,19 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
 // twice; the backward reads a row of up to 16384 values once (one tile of the
 // tile kernel up to 8192, LDS above) and a wider one twice (the streamed
 // pair), then the column reduce.
+// One 512-lane tile holds a row of up to kStreamTileColsF32 (reduced in the
+// tile); wider rows: exchange tiles of kXchTileColsF32 up to the exchange's
+// width, else the row sums kernel's 8192-column tiles.
 int32_t stream_tiles_f32(int64_t hidden) {
-    return (int32_t)ceil_div(hidden, kStreamTileColsF32);
+    if (hidden <= kStreamTileColsF32) return 1;
+    return (int32_t)ceil_div(hidden, stream_bwd_xch(hidden) ? kXchTileColsF32 : kStreamTileColsF32);
 }
 int32_t stream_walkers_f32(int64_t rows, int64_t hidden) {
-    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, 255 / stream_tiles_f32(hidden)));
+    const int32_t tiles = stream_tiles_f32(hidden);
+    const int cap = tiles > 1 && stream_bwd_xch(hidden) && kXchLanesF32 < kStreamTileLanes
+                        ? kXchWgCap
+                        : 255;
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, cap / tiles));
 }
 bool f32_hidden_ok(int64_t hidden) {
     return hidden >= 4 && hidden % 4 == 0 && hidden <= kStreamMaxHidden;

@@ -132,7 +132,7 @@ hipError_t launch_tiles_xch(const DynBwdArgs& a, uint64_t* xch, int32_t tiles, i
     constexpr int D = kF32 ? tile_depth<LN, DRES>() : kXchDepthBf16;
     hipLaunchKernelGGL(
         (stream_bwd_tile_kernel<E, V, LN, DRES, D, false, true>),
-        dim3((unsigned)(walkers * tiles)), dim3(kF32 ? kStreamTileLanes : kXchLanesBf16), 0,
+        dim3((unsigned)(walkers * tiles)), dim3(kF32 ? kXchLanesF32 : kXchLanesBf16), 0,
         stream, a, (const float*)nullptr, (int)tiles, xch, stream_bwd_spin_limit());
     return hipGetLastError();
 }

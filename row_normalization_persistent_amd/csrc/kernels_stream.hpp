@@ -894,8 +894,8 @@ __global__ __launch_bounds__(256) void stream_zero_kernel(u32x4* p, int64_t n) {
 template <typename E, int V, bool LN, bool DRES, int D, bool INROW = false, bool XCH = false>
 __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     DynBwdArgs a, const float* stats, int tiles, uint64_t* xch, uint32_t spin_limit) {
-    // lanes: kXchLanesBf16 for the bf16 exchange, else kStreamTileLanes
-    constexpr int T = XCH && sizeof(E) == 2 ? kXchLanesBf16 : kStreamTileLanes;
+    // lanes: the exchange's kXchLanesBf16 / kXchLanesF32, else kStreamTileLanes
+    constexpr int T = !XCH ? kStreamTileLanes : sizeof(E) == 2 ? kXchLanesBf16 : kXchLanesF32;
     constexpr int EP = Elems<E>::kPer;
     constexpr int ES = (int)sizeof(E);
     static_assert(!(INROW && XCH), "one way to form the row's sums");

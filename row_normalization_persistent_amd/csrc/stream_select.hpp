@@ -77,6 +77,16 @@ constexpr int kXchVecsBf16 = 2;
 #endif
 constexpr int kXchLanesBf16 = ROWNORM_XCH_LANES;
 constexpr int kXchTileColsBf16 = kXchLanesBf16 * kXchVecsBf16 * 8;
+// fp32 exchange tiles (rows past one 8192-column tile): 256 lanes x 4
+// accesses (4096 columns), two workgroups a CU as for bf16: against 512
+// lanes, 4096 x 20480 LayerNorm 207.7 -> 188.5 us, 8192 x 16388 RMSNorm
+// 355 -> 322, 2048 x 65536 fused 345 -> 330, 2048 x 32768 LayerNorm 163 ->
+// 158.5; 1.5-5 % slower at 131072 / 262144 columns (512 / 128 rows).
+#ifndef ROWNORM_XCH_LANES_F32
+#define ROWNORM_XCH_LANES_F32 256
+#endif
+constexpr int kXchLanesF32 = ROWNORM_XCH_LANES_F32;
+constexpr int kXchTileColsF32 = kXchLanesF32 * 4 * 4;
 // workgroups of a bf16 streamed backward with the exchange: two a CU, all
 // co-resident on 256 CUs
 #ifndef ROWNORM_XCH_WG_CAP

@@ -759,19 +759,21 @@ def test_f32_validation():
 
 def test_f32_workspace_sizes():
     """Workspace of the fp32 backward: a slab of padded hidden fp32 per output
-    column sum and row walker (at most 255 / ceil(hidden / 8192) walkers), plus
-    with 2 to 32 column tiles the tiles' exchange area (per walker 12 walk
-    steps of 16 bytes a tile), with more 8 bytes a row (the row sums); at
-    8196 ... 16384 columns min(rows, 256) walkers."""
+    column sum and row walker, plus the tiles' partial-sum exchange area (per
+    walker 12 walk steps of 16 bytes a tile) over 16388 ... 262144 columns
+    (tiles of 4096, at most 511 / tiles walkers), 8 bytes a row (the row
+    sums) past that (tiles of 8192, at most 255 / tiles walkers); one tile
+    up to 8192 columns (min(rows, 255) walkers); at 8196 ... 16384 columns
+    min(rows, 256) walkers."""
     ws = rn.workspace_bytes_f32
     pad = lambda h: -(-h // 64) * 64
     assert ws("layernorm_bwd", 8192, 4096) == 255 * 2 * 4096 * 4
     assert ws("rmsnorm_bwd", 8192, 4096) == 255 * 4096 * 4
     assert ws("fused_add_rmsnorm_bwd", 3, 4100) == 3 * pad(4100) * 4
     assert ws("layernorm_bwd", 1000, 1 << 20) == 1 * 2 * (1 << 20) * 4 + 1000 * 8
-    assert ws("layernorm_bwd", 1000, 1 << 18) == 7 * 2 * (1 << 18) * 4 + 7 * 12 * 32 * 16
+    assert ws("layernorm_bwd", 1000, 1 << 18) == 7 * 2 * (1 << 18) * 4 + 7 * 12 * 64 * 16
     assert ws("layernorm_bwd", 1000, (1 << 18) + 4) == 7 * 2 * pad((1 << 18) + 4) * 4 + 1000 * 8
-    assert ws("layernorm_bwd", 1000, 16384 + 4) == 85 * 2 * pad(16388) * 4 + 85 * 12 * 3 * 16
+    assert ws("layernorm_bwd", 1000, 16384 + 4) == 102 * 2 * pad(16388) * 4 + 102 * 12 * 5 * 16
     # 8196 ... 16384 columns: the LDS-staged kernel, min(rows, 256) slabs
     assert ws("layernorm_bwd", 1000, 16384) == 256 * 2 * 16384 * 4
     assert ws("rmsnorm_bwd", 3, 8196) == 3 * pad(8196) * 4

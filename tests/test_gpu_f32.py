@@ -1,8 +1,8 @@
 """GPU parity of the fp32-activation entry points (`norm_*_f32`) against the
 CPU oracle's fp32 functions, through the C ABI: the six operations over
 widths from 4 to 2^20 columns (ragged tails of the 16-byte accesses, the
-8192-column tiles of the backward and the 1024-lane passes of the forward),
-row counts from 1 to the thousands, in-place calls, LayerNorm without
+4096- and 8192-column tiles of the backward and the 1024-lane passes of the
+forward), row counts from 1 to the thousands, in-place calls, LayerNorm without
 statistics, zero rows, memory past the outputs left untouched, bitwise
 run-to-run determinism, and graph replays.  Rules (the fp32 bound derived
 from the kernels' summation order) in parity.py."""
@@ -39,6 +39,8 @@ def f64(a):
 def walkers(rows, h):
     if 8196 <= h <= 16384:  # the LDS-staged kernel: one slab per workgroup
         return max(1, min(rows, 256))
+    if 16388 <= h <= 262144:  # exchange tiles of 4096 columns, two workgroups a CU
+        return max(1, min(rows, 511 // -(-h // 4096)))
     return max(1, min(rows, 255 // -(-h // 8192)))
 
 
