@@ -666,9 +666,18 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
         t.s1 = in ? s1 : 0.0f;
     }
     if constexpr (LN) {
-        const float m = a.mean[rc], q = a.rstd[rc];
-        t.mean = in ? m : 0.0f;
-        t.rstd = in ? q : 0.0f;
+        if constexpr (XCH && kXchVecStats) {
+            // vector loads (an opaque lane index): counted with the row's own
+            // loads, not with the LDS reductions' scalar counter; the uses
+            // zero a past-end row's values, a select here would wait
+            const int ri = opaque_lane((int)rc);
+            t.mean = a.mean[ri];
+            t.rstd = a.rstd[ri];
+        } else {
+            const float m = a.mean[rc], q = a.rstd[rc];
+            t.mean = in ? m : 0.0f;
+            t.rstd = in ? q : 0.0f;
+        }
     }
 }
 
@@ -846,6 +855,8 @@ __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[
         }
     }
     const rsrc_t rdx = row_rsrc_ld(a.dx, row, a.rows, a.ld_dx * ES, a.hidden * ES);
+    // LayerNorm: a past-end row's statistics are zero (loads may leave them raw)
+    const float tm = LN && t.in ? t.mean : 0.0f, tr = LN && t.in ? t.rstd : 0.0f;
 #pragma unroll
     for (int b = 0; b < V; ++b) {
         float xf[EP], df[EP], wf[EP], o[EP];
@@ -856,8 +867,8 @@ __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[
         for (int e = 0; e < EP; ++e) {
             const float g = df[e] * wf[e];
             if constexpr (LN) {
-                const float xh = (xf[e] - t.mean) * t.rstd;
-                o[e] = t.rstd * (g - t.s0 - xh * t.s1);
+                const float xh = (xf[e] - tm) * tr;
+                o[e] = tr * (g - t.s0 - xh * t.s1);
                 pw[b][e] += df[e] * xh;
                 pb[b][e] += df[e];
             } else {
@@ -965,8 +976,8 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
             float v[2 * D];
 #pragma unroll
             for (int d = 0; d < D; ++d)
-                tile_sums<E, V, LN>(rb[d].x, rb[d].dy, wv, rb[d].mean, rb[d].rstd, v[2 * d],
-                                    v[2 * d + 1]);
+                tile_sums<E, V, LN>(rb[d].x, rb[d].dy, wv, rb[d].in ? rb[d].mean : 0.0f,
+                                    rb[d].in ? rb[d].rstd : 0.0f, v[2 * d], v[2 * d + 1]);
             row_sum_n<T, 2 * D>(v, red + parity * 2 * D * (T / kWave), lane);
             parity ^= 1;
             const int64_t r0 = opaque_row(walker + i * P);
@@ -1053,8 +1064,10 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
                     } else {
                         xch_reread_row<E, V, LN, T>(a, r0 + d * P, tiles, tile,
                                                  xown[k * 2 * D + 2 * d],
-                                                 xown[k * 2 * D + 2 * d + 1], rb[d].mean,
-                                                 rb[d].rstd, redf, lane, S1, S2);
+                                                 xown[k * 2 * D + 2 * d + 1],
+                                                 rb[d].in ? rb[d].mean : 0.0f,
+                                                 rb[d].in ? rb[d].rstd : 0.0f, redf, lane, S1,
+                                                 S2);
                     }
                 }
                 TileRow<V, DRES>& t = rb[d];

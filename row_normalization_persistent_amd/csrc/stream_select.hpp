@@ -65,6 +65,15 @@ constexpr int kXchRing = ROWNORM_XCH_RING;
 #define ROWNORM_XCH_AHEAD 1
 #endif
 constexpr bool kXchAhead = ROWNORM_XCH_AHEAD != 0;
+// LayerNorm's per-row mean and rstd by vector loads in the exchanging kernel:
+// scalar loads share their counter with LDS, so each group's reductions
+// waited for the statistics of the rows just reloaded.  Against scalar
+// loads: bf16 4096 x 65536 350 -> 322 us, 2048 x 98304 267 -> 247,
+// 1024 x 131072 200 -> 187, 8192 x 40000 397 -> 375; fp32 1-2 %.
+#ifndef ROWNORM_XCH_VEC_STATS
+#define ROWNORM_XCH_VEC_STATS 1
+#endif
+constexpr bool kXchVecStats = ROWNORM_XCH_VEC_STATS != 0;
 // bf16 tiles of the exchanging kernel: 256 lanes x 2 accesses (4096 columns;
 // at 4 accesses the exchange's registers push the kernel into spills).  Two
 // such workgroups fit a CU (at most 256 VGPRs a lane, the kernel's launch
