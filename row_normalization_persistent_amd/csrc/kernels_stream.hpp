@@ -666,7 +666,7 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
         t.s1 = in ? s1 : 0.0f;
     }
     if constexpr (LN) {
-        if constexpr (XCH && kXchVecStats) {
+        if constexpr ((XCH && kXchVecStats) || (INROW && kInrowVecStats)) {
             // vector loads (an opaque lane index): counted with the row's own
             // loads, not with the LDS reductions' scalar counter; the uses
             // zero a past-end row's values, a select here would wait
@@ -820,6 +820,7 @@ __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[
     constexpr int ES = (int)sizeof(E);
     if constexpr (INROW) {
         // the row's two reductions, as stream_bwd_stats_kernel forms them
+        const float tmi = LN && t.in ? t.mean : 0.0f, tri = LN && t.in ? t.rstd : 0.0f;
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int b = 0; b < V; ++b) {
@@ -832,7 +833,7 @@ __device__ __forceinline__ void tile_row(TileRow<V, DRES>& t, const u32x4 (&wv)[
                 const float g = df[e] * wf[e];
                 if constexpr (LN) {
                     s1 += g;
-                    s2 += g * ((xf[e] - t.mean) * t.rstd);
+                    s2 += g * ((xf[e] - tmi) * tri);
                 } else {
                     s1 += xf[e] * xf[e];
                     s2 += g * xf[e];

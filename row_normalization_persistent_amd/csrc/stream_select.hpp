@@ -74,6 +74,13 @@ constexpr bool kXchAhead = ROWNORM_XCH_AHEAD != 0;
 #define ROWNORM_XCH_VEC_STATS 1
 #endif
 constexpr bool kXchVecStats = ROWNORM_XCH_VEC_STATS != 0;
+// the same for the fp32 one-tile kernel, which reduces each row in LDS:
+// 8192 x 1024 33.5 -> 30.3 us, 8192 x 4096 75.8 -> 73.8, level at 4096 x 8192
+// and 16384 x 4096, 16384 x 2048 80.7 -> 82 (2 % slower)
+#ifndef ROWNORM_INROW_VEC_STATS
+#define ROWNORM_INROW_VEC_STATS 1
+#endif
+constexpr bool kInrowVecStats = ROWNORM_INROW_VEC_STATS != 0;
 // bf16 tiles of the exchanging kernel: 256 lanes x 2 accesses (4096 columns;
 // at 4 accesses the exchange's registers push the kernel into spills).  Two
 // such workgroups fit a CU (at most 256 VGPRs a lane, the kernel's launch
