@@ -44,7 +44,9 @@ struct BwdRow {
 // bitwise unchanged.  The LDS waits of the row's reduction also wait for the
 // next row's scalar loads (one counter covers both); fetching a walk's 64
 // next pairs by one vector load instead and reading each with readlane was
-// 3-5 % slower still (8192 x 4096 / 8192, 16384 x 4096).
+// 3-5 % slower still (8192 x 4096 / 8192, 16384 x 4096), and so were per-row
+// vector loads zeroed at the use rather than the load (8192 x 4096 41.3 ->
+// 42.6 us, 8192 x 8192 78 -> 82).
 template <int H, int T, int V>
 __device__ __forceinline__ void load_bwd_row(BwdRow<V>& r, const u32x4* x, const u32x4* dy,
                                              const float* __restrict__ mean,
