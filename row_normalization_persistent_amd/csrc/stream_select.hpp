@@ -109,6 +109,8 @@ constexpr int kXchTileColsF32 = kXchLanesF32 * 4 * 4;
 #define ROWNORM_XCH_WG_CAP 511
 #endif
 constexpr int kXchWgCap = ROWNORM_XCH_WG_CAP;
+static_assert(kXchWgCap <= 255 || kXchLanesBf16 <= kStreamTileLanes / 2,
+              "more than one exchange workgroup a CU needs tiles of at most half the lanes");
 #ifndef ROWNORM_XCH_DEPTH
 #define ROWNORM_XCH_DEPTH 3
 #endif
