@@ -667,10 +667,12 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
     }
     if constexpr (LN) {
         if constexpr ((XCH && kXchVecStats) || (INROW && kInrowVecStats)) {
-            // vector loads (an opaque lane index): counted with the row's own
-            // loads, not with the LDS reductions' scalar counter; the uses
-            // zero a past-end row's values, a select here would wait
-            const int ri = opaque_lane((int)rc);
+            // vector loads (the row index made opaque in vector registers, 64
+            // bits: the one-tile kernel takes any row count): counted with the
+            // row's own loads, not with the LDS reductions' scalar counter; the
+            // uses zero a past-end row's values, a select here would wait
+            int64_t ri = rc;
+            asm volatile("" : "+v"(ri));
             t.mean = a.mean[ri];
             t.rstd = a.rstd[ri];
         } else {
