@@ -161,7 +161,8 @@ def test_forward_f32_deterministic():
 # one-tile rows (up to 8192), LDS-staged rows (8196 ... 16384: 5 ... 8 accesses
 # a lane), tiled rows beyond
 BWD_SHAPES = [(4, 1), (12, 7), (1024, 300), (4096, 1000), (4100, 37), (8192, 45), (8196, 65),
-              (10244, 33), (12288, 300), (16384, 300), (16388, 40), (65536, 17), (1 << 20, 2)]
+              (10244, 33), (12288, 300), (16384, 300), (16388, 40), (65536, 17), (262144, 5),
+              (262148, 3), (1 << 20, 2)]
 
 
 def ln_stats_f32(x, eps):

@@ -163,8 +163,10 @@ def test_stream_forward_behind_the_row_split(op):
 
 
 # ------------------------------------------------------------------ backward
+# both sides of 262144 columns: the widest rows whose tiles exchange partial
+# row sums, and the first that take the row sums kernel and read x, dy again
 BWD_CASES = [(32776, 37), (40000, 300), (65536, 300), (100000, 37), (131072, 1),
-             (1 << 20, 3)]
+             (262144, 11), (262152, 5), (1 << 20, 3)]
 
 
 def lnb_inputs(rows, h, seed):
@@ -223,7 +225,9 @@ def check_rmsb(inp, fused, got, what):
 
 @pytest.mark.parametrize("h,rows", BWD_CASES)
 def test_stream_layernorm_bwd(h, rows):
-    assert "stream_bwd_tile_kernel" in rn.describe_config("layernorm_bwd", rows, h)
+    d = rn.describe_config("layernorm_bwd", rows, h)
+    assert "stream_bwd_tile_kernel" in d
+    assert ("exchanging partial row sums" in d) == (h <= 262144), d
     inp = lnb_inputs(rows, h, seed=h + rows)
     check_lnb(inp, run_lnb(inp), f"layernorm_bwd {rows}x{h}")
 
