@@ -667,14 +667,21 @@ __device__ __forceinline__ void load_tile_row(TileRow<V, DRES>& t, const DynBwdA
     }
     if constexpr (LN) {
         if constexpr ((XCH && kXchVecStats) || (INROW && kInrowVecStats)) {
-            // vector loads (the row index made opaque in vector registers, 64
-            // bits: the one-tile kernel takes any row count): counted with the
-            // row's own loads, not with the LDS reductions' scalar counter; the
-            // uses zero a past-end row's values, a select here would wait
-            int64_t ri = rc;
-            asm volatile("" : "+v"(ri));
-            t.mean = a.mean[ri];
-            t.rstd = a.rstd[ri];
+            // vector loads (the row index made opaque in vector registers):
+            // counted with the row's own loads, not with the LDS reductions'
+            // scalar counter; the uses zero a past-end row's values, a select
+            // here would wait.  32 bits where the host keeps rows below 2^31
+            // (the exchange), 64 for the one-tile kernel (any row count).
+            if constexpr (XCH) {
+                const int ri = opaque_lane((int)rc);
+                t.mean = a.mean[ri];
+                t.rstd = a.rstd[ri];
+            } else {
+                int64_t ri = rc;
+                asm volatile("" : "+v"(ri));
+                t.mean = a.mean[ri];
+                t.rstd = a.rstd[ri];
+            }
         } else {
             const float m = a.mean[rc], q = a.rstd[rc];
             t.mean = in ? m : 0.0f;
