@@ -310,6 +310,18 @@ int32_t stream_walkers(int64_t rows, int64_t hidden) {
     return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, cap / stream_tiles(hidden)));
 }
 
+// Exchanging tiles wait for each other, so the library's own walker count is
+// kept to what the device holds at once (two workgroups a CU at half the
+// tile lanes, else one): on a part with fewer CUs than the 256 the caps
+// assume (a partition), its waits would otherwise run to their limit.  Never
+// raises the count, so the workspace sized for the cap still holds.
+int32_t resident_walkers(int32_t walkers, int32_t tiles, int lanes) {
+    int cu = 0;
+    if (tiles < 2 || current_cu_count(&cu) != NORM_SUCCESS) return walkers;
+    const int64_t slots = (int64_t)cu * (lanes <= kStreamTileLanes / 2 ? 2 : 1);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(walkers, slots / tiles));
+}
+
 // partial-sum slabs per walker: dweight and dbias for LayerNorm, dweight for RMSNorm
 int bwd_outs(norm_op op) { return op == NORM_OP_LAYERNORM_BWD ? 2 : 1; }
 
@@ -1058,6 +1070,8 @@ norm_status run_bwd(norm_op op, const BwdCall& c, const norm_launch_cfg* cfg,
             streamed = true;  // row statistics, then column tiles (kernels_stream.hpp)
         if (!dyn_launch && !streamed)
             return cfg ? NORM_ERROR_INVALID_VALUE : NORM_ERROR_UNSUPPORTED_HIDDEN;
+        if (streamed && !cfg && stream_bwd_xch(c.hidden))
+            k.grid = resident_walkers(k.grid, stream_tiles(c.hidden), kXchLanesBf16);
         const int64_t slabs = k.grid;  // one slab per workgroup (streamed: per walker)
         if (!dyn_slabs_fit(op, c.hidden, slabs) ||
             (streamed && slabs * stream_tiles(c.hidden) > INT32_MAX))
@@ -1266,7 +1280,9 @@ norm_status run_bwd_f32(norm_op op, const BwdCall& c, hipStream_t stream) {
                 (ln && (!aligned(c.mean, 4) || !aligned(c.rstd, 4)))))
         return NORM_ERROR_MISALIGNED;
     const int32_t tiles = stream_tiles_f32(c.hidden);
-    const int32_t walkers = bwd_walkers_f32(c.rows, c.hidden);
+    int32_t walkers = bwd_walkers_f32(c.rows, c.hidden);
+    if (!f32_wide(c.hidden) && stream_bwd_xch(c.hidden))
+        walkers = resident_walkers(walkers, tiles, kXchLanesF32);
     const size_t ws_need = bwd_ws_bytes_f32(op, c.hidden, any ? walkers : 0, any ? c.rows : 0);
 
     const int64_t mrows = any ? c.rows : 0;
