@@ -1062,7 +1062,19 @@ def streamed_ops(torch, rn, wl, dev, stream, reps):
     out.append(_op_rec("rmsnorm_bwd", rows, h, 6 * h * rows + 6 * h, t,
                        note="streamed kernels: column tiles exchanging partial row sums "
                             "(x and dy read once) + column reduce"))
-    del xs, dys, dxs, x0, dy0, ws
+    drs = [torch.empty_like(x0) for _ in range(n)]
+    for d in drs:
+        d.copy_(dy0)
+    torch.cuda.synchronize()
+    t = graph_time_per_launch(torch, stream, [
+        (lambda j=j: rn.fused_add_rmsnorm_bwd(dys[j], xs[j], w, wl.EPS_RMS, dres=drs[j],
+                                              ds=dxs[j], dweight=dw, workspace=ws,
+                                              stream=stream))
+        for j in range(n)], reps)
+    out.append(_op_rec("fused_add_rmsnorm_bwd", rows, h, 8 * h * rows + 6 * h, t,
+                       note="streamed kernels: column tiles exchanging partial row sums "
+                            "(dout, dres and s read once) + column reduce"))
+    del xs, dys, dxs, drs, x0, dy0, ws
     torch.cuda.synchronize()
     return out
 
@@ -1378,6 +1390,9 @@ STREAM_F32_WORKLOADS = [
     ("rmsnorm_bwd (tile exchange)", 4096, 65536,
      "stream_bwd_tile_kernel<unsignedshort,2,false,false,3,false,true>",
      lambda r, h: 6 * h * r + 2 * h),
+    ("fused_add_rmsnorm_bwd (tile exchange)", 4096, 65536,
+     "stream_bwd_tile_kernel<unsignedshort,2,false,true,3,false,true>",
+     lambda r, h: 8 * h * r + 2 * h),
     ("fused_add_rmsnorm_f32", 8192, 4096, "stream_fwd_kernel<float,0,256,4>",
      lambda r, h: 16 * h * r + 4 * h),
     ("rmsnorm_fwd_f32", 4096, 16384, "stream_fwd_kernel<float,1,1024,4>",
