@@ -472,6 +472,10 @@ NORM_API norm_status norm_select_split(norm_op op, int64_t rows, int64_t hidden,
  * persistent scheduler for static fusion", author description: when the
  * batch cannot fill the machine, spread each row over more lanes).
  * cu_count <= 0 queries the current device.  Pure host logic otherwise.
+ * Backward rows past 32768 columns that exchange partial sums between
+ * column tiles get at most 2 * cu_count / tiles row walkers, so that all of
+ * the launch's workgroups are resident at once (the launch applies the same
+ * cap with the current device's CUs).
  * The choice assumes contiguous rows and 16-byte-aligned pointers; a call
  * with strides or smaller alignment may run a run-time-hidden shape with
  * narrower accesses instead. */

@@ -315,11 +315,15 @@ int32_t stream_walkers(int64_t rows, int64_t hidden) {
 // tile lanes, else one): on a part with fewer CUs than the 256 the caps
 // assume (a partition), its waits would otherwise run to their limit.  Never
 // raises the count, so the workspace sized for the cap still holds.
+int32_t resident_walkers_on(int32_t walkers, int32_t tiles, int lanes, int cu) {
+    if (tiles < 2 || cu <= 0) return walkers;
+    const int64_t slots = (int64_t)cu * (lanes <= kStreamTileLanes / 2 ? 2 : 1);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(walkers, slots / tiles));
+}
 int32_t resident_walkers(int32_t walkers, int32_t tiles, int lanes) {
     int cu = 0;
     if (tiles < 2 || current_cu_count(&cu) != NORM_SUCCESS) return walkers;
-    const int64_t slots = (int64_t)cu * (lanes <= kStreamTileLanes / 2 ? 2 : 1);
-    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(walkers, slots / tiles));
+    return resident_walkers_on(walkers, tiles, lanes, cu);
 }
 
 // partial-sum slabs per walker: dweight and dbias for LayerNorm, dweight for RMSNorm
@@ -1166,6 +1170,15 @@ norm_status select(norm_op op, int64_t rows, int64_t hidden, int32_t cu_count,
     if (is_bwd(op)) {
         k = hidden_compiled(hidden) ? choose_bwd(op, rows, hidden)
                                     : choose_dyn_bwd(op, rows, hidden, w, hidden);
+        // the exchange's walkers as the launch caps them to the CUs (given, or
+        // the current device's; with neither, the 256-CU default)
+        if (k.vector_elems == 8 && k.threads_per_row == kStreamTileLanes &&
+            stream_bwd_ok(op, hidden, 8) && stream_bwd_xch(hidden) &&
+            !find_wide(op, hidden, k.threads_per_row, 8)) {
+            int cu = cu_count;
+            if (cu <= 0 && current_cu_count(&cu) != NORM_SUCCESS) cu = 0;
+            k.grid = resident_walkers_on(k.grid, stream_tiles(hidden), kXchLanesBf16, cu);
+        }
     } else {
         int cu = cu_count;
         if (cu <= 0) {

@@ -263,6 +263,12 @@ def test_describe_config():
     d = rn.describe_config("layernorm_bwd", 1000, 65536, cu_count=256)
     assert "31 row walkers x 16 column tiles" in d and "exchanging partial row sums" in d and \
         f"workspace {rn.workspace_bytes(1000, 65536)}" in d
+    # fewer CUs (a partition): the exchange's workgroups stay co-resident, two
+    # a CU: 2 x 32 / 16 tiles = 4 walkers
+    assert rn.select_config("layernorm_bwd", 1000, 65536, cu_count=32).grid == 4
+    assert "4 row walkers x 16 column tiles" in \
+        rn.describe_config("layernorm_bwd", 1000, 65536, cu_count=32)
+    assert rn.select_config("layernorm_bwd", 1000, 65536).grid == 31  # no CU count: 256-CU caps
     d = rn.describe_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     c = rn.select_config("rmsnorm_fwd", 4096, 5120, cu_count=256)
     assert f"rmsnorm_fwd_dyn_kernel<8,{c.threads_per_row}," in d
