@@ -279,7 +279,8 @@ def test_backward_f32_deterministic_and_dirty_workspace():
 
 def test_backward_f32_reread_path_is_bitwise_the_exchange():
     """Rows of several column tiles: the tiles' exchanged partial row sums and
-    the re-read path (spin limit 0: no tile waits) give the same bits."""
+    the re-read path (spin limit 0: no tile waits; 1 or 4 polls: some tiles
+    give up while others wait) give the same bits."""
     rows, h = 300, 40004
     inp = wl.layernorm_bwd_inputs(rows, h, seed=15, f32=True)
     mean32, rstd32 = ln_stats_f32(inp["x"], inp["eps"])
@@ -295,13 +296,16 @@ def test_backward_f32_reread_path_is_bitwise_the_exchange():
         return [t.clone() for t in (*ln, *rms, *fused)]
 
     fast = run()
-    old = rn.set_bwd_spin_limit(0)
-    try:
-        slow = run()
-    finally:
-        rn.set_bwd_spin_limit(old)
-    for k, (a, c) in enumerate(zip(fast, slow)):
-        assert torch.equal(a.view(torch.int32), c.view(torch.int32)), f"output {k}"
+    # 0: no tile waits; 1 and 4 polls: some tiles give up, others do not
+    for limit in (1, 4, 0):
+        old = rn.set_bwd_spin_limit(limit)
+        try:
+            slow = run()
+        finally:
+            rn.set_bwd_spin_limit(old)
+        for k, (a, c) in enumerate(zip(fast, slow)):
+            assert torch.equal(a.view(torch.int32), c.view(torch.int32)), \
+                f"spin limit {limit}, output {k}"
     check_ln_bwd(inp, mean32, rstd32, host(slow[0]), host(slow[1]), host(slow[2]),
                  "layernorm bwd f32, re-read path")
 
