@@ -1186,7 +1186,7 @@ def _cores():
     """(threads the oracle runs on, cores this process may run on).  The
     threads are every core in sched_getaffinity(0), capped by the host's
     per-GPU CPU share when the environment states one (OMP_NUM_THREADS: a
-    one-GPU machine allots 16 cores whatever the affinity mask shows)."""
+    host may allot a GPU's process fewer cores than the affinity mask shows)."""
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
