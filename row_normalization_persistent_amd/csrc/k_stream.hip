@@ -128,10 +128,11 @@ hipError_t launch_tiles_xch(const DynBwdArgs& a, uint64_t* xch, int32_t tiles, i
     if (e != hipSuccess) return e;
     constexpr bool kF32 = std::is_same_v<E, float>;
     constexpr int V = kF32 ? kStreamTileVecs : kXchVecsBf16;
-    // fp32: two rings of 2 (LayerNorm, RMSNorm) or the stats path's one ring (fused);
-    // bf16: 2 accesses a lane, two rings of kXchDepthBf16
+    // fp32: two rings of 2 (LayerNorm, RMSNorm) or of 1 (fused); bf16: 2 accesses
+    // a lane, two rings of kXchDepthBf16
     constexpr int D =
-        kF32 ? (kXchAheadF32 && !DRES ? 2 : tile_depth<LN, DRES>()) : kXchDepthBf16;
+        kF32 ? (kXchAheadF32 && !DRES ? 2 : kXchAheadF32Dres ? 1 : tile_depth<LN, DRES>())
+             : kXchDepthBf16;
     hipLaunchKernelGGL(
         (stream_bwd_tile_kernel<E, V, LN, DRES, D, false, true>),
         dim3((unsigned)(walkers * tiles)), dim3(kF32 ? kXchLanesF32 : kXchLanesBf16), 0,

@@ -966,11 +966,11 @@ __global__ __launch_bounds__(kStreamTileLanes) void stream_bwd_tile_kernel(
     if constexpr (XCH) {
         // The ring's D rows are one group: their partials in one reduction,
         // their exchange in one round trip of polls, then dx row by row.
-        // AHEAD (bf16, and fp32 without dres, whose two rings of 2 rows fit
-        // where the fused op's spill): two rings, the group at i + D published
-        // before the group at i is waited on, so the round trip overlaps a
-        // group's loads and sums.
-        constexpr bool AHEAD = kXchAhead && (ES == 2 || (kXchAheadF32 && !DRES));
+        // AHEAD (bf16; fp32 with two rings of 2 rows, the fused op of 1): two
+        // rings, the group at i + D published before the group at i is waited
+        // on, so the round trip overlaps a group's loads and sums.
+        constexpr bool AHEAD =
+            kXchAhead && (ES == 2 || (kXchAheadF32 && (!DRES || kXchAheadF32Dres)));
         constexpr int kStep = AHEAD ? 2 * D : D;  // walk steps between a ring's groups
         static_assert(AHEAD ? 4 * D <= kXchRing : 2 * D <= kXchRing,
                       "slots of the groups other tiles may still read");

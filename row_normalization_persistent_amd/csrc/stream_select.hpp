@@ -74,6 +74,13 @@ constexpr bool kXchAhead = ROWNORM_XCH_AHEAD != 0;
 #define ROWNORM_XCH_AHEAD_F32 1
 #endif
 constexpr bool kXchAheadF32 = ROWNORM_XCH_AHEAD_F32 != 0;
+// the fp32 fused op, whose dres rows leave room for two rings of one row:
+// against one ring of 2, 512 x 131072 207.5 -> 175.5 us, 2048 x 65536 333 ->
+// 315, 1024 x 49152 127.4 -> 122.2, level at 20480, 8192 x 16388 2 % slower
+#ifndef ROWNORM_XCH_AHEAD_F32_DRES
+#define ROWNORM_XCH_AHEAD_F32_DRES 1
+#endif
+constexpr bool kXchAheadF32Dres = ROWNORM_XCH_AHEAD_F32_DRES != 0;
 // LayerNorm's per-row mean and rstd by vector loads in the exchanging kernel:
 // scalar loads share their counter with LDS, so each group's reductions
 // waited for the statistics of the rows just reloaded.  Against scalar
